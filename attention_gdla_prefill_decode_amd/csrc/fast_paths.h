@@ -1,0 +1,64 @@
+// Interfaces of the bf16 MFMA paths for gfx950 (d_head 128, d_rope 64, d_kv_latent 512).
+#pragma once
+
+#include "gdla_internal.h"
+
+namespace gdla {
+
+// ---- bf16 MFMA GEMM ----
+bool fast_gemm_supported(const GemmBatch &g);
+hipError_t launch_gemm_bf16_mfma(GemmBatch &g, hipStream_t s);
+
+// ---- fused prefill attention ----
+struct FastPrefillLayout {
+  size_t q;      // [M, n_H, d_h + d_r] bf16: q^C and rotated q^R of every head, one row per head
+  size_t qrp;    // [M, n_H, d_r] fp32: q^R before RoPE
+  size_t hn;     // [M, n_N, d_h] fp32: normalised noise-head outputs
+};
+
+template <class Add>
+FastPrefillLayout plan_fast_prefill(const LayerDims &d, int32_t B, int32_t T, Add add) {
+  const size_t M = (size_t)B * T;
+  FastPrefillLayout L{};
+  L.q = add(2 * M * d.n_heads * (d.d_h + d.d_r));
+  L.qrp = add(4 * M * d.n_heads * d.d_r);
+  L.hn = add(4 * M * d.n_noise * d.d_h);
+  return L;
+}
+
+bool fast_prefill_supported(const LayerDims &d, gdla_dtype dt);
+gdla_status run_fast_prefill(const LayerDims &d, const gdla_weights *w, int32_t B, int32_t T,
+                             const int32_t *pos_dev, const int32_t *pos_host, void *cache,
+                             int32_t max_len, void *cq, float *lam, float *gate, void *kx,
+                             void *vx, int32_t lcap, void *y, float *out_heads,
+                             const FastPrefillLayout &L, void *ws, hipStream_t s);
+
+// ---- absorbed split-L decode ----
+struct FastDecodeLayout {
+  size_t qabs;   // [B, n_H, d_c + d_r] bf16
+  size_t part_o; // [B, splits, n_H, d_c] fp32
+  size_t part_ml;// [B, splits, n_H, 2] fp32
+  size_t o;      // [B, n_H, d_c] fp32
+  int32_t splits;
+};
+
+int32_t fast_decode_splits(int32_t B, int32_t max_len);
+
+template <class Add>
+FastDecodeLayout plan_fast_decode(const LayerDims &d, int32_t B, int32_t max_len, Add add) {
+  FastDecodeLayout L{};
+  L.splits = fast_decode_splits(B, max_len);
+  L.qabs = add(2 * (size_t)B * d.n_heads * (d.d_c + d.d_r));
+  L.part_o = add(4 * (size_t)B * L.splits * d.n_heads * d.d_c);
+  L.part_ml = add(4 * (size_t)B * L.splits * d.n_heads * 2);
+  L.o = add(4 * (size_t)B * d.n_heads * d.d_c);
+  return L;
+}
+
+bool fast_decode_supported(const LayerDims &d, gdla_dtype dt);
+gdla_status run_fast_decode(const LayerDims &d, const gdla_weights *w, int32_t B,
+                            const int32_t *pos_dev, const int32_t *pos_host, void *cache,
+                            int32_t max_len, const float *qc, const float *qr, float *heads,
+                            const FastDecodeLayout &L, void *ws, hipStream_t s);
+
+}  // namespace gdla

@@ -1,0 +1,445 @@
+// Host side of the GDLA C ABI: argument validation, workspace planning and the launch sequence of
+// gdla_latent_append / gdla_prefill / gdla_decode.  Every check runs before the first launch.
+#include "gdla_internal.h"
+#include "fast_paths.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#define GDLA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace gdla {
+namespace {
+
+thread_local char g_err[256] = "";
+
+gdla_status fail(gdla_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+#define HIP_TRY(expr)                                                                    \
+  do {                                                                                   \
+    hipError_t e_ = (expr);                                                              \
+    if (e_ != hipSuccess) return fail(GDLA_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+size_t esize(gdla_dtype dt) { return dt == GDLA_F32 ? 4 : 2; }
+
+gdla_status check_dims(const gdla_dims *d, LayerDims &ld) {
+  if (!d) return fail(GDLA_ERR_INVALID_ARG, "dims is NULL");
+  if (d->dtype != GDLA_F32 && d->dtype != GDLA_BF16) return fail(GDLA_ERR_INVALID_ARG, "unknown dtype");
+  if (d->d_model <= 0 || d->n_heads <= 0 || d->n_signal <= 0 || d->n_noise <= 0 ||
+      d->n_kv_heads <= 0 || d->d_q_latent <= 0 || d->d_kv_latent <= 0 || d->d_head <= 0 ||
+      d->d_rope <= 0 || d->window < 0)
+    return fail(GDLA_ERR_INVALID_ARG, "non-positive layer size");
+  if (d->n_signal + d->n_noise != d->n_heads)
+    return fail(GDLA_ERR_INVALID_ARG, "n_signal + n_noise != n_heads");
+  if (d->n_signal % d->n_noise != 0) return fail(GDLA_ERR_INVALID_ARG, "n_noise must divide n_signal");
+  if (d->n_noise % d->n_kv_heads != 0) return fail(GDLA_ERR_INVALID_ARG, "n_kv_heads must divide n_noise");
+  if (d->d_rope % 2 != 0) return fail(GDLA_ERR_INVALID_ARG, "d_rope must be even");
+  if (!(d->rms_eps >= 0.f) || !(d->rope_theta > 0.f) || !(d->softmax_scale >= 0.f))
+    return fail(GDLA_ERR_INVALID_ARG, "rms_eps, rope_theta or softmax_scale out of range");
+  // Limits of the generic kernels (per-lane register arrays and LDS tables).
+  if (d->d_head > 256 || d->d_rope > 64 || d->d_kv_latent + d->d_rope > 1024)
+    return fail(GDLA_ERR_UNSUPPORTED, "d_head <= 256, d_rope <= 64, d_kv_latent + d_rope <= 1024");
+  ld.d_model = d->d_model; ld.n_heads = d->n_heads; ld.n_signal = d->n_signal;
+  ld.n_noise = d->n_noise; ld.n_kv = d->n_kv_heads; ld.d_cq = d->d_q_latent;
+  ld.d_c = d->d_kv_latent; ld.d_h = d->d_head; ld.d_r = d->d_rope; ld.window = d->window;
+  ld.eps = d->rms_eps; ld.theta = d->rope_theta;
+  ld.scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / sqrtf((float)(d->d_head + d->d_rope));
+  return GDLA_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// ---------------------------------------------------------------------------------------------
+// Workspace planning.  Every buffer starts on a 256-byte boundary.
+struct Plan {
+  size_t bytes = 0;
+  size_t add(size_t n) {
+    const size_t off = bytes;
+    bytes += (n + 255) & ~size_t(255);
+    return off;
+  }
+};
+
+// Keys [lo_b, hi_b) of sequence b that a prefill over T tokens starting at p0 may read.
+inline int32_t key_lo(int32_t p0, int32_t window) { return window > 0 ? std::max(0, p0 - window + 1) : 0; }
+
+struct PrefillLayout {
+  size_t pos, aq, ckv, krp, laml, cq, lam, qc, qrp, qr, gate, kx, vx, heads, y, total;
+  int32_t lcap;
+  FastPrefillLayout fast;
+  bool use_fast;
+};
+
+int32_t key_capacity(const LayerDims &d, int32_t B, int32_t T, const int32_t *pos, int32_t max_len) {
+  int32_t lcap = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t p0 = pos ? pos[b] : max_len - T;
+    const int32_t lo = pos ? key_lo(p0, d.window) : 0;
+    lcap = std::max(lcap, p0 + T - lo);
+  }
+  return lcap;
+}
+
+PrefillLayout plan_prefill(const LayerDims &d, gdla_dtype dt, int32_t B, int32_t T,
+                           const int32_t *pos, int32_t max_len) {
+  PrefillLayout L{};
+  const size_t es = esize(dt);
+  const size_t M = (size_t)B * T;
+  L.lcap = key_capacity(d, B, T, pos, max_len);
+  L.use_fast = fast_prefill_supported(d, dt);
+  Plan p;
+  L.pos = p.add(sizeof(int32_t) * B);
+  L.aq = p.add(4 * M * d.d_cq);
+  L.ckv = p.add(4 * M * d.d_c);
+  L.krp = p.add(4 * M * d.d_r);
+  L.laml = p.add(4 * M * d.n_signal);
+  L.cq = p.add(es * M * d.d_cq);
+  L.lam = p.add(4 * M * d.n_signal);
+  L.gate = p.add(4 * M * d.n_signal * d.d_h);
+  L.kx = p.add(es * (size_t)B * d.n_kv * L.lcap * d.d_h);
+  L.vx = p.add(es * (size_t)B * d.n_kv * L.lcap * d.d_h);
+  L.y = p.add(es * M * d.n_signal * d.d_h);
+  if (L.use_fast) {
+    L.fast = plan_fast_prefill(d, B, T, [&](size_t n) { return p.add(n); });
+  } else {
+    L.qc = p.add(es * M * d.n_heads * d.d_h);
+    L.qrp = p.add(4 * M * d.n_heads * d.d_r);
+    L.qr = p.add(es * M * d.n_heads * d.d_r);
+    L.heads = p.add(4 * M * d.n_heads * d.d_h);
+  }
+  L.total = p.bytes;
+  return L;
+}
+
+struct DecodeLayout {
+  size_t pos, aq, ckv, krp, laml, cq, lam, qc, qrp, qr, gate, qabs, o, heads, y, total;
+  FastDecodeLayout fast;
+  bool use_fast;
+};
+
+DecodeLayout plan_decode(const LayerDims &d, gdla_dtype dt, int32_t B, int32_t max_len) {
+  DecodeLayout L{};
+  const size_t es = esize(dt);
+  const size_t M = (size_t)B;
+  L.use_fast = fast_decode_supported(d, dt);
+  Plan p;
+  L.pos = p.add(sizeof(int32_t) * B);
+  L.aq = p.add(4 * M * d.d_cq);
+  L.ckv = p.add(4 * M * d.d_c);
+  L.krp = p.add(4 * M * d.d_r);
+  L.laml = p.add(4 * M * d.n_signal);
+  L.cq = p.add(es * M * d.d_cq);
+  L.lam = p.add(4 * M * d.n_signal);
+  L.qc = p.add(4 * M * d.n_heads * d.d_h);
+  L.qrp = p.add(4 * M * d.n_heads * d.d_r);
+  L.qr = p.add(4 * M * d.n_heads * d.d_r);
+  L.gate = p.add(4 * M * d.n_signal * d.d_h);
+  L.heads = p.add(4 * M * d.n_heads * d.d_h);
+  L.y = p.add(es * M * d.n_signal * d.d_h);
+  if (L.use_fast) {
+    L.fast = plan_fast_decode(d, B, max_len, [&](size_t n) { return p.add(n); });
+  } else {
+    L.qabs = p.add(4 * M * d.n_heads * (d.d_c + d.d_r));
+    L.o = p.add(4 * M * d.n_heads * d.d_c);
+  }
+  L.total = p.bytes;
+  return L;
+}
+
+struct AppendLayout {
+  size_t pos, ckv, krp, total;
+};
+
+AppendLayout plan_append(const LayerDims &d, int32_t B, int32_t T) {
+  AppendLayout L{};
+  const size_t M = (size_t)B * T;
+  Plan p;
+  L.pos = p.add(sizeof(int32_t) * B);
+  L.ckv = p.add(4 * M * d.d_c);
+  L.krp = p.add(4 * M * d.d_r);
+  L.total = p.bytes;
+  return L;
+}
+
+// ---------------------------------------------------------------------------------------------
+gdla_status check_call(const gdla_dims *dims, const gdla_weights *w, const void *x, int32_t B,
+                       int32_t T, const int32_t *pos, const void *cache, int32_t max_len,
+                       const void *out, bool need_query_weights, LayerDims &ld) {
+  gdla_status st = check_dims(dims, ld);
+  if (st != GDLA_OK) return st;
+  if (B < 0 || T < 0 || max_len <= 0) return fail(GDLA_ERR_INVALID_ARG, "negative B/T or max_len <= 0");
+  if (B == 0 || T == 0) return GDLA_OK;
+  if (!w) return fail(GDLA_ERR_INVALID_ARG, "weights is NULL");
+  if (!x || !cache || !pos) return fail(GDLA_ERR_INVALID_ARG, "x, cache or pos_host is NULL");
+  if (need_query_weights && !out) return fail(GDLA_ERR_INVALID_ARG, "out is NULL");
+  const void *req[] = {w->w_dkv, w->w_kr};
+  for (const void *p : req)
+    if (!p) return fail(GDLA_ERR_INVALID_ARG, "a required weight pointer is NULL");
+  if (need_query_weights) {
+    const void *req2[] = {w->w_qa, w->w_qc, w->w_qr, w->w_uk, w->w_uv, w->w_lambda, w->w_gate, w->w_o};
+    for (const void *p : req2)
+      if (!p) return fail(GDLA_ERR_INVALID_ARG, "a required weight pointer is NULL");
+  }
+  const void *al[] = {x, cache, out, w->w_qa, w->w_qc, w->w_qr, w->w_dkv, w->w_kr, w->w_uk,
+                      w->w_uv, w->w_lambda, w->w_gate, w->w_o, w->gamma_q, w->gamma_kv};
+  for (const void *p : al)
+    if (p && !aligned16(p)) return fail(GDLA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  for (int32_t b = 0; b < B; ++b) {
+    if (pos[b] < 0) return fail(GDLA_ERR_OUT_OF_RANGE, "pos_host[%d] = %d < 0", b, pos[b]);
+    if ((int64_t)pos[b] + T > max_len)
+      return fail(GDLA_ERR_OUT_OF_RANGE, "pos_host[%d] + T = %lld > max_len %d", b,
+                  (long long)pos[b] + T, max_len);
+  }
+  return GDLA_OK;
+}
+
+gdla_status check_ws(const void *ws, size_t ws_bytes, size_t need) {
+  if (ws_bytes < need) return fail(GDLA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (need > 0 && !ws) return fail(GDLA_ERR_INVALID_ARG, "workspace is NULL");
+  if (((uintptr_t)ws & 255u) != 0) return fail(GDLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return GDLA_OK;
+}
+
+template <typename T> T *at(void *base, size_t off) { return (T *)((char *)base + off); }
+
+GemmProblem gp(const void *A, int64_t lda, const void *B, int64_t ldb, void *C, int64_t ldc,
+               int32_t M, int32_t N, int32_t K, bool c_f32, int epi = EPI_NONE) {
+  GemmProblem p{};
+  p.A = A; p.lda = lda; p.B = B; p.ldb = ldb; p.C = C; p.ldc = ldc;
+  p.M = M; p.N = N; p.K = K; p.hw = N > 0 ? N : 1; p.hs = 0; p.ho = 0;
+  p.c_f32 = c_f32 ? 1 : 0; p.epi = epi;
+  return p;
+}
+
+// First projection, Eq.(1), (3), (7) (x W_qa, x W_dkv, x W_kr, x W_lambda) and the row-wise
+// normalisation / RoPE / cache append / sigmoid step.
+gdla_status project_and_append(const LayerDims &d, DT dt, const gdla_weights *w, const void *x,
+                               int32_t M, int32_t T, const int32_t *pos_dev, void *cache,
+                               int32_t max_len, float *aq, float *ckv, float *krp, float *laml,
+                               void *cq, float *lam, const float *lam_override, hipStream_t s) {
+  GemmBatch g{};
+  g.p[g.n++] = gp(x, d.d_model, w->w_dkv, d.d_c, ckv, d.d_c, M, d.d_c, d.d_model, true);
+  g.p[g.n++] = gp(x, d.d_model, w->w_kr, d.d_r, krp, d.d_r, M, d.d_r, d.d_model, true);
+  if (cq) g.p[g.n++] = gp(x, d.d_model, w->w_qa, d.d_cq, aq, d.d_cq, M, d.d_cq, d.d_model, true);
+  if (lam && !lam_override)
+    g.p[g.n++] = gp(x, d.d_model, w->w_lambda, d.n_signal, laml, d.n_signal, M, d.n_signal, d.d_model, true);
+  HIP_TRY(launch_gemm(g, dt, s));
+  PrepArgs a{};
+  a.aq = aq; a.ckv = ckv; a.kr = krp; a.lam_logit = laml; a.lam_override = lam_override;
+  a.gamma_q = w->gamma_q; a.gamma_kv = w->gamma_kv; a.cq = cq; a.lam = lam; a.cache = cache;
+  a.pos = pos_dev; a.M = M; a.T = T; a.max_len = max_len;
+  HIP_TRY(launch_prep(a, d, dt, s));
+  return GDLA_OK;
+}
+
+}  // namespace
+
+// GEMM dispatch shared by all entry points: MFMA kernels for bf16 when every problem fits them.
+hipError_t launch_gemm(GemmBatch &g, DT dt, hipStream_t s) {
+  if (dt == DT::BF16 && fast_gemm_supported(g)) return launch_gemm_bf16_mfma(g, s);
+  return launch_gemm_generic(g, dt, s);
+}
+
+}  // namespace gdla
+
+using namespace gdla;
+
+GDLA_EXPORT const char *gdla_status_string(gdla_status s) {
+  switch (s) {
+    case GDLA_OK: return "GDLA_OK";
+    case GDLA_ERR_INVALID_ARG: return "GDLA_ERR_INVALID_ARG";
+    case GDLA_ERR_UNSUPPORTED: return "GDLA_ERR_UNSUPPORTED";
+    case GDLA_ERR_WORKSPACE: return "GDLA_ERR_WORKSPACE";
+    case GDLA_ERR_OUT_OF_RANGE: return "GDLA_ERR_OUT_OF_RANGE";
+    case GDLA_ERR_HIP: return "GDLA_ERR_HIP";
+  }
+  return "unknown gdla_status";
+}
+
+GDLA_EXPORT const char *gdla_last_error(void) { return g_err; }
+
+GDLA_EXPORT size_t gdla_workspace_bytes(const gdla_dims *dims, int32_t op, int32_t B, int32_t T,
+                                        const int32_t *pos_host, int32_t max_len) {
+  LayerDims d;
+  if (check_dims(dims, d) != GDLA_OK) return 0;
+  if (B < 0 || T < 0 || max_len <= 0 || (op == GDLA_OP_DECODE && T != 1 && T != 0)) return 0;
+  if (B == 0 || T == 0) return 0;
+  if (T > max_len) return 0;
+  if (pos_host) {
+    for (int32_t b = 0; b < B; ++b)
+      if (pos_host[b] < 0 || (int64_t)pos_host[b] + T > max_len) return 0;
+  }
+  switch (op) {
+    case GDLA_OP_PREFILL: return plan_prefill(d, dims->dtype, B, T, pos_host, max_len).total;
+    case GDLA_OP_DECODE: return plan_decode(d, dims->dtype, B, max_len).total;
+    case GDLA_OP_APPEND: return plan_append(d, B, T).total;
+    default: return 0;
+  }
+}
+
+GDLA_EXPORT gdla_status gdla_latent_append(const gdla_dims *dims, const gdla_weights *w,
+                                           const void *x, int32_t B, int32_t T,
+                                           const int32_t *pos_host, void *cache, int32_t max_len,
+                                           void *ws, size_t ws_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  LayerDims d;
+  gdla_status st = check_call(dims, w, x, B, T, pos_host, cache, max_len, nullptr, false, d);
+  if (st != GDLA_OK || B == 0 || T == 0) return st;
+  const AppendLayout L = plan_append(d, B, T);
+  if ((st = check_ws(ws, ws_bytes, L.total)) != GDLA_OK) return st;
+  const DT dt = dims->dtype == GDLA_F32 ? DT::F32 : DT::BF16;
+  int32_t *pos_dev = at<int32_t>(ws, L.pos);
+  HIP_TRY(launch_set_i32(pos_dev, pos_host, B, stream));
+  return project_and_append(d, dt, w, x, B * T, T, pos_dev, cache, max_len, nullptr,
+                            at<float>(ws, L.ckv), at<float>(ws, L.krp), nullptr, nullptr, nullptr,
+                            nullptr, stream);
+}
+
+GDLA_EXPORT gdla_status gdla_prefill(const gdla_dims *dims, const gdla_weights *w, const void *x,
+                                     int32_t B, int32_t T, const int32_t *pos_host, void *cache,
+                                     int32_t max_len, void *out, void *ws, size_t ws_bytes,
+                                     const gdla_debug *dbg, hipStream_t stream) {
+  g_err[0] = 0;
+  LayerDims d;
+  gdla_status st = check_call(dims, w, x, B, T, pos_host, cache, max_len, out, true, d);
+  if (st != GDLA_OK || B == 0 || T == 0) return st;
+  const PrefillLayout L = plan_prefill(d, dims->dtype, B, T, pos_host, max_len);
+  if ((st = check_ws(ws, ws_bytes, L.total)) != GDLA_OK) return st;
+  const DT dt = dims->dtype == GDLA_F32 ? DT::F32 : DT::BF16;
+  const size_t es = esize(dims->dtype);
+  const int32_t M = B * T;
+  const float *lam_override = dbg ? dbg->lambda_override : nullptr;
+  float *out_heads = dbg ? dbg->out_heads : nullptr;
+
+  int32_t *pos_dev = at<int32_t>(ws, L.pos);
+  HIP_TRY(launch_set_i32(pos_dev, pos_host, B, stream));
+  // Eq.(1), (3), (4), (7) and the cache append of this chunk's rows.
+  st = project_and_append(d, dt, w, x, M, T, pos_dev, cache, max_len, at<float>(ws, L.aq),
+                          at<float>(ws, L.ckv), at<float>(ws, L.krp), at<float>(ws, L.laml),
+                          at<void>(ws, L.cq), at<float>(ws, L.lam), lam_override, stream);
+  if (st != GDLA_OK) return st;
+
+  // Eq.(5): expand K^C and V of every visible key, head-major [B, n_kv, lcap, d_h].
+  const int64_t row = d.d_c + d.d_r;
+  const int64_t kv_seq = (int64_t)d.n_kv * L.lcap * d.d_h;
+  for (int32_t b0 = 0; b0 < B; b0 += kMaxGemmProblems / 2) {
+    GemmBatch g{};
+    for (int32_t b = b0; b < std::min(B, b0 + kMaxGemmProblems / 2); ++b) {
+      const int32_t lo = key_lo(pos_host[b], d.window);
+      const int32_t nk = pos_host[b] + T - lo;
+      const char *a = (const char *)cache + ((int64_t)b * max_len + lo) * row * es;
+      GemmProblem pk = gp(a, row, w->w_uk, (int64_t)d.n_kv * d.d_h,
+                          at<char>(ws, L.kx) + b * kv_seq * es, d.d_h, nk, d.n_kv * d.d_h, d.d_c, false);
+      pk.hw = d.d_h;
+      pk.hs = (int64_t)L.lcap * d.d_h;
+      GemmProblem pv = pk;
+      pv.B = w->w_uv;
+      pv.C = at<char>(ws, L.vx) + b * kv_seq * es;
+      g.p[g.n++] = pk;
+      g.p[g.n++] = pv;
+    }
+    HIP_TRY(launch_gemm(g, dt, stream));
+  }
+
+  if (L.use_fast) {
+    st = run_fast_prefill(d, w, B, T, pos_dev, pos_host, cache, max_len, at<void>(ws, L.cq),
+                          at<float>(ws, L.lam), at<float>(ws, L.gate), at<void>(ws, L.kx),
+                          at<void>(ws, L.vx), L.lcap, at<void>(ws, L.y), out_heads, L.fast, ws,
+                          stream);
+    if (st != GDLA_OK) return fail(st, "fast prefill path failed: %s", hipGetErrorString(hipGetLastError()));
+  } else {
+    // Eq.(2), (9): q^C, pre-RoPE q^R and gate logits.
+    GemmBatch g{};
+    g.p[g.n++] = gp(at<void>(ws, L.cq), d.d_cq, w->w_qc, (int64_t)d.n_heads * d.d_h, at<void>(ws, L.qc),
+                    (int64_t)d.n_heads * d.d_h, M, d.n_heads * d.d_h, d.d_cq, false);
+    g.p[g.n++] = gp(at<void>(ws, L.cq), d.d_cq, w->w_qr, (int64_t)d.n_heads * d.d_r, at<float>(ws, L.qrp),
+                    (int64_t)d.n_heads * d.d_r, M, d.n_heads * d.d_r, d.d_cq, true);
+    g.p[g.n++] = gp(at<void>(ws, L.cq), d.d_cq, w->w_gate, (int64_t)d.n_signal * d.d_h, at<float>(ws, L.gate),
+                    (int64_t)d.n_signal * d.d_h, M, d.n_signal * d.d_h, d.d_cq, true);
+    HIP_TRY(launch_gemm(g, dt, stream));
+    HIP_TRY(launch_rope_heads(at<float>(ws, L.qrp), at<void>(ws, L.qr), (int64_t)d.n_heads * d.d_r, 0, M, T,
+                              d.n_heads, d.d_r, pos_dev, d.theta, dt, stream));
+    AttnGenericArgs a{};
+    a.qc = at<void>(ws, L.qc); a.qr = at<void>(ws, L.qr); a.kx = at<void>(ws, L.kx);
+    a.vx = at<void>(ws, L.vx); a.cache = cache; a.heads = at<float>(ws, L.heads); a.pos = pos_dev;
+    a.M = M; a.T = T; a.max_len = max_len; a.lcap = L.lcap;
+    HIP_TRY(launch_attention_generic(a, d, dt, stream));
+    if (out_heads)
+      HIP_TRY(launch_copy_rows_f32(at<float>(ws, L.heads), (int64_t)d.n_heads * d.d_h, out_heads,
+                                   (int64_t)d.n_heads * d.d_h, M, d.n_heads * d.d_h, stream));
+    HIP_TRY(launch_combine(at<float>(ws, L.heads), at<float>(ws, L.lam), at<float>(ws, L.gate),
+                           at<void>(ws, L.y), M, d, dt, stream));
+  }
+  // Eq.(10): out = Y W_o.
+  GemmBatch g{};
+  g.p[g.n++] = gp(at<void>(ws, L.y), (int64_t)d.n_signal * d.d_h, w->w_o, d.d_model, out, d.d_model, M,
+                  d.d_model, d.n_signal * d.d_h, false);
+  HIP_TRY(launch_gemm(g, dt, stream));
+  return GDLA_OK;
+}
+
+GDLA_EXPORT gdla_status gdla_decode(const gdla_dims *dims, const gdla_weights *w, const void *x,
+                                    int32_t B, const int32_t *pos_host, void *cache,
+                                    int32_t max_len, void *out, void *ws, size_t ws_bytes,
+                                    const gdla_debug *dbg, hipStream_t stream) {
+  g_err[0] = 0;
+  LayerDims d;
+  gdla_status st = check_call(dims, w, x, B, 1, pos_host, cache, max_len, out, true, d);
+  if (st != GDLA_OK || B == 0) return st;
+  const DecodeLayout L = plan_decode(d, dims->dtype, B, max_len);
+  if ((st = check_ws(ws, ws_bytes, L.total)) != GDLA_OK) return st;
+  const DT dt = dims->dtype == GDLA_F32 ? DT::F32 : DT::BF16;
+  const float *lam_override = dbg ? dbg->lambda_override : nullptr;
+  float *out_heads = dbg ? dbg->out_heads : nullptr;
+
+  int32_t *pos_dev = at<int32_t>(ws, L.pos);
+  HIP_TRY(launch_set_i32(pos_dev, pos_host, B, stream));
+  st = project_and_append(d, dt, w, x, B, 1, pos_dev, cache, max_len, at<float>(ws, L.aq),
+                          at<float>(ws, L.ckv), at<float>(ws, L.krp), at<float>(ws, L.laml),
+                          at<void>(ws, L.cq), at<float>(ws, L.lam), lam_override, stream);
+  if (st != GDLA_OK) return st;
+  // Eq.(2), (9) in fp32 (decode keeps the query in fp32 until it is mapped into the latent).
+  GemmBatch g{};
+  g.p[g.n++] = gp(at<void>(ws, L.cq), d.d_cq, w->w_qc, (int64_t)d.n_heads * d.d_h, at<float>(ws, L.qc),
+                  (int64_t)d.n_heads * d.d_h, B, d.n_heads * d.d_h, d.d_cq, true);
+  g.p[g.n++] = gp(at<void>(ws, L.cq), d.d_cq, w->w_qr, (int64_t)d.n_heads * d.d_r, at<float>(ws, L.qrp),
+                  (int64_t)d.n_heads * d.d_r, B, d.n_heads * d.d_r, d.d_cq, true);
+  g.p[g.n++] = gp(at<void>(ws, L.cq), d.d_cq, w->w_gate, (int64_t)d.n_signal * d.d_h, at<float>(ws, L.gate),
+                  (int64_t)d.n_signal * d.d_h, B, d.n_signal * d.d_h, d.d_cq, true);
+  HIP_TRY(launch_gemm(g, dt, stream));
+  HIP_TRY(launch_rope_heads(at<float>(ws, L.qrp), at<float>(ws, L.qr), (int64_t)d.n_heads * d.d_r, 0, B, 1,
+                            d.n_heads, d.d_r, pos_dev, d.theta, DT::F32, stream));
+  if (L.use_fast) {
+    st = run_fast_decode(d, w, B, pos_dev, pos_host, cache, max_len, at<float>(ws, L.qc),
+                         at<float>(ws, L.qr), at<float>(ws, L.heads), L.fast, ws, stream);
+    if (st != GDLA_OK) return fail(st, "fast decode path failed: %s", hipGetErrorString(hipGetLastError()));
+  } else {
+    HIP_TRY(launch_absorb_generic(at<float>(ws, L.qc), at<float>(ws, L.qr), w->w_uk, at<float>(ws, L.qabs),
+                                  B, d, dt, stream));
+    HIP_TRY(launch_latent_attention_generic(at<float>(ws, L.qabs), cache, at<float>(ws, L.o), pos_dev, B,
+                                            max_len, d, dt, stream));
+    HIP_TRY(launch_unabsorb_generic(at<float>(ws, L.o), w->w_uv, at<float>(ws, L.heads), B, d, dt, stream));
+  }
+  if (out_heads)
+    HIP_TRY(launch_copy_rows_f32(at<float>(ws, L.heads), (int64_t)d.n_heads * d.d_h, out_heads,
+                                 (int64_t)d.n_heads * d.d_h, B, d.n_heads * d.d_h, stream));
+  HIP_TRY(launch_combine(at<float>(ws, L.heads), at<float>(ws, L.lam), at<float>(ws, L.gate),
+                         at<void>(ws, L.y), B, d, dt, stream));
+  g = GemmBatch{};
+  g.p[g.n++] = gp(at<void>(ws, L.y), (int64_t)d.n_signal * d.d_h, w->w_o, d.d_model, out, d.d_model, B,
+                  d.d_model, d.n_signal * d.d_h, false);
+  HIP_TRY(launch_gemm(g, dt, stream));
+  return GDLA_OK;
+}

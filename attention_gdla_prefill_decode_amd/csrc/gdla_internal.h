@@ -1,0 +1,120 @@
+// Internal declarations of the GDLA library: problem descriptors shared by the host orchestrator
+// (gdla_api.hip) and the kernel files, and the launch functions each kernel file exports.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/gdla.h"
+
+namespace gdla {
+
+typedef __bf16 bf16_t;
+
+enum class DT : int32_t { F32 = 0, BF16 = 1 };
+
+// One GEMM problem: C[m, col(n)] = epi(sum_k A[m, k] * B[k, n]), fp32 accumulation.
+// A is [M, K] with row stride lda, B is [K, N] with row stride ldb (both in the input dtype).
+// Output column n of row m is stored at C + m * ldc + (n / hw) * hs + ho + (n % hw) (elements of
+// the output dtype), which lets one launch write head-major or interleaved layouts.
+struct GemmProblem {
+  const void *A;
+  const void *B;
+  void *C;
+  int64_t lda, ldb, ldc;
+  int64_t hs;
+  int32_t M, N, K;
+  int32_t hw, ho;
+  int32_t c_f32;   // 1: fp32 output, 0: output in the input dtype
+  int32_t epi;     // EPI_*
+  int32_t tile0;   // first linear tile index of this problem (filled by the launcher)
+  int32_t tiles_n; // tiles along N (filled by the launcher)
+};
+
+enum { EPI_NONE = 0, EPI_SIGMOID = 1 };
+
+constexpr int kMaxGemmProblems = 8;
+
+struct GemmBatch {
+  GemmProblem p[kMaxGemmProblems];
+  int32_t n;
+  int32_t total_tiles;
+};
+
+// Per-call layer description used by device code (all int32 sizes).
+struct LayerDims {
+  int32_t d_model, n_heads, n_signal, n_noise, n_kv, d_cq, d_c, d_h, d_r, window;
+  float eps, theta, scale;
+};
+
+__host__ __device__ inline int kv_head_of(int h, int n_signal, int n_kv) {
+  return h < n_signal ? (h % n_kv) : ((h - n_signal) % n_kv);
+}
+
+// GEMM dispatch: bf16 MFMA kernels when every problem of the batch fits them, else generic.
+hipError_t launch_gemm(GemmBatch &batch, DT dt, hipStream_t s);
+
+// ---------------- generic kernels (any sizes; fp32 or bf16 storage, fp32 math) ---------------
+hipError_t launch_gemm_generic(GemmBatch &batch, DT in_dt, hipStream_t s);
+
+// Row-wise preparation after the first projection (one row per new token):
+//   c^Q = RMSNorm(aq) * gamma_q -> cq (input dtype)          [skipped when cq == nullptr]
+//   cache row (b, pos[b] + t) = [RMSNorm(ckv) * gamma_kv ; RoPE(kr, pos)]
+//   lam = sigmoid(lam_logit) or lam_override                 [skipped when lam == nullptr]
+struct PrepArgs {
+  const float *aq;        // [M, d_cq]
+  const float *ckv;       // [M, d_c]
+  const float *kr;        // [M, d_r]
+  const float *lam_logit; // [M, n_S]
+  const float *lam_override;
+  const void *gamma_q, *gamma_kv;
+  void *cq;               // [M, d_cq]
+  float *lam;             // [M, n_S]
+  void *cache;            // [B, max_len, d_c + d_r]
+  const int32_t *pos;     // [B] device
+  int32_t M, T, max_len;
+};
+hipError_t launch_prep(const PrepArgs &a, const LayerDims &d, DT dt, hipStream_t s);
+
+// In-place style RoPE of per-head rows: dst[m, h, :] = RoPE(src[m, h, :], pos[m / T] + m % T).
+hipError_t launch_rope_heads(const float *src, void *dst, int64_t dst_ld, int32_t dst_off,
+                             int32_t M, int32_t T, int32_t n_heads, int32_t d_r,
+                             const int32_t *pos, float theta, DT dt, hipStream_t s);
+
+// Expanded-form attention, one wave per (query row, head).  qc [M, n_H, d_h], qr [M, n_H, d_r]
+// (after RoPE), kx / vx [B, n_kv, lcap, d_h] holding keys lo_b .. lo_b + lcap - 1, k^R read from
+// the cache.  Writes heads [M, n_H, d_h] fp32.
+struct AttnGenericArgs {
+  const void *qc, *qr, *kx, *vx, *cache;
+  float *heads;
+  const int32_t *pos;
+  int32_t M, T, max_len, lcap;
+};
+hipError_t launch_attention_generic(const AttnGenericArgs &a, const LayerDims &d, DT dt,
+                                    hipStream_t s);
+
+// Eq.(8)-(10) before W_o: y[m, i, e] = sigmoid(g[m, i, e]) * (H[m, i, e] - lam[m, i] *
+// H[m, n_S + i mod n_N, e]) in the input dtype.
+hipError_t launch_combine(const float *heads, const float *lam, const float *gate, void *y,
+                          int32_t M, const LayerDims &d, DT dt, hipStream_t s);
+
+// Absorbed decode (one query per sequence at position pos[b]):
+//   qabs[b, h] = [q^C_h W_uk[:, kv(h)]^T ; q^R_h]      (fp32, [B, n_H, d_c + d_r])
+hipError_t launch_absorb_generic(const float *qc, const float *qr, const void *w_uk, float *qabs,
+                                 int32_t B, const LayerDims &d, DT dt, hipStream_t s);
+//   o[b, h] = sum_s softmax_s(tau qabs[b, h] . cache[b, s]) cache[b, s, 0:d_c]   (fp32)
+hipError_t launch_latent_attention_generic(const float *qabs, const void *cache, float *o,
+                                           const int32_t *pos, int32_t B, int32_t max_len,
+                                           const LayerDims &d, DT dt, hipStream_t s);
+//   heads[b, h] = o[b, h] W_uv[:, kv(h)]   (fp32 [B, n_H, d_h])
+hipError_t launch_unabsorb_generic(const float *o, const void *w_uv, float *heads, int32_t B,
+                                   const LayerDims &d, DT dt, hipStream_t s);
+
+// Copies up to 128 host values into a device int32 array through kernel arguments, so that no
+// host-to-device copy (and no pinned host buffer) is needed.
+hipError_t launch_set_i32(int32_t *dst, const int32_t *src_host, int32_t n, hipStream_t s);
+// Copies fp32 rows to another fp32 buffer with a different row stride (debug outputs).
+hipError_t launch_copy_rows_f32(const float *src, int64_t src_ld, float *dst, int64_t dst_ld,
+                                int32_t rows, int32_t cols, hipStream_t s);
+
+}  // namespace gdla

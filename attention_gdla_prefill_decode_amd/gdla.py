@@ -1,0 +1,186 @@
+"""Thin ctypes binding of libgdla.so (include/gdla.h).
+
+Argument marshalling only: torch tensors supply device memory and the current stream; every step
+of the GDLA forward runs in the library's HIP kernels.  There is no fallback: if libgdla.so is
+missing, or a call fails, an exception is raised.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgdla.so")
+
+GDLA_OK, GDLA_ERR_INVALID_ARG, GDLA_ERR_UNSUPPORTED, GDLA_ERR_WORKSPACE, GDLA_ERR_OUT_OF_RANGE, \
+    GDLA_ERR_HIP = range(6)
+GDLA_F32, GDLA_BF16 = 0, 1
+GDLA_OP_PREFILL, GDLA_OP_DECODE, GDLA_OP_APPEND = 0, 1, 2
+
+WEIGHT_FIELDS = ("w_qa", "gamma_q", "w_qc", "w_qr", "w_dkv", "w_kr", "gamma_kv", "w_uk", "w_uv",
+                 "w_lambda", "w_gate", "w_o")
+
+EXPORTED = ("gdla_workspace_bytes", "gdla_latent_append", "gdla_prefill", "gdla_decode",
+            "gdla_status_string", "gdla_last_error")
+
+
+class GdlaDims(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("n_signal", ctypes.c_int32), ("n_noise", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("d_q_latent", ctypes.c_int32),
+                ("d_kv_latent", ctypes.c_int32), ("d_head", ctypes.c_int32),
+                ("d_rope", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
+                ("softmax_scale", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+class GdlaWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_FIELDS]
+
+
+class GdlaDebug(ctypes.Structure):
+    _fields_ = [("lambda_override", ctypes.c_void_p), ("out_heads", ctypes.c_void_p)]
+
+
+class GdlaError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(message)
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libgdla.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first with "
+                               "`python -m attention_gdla_prefill_decode_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        L.gdla_workspace_bytes.restype = ctypes.c_size_t
+        L.gdla_workspace_bytes.argtypes = [P(GdlaDims), ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32]
+        L.gdla_latent_append.restype = ctypes.c_int
+        L.gdla_latent_append.argtypes = [P(GdlaDims), P(GdlaWeights), ctypes.c_void_p,
+                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                         ctypes.c_size_t, ctypes.c_void_p]
+        L.gdla_prefill.restype = ctypes.c_int
+        L.gdla_prefill.argtypes = [P(GdlaDims), P(GdlaWeights), ctypes.c_void_p, ctypes.c_int32,
+                                   ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_size_t, P(GdlaDebug), ctypes.c_void_p]
+        L.gdla_decode.restype = ctypes.c_int
+        L.gdla_decode.argtypes = [P(GdlaDims), P(GdlaWeights), ctypes.c_void_p, ctypes.c_int32,
+                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                  P(GdlaDebug), ctypes.c_void_p]
+        L.gdla_status_string.restype = ctypes.c_char_p
+        L.gdla_status_string.argtypes = [ctypes.c_int]
+        L.gdla_last_error.restype = ctypes.c_char_p
+        L.gdla_last_error.argtypes = []
+        _lib = L
+    return _lib
+
+
+def make_dims(cfg, window=None, dtype=None, eps=1e-6, theta=10000.0, scale=0.0):
+    """gdla_dims from a workload dict (keys d_model, n_heads, ..., dtype 'f32' / 'bf16')."""
+    dt = cfg["dtype"] if dtype is None else dtype
+    return GdlaDims(cfg["d_model"], cfg["n_heads"], cfg["n_signal"], cfg["n_noise"], cfg["n_kv"],
+                    cfg["d_q_latent"], cfg["d_kv_latent"], cfg["d_head"], cfg["d_rope"],
+                    cfg.get("window", 0) if window is None else window, eps, theta, scale,
+                    GDLA_F32 if dt == "f32" else GDLA_BF16)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def make_weights(weights, gamma_q=None, gamma_kv=None):
+    """gdla_weights from a dict of device tensors ([in, out] row-major, contiguous)."""
+    vals = dict(weights)
+    vals["gamma_q"], vals["gamma_kv"] = gamma_q, gamma_kv
+    for k, v in vals.items():
+        if v is not None and not v.is_contiguous():
+            raise ValueError(f"weight {k} must be contiguous")
+    return GdlaWeights(*[None if vals.get(n) is None else vals[n].data_ptr() for n in WEIGHT_FIELDS])
+
+
+def _pos_array(pos):
+    arr = (ctypes.c_int32 * len(pos))(*[int(p) for p in pos])
+    return arr
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status):
+    if status != GDLA_OK:
+        L = lib()
+        raise GdlaError(status, "%s: %s" % (L.gdla_status_string(status).decode(),
+                                            L.gdla_last_error().decode()))
+
+
+def gdla_workspace_bytes(dims, op, B, T, pos, max_len):
+    pa = None if pos is None else _pos_array(pos)
+    return int(lib().gdla_workspace_bytes(ctypes.byref(dims), op, B, T, pa, max_len))
+
+
+def _workspace(dims, op, B, T, pos, max_len, ws, device):
+    need = gdla_workspace_bytes(dims, op, B, T, pos, max_len)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return ws, ws.numel()
+
+
+def _debug(lambda_override, out_heads):
+    if lambda_override is None and out_heads is None:
+        return None
+    return GdlaDebug(None if lambda_override is None else lambda_override.data_ptr(),
+                     None if out_heads is None else out_heads.data_ptr())
+
+
+def gdla_latent_append(dims, weights, x, pos, cache, ws=None, stream=None):
+    """Writes cache rows [pos[b], pos[b] + T) from x [B, T, d_model]."""
+    B, T = x.shape[0], x.shape[1]
+    max_len = cache.shape[1]
+    ws, nbytes = _workspace(dims, GDLA_OP_APPEND, B, T, pos, max_len, ws, x.device)
+    _check(lib().gdla_latent_append(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B, T,
+                                    _pos_array(pos), _ptr(cache), max_len, _ptr(ws), nbytes,
+                                    _stream(stream)))
+
+
+def gdla_prefill(dims, weights, x, pos, cache, out=None, ws=None, lambda_override=None,
+                 out_heads=None, stream=None):
+    """x [B, T, d_model] at positions pos[b] + t; appends to cache; returns out [B, T, d_model]."""
+    B, T = x.shape[0], x.shape[1]
+    max_len = cache.shape[1]
+    if out is None:
+        out = torch.empty_like(x)
+    ws, nbytes = _workspace(dims, GDLA_OP_PREFILL, B, T, pos, max_len, ws, x.device)
+    dbg = _debug(lambda_override, out_heads)
+    _check(lib().gdla_prefill(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B, T,
+                              _pos_array(pos), _ptr(cache), max_len, _ptr(out), _ptr(ws), nbytes,
+                              None if dbg is None else ctypes.byref(dbg), _stream(stream)))
+    return out
+
+
+def gdla_decode(dims, weights, x, pos, cache, out=None, ws=None, lambda_override=None,
+                out_heads=None, stream=None):
+    """x [B, d_model], token b at position pos[b]; appends to cache; returns out [B, d_model]."""
+    B = x.shape[0]
+    max_len = cache.shape[1]
+    if out is None:
+        out = torch.empty_like(x)
+    ws, nbytes = _workspace(dims, GDLA_OP_DECODE, B, 1, pos, max_len, ws, x.device)
+    dbg = _debug(lambda_override, out_heads)
+    _check(lib().gdla_decode(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B,
+                             _pos_array(pos), _ptr(cache), max_len, _ptr(out), _ptr(ws), nbytes,
+                             None if dbg is None else ctypes.byref(dbg), _stream(stream)))
+    return out

@@ -1,0 +1,154 @@
+/*
+ * gdla.h -- C ABI of the GDLA (Grouped Differential Latent Attention) forward library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the GDLA token mixer of the Motif 3 Technical Report (picx.dev summary,
+ * section 2.2, Eq.(1)-(10); paperglide reader, section "Model Architecture", Figure 1 caption):
+ *
+ *   c^Q  = RMSNorm(x W_qa) * gamma_q                                   Eq.(1)
+ *   q^C  = c^Q W_qc,  q^R = RoPE(c^Q W_qr)            (per query head)  Eq.(2)
+ *   c^KV = x W_dkv,   k^R = RoPE(x W_kr)              (one k^R/token)   Eq.(3)
+ *   cbar = RMSNorm(c^KV) * gamma_kv                                     Eq.(4)
+ *   K^C  = cbar W_uk, V = cbar W_uv                   (per KV head)     Eq.(5)
+ *   n_N  = n_H / (g + 1), n_S = g n_N                                   Eq.(6)
+ *   lambda = sigmoid(x W_lambda)                      (one per signal head and token) Eq.(7)
+ *   H_h  = softmax_s(tau (q^C_h . K^C_s + q^R_h . k^R_s)) V_s          (per head)
+ *   D_i  = H_i - lambda_i H_{n_S + (i mod n_N)}                         Eq.(8)
+ *   G    = c^Q W_gate                                                   Eq.(9)
+ *   out  = vec(sigmoid(G) * D) W_o                                      Eq.(10)
+ *
+ * Readings where the pages are silent (shared with the oracle and the tests):
+ *   - heads 0..n_S-1 are signal heads, n_S..n_H-1 noise heads;
+ *   - Repeat_g tiles: signal head i subtracts noise head (i mod n_N);
+ *   - query head -> KV head: signal i -> i mod n_KV, noise j -> j mod n_KV (n_KV divides n_N);
+ *   - RoPE rotates the pair (j, j + d_rope/2) by p * rope_theta^(-2j/d_rope), p = absolute
+ *     0-based position of the token;
+ *   - tau = softmax_scale, or 1/sqrt(d_head + d_rope) when softmax_scale is 0;
+ *   - key s is visible from query p iff s <= p and (window == 0 or p - s < window).
+ *
+ * The latent KV cache holds, per sequence and position, one row [cbar (d_kv_latent) ; k^R
+ * (d_rope)] after RMSNorm/gamma and after RoPE: the MLA property that only the latent is stored
+ * and K/V are rebuilt inside attention (paperglide reader, "Model Architecture", MLA answer).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless their name ends in _host.
+ *   - Tensors are dense and row-major; every tensor of one call has the dtype dims->dtype.
+ *     Weights use the row-vector convention x W, so W is [in, out].
+ *   - Accumulation is fp32 in every dtype.
+ *   - The caller owns every buffer (inputs, weights, cache, out, workspace, debug outputs).
+ *     The library allocates no device memory, keeps no per-call state, never synchronises the
+ *     stream and launches only on `stream`.  Calls on different streams may run concurrently if
+ *     their workspaces, outputs and written cache rows do not overlap.
+ *   - All argument checks run before the first launch: on any error nothing is launched and no
+ *     buffer is written.  A HIP launch failure returns GDLA_ERR_HIP (work already queued on the
+ *     stream by the same call may then have run).  No C++ exception crosses this interface.
+ *   - gdla_last_error() returns a short description of the last failure on the calling thread.
+ */
+#ifndef GDLA_H_
+#define GDLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDLA_OK = 0,
+  GDLA_ERR_INVALID_ARG = 1,   /* null pointer, inconsistent sizes, bad alignment */
+  GDLA_ERR_UNSUPPORTED = 2,   /* valid layer, but a size or dtype this build does not serve */
+  GDLA_ERR_WORKSPACE = 3,     /* ws_bytes smaller than gdla_workspace_bytes(...) */
+  GDLA_ERR_OUT_OF_RANGE = 4,  /* a position + T exceeds max_len, or a negative position */
+  GDLA_ERR_HIP = 5            /* a HIP runtime call or kernel launch failed */
+} gdla_status;
+
+typedef enum { GDLA_F32 = 0, GDLA_BF16 = 1 } gdla_dtype;
+
+typedef enum { GDLA_OP_PREFILL = 0, GDLA_OP_DECODE = 1, GDLA_OP_APPEND = 2 } gdla_op;
+
+/* Layer sizes (picx.dev summary section 2.2).  n_heads = n_signal + n_noise, n_signal is a
+ * multiple g of n_noise (Eq.(6)), and n_kv_heads divides n_noise. */
+typedef struct {
+  int32_t d_model;       /* width of x and out */
+  int32_t n_heads;       /* n_H: all query heads */
+  int32_t n_signal;      /* n_S */
+  int32_t n_noise;       /* n_N */
+  int32_t n_kv_heads;    /* KV heads shared by the signal and noise paths */
+  int32_t d_q_latent;    /* width of c^Q */
+  int32_t d_kv_latent;   /* width of c^KV / cbar */
+  int32_t d_head;        /* q^C, K^C and V width per head */
+  int32_t d_rope;        /* q^R and k^R width (even) */
+  int32_t window;        /* 0: full causal; W > 0: key s visible iff 0 <= p - s < W */
+  float rms_eps;         /* RMSNorm epsilon (e.g. 1e-6) */
+  float rope_theta;      /* RoPE base (e.g. 10000) */
+  float softmax_scale;   /* 0 selects 1/sqrt(d_head + d_rope) */
+  gdla_dtype dtype;      /* GDLA_F32, or GDLA_BF16 (inputs, weights, cache and out in bf16) */
+} gdla_dims;
+
+/* Layer weights, all [in, out] row-major in dims->dtype.  gamma_q / gamma_kv may be NULL (all
+ * ones).  Head h of w_qc / w_qr / w_gate and KV head j of w_uk / w_uv are the column blocks h / j.
+ * w_o rows follow vec(Y): row i*d_head + e belongs to signal head i, element e. */
+typedef struct {
+  const void *w_qa;      /* [d_model, d_q_latent]              Eq.(1) */
+  const void *gamma_q;   /* [d_q_latent] or NULL                Eq.(1) */
+  const void *w_qc;      /* [d_q_latent, n_heads * d_head]      Eq.(2) */
+  const void *w_qr;      /* [d_q_latent, n_heads * d_rope]      Eq.(2) */
+  const void *w_dkv;     /* [d_model, d_kv_latent]              Eq.(3) */
+  const void *w_kr;      /* [d_model, d_rope]                   Eq.(3) */
+  const void *gamma_kv;  /* [d_kv_latent] or NULL               Eq.(4) */
+  const void *w_uk;      /* [d_kv_latent, n_kv_heads * d_head]  Eq.(5) */
+  const void *w_uv;      /* [d_kv_latent, n_kv_heads * d_head]  Eq.(5) */
+  const void *w_lambda;  /* [d_model, n_signal]                 Eq.(7) */
+  const void *w_gate;    /* [d_q_latent, n_signal * d_head]     Eq.(9) */
+  const void *w_o;       /* [n_signal * d_head, d_model]        Eq.(10) */
+} gdla_weights;
+
+/* Optional test hooks; pass NULL (or a struct of NULLs) in production. */
+typedef struct {
+  const float *lambda_override;  /* [B, T, n_signal] fp32: used instead of sigmoid(x W_lambda) */
+  float *out_heads;              /* [B, T, n_heads, d_head] fp32: per-head H before Eq.(8) */
+} gdla_debug;
+
+/* Bytes of workspace that op needs for B sequences of T new tokens each (T = 1 for decode).
+ * pos_host (host, [B], may be NULL) gives the first new position of each sequence; with NULL the
+ * size is an upper bound for any positions with pos + T <= max_len.  Returns 0 for invalid
+ * dims or sizes.  The workspace must be 256-byte aligned. */
+size_t gdla_workspace_bytes(const gdla_dims *dims, int32_t op, int32_t B, int32_t T,
+                            const int32_t *pos_host, int32_t max_len);
+
+/* Eq.(3)-(4) plus RoPE: writes cache rows [pos_host[b], pos_host[b] + T) of every sequence b from
+ * x [B, T, d_model].  cache is [B, max_len, d_kv_latent + d_rope]; other rows are untouched. */
+gdla_status gdla_latent_append(const gdla_dims *dims, const gdla_weights *w, const void *x,
+                               int32_t B, int32_t T, const int32_t *pos_host, void *cache,
+                               int32_t max_len, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Prefill / chunked prefill, Eq.(1)-(10): the T tokens of sequence b sit at positions
+ * pos_host[b] .. pos_host[b] + T - 1.  Their latent rows are appended to the cache, then every
+ * token attends over cache rows [0, its position] (window permitting), expanded K/V form.
+ * x [B, T, d_model] -> out [B, T, d_model].  out must not alias x, the cache or the workspace. */
+gdla_status gdla_prefill(const gdla_dims *dims, const gdla_weights *w, const void *x, int32_t B,
+                         int32_t T, const int32_t *pos_host, void *cache, int32_t max_len,
+                         void *out, void *ws, size_t ws_bytes, const gdla_debug *dbg,
+                         hipStream_t stream);
+
+/* One decode step per sequence: token b (x [B, d_model]) sits at position pos_host[b] (= number
+ * of rows already cached).  Its latent row is appended, then it attends over cache rows
+ * [0, pos_host[b]] in the absorbed form (queries mapped into the latent space, values mapped out
+ * after the softmax average).  out [B, d_model]. */
+gdla_status gdla_decode(const gdla_dims *dims, const gdla_weights *w, const void *x, int32_t B,
+                        const int32_t *pos_host, void *cache, int32_t max_len, void *out,
+                        void *ws, size_t ws_bytes, const gdla_debug *dbg, hipStream_t stream);
+
+/* Static description of a status code. */
+const char *gdla_status_string(gdla_status s);
+
+/* Description of the last failure on the calling thread ("" if none). */
+const char *gdla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDLA_H_ */

@@ -1,0 +1,135 @@
+"""Shared helpers of the GPU tests, the smoke check and the benchmark: run the GDLA library and the
+fp64 oracle on the same seeded inputs and measure the difference."""
+
+import numpy as np
+import torch
+
+import oracle.gdla_ref as ref
+import synth
+import attention_gdla_prefill_decode_amd as gd
+
+# Tolerances on `out` (max-abs and relative L2 over the whole output).
+TOL = {"f32": (1e-5, 1e-5), "bf16": (2e-2, 5e-3)}
+
+# A small layer with the big head sizes (d_head 128, d_rope 64, d_kv_latent 512): 8 signal heads,
+# 2 noise heads, 2 KV heads, so g = 4 as in the 80-head layer.
+SMALL_BF16 = dict(d_model=256, n_heads=10, n_signal=8, n_noise=2, n_kv=2, d_q_latent=128,
+                  d_kv_latent=512, d_head=128, d_rope=64, batch=1, seq=64, p0=0, max_len=64,
+                  window=0, dtype="bf16", seed=7)
+
+
+def to_np(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def oracle_weights(inp):
+    w = {k: to_np(v) for k, v in inp["weights"].items()}
+    w["gamma_q"] = None if inp["gamma_q"] is None else to_np(inp["gamma_q"])
+    w["gamma_kv"] = None if inp["gamma_kv"] is None else to_np(inp["gamma_kv"])
+    return w
+
+
+def oracle_dims(cfg, window):
+    return ref.Dims(cfg["n_heads"], cfg["n_signal"], cfg["n_noise"], cfg["n_kv"], cfg["d_head"],
+                    cfg["d_rope"], window)
+
+
+def errors(got, exp):
+    got = np.asarray(got, dtype=np.float64)
+    exp = np.asarray(exp, dtype=np.float64)
+    diff = got - exp
+    max_abs = float(np.max(np.abs(diff))) if diff.size else 0.0
+    den = float(np.linalg.norm(exp))
+    rel = float(np.linalg.norm(diff)) / den if den > 0 else float(np.linalg.norm(diff))
+    rms = float(np.sqrt(np.mean(exp * exp))) if exp.size else 0.0
+    return max_abs, rel, rms
+
+
+def check(got, exp, dtype, what):
+    max_abs, rel, rms = errors(got, exp)
+    tol_abs, tol_rel = TOL[dtype]
+    msg = f"{what}: max-abs {max_abs:.3e} (tol {tol_abs:g}), rel-L2 {rel:.3e} (tol {tol_rel:g}), ref RMS {rms:.3e}"
+    assert max_abs <= tol_abs and rel <= tol_rel, msg
+    return msg
+
+
+def device_inputs(inp, device="cuda"):
+    d = {"x": inp["x"].to(device), "cache": inp["cache"].to(device),
+         "weights": {k: v.to(device).contiguous() for k, v in inp["weights"].items()},
+         "gamma_q": None if inp["gamma_q"] is None else inp["gamma_q"].to(device),
+         "gamma_kv": None if inp["gamma_kv"] is None else inp["gamma_kv"].to(device)}
+    d["wstruct"] = gd.make_weights(d["weights"], d["gamma_q"], d["gamma_kv"])
+    return d
+
+
+def prefill_case(cfg, seq, p0, window=0, seed=None, random_gamma=True, lam_zero=False,
+                 want_heads=False):
+    """Runs gdla_prefill on GPU and the oracle on CPU for every sequence; returns both outputs."""
+    batch = len(p0)
+    inp = synth.make_inputs(cfg, "cpu", seed=seed, batch=batch, seq=seq, p0=p0,
+                            random_gamma=random_gamma)
+    dev = device_inputs(inp)
+    dims = gd.make_dims(cfg, window=window)
+    lam = None
+    if lam_zero:
+        lam = torch.zeros((batch, seq, cfg["n_signal"]), dtype=torch.float32, device="cuda")
+    heads = None
+    if want_heads:
+        heads = torch.empty((batch, seq, cfg["n_heads"], cfg["d_head"]), dtype=torch.float32,
+                            device="cuda")
+    out = gd.gdla_prefill(dims, dev["wstruct"], dev["x"], inp["p0"], dev["cache"],
+                          lambda_override=lam, out_heads=heads)
+    torch.cuda.synchronize()
+    w = oracle_weights(inp)
+    od = oracle_dims(cfg, window)
+    exp_out, exp_rows, exp_heads = [], [], []
+    for b in range(batch):
+        pre = to_np(inp["cache"][b, :inp["p0"][b]]) if inp["p0"][b] > 0 else None
+        r = ref.gdla_forward(to_np(inp["x"][b]), w, od, pre, inp["p0"][b],
+                             None if lam is None else np.zeros((seq, cfg["n_signal"])))
+        exp_out.append(r["out"])
+        exp_rows.append(r["cache_rows"])
+        exp_heads.append(r["heads"])
+    got_rows = [to_np(dev["cache"][b, inp["p0"][b]:inp["p0"][b] + seq]) for b in range(batch)]
+    return {"out": to_np(out), "exp_out": np.stack(exp_out), "rows": got_rows,
+            "exp_rows": exp_rows, "heads": None if heads is None else to_np(heads),
+            "exp_heads": np.stack(exp_heads), "inp": inp, "dev": dev, "dims": dims}
+
+
+def decode_case(cfg, p0, seed=None, random_gamma=True, want_heads=False):
+    """One decode step per sequence (token b at position p0[b]) on GPU and in the oracle."""
+    batch = len(p0)
+    inp = synth.make_inputs(cfg, "cpu", seed=seed, batch=batch, seq=1, p0=p0,
+                            random_gamma=random_gamma)
+    dev = device_inputs(inp)
+    dims = gd.make_dims(cfg, window=cfg.get("window", 0))
+    heads = None
+    if want_heads:
+        heads = torch.empty((batch, cfg["n_heads"], cfg["d_head"]), dtype=torch.float32,
+                            device="cuda")
+    out = gd.gdla_decode(dims, dev["wstruct"], dev["x"][:, 0].contiguous(), inp["p0"],
+                         dev["cache"], out_heads=heads)
+    torch.cuda.synchronize()
+    w = oracle_weights(inp)
+    od = oracle_dims(cfg, cfg.get("window", 0))
+    prefixes = [to_np(inp["cache"][b, :inp["p0"][b]]) if inp["p0"][b] > 0 else None
+                for b in range(batch)]
+    r = ref.gdla_decode(to_np(inp["x"][:, 0]), w, od, prefixes, inp["p0"])
+    return {"out": to_np(out), "exp_out": r["out"], "heads": None if heads is None else to_np(heads),
+            "exp_heads": r["heads"],
+            "rows": np.stack([to_np(dev["cache"][b, inp["p0"][b]]) for b in range(batch)]),
+            "exp_rows": r["cache_rows"]}
+
+
+def check_rows(got, exp, dtype, what):
+    """Cache rows: fp32 to 1e-5; bf16 rows are rounded once (a near-tie may round the other way
+    after fp32 arithmetic), so within one bf16 ulp, 2^-7 relative, plus 1e-5."""
+    got = np.asarray(got, dtype=np.float64)
+    exp = np.asarray(exp, dtype=np.float64)
+    if dtype == "f32":
+        err = float(np.max(np.abs(got - exp)))
+        assert err <= 1e-5, f"{what}: cache rows max-abs {err:.3e}"
+    else:
+        bound = np.abs(exp) * 2.0 ** -7 + 1e-5
+        bad = np.abs(got - exp) > bound
+        assert not bad.any(), f"{what}: {int(bad.sum())} cache entries beyond one bf16 rounding"

@@ -1,0 +1,170 @@
+"""CPU tests of the C-ABI boundary: the library loads, exports every function include/gdla.h
+declares, and every argument error is reported before any GPU work (these calls never reach a
+launch, so they run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_gdla_prefill_decode_amd as gd
+from attention_gdla_prefill_decode_amd import gdla as gb
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdla.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdla_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = gd.lib()
+    names = declared_functions()
+    assert set(names) == set(gd.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_status_strings():
+    lib = gd.lib()
+    for code, name in enumerate(["GDLA_OK", "GDLA_ERR_INVALID_ARG", "GDLA_ERR_UNSUPPORTED",
+                                 "GDLA_ERR_WORKSPACE", "GDLA_ERR_OUT_OF_RANGE", "GDLA_ERR_HIP"]):
+        assert lib.gdla_status_string(code).decode() == name
+    assert lib.gdla_status_string(99).decode() == "unknown gdla_status"
+
+
+def big_dims(**kw):
+    cfg = dict(synth.WORKLOADS["prefill_8k"])
+    cfg.update(kw)
+    return gd.make_dims(cfg)
+
+
+def test_workspace_bytes():
+    d = big_dims()
+    pre = gd.gdla_workspace_bytes(d, gd.GDLA_OP_PREFILL, 1, 8192, [0], 8192)
+    assert pre > 0 and pre % 256 == 0
+    # the expanded K/V of 8192 keys x 16 heads x 128 x 2 (K, V) in bf16 alone is 64 MiB
+    assert pre >= 8192 * 16 * 128 * 2 * 2
+    assert gd.gdla_workspace_bytes(d, gd.GDLA_OP_PREFILL, 1, 8192, None, 8192) == pre
+    dec = gd.gdla_workspace_bytes(d, gd.GDLA_OP_DECODE, 64, 1, [65535] * 64, 65536)
+    assert dec > 0
+    app = gd.gdla_workspace_bytes(d, gd.GDLA_OP_APPEND, 2, 10, [0, 5], 64)
+    assert 0 < app < pre
+    # windowed prefill needs keys from p0 - W + 1 only
+    dw = big_dims(window=4096)
+    assert gd.gdla_workspace_bytes(dw, gd.GDLA_OP_PREFILL, 1, 4096, [100000], 262144) < \
+        gd.gdla_workspace_bytes(d, gd.GDLA_OP_PREFILL, 1, 4096, [100000], 262144)
+    # invalid requests report 0
+    assert gd.gdla_workspace_bytes(d, gd.GDLA_OP_PREFILL, 1, 10, [8190], 8192) == 0
+    assert gd.gdla_workspace_bytes(d, gd.GDLA_OP_DECODE, 4, 2, None, 64) == 0
+    assert gd.gdla_workspace_bytes(d, 7, 1, 1, None, 64) == 0
+    assert gd.gdla_workspace_bytes(big_dims(n_noise=15), gd.GDLA_OP_PREFILL, 1, 1, None, 8) == 0
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def call_prefill(dims, weights=None, x=FAKE, B=1, T=4, pos=(0,), cache=FAKE, max_len=64, out=FAKE,
+                 ws=FAKE, ws_bytes=1 << 40):
+    lib = gd.lib()
+    w = weights if weights is not None else gb.GdlaWeights(*([FAKE] * 12))
+    pa = (ctypes.c_int32 * len(pos))(*pos) if pos is not None else None
+    st = lib.gdla_prefill(ctypes.byref(dims), ctypes.byref(w), x, B, T, pa, cache, max_len, out,
+                          ws, ws_bytes, None, None)
+    return st, lib.gdla_last_error().decode()
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("bad_split", gb.GDLA_ERR_INVALID_ARG),
+    ("noise_not_divisor", gb.GDLA_ERR_INVALID_ARG),
+    ("kv_not_divisor", gb.GDLA_ERR_INVALID_ARG),
+    ("odd_rope", gb.GDLA_ERR_INVALID_ARG),
+    ("negative_window", gb.GDLA_ERR_INVALID_ARG),
+    ("bad_dtype", gb.GDLA_ERR_INVALID_ARG),
+    ("huge_head", gb.GDLA_ERR_UNSUPPORTED),
+    ("null_x", gb.GDLA_ERR_INVALID_ARG),
+    ("null_out", gb.GDLA_ERR_INVALID_ARG),
+    ("null_weight", gb.GDLA_ERR_INVALID_ARG),
+    ("null_pos", gb.GDLA_ERR_INVALID_ARG),
+    ("misaligned_x", gb.GDLA_ERR_INVALID_ARG),
+    ("pos_past_end", gb.GDLA_ERR_OUT_OF_RANGE),
+    ("negative_pos", gb.GDLA_ERR_OUT_OF_RANGE),
+    ("small_workspace", gb.GDLA_ERR_WORKSPACE),
+    ("misaligned_workspace", gb.GDLA_ERR_INVALID_ARG),
+])
+def test_prefill_argument_errors(case, expect):
+    kw = {}
+    dims = big_dims()
+    if case == "bad_split":
+        dims = big_dims(n_signal=60)
+    elif case == "noise_not_divisor":
+        dims = big_dims(n_signal=62, n_noise=18)
+    elif case == "kv_not_divisor":
+        dims = big_dims(n_kv=5)
+    elif case == "odd_rope":
+        dims = big_dims(d_rope=63)
+    elif case == "negative_window":
+        dims = big_dims(window=-1)
+    elif case == "bad_dtype":
+        dims.dtype = 9
+    elif case == "huge_head":
+        dims = big_dims(d_head=512)
+    elif case == "null_x":
+        kw["x"] = None
+    elif case == "null_out":
+        kw["out"] = None
+    elif case == "null_weight":
+        w = gb.GdlaWeights(*([FAKE] * 12))
+        w.w_uv = None
+        kw["weights"] = w
+    elif case == "null_pos":
+        kw["pos"] = None
+    elif case == "misaligned_x":
+        kw["x"] = FAKE + 2
+    elif case == "pos_past_end":
+        kw["pos"] = (61,)
+    elif case == "negative_pos":
+        kw["pos"] = (-1,)
+    elif case == "small_workspace":
+        kw["ws_bytes"] = 1024
+    elif case == "misaligned_workspace":
+        kw["ws"] = FAKE + 16
+    st, msg = call_prefill(dims, **kw)
+    assert st == expect, (st, msg)
+    assert msg, "a failure must leave a description in gdla_last_error()"
+
+
+def test_empty_inputs_are_noops():
+    # B = 0 or T = 0: nothing to do, nothing launched, GDLA_OK, no pointers needed
+    st, _ = call_prefill(big_dims(), x=None, B=0, pos=None, cache=None, out=None, ws=None)
+    assert st == gb.GDLA_OK
+    st, _ = call_prefill(big_dims(), x=None, T=0, cache=None, out=None, ws=None)
+    assert st == gb.GDLA_OK
+
+
+def test_decode_and_append_argument_errors():
+    lib = gd.lib()
+    d = big_dims()
+    w = gb.GdlaWeights(*([FAKE] * 12))
+    pos = (ctypes.c_int32 * 2)(5, 64)
+    st = lib.gdla_decode(ctypes.byref(d), ctypes.byref(w), FAKE, 2, pos, FAKE, 64, FAKE, FAKE,
+                         1 << 40, None, None)
+    assert st == gb.GDLA_ERR_OUT_OF_RANGE
+    pos = (ctypes.c_int32 * 2)(5, 6)
+    st = lib.gdla_decode(ctypes.byref(d), ctypes.byref(w), FAKE, 2, pos, FAKE, 64, FAKE, FAKE, 16,
+                         None, None)
+    assert st == gb.GDLA_ERR_WORKSPACE
+    w.w_kr = None
+    st = lib.gdla_latent_append(ctypes.byref(d), ctypes.byref(w), FAKE, 2, 3, pos, FAKE, 64, FAKE,
+                                1 << 40, None)
+    assert st == gb.GDLA_ERR_INVALID_ARG
+    w.w_kr = FAKE
+    w.w_qa = None  # the query weights are not needed to append latents
+    st = lib.gdla_latent_append(ctypes.byref(d), ctypes.byref(w), FAKE, 2, 3, pos, FAKE, 64, FAKE,
+                                16, None)
+    assert st == gb.GDLA_ERR_WORKSPACE

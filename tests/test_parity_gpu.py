@@ -1,0 +1,164 @@
+"""GPU parity of the GDLA library against the fp64 oracle, element by element, at sizes the
+oracle finishes in seconds (several tiles and a ragged tail), plus GPU-side invariants."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import oracle
+import attention_gdla_prefill_decode_amd as gd
+from tests import harness as H
+
+pytestmark = pytest.mark.gpu
+
+TINY = synth.WORKLOADS["tiny_fp32"]
+BF = H.SMALL_BF16
+
+
+def setup_module(module):
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+# ---------------------------------------------------------------- fp32 (tolerance 1e-5)
+def test_tiny_fp32_prefill_full():
+    r = H.prefill_case(TINY, 128, [0], random_gamma=False)
+    _say(H.check(r["out"], r["exp_out"], "f32", "tiny fp32 T=128"))
+    H.check_rows(r["rows"][0], r["exp_rows"][0], "f32", "tiny fp32 cache rows")
+
+
+@pytest.mark.parametrize("seq,p0,window", [
+    (37, [0, 11], 0), (50, [20], 16), (7, [0], 1), (64, [3, 0, 60], 5), (1, [0], 0), (1, [90], 0),
+    (100, [0], 200),
+])
+def test_fp32_prefill_variants(seq, p0, window):
+    r = H.prefill_case(TINY, seq, p0, window=window, seed=13)
+    _say(H.check(r["out"], r["exp_out"], "f32", f"fp32 T={seq} p0={p0} W={window}"))
+    for b in range(len(p0)):
+        H.check_rows(r["rows"][b], r["exp_rows"][b], "f32", "fp32 cache rows")
+
+
+def test_fp32_heads_debug_output():
+    r = H.prefill_case(TINY, 40, [9], window=12, want_heads=True)
+    err = np.max(np.abs(r["heads"] - r["exp_heads"]))
+    assert err <= 1e-5, err
+
+
+def test_fp32_decode():
+    r = H.decode_case(TINY, [0, 5, 127, 64], want_heads=True)
+    _say(H.check(r["out"], r["exp_out"], "f32", "fp32 decode"))
+    assert np.max(np.abs(r["heads"] - r["exp_heads"])) <= 1e-5
+    H.check_rows(r["rows"], r["exp_rows"], "f32", "fp32 decode cache rows")
+
+
+# ---------------------------------------------------------------- bf16 (2e-2 / 5e-3)
+@pytest.mark.parametrize("seq,p0,window", [
+    (300, [0], 0), (200, [0, 77], 0), (257, [5], 64), (129, [0], 1), (64, [40], 100000),
+])
+def test_bf16_prefill(seq, p0, window):
+    r = H.prefill_case(BF, seq, p0, window=window, seed=17)
+    _say(H.check(r["out"], r["exp_out"], "bf16", f"bf16 T={seq} p0={p0} W={window}"))
+    for b in range(len(p0)):
+        H.check_rows(r["rows"][b], r["exp_rows"][b], "bf16", "bf16 cache rows")
+
+
+def test_bf16_heads_debug_output():
+    r = H.prefill_case(BF, 160, [0], want_heads=True)
+    _say(H.check(r["heads"], r["exp_heads"], "bf16", "bf16 per-head H"))
+
+
+@pytest.mark.parametrize("p0", [[0, 1, 300, 1000], [4095]])
+def test_bf16_decode(p0):
+    r = H.decode_case(BF, p0, want_heads=True)
+    _say(H.check(r["out"], r["exp_out"], "bf16", f"bf16 decode p0={p0}"))
+    _say(H.check(r["heads"], r["exp_heads"], "bf16", "bf16 decode per-head H"))
+    H.check_rows(r["rows"], r["exp_rows"], "bf16", "bf16 decode cache rows")
+
+
+def test_bf16_lambda_zero_is_gated_mla():
+    r = H.prefill_case(BF, 96, [0, 20], window=32, lam_zero=True)
+    inp = r["inp"]
+    w = H.oracle_weights(inp)
+    for b, p in enumerate(inp["p0"]):
+        pre = H.to_np(inp["cache"][b, :p]) if p > 0 else None
+        exp = oracle.mla_forward(H.to_np(inp["x"][b]), w, BF["n_signal"], BF["n_kv"], BF["n_noise"],
+                                 BF["d_head"], BF["d_rope"], 32, prefix=pre, p0=p)
+        _say(H.check(r["out"][b], exp, "bf16", f"lambda=0 vs gated MLA, seq {b}"))
+
+
+def test_latent_append():
+    for cfg, dt in ((TINY, "f32"), (BF, "bf16")):
+        inp = synth.make_inputs(cfg, "cpu", batch=2, seq=33, p0=[0, 50], random_gamma=True)
+        dev = H.device_inputs(inp)
+        dims = gd.make_dims(cfg)
+        gd.gdla_latent_append(dims, dev["wstruct"], dev["x"], inp["p0"], dev["cache"])
+        torch.cuda.synchronize()
+        w = H.oracle_weights(inp)
+        od = H.oracle_dims(cfg, 0)
+        for b, p in enumerate(inp["p0"]):
+            c_bar, k_r = oracle.latent_path(H.to_np(inp["x"][b]), w, od, p + np.arange(33))
+            exp = np.concatenate([c_bar, k_r], axis=1)
+            H.check_rows(H.to_np(dev["cache"][b, p:p + 33]), exp, dt, f"append {dt} seq {b}")
+            # rows outside [p, p + 33) are untouched
+            assert torch.equal(dev["cache"][b, :p].cpu(), inp["cache"][b, :p])
+            assert torch.equal(dev["cache"][b, p + 33:].cpu(), inp["cache"][b, p + 33:])
+
+
+# ---------------------------------------------------------------- GPU-side invariants
+def test_chunked_and_decode_match_one_call():
+    cfg = BF
+    inp = synth.make_inputs(cfg, "cpu", batch=1, seq=130, p0=0, random_gamma=True)
+    dev = H.device_inputs(inp)
+    dims = gd.make_dims(cfg, window=48)
+    base = dev["cache"].clone()
+    mono = gd.gdla_prefill(dims, dev["wstruct"], dev["x"], [0], base)
+    c2 = dev["cache"].clone()
+    a = gd.gdla_prefill(dims, dev["wstruct"], dev["x"][:, :70].contiguous(), [0], c2)
+    b = gd.gdla_prefill(dims, dev["wstruct"], dev["x"][:, 70:129].contiguous(), [70], c2)
+    dec = gd.gdla_decode(dims, dev["wstruct"], dev["x"][:, 129].contiguous(), [129], c2)
+    torch.cuda.synchronize()
+    got = torch.cat([a, b, dec[:, None]], dim=1)
+    _say(H.check(H.to_np(got), H.to_np(mono), "bf16", "chunks + decode vs one call"))
+    assert torch.equal(base[:, :130], c2[:, :130]), "cache rows must not depend on chunking"
+
+
+def test_window_at_least_length_equals_full():
+    inp = synth.make_inputs(BF, "cpu", batch=1, seq=150, p0=0)
+    dev = H.device_inputs(inp)
+    outs = []
+    for window in (0, 150, 1 << 20):
+        cache = dev["cache"].clone()
+        outs.append(gd.gdla_prefill(gd.make_dims(BF, window=window), dev["wstruct"], dev["x"], [0],
+                                    cache))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+def test_repeat_runs_are_bitwise_identical():
+    for cfg, seq in ((TINY, 70), (BF, 140)):
+        inp = synth.make_inputs(cfg, "cpu", batch=2, seq=seq, p0=[0, 9])
+        dev = H.device_inputs(inp)
+        dims = gd.make_dims(cfg, window=0)
+        o1 = gd.gdla_prefill(dims, dev["wstruct"], dev["x"], inp["p0"], dev["cache"].clone())
+        o2 = gd.gdla_prefill(dims, dev["wstruct"], dev["x"], inp["p0"], dev["cache"].clone())
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2)
+
+
+def test_workspace_reuse_and_explicit_stream():
+    inp = synth.make_inputs(BF, "cpu", batch=1, seq=64, p0=0)
+    dev = H.device_inputs(inp)
+    dims = gd.make_dims(BF)
+    need = gd.gdla_workspace_bytes(dims, gd.GDLA_OP_PREFILL, 1, 64, [0], 64)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")  # garbage-filled workspace
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o1 = gd.gdla_prefill(dims, dev["wstruct"], dev["x"], [0], dev["cache"].clone(), ws=ws, stream=s)
+    s.synchronize()
+    o2 = gd.gdla_prefill(dims, dev["wstruct"], dev["x"], [0], dev["cache"].clone())
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
