@@ -5,13 +5,14 @@
 
 namespace gdla {
 
-// ---- bf16 MFMA GEMM ----
-bool fast_gemm_supported(const GemmBatch &g);
-hipError_t launch_gemm_bf16_mfma(GemmBatch &g, hipStream_t s);
+// ---- MFMA GEMM: bf16 x bf16, or fp16 A x (bf16 B converted to fp16); all problems of one
+// launch share a_f16 ----
+bool fast_gemm_problem_ok(const GemmProblem &p);
+hipError_t launch_gemm_mfma(GemmBatch &g, hipStream_t s);
 
 // ---- fused prefill attention ----
 struct FastPrefillLayout {
-  size_t q;      // [M, n_H, d_h + d_r] bf16: q^C and rotated q^R of every head, one row per head
+  size_t q;      // [M, n_H, d_h + d_r] fp16: q^C and rotated q^R of every head, one row per head
   size_t qrp;    // [M, n_H, d_r] fp32: q^R before RoPE
   size_t hn;     // [M, n_N, d_h] fp32: normalised noise-head outputs
 };
@@ -31,7 +32,7 @@ gdla_status run_fast_prefill(const LayerDims &d, const gdla_weights *w, int32_t 
                              const int32_t *pos_dev, const int32_t *pos_host, void *cache,
                              int32_t max_len, void *cq, float *lam, float *gate, void *kx,
                              void *vx, int32_t lcap, void *y, float *out_heads,
-                             const FastPrefillLayout &L, void *ws, hipStream_t s);
+                             const FastPrefillLayout &L, void *ws, hipStream_t s, StageEvents &se);
 
 // ---- absorbed split-L decode ----
 struct FastDecodeLayout {
@@ -59,6 +60,6 @@ bool fast_decode_supported(const LayerDims &d, gdla_dtype dt);
 gdla_status run_fast_decode(const LayerDims &d, const gdla_weights *w, int32_t B,
                             const int32_t *pos_dev, const int32_t *pos_host, void *cache,
                             int32_t max_len, const float *qc, const float *qr, float *heads,
-                            const FastDecodeLayout &L, void *ws, hipStream_t s);
+                            const FastDecodeLayout &L, void *ws, hipStream_t s, StageEvents &se);
 
 }  // namespace gdla

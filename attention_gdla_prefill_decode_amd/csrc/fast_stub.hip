@@ -2,19 +2,11 @@
 #include "fast_paths.h"
 
 namespace gdla {
-bool fast_gemm_supported(const GemmBatch &) { return false; }
-hipError_t launch_gemm_bf16_mfma(GemmBatch &, hipStream_t) { return hipErrorNotSupported; }
-bool fast_prefill_supported(const LayerDims &, gdla_dtype) { return false; }
-gdla_status run_fast_prefill(const LayerDims &, const gdla_weights *, int32_t, int32_t, const int32_t *,
-                             const int32_t *, void *, int32_t, void *, float *, float *, void *, void *,
-                             int32_t, void *, float *, const FastPrefillLayout &, void *, hipStream_t) {
-  return GDLA_ERR_UNSUPPORTED;
-}
 int32_t fast_decode_splits(int32_t, int32_t) { return 1; }
 bool fast_decode_supported(const LayerDims &, gdla_dtype) { return false; }
 gdla_status run_fast_decode(const LayerDims &, const gdla_weights *, int32_t, const int32_t *, const int32_t *,
                             void *, int32_t, const float *, const float *, float *, const FastDecodeLayout &,
-                            void *, hipStream_t) {
+                            void *, hipStream_t, StageEvents &) {
   return GDLA_ERR_UNSUPPORTED;
 }
 }  // namespace gdla

@@ -219,7 +219,7 @@ GemmProblem gp(const void *A, int64_t lda, const void *B, int64_t ldb, void *C, 
   GemmProblem p{};
   p.A = A; p.lda = lda; p.B = B; p.ldb = ldb; p.C = C; p.ldc = ldc;
   p.M = M; p.N = N; p.K = K; p.hw = N > 0 ? N : 1; p.hs = 0; p.ho = 0;
-  p.c_f32 = c_f32 ? 1 : 0; p.epi = epi;
+  p.c_dt = c_f32 ? CD_F32 : CD_IN; p.a_f16 = 0; p.epi = epi;
   return p;
 }
 
@@ -228,28 +228,47 @@ GemmProblem gp(const void *A, int64_t lda, const void *B, int64_t ldb, void *C, 
 gdla_status project_and_append(const LayerDims &d, DT dt, const gdla_weights *w, const void *x,
                                int32_t M, int32_t T, const int32_t *pos_dev, void *cache,
                                int32_t max_len, float *aq, float *ckv, float *krp, float *laml,
-                               void *cq, float *lam, const float *lam_override, hipStream_t s) {
+                               void *cq, float *lam, const float *lam_override, hipStream_t s,
+                               StageEvents &se, bool cq_f16 = false) {
   GemmBatch g{};
   g.p[g.n++] = gp(x, d.d_model, w->w_dkv, d.d_c, ckv, d.d_c, M, d.d_c, d.d_model, true);
   g.p[g.n++] = gp(x, d.d_model, w->w_kr, d.d_r, krp, d.d_r, M, d.d_r, d.d_model, true);
   if (cq) g.p[g.n++] = gp(x, d.d_model, w->w_qa, d.d_cq, aq, d.d_cq, M, d.d_cq, d.d_model, true);
   if (lam && !lam_override)
     g.p[g.n++] = gp(x, d.d_model, w->w_lambda, d.n_signal, laml, d.n_signal, M, d.n_signal, d.d_model, true);
+  se.begin(GDLA_STAGE_PROJ_IN);
   HIP_TRY(launch_gemm(g, dt, s));
+  se.end(GDLA_STAGE_PROJ_IN);
   PrepArgs a{};
   a.aq = aq; a.ckv = ckv; a.kr = krp; a.lam_logit = laml; a.lam_override = lam_override;
   a.gamma_q = w->gamma_q; a.gamma_kv = w->gamma_kv; a.cq = cq; a.lam = lam; a.cache = cache;
-  a.pos = pos_dev; a.M = M; a.T = T; a.max_len = max_len;
+  a.pos = pos_dev; a.M = M; a.T = T; a.max_len = max_len; a.cq_f16 = cq_f16 ? 1 : 0;
+  se.begin(GDLA_STAGE_NORM_APPEND);
   HIP_TRY(launch_prep(a, d, dt, s));
+  se.end(GDLA_STAGE_NORM_APPEND);
   return GDLA_OK;
 }
 
 }  // namespace
 
-// GEMM dispatch shared by all entry points: MFMA kernels for bf16 when every problem fits them.
+// GEMM dispatch shared by all entry points: bf16 problems that fit the MFMA kernel (K a multiple
+// of 64, N and the row strides multiples of 8, 16-byte aligned operands) run there, the rest on
+// the generic kernel.
 hipError_t launch_gemm(GemmBatch &g, DT dt, hipStream_t s) {
-  if (dt == DT::BF16 && fast_gemm_supported(g)) return launch_gemm_bf16_mfma(g, s);
-  return launch_gemm_generic(g, dt, s);
+  if (dt != DT::BF16) return launch_gemm_generic(g, dt, s);
+  GemmBatch fast[2] = {}, slow{};
+  for (int i = 0; i < g.n; ++i) {
+    const GemmProblem &p = g.p[i];
+    if (fast_gemm_problem_ok(p)) fast[p.a_f16 ? 1 : 0].p[fast[p.a_f16 ? 1 : 0].n++] = p;
+    else if (p.a_f16 || p.c_dt > CD_IN) return hipErrorInvalidValue;  // only the MFMA kernel serves these
+    else slow.p[slow.n++] = p;
+  }
+  for (int k = 0; k < 2; ++k)
+    if (fast[k].n) {
+      const hipError_t e = launch_gemm_mfma(fast[k], s);
+      if (e != hipSuccess) return e;
+    }
+  return slow.n ? launch_gemm_generic(slow, dt, s) : hipSuccess;
 }
 
 }  // namespace gdla
@@ -302,9 +321,10 @@ GDLA_EXPORT gdla_status gdla_latent_append(const gdla_dims *dims, const gdla_wei
   const DT dt = dims->dtype == GDLA_F32 ? DT::F32 : DT::BF16;
   int32_t *pos_dev = at<int32_t>(ws, L.pos);
   HIP_TRY(launch_set_i32(pos_dev, pos_host, B, stream));
+  StageEvents se;
   return project_and_append(d, dt, w, x, B * T, T, pos_dev, cache, max_len, nullptr,
                             at<float>(ws, L.ckv), at<float>(ws, L.krp), nullptr, nullptr, nullptr,
-                            nullptr, stream);
+                            nullptr, stream, se);
 }
 
 GDLA_EXPORT gdla_status gdla_prefill(const gdla_dims *dims, const gdla_weights *w, const void *x,
@@ -322,18 +342,24 @@ GDLA_EXPORT gdla_status gdla_prefill(const gdla_dims *dims, const gdla_weights *
   const int32_t M = B * T;
   const float *lam_override = dbg ? dbg->lambda_override : nullptr;
   float *out_heads = dbg ? dbg->out_heads : nullptr;
+  StageEvents se;
+  se.ev = dbg ? dbg->stage_events : nullptr;
+  se.s = stream;
 
   int32_t *pos_dev = at<int32_t>(ws, L.pos);
   HIP_TRY(launch_set_i32(pos_dev, pos_host, B, stream));
   // Eq.(1), (3), (4), (7) and the cache append of this chunk's rows.
   st = project_and_append(d, dt, w, x, M, T, pos_dev, cache, max_len, at<float>(ws, L.aq),
                           at<float>(ws, L.ckv), at<float>(ws, L.krp), at<float>(ws, L.laml),
-                          at<void>(ws, L.cq), at<float>(ws, L.lam), lam_override, stream);
+                          at<void>(ws, L.cq), at<float>(ws, L.lam), lam_override, stream, se,
+                          L.use_fast);
   if (st != GDLA_OK) return st;
 
-  // Eq.(5): expand K^C and V of every visible key, head-major [B, n_kv, lcap, d_h].
+  // Eq.(5): expand K^C and V of every visible key, head-major [B, n_kv, lcap, d_h] (fp16 on the
+  // MFMA path, the layer dtype otherwise).
   const int64_t row = d.d_c + d.d_r;
   const int64_t kv_seq = (int64_t)d.n_kv * L.lcap * d.d_h;
+  se.begin(GDLA_STAGE_EXPAND_KV);
   for (int32_t b0 = 0; b0 < B; b0 += kMaxGemmProblems / 2) {
     GemmBatch g{};
     for (int32_t b = b0; b < std::min(B, b0 + kMaxGemmProblems / 2); ++b) {
@@ -344,6 +370,7 @@ GDLA_EXPORT gdla_status gdla_prefill(const gdla_dims *dims, const gdla_weights *
                           at<char>(ws, L.kx) + b * kv_seq * es, d.d_h, nk, d.n_kv * d.d_h, d.d_c, false);
       pk.hw = d.d_h;
       pk.hs = (int64_t)L.lcap * d.d_h;
+      if (L.use_fast) pk.c_dt = CD_F16;
       GemmProblem pv = pk;
       pv.B = w->w_uv;
       pv.C = at<char>(ws, L.vx) + b * kv_seq * es;
@@ -352,15 +379,17 @@ GDLA_EXPORT gdla_status gdla_prefill(const gdla_dims *dims, const gdla_weights *
     }
     HIP_TRY(launch_gemm(g, dt, stream));
   }
+  se.end(GDLA_STAGE_EXPAND_KV);
 
   if (L.use_fast) {
     st = run_fast_prefill(d, w, B, T, pos_dev, pos_host, cache, max_len, at<void>(ws, L.cq),
                           at<float>(ws, L.lam), at<float>(ws, L.gate), at<void>(ws, L.kx),
                           at<void>(ws, L.vx), L.lcap, at<void>(ws, L.y), out_heads, L.fast, ws,
-                          stream);
+                          stream, se);
     if (st != GDLA_OK) return fail(st, "fast prefill path failed: %s", hipGetErrorString(hipGetLastError()));
   } else {
     // Eq.(2), (9): q^C, pre-RoPE q^R and gate logits.
+    se.begin(GDLA_STAGE_PROJ_Q);
     GemmBatch g{};
     g.p[g.n++] = gp(at<void>(ws, L.cq), d.d_cq, w->w_qc, (int64_t)d.n_heads * d.d_h, at<void>(ws, L.qc),
                     (int64_t)d.n_heads * d.d_h, M, d.n_heads * d.d_h, d.d_cq, false);
@@ -369,24 +398,36 @@ GDLA_EXPORT gdla_status gdla_prefill(const gdla_dims *dims, const gdla_weights *
     g.p[g.n++] = gp(at<void>(ws, L.cq), d.d_cq, w->w_gate, (int64_t)d.n_signal * d.d_h, at<float>(ws, L.gate),
                     (int64_t)d.n_signal * d.d_h, M, d.n_signal * d.d_h, d.d_cq, true);
     HIP_TRY(launch_gemm(g, dt, stream));
-    HIP_TRY(launch_rope_heads(at<float>(ws, L.qrp), at<void>(ws, L.qr), (int64_t)d.n_heads * d.d_r, 0, M, T,
-                              d.n_heads, d.d_r, pos_dev, d.theta, dt, stream));
+    HIP_TRY(launch_rope_heads(at<float>(ws, L.qrp), at<void>(ws, L.qr), (int64_t)d.n_heads * d.d_r, d.d_r, 0,
+                              M, T, d.n_heads, d.d_r, pos_dev, d.theta, dt, stream));
+    se.end(GDLA_STAGE_PROJ_Q);
     AttnGenericArgs a{};
     a.qc = at<void>(ws, L.qc); a.qr = at<void>(ws, L.qr); a.kx = at<void>(ws, L.kx);
     a.vx = at<void>(ws, L.vx); a.cache = cache; a.heads = at<float>(ws, L.heads); a.pos = pos_dev;
     a.M = M; a.T = T; a.max_len = max_len; a.lcap = L.lcap;
+    se.begin(GDLA_STAGE_ATTN_NOISE);
     HIP_TRY(launch_attention_generic(a, d, dt, stream));
+    se.end(GDLA_STAGE_ATTN_NOISE);
+    se.begin(GDLA_STAGE_ATTN_SIGNAL);
     if (out_heads)
       HIP_TRY(launch_copy_rows_f32(at<float>(ws, L.heads), (int64_t)d.n_heads * d.d_h, out_heads,
                                    (int64_t)d.n_heads * d.d_h, M, d.n_heads * d.d_h, stream));
     HIP_TRY(launch_combine(at<float>(ws, L.heads), at<float>(ws, L.lam), at<float>(ws, L.gate),
                            at<void>(ws, L.y), M, d, dt, stream));
+    se.end(GDLA_STAGE_ATTN_SIGNAL);
   }
-  // Eq.(10): out = Y W_o.
+  // Eq.(10): out = Y W_o (Y is fp16 on the MFMA path).
   GemmBatch g{};
   g.p[g.n++] = gp(at<void>(ws, L.y), (int64_t)d.n_signal * d.d_h, w->w_o, d.d_model, out, d.d_model, M,
                   d.d_model, d.n_signal * d.d_h, false);
+  if (L.use_fast) {
+    g.p[0].a_f16 = 1;
+    g.p[0].c_dt = CD_BF16;
+  }
+  se.begin(GDLA_STAGE_PROJ_OUT);
   HIP_TRY(launch_gemm(g, dt, stream));
+  se.end(GDLA_STAGE_PROJ_OUT);
+  se.finish();
   return GDLA_OK;
 }
 
@@ -403,14 +444,18 @@ GDLA_EXPORT gdla_status gdla_decode(const gdla_dims *dims, const gdla_weights *w
   const DT dt = dims->dtype == GDLA_F32 ? DT::F32 : DT::BF16;
   const float *lam_override = dbg ? dbg->lambda_override : nullptr;
   float *out_heads = dbg ? dbg->out_heads : nullptr;
+  StageEvents se;
+  se.ev = dbg ? dbg->stage_events : nullptr;
+  se.s = stream;
 
   int32_t *pos_dev = at<int32_t>(ws, L.pos);
   HIP_TRY(launch_set_i32(pos_dev, pos_host, B, stream));
   st = project_and_append(d, dt, w, x, B, 1, pos_dev, cache, max_len, at<float>(ws, L.aq),
                           at<float>(ws, L.ckv), at<float>(ws, L.krp), at<float>(ws, L.laml),
-                          at<void>(ws, L.cq), at<float>(ws, L.lam), lam_override, stream);
+                          at<void>(ws, L.cq), at<float>(ws, L.lam), lam_override, stream, se);
   if (st != GDLA_OK) return st;
   // Eq.(2), (9) in fp32 (decode keeps the query in fp32 until it is mapped into the latent).
+  se.begin(GDLA_STAGE_PROJ_Q);
   GemmBatch g{};
   g.p[g.n++] = gp(at<void>(ws, L.cq), d.d_cq, w->w_qc, (int64_t)d.n_heads * d.d_h, at<float>(ws, L.qc),
                   (int64_t)d.n_heads * d.d_h, B, d.n_heads * d.d_h, d.d_cq, true);
@@ -419,17 +464,21 @@ GDLA_EXPORT gdla_status gdla_decode(const gdla_dims *dims, const gdla_weights *w
   g.p[g.n++] = gp(at<void>(ws, L.cq), d.d_cq, w->w_gate, (int64_t)d.n_signal * d.d_h, at<float>(ws, L.gate),
                   (int64_t)d.n_signal * d.d_h, B, d.n_signal * d.d_h, d.d_cq, true);
   HIP_TRY(launch_gemm(g, dt, stream));
-  HIP_TRY(launch_rope_heads(at<float>(ws, L.qrp), at<float>(ws, L.qr), (int64_t)d.n_heads * d.d_r, 0, B, 1,
-                            d.n_heads, d.d_r, pos_dev, d.theta, DT::F32, stream));
+  HIP_TRY(launch_rope_heads(at<float>(ws, L.qrp), at<float>(ws, L.qr), (int64_t)d.n_heads * d.d_r, d.d_r, 0,
+                            B, 1, d.n_heads, d.d_r, pos_dev, d.theta, DT::F32, stream));
+  se.end(GDLA_STAGE_PROJ_Q);
   if (L.use_fast) {
     st = run_fast_decode(d, w, B, pos_dev, pos_host, cache, max_len, at<float>(ws, L.qc),
-                         at<float>(ws, L.qr), at<float>(ws, L.heads), L.fast, ws, stream);
+                         at<float>(ws, L.qr), at<float>(ws, L.heads), L.fast, ws, stream, se);
     if (st != GDLA_OK) return fail(st, "fast decode path failed: %s", hipGetErrorString(hipGetLastError()));
   } else {
+    se.begin(GDLA_STAGE_ATTN_NOISE);
     HIP_TRY(launch_absorb_generic(at<float>(ws, L.qc), at<float>(ws, L.qr), w->w_uk, at<float>(ws, L.qabs),
                                   B, d, dt, stream));
     HIP_TRY(launch_latent_attention_generic(at<float>(ws, L.qabs), cache, at<float>(ws, L.o), pos_dev, B,
                                             max_len, d, dt, stream));
+    se.end(GDLA_STAGE_ATTN_NOISE);
+    se.begin(GDLA_STAGE_ATTN_SIGNAL);
     HIP_TRY(launch_unabsorb_generic(at<float>(ws, L.o), w->w_uv, at<float>(ws, L.heads), B, d, dt, stream));
   }
   if (out_heads)
@@ -437,9 +486,13 @@ GDLA_EXPORT gdla_status gdla_decode(const gdla_dims *dims, const gdla_weights *w
                                  (int64_t)d.n_heads * d.d_h, B, d.n_heads * d.d_h, stream));
   HIP_TRY(launch_combine(at<float>(ws, L.heads), at<float>(ws, L.lam), at<float>(ws, L.gate),
                          at<void>(ws, L.y), B, d, dt, stream));
+  se.end(GDLA_STAGE_ATTN_SIGNAL);
   g = GemmBatch{};
   g.p[g.n++] = gp(at<void>(ws, L.y), (int64_t)d.n_signal * d.d_h, w->w_o, d.d_model, out, d.d_model, B,
                   d.d_model, d.n_signal * d.d_h, false);
+  se.begin(GDLA_STAGE_PROJ_OUT);
   HIP_TRY(launch_gemm(g, dt, stream));
+  se.end(GDLA_STAGE_PROJ_OUT);
+  se.finish();
   return GDLA_OK;
 }

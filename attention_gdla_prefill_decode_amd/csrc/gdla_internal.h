@@ -10,8 +10,9 @@
 namespace gdla {
 
 typedef __bf16 bf16_t;
+typedef _Float16 f16_t;
 
-enum class DT : int32_t { F32 = 0, BF16 = 1 };
+enum class DT : int32_t { F32 = 0, BF16 = 1, F16 = 2 };
 
 // One GEMM problem: C[m, col(n)] = epi(sum_k A[m, k] * B[k, n]), fp32 accumulation.
 // A is [M, K] with row stride lda, B is [K, N] with row stride ldb (both in the input dtype).
@@ -25,13 +26,16 @@ struct GemmProblem {
   int64_t hs;
   int32_t M, N, K;
   int32_t hw, ho;
-  int32_t c_f32;   // 1: fp32 output, 0: output in the input dtype
+  int32_t c_dt;    // CD_*: output dtype
+  int32_t a_f16;   // 1: A is fp16 and the bf16 B is converted to fp16 while staged (MFMA only)
   int32_t epi;     // EPI_*
   int32_t tile0;   // first linear tile index of this problem (filled by the launcher)
   int32_t tiles_n; // tiles along N (filled by the launcher)
 };
 
 enum { EPI_NONE = 0, EPI_SIGMOID = 1 };
+// Output dtypes: fp32, the input dtype, bf16, fp16 (the generic kernel serves CD_F32 / CD_IN).
+enum { CD_F32 = 0, CD_IN = 1, CD_BF16 = 2, CD_F16 = 3 };
 
 constexpr int kMaxGemmProblems = 8;
 
@@ -51,6 +55,23 @@ __host__ __device__ inline int kv_head_of(int h, int n_signal, int n_kv) {
   return h < n_signal ? (h % n_kv) : ((h - n_signal) % n_kv);
 }
 
+// Records caller-provided stage events (gdla_debug.stage_events) around the stages of a call;
+// stages a call does not run get their two events recorded back to back by finish().
+struct StageEvents {
+  hipEvent_t *ev = nullptr;
+  hipStream_t s = nullptr;
+  unsigned done = 0;
+  void begin(int k) { if (ev) hipEventRecord(ev[2 * k], s); }
+  void end(int k) {
+    if (ev) { hipEventRecord(ev[2 * k + 1], s); done |= 1u << k; }
+  }
+  void finish() {
+    if (!ev) return;
+    for (int k = 0; k < GDLA_N_STAGES; ++k)
+      if (!(done & (1u << k))) { begin(k); end(k); }
+  }
+};
+
 // GEMM dispatch: bf16 MFMA kernels when every problem of the batch fits them, else generic.
 hipError_t launch_gemm(GemmBatch &batch, DT dt, hipStream_t s);
 
@@ -68,16 +89,18 @@ struct PrepArgs {
   const float *lam_logit; // [M, n_S]
   const float *lam_override;
   const void *gamma_q, *gamma_kv;
-  void *cq;               // [M, d_cq]
+  void *cq;               // [M, d_cq] in the input dtype, or fp16 when cq_f16
   float *lam;             // [M, n_S]
   void *cache;            // [B, max_len, d_c + d_r]
   const int32_t *pos;     // [B] device
   int32_t M, T, max_len;
+  int32_t cq_f16;
 };
 hipError_t launch_prep(const PrepArgs &a, const LayerDims &d, DT dt, hipStream_t s);
 
-// In-place style RoPE of per-head rows: dst[m, h, :] = RoPE(src[m, h, :], pos[m / T] + m % T).
-hipError_t launch_rope_heads(const float *src, void *dst, int64_t dst_ld, int32_t dst_off,
+// RoPE of per-head rows: dst[m * dst_ld + h * dst_hs + dst_off + j] = RoPE(src[m, h, :], p)[j]
+// with src fp32 [M, n_heads, d_r] and p = pos[m / T] + m % T.
+hipError_t launch_rope_heads(const float *src, void *dst, int64_t dst_ld, int32_t dst_hs, int32_t dst_off,
                              int32_t M, int32_t T, int32_t n_heads, int32_t d_r,
                              const int32_t *pos, float theta, DT dt, hipStream_t s);
 

@@ -22,6 +22,10 @@ template <> __device__ __forceinline__ void st<float>(float *p, int64_t i, float
 template <> __device__ __forceinline__ void st<bf16_t>(bf16_t *p, int64_t i, float v) {
   p[i] = (bf16_t)v;
 }
+// fp16 stores saturate to the finite range (+-65504) instead of producing infinities.
+template <> __device__ __forceinline__ void st<f16_t>(f16_t *p, int64_t i, float v) {
+  p[i] = (f16_t)fminf(fmaxf(v, -65504.f), 65504.f);
+}
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
@@ -91,7 +95,7 @@ __global__ void __launch_bounds__(256) gemm_generic_kernel(GemmBatch batch) {
       float v = acc[i][j];
       if (P.epi == EPI_SIGMOID) v = sigmoidf_(v);
       const int64_t off = (int64_t)m * P.ldc + (int64_t)(n / P.hw) * P.hs + P.ho + (n % P.hw);
-      if (P.c_f32) ((float *)P.C)[off] = v;
+      if (P.c_dt == CD_F32) ((float *)P.C)[off] = v;
       else st<TI>((TI *)P.C, off, v);
     }
   }
@@ -142,8 +146,11 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs a, LayerDims d) {
     float ss = 0.f;
     for (int j = threadIdx.x; j < d.d_cq; j += 256) ss += row[j] * row[j];
     const float r = rsqrtf(block_sum256(ss, red) / d.d_cq + d.eps);
-    for (int j = threadIdx.x; j < d.d_cq; j += 256)
-      st<T>((T *)a.cq, (int64_t)m * d.d_cq + j, row[j] * r * (gq ? ld<T>(gq, j) : 1.f));
+    for (int j = threadIdx.x; j < d.d_cq; j += 256) {
+      const float v = row[j] * r * (gq ? ld<T>(gq, j) : 1.f);
+      if (a.cq_f16) st<f16_t>((f16_t *)a.cq, (int64_t)m * d.d_cq + j, v);
+      else st<T>((T *)a.cq, (int64_t)m * d.d_cq + j, v);
+    }
   }
   T *crow = (T *)a.cache + ((int64_t)b * a.max_len + p) * (d.d_c + d.d_r);
   {
@@ -179,7 +186,7 @@ hipError_t launch_prep(const PrepArgs &a, const LayerDims &d, DT dt, hipStream_t
 
 template <typename T>
 __global__ void __launch_bounds__(256) rope_heads_kernel(const float *src, T *dst, int64_t dst_ld,
-                                                         int32_t dst_off, int32_t T_, int32_t n_heads,
+                                                         int32_t dst_hs, int32_t dst_off, int32_t T_, int32_t n_heads,
                                                          int32_t d_r, const int32_t *pos,
                                                          float theta) {
   __shared__ float cs[2][128];  // d_r <= 256
@@ -193,22 +200,25 @@ __global__ void __launch_bounds__(256) rope_heads_kernel(const float *src, T *ds
     const float c = cs[0][j], s = cs[1][j];
     const float *r = src + ((int64_t)m * n_heads + h) * d_r;
     const float u = r[j], v = r[j + half];
-    T *o = dst + (int64_t)m * dst_ld + (int64_t)h * d_r + dst_off;
+    T *o = dst + (int64_t)m * dst_ld + (int64_t)h * dst_hs + dst_off;
     st<T>(o, j, u * c - v * s);
     st<T>(o, j + half, u * s + v * c);
   }
 }
 
-hipError_t launch_rope_heads(const float *src, void *dst, int64_t dst_ld, int32_t dst_off,
-                             int32_t M, int32_t T, int32_t n_heads, int32_t d_r,
+hipError_t launch_rope_heads(const float *src, void *dst, int64_t dst_ld, int32_t dst_hs,
+                             int32_t dst_off, int32_t M, int32_t T, int32_t n_heads, int32_t d_r,
                              const int32_t *pos, float theta, DT dt, hipStream_t s) {
   if (M == 0) return hipSuccess;
   if (dt == DT::F32)
     hipLaunchKernelGGL(rope_heads_kernel<float>, dim3(M), dim3(256), 0, s, src, (float *)dst,
-                       dst_ld, dst_off, T, n_heads, d_r, pos, theta);
+                       dst_ld, dst_hs, dst_off, T, n_heads, d_r, pos, theta);
+  else if (dt == DT::F16)
+    hipLaunchKernelGGL(rope_heads_kernel<f16_t>, dim3(M), dim3(256), 0, s, src, (f16_t *)dst,
+                       dst_ld, dst_hs, dst_off, T, n_heads, d_r, pos, theta);
   else
     hipLaunchKernelGGL(rope_heads_kernel<bf16_t>, dim3(M), dim3(256), 0, s, src, (bf16_t *)dst,
-                       dst_ld, dst_off, T, n_heads, d_r, pos, theta);
+                       dst_ld, dst_hs, dst_off, T, n_heads, d_r, pos, theta);
   return hipGetLastError();
 }
 

@@ -40,7 +40,48 @@ class GdlaWeights(ctypes.Structure):
 
 
 class GdlaDebug(ctypes.Structure):
-    _fields_ = [("lambda_override", ctypes.c_void_p), ("out_heads", ctypes.c_void_p)]
+    _fields_ = [("lambda_override", ctypes.c_void_p), ("out_heads", ctypes.c_void_p),
+                ("stage_events", ctypes.c_void_p)]
+
+
+STAGES = ("proj_in", "norm_append", "expand_kv", "proj_q", "attn_noise", "attn_signal", "proj_out")
+
+
+class StageTimer:
+    """2 x len(STAGES) HIP events for gdla_debug.stage_events; elapsed() gives per-stage ms."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = (ctypes.c_void_p * (2 * len(STAGES)))()
+        for i in range(2 * len(STAGES)):
+            ev = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.events[i] = ev
+        self.ptr = ctypes.cast(self.events, ctypes.c_void_p).value
+
+    def elapsed(self):
+        """Per-stage milliseconds of the last call that recorded these events."""
+        out = {}
+        for k, name in enumerate(STAGES):
+            self.hip.hipEventSynchronize(self.events[2 * k + 1])
+            ms = ctypes.c_float()
+            if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.events[2 * k],
+                                            self.events[2 * k + 1]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out[name] = ms.value
+        return out
+
+    def __del__(self):
+        try:
+            for i in range(2 * len(STAGES)):
+                self.hip.hipEventDestroy(self.events[i])
+        except Exception:
+            pass
 
 
 class GdlaError(RuntimeError):
@@ -139,11 +180,12 @@ def _workspace(dims, op, B, T, pos, max_len, ws, device):
     return ws, ws.numel()
 
 
-def _debug(lambda_override, out_heads):
-    if lambda_override is None and out_heads is None:
+def _debug(lambda_override, out_heads, timer=None):
+    if lambda_override is None and out_heads is None and timer is None:
         return None
     return GdlaDebug(None if lambda_override is None else lambda_override.data_ptr(),
-                     None if out_heads is None else out_heads.data_ptr())
+                     None if out_heads is None else out_heads.data_ptr(),
+                     None if timer is None else timer.ptr)
 
 
 def gdla_latent_append(dims, weights, x, pos, cache, ws=None, stream=None):
@@ -157,14 +199,14 @@ def gdla_latent_append(dims, weights, x, pos, cache, ws=None, stream=None):
 
 
 def gdla_prefill(dims, weights, x, pos, cache, out=None, ws=None, lambda_override=None,
-                 out_heads=None, stream=None):
+                 out_heads=None, stream=None, timer=None):
     """x [B, T, d_model] at positions pos[b] + t; appends to cache; returns out [B, T, d_model]."""
     B, T = x.shape[0], x.shape[1]
     max_len = cache.shape[1]
     if out is None:
         out = torch.empty_like(x)
     ws, nbytes = _workspace(dims, GDLA_OP_PREFILL, B, T, pos, max_len, ws, x.device)
-    dbg = _debug(lambda_override, out_heads)
+    dbg = _debug(lambda_override, out_heads, timer)
     _check(lib().gdla_prefill(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B, T,
                               _pos_array(pos), _ptr(cache), max_len, _ptr(out), _ptr(ws), nbytes,
                               None if dbg is None else ctypes.byref(dbg), _stream(stream)))
@@ -172,14 +214,14 @@ def gdla_prefill(dims, weights, x, pos, cache, out=None, ws=None, lambda_overrid
 
 
 def gdla_decode(dims, weights, x, pos, cache, out=None, ws=None, lambda_override=None,
-                out_heads=None, stream=None):
+                out_heads=None, stream=None, timer=None):
     """x [B, d_model], token b at position pos[b]; appends to cache; returns out [B, d_model]."""
     B = x.shape[0]
     max_len = cache.shape[1]
     if out is None:
         out = torch.empty_like(x)
     ws, nbytes = _workspace(dims, GDLA_OP_DECODE, B, 1, pos, max_len, ws, x.device)
-    dbg = _debug(lambda_override, out_heads)
+    dbg = _debug(lambda_override, out_heads, timer)
     _check(lib().gdla_decode(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B,
                              _pos_array(pos), _ptr(cache), max_len, _ptr(out), _ptr(ws), nbytes,
                              None if dbg is None else ctypes.byref(dbg), _stream(stream)))

@@ -1,0 +1,215 @@
+"""Benchmark of the GDLA forward on one MI355X: one step = one gdla_prefill call over the
+8192-token single-layer workload (batch 1, d_model 4096, 64 signal + 16 noise heads, 16 KV heads,
+latents 1024 / 512, head dim 128, rotary dim 64, full causal), inputs seeded and resident in HBM.
+
+Prints one JSON line: whole-step throughput (algorithmic FLOP of the layer / step time), the
+roofline of the dominant kernel (signal-head attention, timed with HIP events recorded by the
+library around it), and the fp64 CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode] [--no-cpu-baseline]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "GDLA prefill TFLOP/s (% bf16 MFMA peak); decode latent-KV GB/s (% HBM peak)"
+
+
+def visible_pairs(p0, t, window):
+    """Number of (query, key) pairs with key <= query position and, for window W, within W."""
+    total = 0
+    for i in range(t):
+        p = p0 + i
+        total += min(p + 1, window) if window > 0 else p + 1
+    return total
+
+
+def layer_flops(cfg, t, p0, window):
+    """Algorithmic FLOP of one GDLA layer call on one sequence (attention counts visible pairs)."""
+    d, dcq, dc, nh, ns = cfg["d_model"], cfg["d_q_latent"], cfg["d_kv_latent"], cfg["n_heads"], cfg["n_signal"]
+    nkv, dh, dr = cfg["n_kv"], cfg["d_head"], cfg["d_rope"]
+    pairs = visible_pairs(p0, t, window)
+    attn_signal = 2.0 * ns * pairs * (2 * dh + dr)
+    attn_noise = 2.0 * (nh - ns) * pairs * (2 * dh + dr)
+    keys = p0 + t - (max(0, p0 - window + 1) if window > 0 else 0)
+    proj = 2.0 * t * (d * (dcq + dc + dr + ns) + dcq * (nh * dh + nh * dr + ns * dh) + ns * dh * d)
+    expand = 2.0 * keys * dc * (2 * nkv * dh)
+    return {"attn_signal": attn_signal, "attn_noise": attn_noise, "proj": proj, "expand": expand,
+            "total": attn_signal + attn_noise + proj + expand, "pairs": pairs}
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "attention_gdla_prefill_decode_amd", "csrc", "attn_prefill.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """HBM bytes per launch of the dominant kernel from the committed counter summary, if it was
+    taken on the current kernel source (else None)."""
+    p = os.path.join(ROOT, "profiles", "attn_signal_prefill_8k_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(rows=768):
+    """The fp64 oracle on the last `rows` query rows of the 8K workload with their full causal
+    context, drawn with the same recipe on the CPU; returns its throughput in TFLOP/s."""
+    import numpy as np
+    import synth
+    import oracle.gdla_ref as ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        threads = os.cpu_count()
+    cfg = synth.WORKLOADS["prefill_8k"]
+    t = cfg["seq"]
+    inp = synth.make_inputs(cfg, "cpu")
+    w = {k: v.double().numpy() for k, v in inp["weights"].items()}
+    x = inp["x"][0].double().numpy()
+    dims = ref.Dims(cfg["n_heads"], cfg["n_signal"], cfg["n_noise"], cfg["n_kv"], cfg["d_head"],
+                    cfg["d_rope"], 0)
+    sel = np.arange(t - rows, t)
+    t0 = time.perf_counter()
+    ref.gdla_forward(x, w, dims, None, 0, rows=sel)
+    dt = time.perf_counter() - t0
+    d, dcq, dc, nh, ns = cfg["d_model"], cfg["d_q_latent"], cfg["d_kv_latent"], cfg["n_heads"], cfg["n_signal"]
+    dh, dr, nkv = cfg["d_head"], cfg["d_rope"], cfg["n_kv"]
+    pairs = sum(p + 1 for p in range(t - rows, t))
+    flops = (2.0 * nh * pairs * (2 * dh + dr)                       # attention of the rows
+             + 2.0 * rows * (d * (dcq + ns) + dcq * (nh * dh + nh * dr + ns * dh) + ns * dh * d)
+             + 2.0 * t * d * (dc + dr)                              # latents of every key
+             + 2.0 * t * dc * (2 * nkv * dh))                       # K/V expansion of every key
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"fp64 NumPy oracle, last {rows} of 8192 query rows of the same layer with "
+                      f"their full causal context (latents and K/V of all 8192 keys), "
+                      f"{flops / 1e12:.3f} TFLOP of algorithmic work"}
+
+
+def bench_decode(steps, warmup):
+    import torch
+    import synth
+    import attention_gdla_prefill_decode_amd as gd
+    cfg = synth.WORKLOADS["decode_64x64k"]
+    inp = synth.make_inputs(cfg, "cuda")
+    w = gd.make_weights(inp["weights"])
+    dims = gd.make_dims(cfg)
+    x = inp["x"][:, 0].contiguous()
+    pos = inp["p0"]
+    ws = torch.empty(gd.gdla_workspace_bytes(dims, gd.GDLA_OP_DECODE, len(pos), 1, pos, cfg["max_len"]),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(x)
+    timer = gd.StageTimer()
+    for _ in range(warmup):
+        gd.gdla_decode(dims, w, x, pos, inp["cache"], out=out, ws=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    attn_ms = 0.0
+    e0.record()
+    for _ in range(steps):
+        gd.gdla_decode(dims, w, x, pos, inp["cache"], out=out, ws=ws, timer=timer)
+        st = timer.elapsed()
+        attn_ms += st["attn_noise"] + st["attn_signal"]
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    cache_bytes = len(pos) * cfg["max_len"] * (cfg["d_kv_latent"] + cfg["d_rope"]) * 2
+    return {"workload": "decode_64x64k", "ms_per_step": round(ms, 4),
+            "latent_cache_GBps_whole_step": round(cache_bytes / ms / 1e6, 1),
+            "attention_ms": round(attn_ms / steps, 4),
+            "latent_cache_GBps_attention": round(cache_bytes / (attn_ms / steps) / 1e6, 1),
+            "frac_hbm_attention": round(cache_bytes / (attn_ms / steps) / 1e6 / PEAK_HBM_GBS, 4)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode", action="store_true", help="also time the 64 x 64K decode workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build runs on a single MI355X and has no "
+              f"multi-GPU path (asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import attention_gdla_prefill_decode_amd as gd
+
+    cfg = synth.WORKLOADS["prefill_8k"]
+    t, p0 = cfg["seq"], cfg["p0"]
+    inp = synth.make_inputs(cfg, "cuda")
+    w = gd.make_weights(inp["weights"])
+    dims = gd.make_dims(cfg)
+    x, cache = inp["x"], inp["cache"]
+    pos = inp["p0"]
+    ws = torch.empty(gd.gdla_workspace_bytes(dims, gd.GDLA_OP_PREFILL, 1, t, pos, cfg["max_len"]),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(x)
+    timer = gd.StageTimer()
+    for _ in range(args.warmup):
+        gd.gdla_prefill(dims, w, x, pos, cache, out=out, ws=ws)
+    torch.cuda.synchronize()
+
+    stage_tot = {k: 0.0 for k in gd.STAGES}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        gd.gdla_prefill(dims, w, x, pos, cache, out=out, ws=ws, timer=timer)
+        for k, v in timer.elapsed().items():
+            stage_tot[k] += v
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    stages = {k: round(v / args.steps, 4) for k, v in stage_tot.items()}
+    fl = layer_flops(cfg, t, p0, 0)
+    value = fl["total"] / (ms * 1e-3) / 1e12
+    attn_ms = stages["attn_signal"]
+    achieved = fl["attn_signal"] / (attn_ms * 1e-3) / 1e12
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16+fp16 (fp32 accumulate)", "data": "synthetic",
+        "config": {"workload": "prefill_8k", "batch": 1, "seq_len": t, "d_model": cfg["d_model"],
+                   "heads": "64 signal + 16 noise, 16 KV", "latents": "1024 / 512",
+                   "head_dim": cfg["d_head"], "rope_dim": cfg["d_rope"], "window": 0,
+                   "parallelism": "none (1 GPU)"},
+        "frac_of_mfma_peak_whole_step": round(value / PEAK_MFMA_TFLOPS, 4),
+        "roofline": {"kernel": "attn_prefill_kernel<signal>", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
+                     "traffic": traffic_from_profile(),
+                     "flop_per_launch": fl["attn_signal"], "avg_launch_ms": attn_ms},
+        "stages_ms": stages,
+        "out_finite": bool(torch.isfinite(out).all().item()),
+    }
+    if args.decode:
+        result["decode"] = bench_decode(max(3, args.steps // 4), 2)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -105,11 +105,29 @@ typedef struct {
   const void *w_o;       /* [n_signal * d_head, d_model]        Eq.(10) */
 } gdla_weights;
 
-/* Optional test hooks; pass NULL (or a struct of NULLs) in production. */
+/* Optional test and profiling hooks; pass NULL (or a struct of NULLs) in production. */
 typedef struct {
   const float *lambda_override;  /* [B, T, n_signal] fp32: used instead of sigmoid(x W_lambda) */
   float *out_heads;              /* [B, T, n_heads, d_head] fp32: per-head H before Eq.(8) */
+  /* Host array of 2 * GDLA_N_STAGES caller-created hipEvent_t (or NULL).  When set, the call
+   * records stage_events[2k] on `stream` before stage k and stage_events[2k + 1] after it, so a
+   * caller can time every kernel of the call with hipEventElapsedTime.  Stages that a call does
+   * not run get both events recorded back to back. */
+  hipEvent_t *stage_events;
 } gdla_debug;
+
+/* Stages reported through gdla_debug.stage_events. */
+enum {
+  GDLA_STAGE_PROJ_IN = 0,    /* x [W_qa | W_dkv | W_kr | W_lambda]                  Eq.(1),(3),(7) */
+  GDLA_STAGE_NORM_APPEND,    /* RMSNorm, RoPE of k^R, sigmoid, cache append         Eq.(1),(4),(7) */
+  GDLA_STAGE_EXPAND_KV,      /* prefill: K^C, V of the visible keys                 Eq.(5) */
+  GDLA_STAGE_PROJ_Q,         /* c^Q [W_qc | W_qr | W_gate], RoPE of q^R             Eq.(2),(9) */
+  GDLA_STAGE_ATTN_NOISE,     /* prefill: noise-head attention; decode: absorb + latent attention */
+  GDLA_STAGE_ATTN_SIGNAL,    /* prefill: signal-head attention + Eq.(8) combine + gate;
+                                decode: un-absorb + combine + gate                  Eq.(8)-(10) */
+  GDLA_STAGE_PROJ_OUT,       /* vec(.) W_o                                          Eq.(10) */
+  GDLA_N_STAGES
+};
 
 /* Bytes of workspace that op needs for B sequences of T new tokens each (T = 1 for decode).
  * pos_host (host, [B], may be NULL) gives the first new position of each sequence; with NULL the

@@ -270,14 +270,16 @@ def gdla_forward(x, w, dims, prefix=None, p0=0, lam_override=None, form="expande
     rows:   optional indices of the query rows to evaluate (all rows by default); the cache rows of
             all T tokens are always produced, since later rows attend to them.
     Returns a dict with out [R, d_model], cache_rows [T, d_c + d_R], heads H [R, n_H, d_h],
-    lam [T, n_S], and the intermediates.
+    lam [R, n_S], and the intermediates of the R evaluated rows.
     """
     x = _f64(x)
     t = x.shape[0]
     pos = p0 + np.arange(t)
-    c_q, q_c, q_r, gate = query_path(x, w, dims, pos)
+    sel = np.arange(t) if rows is None else np.asarray(rows)
+    # queries, gates and lambdas only for the evaluated rows; latents for every new token
+    c_q, q_c, q_r, gate = query_path(x[sel], w, dims, pos[sel])
     c_bar_new, k_r_new = latent_path(x, w, dims, pos)
-    lam = lambda_path(x, w) if lam_override is None else _f64(lam_override)
+    lam = lambda_path(x[sel], w) if lam_override is None else _f64(lam_override)[sel]
     cache_rows = np.concatenate([c_bar_new, k_r_new], axis=1)
     d_c = c_bar_new.shape[1]
     if p0 > 0:
@@ -288,18 +290,17 @@ def gdla_forward(x, w, dims, prefix=None, p0=0, lam_override=None, form="expande
     else:
         keys = cache_rows
     c_bar_all, k_r_all = keys[:, :d_c], keys[:, d_c:]
-    sel = np.arange(t) if rows is None else np.asarray(rows)
     qpos = pos[sel]
     hi = int(np.max(qpos)) + 1
     if form == "expanded":
         k_c, v = expand_kv(c_bar_all[:hi], w, dims)
-        heads = attention_expanded(q_c[sel], q_r[sel], k_c, k_r_all[:hi], v, qpos, dims)
+        heads = attention_expanded(q_c, q_r, k_c, k_r_all[:hi], v, qpos, dims)
     elif form == "absorbed":
-        heads = attention_absorbed(q_c[sel], q_r[sel], c_bar_all[:hi], k_r_all[:hi], w, dims, qpos)
+        heads = attention_absorbed(q_c, q_r, c_bar_all[:hi], k_r_all[:hi], w, dims, qpos)
     else:
         raise ValueError("form must be 'expanded' or 'absorbed'")
-    d = differential_combine(heads, lam[sel], dims)
-    y = gate_output(d, gate[sel])
+    d = differential_combine(heads, lam, dims)
+    y = gate_output(d, gate)
     out = output_projection(y, w["w_o"])
     return {"out": out, "cache_rows": cache_rows, "heads": heads, "lam": lam, "gate": gate,
             "D": d, "Y": y, "c_q": c_q, "q_c": q_c, "q_r": q_r}
