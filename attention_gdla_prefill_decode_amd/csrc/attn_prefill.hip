@@ -340,6 +340,7 @@ gdla_status run_fast_prefill(const LayerDims &d, const gdla_weights *w, int32_t 
   float *hn = (float *)((char *)ws + L.hn);
   // Eq.(2), (9): q^C straight into the per-head [q^C ; q^R] rows, q^R before RoPE, gate logits.
   GemmBatch g{};
+  se.begin(GDLA_STAGE_PROJ_Q);
   // c^Q is fp16 here; the bf16 weights are converted to fp16 while the GEMM stages them.
   auto add = [&](const void *B_, int N, void *C, int64_t ldc, int c_dt, int hw, int64_t hs) {
     GemmProblem p{};

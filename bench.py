@@ -67,7 +67,7 @@ def traffic_from_profile():
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(rows=768):
+def cpu_baseline(rows=2048):
     """The fp64 oracle on the last `rows` query rows of the 8K workload with their full causal
     context, drawn with the same recipe on the CPU; returns its throughput in TFLOP/s."""
     import numpy as np
@@ -116,20 +116,21 @@ def bench_decode(steps, warmup):
     ws = torch.empty(gd.gdla_workspace_bytes(dims, gd.GDLA_OP_DECODE, len(pos), 1, pos, cfg["max_len"]),
                      dtype=torch.uint8, device="cuda")
     out = torch.empty_like(x)
-    timer = gd.StageTimer()
+    timers = [gd.StageTimer() for _ in range(steps)]
     for _ in range(warmup):
         gd.gdla_decode(dims, w, x, pos, inp["cache"], out=out, ws=ws)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    attn_ms = 0.0
     e0.record()
-    for _ in range(steps):
-        gd.gdla_decode(dims, w, x, pos, inp["cache"], out=out, ws=ws, timer=timer)
-        st = timer.elapsed()
-        attn_ms += st["attn_noise"] + st["attn_signal"]
+    for i in range(steps):
+        gd.gdla_decode(dims, w, x, pos, inp["cache"], out=out, ws=ws, timer=timers[i])
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    attn_ms = 0.0
+    for tm in timers:
+        st = tm.elapsed()
+        attn_ms += st["attn_noise"] + st["attn_signal"]
     cache_bytes = len(pos) * cfg["max_len"] * (cfg["d_kv_latent"] + cfg["d_rope"]) * 2
     return {"workload": "decode_64x64k", "ms_per_step": round(ms, 4),
             "latent_cache_GBps_whole_step": round(cache_bytes / ms / 1e6, 1),
@@ -165,22 +166,24 @@ def main():
     ws = torch.empty(gd.gdla_workspace_bytes(dims, gd.GDLA_OP_PREFILL, 1, t, pos, cfg["max_len"]),
                      dtype=torch.uint8, device="cuda")
     out = torch.empty_like(x)
-    timer = gd.StageTimer()
+    # one set of stage events per timed step, read after the timed region (no host sync inside)
+    timers = [gd.StageTimer() for _ in range(args.steps)]
     for _ in range(args.warmup):
         gd.gdla_prefill(dims, w, x, pos, cache, out=out, ws=ws)
     torch.cuda.synchronize()
 
-    stage_tot = {k: 0.0 for k in gd.STAGES}
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
-    for _ in range(args.steps):
-        gd.gdla_prefill(dims, w, x, pos, cache, out=out, ws=ws, timer=timer)
-        for k, v in timer.elapsed().items():
-            stage_tot[k] += v
+    for i in range(args.steps):
+        gd.gdla_prefill(dims, w, x, pos, cache, out=out, ws=ws, timer=timers[i])
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+    stage_tot = {k: 0.0 for k in gd.STAGES}
+    for tm in timers:
+        for k, v in tm.elapsed().items():
+            stage_tot[k] += v
     stages = {k: round(v / args.steps, 4) for k, v in stage_tot.items()}
     fl = layer_flops(cfg, t, p0, 0)
     value = fl["total"] / (ms * 1e-3) / 1e12
