@@ -28,6 +28,12 @@ FastPrefillLayout plan_fast_prefill(const LayerDims &d, int32_t B, int32_t T, Ad
 }
 
 bool fast_prefill_supported(const LayerDims &d, gdla_dtype dt);
+// Elements per expanded key row on the MFMA path: [K^C (d_h) ; k^R (d_rope)] in fp16.
+int32_t fast_prefill_key_row();
+// Copies k^R of the visible keys from the bf16 cache (converted to fp16) into columns d_h ..
+// d_h + d_rope - 1 of every KV head's expanded key rows.
+hipError_t launch_kr_fill(const void *cache, void *kx, const int32_t *pos_dev, int32_t B, int32_t T,
+                          int32_t lcap, int32_t max_len, const LayerDims &d, hipStream_t s);
 gdla_status run_fast_prefill(const LayerDims &d, const gdla_weights *w, int32_t B, int32_t T,
                              const int32_t *pos_dev, const int32_t *pos_host, void *cache,
                              int32_t max_len, void *cq, float *lam, float *gate, void *kx,

@@ -108,7 +108,7 @@ PrefillLayout plan_prefill(const LayerDims &d, gdla_dtype dt, int32_t B, int32_t
   L.cq = p.add(es * M * d.d_cq);
   L.lam = p.add(4 * M * d.n_signal);
   L.gate = p.add(4 * M * d.n_signal * d.d_h);
-  L.kx = p.add(es * (size_t)B * d.n_kv * L.lcap * d.d_h);
+  L.kx = p.add(es * (size_t)B * d.n_kv * L.lcap * (L.use_fast ? fast_prefill_key_row() : d.d_h));
   L.vx = p.add(es * (size_t)B * d.n_kv * L.lcap * d.d_h);
   L.y = p.add(es * M * d.n_signal * d.d_h);
   if (L.use_fast) {
@@ -355,10 +355,13 @@ GDLA_EXPORT gdla_status gdla_prefill(const gdla_dims *dims, const gdla_weights *
                           L.use_fast);
   if (st != GDLA_OK) return st;
 
-  // Eq.(5): expand K^C and V of every visible key, head-major [B, n_kv, lcap, d_h] (fp16 on the
-  // MFMA path, the layer dtype otherwise).
+  // Eq.(5): expand K^C and V of every visible key, head-major [B, n_kv, lcap, *].  The MFMA path
+  // keeps fp16 key rows [K^C ; k^R] of d_h + d_rope values (k^R copied from the cache into every
+  // head's rows); the generic path keeps K^C rows of d_h values in the layer dtype.
   const int64_t row = d.d_c + d.d_r;
-  const int64_t kv_seq = (int64_t)d.n_kv * L.lcap * d.d_h;
+  const int64_t krow = L.use_fast ? fast_prefill_key_row() : d.d_h;
+  const int64_t k_seq = (int64_t)d.n_kv * L.lcap * krow;
+  const int64_t v_seq = (int64_t)d.n_kv * L.lcap * d.d_h;
   se.begin(GDLA_STAGE_EXPAND_KV);
   for (int32_t b0 = 0; b0 < B; b0 += kMaxGemmProblems / 2) {
     GemmBatch g{};
@@ -366,19 +369,23 @@ GDLA_EXPORT gdla_status gdla_prefill(const gdla_dims *dims, const gdla_weights *
       const int32_t lo = key_lo(pos_host[b], d.window);
       const int32_t nk = pos_host[b] + T - lo;
       const char *a = (const char *)cache + ((int64_t)b * max_len + lo) * row * es;
-      GemmProblem pk = gp(a, row, w->w_uk, (int64_t)d.n_kv * d.d_h,
-                          at<char>(ws, L.kx) + b * kv_seq * es, d.d_h, nk, d.n_kv * d.d_h, d.d_c, false);
+      GemmProblem pk = gp(a, row, w->w_uk, (int64_t)d.n_kv * d.d_h, at<char>(ws, L.kx) + b * k_seq * es,
+                          krow, nk, d.n_kv * d.d_h, d.d_c, false);
       pk.hw = d.d_h;
-      pk.hs = (int64_t)L.lcap * d.d_h;
+      pk.hs = (int64_t)L.lcap * krow;
       if (L.use_fast) pk.c_dt = CD_F16;
       GemmProblem pv = pk;
       pv.B = w->w_uv;
-      pv.C = at<char>(ws, L.vx) + b * kv_seq * es;
+      pv.C = at<char>(ws, L.vx) + b * v_seq * es;
+      pv.ldc = d.d_h;
+      pv.hs = (int64_t)L.lcap * d.d_h;
       g.p[g.n++] = pk;
       g.p[g.n++] = pv;
     }
     HIP_TRY(launch_gemm(g, dt, stream));
   }
+  if (L.use_fast)
+    HIP_TRY(launch_kr_fill(cache, at<void>(ws, L.kx), pos_dev, B, T, L.lcap, max_len, d, stream));
   se.end(GDLA_STAGE_EXPAND_KV);
 
   if (L.use_fast) {
