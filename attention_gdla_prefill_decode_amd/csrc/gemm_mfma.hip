@@ -7,11 +7,13 @@
 // section 2.2: x W^Q_a, x W^KV_a, x W^lambda in Eq.(1), (3), (7); c^Q W^Q_b, c^Q W^G in Eq.(2),
 // (9); cbar W^KV_b in Eq.(5); vec(.) W^O in Eq.(10)).
 //
-// Block tile 128 x 128, K slices of 64 staged in LDS (double buffered, one barrier per slice),
-// 4 waves of 64 x 64, each a 2 x 2 grid of v_mfma_f32_32x32x16_bf16.  A fragments (8 consecutive
-// k of one row) come from ds_read_b128; B is stored [k][n] in LDS and its fragments (8 consecutive
-// k of one column) come from two ds_read_tr16_b64.  Row paddings keep both reads free of bank
-// conflicts.  Tiles are spread so that each XCD gets a contiguous range of tiles.
+// Block tile 128 x 128, K slices of 32 staged in LDS (double buffered, one barrier per slice),
+// 4 waves of 64 x 64, each a 2 x 2 grid of v_mfma_f32_32x32x16 (bf16 or fp16).  A fragments (8
+// consecutive k of one row) come from ds_read_b128; B is stored [k][n] in LDS and its fragments (8
+// consecutive k of one column) come from two ds_read_tr16_b64.  Row paddings keep both reads free
+// of bank conflicts.  The short K slice keeps LDS at 40 KB and registers at about 123, so 4
+// workgroups (16 waves) share a CU and hide each other's load latency.  Tiles are spread so that
+// each XCD gets a contiguous range of tiles.
 #include "fast_paths.h"
 
 namespace gdla {
@@ -24,7 +26,7 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int BM = 128, BN = 128, BK = 32;
 constexpr int LDA_S = BK + 8;    // A row stride in LDS (elements)
 constexpr int LDB_S = BN + 32;   // B row stride in LDS (elements)
 constexpr int A_STAGE = BM * LDA_S;
@@ -65,7 +67,7 @@ __device__ __forceinline__ int remap_xcd(int bid, int total) {
 }
 
 template <typename TA>  // bf16_t: bf16 x bf16; f16_t: fp16 A x converted B
-__global__ void __launch_bounds__(256, 2) gemm_mfma_kernel(GemmBatch batch) {
+__global__ void __launch_bounds__(256, 4) gemm_mfma_kernel(GemmBatch batch) {
   typedef typename Frag<TA>::v8 v8;
   typedef typename Frag<TA>::v4 v4;
   constexpr bool CONVERT_B = __is_same(TA, f16_t);
@@ -83,13 +85,14 @@ __global__ void __launch_bounds__(256, 2) gemm_mfma_kernel(GemmBatch batch) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // global -> register staging: 4 A chunks and 4 B chunks of 8 bf16 per thread
-  uint4 ra[4], rb[4];
+  // global -> register staging: NCH A chunks and NCH B chunks of 8 elements per thread
+  constexpr int NCH = BK / 16;  // chunks of each operand per thread
+  uint4 ra[NCH], rb[NCH];
   auto load_global = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NCH; ++i) {
       const int c = tid + 256 * i;
-      const int r = c >> 3, kc = (c & 7) * 8;
+      const int r = c / (BK / 8), kc = (c % (BK / 8)) * 8;
       const int gm = m0 + r;
       ra[i] = gm < P.M ? *(const uint4 *)(A + (int64_t)gm * P.lda + k0 + kc) : make_uint4(0, 0, 0, 0);
       const int kr = c >> 4, nc = (c & 15) * 8;
@@ -100,9 +103,9 @@ __global__ void __launch_bounds__(256, 2) gemm_mfma_kernel(GemmBatch batch) {
   };
   auto store_lds = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NCH; ++i) {
       const int c = tid + 256 * i;
-      *(uint4 *)(As + buf * A_STAGE + (c >> 3) * LDA_S + (c & 7) * 8) = ra[i];
+      *(uint4 *)(As + buf * A_STAGE + (c / (BK / 8)) * LDA_S + (c % (BK / 8)) * 8) = ra[i];
       *(uint4 *)(Bs + buf * B_STAGE + (c >> 4) * LDB_S + (c & 15) * 8) = rb[i];
     }
   };
