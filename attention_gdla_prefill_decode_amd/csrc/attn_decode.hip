@@ -1,0 +1,493 @@
+// Absorbed-weight GDLA decode for gfx950 (d_kv_latent 512, d_rope 64): split-L attention of every
+// query head directly over the bf16 latent cache, then the LSE merge of the splits.
+//
+// The MLA property the Motif 3 Technical Report relies on (paperglide reader, section "Model
+// Architecture", MLA answer; picx.dev summary section 2.2, Eq.(5)) is that only the latent is
+// cached and K/V are rebuilt inside attention.  With q~_h = [q^C_h W_uk[:, kv(h)]^T ; q^R_h]:
+//     score_s = tau q~_h . cache_s,    o_h = sum_s softmax(score)_s cbar_s,    H_h = o_h W_uv[:, kv(h)]
+// which is exactly the expanded form, re-associated.  Every cached row is read once per sequence
+// and serves all query heads.
+//
+// Kernel layout: one workgroup per (sequence, key split), one wave per SIMD.  Query heads come in
+// blocks of 16 (the N side of v_mfma_f32_16x16x32_bf16); wave w owns block w (all 512 output dims)
+// and, when there are five blocks (65..80 heads), also output dims 128 w .. 128 w + 127 of block 4.
+// Every wave computes the scores of block 4 itself from the same LDS fragments it already reads for
+// its own block, so the fifth block costs MFMA work but no LDS traffic and no cross-wave traffic.
+// q~ (2 x 72 registers) and O^T (128 + 32) stay in registers.
+// Cache tiles of 64 rows (576 bf16 = 72 chunks of 16 bytes each) are loaded by direct global -> LDS
+// 16-byte loads into two distinct LDS buffers (one tile in flight while the other is consumed);
+// every tile serves all heads.  Per tile and wave:
+//   S^T[key, head] = cache[key, 0:576] . q~[head, 0:576]   (A = cache rows, B = q~ from registers)
+//   per-head online softmax (lanes l, l^16, l^32, l^48 hold one head), lazy rescaling,
+//   O^T[dim, head] += cbar^T[dim, key] . P^T[key, head]    (A = cbar^T by ds_read_b64_tr_b16,
+//                                                           B = P^T straight from the S registers)
+// Rows are unpadded; chunk c of row r sits at c ^ f(r) with f(r) = 4 r_2 + 2 r_1 + r_3 (r_i = bit i
+// of r): the 16-byte row reads (16 consecutive rows, one chunk) and the transposing reads (8
+// consecutive rows, 2 aligned chunks) then both hit distinct groups of 4 banks.
+// Each split writes its unnormalised O, its reference max m and sum l; merge_splits combines them.
+#include "fast_paths.h"
+
+#include <algorithm>
+
+namespace gdla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int DC = 512, DR = 64, ROW = DC + DR;
+constexpr int RB = ROW * 2;        // bytes per cache row
+constexpr int RCH = ROW / 8;       // 72 chunks per cache row
+constexpr int KT = 64;             // keys per tile
+constexpr int TILE = KT * ROW;     // elements per tile
+constexpr int TILE_CH = KT * RCH;  // chunks per tile (4608 = 72 wave-instructions)
+constexpr int NKST = ROW / 32;     // 18 k-steps of 32 in S
+constexpr int NDB = DC / 16;       // 32 dim blocks of 16 in O^T
+constexpr int MAX_WAVES = 4;
+constexpr int MAX_HEADS = 16 * (MAX_WAVES + 1);
+constexpr int SH_DB = NDB / MAX_WAVES;  // dim blocks of the shared head block per wave (8)
+
+struct DecodeArgs {
+  const bf16_t *qabs;  // [B, n_H, 576] bf16
+  const bf16_t *cache; // [B, max_len, 576] bf16
+  const int32_t *pos;  // [B] position of the new token (keys 0 .. pos are visible)
+  float *part_o;       // [B, splits, n_H, 512]
+  float *part_ml;      // [B, splits, n_H, 2]
+  int32_t n_heads, max_len, window, splits;
+  float c;             // softmax scale * log2(e)
+};
+
+__host__ __device__ constexpr int swz(int r) { return 4 * ((r >> 2) & 1) + 2 * ((r >> 1) & 1) + ((r >> 3) & 1); }
+
+__device__ __forceinline__ bf16x4 tr_read(const char *p) {
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p));
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float head_max(float v) {  // over lanes l, l^16, l^32, l^48
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+__device__ __forceinline__ float head_sum(float v) {
+  v += __shfl_xor(v, 16, 64);
+  return v + __shfl_xor(v, 32, 64);
+}
+
+// Softmax state of one 16-head block in one wave.  The probabilities of a split are taken against a
+// fixed reference mref (the first tile's maximum), so the accumulators are never rescaled inside
+// the loop; a later score more than 64 (in log2 units) above mref raises `redo`, and the split is
+// then computed again with mref = the exact maximum mrun, so nothing can overflow.
+struct SoftmaxState {
+  float mref = -INFINITY, mrun = -INFINITY, l = 0.f;
+  bool redo = false;
+};
+
+// Scores -> probabilities for one tile: masks keys >= k_end, updates the state and returns P^T as
+// the B operands of the two 32-key steps.
+__device__ __forceinline__ void softmax_tile(f32x4 (&S)[4], SoftmaxState &st, bool first, int s0, int k_end,
+                                             int g, float c, bf16x8 (&P)[2]) {
+  float v[16];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[4 * kb + j] = S[kb][j];
+  if (s0 + KT > k_end) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (s0 + 16 * (i >> 2) + 4 * g + (i & 3) >= k_end) v[i] = -INFINITY;
+  }
+  float mt = v[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mt = fmaxf(mt, v[i]);
+  mt = head_max(mt);
+  if (first) st.mref = mt;
+  st.mrun = fmaxf(st.mrun, mt);
+  st.redo |= (mt - st.mref) * c > 64.0f;
+  const float ms = st.mref * c;
+  float rs = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    v[i] = __builtin_amdgcn_exp2f(v[i] * c - ms);
+    rs += v[i];
+  }
+  st.l += rs;
+  // slot e of step ks <-> key 32 ks + 16 (e / 4) + 4 g + e % 4
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) P[ks][e] = (bf16_t)v[4 * (2 * ks + (e >> 2)) + (e & 3)];
+}
+
+template <bool SHARED>
+__global__ void __launch_bounds__(256, 1) latent_decode_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16_t C0[TILE];
+  __shared__ __attribute__((aligned(16))) bf16_t C1[TILE];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  const int b = blockIdx.y, sp = blockIdx.x;
+  const int p = a.pos[b];
+  const int lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
+  const int span = p + 1 - lo;
+  const int kps = ((span + a.splits - 1) / a.splits + KT - 1) / KT * KT;  // keys per split
+  const int k_begin = lo + sp * kps, k_end = min(p + 1, k_begin + kps);
+  const int ntiles = k_end > k_begin ? (k_end - k_begin + KT - 1) / KT : 0;
+  const int col = lane & 15, g = lane >> 4;
+  const int head = 16 * wave + col, head4 = 16 * MAX_WAVES + col;
+  const bool head_ok = head < a.n_heads, head4_ok = SHARED && head4 < a.n_heads;
+
+  // q~ fragments (B operand): Qf[kst] = dims 32 kst + 8 g .. + 7 of head `head`; Q4 of `head4`
+  bf16x8 Qf[NKST], Q4[SHARED ? NKST : 1];
+  {
+    const bf16_t *qb = a.qabs + (int64_t)b * a.n_heads * ROW + 8 * g;
+    const bf16_t *qp = qb + (int64_t)(head_ok ? head : 0) * ROW;
+#pragma unroll
+    for (int k = 0; k < NKST; ++k) {
+      Qf[k] = *(const bf16x8 *)(qp + 32 * k);
+      if (!head_ok) Qf[k] = bf16x8{};
+    }
+    if (SHARED) {
+      const bf16_t *q4 = qb + (int64_t)(head4_ok ? head4 : 0) * ROW;
+#pragma unroll
+      for (int k = 0; k < NKST; ++k) {
+        Q4[k] = *(const bf16x8 *)(q4 + 32 * k);
+        if (!head4_ok) Q4[k] = bf16x8{};
+      }
+    }
+  }
+
+  const bf16_t *cb = a.cache + (int64_t)b * a.max_len * ROW;
+  auto issue = [&](bf16_t *cs, int s0) {
+    // keys past k_end are clamped to k_end - 1 (masked below, and always inside the cache)
+    for (int j = wave; j < TILE_CH / 64; j += nwaves) {
+      const int sl = j * 64 + lane;
+      const int row = sl / RCH, c = (sl % RCH) ^ swz(row);
+      const int s = min(s0 + row, k_end - 1);
+      __builtin_amdgcn_global_load_lds(cb + (int64_t)s * ROW + c * 8, (lds_void *)(cs + j * 64 * 8), 16, 0, 0);
+    }
+  };
+
+  f32x4 O[NDB], O4[SHARED ? SH_DB : 1];
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) O[d] = f32x4{};
+#pragma unroll
+  for (int d = 0; d < (SHARED ? SH_DB : 1); ++d) O4[d] = f32x4{};
+  SoftmaxState st, st4;
+  int pass = 0;
+
+  // Lane-dependent byte offsets of the LDS reads; everything else is an immediate.
+  // S phase: row 16 kb + col, logical chunk 4 kst + g; swz(row) = swz(col) for every kb.
+  int offS[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) offS[q] = col * RB + (((4 * q + g) ^ swz(col)) * 16);
+  // PV phase: lane (g, jj, qq) of a transposing read addresses row 32 ks + 16 hi + 4 g + jj and dims
+  // 16 d + 4 qq .. + 3, i.e. logical chunk 2 d + (qq >> 1), half qq & 1; swz(row) = swz(4 g + jj).
+  const int jj = (lane & 15) >> 2, qq = lane & 3;
+  int offP[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = 4 * g + jj;
+    offP[q] = r * RB + (((2 * q + (qq >> 1)) ^ swz(r)) * 16) + (qq & 1) * 8;
+  }
+  // Dim blocks are visited in the order d = (dr + SH_DB * wave) mod NDB and O[dr] holds block d, so
+  // that the blocks dr < SH_DB are this wave's share of the shared head block (compile-time indices).
+  const int rot = 2 * wave;  // (SH_DB * wave) / 4
+
+  auto compute = [&](const bf16_t *cs, int s0) {
+    const char *cbyte = (const char *)cs;
+    f32x4 S[4], S4[4];
+    // S phase, software-pipelined one k-step ahead: [reads kst + 1][MFMAs kst]
+    bf16x8 af[2][4];
+    auto ldA = [&](bf16x8 (&f)[4], int kst) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        f[kb] = *(const bf16x8 *)(cbyte + offS[kst & 1] + kb * 16 * RB + (kst >> 1) * 128);
+    };
+    ldA(af[0], 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int kst = 0; kst < NKST; ++kst) {
+      if (kst + 1 < NKST) ldA(af[(kst + 1) & 1], kst + 1);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        S[kb] = mfma16(af[kst & 1][kb], Qf[kst], kst == 0 ? f32x4{} : S[kb]);
+        if (SHARED) S4[kb] = mfma16(af[kst & 1][kb], Q4[kst], kst == 0 ? f32x4{} : S4[kb]);
+      }
+      if (kst + 1 < NKST) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, SHARED ? 8 : 4, 0);
+    }
+    bf16x8 P[2], P4[2];
+    const bool first = pass == 0 && s0 == k_begin;
+    softmax_tile(S, st, first, s0, k_end, g, a.c, P);
+    if (SHARED) softmax_tile(S4, st4, first, s0, k_end, g, a.c, P4);
+    // PV phase, pipelined the same way: [reads of block dr + 1][MFMAs of block dr]
+    bf16x8 vf[2][2];
+    auto ldV = [&](bf16x8 (&f)[2], int dr) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const char *p0 = cbyte + offP[dr & 3] + ks * 32 * RB + ((((dr >> 2) + rot) & 7) * 128);
+        const bf16x4 lo4 = tr_read(p0);
+        const bf16x4 hi4 = tr_read(p0 + 16 * RB);
+        f[ks] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    };
+    ldV(vf[0], 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int dr = 0; dr < NDB; ++dr) {
+      if (dr + 1 < NDB) ldV(vf[(dr + 1) & 1], dr + 1);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        O[dr] = mfma16(vf[dr & 1][ks], P[ks], O[dr]);
+        if (SHARED && dr < SH_DB) O4[dr] = mfma16(vf[dr & 1][ks], P4[ks], O4[dr]);
+      }
+      if (dr + 1 < NDB) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      if (SHARED && dr < SH_DB) __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      else __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+  };
+
+  for (;;) {
+    if (ntiles > 0) issue(C0, k_begin);
+    __syncthreads();
+    for (int it = 0; it < ntiles; ++it) {
+      const int s0 = k_begin + it * KT;
+      if (it + 1 < ntiles) issue((it & 1) ? C0 : C1, s0 + KT);
+      compute((it & 1) ? C1 : C0, s0);
+      __syncthreads();
+    }
+    if (pass == 1 || !__syncthreads_or(st.redo || st4.redo)) break;
+    // second pass against the exact maximum (scores more than 2^64 above the first tile's maximum)
+    pass = 1;
+    st.mref = st.mrun;
+    st.l = 0.f;
+    st4.mref = st4.mrun;
+    st4.l = 0.f;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) O[d] = f32x4{};
+#pragma unroll
+    for (int d = 0; d < (SHARED ? SH_DB : 1); ++d) O4[d] = f32x4{};
+  }
+
+  const float lt = head_sum(st.l);
+  if (head_ok) {
+    const int64_t ph = ((int64_t)b * a.splits + sp) * a.n_heads + head;
+    if (g == 0) {
+      a.part_ml[ph * 2] = st.mref;
+      a.part_ml[ph * 2 + 1] = lt;
+    }
+    // O[dr][j] = O^T[dim 16 d + 4 g + j][head], d = (dr + SH_DB * wave) mod NDB
+    float *po = a.part_o + ph * DC + 4 * g;
+#pragma unroll
+    for (int dr = 0; dr < NDB; ++dr)
+      *(float4 *)(po + 16 * ((dr + SH_DB * wave) % NDB)) = make_float4(O[dr][0], O[dr][1], O[dr][2], O[dr][3]);
+  }
+  if (SHARED) {
+    const float lt4 = head_sum(st4.l);
+    if (head4_ok) {
+      const int64_t ph = ((int64_t)b * a.splits + sp) * a.n_heads + head4;
+      if (wave == 0 && g == 0) {
+        a.part_ml[ph * 2] = st4.mref;
+        a.part_ml[ph * 2 + 1] = lt4;
+      }
+      float *po = a.part_o + ph * DC + 4 * g + 16 * SH_DB * wave;
+#pragma unroll
+      for (int d = 0; d < SH_DB; ++d)
+        *(float4 *)(po + 16 * d) = make_float4(O4[d][0], O4[d][1], O4[d][2], O4[d][3]);
+    }
+  }
+}
+
+// o[b, h] = sum_sp exp2((m_sp - M) c) o_sp / sum_sp exp2((m_sp - M) c) l_sp, M = max_sp m_sp.
+__global__ void __launch_bounds__(128) merge_splits_kernel(const float *part_o, const float *part_ml, float *o,
+                                                         int32_t n_heads, int32_t splits, float c) {
+  const int bh = blockIdx.x;  // b * n_heads + h
+  const int b = bh / n_heads, h = bh % n_heads;
+  float M = -INFINITY;
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[(((int64_t)b * splits + s) * n_heads + h) * 2]);
+  float L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < splits; ++s) {
+    const int64_t ph = ((int64_t)b * splits + s) * n_heads + h;
+    const float ms = part_ml[ph * 2];
+    if (ms == -INFINITY) continue;  // empty split
+    const float w = __builtin_amdgcn_exp2f((ms - M) * c);
+    L += w * part_ml[ph * 2 + 1];
+    const float4 v = *(const float4 *)(part_o + ph * DC + 4 * threadIdx.x);
+    acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
+  }
+  const float inv = 1.0f / L;
+  *(float4 *)(o + (int64_t)bh * DC + 4 * threadIdx.x) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+}
+
+// Query rows that share one KV head.  Block (i, kv) takes rows i R .. i R + R - 1 of the list
+// (b, k) -> b * hk + k over sequences b and the hk heads k of kv (signal heads first).
+constexpr int R = 16;
+
+__device__ __forceinline__ int kv_heads(int kv, const LayerDims &d, int &ns) {
+  ns = kv < d.n_signal ? (d.n_signal - kv + d.n_kv - 1) / d.n_kv : 0;
+  const int nn = kv < d.n_noise ? (d.n_noise - kv + d.n_kv - 1) / d.n_kv : 0;
+  return ns + nn;
+}
+__device__ __forceinline__ int kv_head(int kv, int k, int ns, const LayerDims &d) {
+  return k < ns ? kv + d.n_kv * k : d.n_signal + kv + d.n_kv * (k - ns);
+}
+
+// q~ = [q^C_h W_uk[:, kv(h)]^T ; q^R_h] in bf16.  Each thread keeps one W_uk row slice (d_h values
+// of latent dimension c) in registers and applies it to the block's R query rows.
+__global__ void __launch_bounds__(256) absorb_kernel(const float *qc, const float *qr, const bf16_t *w_uk,
+                                                     bf16_t *qabs, int32_t B, LayerDims d) {
+  __shared__ __attribute__((aligned(16))) float qs[R][128];
+  __shared__ int64_t rowq[R];
+  const int kv = blockIdx.y, tid = threadIdx.x;
+  int ns;
+  const int hk = kv_heads(kv, d, ns);
+  const int r0 = blockIdx.x * R, nr = min(R, B * hk - r0);
+  if (nr <= 0) return;
+  if (tid < nr) {
+    const int L = r0 + tid, b = L / hk;
+    rowq[tid] = (int64_t)b * d.n_heads + kv_head(kv, L % hk, ns, d);
+  }
+  __syncthreads();
+  for (int i = tid; i < nr * 32; i += 256) {
+    const int r = i >> 5, e = (i & 31) * 4;
+    *(float4 *)&qs[r][e] = *(const float4 *)(qc + rowq[r] * 128 + e);
+  }
+  for (int i = tid; i < nr * DR; i += 256) {
+    const int r = i / DR, e = i % DR;
+    qabs[rowq[r] * ROW + DC + e] = (bf16_t)qr[rowq[r] * DR + e];
+  }
+  __syncthreads();
+  const int64_t ldw = (int64_t)d.n_kv * 128;
+  for (int c = tid; c < DC; c += 256) {
+    uint4 w[16];
+    const bf16_t *wr = w_uk + (int64_t)c * ldw + kv * 128;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i] = *(const uint4 *)(wr + 8 * i);
+    for (int r = 0; r < nr; ++r) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float4 qa = *(const float4 *)&qs[r][8 * i], qb = *(const float4 *)&qs[r][8 * i + 4];
+        const unsigned u[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+        acc = fmaf(qa.x, __uint_as_float(u[0] << 16), acc);
+        acc = fmaf(qa.y, __uint_as_float(u[0] & 0xffff0000u), acc);
+        acc = fmaf(qa.z, __uint_as_float(u[1] << 16), acc);
+        acc = fmaf(qa.w, __uint_as_float(u[1] & 0xffff0000u), acc);
+        acc = fmaf(qb.x, __uint_as_float(u[2] << 16), acc);
+        acc = fmaf(qb.y, __uint_as_float(u[2] & 0xffff0000u), acc);
+        acc = fmaf(qb.z, __uint_as_float(u[3] << 16), acc);
+        acc = fmaf(qb.w, __uint_as_float(u[3] & 0xffff0000u), acc);
+      }
+      qabs[rowq[r] * ROW + c] = (bf16_t)acc;
+    }
+  }
+}
+
+// H_h = o_h W_uv[:, kv(h)] in fp32, for the block's R rows.  Thread (half, e) sums latent
+// dimensions half * 256 .. + 255 for output column e; the two halves are added through LDS.
+__global__ void __launch_bounds__(256) unabsorb_kernel(const float *o, const bf16_t *w_uv, float *heads,
+                                                       int32_t B, LayerDims d) {
+  __shared__ __attribute__((aligned(16))) float os[R][DC];
+  __shared__ float red[R][128];
+  __shared__ int64_t rowq[R];
+  const int kv = blockIdx.y, tid = threadIdx.x;
+  int ns;
+  const int hk = kv_heads(kv, d, ns);
+  const int r0 = blockIdx.x * R, nr = min(R, B * hk - r0);
+  if (nr <= 0) return;
+  if (tid < nr) {
+    const int L = r0 + tid, b = L / hk;
+    rowq[tid] = (int64_t)b * d.n_heads + kv_head(kv, L % hk, ns, d);
+  }
+  __syncthreads();
+  for (int i = tid; i < nr * (DC / 4); i += 256) {
+    const int r = i / (DC / 4), c = (i % (DC / 4)) * 4;
+    *(float4 *)&os[r][c] = *(const float4 *)(o + rowq[r] * DC + c);
+  }
+  for (int i = nr * (DC / 4) + tid; i < R * (DC / 4); i += 256) {
+    const int r = i / (DC / 4), c = (i % (DC / 4)) * 4;
+    *(float4 *)&os[r][c] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  __syncthreads();
+  const int e = tid & 127, half = tid >> 7;
+  const int64_t ldw = (int64_t)d.n_kv * 128;
+  const bf16_t *wc = w_uv + kv * 128 + e;
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+  for (int c = half * 256; c < half * 256 + 256; c += 4) {
+    const float w0 = (float)wc[(int64_t)c * ldw], w1 = (float)wc[(int64_t)(c + 1) * ldw];
+    const float w2 = (float)wc[(int64_t)(c + 2) * ldw], w3 = (float)wc[(int64_t)(c + 3) * ldw];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float4 v = *(const float4 *)&os[r][c];
+      acc[r] = fmaf(v.x, w0, fmaf(v.y, w1, fmaf(v.z, w2, fmaf(v.w, w3, acc[r]))));
+    }
+  }
+  if (half) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) red[r][e] = acc[r];
+  }
+  __syncthreads();
+  if (!half) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (r < nr) heads[rowq[r] * 128 + e] = acc[r] + red[r][e];
+  }
+}
+
+}  // namespace
+
+bool fast_decode_supported(const LayerDims &d, gdla_dtype dt) {
+  return dt == GDLA_BF16 && d.d_c == DC && d.d_r == DR && d.d_h == 128 && d.n_heads <= MAX_HEADS;
+}
+
+int32_t fast_decode_splits(int32_t B, int32_t max_len) {
+  // about one workgroup per CU (256 CUs), at least 1024 keys per split
+  const int32_t by_cu = (256 + B - 1) / B;
+  const int32_t by_len = std::max(1, max_len / 1024);
+  return std::max(1, std::min(by_cu, by_len));
+}
+
+gdla_status run_fast_decode(const LayerDims &d, const gdla_weights *w, int32_t B, const int32_t *pos_dev,
+                            const int32_t *pos_host, void *cache, int32_t max_len, const float *qc,
+                            const float *qr, float *heads, const FastDecodeLayout &L, void *ws, hipStream_t s,
+                            StageEvents &se) {
+  (void)pos_host;
+  bf16_t *qabs = (bf16_t *)((char *)ws + L.qabs);
+  float *part_o = (float *)((char *)ws + L.part_o);
+  float *part_ml = (float *)((char *)ws + L.part_ml);
+  float *o = (float *)((char *)ws + L.o);
+  const int hk_max = (d.n_signal + d.n_kv - 1) / d.n_kv + (d.n_noise + d.n_kv - 1) / d.n_kv;
+  const dim3 gk((unsigned)((B * hk_max + R - 1) / R), (unsigned)d.n_kv);
+  se.begin(GDLA_STAGE_ATTN_NOISE);
+  hipLaunchKernelGGL(absorb_kernel, gk, dim3(256), 0, s, qc, qr, (const bf16_t *)w->w_uk, qabs, B, d);
+  if (hipGetLastError() != hipSuccess) return GDLA_ERR_HIP;
+  DecodeArgs a{};
+  a.qabs = qabs; a.cache = (const bf16_t *)cache; a.pos = pos_dev; a.part_o = part_o; a.part_ml = part_ml;
+  const int nblk = (d.n_heads + 15) / 16;
+  a.n_heads = d.n_heads; a.max_len = max_len; a.window = d.window; a.splits = L.splits;
+  a.c = d.scale * 1.4426950408889634f;
+  if (nblk > MAX_WAVES)
+    hipLaunchKernelGGL(latent_decode_kernel<true>, dim3(L.splits, B), dim3(64 * MAX_WAVES), 0, s, a);
+  else
+    hipLaunchKernelGGL(latent_decode_kernel<false>, dim3(L.splits, B), dim3(64 * nblk), 0, s, a);
+  if (hipGetLastError() != hipSuccess) return GDLA_ERR_HIP;
+  hipLaunchKernelGGL(merge_splits_kernel, dim3(B * d.n_heads), dim3(128), 0, s, part_o, part_ml, o, d.n_heads,
+                     L.splits, a.c);
+  if (hipGetLastError() != hipSuccess) return GDLA_ERR_HIP;
+  se.end(GDLA_STAGE_ATTN_NOISE);
+  se.begin(GDLA_STAGE_ATTN_SIGNAL);
+  hipLaunchKernelGGL(unabsorb_kernel, gk, dim3(256), 0, s, o, (const bf16_t *)w->w_uv, heads, B, d);
+  if (hipGetLastError() != hipSuccess) return GDLA_ERR_HIP;
+  return GDLA_OK;
+}
+
+}  // namespace gdla

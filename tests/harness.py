@@ -18,6 +18,12 @@ SMALL_BF16 = dict(d_model=256, n_heads=10, n_signal=8, n_noise=2, n_kv=2, d_q_la
                   window=0, dtype="bf16", seed=7)
 
 
+# The widest fast-path head layouts: five blocks of 16 heads (the fifth shared by all waves) and
+# a partly filled fifth block.
+BF80 = dict(SMALL_BF16, n_heads=80, n_signal=64, n_noise=16, n_kv=16)
+BF72 = dict(SMALL_BF16, n_heads=72, n_signal=64, n_noise=8, n_kv=4)
+
+
 def to_np(t):
     return t.detach().to("cpu", torch.float64).numpy()
 
@@ -96,11 +102,14 @@ def prefill_case(cfg, seq, p0, window=0, seed=None, random_gamma=True, lam_zero=
             "exp_heads": np.stack(exp_heads), "inp": inp, "dev": dev, "dims": dims}
 
 
-def decode_case(cfg, p0, seed=None, random_gamma=True, want_heads=False):
-    """One decode step per sequence (token b at position p0[b]) on GPU and in the oracle."""
+def decode_case(cfg, p0, seed=None, random_gamma=True, want_heads=False, prep=None):
+    """One decode step per sequence (token b at position p0[b]) on GPU and in the oracle.
+    `prep(inp)` may rewrite the CPU inputs (e.g. the cache prefix) before both sides see them."""
     batch = len(p0)
     inp = synth.make_inputs(cfg, "cpu", seed=seed, batch=batch, seq=1, p0=p0,
                             random_gamma=random_gamma)
+    if prep is not None:
+        prep(inp)
     dev = device_inputs(inp)
     dims = gd.make_dims(cfg, window=cfg.get("window", 0))
     heads = None

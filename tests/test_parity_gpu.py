@@ -71,6 +71,59 @@ def test_bf16_heads_debug_output():
     _say(H.check(r["heads"], r["exp_heads"], "bf16", "bf16 per-head H"))
 
 
+@pytest.mark.parametrize("cfg,p0", [
+    (H.BF80, [0, 700, 2047]), (H.BF72, [3000, 5]), (dict(H.BF80, window=1000), [2500, 40, 999]),
+    (dict(H.BF72, window=64), [63, 64, 1300]),
+], ids=["80h", "72h", "80h-window", "72h-window64"])
+def test_bf16_decode_wide(cfg, p0):
+    r = H.decode_case(cfg, p0, seed=23, want_heads=True)
+    _say(H.check(r["out"], r["exp_out"], "bf16", f"bf16 decode {cfg['n_heads']} heads p0={p0}"))
+    _say(H.check(r["heads"], r["exp_heads"], "bf16", "per-head H"))
+
+
+def _max_logit_log2(inp, cfg, b, keys):
+    """Largest scaled score (log2 units) of any head of sequence b over the given cache rows."""
+    w = H.oracle_weights(inp)
+    od = H.oracle_dims(cfg, cfg.get("window", 0))
+    p = inp["p0"][b]
+    _, q_c, q_r, _ = oracle.gdla_ref.query_path(H.to_np(inp["x"][b:b + 1, 0]), w, od, np.array([p]))
+    rows = H.to_np(inp["cache"][b, keys])
+    d_c = cfg["d_kv_latent"]
+    best = -np.inf
+    for h in range(cfg["n_heads"]):
+        kv = oracle.gdla_ref.kv_head_of(h, od)
+        w_uk = w["w_uk"][:, kv * cfg["d_head"]:(kv + 1) * cfg["d_head"]]
+        s = rows[:, :d_c] @ (w_uk @ q_c[0, h]) + rows[:, d_c:] @ q_r[0, h]
+        best = max(best, float(np.max(s)) * od.scale / np.log(2.0))
+    return best
+
+
+def test_bf16_decode_score_jump_recomputes_split():
+    """Keys far above the first tile's maximum (more than 2^64 in probability) force the
+    second pass against the exact maximum; the result must still match the oracle.  The later
+    keys all repeat one row, so their scores tie and bf16 rounding cannot tip the balance, and
+    only its k^R part is scaled up, which raises the scores but leaves the values (cbar) alone."""
+    p0 = 900  # one key split
+    d_c = H.BF80["d_kv_latent"]
+
+    def prep(inp):
+        cache = inp["cache"]
+        cache[0, :64] = 0  # first tile: every score exactly 0
+        row = cache[0, 64].clone().double()
+        for _ in range(4):  # scale k^R until some head scores about 80 (log2 units)
+            cache[0, 64] = row.to(cache.dtype)
+            top = _max_logit_log2(inp, H.BF80, 0, slice(64, 65))
+            if top > 75.0:
+                break
+            row[d_c:] *= max(2.0, 80.0 / max(top, 0.5))
+        cache[0, 64:p0] = row.to(cache.dtype)
+        assert _max_logit_log2(inp, H.BF80, 0, slice(64, 65)) > 70.0
+
+    r = H.decode_case(H.BF80, [p0], seed=29, prep=prep)
+    assert np.all(np.isfinite(r["out"]))
+    _say(H.check(r["out"], r["exp_out"], "bf16", "bf16 decode after a score jump"))
+
+
 @pytest.mark.parametrize("p0", [[0, 1, 300, 1000], [4095]])
 def test_bf16_decode(p0):
     r = H.decode_case(BF, p0, want_heads=True)
