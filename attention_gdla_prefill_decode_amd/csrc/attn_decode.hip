@@ -21,10 +21,12 @@
 //   per-head online softmax (lanes l, l^16, l^32, l^48 hold one head), lazy rescaling,
 //   O^T[dim, head] += cbar^T[dim, key] . P^T[key, head]    (A = cbar^T by ds_read_b64_tr_b16,
 //                                                           B = P^T straight from the S registers)
-// Rows are unpadded; chunk c of row r sits at c ^ f(r) with f(r) = 4 r_2 + 2 r_1 + r_3 (r_i = bit i
-// of r): the 16-byte row reads (16 consecutive rows, one chunk) and the transposing reads (8
-// consecutive rows, 2 aligned chunks) then both hit distinct groups of 4 banks.
-// Each split writes its unnormalised O, its reference max m and sum l; merge_splits combines them.
+// Rows are unpadded; chunk c of row r sits at c ^ f(r) with f(r) = 4 r_1 + 2 (r_0 ^ r_2) +
+// (r_0 ^ r_3) (r_i = bit i of r).  The 16-byte row reads (consecutive rows, one chunk) and the
+// transposing reads (4 consecutive rows, an aligned pair of chunks) then hit distinct banks whether
+// the LDS serves 32 or 64 banks of 4 bytes per clock.
+// Each split writes its unnormalised O, its reference m (log2 units) and sum l; merge_splits
+// combines them.
 #include "fast_paths.h"
 
 #include <algorithm>
@@ -42,12 +44,14 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int DC = 512, DR = 64, ROW = DC + DR;
 constexpr int RB = ROW * 2;        // bytes per cache row
 constexpr int RCH = ROW / 8;       // 72 chunks per cache row
-constexpr int KT = 64;             // keys per tile
+constexpr int KT = 32;             // keys per tile
+constexpr int NBUF = 4;            // LDS ring of tiles: three in flight while one is consumed
 constexpr int TILE = KT * ROW;     // elements per tile
-constexpr int TILE_CH = KT * RCH;  // chunks per tile (4608 = 72 wave-instructions)
+constexpr int TILE_CH = KT * RCH;  // chunks per tile (2304 = 36 wave-instructions)
 constexpr int NKST = ROW / 32;     // 18 k-steps of 32 in S
 constexpr int NDB = DC / 16;       // 32 dim blocks of 16 in O^T
-constexpr int MAX_WAVES = 4;
+constexpr int MAX_WAVES = 4;      // always launched: one wave per SIMD
+constexpr int DMA_PER_WAVE = TILE_CH / 64 / MAX_WAVES;  // 16-byte loads per lane and tile (9)
 constexpr int MAX_HEADS = 16 * (MAX_WAVES + 1);
 constexpr int SH_DB = NDB / MAX_WAVES;  // dim blocks of the shared head block per wave (8)
 
@@ -61,7 +65,9 @@ struct DecodeArgs {
   float c;             // softmax scale * log2(e)
 };
 
-__host__ __device__ constexpr int swz(int r) { return 4 * ((r >> 2) & 1) + 2 * ((r >> 1) & 1) + ((r >> 3) & 1); }
+__host__ __device__ constexpr int swz(int r) {
+  return 4 * ((r >> 1) & 1) + 2 * ((r & 1) ^ ((r >> 2) & 1)) + ((r & 1) ^ ((r >> 3) & 1));
+}
 
 __device__ __forceinline__ bf16x4 tr_read(const char *p) {
   return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p));
@@ -81,56 +87,59 @@ __device__ __forceinline__ float head_sum(float v) {
 }
 
 // Softmax state of one 16-head block in one wave.  The probabilities of a split are taken against a
-// fixed reference mref (the first tile's maximum), so the accumulators are never rescaled inside
-// the loop; a later score more than 64 (in log2 units) above mref raises `redo`, and the split is
-// then computed again with mref = the exact maximum mrun, so nothing can overflow.
+// fixed reference mref = 0 (scores in log2 units), so the accumulators are never rescaled and the
+// tile loop needs no cross-lane reduction.  A score more than 64 above the reference (overflow
+// risk), or a split whose maximum stays more than 64 below it (underflow risk), raises `redo`, and
+// the split is then computed again against its exact maximum, so neither can happen.  mrun and l
+// are kept per lane (each lane sees a quarter of the keys of its head) and reduced over the 4 lanes
+// of a head at the end.
 struct SoftmaxState {
-  float mref = -INFINITY, mrun = -INFINITY, l = 0.f;
+  float mref = 0.f, mrun = -INFINITY, l = 0.f;
   bool redo = false;
 };
 
-// Scores -> probabilities for one tile: masks keys >= k_end, updates the state and returns P^T as
-// the B operands of the two 32-key steps.
-__device__ __forceinline__ void softmax_tile(f32x4 (&S)[4], SoftmaxState &st, bool first, int s0, int k_end,
-                                             int g, float c, bf16x8 (&P)[2]) {
-  float v[16];
+// Scores -> probabilities for one tile (score of key s0 + 16 kb + 4 g + j in S[kb][j]); `lim` =
+// k_end - s0 - 4 g masks the keys past the split.  Returns P^T as the B operand of the 32-key step
+// (slot e <-> key 16 (e / 4) + 4 g + e % 4).  Branch-free, so it stays in the MFMA block.
+__device__ __forceinline__ void softmax_tile(f32x4 (&S)[2], SoftmaxState &st, int lim, float c, bf16x8 &P) {
+  float v[8];
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v[4 * kb + j] = S[kb][j];
-  if (s0 + KT > k_end) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (s0 + 16 * (i >> 2) + 4 * g + (i & 3) >= k_end) v[i] = -INFINITY;
+  for (int i = 0; i < 8; ++i) {
+    const int kidx = 16 * (i >> 2) + (i & 3);
+    v[i] = kidx < lim ? S[i >> 2][i & 3] * c : -INFINITY;
   }
   float mt = v[0];
 #pragma unroll
-  for (int i = 1; i < 16; ++i) mt = fmaxf(mt, v[i]);
-  mt = head_max(mt);
-  if (first) st.mref = mt;
+  for (int i = 1; i < 8; ++i) mt = fmaxf(mt, v[i]);
   st.mrun = fmaxf(st.mrun, mt);
-  st.redo |= (mt - st.mref) * c > 64.0f;
-  const float ms = st.mref * c;
-  float rs = 0.f;
+  st.redo |= mt - st.mref > 64.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    v[i] = __builtin_amdgcn_exp2f(v[i] * c - ms);
-    rs += v[i];
+  for (int i = 0; i < 8; ++i) {
+    v[i] = __builtin_amdgcn_exp2f(v[i] - st.mref);
+    st.l += v[i];
+    P[i] = (bf16_t)v[i];
   }
-  st.l += rs;
-  // slot e of step ks <-> key 32 ks + 16 (e / 4) + 4 g + e % 4
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) P[ks][e] = (bf16_t)v[4 * (2 * ks + (e >> 2)) + (e & 3)];
+}
+
+// 16 bytes global -> LDS (M0 + 16 lane) without the compiler's LDS-DMA tracking: the waits for
+// these loads are explicit (s_waitcnt vmcnt before the barrier that publishes a tile).  M0 is set
+// right before the load (one wait state between them); nothing else in the kernel uses M0.
+__device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(lds_addr)
+               : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
 
 template <bool SHARED>
 __global__ void __launch_bounds__(256, 1) latent_decode_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t C0[TILE];
-  __shared__ __attribute__((aligned(16))) bf16_t C1[TILE];
+  __shared__ __attribute__((aligned(16))) bf16_t CB[NBUF * TILE];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = blockIdx.y, sp = blockIdx.x;
   const int p = a.pos[b];
   const int lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
@@ -163,13 +172,32 @@ __global__ void __launch_bounds__(256, 1) latent_decode_kernel(DecodeArgs a) {
   }
 
   const bf16_t *cb = a.cache + (int64_t)b * a.max_len * ROW;
-  auto issue = [&](bf16_t *cs, int s0) {
-    // keys past k_end are clamped to k_end - 1 (masked below, and always inside the cache)
-    for (int j = wave; j < TILE_CH / 64; j += nwaves) {
-      const int sl = j * 64 + lane;
-      const int row = sl / RCH, c = (sl % RCH) ^ swz(row);
-      const int s = min(s0 + row, k_end - 1);
-      __builtin_amdgcn_global_load_lds(cb + (int64_t)s * ROW + c * 8, (lds_void *)(cs + j * 64 * 8), 16, 0, 0);
+  // Tile t goes to ring slot t % NBUF; wave w issues wave-instructions w, w + 4, ... of the tile
+  // (DMA_PER_WAVE of them).  rowoff[i] is this lane's source offset (bytes) inside the tile.
+  // Keys past k_end are clamped to k_end - 1 (masked later, and always inside the cache).
+  const uint32_t ring = lds_u32(CB);
+  int rowoff[DMA_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < DMA_PER_WAVE; ++i) {
+    const int sl = (wave + MAX_WAVES * i) * 64 + lane;
+    const int row = sl / RCH;
+    rowoff[i] = row * RB + (((sl % RCH) ^ swz(row)) * 16);
+  }
+  auto issue = [&](int t) {
+    const int s0 = k_begin + t * KT;
+    const uint32_t base = ring + (uint32_t)((t % NBUF) * TILE * 2) + wave * 1024;
+    const char *src = (const char *)(cb + (int64_t)s0 * ROW);
+    if (s0 + KT <= k_end) {
+#pragma unroll
+      for (int i = 0; i < DMA_PER_WAVE; ++i)
+        dma16(src + rowoff[i], __builtin_amdgcn_readfirstlane(base + i * MAX_WAVES * 1024));
+    } else {
+#pragma unroll
+      for (int i = 0; i < DMA_PER_WAVE; ++i) {
+        const int row = rowoff[i] / RB;
+        const int off = rowoff[i] - row * RB + (min(s0 + row, k_end - 1) - s0) * RB;
+        dma16(src + off, __builtin_amdgcn_readfirstlane(base + i * MAX_WAVES * 1024));
+      }
     }
   };
 
@@ -201,69 +229,76 @@ __global__ void __launch_bounds__(256, 1) latent_decode_kernel(DecodeArgs a) {
 
   auto compute = [&](const bf16_t *cs, int s0) {
     const char *cbyte = (const char *)cs;
-    f32x4 S[4], S4[4];
-    // S phase, software-pipelined one k-step ahead: [reads kst + 1][MFMAs kst]
-    bf16x8 af[2][4];
-    auto ldA = [&](bf16x8 (&f)[4], int kst) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        f[kb] = *(const bf16x8 *)(cbyte + offS[kst & 1] + kb * 16 * RB + (kst >> 1) * 128);
+    f32x4 S[2], S4[2];
+    // S phase, key block by key block, software-pipelined two k-steps ahead:
+    // [reads of step n + 2][MFMAs of step n]; the own and the shared block use the same fragment
+    bf16x8 af[3];
+    auto ldA = [&](bf16x8 &f, int n) {  // n = 18 kb + kst
+      const int kb = n / NKST, kst = n % NKST;
+      f = *(const bf16x8 *)(cbyte + offS[kst & 1] + kb * 16 * RB + (kst >> 1) * 128);
     };
     ldA(af[0], 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    ldA(af[1], 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-    for (int kst = 0; kst < NKST; ++kst) {
-      if (kst + 1 < NKST) ldA(af[(kst + 1) & 1], kst + 1);
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        S[kb] = mfma16(af[kst & 1][kb], Qf[kst], kst == 0 ? f32x4{} : S[kb]);
-        if (SHARED) S4[kb] = mfma16(af[kst & 1][kb], Q4[kst], kst == 0 ? f32x4{} : S4[kb]);
-      }
-      if (kst + 1 < NKST) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, SHARED ? 8 : 4, 0);
+    for (int n = 0; n < 2 * NKST; ++n) {
+      const int kb = n / NKST, kst = n % NKST;
+      if (n + 2 < 2 * NKST) ldA(af[(n + 2) % 3], n + 2);
+      S[kb] = mfma16(af[n % 3], Qf[kst], kst == 0 ? f32x4{} : S[kb]);
+      if (SHARED) S4[kb] = mfma16(af[n % 3], Q4[kst], kst == 0 ? f32x4{} : S4[kb]);
+      if (n + 2 < 2 * NKST) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, SHARED ? 2 : 1, 0);
     }
-    bf16x8 P[2], P4[2];
-    const bool first = pass == 0 && s0 == k_begin;
-    softmax_tile(S, st, first, s0, k_end, g, a.c, P);
-    if (SHARED) softmax_tile(S4, st4, first, s0, k_end, g, a.c, P4);
-    // PV phase, pipelined the same way: [reads of block dr + 1][MFMAs of block dr]
-    bf16x8 vf[2][2];
-    auto ldV = [&](bf16x8 (&f)[2], int dr) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const char *p0 = cbyte + offP[dr & 3] + ks * 32 * RB + ((((dr >> 2) + rot) & 7) * 128);
-        const bf16x4 lo4 = tr_read(p0);
-        const bf16x4 hi4 = tr_read(p0 + 16 * RB);
-        f[ks] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
+    bf16x8 P, P4;
+    const int lim = k_end - s0 - 4 * g;
+    softmax_tile(S, st, lim, a.c, P);
+    if (SHARED) softmax_tile(S4, st4, lim, a.c, P4);
+    // PV phase, pipelined two dim blocks ahead: [reads of block dr + 2][MFMAs of block dr]
+    bf16x8 vf[3];
+    auto ldV = [&](bf16x8 &f, int dr) {
+      const char *p0 = cbyte + offP[dr & 3] + ((((dr >> 2) + rot) & 7) * 128);
+      const bf16x4 lo4 = tr_read(p0);
+      const bf16x4 hi4 = tr_read(p0 + 16 * RB);
+      f = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
     };
     ldV(vf[0], 0);
+    ldV(vf[1], 1);
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int dr = 0; dr < NDB; ++dr) {
-      if (dr + 1 < NDB) ldV(vf[(dr + 1) & 1], dr + 1);
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        O[dr] = mfma16(vf[dr & 1][ks], P[ks], O[dr]);
-        if (SHARED && dr < SH_DB) O4[dr] = mfma16(vf[dr & 1][ks], P4[ks], O4[dr]);
-      }
-      if (dr + 1 < NDB) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-      if (SHARED && dr < SH_DB) __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      else __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (dr + 2 < NDB) ldV(vf[(dr + 2) % 3], dr + 2);
+      O[dr] = mfma16(vf[dr % 3], P, O[dr]);
+      if (SHARED && dr < SH_DB) O4[dr] = mfma16(vf[dr % 3], P4, O4[dr]);
+      if (dr + 2 < NDB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if (SHARED && dr < SH_DB) __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      else __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
   };
 
+  // vmcnt(n): at most n of this wave's loads still in flight (n = 0, one tile, two tiles)
+  auto wait_tiles_after = [&](int n_after) {
+    if (n_after >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DMA_PER_WAVE) : "memory");
+    else if (n_after == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_PER_WAVE) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
   for (;;) {
-    if (ntiles > 0) issue(C0, k_begin);
+    for (int t = 0; t < NBUF - 1 && t < ntiles; ++t) issue(t);
+    for (int t = 0; t < ntiles; ++t) {
+      wait_tiles_after(min(ntiles - 1 - t, NBUF - 2));
+      __syncthreads();  // tile t has landed for every wave; every wave is done with tile t - 1
+      if (t + NBUF - 1 < ntiles) issue(t + NBUF - 1);
+      compute(CB + (t % NBUF) * TILE, k_begin + t * KT);
+    }
     __syncthreads();
-    for (int it = 0; it < ntiles; ++it) {
-      const int s0 = k_begin + it * KT;
-      if (it + 1 < ntiles) issue((it & 1) ? C0 : C1, s0 + KT);
-      compute((it & 1) ? C1 : C0, s0);
-      __syncthreads();
+    // reduce the per-lane maxima over the 4 lanes of each head; check for underflow
+    st.mrun = head_max(st.mrun);
+    st.redo |= ntiles > 0 && st.mrun - st.mref < -64.0f;
+    if (SHARED) {
+      st4.mrun = head_max(st4.mrun);
+      st4.redo |= ntiles > 0 && st4.mrun - st4.mref < -64.0f;
     }
     if (pass == 1 || !__syncthreads_or(st.redo || st4.redo)) break;
-    // second pass against the exact maximum (scores more than 2^64 above the first tile's maximum)
+    // second pass against the exact maximum
     pass = 1;
     st.mref = st.mrun;
     st.l = 0.f;
@@ -279,7 +314,7 @@ __global__ void __launch_bounds__(256, 1) latent_decode_kernel(DecodeArgs a) {
   if (head_ok) {
     const int64_t ph = ((int64_t)b * a.splits + sp) * a.n_heads + head;
     if (g == 0) {
-      a.part_ml[ph * 2] = st.mref;
+      a.part_ml[ph * 2] = ntiles > 0 ? st.mref : -INFINITY;
       a.part_ml[ph * 2 + 1] = lt;
     }
     // O[dr][j] = O^T[dim 16 d + 4 g + j][head], d = (dr + SH_DB * wave) mod NDB
@@ -293,7 +328,7 @@ __global__ void __launch_bounds__(256, 1) latent_decode_kernel(DecodeArgs a) {
     if (head4_ok) {
       const int64_t ph = ((int64_t)b * a.splits + sp) * a.n_heads + head4;
       if (wave == 0 && g == 0) {
-        a.part_ml[ph * 2] = st4.mref;
+        a.part_ml[ph * 2] = ntiles > 0 ? st4.mref : -INFINITY;
         a.part_ml[ph * 2 + 1] = lt4;
       }
       float *po = a.part_o + ph * DC + 4 * g + 16 * SH_DB * wave;
@@ -304,9 +339,10 @@ __global__ void __launch_bounds__(256, 1) latent_decode_kernel(DecodeArgs a) {
   }
 }
 
-// o[b, h] = sum_sp exp2((m_sp - M) c) o_sp / sum_sp exp2((m_sp - M) c) l_sp, M = max_sp m_sp.
+// o[b, h] = sum_sp 2^(m_sp - M) o_sp / sum_sp 2^(m_sp - M) l_sp, M = max_sp m_sp (each split's
+// reference in log2 units; -inf marks an empty split).
 __global__ void __launch_bounds__(128) merge_splits_kernel(const float *part_o, const float *part_ml, float *o,
-                                                         int32_t n_heads, int32_t splits, float c) {
+                                                         int32_t n_heads, int32_t splits) {
   const int bh = blockIdx.x;  // b * n_heads + h
   const int b = bh / n_heads, h = bh % n_heads;
   float M = -INFINITY;
@@ -317,7 +353,7 @@ __global__ void __launch_bounds__(128) merge_splits_kernel(const float *part_o, 
     const int64_t ph = ((int64_t)b * splits + s) * n_heads + h;
     const float ms = part_ml[ph * 2];
     if (ms == -INFINITY) continue;  // empty split
-    const float w = __builtin_amdgcn_exp2f((ms - M) * c);
+    const float w = __builtin_amdgcn_exp2f(ms - M);
     L += w * part_ml[ph * 2 + 1];
     const float4 v = *(const float4 *)(part_o + ph * DC + 4 * threadIdx.x);
     acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
@@ -467,24 +503,25 @@ gdla_status run_fast_decode(const LayerDims &d, const gdla_weights *w, int32_t B
   float *o = (float *)((char *)ws + L.o);
   const int hk_max = (d.n_signal + d.n_kv - 1) / d.n_kv + (d.n_noise + d.n_kv - 1) / d.n_kv;
   const dim3 gk((unsigned)((B * hk_max + R - 1) / R), (unsigned)d.n_kv);
-  se.begin(GDLA_STAGE_ATTN_NOISE);
   hipLaunchKernelGGL(absorb_kernel, gk, dim3(256), 0, s, qc, qr, (const bf16_t *)w->w_uk, qabs, B, d);
   if (hipGetLastError() != hipSuccess) return GDLA_ERR_HIP;
+  se.end(GDLA_STAGE_PROJ_Q);
   DecodeArgs a{};
   a.qabs = qabs; a.cache = (const bf16_t *)cache; a.pos = pos_dev; a.part_o = part_o; a.part_ml = part_ml;
   const int nblk = (d.n_heads + 15) / 16;
   a.n_heads = d.n_heads; a.max_len = max_len; a.window = d.window; a.splits = L.splits;
   a.c = d.scale * 1.4426950408889634f;
+  se.begin(GDLA_STAGE_ATTN_NOISE);
   if (nblk > MAX_WAVES)
     hipLaunchKernelGGL(latent_decode_kernel<true>, dim3(L.splits, B), dim3(64 * MAX_WAVES), 0, s, a);
   else
-    hipLaunchKernelGGL(latent_decode_kernel<false>, dim3(L.splits, B), dim3(64 * nblk), 0, s, a);
-  if (hipGetLastError() != hipSuccess) return GDLA_ERR_HIP;
-  hipLaunchKernelGGL(merge_splits_kernel, dim3(B * d.n_heads), dim3(128), 0, s, part_o, part_ml, o, d.n_heads,
-                     L.splits, a.c);
+    hipLaunchKernelGGL(latent_decode_kernel<false>, dim3(L.splits, B), dim3(64 * MAX_WAVES), 0, s, a);
   if (hipGetLastError() != hipSuccess) return GDLA_ERR_HIP;
   se.end(GDLA_STAGE_ATTN_NOISE);
   se.begin(GDLA_STAGE_ATTN_SIGNAL);
+  hipLaunchKernelGGL(merge_splits_kernel, dim3(B * d.n_heads), dim3(128), 0, s, part_o, part_ml, o, d.n_heads,
+                     L.splits);
+  if (hipGetLastError() != hipSuccess) return GDLA_ERR_HIP;
   hipLaunchKernelGGL(unabsorb_kernel, gk, dim3(256), 0, s, o, (const bf16_t *)w->w_uv, heads, B, d);
   if (hipGetLastError() != hipSuccess) return GDLA_ERR_HIP;
   return GDLA_OK;

@@ -473,12 +473,13 @@ GDLA_EXPORT gdla_status gdla_decode(const gdla_dims *dims, const gdla_weights *w
   HIP_TRY(launch_gemm(g, dt, stream));
   HIP_TRY(launch_rope_heads(at<float>(ws, L.qrp), at<float>(ws, L.qr), (int64_t)d.n_heads * d.d_r, d.d_r, 0,
                             B, 1, d.n_heads, d.d_r, pos_dev, d.theta, DT::F32, stream));
-  se.end(GDLA_STAGE_PROJ_Q);
   if (L.use_fast) {
+    // ends GDLA_STAGE_PROJ_Q after the absorbed query; leaves GDLA_STAGE_ATTN_SIGNAL open
     st = run_fast_decode(d, w, B, pos_dev, pos_host, cache, max_len, at<float>(ws, L.qc),
                          at<float>(ws, L.qr), at<float>(ws, L.heads), L.fast, ws, stream, se);
     if (st != GDLA_OK) return fail(st, "fast decode path failed: %s", hipGetErrorString(hipGetLastError()));
   } else {
+    se.end(GDLA_STAGE_PROJ_Q);
     se.begin(GDLA_STAGE_ATTN_NOISE);
     HIP_TRY(launch_absorb_generic(at<float>(ws, L.qc), at<float>(ws, L.qr), w->w_uk, at<float>(ws, L.qabs),
                                   B, d, dt, stream));

@@ -61,9 +61,9 @@ struct StageEvents {
   hipEvent_t *ev = nullptr;
   hipStream_t s = nullptr;
   unsigned done = 0;
-  void begin(int k) { if (ev) hipEventRecord(ev[2 * k], s); }
+  void begin(int k) { if (ev) (void)hipEventRecord(ev[2 * k], s); }
   void end(int k) {
-    if (ev) { hipEventRecord(ev[2 * k + 1], s); done |= 1u << k; }
+    if (ev) { (void)hipEventRecord(ev[2 * k + 1], s); done |= 1u << k; }
   }
   void finish() {
     if (!ev) return;

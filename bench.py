@@ -127,16 +127,25 @@ def bench_decode(steps, warmup):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    attn_ms = 0.0
+    stages = {k: 0.0 for k in gd.STAGES}
     for tm in timers:
-        st = tm.elapsed()
-        attn_ms += st["attn_noise"] + st["attn_signal"]
-    cache_bytes = len(pos) * cfg["max_len"] * (cfg["d_kv_latent"] + cfg["d_rope"]) * 2
-    return {"workload": "decode_64x64k", "ms_per_step": round(ms, 4),
-            "latent_cache_GBps_whole_step": round(cache_bytes / ms / 1e6, 1),
-            "attention_ms": round(attn_ms / steps, 4),
-            "latent_cache_GBps_attention": round(cache_bytes / (attn_ms / steps) / 1e6, 1),
-            "frac_hbm_attention": round(cache_bytes / (attn_ms / steps) / 1e6 / PEAK_HBM_GBS, 4)}
+        for k, v in tm.elapsed().items():
+            stages[k] += v / steps
+    # Algorithmic bytes of the latent-attention kernel: every visible cache row once, the absorbed
+    # query of every head (bf16) and the attended latent o of every head (fp32).
+    keys = sum(min(p + 1, cfg["window"]) if cfg["window"] > 0 else p + 1 for p in pos)
+    row = cfg["d_kv_latent"] + cfg["d_rope"]
+    nbytes = keys * row * 2 + len(pos) * cfg["n_heads"] * (row * 2 + cfg["d_kv_latent"] * 4)
+    kern_ms = stages["attn_noise"]
+    gbs = nbytes / kern_ms / 1e6
+    return {"workload": "decode_64x64k", "batch": len(pos), "context": int(pos[0]) + 1,
+            "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(len(pos) / ms * 1e3, 1),
+            "roofline": {"kernel": "latent_decode_kernel<shared>", "bound": "hbm",
+                         "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": nbytes,
+                         "avg_launch_ms": round(kern_ms, 4)},
+            "stages_ms": {k: round(v, 4) for k, v in stages.items()}}
 
 
 def main():
@@ -145,6 +154,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode", action="store_true", help="also time the 64 x 64K decode workload")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only the 64 x 64K decode workload (prints its JSON object)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -155,6 +166,10 @@ def main():
     import torch
     import synth
     import attention_gdla_prefill_decode_amd as gd
+
+    if args.decode_only:
+        print(json.dumps(bench_decode(args.steps, args.warmup)), flush=True)
+        return
 
     cfg = synth.WORKLOADS["prefill_8k"]
     t, p0 = cfg["seq"], cfg["p0"]

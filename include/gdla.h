@@ -121,10 +121,12 @@ enum {
   GDLA_STAGE_PROJ_IN = 0,    /* x [W_qa | W_dkv | W_kr | W_lambda]                  Eq.(1),(3),(7) */
   GDLA_STAGE_NORM_APPEND,    /* RMSNorm, RoPE of k^R, sigmoid, cache append         Eq.(1),(4),(7) */
   GDLA_STAGE_EXPAND_KV,      /* prefill: K^C, V of the visible keys                 Eq.(5) */
-  GDLA_STAGE_PROJ_Q,         /* c^Q [W_qc | W_qr | W_gate], RoPE of q^R             Eq.(2),(9) */
-  GDLA_STAGE_ATTN_NOISE,     /* prefill: noise-head attention; decode: absorb + latent attention */
+  GDLA_STAGE_PROJ_Q,         /* c^Q [W_qc | W_qr | W_gate], RoPE of q^R; decode on the bf16 MFMA
+                                path also the absorbed query q~                     Eq.(2),(9) */
+  GDLA_STAGE_ATTN_NOISE,     /* prefill: noise-head attention; decode: latent attention of all
+                                heads over the cache (MFMA path: the split-L kernel alone) */
   GDLA_STAGE_ATTN_SIGNAL,    /* prefill: signal-head attention + Eq.(8) combine + gate;
-                                decode: un-absorb + combine + gate                  Eq.(8)-(10) */
+                                decode: split merge, un-absorb, combine + gate      Eq.(8)-(10) */
   GDLA_STAGE_PROJ_OUT,       /* vec(.) W_o                                          Eq.(10) */
   GDLA_N_STAGES
 };
