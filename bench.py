@@ -7,6 +7,11 @@ roofline of the dominant kernel (signal-head attention, timed with HIP events re
 library around it), and the fp64 CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode] [--no-cpu-baseline]
+                    [--workload prefill_8k|swa_prefill_2x32k|chunked_prefill_4k_256k|decode_64x64k]
+
+--workload picks another workload for the timed line (2 x 32K prefill with a 4096 window; a
+4096-token chunk against a 256K cache; one decode step of 64 sequences at 64K context, reported
+in GB/s of latent cache); --decode appends the decode measurement to the 8K line.
 """
 
 import argparse
@@ -47,22 +52,22 @@ def layer_flops(cfg, t, p0, window):
             "total": attn_signal + attn_noise + proj + expand, "pairs": pairs}
 
 
-def kernel_source_sha():
+def source_sha(rel):
     h = hashlib.sha256()
-    with open(os.path.join(ROOT, "attention_gdla_prefill_decode_amd", "csrc", "attn_prefill.hip"), "rb") as f:
+    with open(os.path.join(ROOT, rel), "rb") as f:
         h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile():
-    """HBM bytes per launch of the dominant kernel from the committed counter summary, if it was
-    taken on the current kernel source (else None)."""
-    p = os.path.join(ROOT, "profiles", "attn_signal_prefill_8k_traffic.json")
+def traffic_from_profile(name):
+    """HBM bytes per launch of a dominant kernel from its committed counter summary
+    (profiles/<name>), if the counters were taken on the current kernel source (else None)."""
+    p = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(p):
         return None
     with open(p) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha") != kernel_source_sha():
+    if t.get("kernel_source_sha") != source_sha(t["kernel_source"]):
         return None
     return t.get("bytes_per_launch")
 
@@ -140,10 +145,13 @@ def bench_decode(steps, warmup):
     gbs = nbytes / kern_ms / 1e6
     return {"workload": "decode_64x64k", "batch": len(pos), "context": int(pos[0]) + 1,
             "ms_per_step": round(ms, 4),
+            "latent_GBps_whole_step": round(nbytes / ms / 1e6, 1),
             "tokens_per_s": round(len(pos) / ms * 1e3, 1),
             "roofline": {"kernel": "latent_decode_kernel<shared>", "bound": "hbm",
                          "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": nbytes,
+                         "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": traffic_from_profile("latent_decode_64x64k_traffic.json"),
+                         "bytes_per_launch": nbytes,
                          "avg_launch_ms": round(kern_ms, 4)},
             "stages_ms": {k: round(v, 4) for k, v in stages.items()}}
 
@@ -156,7 +164,13 @@ def main():
     ap.add_argument("--decode", action="store_true", help="also time the 64 x 64K decode workload")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the 64 x 64K decode workload (prints its JSON object)")
+    ap.add_argument("--workload", default="prefill_8k",
+                    choices=["prefill_8k", "swa_prefill_2x32k", "chunked_prefill_4k_256k", "decode_64x64k"],
+                    help="workload of the timed line (default: the 8K prefill)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only copy 1 GiB device to device three times (a known-size reference "
+                         "for the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build runs on a single MI355X and has no "
@@ -167,18 +181,42 @@ def main():
     import synth
     import attention_gdla_prefill_decode_amd as gd
 
+    if args.copy_probe:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_per_launch": n, "launches": 3}), flush=True)
+        return
+
     if args.decode_only:
         print(json.dumps(bench_decode(args.steps, args.warmup)), flush=True)
         return
 
-    cfg = synth.WORKLOADS["prefill_8k"]
-    t, p0 = cfg["seq"], cfg["p0"]
+    if args.workload == "decode_64x64k":
+        d = bench_decode(args.steps, args.warmup)
+        result = {
+            "metric": METRIC, "value": round(d["latent_GBps_whole_step"], 1), "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": d["ms_per_step"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16 (fp32 accumulate)", "data": "synthetic",
+            "config": {"workload": "decode_64x64k", "batch": 64, "context": 65536,
+                       "parallelism": "none (1 GPU)"},
+            "roofline": d["roofline"], "stages_ms": d["stages_ms"], "tokens_per_s": d["tokens_per_s"],
+        }
+        print(json.dumps(result), flush=True)
+        return
+
+    cfg = synth.WORKLOADS[args.workload]
+    bsz, t, p0, win = cfg["batch"], cfg["seq"], cfg["p0"], cfg["window"]
     inp = synth.make_inputs(cfg, "cuda")
     w = gd.make_weights(inp["weights"])
     dims = gd.make_dims(cfg)
     x, cache = inp["x"], inp["cache"]
     pos = inp["p0"]
-    ws = torch.empty(gd.gdla_workspace_bytes(dims, gd.GDLA_OP_PREFILL, 1, t, pos, cfg["max_len"]),
+    ws = torch.empty(gd.gdla_workspace_bytes(dims, gd.GDLA_OP_PREFILL, bsz, t, pos, cfg["max_len"]),
                      dtype=torch.uint8, device="cuda")
     out = torch.empty_like(x)
     # one set of stage events per timed step, read after the timed region (no host sync inside)
@@ -200,31 +238,36 @@ def main():
         for k, v in tm.elapsed().items():
             stage_tot[k] += v
     stages = {k: round(v / args.steps, 4) for k, v in stage_tot.items()}
-    fl = layer_flops(cfg, t, p0, 0)
+    fl = {k: v * bsz for k, v in layer_flops(cfg, t, p0, win).items()}
     value = fl["total"] / (ms * 1e-3) / 1e12
     attn_ms = stages["attn_signal"]
     achieved = fl["attn_signal"] / (attn_ms * 1e-3) / 1e12
+    noise_ms = stages["attn_noise"]
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16+fp16 (fp32 accumulate)", "data": "synthetic",
-        "config": {"workload": "prefill_8k", "batch": 1, "seq_len": t, "d_model": cfg["d_model"],
-                   "heads": "64 signal + 16 noise, 16 KV", "latents": "1024 / 512",
-                   "head_dim": cfg["d_head"], "rope_dim": cfg["d_rope"], "window": 0,
-                   "parallelism": "none (1 GPU)"},
+        "config": {"workload": args.workload, "batch": bsz, "seq_len": t, "cached_before": p0,
+                   "d_model": cfg["d_model"], "heads": "64 signal + 16 noise, 16 KV",
+                   "latents": "1024 / 512", "head_dim": cfg["d_head"], "rope_dim": cfg["d_rope"],
+                   "window": win, "parallelism": "none (1 GPU)"},
         "frac_of_mfma_peak_whole_step": round(value / PEAK_MFMA_TFLOPS, 4),
         "roofline": {"kernel": "attn_prefill_kernel<signal>", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
-                     "traffic": traffic_from_profile(),
+                     "traffic": (traffic_from_profile("attn_signal_prefill_8k_traffic.json")
+                                 if args.workload == "prefill_8k" else None),
                      "flop_per_launch": fl["attn_signal"], "avg_launch_ms": attn_ms},
+        "attention_core": {"kernels": "noise + signal attention", "ms": round(attn_ms + noise_ms, 4),
+                           "TFLOPs": round((fl["attn_signal"] + fl["attn_noise"])
+                                           / ((attn_ms + noise_ms) * 1e-3) / 1e12, 2)},
         "stages_ms": stages,
         "out_finite": bool(torch.isfinite(out).all().item()),
     }
     if args.decode:
         result["decode"] = bench_decode(max(3, args.steps // 4), 2)
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.workload == "prefill_8k":
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result), flush=True)
 
