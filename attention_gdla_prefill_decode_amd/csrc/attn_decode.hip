@@ -9,18 +9,20 @@
 // and serves all query heads.
 //
 // Kernel layout: one workgroup per (sequence, key split), one wave per SIMD.  Query heads come in
-// blocks of 16 (the N side of v_mfma_f32_16x16x32_bf16); wave w owns block w (all 512 output dims)
-// and, when there are five blocks (65..80 heads), also output dims 128 w .. 128 w + 127 of block 4.
-// Every wave computes the scores of block 4 itself from the same LDS fragments it already reads for
-// its own block, so the fifth block costs MFMA work but no LDS traffic and no cross-wave traffic.
-// q~ (2 x 72 registers) and O^T (128 + 32) stay in registers.
-// Cache tiles of 64 rows (576 bf16 = 72 chunks of 16 bytes each) are loaded by direct global -> LDS
-// 16-byte loads into two distinct LDS buffers (one tile in flight while the other is consumed);
-// every tile serves all heads.  Per tile and wave:
+// blocks of 16 (the N side of v_mfma_f32_16x16x32_bf16).
+//   Scores: wave w computes the scores of block w and, when there are five blocks (65..80 heads),
+//   also those of block 4 (every wave, from the fragments it already reads), so q~ of two blocks
+//   (2 x 72 registers) stays in registers.
+//   Values: wave w accumulates output dims 128 w .. 128 w + 127 of every head block (160 registers),
+//   so each wave transposes only its quarter of the tile (the transposing LDS reads are about 3x
+//   slower per byte than plain ones).  The probabilities of blocks 0..3 go through a 4 KB LDS
+//   buffer; block 4's are identical in every wave.
+// Cache tiles of 32 rows (576 bf16 = 72 chunks of 16 bytes each) stream through a 4-slot LDS ring
+// by direct global -> LDS 16-byte loads; every tile serves all heads.  Per tile and wave:
 //   S^T[key, head] = cache[key, 0:576] . q~[head, 0:576]   (A = cache rows, B = q~ from registers)
-//   per-head online softmax (lanes l, l^16, l^32, l^48 hold one head), lazy rescaling,
+//   softmax against a fixed reference (see SoftmaxState), P^T -> LDS, barrier,
 //   O^T[dim, head] += cbar^T[dim, key] . P^T[key, head]    (A = cbar^T by ds_read_b64_tr_b16,
-//                                                           B = P^T straight from the S registers)
+//                                                           B = P^T of each head block)
 // Rows are unpadded; chunk c of row r sits at c ^ f(r) with f(r) = 4 r_1 + 2 (r_0 ^ r_2) +
 // (r_0 ^ r_3) (r_i = bit i of r).  The 16-byte row reads (consecutive rows, one chunk) and the
 // transposing reads (4 consecutive rows, an aligned pair of chunks) then hit distinct banks whether
@@ -53,7 +55,8 @@ constexpr int NDB = DC / 16;       // 32 dim blocks of 16 in O^T
 constexpr int MAX_WAVES = 4;      // always launched: one wave per SIMD
 constexpr int DMA_PER_WAVE = TILE_CH / 64 / MAX_WAVES;  // 16-byte loads per lane and tile (9)
 constexpr int MAX_HEADS = 16 * (MAX_WAVES + 1);
-constexpr int SH_DB = NDB / MAX_WAVES;  // dim blocks of the shared head block per wave (8)
+constexpr int WDB = NDB / MAX_WAVES;    // dim blocks of 16 owned by each wave (8)
+constexpr int NHB = MAX_WAVES + 1;      // head blocks of 16 (at most)
 
 struct DecodeArgs {
   const bf16_t *qabs;  // [B, n_H, 576] bf16
@@ -138,6 +141,7 @@ __device__ __forceinline__ uint32_t lds_u32(const void *p) {
 template <bool SHARED>
 __global__ void __launch_bounds__(256, 1) latent_decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t CB[NBUF * TILE];
+  __shared__ __attribute__((aligned(16))) bf16x8 PB[MAX_WAVES][64];  // P^T of head blocks 0..3
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = blockIdx.y, sp = blockIdx.x;
@@ -201,11 +205,13 @@ __global__ void __launch_bounds__(256, 1) latent_decode_kernel(DecodeArgs a) {
     }
   };
 
-  f32x4 O[NDB], O4[SHARED ? SH_DB : 1];
+  // O[hb][dd] = O^T[dims 16 (WDB wave + dd) + 4 g + j][heads 16 hb + col]
+  constexpr int HB = SHARED ? NHB : MAX_WAVES;
+  f32x4 O[HB][WDB];
 #pragma unroll
-  for (int d = 0; d < NDB; ++d) O[d] = f32x4{};
+  for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-  for (int d = 0; d < (SHARED ? SH_DB : 1); ++d) O4[d] = f32x4{};
+    for (int d = 0; d < WDB; ++d) O[hb][d] = f32x4{};
   SoftmaxState st, st4;
   int pass = 0;
 
@@ -214,18 +220,16 @@ __global__ void __launch_bounds__(256, 1) latent_decode_kernel(DecodeArgs a) {
   int offS[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) offS[q] = col * RB + (((4 * q + g) ^ swz(col)) * 16);
-  // PV phase: lane (g, jj, qq) of a transposing read addresses row 32 ks + 16 hi + 4 g + jj and dims
-  // 16 d + 4 qq .. + 3, i.e. logical chunk 2 d + (qq >> 1), half qq & 1; swz(row) = swz(4 g + jj).
+  // PV phase: lane (g, jj, qq) of a transposing read addresses row 16 hi + 4 g + jj and dims
+  // 16 d + 4 qq .. + 3 with d = WDB wave + dd, i.e. logical chunk 16 wave + 2 dd + (qq >> 1), half
+  // qq & 1; swz(row) = swz(4 g + jj) and the XOR only touches the low 3 bits of the chunk.
   const int jj = (lane & 15) >> 2, qq = lane & 3;
   int offP[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int r = 4 * g + jj;
-    offP[q] = r * RB + (((2 * q + (qq >> 1)) ^ swz(r)) * 16) + (qq & 1) * 8;
+    offP[q] = r * RB + wave * (2 * WDB * 16) + (((2 * q + (qq >> 1)) ^ swz(r)) * 16) + (qq & 1) * 8;
   }
-  // Dim blocks are visited in the order d = (dr + SH_DB * wave) mod NDB and O[dr] holds block d, so
-  // that the blocks dr < SH_DB are this wave's share of the shared head block (compile-time indices).
-  const int rot = 2 * wave;  // (SH_DB * wave) / 4
 
   auto compute = [&](const bf16_t *cs, int s0) {
     const char *cbyte = (const char *)cs;
@@ -253,25 +257,27 @@ __global__ void __launch_bounds__(256, 1) latent_decode_kernel(DecodeArgs a) {
     const int lim = k_end - s0 - 4 * g;
     softmax_tile(S, st, lim, a.c, P);
     if (SHARED) softmax_tile(S4, st4, lim, a.c, P4);
-    // PV phase, pipelined two dim blocks ahead: [reads of block dr + 2][MFMAs of block dr]
+    PB[wave][lane] = P;
+    __syncthreads();  // P^T of blocks 0..3 visible to every wave
+    bf16x8 PH[HB];
+#pragma unroll
+    for (int hb = 0; hb < MAX_WAVES; ++hb) PH[hb] = PB[hb][lane];
+    if (SHARED) PH[HB - 1] = P4;
+    // PV phase over this wave's dim blocks, pipelined two ahead: [reads of dd + 2][MFMAs of dd]
     bf16x8 vf[3];
-    auto ldV = [&](bf16x8 &f, int dr) {
-      const char *p0 = cbyte + offP[dr & 3] + ((((dr >> 2) + rot) & 7) * 128);
+    auto ldV = [&](bf16x8 &f, int dd) {
+      const char *p0 = cbyte + offP[dd & 3] + (dd >> 2) * 128;
       const bf16x4 lo4 = tr_read(p0);
       const bf16x4 hi4 = tr_read(p0 + 16 * RB);
       f = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
     };
     ldV(vf[0], 0);
     ldV(vf[1], 1);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int dr = 0; dr < NDB; ++dr) {
-      if (dr + 2 < NDB) ldV(vf[(dr + 2) % 3], dr + 2);
-      O[dr] = mfma16(vf[dr % 3], P, O[dr]);
-      if (SHARED && dr < SH_DB) O4[dr] = mfma16(vf[dr % 3], P4, O4[dr]);
-      if (dr + 2 < NDB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      if (SHARED && dr < SH_DB) __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      else __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    for (int dd = 0; dd < WDB; ++dd) {
+      if (dd + 2 < WDB) ldV(vf[(dd + 2) % 3], dd + 2);
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) O[hb][dd] = mfma16(vf[dd % 3], PH[hb], O[hb][dd]);
     }
   };
 
@@ -305,37 +311,35 @@ __global__ void __launch_bounds__(256, 1) latent_decode_kernel(DecodeArgs a) {
     st4.mref = st4.mrun;
     st4.l = 0.f;
 #pragma unroll
-    for (int d = 0; d < NDB; ++d) O[d] = f32x4{};
+    for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-    for (int d = 0; d < (SHARED ? SH_DB : 1); ++d) O4[d] = f32x4{};
+      for (int d = 0; d < WDB; ++d) O[hb][d] = f32x4{};
   }
 
+  // (m, l) of head block hb come from the wave that owns its scores (wave 0 for block 4)
   const float lt = head_sum(st.l);
-  if (head_ok) {
+  if (head_ok && g == 0) {
     const int64_t ph = ((int64_t)b * a.splits + sp) * a.n_heads + head;
-    if (g == 0) {
-      a.part_ml[ph * 2] = ntiles > 0 ? st.mref : -INFINITY;
-      a.part_ml[ph * 2 + 1] = lt;
-    }
-    // O[dr][j] = O^T[dim 16 d + 4 g + j][head], d = (dr + SH_DB * wave) mod NDB
-    float *po = a.part_o + ph * DC + 4 * g;
-#pragma unroll
-    for (int dr = 0; dr < NDB; ++dr)
-      *(float4 *)(po + 16 * ((dr + SH_DB * wave) % NDB)) = make_float4(O[dr][0], O[dr][1], O[dr][2], O[dr][3]);
+    a.part_ml[ph * 2] = ntiles > 0 ? st.mref : -INFINITY;
+    a.part_ml[ph * 2 + 1] = lt;
   }
   if (SHARED) {
     const float lt4 = head_sum(st4.l);
-    if (head4_ok) {
+    if (head4_ok && wave == 0 && g == 0) {
       const int64_t ph = ((int64_t)b * a.splits + sp) * a.n_heads + head4;
-      if (wave == 0 && g == 0) {
-        a.part_ml[ph * 2] = ntiles > 0 ? st4.mref : -INFINITY;
-        a.part_ml[ph * 2 + 1] = lt4;
-      }
-      float *po = a.part_o + ph * DC + 4 * g + 16 * SH_DB * wave;
-#pragma unroll
-      for (int d = 0; d < SH_DB; ++d)
-        *(float4 *)(po + 16 * d) = make_float4(O4[d][0], O4[d][1], O4[d][2], O4[d][3]);
+      a.part_ml[ph * 2] = ntiles > 0 ? st4.mref : -INFINITY;
+      a.part_ml[ph * 2 + 1] = lt4;
     }
+  }
+  // this wave's dims of every head: O[hb][dd][j] = O^T[dim 16 (WDB wave + dd) + 4 g + j][16 hb + col]
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    const int h = 16 * hb + col;
+    if (h >= a.n_heads) continue;
+    float *po = a.part_o + (((int64_t)b * a.splits + sp) * a.n_heads + h) * DC + 16 * WDB * wave + 4 * g;
+#pragma unroll
+    for (int dd = 0; dd < WDB; ++dd)
+      *(float4 *)(po + 16 * dd) = make_float4(O[hb][dd][0], O[hb][dd][1], O[hb][dd][2], O[hb][dd][3]);
   }
 }
 
