@@ -21,9 +21,10 @@
 //   S^T[key, query] = K[key, 0:192] . Q[query, 0:192]   (A = K from LDS, B = Q in registers);
 //   online softmax per query (each lane owns one query column; its partner lane l^32 the other
 //     half of the keys), with lazy rescaling, P^T taken straight from the accumulators in fp16;
-//   O^T[dim, query] += V^T[dim, key] . P^T[key, query]  (A = V^T via ds_read_tr16_b64).
-// The key order inside each 16-key MFMA step is permuted identically on both operands, which lets
-// the S accumulator layout serve as the P operand without any shuffle.
+//   O^T[dim, query] += V^T[dim, key] . P^T[key, query]  (A = V^T rows, 16-byte LDS reads).
+// The values arrive transposed from the expansion GEMM ([n_kv][128][keys], keys of every 16-group
+// in the order vt_slot), which is the order in which the S accumulators hold the keys of P^T: the
+// accumulators serve as the P operand without any shuffle and no transposing LDS read is needed.
 // Causal / sliding-window tiles are classified per wave as skipped, full or partial; only partial
 // tiles evaluate the per-element mask s <= p && (W == 0 || p - s < W).
 #include "fast_paths.h"
@@ -50,7 +51,7 @@ constexpr int V_TILE = KT * DH;        // elements of one V tile
 struct AttnArgs {
   const f16_t *q;         // [M, n_H, 192] fp16: q^C then rotated q^R of each head
   const f16_t *kx;        // [B, n_kv, lcap, 192] fp16: [K^C ; k^R] of keys base_b .. base_b + lcap - 1
-  const f16_t *vx;        // [B, n_kv, lcap, 128] fp16: V
+  const f16_t *vx;        // [B, n_kv, 128, lcap] fp16: V^T, keys in vt_slot order per 16-group
   const int32_t *pos;     // [B] first position of the chunk
   const float *lam;       // [M, n_S]
   const float *gate;      // [M, n_S, 128] gate logits
@@ -63,14 +64,12 @@ struct AttnArgs {
   float c;                // softmax scale * log2(e)
 };
 
-// LDS chunk slot of 16-byte chunk c of row `row`.  K: 16 consecutive rows reading the same chunk
-// land on 16 distinct 4-bank groups; V: the 4 rows x 4 chunks of one ds_read_tr16_b64 pass do.
+// LDS chunk slot of 16-byte chunk c of row `row`: 16 consecutive rows reading the same chunk land
+// on 16 distinct 4-bank groups.  K rows are keys (24 chunks), V^T rows are dims (8 chunks = the 64
+// keys of the tile).
+constexpr int VT_CH = KT / 8;
 __device__ __forceinline__ int kslot(int row, int c) { return row * K_CH + (c ^ ((row >> 1) & 7)); }
-__device__ __forceinline__ int vslot(int row, int c) { return row * V_CH + (c ^ ((row & 3) << 2)); }
-
-__device__ __forceinline__ f16x4 tr_read(const f16_t *p) {
-  return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p));
-}
+__device__ __forceinline__ int vslot(int row, int c) { return row * VT_CH + (c ^ ((row >> 1) & 7)); }
 
 __device__ __forceinline__ f32x16 mfma(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -95,7 +94,7 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) f16_t Vs0[V_TILE];
   __shared__ __attribute__((aligned(16))) f16_t Vs1[V_TILE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = blockIdx.z;
   const int qblk = a.n_qblk - 1 - (int)blockIdx.x;  // late (long) query blocks first
   int head, kvh, t0w, tlo, thi;
@@ -117,7 +116,9 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
   const int W = a.window;
   const int p0 = a.pos[b];
   const int base = W > 0 ? max(0, p0 - W + 1) : 0;
-  const int klo = W > 0 ? max(0, p0 + tlo - W + 1) : 0;
+  // first key tile: aligned to 16 keys past `base` (the value layout's key groups); the extra keys
+  // in front are outside the window and masked
+  const int klo = W > 0 ? base + ((max(0, p0 + tlo - W + 1) - base) & ~15) : 0;
   const int khi = p0 + thi + 1;
   const int ntiles = (khi - klo + KT - 1) / KT;
   const int wp_lo = p0 + t0w, wp_hi = p0 + min(t0w + 31, a.T - 1);
@@ -136,7 +137,7 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
   // ---- direct global -> LDS staging of one key tile.  Keys past khi are clamped to khi - 1: they
   // are masked for every valid query, and clamping keeps every load inside the buffers.
   const f16_t *kxh = a.kx + ((int64_t)b * a.n_kv + kvh) * a.lcap * DQK;
-  const f16_t *vxh = a.vx + ((int64_t)b * a.n_kv + kvh) * a.lcap * DH;
+  const f16_t *vth = a.vx + ((int64_t)b * a.n_kv + kvh) * DH * a.lcap;
   auto issue = [&](f16_t *ks, f16_t *vs, int s0) {
 #pragma unroll
     for (int j = 0; j < 3; ++j) {  // K: 24 wave-instructions of 64 chunks, 3 per wave
@@ -149,14 +150,14 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
                                        16, 0, 0);
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {  // V: 16 wave-instructions, 2 per wave
+    for (int j = 0; j < 2; ++j) {  // V^T: 128 dims x 8 chunks = 16 wave-instructions, 2 per wave
+      // keys past khi hold finite values (the expansion's zeroed tail), and get zero probability
       const int slot0 = (wave * 2 + j) * 64;
       const int slot = slot0 + lane;
-      const int row = slot / V_CH, cpos = slot % V_CH;
-      const int c = cpos ^ ((row & 3) << 2);
-      const int s = min(s0 + row, khi - 1);
-      __builtin_amdgcn_global_load_lds(vxh + (int64_t)(s - base) * DH + c * 8, (lds_void *)(vs + slot0 * 8),
-                                       16, 0, 0);
+      const int row = slot / VT_CH, cpos = slot % VT_CH;
+      const int c = cpos ^ ((row >> 1) & 7);
+      __builtin_amdgcn_global_load_lds(vth + (int64_t)row * a.lcap + (s0 - base) + c * 8,
+                                       (lds_void *)(vs + slot0 * 8), 16, 0, 0);
     }
   };
 
@@ -166,26 +167,41 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
   float m = -INFINITY, l = 0.f;
 
   const int hgrp = lane >> 5;  // which half of each 8-key group this lane's accumulators hold
-  // K fragment: row kb*32 + lane%32, chunk 2 kst + hgrp
   const int krow = lane & 31;
-  // V^T fragment (this lane as a source of ds_read_tr16_b64): row 16 kst + 8 t + 4 (G/2) + jj,
-  // chunk 4 db + 2 (G & 1) + qq / 2, half (qq & 1)
-  const int G = lane >> 4, jj = (lane & 15) >> 2, qq = lane & 3;
-  const int vrow = 4 * (G >> 1) + jj;
+  // Lane-dependent byte offsets of the LDS fragment reads; the rest of each address is an
+  // immediate.  K fragment (kb, kst): row 32 kb + krow, chunk 2 kst + hgrp; the row swizzle is
+  // (krow >> 1) & 7 for both kb and only touches the low 3 bits of the chunk, so the lane part
+  // depends on kst & 3 only.  V^T fragment (db, kst): row 32 db + krow, chunk 2 kst + hgrp.
+  int offK[4], offV[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    offK[q] = krow * (K_CH * 16) + (((2 * q + hgrp) ^ ((krow >> 1) & 7)) * 16);
+    offV[q] = krow * (VT_CH * 16) + (((2 * q + hgrp) ^ ((krow >> 1) & 7)) * 16);
+  }
 
   auto compute = [&](const f16_t *ks, const f16_t *vs, int s0) {
     const bool skip = !active || s0 > wp_hi || (W > 0 && wp_lo - (s0 + KT - 1) >= W);
     if (skip) return;
     const bool full = (s0 + KT - 1 <= wp_lo) && (W == 0 || wp_hi - s0 < W);
+    const char *kb8 = (const char *)ks;
+    const char *vb8 = (const char *)vs;
+    // S phase, software-pipelined one k-step ahead: [reads of step kst + 1][MFMAs of step kst]
     f32x16 S[2];
+    f16x8 kf[2][2];
+    auto ldK = [&](f16x8 (&f)[2], int kst) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        f[kb] = *(const f16x8 *)(kb8 + offK[kst & 3] + kb * 32 * K_CH * 16 + (kst >> 2) * 128);
+    };
+    ldK(kf[0], 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
     for (int kst = 0; kst < 12; ++kst) {
+      if (kst + 1 < 12) ldK(kf[(kst + 1) & 1], kst + 1);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int row = kb * 32 + krow;
-        const f16x8 kf = *(const f16x8 *)(ks + kslot(row, 2 * kst + hgrp) * 8);
-        S[kb] = mfma(kf, Qf[kst], kst == 0 ? f32x16{} : S[kb]);
-      }
+      for (int kb = 0; kb < 2; ++kb) S[kb] = mfma(kf[kst & 1][kb], Qf[kst], kst == 0 ? f32x16{} : S[kb]);
+      if (kst + 1 < 12) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
     // v[16 kb + e] is the score of key s0 + 32 kb + 8 (e / 4) + 4 hgrp + e % 4
     float v[32];
@@ -231,17 +247,21 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) P[k4][e] = (f16_t)v[8 * k4 + e];
     l += rs;
+    // PV phase, pipelined one dim block ahead: [reads of block db + 1][MFMAs of block db]
+    f16x8 vf[2][4];
+    auto ldV = [&](f16x8 (&f)[4], int db) {
+#pragma unroll
+      for (int kst = 0; kst < 4; ++kst) f[kst] = *(const f16x8 *)(vb8 + offV[kst] + db * 32 * VT_CH * 16);
+    };
+    ldV(vf[0], 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      const int c = 4 * db + 2 * (G & 1) + (qq >> 1);
+      if (db + 1 < 4) ldV(vf[(db + 1) & 1], db + 1);
 #pragma unroll
-      for (int kst = 0; kst < 4; ++kst) {
-        const f16_t *vp = vs + vslot(16 * kst + vrow, c) * 8 + (qq & 1) * 4;
-        const f16x4 lo = tr_read(vp);
-        const f16x4 hi = tr_read(vp + 8 * DH);  // 8 rows further; the swizzle repeats every 4 rows
-        const f16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        O[db] = mfma(vf, P[kst], O[db]);
-      }
+      for (int kst = 0; kst < 4; ++kst) O[db] = mfma(vf[db & 1][kst], P[kst], O[db]);
+      if (db + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
   };
 
@@ -325,7 +345,26 @@ __global__ void __launch_bounds__(256) kr_fill_kernel(const bf16_t *cache, f16_t
     *(uint4 *)(kx + (((int64_t)b * n_kv + h) * lcap + r) * DQK + DH + ch * 8) = o;
 }
 
+// Zeroes V^T positions of keys nk .. lcap - 1 (one block of 64 threads per (dim row, sequence)).
+__global__ void __launch_bounds__(64) vt_tail_zero_kernel(f16_t *vx, const int32_t *pos, int32_t T,
+                                                          int32_t window, int32_t rows, int32_t lcap) {
+  const int b = blockIdx.y;
+  const int p0 = pos[b];
+  const int lo = window > 0 ? max(0, p0 - window + 1) : 0;
+  const int nk = p0 + T - lo;
+  f16_t *r = vx + ((int64_t)b * rows + blockIdx.x) * lcap;
+  for (int i = (nk & ~15) + threadIdx.x; i < lcap; i += 64)
+    if (vt_slot(i) >= nk) r[i] = (f16_t)0.0f;
+}
+
 }  // namespace
+
+hipError_t launch_vt_tail_zero(void *vx, const int32_t *pos_dev, int32_t B, int32_t T, int32_t lcap,
+                               const LayerDims &d, hipStream_t s) {
+  hipLaunchKernelGGL(vt_tail_zero_kernel, dim3(d.n_kv * DH, B), dim3(64), 0, s, (f16_t *)vx, pos_dev, T,
+                     d.window, d.n_kv * DH, lcap);
+  return hipGetLastError();
+}
 
 bool fast_prefill_supported(const LayerDims &d, gdla_dtype dt) {
   return dt == GDLA_BF16 && d.d_h == DH && d.d_r == DR && d.d_c % 8 == 0 && d.d_cq % 64 == 0 &&

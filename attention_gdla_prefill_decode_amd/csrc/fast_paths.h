@@ -27,6 +27,18 @@ FastPrefillLayout plan_fast_prefill(const LayerDims &d, int32_t B, int32_t T, Ad
   return L;
 }
 
+// Value layout of the MFMA prefill: V^T per KV head, [n_kv][d_head][lcap] fp16, with the keys of
+// every aligned group of 16 stored in the order the probability operand of the PV MFMA expects
+// (key k at position vt_slot(k): bits 2 and 3 swapped; the map is its own inverse).
+__host__ __device__ inline int vt_slot(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+// Key capacity of the value / key buffers on the MFMA path: whole tiles plus one spare tile, so a
+// tile that starts at any 16-key boundary before the last key stays inside the buffer.
+inline int32_t fast_prefill_lcap(int32_t keys) { return (keys + 63) / 64 * 64 + 64; }
+// Zeroes the value positions of keys nk_b .. lcap - 1 of every sequence (never visible, but read
+// as part of whole tiles, so they must hold finite values).
+hipError_t launch_vt_tail_zero(void *vx, const int32_t *pos_dev, int32_t B, int32_t T, int32_t lcap,
+                               const LayerDims &d, hipStream_t s);
+
 bool fast_prefill_supported(const LayerDims &d, gdla_dtype dt);
 // Elements per expanded key row on the MFMA path: [K^C (d_h) ; k^R (d_rope)] in fp16.
 int32_t fast_prefill_key_row();

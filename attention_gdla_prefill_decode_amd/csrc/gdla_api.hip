@@ -97,8 +97,9 @@ PrefillLayout plan_prefill(const LayerDims &d, gdla_dtype dt, int32_t B, int32_t
   PrefillLayout L{};
   const size_t es = esize(dt);
   const size_t M = (size_t)B * T;
-  L.lcap = key_capacity(d, B, T, pos, max_len);
   L.use_fast = fast_prefill_supported(d, dt);
+  L.lcap = key_capacity(d, B, T, pos, max_len);
+  if (L.use_fast) L.lcap = fast_prefill_lcap(L.lcap);
   Plan p;
   L.pos = p.add(sizeof(int32_t) * B);
   L.aq = p.add(4 * M * d.d_cq);
@@ -260,7 +261,7 @@ hipError_t launch_gemm(GemmBatch &g, DT dt, hipStream_t s) {
   for (int i = 0; i < g.n; ++i) {
     const GemmProblem &p = g.p[i];
     if (fast_gemm_problem_ok(p)) fast[p.a_f16 ? 1 : 0].p[fast[p.a_f16 ? 1 : 0].n++] = p;
-    else if (p.a_f16 || p.c_dt > CD_IN) return hipErrorInvalidValue;  // only the MFMA kernel serves these
+    else if (p.a_f16 || p.c_dt > CD_IN || p.c_trans) return hipErrorInvalidValue;  // MFMA kernel only
     else slow.p[slow.n++] = p;
   }
   for (int k = 0; k < 2; ++k)
@@ -379,13 +380,19 @@ GDLA_EXPORT gdla_status gdla_prefill(const gdla_dims *dims, const gdla_weights *
       pv.C = at<char>(ws, L.vx) + b * v_seq * es;
       pv.ldc = d.d_h;
       pv.hs = (int64_t)L.lcap * d.d_h;
+      if (L.use_fast) {  // V^T per KV head (the MFMA attention's value layout)
+        pv.c_trans = 1;
+        pv.ldc = L.lcap;
+      }
       g.p[g.n++] = pk;
       g.p[g.n++] = pv;
     }
     HIP_TRY(launch_gemm(g, dt, stream));
   }
-  if (L.use_fast)
+  if (L.use_fast) {
     HIP_TRY(launch_kr_fill(cache, at<void>(ws, L.kx), pos_dev, B, T, L.lcap, max_len, d, stream));
+    HIP_TRY(launch_vt_tail_zero(at<void>(ws, L.vx), pos_dev, B, T, L.lcap, d, stream));
+  }
   se.end(GDLA_STAGE_EXPAND_KV);
 
   if (L.use_fast) {

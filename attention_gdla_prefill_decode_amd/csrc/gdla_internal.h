@@ -17,7 +17,9 @@ enum class DT : int32_t { F32 = 0, BF16 = 1, F16 = 2 };
 // One GEMM problem: C[m, col(n)] = epi(sum_k A[m, k] * B[k, n]), fp32 accumulation.
 // A is [M, K] with row stride lda, B is [K, N] with row stride ldb (both in the input dtype).
 // Output column n of row m is stored at C + m * ldc + (n / hw) * hs + ho + (n % hw) (elements of
-// the output dtype), which lets one launch write head-major or interleaved layouts.
+// the output dtype), which lets one launch write head-major or interleaved layouts.  With c_trans
+// (MFMA kernel, fp16 output only) it is stored transposed per head instead, at
+// C + (n / hw) * hs + ho + (n % hw) * ldc + vt_slot(m): the value layout of the prefill attention.
 struct GemmProblem {
   const void *A;
   const void *B;
@@ -29,6 +31,7 @@ struct GemmProblem {
   int32_t c_dt;    // CD_*: output dtype
   int32_t a_f16;   // 1: A is fp16 and the bf16 B is converted to fp16 while staged (MFMA only)
   int32_t epi;     // EPI_*
+  int32_t c_trans; // 1: transposed per-head store (see above)
   int32_t tile0;   // first linear tile index of this problem (filled by the launcher)
   int32_t tiles_n; // tiles along N (filled by the launcher)
 };

@@ -159,6 +159,26 @@ __global__ void __launch_bounds__(256, 4) gemm_mfma_kernel(GemmBatch batch) {
     for (int c = 0; c < 2; ++c) {
       const int n = n0 + wn * 64 + c * 32 + (lane & 31);
       if (n >= P.N) continue;
+      if (P.c_trans) {
+        // 4 consecutive rows m .. m + 3 land on 4 consecutive positions of column n's row
+        f16_t *base = (f16_t *)P.C + (int64_t)(n / P.hw) * P.hs + P.ho + (int64_t)(n % P.hw) * P.ldc;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m = m0 + wm * 64 + r * 32 + 8 * q + 4 * (lane >> 5);
+          if (m >= P.M) continue;
+          f16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (f16_t)fminf(fmaxf(acc[r][c][4 * q + e], -65504.f), 65504.f);
+          if (m + 3 < P.M) {
+            *(f16x4 *)(base + vt_slot(m)) = v;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (m + e < P.M) base[vt_slot(m + e)] = v[e];
+          }
+        }
+        continue;
+      }
       const int64_t coff = (int64_t)(n / P.hw) * P.hs + P.ho + (n % P.hw);
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
@@ -180,7 +200,9 @@ __global__ void __launch_bounds__(256, 4) gemm_mfma_kernel(GemmBatch batch) {
 
 bool fast_gemm_problem_ok(const GemmProblem &p) {
   return p.K % BK == 0 && p.K > 0 && p.N % 8 == 0 && p.lda % 8 == 0 && p.ldb % 8 == 0 &&
-         ((uintptr_t)p.A & 15) == 0 && ((uintptr_t)p.B & 15) == 0 && p.hw > 0;
+         ((uintptr_t)p.A & 15) == 0 && ((uintptr_t)p.B & 15) == 0 && p.hw > 0 &&
+         (!p.c_trans || (p.c_dt == CD_F16 && p.ldc % 4 == 0 && (p.hs + p.ho) % 4 == 0 &&
+                         ((uintptr_t)p.C & 7) == 0));
 }
 
 hipError_t launch_gemm_mfma(GemmBatch &g, hipStream_t s) {
