@@ -385,7 +385,8 @@ gdla_status run_fast_prefill(const LayerDims &d, const gdla_weights *w, int32_t 
                              const int32_t *pos_dev, const int32_t *pos_host, void *cache,
                              int32_t max_len, void *cq, float *lam, float *gate, void *kx,
                              void *vx, int32_t lcap, void *y, float *out_heads,
-                             const FastPrefillLayout &L, void *ws, hipStream_t s, StageEvents &se) {
+                             const FastPrefillLayout &L, void *ws, hipStream_t s, StageEvents &se,
+                             const NtWeights *nt) {
   (void)pos_host;
   (void)cache;
   (void)max_len;
@@ -396,18 +397,19 @@ gdla_status run_fast_prefill(const LayerDims &d, const gdla_weights *w, int32_t 
   // Eq.(2), (9): q^C straight into the per-head [q^C ; q^R] rows, q^R before RoPE, gate logits.
   se.begin(GDLA_STAGE_PROJ_Q);
   // c^Q is fp16 here; the bf16 weights are converted to fp16 while the GEMM stages them.
+  // with nt, B is the transposed fp16 weight [N, d_cq]
   GemmBatch g{};
   auto add = [&](const void *B_, int N, void *C, int64_t ldc, int c_dt, int hw, int64_t hs) {
     GemmProblem p{};
-    p.A = cq; p.lda = d.d_cq; p.B = B_; p.ldb = N; p.C = C; p.ldc = ldc;
+    p.A = cq; p.lda = d.d_cq; p.B = B_; p.ldb = nt ? d.d_cq : N; p.C = C; p.ldc = ldc;
     p.M = M; p.N = N; p.K = d.d_cq; p.hw = hw; p.hs = hs; p.ho = 0; p.c_dt = c_dt; p.a_f16 = 1;
     p.epi = EPI_NONE;
     g.p[g.n++] = p;
   };
-  add(w->w_qc, d.n_heads * DH, q, (int64_t)d.n_heads * DQK, CD_F16, DH, DQK);
-  add(w->w_qr, d.n_heads * DR, qrp, (int64_t)d.n_heads * DR, CD_F32, d.n_heads * DR, 0);
-  add(w->w_gate, d.n_signal * DH, gate, (int64_t)d.n_signal * DH, CD_F32, d.n_signal * DH, 0);
-  if (launch_gemm(g, DT::BF16, s) != hipSuccess) return GDLA_ERR_HIP;
+  add(nt ? nt->qc : w->w_qc, d.n_heads * DH, q, (int64_t)d.n_heads * DQK, CD_F16, DH, DQK);
+  add(nt ? nt->qr : w->w_qr, d.n_heads * DR, qrp, (int64_t)d.n_heads * DR, CD_F32, d.n_heads * DR, 0);
+  add(nt ? nt->gate : w->w_gate, d.n_signal * DH, gate, (int64_t)d.n_signal * DH, CD_F32, d.n_signal * DH, 0);
+  if ((nt ? launch_gemm_nt(g, true, s) : launch_gemm(g, DT::BF16, s)) != hipSuccess) return GDLA_ERR_HIP;
   if (launch_rope_heads(qrp, q, (int64_t)d.n_heads * DQK, DQK, DH, M, T, d.n_heads, DR, pos_dev,
                         d.theta, DT::F16, s) != hipSuccess)
     return GDLA_ERR_HIP;

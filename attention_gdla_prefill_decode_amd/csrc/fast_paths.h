@@ -10,6 +10,19 @@ namespace gdla {
 bool fast_gemm_problem_ok(const GemmProblem &p);
 hipError_t launch_gemm_mfma(GemmBatch &g, hipStream_t s);
 
+// ---- large GEMM with transposed (K-contiguous) weights: C = A[M, K] . Bt[N, K]^T, fp16 x fp16
+// or bf16 x bf16 (all problems of one launch share the operand type) ----
+bool nt_gemm_problem_ok(const GemmProblem &p);
+hipError_t launch_gemm_nt(GemmBatch &g, bool f16, hipStream_t s);
+// Wt[N, K] = W[K, N]^T of a bf16 weight, as fp16 (to_f16) or bf16.
+hipError_t launch_transpose_weight(const void *w, void *wt, int32_t K, int32_t N, bool to_f16, hipStream_t s);
+
+// Transposed copies of the layer weights in the workspace (prefill with enough rows to amortise
+// them): x-side weights stay bf16, the weights applied to fp16 activations become fp16.
+struct NtWeights {
+  const void *qa, *dkv, *kr, *lam, *qc, *qr, *gate, *uk, *uv, *o;
+};
+
 // ---- fused prefill attention ----
 struct FastPrefillLayout {
   size_t q;      // [M, n_H, d_h + d_r] fp16: q^C and rotated q^R of every head, one row per head
@@ -50,7 +63,8 @@ gdla_status run_fast_prefill(const LayerDims &d, const gdla_weights *w, int32_t 
                              const int32_t *pos_dev, const int32_t *pos_host, void *cache,
                              int32_t max_len, void *cq, float *lam, float *gate, void *kx,
                              void *vx, int32_t lcap, void *y, float *out_heads,
-                             const FastPrefillLayout &L, void *ws, hipStream_t s, StageEvents &se);
+                             const FastPrefillLayout &L, void *ws, hipStream_t s, StageEvents &se,
+                             const NtWeights *nt);
 
 // ---- absorbed split-L decode ----
 struct FastDecodeLayout {

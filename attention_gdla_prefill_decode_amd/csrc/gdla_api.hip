@@ -77,10 +77,14 @@ inline int32_t key_lo(int32_t p0, int32_t window) { return window > 0 ? std::max
 
 struct PrefillLayout {
   size_t pos, aq, ckv, krp, laml, cq, lam, qc, qrp, qr, gate, kx, vx, heads, y, total;
+  size_t wt_qa, wt_dkv, wt_kr, wt_lam, wt_qc, wt_qr, wt_gate, wt_uk, wt_uv, wt_o;
   int32_t lcap;
   FastPrefillLayout fast;
-  bool use_fast;
+  bool use_fast, use_nt;
 };
+
+// Rows from which the transposed-weight GEMM pays for transposing the weights once per call.
+constexpr int32_t kNtMinRows = 256;
 
 int32_t key_capacity(const LayerDims &d, int32_t B, int32_t T, const int32_t *pos, int32_t max_len) {
   int32_t lcap = 0;
@@ -114,6 +118,19 @@ PrefillLayout plan_prefill(const LayerDims &d, gdla_dtype dt, int32_t B, int32_t
   L.y = p.add(es * M * d.n_signal * d.d_h);
   if (L.use_fast) {
     L.fast = plan_fast_prefill(d, B, T, [&](size_t n) { return p.add(n); });
+    L.use_nt = (int64_t)B * T >= kNtMinRows && d.d_c % 64 == 0;
+    if (L.use_nt) {
+      L.wt_qa = p.add(2 * (size_t)d.d_model * d.d_cq);
+      L.wt_dkv = p.add(2 * (size_t)d.d_model * d.d_c);
+      L.wt_kr = p.add(2 * (size_t)d.d_model * d.d_r);
+      L.wt_lam = p.add(2 * (size_t)d.d_model * d.n_signal);
+      L.wt_qc = p.add(2 * (size_t)d.d_cq * d.n_heads * d.d_h);
+      L.wt_qr = p.add(2 * (size_t)d.d_cq * d.n_heads * d.d_r);
+      L.wt_gate = p.add(2 * (size_t)d.d_cq * d.n_signal * d.d_h);
+      L.wt_uk = p.add(2 * (size_t)d.d_c * d.n_kv * d.d_h);
+      L.wt_uv = p.add(2 * (size_t)d.d_c * d.n_kv * d.d_h);
+      L.wt_o = p.add(2 * (size_t)d.n_signal * d.d_h * d.d_model);
+    }
   } else {
     L.qc = p.add(es * M * d.n_heads * d.d_h);
     L.qrp = p.add(4 * M * d.n_heads * d.d_r);
@@ -230,15 +247,28 @@ gdla_status project_and_append(const LayerDims &d, DT dt, const gdla_weights *w,
                                int32_t M, int32_t T, const int32_t *pos_dev, void *cache,
                                int32_t max_len, float *aq, float *ckv, float *krp, float *laml,
                                void *cq, float *lam, const float *lam_override, hipStream_t s,
-                               StageEvents &se, bool cq_f16 = false) {
+                               StageEvents &se, bool cq_f16 = false, const NtWeights *nt = nullptr) {
   GemmBatch g{};
-  g.p[g.n++] = gp(x, d.d_model, w->w_dkv, d.d_c, ckv, d.d_c, M, d.d_c, d.d_model, true);
-  g.p[g.n++] = gp(x, d.d_model, w->w_kr, d.d_r, krp, d.d_r, M, d.d_r, d.d_model, true);
-  if (cq) g.p[g.n++] = gp(x, d.d_model, w->w_qa, d.d_cq, aq, d.d_cq, M, d.d_cq, d.d_model, true);
+  // with nt, B is the transposed weight [N, K] (row stride K = d_model)
+  auto wb = [&](const void *w_, const void *wt) { return nt ? wt : w_; };
+  auto ldw = [&](int64_t n) { return nt ? (int64_t)d.d_model : n; };
+  g.p[g.n++] = gp(x, d.d_model, wb(w->w_dkv, nt ? nt->dkv : nullptr), ldw(d.d_c), ckv, d.d_c, M, d.d_c,
+                  d.d_model, true);
+  g.p[g.n++] = gp(x, d.d_model, wb(w->w_kr, nt ? nt->kr : nullptr), ldw(d.d_r), krp, d.d_r, M, d.d_r,
+                  d.d_model, true);
+  if (cq)
+    g.p[g.n++] = gp(x, d.d_model, wb(w->w_qa, nt ? nt->qa : nullptr), ldw(d.d_cq), aq, d.d_cq, M, d.d_cq,
+                    d.d_model, true);
   if (lam && !lam_override)
-    g.p[g.n++] = gp(x, d.d_model, w->w_lambda, d.n_signal, laml, d.n_signal, M, d.n_signal, d.d_model, true);
-  se.begin(GDLA_STAGE_PROJ_IN);
-  HIP_TRY(launch_gemm(g, dt, s));
+    g.p[g.n++] = gp(x, d.d_model, wb(w->w_lambda, nt ? nt->lam : nullptr), ldw(d.n_signal), laml, d.n_signal, M,
+                    d.n_signal, d.d_model, true);
+  // with nt the caller has opened GDLA_STAGE_PROJ_IN before transposing the weights
+  if (nt) {
+    HIP_TRY(launch_gemm_nt(g, false, s));
+  } else {
+    se.begin(GDLA_STAGE_PROJ_IN);
+    HIP_TRY(launch_gemm(g, dt, s));
+  }
   se.end(GDLA_STAGE_PROJ_IN);
   PrepArgs a{};
   a.aq = aq; a.ckv = ckv; a.kr = krp; a.lam_logit = laml; a.lam_override = lam_override;
@@ -349,11 +379,34 @@ GDLA_EXPORT gdla_status gdla_prefill(const gdla_dims *dims, const gdla_weights *
 
   int32_t *pos_dev = at<int32_t>(ws, L.pos);
   HIP_TRY(launch_set_i32(pos_dev, pos_host, B, stream));
+  NtWeights ntw{};
+  if (L.use_nt) {
+    // Transposed weights for the K-contiguous GEMM: weights applied to x and to the bf16 cache stay
+    // bf16, those applied to the fp16 c^Q and Y become fp16 (the conversion the other MFMA GEMM
+    // does while staging).
+    se.begin(GDLA_STAGE_PROJ_IN);
+    struct { const void *w; size_t off; int32_t K, N; bool f16; } tw[] = {
+        {w->w_qa, L.wt_qa, d.d_model, d.d_cq, false},
+        {w->w_dkv, L.wt_dkv, d.d_model, d.d_c, false},
+        {w->w_kr, L.wt_kr, d.d_model, d.d_r, false},
+        {w->w_lambda, L.wt_lam, d.d_model, d.n_signal, false},
+        {w->w_qc, L.wt_qc, d.d_cq, d.n_heads * d.d_h, true},
+        {w->w_qr, L.wt_qr, d.d_cq, d.n_heads * d.d_r, true},
+        {w->w_gate, L.wt_gate, d.d_cq, d.n_signal * d.d_h, true},
+        {w->w_uk, L.wt_uk, d.d_c, d.n_kv * d.d_h, false},
+        {w->w_uv, L.wt_uv, d.d_c, d.n_kv * d.d_h, false},
+        {w->w_o, L.wt_o, d.n_signal * d.d_h, d.d_model, true},
+    };
+    for (const auto &t : tw) HIP_TRY(launch_transpose_weight(t.w, at<void>(ws, t.off), t.K, t.N, t.f16, stream));
+    ntw = {at<void>(ws, L.wt_qa), at<void>(ws, L.wt_dkv), at<void>(ws, L.wt_kr), at<void>(ws, L.wt_lam),
+           at<void>(ws, L.wt_qc), at<void>(ws, L.wt_qr), at<void>(ws, L.wt_gate), at<void>(ws, L.wt_uk),
+           at<void>(ws, L.wt_uv), at<void>(ws, L.wt_o)};
+  }
   // Eq.(1), (3), (4), (7) and the cache append of this chunk's rows.
   st = project_and_append(d, dt, w, x, M, T, pos_dev, cache, max_len, at<float>(ws, L.aq),
                           at<float>(ws, L.ckv), at<float>(ws, L.krp), at<float>(ws, L.laml),
                           at<void>(ws, L.cq), at<float>(ws, L.lam), lam_override, stream, se,
-                          L.use_fast);
+                          L.use_fast, L.use_nt ? &ntw : nullptr);
   if (st != GDLA_OK) return st;
 
   // Eq.(5): expand K^C and V of every visible key, head-major [B, n_kv, lcap, *].  The MFMA path
@@ -370,13 +423,13 @@ GDLA_EXPORT gdla_status gdla_prefill(const gdla_dims *dims, const gdla_weights *
       const int32_t lo = key_lo(pos_host[b], d.window);
       const int32_t nk = pos_host[b] + T - lo;
       const char *a = (const char *)cache + ((int64_t)b * max_len + lo) * row * es;
-      GemmProblem pk = gp(a, row, w->w_uk, (int64_t)d.n_kv * d.d_h, at<char>(ws, L.kx) + b * k_seq * es,
-                          krow, nk, d.n_kv * d.d_h, d.d_c, false);
+      GemmProblem pk = gp(a, row, L.use_nt ? ntw.uk : w->w_uk, L.use_nt ? d.d_c : (int64_t)d.n_kv * d.d_h,
+                          at<char>(ws, L.kx) + b * k_seq * es, krow, nk, d.n_kv * d.d_h, d.d_c, false);
       pk.hw = d.d_h;
       pk.hs = (int64_t)L.lcap * krow;
       if (L.use_fast) pk.c_dt = CD_F16;
       GemmProblem pv = pk;
-      pv.B = w->w_uv;
+      pv.B = L.use_nt ? ntw.uv : w->w_uv;
       pv.C = at<char>(ws, L.vx) + b * v_seq * es;
       pv.ldc = d.d_h;
       pv.hs = (int64_t)L.lcap * d.d_h;
@@ -387,7 +440,8 @@ GDLA_EXPORT gdla_status gdla_prefill(const gdla_dims *dims, const gdla_weights *
       g.p[g.n++] = pk;
       g.p[g.n++] = pv;
     }
-    HIP_TRY(launch_gemm(g, dt, stream));
+    if (L.use_nt) HIP_TRY(launch_gemm_nt(g, false, stream));
+    else HIP_TRY(launch_gemm(g, dt, stream));
   }
   if (L.use_fast) {
     HIP_TRY(launch_kr_fill(cache, at<void>(ws, L.kx), pos_dev, B, T, L.lcap, max_len, d, stream));
@@ -399,7 +453,7 @@ GDLA_EXPORT gdla_status gdla_prefill(const gdla_dims *dims, const gdla_weights *
     st = run_fast_prefill(d, w, B, T, pos_dev, pos_host, cache, max_len, at<void>(ws, L.cq),
                           at<float>(ws, L.lam), at<float>(ws, L.gate), at<void>(ws, L.kx),
                           at<void>(ws, L.vx), L.lcap, at<void>(ws, L.y), out_heads, L.fast, ws,
-                          stream, se);
+                          stream, se, L.use_nt ? &ntw : nullptr);
     if (st != GDLA_OK) return fail(st, "fast prefill path failed: %s", hipGetErrorString(hipGetLastError()));
   } else {
     // Eq.(2), (9): q^C, pre-RoPE q^R and gate logits.
@@ -432,14 +486,16 @@ GDLA_EXPORT gdla_status gdla_prefill(const gdla_dims *dims, const gdla_weights *
   }
   // Eq.(10): out = Y W_o (Y is fp16 on the MFMA path).
   GemmBatch g{};
-  g.p[g.n++] = gp(at<void>(ws, L.y), (int64_t)d.n_signal * d.d_h, w->w_o, d.d_model, out, d.d_model, M,
-                  d.d_model, d.n_signal * d.d_h, false);
+  g.p[g.n++] = gp(at<void>(ws, L.y), (int64_t)d.n_signal * d.d_h, L.use_nt ? ntw.o : w->w_o,
+                  L.use_nt ? (int64_t)d.n_signal * d.d_h : d.d_model, out, d.d_model, M, d.d_model,
+                  d.n_signal * d.d_h, false);
   if (L.use_fast) {
     g.p[0].a_f16 = 1;
     g.p[0].c_dt = CD_BF16;
   }
   se.begin(GDLA_STAGE_PROJ_OUT);
-  HIP_TRY(launch_gemm(g, dt, stream));
+  if (L.use_nt) HIP_TRY(launch_gemm_nt(g, true, stream));
+  else HIP_TRY(launch_gemm(g, dt, stream));
   se.end(GDLA_STAGE_PROJ_OUT);
   se.finish();
   return GDLA_OK;

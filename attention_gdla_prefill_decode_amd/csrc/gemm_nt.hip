@@ -1,0 +1,240 @@
+// Large GEMM for the prefill projections on gfx950: C = A[M, K] . Bt[N, K]^T, both operands
+// K-contiguous (the weights arrive transposed, see transpose_weights below), fp16 x fp16 or
+// bf16 x bf16, fp32 accumulation, the epilogue options of GemmProblem.
+//
+// Used for the projections of the GDLA layer (Motif 3 Technical Report, picx.dev summary, section
+// 2.2: Eq.(1), (3), (7) input projections, Eq.(2), (9) query / gate projections, Eq.(5) expansion,
+// Eq.(10) output projection) when the problem is large enough to fill the chip.
+//
+// Block tile 256 x 256, K slices of 64 staged in LDS by direct global -> LDS 16-byte loads (two
+// stages of 64 KB; one in flight while the other is consumed).  8 waves in a 2 x 4 grid, each
+// computing 128 x 64 as 4 x 2 v_mfma_f32_32x32x16 blocks.  Both operands are read from LDS with
+// 16-byte reads (8 consecutive k of one row): with K-contiguous operands no transposing read is
+// needed, and the XOR swizzle (chunk c of row r at c ^ ((r >> 1) & 7)) keeps 16 consecutive rows
+// reading one chunk on distinct banks.  Tiles are spread so that each XCD gets a contiguous range.
+#include "fast_paths.h"
+
+namespace gdla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int ROWB = BK * 2;                  // bytes per staged row (128 = 8 chunks)
+constexpr int A_BYTES = BM * ROWB;            // 32 KB
+constexpr int STAGE_BYTES = (BM + BN) * ROWB; // 64 KB
+constexpr int WAVES = 8;
+constexpr int DMA_PER_WAVE = STAGE_BYTES / 1024 / WAVES;  // 16-byte loads per lane per stage (8)
+
+template <typename T> struct V8;
+template <> struct V8<bf16_t> { typedef bf16x8 t; };
+template <> struct V8<f16_t> { typedef f16x8 t; };
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// 16 bytes global -> LDS (M0 + 16 lane) outside the compiler's LDS-DMA tracking; the wait is the
+// explicit s_waitcnt vmcnt(0) before the barrier that publishes a stage.  M0 is set right before
+// the load (one wait state between them); nothing else in the kernel uses M0.
+__device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(lds_addr)
+               : "memory");
+}
+
+__device__ __forceinline__ int remap_xcd(int bid, int total) {
+  if (total < 8) return bid;
+  const int q = total / 8, r = total % 8, x = bid % 8, i = bid / 8;
+  return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(512, 1) gemm_nt_kernel(GemmBatch batch) {
+  typedef typename V8<T>::t v8;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE_BYTES];
+
+  const int bid = remap_xcd(blockIdx.x, batch.total_tiles);
+  int pi = 0;
+  while (pi + 1 < batch.n && bid >= batch.p[pi + 1].tile0) ++pi;
+  const GemmProblem &P = batch.p[pi];
+  const int tile = bid - P.tile0;
+  const int m0 = (tile / P.tiles_n) * BM, n0 = (tile % P.tiles_n) * BN;
+  const T *A = (const T *)P.A;
+  const T *Bt = (const T *)P.B;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 2, wn = wave & 3;  // wave tile rows 128 wm, cols 64 wn
+
+  // Global source offsets of this lane's DMA_PER_WAVE loads per stage (k0 added per stage): wave
+  // instruction j = wave + 8 i covers 64 chunks; j < 32 stage A rows, the rest Bt rows.  Rows
+  // past M / N are clamped to the last row (their results are never stored).
+  const T *src[DMA_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < DMA_PER_WAVE; ++i) {
+    const int j = wave + WAVES * i;
+    const int jj = j & 31;
+    const int sl = jj * 64 + lane;
+    const int row = sl >> 3, c = (sl & 7) ^ ((row >> 1) & 7);
+    if (j < 32) src[i] = A + (int64_t)min(m0 + row, P.M - 1) * P.lda + c * 8;
+    else src[i] = Bt + (int64_t)min(n0 + row, P.N - 1) * P.ldb + c * 8;
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)smem;
+  auto issue = [&](int stage, int k0) {
+    const uint32_t base = lds0 + stage * STAGE_BYTES;
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i) {
+      const int j = wave + WAVES * i;
+      dma16(src[i] + k0, __builtin_amdgcn_readfirstlane(base + j * 1024));
+    }
+  };
+
+  // Fragment reads: A block mb rows 128 wm + 32 mb + (lane % 32), Bt block nb rows
+  // 64 wn + 32 nb + (lane % 32); k-step kk reads chunk 2 kk + lane / 32.  The row swizzle
+  // depends on lane % 32 only, so the lane part of the offset depends on kk only.
+  const int r32 = lane & 31, h = lane >> 5;
+  int off[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) off[kk] = r32 * ROWB + (((2 * kk + h) ^ ((r32 >> 1) & 7)) * 16);
+  const int a_base = wm * 128 * ROWB, b_base = A_BYTES + wn * 64 * ROWB;
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  auto compute = [&](int stage) {
+    const unsigned char *sb = smem + stage * STAGE_BYTES;
+    v8 af[2][4], bfr[2][2];
+    auto ld = [&](int kk, v8 (&a)[4], v8 (&b)[2]) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) a[mb] = *(const v8 *)(sb + a_base + mb * 32 * ROWB + off[kk]);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) b[nb] = *(const v8 *)(sb + b_base + nb * 32 * ROWB + off[kk]);
+    };
+    ld(0, af[0], bfr[0]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk + 1 < 4) ld(kk + 1, af[(kk + 1) & 1], bfr[(kk + 1) & 1]);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma(af[kk & 1][mb], bfr[kk & 1][nb], acc[mb][nb]);
+      if (kk + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    }
+  };
+
+  const int nk = P.K / BK;
+  issue(0, 0);
+  for (int ks = 0; ks < nk; ++ks) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // stage ks % 2 has landed for every wave; stage (ks + 1) % 2 is free
+    if (ks + 1 < nk) issue((ks + 1) & 1, (ks + 1) * BK);
+    compute(ks & 1);
+  }
+
+  // epilogue: lane holds column (lane & 31) and rows 8 (j / 4) + 4 (lane / 32) + j % 4 of a block
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int n = n0 + wn * 64 + nb * 32 + r32;
+      if (n >= P.N) continue;
+      if (P.c_trans) {
+        f16_t *base = (f16_t *)P.C + (int64_t)(n / P.hw) * P.hs + P.ho + (int64_t)(n % P.hw) * P.ldc;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m = m0 + wm * 128 + mb * 32 + 8 * q + 4 * h;
+          if (m >= P.M) continue;
+          f16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (f16_t)fminf(fmaxf(acc[mb][nb][4 * q + e], -65504.f), 65504.f);
+          if (m + 3 < P.M) {
+            *(f16x4 *)(base + vt_slot(m)) = v;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (m + e < P.M) base[vt_slot(m + e)] = v[e];
+          }
+        }
+        continue;
+      }
+      const int64_t coff = (int64_t)(n / P.hw) * P.hs + P.ho + (n % P.hw);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int m = m0 + wm * 128 + mb * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
+        if (m >= P.M) continue;
+        float v = acc[mb][nb][j];
+        if (P.epi == EPI_SIGMOID) v = 1.0f / (1.0f + __expf(-v));
+        const int64_t o = (int64_t)m * P.ldc + coff;
+        if (P.c_dt == CD_F32) ((float *)P.C)[o] = v;
+        else if (P.c_dt == CD_F16 || (P.c_dt == CD_IN && __is_same(T, f16_t)))
+          ((f16_t *)P.C)[o] = (f16_t)fminf(fmaxf(v, -65504.f), 65504.f);
+        else ((bf16_t *)P.C)[o] = (bf16_t)v;
+      }
+    }
+  }
+}
+
+// Wt[n][k] = W[k][n] for a [K, N] bf16 weight, converted to fp16 (exact in the fp16 normal range,
+// round-to-nearest below it, saturating above) or kept in bf16.  64 x 64 tiles through LDS.
+template <typename TO>
+__global__ void __launch_bounds__(256) transpose_kernel(const bf16_t *W, TO *Wt, int32_t K, int32_t N) {
+  __shared__ float t[64][65];
+  const int k0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4) {
+    const int k = k0 + r, n = n0 + tx;
+    t[r][tx] = (k < K && n < N) ? (float)W[(int64_t)k * N + n] : 0.f;
+  }
+  __syncthreads();
+  for (int r = ty; r < 64; r += 4) {
+    const int n = n0 + r, k = k0 + tx;
+    if (n < N && k < K) {
+      const float v = t[tx][r];
+      if constexpr (__is_same(TO, f16_t)) Wt[(int64_t)n * K + k] = (f16_t)fminf(fmaxf(v, -65504.f), 65504.f);
+      else Wt[(int64_t)n * K + k] = (bf16_t)v;
+    }
+  }
+}
+
+}  // namespace
+
+bool nt_gemm_problem_ok(const GemmProblem &p) {
+  return p.K % BK == 0 && p.K > 0 && p.M > 0 && p.N > 0 && p.lda % 8 == 0 && p.ldb % 8 == 0 &&
+         ((uintptr_t)p.A & 15) == 0 && ((uintptr_t)p.B & 15) == 0 && p.hw > 0 &&
+         (!p.c_trans || (p.c_dt == CD_F16 && p.ldc % 4 == 0 && (p.hs + p.ho) % 4 == 0 &&
+                         ((uintptr_t)p.C & 7) == 0));
+}
+
+hipError_t launch_gemm_nt(GemmBatch &g, bool f16, hipStream_t s) {
+  int t = 0;
+  for (int i = 0; i < g.n; ++i) {
+    GemmProblem &p = g.p[i];
+    if (!nt_gemm_problem_ok(p)) return hipErrorInvalidValue;
+    p.tile0 = t;
+    p.tiles_n = (p.N + BN - 1) / BN;
+    t += ((p.M + BM - 1) / BM) * p.tiles_n;
+  }
+  g.total_tiles = t;
+  if (t == 0) return hipSuccess;
+  if (f16) hipLaunchKernelGGL(gemm_nt_kernel<f16_t>, dim3(t), dim3(64 * WAVES), 0, s, g);
+  else hipLaunchKernelGGL(gemm_nt_kernel<bf16_t>, dim3(t), dim3(64 * WAVES), 0, s, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_weight(const void *w, void *wt, int32_t K, int32_t N, bool to_f16, hipStream_t s) {
+  const dim3 grid((N + 63) / 64, (K + 63) / 64);
+  if (to_f16) hipLaunchKernelGGL(transpose_kernel<f16_t>, grid, dim3(256), 0, s, (const bf16_t *)w, (f16_t *)wt, K, N);
+  else hipLaunchKernelGGL(transpose_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t *)w, (bf16_t *)wt, K, N);
+  return hipGetLastError();
+}
+
+}  // namespace gdla
