@@ -407,11 +407,23 @@ gdla_status run_fast_prefill(const LayerDims &d, const gdla_weights *w, int32_t 
     g.p[g.n++] = p;
   };
   add(nt ? nt->qc : w->w_qc, d.n_heads * DH, q, (int64_t)d.n_heads * DQK, CD_F16, DH, DQK);
-  add(nt ? nt->qr : w->w_qr, d.n_heads * DR, qrp, (int64_t)d.n_heads * DR, CD_F32, d.n_heads * DR, 0);
+  if (nt) {
+    // q^R rotated in the GEMM epilogue, straight into columns 128 .. 191 of every head's q row
+    add(nt->qr, d.n_heads * DR, q, (int64_t)d.n_heads * DQK, CD_F16, DR, DQK);
+    GemmProblem &pr = g.p[g.n - 1];
+    pr.ho = DH;
+    pr.epi = EPI_ROPE;
+    pr.rope_pos = pos_dev;
+    pr.rope_T = T;
+    pr.rope_d = DR;
+    pr.rope_theta = d.theta;
+  } else {
+    add(w->w_qr, d.n_heads * DR, qrp, (int64_t)d.n_heads * DR, CD_F32, d.n_heads * DR, 0);
+  }
   add(nt ? nt->gate : w->w_gate, d.n_signal * DH, gate, (int64_t)d.n_signal * DH, CD_F32, d.n_signal * DH, 0);
   if ((nt ? launch_gemm_nt(g, true, s) : launch_gemm(g, DT::BF16, s)) != hipSuccess) return GDLA_ERR_HIP;
-  if (launch_rope_heads(qrp, q, (int64_t)d.n_heads * DQK, DQK, DH, M, T, d.n_heads, DR, pos_dev,
-                        d.theta, DT::F16, s) != hipSuccess)
+  if (!nt && launch_rope_heads(qrp, q, (int64_t)d.n_heads * DQK, DQK, DH, M, T, d.n_heads, DR, pos_dev,
+                               d.theta, DT::F16, s) != hipSuccess)
     return GDLA_ERR_HIP;
   se.end(GDLA_STAGE_PROJ_Q);
 

@@ -32,11 +32,17 @@ struct GemmProblem {
   int32_t a_f16;   // 1: A is fp16 and the bf16 B is converted to fp16 while staged (MFMA only)
   int32_t epi;     // EPI_*
   int32_t c_trans; // 1: transposed per-head store (see above)
+  // EPI_ROPE (transposed-weight GEMM only): columns come in heads of rope_d; column j < rope_d / 2
+  // and j + rope_d / 2 of a head are rotated by p * theta^(-2j / rope_d), p = rope_pos[m / rope_T]
+  // + m % rope_T (rotate-half RoPE), before the store.
+  const int32_t *rope_pos;
+  int32_t rope_T, rope_d;
+  float rope_theta;
   int32_t tile0;   // first linear tile index of this problem (filled by the launcher)
   int32_t tiles_n; // tiles along N (filled by the launcher)
 };
 
-enum { EPI_NONE = 0, EPI_SIGMOID = 1 };
+enum { EPI_NONE = 0, EPI_SIGMOID = 1, EPI_ROPE = 2 };
 // Output dtypes: fp32, the input dtype, bf16, fp16 (the generic kernel serves CD_F32 / CD_IN).
 enum { CD_F32 = 0, CD_IN = 1, CD_BF16 = 2, CD_F16 = 3 };
 

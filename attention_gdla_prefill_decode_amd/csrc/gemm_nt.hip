@@ -141,6 +141,32 @@ __global__ void __launch_bounds__(512, 1) gemm_nt_kernel(GemmBatch batch) {
   }
 
   // epilogue: lane holds column (lane & 31) and rows 8 (j / 4) + 4 (lane / 32) + j % 4 of a block
+  if (P.epi == EPI_ROPE) {
+    // heads of 64 columns: this wave's 64 columns are one head, and column j of block 0 pairs with
+    // column j + 32 of block 1 in the same lane
+    const int n = n0 + wn * 64 + r32;
+    if (n >= P.N) return;
+    // frequency in revolutions per position, fp64 so that positions up to 2^24 keep their phase
+    const double rev = pow((double)P.rope_theta, -2.0 * (double)r32 / (double)P.rope_d) * 0.15915494309189533577;
+    const int64_t coff = (int64_t)(n / P.hw) * P.hs + P.ho + (n % P.hw);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int m = m0 + wm * 128 + mb * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
+        if (m >= P.M) continue;
+        const int p = P.rope_pos[m / P.rope_T] + m % P.rope_T;
+        double turns = (double)p * rev;
+        turns -= floor(turns);  // angle / 2 pi, reduced to [0, 1)
+        const float sn = __builtin_amdgcn_sinf((float)turns), cs = __builtin_amdgcn_cosf((float)turns);
+        const float u = acc[mb][0][j], v = acc[mb][1][j];
+        f16_t *o = (f16_t *)P.C + (int64_t)m * P.ldc + coff;
+        o[0] = (f16_t)fminf(fmaxf(u * cs - v * sn, -65504.f), 65504.f);
+        o[32] = (f16_t)fminf(fmaxf(u * sn + v * cs, -65504.f), 65504.f);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
@@ -184,7 +210,37 @@ __global__ void __launch_bounds__(512, 1) gemm_nt_kernel(GemmBatch batch) {
 }
 
 // Wt[n][k] = W[k][n] for a [K, N] bf16 weight, converted to fp16 (exact in the fp16 normal range,
-// round-to-nearest below it, saturating above) or kept in bf16.  64 x 64 tiles through LDS.
+// round-to-nearest below it, saturating above) or kept in bf16.  64 x 64 tiles through LDS with
+// 16-byte global loads and stores (K and N multiples of 8; the scalar kernel serves the rest).
+template <typename TO>
+__global__ void __launch_bounds__(256) transpose16_kernel(const bf16_t *W, TO *Wt, int32_t K, int32_t N) {
+  __shared__ bf16_t t[64][72];  // row stride 144 B: consecutive rows of a column read hit distinct banks
+  const int k0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = threadIdx.x + 256 * i;
+    const int r = q >> 3, c = (q & 7) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (k0 + r < K && n0 + c < N) v = *(const uint4 *)(W + (int64_t)(k0 + r) * N + n0 + c);
+    *(uint4 *)&t[r][c] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = threadIdx.x + 256 * i;
+    const int rn = q >> 3, kc = (q & 7) * 8;
+    if (n0 + rn >= N || k0 + kc >= K) continue;
+    TO o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = (float)t[kc + e][rn];
+      if constexpr (__is_same(TO, f16_t)) o[e] = (f16_t)fminf(fmaxf(v, -65504.f), 65504.f);
+      else o[e] = (bf16_t)v;
+    }
+    *(uint4 *)(Wt + (int64_t)(n0 + rn) * K + k0 + kc) = *(const uint4 *)o;
+  }
+}
+
 template <typename TO>
 __global__ void __launch_bounds__(256) transpose_kernel(const bf16_t *W, TO *Wt, int32_t K, int32_t N) {
   __shared__ float t[64][65];
@@ -210,6 +266,8 @@ __global__ void __launch_bounds__(256) transpose_kernel(const bf16_t *W, TO *Wt,
 bool nt_gemm_problem_ok(const GemmProblem &p) {
   return p.K % BK == 0 && p.K > 0 && p.M > 0 && p.N > 0 && p.lda % 8 == 0 && p.ldb % 8 == 0 &&
          ((uintptr_t)p.A & 15) == 0 && ((uintptr_t)p.B & 15) == 0 && p.hw > 0 &&
+         (p.epi != EPI_ROPE || (p.rope_d == 64 && p.hw % 64 == 0 && p.N % 64 == 0 && p.c_dt == CD_F16 &&
+                                p.rope_pos && p.rope_T > 0)) &&
          (!p.c_trans || (p.c_dt == CD_F16 && p.ldc % 4 == 0 && (p.hs + p.ho) % 4 == 0 &&
                          ((uintptr_t)p.C & 7) == 0));
 }
@@ -232,8 +290,15 @@ hipError_t launch_gemm_nt(GemmBatch &g, bool f16, hipStream_t s) {
 
 hipError_t launch_transpose_weight(const void *w, void *wt, int32_t K, int32_t N, bool to_f16, hipStream_t s) {
   const dim3 grid((N + 63) / 64, (K + 63) / 64);
-  if (to_f16) hipLaunchKernelGGL(transpose_kernel<f16_t>, grid, dim3(256), 0, s, (const bf16_t *)w, (f16_t *)wt, K, N);
-  else hipLaunchKernelGGL(transpose_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t *)w, (bf16_t *)wt, K, N);
+  const bool vec = K % 8 == 0 && N % 8 == 0 && ((uintptr_t)w & 15) == 0 && ((uintptr_t)wt & 15) == 0;
+  if (vec && to_f16)
+    hipLaunchKernelGGL(transpose16_kernel<f16_t>, grid, dim3(256), 0, s, (const bf16_t *)w, (f16_t *)wt, K, N);
+  else if (vec)
+    hipLaunchKernelGGL(transpose16_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t *)w, (bf16_t *)wt, K, N);
+  else if (to_f16)
+    hipLaunchKernelGGL(transpose_kernel<f16_t>, grid, dim3(256), 0, s, (const bf16_t *)w, (f16_t *)wt, K, N);
+  else
+    hipLaunchKernelGGL(transpose_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t *)w, (bf16_t *)wt, K, N);
   return hipGetLastError();
 }
 
