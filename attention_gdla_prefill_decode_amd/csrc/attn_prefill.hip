@@ -14,10 +14,9 @@
 // signal heads sharing one KV head times 2 halves of the same 64 tokens, so each K/V tile staged
 // in LDS serves all of them; in the noise launch the waves are 8 consecutive 32-token blocks of one
 // noise head.  Keys are processed in tiles of 64:
-//   staging: direct global -> LDS 16-byte loads (no staging registers), double buffered, the two
-//     buffers distinct LDS arrays so that the compiler waits for a tile's loads only at the
-//     barrier that publishes it; rows are unpadded and XOR-swizzled per 16-byte chunk so both LDS
-//     read patterns below are free of bank conflicts;
+//   staging: direct global -> LDS 16-byte loads (no staging registers) into three tile buffers,
+//     so two tiles are in flight while one is read; rows are unpadded and XOR-swizzled per 16-byte
+//     chunk so both LDS read patterns below are free of bank conflicts;
 //   S^T[key, query] = K[key, 0:192] . Q[query, 0:192]   (A = K from LDS, B = Q in registers);
 //   online softmax per query (each lane owns one query column; its partner lane l^32 the other
 //     half of the keys), with lazy rescaling, P^T taken straight from the accumulators in fp16;
@@ -36,10 +35,7 @@ namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int DH = 128, DR = 64, DQK = DH + DR;
 constexpr int KT = 64;                 // keys per tile
@@ -47,6 +43,9 @@ constexpr int K_CH = DQK / 8;          // 16-byte chunks per key row (24)
 constexpr int V_CH = DH / 8;           // 16-byte chunks per value row (16)
 constexpr int K_TILE = KT * DQK;       // elements of one K tile
 constexpr int V_TILE = KT * DH;        // elements of one V tile
+constexpr int NBUF = 3;                // LDS tile buffers: two tiles in flight while one is read
+constexpr int K_LOADS = K_TILE * 2 / 16 / 64 / 8;  // 16-byte K loads per wave per tile (3)
+constexpr int V_LOADS = V_TILE * 2 / 16 / 64 / 8;  // 16-byte V^T loads per wave per tile (2)
 
 struct AttnArgs {
   const f16_t *q;         // [M, n_H, 192] fp16: q^C then rotated q^R of each head
@@ -71,6 +70,22 @@ constexpr int VT_CH = KT / 8;
 __device__ __forceinline__ int kslot(int row, int c) { return row * K_CH + (c ^ ((row >> 1) & 7)); }
 __device__ __forceinline__ int vslot(int row, int c) { return row * VT_CH + (c ^ ((row >> 1) & 7)); }
 
+// 16 bytes global -> LDS (M0 + 16 lane) without the compiler's LDS-DMA tracking, so that the wait
+// for a tile is explicit (s_waitcnt vmcnt before the barrier that publishes it) and can leave the
+// next tile's loads in flight.  The global address is a wave-uniform base plus a 32-bit per-lane
+// byte offset.  M0 is set right before the load (one wait state between them); nothing else in
+// the kernel uses M0.
+__device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
 __device__ __forceinline__ f32x16 mfma(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
@@ -89,10 +104,8 @@ __device__ __forceinline__ float pair_sum(float v) {
 
 template <bool SIGNAL>
 __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) f16_t Ks0[K_TILE];
-  __shared__ __attribute__((aligned(16))) f16_t Ks1[K_TILE];
-  __shared__ __attribute__((aligned(16))) f16_t Vs0[V_TILE];
-  __shared__ __attribute__((aligned(16))) f16_t Vs1[V_TILE];
+  // NBUF buffers of one key tile each: K rows, then V^T rows
+  __shared__ __attribute__((aligned(16))) f16_t KV[NBUF * (K_TILE + V_TILE)];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = blockIdx.z;
@@ -132,33 +145,39 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
     const f16_t *qp = a.q + ((mrow0 + (ok ? t : 0)) * a.n_heads + (ok ? head : 0)) * DQK + 8 * (lane >> 5);
 #pragma unroll
     for (int ks = 0; ks < 12; ++ks) Qf[ks] = ok ? *(const f16x8 *)(qp + 16 * ks) : f16x8{};
+    // Q has landed before any tile load is issued: the compiler does not see the tile loads, and
+    // a vmcnt(0) it placed for Q inside the loop would also wait for the tiles in flight.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   }
 
-  // ---- direct global -> LDS staging of one key tile.  Keys past khi are clamped to khi - 1: they
-  // are masked for every valid query, and clamping keeps every load inside the buffers.
+  // ---- direct global -> LDS staging of one key tile.  The last tile may run up to 63 keys past
+  // khi: the buffers hold lcap >= (keys rounded up to 64) + 64 rows, those keys are masked for
+  // every valid query (any value, NaN included, is replaced), and their values are the
+  // expansion's zeroed tail.
   const f16_t *kxh = a.kx + ((int64_t)b * a.n_kv + kvh) * a.lcap * DQK;
   const f16_t *vth = a.vx + ((int64_t)b * a.n_kv + kvh) * DH * a.lcap;
-  auto issue = [&](f16_t *ks, f16_t *vs, int s0) {
+  // per-lane byte offsets of this wave's K and V^T loads within a tile (rows swizzled per chunk)
+  uint32_t koff[K_LOADS], voff[V_LOADS];
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {  // K: 24 wave-instructions of 64 chunks, 3 per wave
-      const int slot0 = (wave * 3 + j) * 64;
-      const int slot = slot0 + lane;
-      const int row = slot / K_CH, cpos = slot % K_CH;
-      const int c = cpos ^ ((row >> 1) & 7);
-      const int s = min(s0 + row, khi - 1);
-      __builtin_amdgcn_global_load_lds(kxh + (int64_t)(s - base) * DQK + c * 8, (lds_void *)(ks + slot0 * 8),
-                                       16, 0, 0);
-    }
+  for (int j = 0; j < K_LOADS; ++j) {  // K: 24 wave-instructions of 64 chunks
+    const int slot = (wave * K_LOADS + j) * 64 + lane;
+    const int row = slot / K_CH, cpos = slot % K_CH;
+    koff[j] = (uint32_t)(row * DQK + (cpos ^ ((row >> 1) & 7)) * 8) * 2;
+  }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {  // V^T: 128 dims x 8 chunks = 16 wave-instructions, 2 per wave
-      // keys past khi hold finite values (the expansion's zeroed tail), and get zero probability
-      const int slot0 = (wave * 2 + j) * 64;
-      const int slot = slot0 + lane;
-      const int row = slot / VT_CH, cpos = slot % VT_CH;
-      const int c = cpos ^ ((row >> 1) & 7);
-      __builtin_amdgcn_global_load_lds(vth + (int64_t)row * a.lcap + (s0 - base) + c * 8,
-                                       (lds_void *)(vs + slot0 * 8), 16, 0, 0);
-    }
+  for (int j = 0; j < V_LOADS; ++j) {  // V^T: 128 dims x 8 chunks = 16 wave-instructions
+    const int slot = (wave * V_LOADS + j) * 64 + lane;
+    const int row = slot / VT_CH, cpos = slot % VT_CH;
+    voff[j] = (uint32_t)(row * a.lcap + (cpos ^ ((row >> 1) & 7)) * 8) * 2;
+  }
+  auto issue = [&](int t) {
+    const int s0 = klo + t * KT;
+    f16_t *buf = KV + (t % NBUF) * (K_TILE + V_TILE);
+    const uint32_t kl = lds_u32(buf), vl = lds_u32(buf + K_TILE);
+#pragma unroll
+    for (int j = 0; j < K_LOADS; ++j) dma16(kxh + (int64_t)(s0 - base) * DQK, koff[j], kl + (wave * K_LOADS + j) * 1024);
+#pragma unroll
+    for (int j = 0; j < V_LOADS; ++j) dma16(vth + (s0 - base), voff[j], vl + (wave * V_LOADS + j) * 1024);
   };
 
   f32x16 O[4];
@@ -265,18 +284,16 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
     }
   };
 
-  // Double buffering over two distinct LDS arrays (loop unrolled by two).
-  if (ntiles > 0) issue(Ks0, Vs0, klo);
-  __syncthreads();
-  for (int it = 0; it < ntiles; it += 2) {
-    const int s0 = klo + it * KT;
-    if (it + 1 < ntiles) issue(Ks1, Vs1, s0 + KT);
-    compute(Ks0, Vs0, s0);
-    __syncthreads();
-    if (it + 1 >= ntiles) break;
-    if (it + 2 < ntiles) issue(Ks0, Vs0, s0 + 2 * KT);
-    compute(Ks1, Vs1, s0 + KT);
-    __syncthreads();
+  // Triple buffering: tiles t + 1 and t + 2 are in flight while tile t is read.
+  for (int t = 0; t < NBUF - 1 && t < ntiles; ++t) issue(t);
+  for (int t = 0; t < ntiles; ++t) {
+    // vmcnt(n): at most n of this wave's loads still in flight (those of tile t + 1)
+    if (t + 1 < ntiles) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(K_LOADS + V_LOADS) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // tile t has landed for every wave; every wave is done with tile t - 1
+    if (t + NBUF - 1 < ntiles) issue(t + NBUF - 1);
+    const f16_t *kv = KV + (t % NBUF) * (K_TILE + V_TILE);
+    compute(kv, kv + K_TILE, klo + t * KT);
   }
 
   if (!active) return;
