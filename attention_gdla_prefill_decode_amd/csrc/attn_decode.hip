@@ -138,12 +138,17 @@ __device__ __forceinline__ uint32_t lds_u32(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
 
-template <bool SHARED>
-__global__ void __launch_bounds__(256, 1) latent_decode_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t CB[NBUF * TILE];
-  __shared__ __attribute__((aligned(16))) bf16x8 PB[MAX_WAVES][64];  // P^T of head blocks 0..3
+// Shared head block (heads 64..79): its 36 score MFMAs per tile are split over the waves, wave
+// ROLE taking key block ROLE / 2 and k-steps 9 (ROLE % 2) .. + 8 with the fragments it reads for its
+// own block anyway; the partial sums meet in LDS and every wave then takes the same softmax of the
+// whole block (so its P^T needs no further exchange).
+constexpr int K4N = NKST / 2;  // k-steps of the shared block per wave (9)
 
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+template <bool SHARED, int ROLE>
+__device__ __forceinline__ void decode_body(const DecodeArgs &a, bf16_t *CB, bf16x8 (*PB)[64], f32x4 (*S4B)[64],
+                                            int wave) {
+  constexpr int KB4 = ROLE >> 1, K4LO = (ROLE & 1) * K4N;
+  const int lane = threadIdx.x & 63;
   const int b = blockIdx.y, sp = blockIdx.x;
   const int p = a.pos[b];
   const int lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
@@ -155,8 +160,9 @@ __global__ void __launch_bounds__(256, 1) latent_decode_kernel(DecodeArgs a) {
   const int head = 16 * wave + col, head4 = 16 * MAX_WAVES + col;
   const bool head_ok = head < a.n_heads, head4_ok = SHARED && head4 < a.n_heads;
 
-  // q~ fragments (B operand): Qf[kst] = dims 32 kst + 8 g .. + 7 of head `head`; Q4 of `head4`
-  bf16x8 Qf[NKST], Q4[SHARED ? NKST : 1];
+  // q~ fragments (B operand): Qf[kst] = dims 32 kst + 8 g .. + 7 of head `head`; Q4[k] those of
+  // head `head4` at k-step K4LO + k
+  bf16x8 Qf[NKST], Q4[SHARED ? K4N : 1];
   {
     const bf16_t *qb = a.qabs + (int64_t)b * a.n_heads * ROW + 8 * g;
     const bf16_t *qp = qb + (int64_t)(head_ok ? head : 0) * ROW;
@@ -168,8 +174,8 @@ __global__ void __launch_bounds__(256, 1) latent_decode_kernel(DecodeArgs a) {
     if (SHARED) {
       const bf16_t *q4 = qb + (int64_t)(head4_ok ? head4 : 0) * ROW;
 #pragma unroll
-      for (int k = 0; k < NKST; ++k) {
-        Q4[k] = *(const bf16x8 *)(q4 + 32 * k);
+      for (int k = 0; k < K4N; ++k) {
+        Q4[k] = *(const bf16x8 *)(q4 + 32 * (K4LO + k));
         if (!head4_ok) Q4[k] = bf16x8{};
       }
     }
@@ -233,9 +239,10 @@ __global__ void __launch_bounds__(256, 1) latent_decode_kernel(DecodeArgs a) {
 
   auto compute = [&](const bf16_t *cs, int s0) {
     const char *cbyte = (const char *)cs;
-    f32x4 S[2], S4[2];
+    f32x4 S[2], S4p;
     // S phase, key block by key block, software-pipelined two k-steps ahead:
-    // [reads of step n + 2][MFMAs of step n]; the own and the shared block use the same fragment
+    // [reads of step n + 2][MFMAs of step n]; the own block and this wave's part of the shared
+    // block use the same fragment
     bf16x8 af[3];
     auto ldA = [&](bf16x8 &f, int n) {  // n = 18 kb + kst
       const int kb = n / NKST, kst = n % NKST;
@@ -248,21 +255,28 @@ __global__ void __launch_bounds__(256, 1) latent_decode_kernel(DecodeArgs a) {
     for (int n = 0; n < 2 * NKST; ++n) {
       const int kb = n / NKST, kst = n % NKST;
       if (n + 2 < 2 * NKST) ldA(af[(n + 2) % 3], n + 2);
+      const bool part4 = SHARED && kb == KB4 && kst >= K4LO && kst < K4LO + K4N;
       S[kb] = mfma16(af[n % 3], Qf[kst], kst == 0 ? f32x4{} : S[kb]);
-      if (SHARED) S4[kb] = mfma16(af[n % 3], Q4[kst], kst == 0 ? f32x4{} : S4[kb]);
+      if (part4) S4p = mfma16(af[n % 3], Q4[kst - K4LO], kst == K4LO ? f32x4{} : S4p);
       if (n + 2 < 2 * NKST) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, SHARED ? 2 : 1, 0);
+      if (part4) __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      else __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
-    bf16x8 P, P4;
+    bf16x8 P;
     const int lim = k_end - s0 - 4 * g;
     softmax_tile(S, st, lim, a.c, P);
-    if (SHARED) softmax_tile(S4, st4, lim, a.c, P4);
+    if (SHARED) S4B[wave][lane] = S4p;
     PB[wave][lane] = P;
-    __syncthreads();  // P^T of blocks 0..3 visible to every wave
+    __syncthreads();  // P^T of blocks 0..3 and the shared block's partial scores visible to every wave
     bf16x8 PH[HB];
 #pragma unroll
     for (int hb = 0; hb < MAX_WAVES; ++hb) PH[hb] = PB[hb][lane];
-    if (SHARED) PH[HB - 1] = P4;
+    if (SHARED) {
+      f32x4 S4[2];
+      S4[0] = S4B[0][lane] + S4B[1][lane];
+      S4[1] = S4B[2][lane] + S4B[3][lane];
+      softmax_tile(S4, st4, lim, a.c, PH[HB - 1]);
+    }
     // PV phase over this wave's dim blocks, pipelined two ahead: [reads of dd + 2][MFMAs of dd]
     bf16x8 vf[3];
     auto ldV = [&](bf16x8 &f, int dd) {
@@ -340,6 +354,24 @@ __global__ void __launch_bounds__(256, 1) latent_decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int dd = 0; dd < WDB; ++dd)
       *(float4 *)(po + 16 * dd) = make_float4(O[hb][dd][0], O[hb][dd][1], O[hb][dd][2], O[hb][dd][3]);
+  }
+}
+
+template <bool SHARED>
+__global__ void __launch_bounds__(256, 1) latent_decode_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16_t CB[NBUF * TILE];
+  __shared__ __attribute__((aligned(16))) bf16x8 PB[MAX_WAVES][64];   // P^T of head blocks 0..3
+  __shared__ __attribute__((aligned(16))) f32x4 S4B[MAX_WAVES][64];   // partial scores, shared block
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (!SHARED) {
+    decode_body<false, 0>(a, CB, PB, S4B, wave);
+  } else {
+    switch (wave) {  // wave-uniform: each wave runs the code of its part of the shared block
+      case 0: decode_body<true, 0>(a, CB, PB, S4B, 0); break;
+      case 1: decode_body<true, 1>(a, CB, PB, S4B, 1); break;
+      case 2: decode_body<true, 2>(a, CB, PB, S4B, 2); break;
+      default: decode_body<true, 3>(a, CB, PB, S4B, 3); break;
+    }
   }
 }
 

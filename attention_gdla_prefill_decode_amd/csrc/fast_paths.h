@@ -17,6 +17,16 @@ hipError_t launch_gemm_nt(GemmBatch &g, bool f16, hipStream_t s);
 // Wt[N, K] = W[K, N]^T of a bf16 weight, as fp16 (to_f16) or bf16.
 hipError_t launch_transpose_weight(const void *w, void *wt, int32_t K, int32_t N, bool to_f16, hipStream_t s);
 
+// ---- skinny GEMM for decode batches (M <= 64 rows, N a multiple of 64, K of 64; bf16 A and B
+// with B in its stored [K, N] layout; fp32 or bf16 C).  Split along K when the column tiles do
+// not fill the chip; the fp32 partial sums need skinny_gemm_partial_bytes(g) of workspace, never
+// more than skinny_gemm_partial_bound(M). ----
+bool skinny_problem_ok(const GemmProblem &p);
+bool skinny_gemm_ok(const GemmBatch &g);  // every problem ok, one M for all
+size_t skinny_gemm_partial_bytes(const GemmBatch &g);
+size_t skinny_gemm_partial_bound(int32_t M);
+hipError_t launch_gemm_skinny(const GemmBatch &g, void *partial, size_t partial_bytes, hipStream_t s);
+
 // Transposed copies of the layer weights in the workspace (prefill with enough rows to amortise
 // them): x-side weights stay bf16, the weights applied to fp16 activations become fp16.
 struct NtWeights {

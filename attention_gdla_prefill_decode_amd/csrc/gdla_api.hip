@@ -142,7 +142,8 @@ PrefillLayout plan_prefill(const LayerDims &d, gdla_dtype dt, int32_t B, int32_t
 }
 
 struct DecodeLayout {
-  size_t pos, aq, ckv, krp, laml, cq, lam, qc, qrp, qr, gate, qabs, o, heads, y, total;
+  size_t pos, aq, ckv, krp, laml, cq, lam, qc, qrp, qr, gate, qabs, o, heads, y, skinny, total;
+  size_t skinny_bytes;  // split-K partial sums of the skinny projection GEMMs (0: not used)
   FastDecodeLayout fast;
   bool use_fast;
 };
@@ -166,6 +167,8 @@ DecodeLayout plan_decode(const LayerDims &d, gdla_dtype dt, int32_t B, int32_t m
   L.gate = p.add(4 * M * d.n_signal * d.d_h);
   L.heads = p.add(4 * M * d.n_heads * d.d_h);
   L.y = p.add(es * M * d.n_signal * d.d_h);
+  L.skinny_bytes = (dt == GDLA_BF16 && B <= 64) ? skinny_gemm_partial_bound(B) : 0;
+  L.skinny = p.add(L.skinny_bytes);
   if (L.use_fast) {
     L.fast = plan_fast_decode(d, B, max_len, [&](size_t n) { return p.add(n); });
   } else {
@@ -241,13 +244,33 @@ GemmProblem gp(const void *A, int64_t lda, const void *B, int64_t ldb, void *C, 
   return p;
 }
 
+// The projections of a decode batch: problems the skinny split-K kernel serves (bf16, at most 64
+// rows, columns in tiles of 64) run there, given workspace for its partial sums; the rest go to
+// the general dispatch.
+hipError_t launch_gemm_rows(GemmBatch &g, DT dt, void *partial, size_t partial_bytes, hipStream_t s) {
+  if (dt != DT::BF16 || partial_bytes == 0) return launch_gemm(g, dt, s);
+  GemmBatch sk{}, rest{};
+  for (int i = 0; i < g.n; ++i) {
+    if (skinny_problem_ok(g.p[i])) sk.p[sk.n++] = g.p[i];
+    else rest.p[rest.n++] = g.p[i];
+  }
+  if (sk.n && skinny_gemm_partial_bytes(sk) <= partial_bytes) {
+    const hipError_t e = launch_gemm_skinny(sk, partial, partial_bytes, s);
+    if (e != hipSuccess) return e;
+  } else {
+    for (int i = 0; i < sk.n; ++i) rest.p[rest.n++] = sk.p[i];
+  }
+  return rest.n ? launch_gemm(rest, dt, s) : hipSuccess;
+}
+
 // First projection, Eq.(1), (3), (7) (x W_qa, x W_dkv, x W_kr, x W_lambda) and the row-wise
 // normalisation / RoPE / cache append / sigmoid step.
 gdla_status project_and_append(const LayerDims &d, DT dt, const gdla_weights *w, const void *x,
                                int32_t M, int32_t T, const int32_t *pos_dev, void *cache,
                                int32_t max_len, float *aq, float *ckv, float *krp, float *laml,
                                void *cq, float *lam, const float *lam_override, hipStream_t s,
-                               StageEvents &se, bool cq_f16 = false, const NtWeights *nt = nullptr) {
+                               StageEvents &se, bool cq_f16 = false, const NtWeights *nt = nullptr,
+                               void *partial = nullptr, size_t partial_bytes = 0) {
   GemmBatch g{};
   // with nt, B is the transposed weight [N, K] (row stride K = d_model)
   auto wb = [&](const void *w_, const void *wt) { return nt ? wt : w_; };
@@ -267,7 +290,7 @@ gdla_status project_and_append(const LayerDims &d, DT dt, const gdla_weights *w,
     HIP_TRY(launch_gemm_nt(g, false, s));
   } else {
     se.begin(GDLA_STAGE_PROJ_IN);
-    HIP_TRY(launch_gemm(g, dt, s));
+    HIP_TRY(launch_gemm_rows(g, dt, partial, partial_bytes, s));
   }
   se.end(GDLA_STAGE_PROJ_IN);
   PrepArgs a{};
@@ -520,9 +543,11 @@ GDLA_EXPORT gdla_status gdla_decode(const gdla_dims *dims, const gdla_weights *w
 
   int32_t *pos_dev = at<int32_t>(ws, L.pos);
   HIP_TRY(launch_set_i32(pos_dev, pos_host, B, stream));
+  void *partial = at<void>(ws, L.skinny);
   st = project_and_append(d, dt, w, x, B, 1, pos_dev, cache, max_len, at<float>(ws, L.aq),
                           at<float>(ws, L.ckv), at<float>(ws, L.krp), at<float>(ws, L.laml),
-                          at<void>(ws, L.cq), at<float>(ws, L.lam), lam_override, stream, se);
+                          at<void>(ws, L.cq), at<float>(ws, L.lam), lam_override, stream, se, false, nullptr,
+                          partial, L.skinny_bytes);
   if (st != GDLA_OK) return st;
   // Eq.(2), (9) in fp32 (decode keeps the query in fp32 until it is mapped into the latent).
   se.begin(GDLA_STAGE_PROJ_Q);
@@ -533,7 +558,7 @@ GDLA_EXPORT gdla_status gdla_decode(const gdla_dims *dims, const gdla_weights *w
                   (int64_t)d.n_heads * d.d_r, B, d.n_heads * d.d_r, d.d_cq, true);
   g.p[g.n++] = gp(at<void>(ws, L.cq), d.d_cq, w->w_gate, (int64_t)d.n_signal * d.d_h, at<float>(ws, L.gate),
                   (int64_t)d.n_signal * d.d_h, B, d.n_signal * d.d_h, d.d_cq, true);
-  HIP_TRY(launch_gemm(g, dt, stream));
+  HIP_TRY(launch_gemm_rows(g, dt, partial, L.skinny_bytes, stream));
   HIP_TRY(launch_rope_heads(at<float>(ws, L.qrp), at<float>(ws, L.qr), (int64_t)d.n_heads * d.d_r, d.d_r, 0,
                             B, 1, d.n_heads, d.d_r, pos_dev, d.theta, DT::F32, stream));
   if (L.use_fast) {
@@ -562,7 +587,7 @@ GDLA_EXPORT gdla_status gdla_decode(const gdla_dims *dims, const gdla_weights *w
   g.p[g.n++] = gp(at<void>(ws, L.y), (int64_t)d.n_signal * d.d_h, w->w_o, d.d_model, out, d.d_model, B,
                   d.d_model, d.n_signal * d.d_h, false);
   se.begin(GDLA_STAGE_PROJ_OUT);
-  HIP_TRY(launch_gemm(g, dt, stream));
+  HIP_TRY(launch_gemm_rows(g, dt, partial, L.skinny_bytes, stream));
   se.end(GDLA_STAGE_PROJ_OUT);
   se.finish();
   return GDLA_OK;
