@@ -60,6 +60,8 @@ struct AttnArgs {
   int32_t T, lcap;
   int32_t n_heads, n_signal, n_noise, n_kv, window;
   int32_t sig_per_kv, chunks, n_qblk;
+  int32_t ny;             // workgroups per query block and sequence (KV-head chunks or noise heads)
+  int32_t nb;             // sequences
   float c;                // softmax scale * log2(e)
 };
 
@@ -108,19 +110,24 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) f16_t KV[NBUF * (K_TILE + V_TILE)];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int b = blockIdx.z;
-  const int qblk = a.n_qblk - 1 - (int)blockIdx.x;  // late (long) query blocks first
+  // 1-D grid, longest work first: late (long) query blocks of every head and sequence before any
+  // earlier one.  The head index varies fastest, so with 16 KV heads each of the 8 XCDs (which
+  // take workgroups round-robin) always serves the same two KV heads and their K/V stay in its L2.
+  const int per_q = a.ny * a.nb;
+  const int qblk = a.n_qblk - 1 - (int)blockIdx.x / per_q;
+  const int yy = (int)blockIdx.x % per_q % a.ny;
+  const int b = (int)blockIdx.x % per_q / a.ny;
   int head, kvh, t0w, tlo, thi;
   if (SIGNAL) {
-    kvh = blockIdx.y / a.chunks;
-    const int r = (blockIdx.y % a.chunks) * 4 + (wave >> 1);
+    kvh = yy / a.chunks;
+    const int r = (yy % a.chunks) * 4 + (wave >> 1);
     head = r < a.sig_per_kv ? kvh + a.n_kv * r : -1;
     tlo = qblk * 64;
     t0w = tlo + 32 * (wave & 1);
     thi = min(tlo + 63, a.T - 1);
   } else {
-    head = a.n_signal + blockIdx.y;
-    kvh = blockIdx.y % a.n_kv;
+    head = a.n_signal + yy;
+    kvh = yy % a.n_kv;
     tlo = qblk * 256;
     t0w = tlo + 32 * wave;
     thi = min(tlo + 255, a.T - 1);
@@ -454,13 +461,16 @@ gdla_status run_fast_prefill(const LayerDims &d, const gdla_weights *w, int32_t 
   a.chunks = (a.sig_per_kv + 3) / 4;
   a.c = d.scale * 1.4426950408889634f;
   a.n_qblk = (T + 255) / 256;
+  a.ny = d.n_noise;
   se.begin(GDLA_STAGE_ATTN_NOISE);
-  hipLaunchKernelGGL(attn_prefill_kernel<false>, dim3(a.n_qblk, d.n_noise, B), dim3(512), 0, s, a);
+  a.nb = B;
+  hipLaunchKernelGGL(attn_prefill_kernel<false>, dim3(a.n_qblk * a.ny * B), dim3(512), 0, s, a);
   if (hipGetLastError() != hipSuccess) return GDLA_ERR_HIP;
   se.end(GDLA_STAGE_ATTN_NOISE);
   a.n_qblk = (T + 63) / 64;
+  a.ny = d.n_kv * a.chunks;
   se.begin(GDLA_STAGE_ATTN_SIGNAL);
-  hipLaunchKernelGGL(attn_prefill_kernel<true>, dim3(a.n_qblk, d.n_kv * a.chunks, B), dim3(512), 0, s, a);
+  hipLaunchKernelGGL(attn_prefill_kernel<true>, dim3(a.n_qblk * a.ny * B), dim3(512), 0, s, a);
   if (hipGetLastError() != hipSuccess) return GDLA_ERR_HIP;
   se.end(GDLA_STAGE_ATTN_SIGNAL);
   return GDLA_OK;
