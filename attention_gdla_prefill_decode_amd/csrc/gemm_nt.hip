@@ -14,6 +14,8 @@
 // reading one chunk on distinct banks.  Tiles are spread so that each XCD gets a contiguous range.
 #include "fast_paths.h"
 
+#include <type_traits>
+
 namespace gdla {
 namespace {
 
@@ -52,6 +54,80 @@ __device__ __forceinline__ int remap_xcd(int bid, int total) {
   if (total < 8) return bid;
   const int q = total / 8, r = total % 8, x = bid % 8, i = bid / 8;
   return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
+
+// Epilogue through LDS: the wave stages 32 rows x its 64 columns at a time (after the epilogue
+// function, in the output type: KIND 0 fp32, 1 fp16, 2 bf16) in its own area `wt` and writes them
+// back as 16-byte row segments, which lie inside one head since head widths are multiples of 8.
+// Staged rows are padded so the two rows a staging store touches (4 apart) fall on other banks.
+// acc[mb][nb][j] = C[r0 + 32 mb + 8 (j / 4) + 4 (lane / 32) + j % 4][c0 + 32 nb + lane % 32].
+template <int KIND>
+__device__ __forceinline__ void staged_epilogue(const GemmProblem &P, const f32x16 (&acc)[4][2], unsigned char *wt,
+                                                int r0, int c0, int lane) {
+  constexpr int ESZ = KIND == 0 ? 4 : 2, EPS = 16 / ESZ, SPR = 64 / EPS;
+  constexpr int PITCH = KIND == 0 ? 272 : 144;
+  const int r32 = lane & 31, h = lane >> 5;
+  const double rev = P.epi == EPI_ROPE
+                         ? pow((double)P.rope_theta, -2.0 * (double)r32 / (double)P.rope_d) * 0.15915494309189533577
+                         : 0.0;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int mrow0 = r0 + mb * 32;
+    float v0[16], v1[16];  // columns r32 and r32 + 32
+    if (P.epi == EPI_ROPE) {
+      // heads of 64 columns: the wave's 64 columns are one head, and column j of block 0 pairs
+      // with column j + 32 of block 1 in the same lane
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int m = min(mrow0 + 8 * (j >> 2) + 4 * h + (j & 3), P.M - 1);
+        const int pp = P.rope_pos[m / P.rope_T] + m % P.rope_T;
+        double turns = (double)pp * rev;
+        turns -= floor(turns);  // angle / 2 pi, reduced to [0, 1)
+        const float sn = __builtin_amdgcn_sinf((float)turns), cs = __builtin_amdgcn_cosf((float)turns);
+        const float u = acc[mb][0][j], v = acc[mb][1][j];
+        v0[j] = u * cs - v * sn;
+        v1[j] = u * sn + v * cs;
+      }
+    } else if (P.epi == EPI_SIGMOID) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        v0[j] = 1.0f / (1.0f + __expf(-acc[mb][0][j]));
+        v1[j] = 1.0f / (1.0f + __expf(-acc[mb][1][j]));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        v0[j] = acc[mb][0][j];
+        v1[j] = acc[mb][1][j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      unsigned char *q = wt + (8 * (j >> 2) + 4 * h + (j & 3)) * PITCH + r32 * ESZ;
+      if constexpr (KIND == 0) {
+        *(float *)q = v0[j];
+        *(float *)(q + 32 * ESZ) = v1[j];
+      } else if constexpr (KIND == 1) {
+        *(f16_t *)q = (f16_t)fminf(fmaxf(v0[j], -65504.f), 65504.f);
+        *(f16_t *)(q + 32 * ESZ) = (f16_t)fminf(fmaxf(v1[j], -65504.f), 65504.f);
+      } else {
+        *(bf16_t *)q = (bf16_t)v0[j];
+        *(bf16_t *)(q + 32 * ESZ) = (bf16_t)v1[j];
+      }
+    }
+    // 32 rows x SPR segments, 64 per instruction
+#pragma unroll
+    for (int it = 0; it < 32 * SPR / 64; ++it) {
+      const int seg = it * 64 + lane;
+      const int row = seg / SPR, cs = seg % SPR;
+      const int m = mrow0 + row, n = c0 + cs * EPS;
+      const uint4 val = *(const uint4 *)(wt + row * PITCH + cs * 16);
+      if (m < P.M && n < P.N) {
+        const int64_t o = (int64_t)m * P.ldc + (int64_t)(n / P.hw) * P.hs + P.ho + (n % P.hw);
+        *(uint4 *)((unsigned char *)P.C + o * ESZ) = val;
+      }
+    }
+  }
 }
 
 template <typename T>
@@ -141,6 +217,19 @@ __global__ void __launch_bounds__(512, 1) gemm_nt_kernel(GemmBatch batch) {
   }
 
   // epilogue: lane holds column (lane & 31) and rows 8 (j / 4) + 4 (lane / 32) + j % 4 of a block
+  // output kinds of the staged epilogue: 0 fp32, 1 fp16, 2 bf16
+  const int okind = P.c_dt == CD_F32 ? 0 : (P.c_dt == CD_F16 || (P.c_dt == CD_IN && __is_same(T, f16_t))) ? 1 : 2;
+  const int eps = okind == 0 ? 4 : 8;  // elements per 16-byte segment
+  const bool vec = !P.c_trans && P.N % 8 == 0 && P.ldc % eps == 0 && P.hs % eps == 0 && P.ho % eps == 0 &&
+                   P.hw % 8 == 0 && ((uintptr_t)P.C & 15) == 0;
+  if (vec) {
+    __syncthreads();  // every wave is done with the stage buffers
+    unsigned char *wt = smem + wave * 32 * 272;
+    if (okind == 0) staged_epilogue<0>(P, acc, wt, m0 + wm * 128, n0 + wn * 64, lane);
+    else if (okind == 1) staged_epilogue<1>(P, acc, wt, m0 + wm * 128, n0 + wn * 64, lane);
+    else staged_epilogue<2>(P, acc, wt, m0 + wm * 128, n0 + wn * 64, lane);
+    return;
+  }
   if (P.epi == EPI_ROPE) {
     // heads of 64 columns: this wave's 64 columns are one head, and column j of block 0 pairs with
     // column j + 32 of block 1 in the same lane
