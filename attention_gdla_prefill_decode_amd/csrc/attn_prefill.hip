@@ -7,7 +7,8 @@
 // heads, the grouped differential combine and the sigmoid gate of Eq.(8)-(10):
 //     Y_i = sigmoid(G_i) * (H_i - lambda_i * H_{n_S + i mod n_N}).
 // Two launches: the noise heads first (they write H_N in fp32), then the signal heads, whose
-// epilogue reads H_N, lambda and the gate logits and writes Y in fp16 for the output projection.
+// epilogue reads H_N, lambda and the gate (sigmoid values in fp16 from the projection's epilogue,
+// or fp32 logits) and writes Y in fp16 for the output projection.
 //
 // Work split: a workgroup is 8 waves (2 per SIMD, so one wave's softmax overlaps the other's
 // matrix work); each wave owns 32 query rows of one head.  In the signal launch the waves are 4
@@ -53,7 +54,8 @@ struct AttnArgs {
   const f16_t *vx;        // [B, n_kv, 128, lcap] fp16: V^T, keys in vt_slot order per 16-group
   const int32_t *pos;     // [B] first position of the chunk
   const float *lam;       // [M, n_S]
-  const float *gate;      // [M, n_S, 128] gate logits
+  const void *gate;       // [M, n_S, 128]: sigmoid(G) in fp16 (gate_f16) or the logits G in fp32
+  int32_t gate_f16;
   float *hn;              // [M, n_N, 128] normalised noise-head outputs
   f16_t *y;               // [M, n_S * 128] fp16
   float *out_heads;       // [M, n_H, 128] or null
@@ -324,7 +326,7 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
       }
   } else {
     const float lam = a.lam[mr * a.n_signal + head];
-    const float *g = a.gate + (mr * a.n_signal + head) * DH;
+    const int64_t goff = (mr * a.n_signal + head) * DH;
     const float *hn = a.hn + (mr * a.n_noise + head % a.n_noise) * DH;
     f16_t *y = a.y + mr * (int64_t)a.n_signal * DH + (int64_t)head * DH;
 #pragma unroll
@@ -332,16 +334,27 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int dim = db * 32 + 8 * i + 4 * hgrp;
-        const float4 gv = *(const float4 *)(g + dim);
+        float sg[4];
+        if (a.gate_f16) {
+          const f16x4 gh = *(const f16x4 *)((const f16_t *)a.gate + goff + dim);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sg[e] = (float)gh[e];
+        } else {
+          const float4 gv = *(const float4 *)((const float *)a.gate + goff + dim);
+          sg[0] = 1.0f / (1.0f + __expf(-gv.x));
+          sg[1] = 1.0f / (1.0f + __expf(-gv.y));
+          sg[2] = 1.0f / (1.0f + __expf(-gv.z));
+          sg[3] = 1.0f / (1.0f + __expf(-gv.w));
+        }
         const float4 nv = *(const float4 *)(hn + dim);
         const float o0 = O[db][4 * i] * inv, o1 = O[db][4 * i + 1] * inv;
         const float o2 = O[db][4 * i + 2] * inv, o3 = O[db][4 * i + 3] * inv;
         if (oh) *(float4 *)(oh + dim) = make_float4(o0, o1, o2, o3);
         f16x4 yv;
-        yv[0] = to_f16((o0 - lam * nv.x) / (1.0f + __expf(-gv.x)));
-        yv[1] = to_f16((o1 - lam * nv.y) / (1.0f + __expf(-gv.y)));
-        yv[2] = to_f16((o2 - lam * nv.z) / (1.0f + __expf(-gv.z)));
-        yv[3] = to_f16((o3 - lam * nv.w) / (1.0f + __expf(-gv.w)));
+        yv[0] = to_f16((o0 - lam * nv.x) * sg[0]);
+        yv[1] = to_f16((o1 - lam * nv.y) * sg[1]);
+        yv[2] = to_f16((o2 - lam * nv.z) * sg[2]);
+        yv[3] = to_f16((o3 - lam * nv.w) * sg[3]);
         *(f16x4 *)(y + dim) = yv;
       }
   }
@@ -444,7 +457,10 @@ gdla_status run_fast_prefill(const LayerDims &d, const gdla_weights *w, int32_t 
   } else {
     add(w->w_qr, d.n_heads * DR, qrp, (int64_t)d.n_heads * DR, CD_F32, d.n_heads * DR, 0);
   }
-  add(nt ? nt->gate : w->w_gate, d.n_signal * DH, gate, (int64_t)d.n_signal * DH, CD_F32, d.n_signal * DH, 0);
+  // with nt the gate leaves the GEMM as sigmoid(G) in fp16, else as fp32 logits
+  add(nt ? nt->gate : w->w_gate, d.n_signal * DH, gate, (int64_t)d.n_signal * DH, nt ? CD_F16 : CD_F32,
+      d.n_signal * DH, 0);
+  if (nt) g.p[g.n - 1].epi = EPI_SIGMOID;
   if ((nt ? launch_gemm_nt(g, true, s) : launch_gemm(g, DT::BF16, s)) != hipSuccess) return GDLA_ERR_HIP;
   if (!nt && launch_rope_heads(qrp, q, (int64_t)d.n_heads * DQK, DQK, DH, M, T, d.n_heads, DR, pos_dev,
                                d.theta, DT::F16, s) != hipSuccess)
@@ -453,7 +469,7 @@ gdla_status run_fast_prefill(const LayerDims &d, const gdla_weights *w, int32_t 
 
   AttnArgs a{};
   a.q = q; a.kx = (const f16_t *)kx; a.vx = (const f16_t *)vx;
-  a.pos = pos_dev; a.lam = lam; a.gate = gate; a.hn = hn; a.y = (f16_t *)y; a.out_heads = out_heads;
+  a.pos = pos_dev; a.lam = lam; a.gate = gate; a.gate_f16 = nt ? 1 : 0; a.hn = hn; a.y = (f16_t *)y; a.out_heads = out_heads;
   a.T = T; a.lcap = lcap;
   a.n_heads = d.n_heads; a.n_signal = d.n_signal; a.n_noise = d.n_noise; a.n_kv = d.n_kv;
   a.window = d.window;
