@@ -118,7 +118,8 @@ PrefillLayout plan_prefill(const LayerDims &d, gdla_dtype dt, int32_t B, int32_t
   L.y = p.add(es * M * d.n_signal * d.d_h);
   if (L.use_fast) {
     L.fast = plan_fast_prefill(d, B, T, [&](size_t n) { return p.add(n); });
-    L.use_nt = (int64_t)B * T >= kNtMinRows && d.d_c % 64 == 0;
+    // (the RoPE epilogue of the transposed-weight GEMM takes sequences of at least 32 tokens)
+    L.use_nt = (int64_t)B * T >= kNtMinRows && T >= 32 && d.d_c % 64 == 0;
     if (L.use_nt) {
       L.wt_qa = p.add(2 * (size_t)d.d_model * d.d_cq);
       L.wt_dkv = p.add(2 * (size_t)d.d_model * d.d_c);
@@ -282,12 +283,19 @@ gdla_status project_and_append(const LayerDims &d, DT dt, const gdla_weights *w,
   if (cq)
     g.p[g.n++] = gp(x, d.d_model, wb(w->w_qa, nt ? nt->qa : nullptr), ldw(d.d_cq), aq, d.d_cq, M, d.d_cq,
                     d.d_model, true);
-  if (lam && !lam_override)
-    g.p[g.n++] = gp(x, d.d_model, wb(w->w_lambda, nt ? nt->lam : nullptr), ldw(d.n_signal), laml, d.n_signal, M,
-                    d.n_signal, d.d_model, true);
+  GemmBatch plain{};  // with nt: problems whose output the transposed-weight GEMM cannot store
+  if (lam && !lam_override) {
+    GemmProblem pl = gp(x, d.d_model, wb(w->w_lambda, nt ? nt->lam : nullptr), ldw(d.n_signal), laml, d.n_signal,
+                        M, d.n_signal, d.d_model, true);
+    if (nt && !nt_gemm_problem_ok(pl))
+      plain.p[plain.n++] = gp(x, d.d_model, w->w_lambda, d.n_signal, laml, d.n_signal, M, d.n_signal, d.d_model, true);
+    else
+      g.p[g.n++] = pl;
+  }
   // with nt the caller has opened GDLA_STAGE_PROJ_IN before transposing the weights
   if (nt) {
     HIP_TRY(launch_gemm_nt(g, false, s));
+    if (plain.n) HIP_TRY(launch_gemm(plain, dt, s));
   } else {
     se.begin(GDLA_STAGE_PROJ_IN);
     HIP_TRY(launch_gemm_rows(g, dt, partial, partial_bytes, s));

@@ -74,13 +74,17 @@ __device__ __forceinline__ void staged_epilogue(const GemmProblem &P, const f32x
   for (int mb = 0; mb < 4; ++mb) {
     const int mrow0 = r0 + mb * 32;
     float v0[16], v1[16];  // columns r32 and r32 + 32
-    if (P.epi == EPI_ROPE) {
+    if (KIND == 1 && P.epi == EPI_ROPE) {
       // heads of 64 columns: the wave's 64 columns are one head, and column j of block 0 pairs
-      // with column j + 32 of block 1 in the same lane
+      // with column j + 32 of block 1 in the same lane.  Row m is token m % T of sequence m / T;
+      // the 32 rows of this block span at most two sequences (T >= 32 is checked on the host).
+      const int sb = min(mrow0, P.M - 1) / P.rope_T;
+      const int sb_end = (sb + 1) * P.rope_T;
+      const int pos0 = P.rope_pos[sb], pos1 = sb_end < P.M ? P.rope_pos[sb + 1] : 0;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int m = min(mrow0 + 8 * (j >> 2) + 4 * h + (j & 3), P.M - 1);
-        const int pp = P.rope_pos[m / P.rope_T] + m % P.rope_T;
+        const int pp = m < sb_end ? pos0 + (m - sb * P.rope_T) : pos1 + (m - sb_end);
         double turns = (double)pp * rev;
         turns -= floor(turns);  // angle / 2 pi, reduced to [0, 1)
         const float sn = __builtin_amdgcn_sinf((float)turns), cs = __builtin_amdgcn_cosf((float)turns);
@@ -91,8 +95,8 @@ __device__ __forceinline__ void staged_epilogue(const GemmProblem &P, const f32x
     } else if (P.epi == EPI_SIGMOID) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        v0[j] = 1.0f / (1.0f + __expf(-acc[mb][0][j]));
-        v1[j] = 1.0f / (1.0f + __expf(-acc[mb][1][j]));
+        v0[j] = __builtin_amdgcn_rcpf(1.0f + __expf(-acc[mb][0][j]));
+        v1[j] = __builtin_amdgcn_rcpf(1.0f + __expf(-acc[mb][1][j]));
       }
     } else {
 #pragma unroll
@@ -219,10 +223,7 @@ __global__ void __launch_bounds__(512, 1) gemm_nt_kernel(GemmBatch batch) {
   // epilogue: lane holds column (lane & 31) and rows 8 (j / 4) + 4 (lane / 32) + j % 4 of a block
   // output kinds of the staged epilogue: 0 fp32, 1 fp16, 2 bf16
   const int okind = P.c_dt == CD_F32 ? 0 : (P.c_dt == CD_F16 || (P.c_dt == CD_IN && __is_same(T, f16_t))) ? 1 : 2;
-  const int eps = okind == 0 ? 4 : 8;  // elements per 16-byte segment
-  const bool vec = !P.c_trans && P.N % 8 == 0 && P.ldc % eps == 0 && P.hs % eps == 0 && P.ho % eps == 0 &&
-                   P.hw % 8 == 0 && ((uintptr_t)P.C & 15) == 0;
-  if (vec) {
+  if (!P.c_trans) {  // row-major outputs: 16-byte storable (nt_gemm_problem_ok)
     __syncthreads();  // every wave is done with the stage buffers
     unsigned char *wt = smem + wave * 32 * 272;
     if (okind == 0) staged_epilogue<0>(P, acc, wt, m0 + wm * 128, n0 + wn * 64, lane);
@@ -230,40 +231,15 @@ __global__ void __launch_bounds__(512, 1) gemm_nt_kernel(GemmBatch batch) {
     else staged_epilogue<2>(P, acc, wt, m0 + wm * 128, n0 + wn * 64, lane);
     return;
   }
-  if (P.epi == EPI_ROPE) {
-    // heads of 64 columns: this wave's 64 columns are one head, and column j of block 0 pairs with
-    // column j + 32 of block 1 in the same lane
-    const int n = n0 + wn * 64 + r32;
-    if (n >= P.N) return;
-    // frequency in revolutions per position, fp64 so that positions up to 2^24 keep their phase
-    const double rev = pow((double)P.rope_theta, -2.0 * (double)r32 / (double)P.rope_d) * 0.15915494309189533577;
-    const int64_t coff = (int64_t)(n / P.hw) * P.hs + P.ho + (n % P.hw);
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int m = m0 + wm * 128 + mb * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
-        if (m >= P.M) continue;
-        const int p = P.rope_pos[m / P.rope_T] + m % P.rope_T;
-        double turns = (double)p * rev;
-        turns -= floor(turns);  // angle / 2 pi, reduced to [0, 1)
-        const float sn = __builtin_amdgcn_sinf((float)turns), cs = __builtin_amdgcn_cosf((float)turns);
-        const float u = acc[mb][0][j], v = acc[mb][1][j];
-        f16_t *o = (f16_t *)P.C + (int64_t)m * P.ldc + coff;
-        o[0] = (f16_t)fminf(fmaxf(u * cs - v * sn, -65504.f), 65504.f);
-        o[32] = (f16_t)fminf(fmaxf(u * sn + v * cs, -65504.f), 65504.f);
-      }
-    }
-    return;
-  }
+  // transposed per-head store of the value expansion (V^T, keys in vt_slot order): 8-byte stores
+  // along the rows
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int n = n0 + wn * 64 + nb * 32 + r32;
       if (n >= P.N) continue;
-      if (P.c_trans) {
-        f16_t *base = (f16_t *)P.C + (int64_t)(n / P.hw) * P.hs + P.ho + (int64_t)(n % P.hw) * P.ldc;
+      f16_t *base = (f16_t *)P.C + (int64_t)(n / P.hw) * P.hs + P.ho + (int64_t)(n % P.hw) * P.ldc;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int m = m0 + wm * 128 + mb * 32 + 8 * q + 4 * h;
@@ -279,21 +255,6 @@ __global__ void __launch_bounds__(512, 1) gemm_nt_kernel(GemmBatch batch) {
               if (m + e < P.M) base[vt_slot(m + e)] = v[e];
           }
         }
-        continue;
-      }
-      const int64_t coff = (int64_t)(n / P.hw) * P.hs + P.ho + (n % P.hw);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int m = m0 + wm * 128 + mb * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
-        if (m >= P.M) continue;
-        float v = acc[mb][nb][j];
-        if (P.epi == EPI_SIGMOID) v = 1.0f / (1.0f + __expf(-v));
-        const int64_t o = (int64_t)m * P.ldc + coff;
-        if (P.c_dt == CD_F32) ((float *)P.C)[o] = v;
-        else if (P.c_dt == CD_F16 || (P.c_dt == CD_IN && __is_same(T, f16_t)))
-          ((f16_t *)P.C)[o] = (f16_t)fminf(fmaxf(v, -65504.f), 65504.f);
-        else ((bf16_t *)P.C)[o] = (bf16_t)v;
-      }
     }
   }
 }
@@ -356,9 +317,13 @@ bool nt_gemm_problem_ok(const GemmProblem &p) {
   return p.K % BK == 0 && p.K > 0 && p.M > 0 && p.N > 0 && p.lda % 8 == 0 && p.ldb % 8 == 0 &&
          ((uintptr_t)p.A & 15) == 0 && ((uintptr_t)p.B & 15) == 0 && p.hw > 0 &&
          (p.epi != EPI_ROPE || (p.rope_d == 64 && p.hw % 64 == 0 && p.N % 64 == 0 && p.c_dt == CD_F16 &&
-                                p.rope_pos && p.rope_T > 0)) &&
+                                p.rope_pos && p.rope_T >= 32)) &&
          (!p.c_trans || (p.c_dt == CD_F16 && p.ldc % 4 == 0 && (p.hs + p.ho) % 4 == 0 &&
-                         ((uintptr_t)p.C & 7) == 0));
+                         ((uintptr_t)p.C & 7) == 0)) &&
+         // row-major outputs leave as 16-byte row segments inside one head
+         (p.c_trans || (p.N % 8 == 0 && p.hw % 8 == 0 && ((uintptr_t)p.C & 15) == 0 &&
+                        p.ldc % (p.c_dt == CD_F32 ? 4 : 8) == 0 && p.hs % (p.c_dt == CD_F32 ? 4 : 8) == 0 &&
+                        p.ho % (p.c_dt == CD_F32 ? 4 : 8) == 0));
 }
 
 hipError_t launch_gemm_nt(GemmBatch &g, bool f16, hipStream_t s) {
