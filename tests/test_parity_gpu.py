@@ -66,6 +66,22 @@ def test_bf16_prefill(seq, p0, window):
         H.check_rows(r["rows"][b], r["exp_rows"][b], "bf16", "bf16 cache rows")
 
 
+def test_bf16_prefill_odd_signal_heads():
+    # 12 signal heads: the lambda projection's 12 columns cannot leave the transposed-weight GEMM
+    # as 16-byte segments and go to the general GEMM (>= 256 rows take the transposed path)
+    cfg = dict(BF, n_heads=16, n_signal=12, n_noise=4, n_kv=4)
+    r = H.prefill_case(cfg, 288, [0], seed=23)
+    _say(H.check(r["out"], r["exp_out"], "bf16", "bf16 12+4 heads T=288"))
+
+
+def test_bf16_prefill_many_short_sequences():
+    # 12 sequences of 24 tokens: >= 256 rows but sequences shorter than 32 (no RoPE epilogue)
+    r = H.prefill_case(BF, 24, [0, 3, 10, 0, 1, 7, 30, 2, 0, 5, 9, 4], seed=31)
+    _say(H.check(r["out"], r["exp_out"], "bf16", "bf16 12 x 24 tokens"))
+    for b in range(12):
+        H.check_rows(r["rows"][b], r["exp_rows"][b], "bf16", "bf16 cache rows")
+
+
 def test_bf16_heads_debug_output():
     r = H.prefill_case(BF, 160, [0], want_heads=True)
     _say(H.check(r["heads"], r["exp_heads"], "bf16", "bf16 per-head H"))
@@ -129,6 +145,13 @@ def test_bf16_decode(p0):
     r = H.decode_case(BF, p0, want_heads=True)
     _say(H.check(r["out"], r["exp_out"], "bf16", f"bf16 decode p0={p0}"))
     _say(H.check(r["heads"], r["exp_heads"], "bf16", "bf16 decode per-head H"))
+    H.check_rows(r["rows"], r["exp_rows"], "bf16", "bf16 decode cache rows")
+
+
+def test_bf16_decode_batch_over_64():
+    # 72 sequences: more rows than the skinny projection kernel takes (general GEMM)
+    r = H.decode_case(BF, [(37 * b) % 500 for b in range(72)], seed=41)
+    _say(H.check(r["out"], r["exp_out"], "bf16", "bf16 decode B=72"))
     H.check_rows(r["rows"], r["exp_rows"], "bf16", "bf16 decode cache rows")
 
 
