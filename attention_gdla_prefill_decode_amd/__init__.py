@@ -6,5 +6,5 @@ This package is its thin Python binding; see gdla.py.
 
 from .gdla import (EXPORTED, GDLA_BF16, GDLA_F32, GDLA_OP_APPEND, GDLA_OP_DECODE,  # noqa: F401
                    GDLA_OP_PREFILL, STAGES, GdlaDebug, StageTimer, GdlaDims, GdlaError, GdlaWeights, LIB_PATH,
-                   gdla_decode, gdla_latent_append, gdla_prefill, gdla_workspace_bytes, lib,
-                   make_dims, make_weights)
+                   MAX_DECODE_TOKENS, gdla_decode, gdla_decode_tokens, gdla_latent_append,
+                   gdla_prefill, gdla_workspace_bytes, lib, make_dims, make_weights)

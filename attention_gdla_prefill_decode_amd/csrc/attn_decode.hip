@@ -58,15 +58,31 @@ constexpr int MAX_HEADS = 16 * (MAX_WAVES + 1);
 constexpr int WDB = NDB / MAX_WAVES;    // dim blocks of 16 owned by each wave (8)
 constexpr int NHB = MAX_WAVES + 1;      // head blocks of 16 (at most)
 
+// Queries are indexed by v = b q_len + i: token i of sequence b, at position pos[b] + i.
 struct DecodeArgs {
-  const bf16_t *qabs;  // [B, n_H, 576] bf16
+  const bf16_t *qabs;  // [B q_len, n_H, 576] bf16
   const bf16_t *cache; // [B, max_len, 576] bf16
-  const int32_t *pos;  // [B] position of the new token (keys 0 .. pos are visible)
-  float *part_o;       // [B, splits, n_H, 512]
-  float *part_ml;      // [B, splits, n_H, 2]
-  int32_t n_heads, max_len, window, splits;
+  const int32_t *pos;  // [B] position of the first new token (token i sees keys 0 .. pos + i)
+  float *part_o;       // [B q_len, splits, n_H, 512]
+  float *part_ml;      // [B q_len, splits, n_H, 2]
+  int32_t B, q_len, n_heads, max_len, window, splits;
   float c;             // softmax scale * log2(e)
 };
+
+// Workgroup -> (sequence b, token i, split sp).  The units u = b splits + sp come in groups of 8,
+// one per XCD (the XCDs take workgroups round-robin); within a group the q_len tokens of a unit are
+// 8 workgroups apart, so they run on the same XCD at the same time and read the unit's cache tiles
+// once from HBM and then from that XCD's L2.  Returns false for the padding of the last group.
+__device__ __forceinline__ bool decode_unit(const DecodeArgs &a, int &b, int &tok, int &sp) {
+  const int id = blockIdx.x, q = a.q_len;
+  const int u = id / (8 * q) * 8 + id % 8;
+  tok = id / 8 % q;
+  b = u / a.splits;
+  sp = u % a.splits;
+  return b < a.B;
+}
+
+int decode_grid(int B, int q_len, int splits) { return (B * splits + 7) / 8 * 8 * q_len; }
 
 __host__ __device__ constexpr int swz(int r) {
   return 4 * ((r >> 1) & 1) + 2 * ((r & 1) ^ ((r >> 2) & 1)) + ((r & 1) ^ ((r >> 3) & 1));
@@ -149,8 +165,10 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, bf16_t *CB, bf1
                                             int wave) {
   constexpr int KB4 = ROLE >> 1, K4LO = (ROLE & 1) * K4N;
   const int lane = threadIdx.x & 63;
-  const int b = blockIdx.y, sp = blockIdx.x;
-  const int p = a.pos[b];
+  int b, tok, sp;
+  decode_unit(a, b, tok, sp);
+  const int v = b * a.q_len + tok;  // query row set
+  const int p = a.pos[b] + tok;
   const int lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
   const int span = p + 1 - lo;
   const int kps = ((span + a.splits - 1) / a.splits + KT - 1) / KT * KT;  // keys per split
@@ -164,7 +182,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, bf16_t *CB, bf1
   // head `head4` at k-step K4LO + k
   bf16x8 Qf[NKST], Q4[SHARED ? K4N : 1];
   {
-    const bf16_t *qb = a.qabs + (int64_t)b * a.n_heads * ROW + 8 * g;
+    const bf16_t *qb = a.qabs + (int64_t)v * a.n_heads * ROW + 8 * g;
     const bf16_t *qp = qb + (int64_t)(head_ok ? head : 0) * ROW;
 #pragma unroll
     for (int k = 0; k < NKST; ++k) {
@@ -333,14 +351,14 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, bf16_t *CB, bf1
   // (m, l) of head block hb come from the wave that owns its scores (wave 0 for block 4)
   const float lt = head_sum(st.l);
   if (head_ok && g == 0) {
-    const int64_t ph = ((int64_t)b * a.splits + sp) * a.n_heads + head;
+    const int64_t ph = ((int64_t)v * a.splits + sp) * a.n_heads + head;
     a.part_ml[ph * 2] = ntiles > 0 ? st.mref : -INFINITY;
     a.part_ml[ph * 2 + 1] = lt;
   }
   if (SHARED) {
     const float lt4 = head_sum(st4.l);
     if (head4_ok && wave == 0 && g == 0) {
-      const int64_t ph = ((int64_t)b * a.splits + sp) * a.n_heads + head4;
+      const int64_t ph = ((int64_t)v * a.splits + sp) * a.n_heads + head4;
       a.part_ml[ph * 2] = ntiles > 0 ? st4.mref : -INFINITY;
       a.part_ml[ph * 2 + 1] = lt4;
     }
@@ -350,7 +368,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, bf16_t *CB, bf1
   for (int hb = 0; hb < HB; ++hb) {
     const int h = 16 * hb + col;
     if (h >= a.n_heads) continue;
-    float *po = a.part_o + (((int64_t)b * a.splits + sp) * a.n_heads + h) * DC + 16 * WDB * wave + 4 * g;
+    float *po = a.part_o + (((int64_t)v * a.splits + sp) * a.n_heads + h) * DC + 16 * WDB * wave + 4 * g;
 #pragma unroll
     for (int dd = 0; dd < WDB; ++dd)
       *(float4 *)(po + 16 * dd) = make_float4(O[hb][dd][0], O[hb][dd][1], O[hb][dd][2], O[hb][dd][3]);
@@ -363,6 +381,10 @@ __global__ void __launch_bounds__(256, 1) latent_decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) bf16x8 PB[MAX_WAVES][64];   // P^T of head blocks 0..3
   __shared__ __attribute__((aligned(16))) f32x4 S4B[MAX_WAVES][64];   // partial scores, shared block
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  {
+    int b, tok, sp;
+    if (!decode_unit(a, b, tok, sp)) return;  // uniform over the workgroup, before any barrier
+  }
   if (!SHARED) {
     decode_body<false, 0>(a, CB, PB, S4B, wave);
   } else {
@@ -528,37 +550,39 @@ int32_t fast_decode_splits(int32_t B, int32_t max_len) {
   return std::max(1, std::min(by_cu, by_len));
 }
 
-gdla_status run_fast_decode(const LayerDims &d, const gdla_weights *w, int32_t B, const int32_t *pos_dev,
-                            const int32_t *pos_host, void *cache, int32_t max_len, const float *qc,
+gdla_status run_fast_decode(const LayerDims &d, const gdla_weights *w, int32_t B, int32_t T,
+                            const int32_t *pos_dev, void *cache, int32_t max_len, const float *qc,
                             const float *qr, float *heads, const FastDecodeLayout &L, void *ws, hipStream_t s,
                             StageEvents &se) {
-  (void)pos_host;
+  const int32_t BT = B * T;  // query rows sets: token i of sequence b is row set b T + i
   bf16_t *qabs = (bf16_t *)((char *)ws + L.qabs);
   float *part_o = (float *)((char *)ws + L.part_o);
   float *part_ml = (float *)((char *)ws + L.part_ml);
   float *o = (float *)((char *)ws + L.o);
   const int hk_max = (d.n_signal + d.n_kv - 1) / d.n_kv + (d.n_noise + d.n_kv - 1) / d.n_kv;
-  const dim3 gk((unsigned)((B * hk_max + R - 1) / R), (unsigned)d.n_kv);
-  hipLaunchKernelGGL(absorb_kernel, gk, dim3(256), 0, s, qc, qr, (const bf16_t *)w->w_uk, qabs, B, d);
+  const dim3 gk((unsigned)((BT * hk_max + R - 1) / R), (unsigned)d.n_kv);
+  hipLaunchKernelGGL(absorb_kernel, gk, dim3(256), 0, s, qc, qr, (const bf16_t *)w->w_uk, qabs, BT, d);
   if (hipGetLastError() != hipSuccess) return GDLA_ERR_HIP;
   se.end(GDLA_STAGE_PROJ_Q);
   DecodeArgs a{};
   a.qabs = qabs; a.cache = (const bf16_t *)cache; a.pos = pos_dev; a.part_o = part_o; a.part_ml = part_ml;
   const int nblk = (d.n_heads + 15) / 16;
+  a.B = B; a.q_len = T;
   a.n_heads = d.n_heads; a.max_len = max_len; a.window = d.window; a.splits = L.splits;
   a.c = d.scale * 1.4426950408889634f;
   se.begin(GDLA_STAGE_ATTN_NOISE);
+  const dim3 grid((unsigned)decode_grid(B, T, L.splits));
   if (nblk > MAX_WAVES)
-    hipLaunchKernelGGL(latent_decode_kernel<true>, dim3(L.splits, B), dim3(64 * MAX_WAVES), 0, s, a);
+    hipLaunchKernelGGL(latent_decode_kernel<true>, grid, dim3(64 * MAX_WAVES), 0, s, a);
   else
-    hipLaunchKernelGGL(latent_decode_kernel<false>, dim3(L.splits, B), dim3(64 * MAX_WAVES), 0, s, a);
+    hipLaunchKernelGGL(latent_decode_kernel<false>, grid, dim3(64 * MAX_WAVES), 0, s, a);
   if (hipGetLastError() != hipSuccess) return GDLA_ERR_HIP;
   se.end(GDLA_STAGE_ATTN_NOISE);
   se.begin(GDLA_STAGE_ATTN_SIGNAL);
-  hipLaunchKernelGGL(merge_splits_kernel, dim3(B * d.n_heads), dim3(128), 0, s, part_o, part_ml, o, d.n_heads,
+  hipLaunchKernelGGL(merge_splits_kernel, dim3(BT * d.n_heads), dim3(128), 0, s, part_o, part_ml, o, d.n_heads,
                      L.splits);
   if (hipGetLastError() != hipSuccess) return GDLA_ERR_HIP;
-  hipLaunchKernelGGL(unabsorb_kernel, gk, dim3(256), 0, s, o, (const bf16_t *)w->w_uv, heads, B, d);
+  hipLaunchKernelGGL(unabsorb_kernel, gk, dim3(256), 0, s, o, (const bf16_t *)w->w_uv, heads, BT, d);
   if (hipGetLastError() != hipSuccess) return GDLA_ERR_HIP;
   return GDLA_OK;
 }

@@ -17,7 +17,7 @@ hipError_t launch_gemm_nt(GemmBatch &g, bool f16, hipStream_t s);
 // Wt[N, K] = W[K, N]^T of a bf16 weight, as fp16 (to_f16) or bf16.
 hipError_t launch_transpose_weight(const void *w, void *wt, int32_t K, int32_t N, bool to_f16, hipStream_t s);
 
-// ---- skinny GEMM for decode batches (M <= 64 rows, N a multiple of 64, K of 64; bf16 A and B
+// ---- skinny GEMM for decode batches (M <= 256 rows, N a multiple of 64, K of 64; bf16 A and B
 // with B in its stored [K, N] layout; fp32 or bf16 C).  Split along K when the column tiles do
 // not fill the chip; the fp32 partial sums need skinny_gemm_partial_bytes(g) of workspace, never
 // more than skinny_gemm_partial_bound(M). ----
@@ -77,15 +77,16 @@ gdla_status run_fast_prefill(const LayerDims &d, const gdla_weights *w, int32_t 
                              const NtWeights *nt);
 
 // ---- absorbed split-L decode ----
+// Sizes are per query row set: BT = B T for T new tokens per sequence.
 struct FastDecodeLayout {
-  size_t qabs;   // [B, n_H, d_c + d_r] bf16
-  size_t part_o; // [B, splits, n_H, d_c] fp32
-  size_t part_ml;// [B, splits, n_H, 2] fp32
-  size_t o;      // [B, n_H, d_c] fp32
+  size_t qabs;   // [BT, n_H, d_c + d_r] bf16
+  size_t part_o; // [BT, splits, n_H, d_c] fp32
+  size_t part_ml;// [BT, splits, n_H, 2] fp32
+  size_t o;      // [BT, n_H, d_c] fp32
   int32_t splits;
 };
 
-int32_t fast_decode_splits(int32_t B, int32_t max_len);
+int32_t fast_decode_splits(int32_t BT, int32_t max_len);
 
 template <class Add>
 FastDecodeLayout plan_fast_decode(const LayerDims &d, int32_t B, int32_t max_len, Add add) {
@@ -99,9 +100,11 @@ FastDecodeLayout plan_fast_decode(const LayerDims &d, int32_t B, int32_t max_len
 }
 
 bool fast_decode_supported(const LayerDims &d, gdla_dtype dt);
-gdla_status run_fast_decode(const LayerDims &d, const gdla_weights *w, int32_t B,
-                            const int32_t *pos_dev, const int32_t *pos_host, void *cache,
-                            int32_t max_len, const float *qc, const float *qr, float *heads,
-                            const FastDecodeLayout &L, void *ws, hipStream_t s, StageEvents &se);
+// T new tokens per sequence (token i of sequence b at position pos_dev[b] + i, already appended);
+// qc, qr, heads hold B T row sets of n_H heads.
+gdla_status run_fast_decode(const LayerDims &d, const gdla_weights *w, int32_t B, int32_t T,
+                            const int32_t *pos_dev, void *cache, int32_t max_len, const float *qc,
+                            const float *qr, float *heads, const FastDecodeLayout &L, void *ws,
+                            hipStream_t s, StageEvents &se);
 
 }  // namespace gdla

@@ -149,10 +149,11 @@ struct DecodeLayout {
   bool use_fast;
 };
 
-DecodeLayout plan_decode(const LayerDims &d, gdla_dtype dt, int32_t B, int32_t max_len) {
+// T new tokens per sequence: M = B T query rows.
+DecodeLayout plan_decode(const LayerDims &d, gdla_dtype dt, int32_t B, int32_t T, int32_t max_len) {
   DecodeLayout L{};
   const size_t es = esize(dt);
-  const size_t M = (size_t)B;
+  const size_t M = (size_t)B * T;
   L.use_fast = fast_decode_supported(d, dt);
   Plan p;
   L.pos = p.add(sizeof(int32_t) * B);
@@ -168,10 +169,10 @@ DecodeLayout plan_decode(const LayerDims &d, gdla_dtype dt, int32_t B, int32_t m
   L.gate = p.add(4 * M * d.n_signal * d.d_h);
   L.heads = p.add(4 * M * d.n_heads * d.d_h);
   L.y = p.add(es * M * d.n_signal * d.d_h);
-  L.skinny_bytes = (dt == GDLA_BF16 && B <= 64) ? skinny_gemm_partial_bound(B) : 0;
+  L.skinny_bytes = (dt == GDLA_BF16 && M <= 256) ? skinny_gemm_partial_bound((int32_t)M) : 0;
   L.skinny = p.add(L.skinny_bytes);
   if (L.use_fast) {
-    L.fast = plan_fast_decode(d, B, max_len, [&](size_t n) { return p.add(n); });
+    L.fast = plan_fast_decode(d, (int32_t)M, max_len, [&](size_t n) { return p.add(n); });
   } else {
     L.qabs = p.add(4 * M * d.n_heads * (d.d_c + d.d_r));
     L.o = p.add(4 * M * d.n_heads * d.d_c);
@@ -245,7 +246,7 @@ GemmProblem gp(const void *A, int64_t lda, const void *B, int64_t ldb, void *C, 
   return p;
 }
 
-// The projections of a decode batch: problems the skinny split-K kernel serves (bf16, at most 64
+// The projections of a decode batch: problems the skinny split-K kernel serves (bf16, at most 256
 // rows, columns in tiles of 64) run there, given workspace for its partial sums; the rest go to
 // the general dispatch.
 hipError_t launch_gemm_rows(GemmBatch &g, DT dt, void *partial, size_t partial_bytes, hipStream_t s) {
@@ -355,7 +356,7 @@ GDLA_EXPORT size_t gdla_workspace_bytes(const gdla_dims *dims, int32_t op, int32
                                         const int32_t *pos_host, int32_t max_len) {
   LayerDims d;
   if (check_dims(dims, d) != GDLA_OK) return 0;
-  if (B < 0 || T < 0 || max_len <= 0 || (op == GDLA_OP_DECODE && T != 1 && T != 0)) return 0;
+  if (B < 0 || T < 0 || max_len <= 0 || (op == GDLA_OP_DECODE && T > GDLA_MAX_DECODE_TOKENS)) return 0;
   if (B == 0 || T == 0) return 0;
   if (T > max_len) return 0;
   if (pos_host) {
@@ -364,7 +365,7 @@ GDLA_EXPORT size_t gdla_workspace_bytes(const gdla_dims *dims, int32_t op, int32
   }
   switch (op) {
     case GDLA_OP_PREFILL: return plan_prefill(d, dims->dtype, B, T, pos_host, max_len).total;
-    case GDLA_OP_DECODE: return plan_decode(d, dims->dtype, B, max_len).total;
+    case GDLA_OP_DECODE: return plan_decode(d, dims->dtype, B, T, max_len).total;
     case GDLA_OP_APPEND: return plan_append(d, B, T).total;
     default: return 0;
   }
@@ -532,17 +533,21 @@ GDLA_EXPORT gdla_status gdla_prefill(const gdla_dims *dims, const gdla_weights *
   return GDLA_OK;
 }
 
-GDLA_EXPORT gdla_status gdla_decode(const gdla_dims *dims, const gdla_weights *w, const void *x,
-                                    int32_t B, const int32_t *pos_host, void *cache,
-                                    int32_t max_len, void *out, void *ws, size_t ws_bytes,
-                                    const gdla_debug *dbg, hipStream_t stream) {
+namespace gdla {
+namespace {
+
+// Absorbed decode of T new tokens per sequence (row m = b T + i: token i of sequence b).
+gdla_status decode_impl(const gdla_dims *dims, const gdla_weights *w, const void *x, int32_t B, int32_t T,
+                        const int32_t *pos_host, void *cache, int32_t max_len, void *out, void *ws,
+                        size_t ws_bytes, const gdla_debug *dbg, hipStream_t stream) {
   g_err[0] = 0;
   LayerDims d;
-  gdla_status st = check_call(dims, w, x, B, 1, pos_host, cache, max_len, out, true, d);
-  if (st != GDLA_OK || B == 0) return st;
-  const DecodeLayout L = plan_decode(d, dims->dtype, B, max_len);
+  gdla_status st = check_call(dims, w, x, B, T, pos_host, cache, max_len, out, true, d);
+  if (st != GDLA_OK || B == 0 || T == 0) return st;
+  const DecodeLayout L = plan_decode(d, dims->dtype, B, T, max_len);
   if ((st = check_ws(ws, ws_bytes, L.total)) != GDLA_OK) return st;
   const DT dt = dims->dtype == GDLA_F32 ? DT::F32 : DT::BF16;
+  const int32_t M = B * T;
   const float *lam_override = dbg ? dbg->lambda_override : nullptr;
   float *out_heads = dbg ? dbg->out_heads : nullptr;
   StageEvents se;
@@ -552,7 +557,7 @@ GDLA_EXPORT gdla_status gdla_decode(const gdla_dims *dims, const gdla_weights *w
   int32_t *pos_dev = at<int32_t>(ws, L.pos);
   HIP_TRY(launch_set_i32(pos_dev, pos_host, B, stream));
   void *partial = at<void>(ws, L.skinny);
-  st = project_and_append(d, dt, w, x, B, 1, pos_dev, cache, max_len, at<float>(ws, L.aq),
+  st = project_and_append(d, dt, w, x, M, T, pos_dev, cache, max_len, at<float>(ws, L.aq),
                           at<float>(ws, L.ckv), at<float>(ws, L.krp), at<float>(ws, L.laml),
                           at<void>(ws, L.cq), at<float>(ws, L.lam), lam_override, stream, se, false, nullptr,
                           partial, L.skinny_bytes);
@@ -561,42 +566,63 @@ GDLA_EXPORT gdla_status gdla_decode(const gdla_dims *dims, const gdla_weights *w
   se.begin(GDLA_STAGE_PROJ_Q);
   GemmBatch g{};
   g.p[g.n++] = gp(at<void>(ws, L.cq), d.d_cq, w->w_qc, (int64_t)d.n_heads * d.d_h, at<float>(ws, L.qc),
-                  (int64_t)d.n_heads * d.d_h, B, d.n_heads * d.d_h, d.d_cq, true);
+                  (int64_t)d.n_heads * d.d_h, M, d.n_heads * d.d_h, d.d_cq, true);
   g.p[g.n++] = gp(at<void>(ws, L.cq), d.d_cq, w->w_qr, (int64_t)d.n_heads * d.d_r, at<float>(ws, L.qrp),
-                  (int64_t)d.n_heads * d.d_r, B, d.n_heads * d.d_r, d.d_cq, true);
+                  (int64_t)d.n_heads * d.d_r, M, d.n_heads * d.d_r, d.d_cq, true);
   g.p[g.n++] = gp(at<void>(ws, L.cq), d.d_cq, w->w_gate, (int64_t)d.n_signal * d.d_h, at<float>(ws, L.gate),
-                  (int64_t)d.n_signal * d.d_h, B, d.n_signal * d.d_h, d.d_cq, true);
+                  (int64_t)d.n_signal * d.d_h, M, d.n_signal * d.d_h, d.d_cq, true);
   HIP_TRY(launch_gemm_rows(g, dt, partial, L.skinny_bytes, stream));
   HIP_TRY(launch_rope_heads(at<float>(ws, L.qrp), at<float>(ws, L.qr), (int64_t)d.n_heads * d.d_r, d.d_r, 0,
-                            B, 1, d.n_heads, d.d_r, pos_dev, d.theta, DT::F32, stream));
+                            M, T, d.n_heads, d.d_r, pos_dev, d.theta, DT::F32, stream));
   if (L.use_fast) {
     // ends GDLA_STAGE_PROJ_Q after the absorbed query; leaves GDLA_STAGE_ATTN_SIGNAL open
-    st = run_fast_decode(d, w, B, pos_dev, pos_host, cache, max_len, at<float>(ws, L.qc),
-                         at<float>(ws, L.qr), at<float>(ws, L.heads), L.fast, ws, stream, se);
+    st = run_fast_decode(d, w, B, T, pos_dev, cache, max_len, at<float>(ws, L.qc), at<float>(ws, L.qr),
+                         at<float>(ws, L.heads), L.fast, ws, stream, se);
     if (st != GDLA_OK) return fail(st, "fast decode path failed: %s", hipGetErrorString(hipGetLastError()));
   } else {
     se.end(GDLA_STAGE_PROJ_Q);
     se.begin(GDLA_STAGE_ATTN_NOISE);
     HIP_TRY(launch_absorb_generic(at<float>(ws, L.qc), at<float>(ws, L.qr), w->w_uk, at<float>(ws, L.qabs),
-                                  B, d, dt, stream));
-    HIP_TRY(launch_latent_attention_generic(at<float>(ws, L.qabs), cache, at<float>(ws, L.o), pos_dev, B,
+                                  M, d, dt, stream));
+    HIP_TRY(launch_latent_attention_generic(at<float>(ws, L.qabs), cache, at<float>(ws, L.o), pos_dev, B, T,
                                             max_len, d, dt, stream));
     se.end(GDLA_STAGE_ATTN_NOISE);
     se.begin(GDLA_STAGE_ATTN_SIGNAL);
-    HIP_TRY(launch_unabsorb_generic(at<float>(ws, L.o), w->w_uv, at<float>(ws, L.heads), B, d, dt, stream));
+    HIP_TRY(launch_unabsorb_generic(at<float>(ws, L.o), w->w_uv, at<float>(ws, L.heads), M, d, dt, stream));
   }
   if (out_heads)
     HIP_TRY(launch_copy_rows_f32(at<float>(ws, L.heads), (int64_t)d.n_heads * d.d_h, out_heads,
-                                 (int64_t)d.n_heads * d.d_h, B, d.n_heads * d.d_h, stream));
+                                 (int64_t)d.n_heads * d.d_h, M, d.n_heads * d.d_h, stream));
   HIP_TRY(launch_combine(at<float>(ws, L.heads), at<float>(ws, L.lam), at<float>(ws, L.gate),
-                         at<void>(ws, L.y), B, d, dt, stream));
+                         at<void>(ws, L.y), M, d, dt, stream));
   se.end(GDLA_STAGE_ATTN_SIGNAL);
   g = GemmBatch{};
-  g.p[g.n++] = gp(at<void>(ws, L.y), (int64_t)d.n_signal * d.d_h, w->w_o, d.d_model, out, d.d_model, B,
+  g.p[g.n++] = gp(at<void>(ws, L.y), (int64_t)d.n_signal * d.d_h, w->w_o, d.d_model, out, d.d_model, M,
                   d.d_model, d.n_signal * d.d_h, false);
   se.begin(GDLA_STAGE_PROJ_OUT);
   HIP_TRY(launch_gemm_rows(g, dt, partial, L.skinny_bytes, stream));
   se.end(GDLA_STAGE_PROJ_OUT);
   se.finish();
   return GDLA_OK;
+}
+
+}  // namespace
+}  // namespace gdla
+
+GDLA_EXPORT gdla_status gdla_decode(const gdla_dims *dims, const gdla_weights *w, const void *x,
+                                    int32_t B, const int32_t *pos_host, void *cache,
+                                    int32_t max_len, void *out, void *ws, size_t ws_bytes,
+                                    const gdla_debug *dbg, hipStream_t stream) {
+  return decode_impl(dims, w, x, B, 1, pos_host, cache, max_len, out, ws, ws_bytes, dbg, stream);
+}
+
+GDLA_EXPORT gdla_status gdla_decode_tokens(const gdla_dims *dims, const gdla_weights *w, const void *x,
+                                           int32_t B, int32_t T, const int32_t *pos_host, void *cache,
+                                           int32_t max_len, void *out, void *ws, size_t ws_bytes,
+                                           const gdla_debug *dbg, hipStream_t stream) {
+  if (T < 0 || T > GDLA_MAX_DECODE_TOKENS) {
+    g_err[0] = 0;
+    return fail(GDLA_ERR_INVALID_ARG, "T = %d outside 0 .. %d", T, GDLA_MAX_DECODE_TOKENS);
+  }
+  return decode_impl(dims, w, x, B, T, pos_host, cache, max_len, out, ws, ws_bytes, dbg, stream);
 }

@@ -130,14 +130,17 @@ hipError_t launch_attention_generic(const AttnGenericArgs &a, const LayerDims &d
 hipError_t launch_combine(const float *heads, const float *lam, const float *gate, void *y,
                           int32_t M, const LayerDims &d, DT dt, hipStream_t s);
 
-// Absorbed decode (one query per sequence at position pos[b]):
+// Absorbed decode.  The absorb / un-absorb steps work on any number of query row sets; the
+// attention step takes q_len tokens per sequence, row set v = b q_len + i at position pos[b] + i.
 //   qabs[b, h] = [q^C_h W_uk[:, kv(h)]^T ; q^R_h]      (fp32, [B, n_H, d_c + d_r])
 hipError_t launch_absorb_generic(const float *qc, const float *qr, const void *w_uk, float *qabs,
                                  int32_t B, const LayerDims &d, DT dt, hipStream_t s);
-//   o[b, h] = sum_s softmax_s(tau qabs[b, h] . cache[b, s]) cache[b, s, 0:d_c]   (fp32)
+//   o[v, h] = sum_s softmax_s(tau qabs[v, h] . cache[b, s]) cache[b, s, 0:d_c]   (fp32), s over the
+//   visible keys of position pos[b] + i
 hipError_t launch_latent_attention_generic(const float *qabs, const void *cache, float *o,
-                                           const int32_t *pos, int32_t B, int32_t max_len,
-                                           const LayerDims &d, DT dt, hipStream_t s);
+                                           const int32_t *pos, int32_t B, int32_t q_len,
+                                           int32_t max_len, const LayerDims &d, DT dt,
+                                           hipStream_t s);
 //   heads[b, h] = o[b, h] W_uv[:, kv(h)]   (fp32 [B, n_H, d_h])
 hipError_t launch_unabsorb_generic(const float *o, const void *w_uv, float *heads, int32_t B,
                                    const LayerDims &d, DT dt, hipStream_t s);

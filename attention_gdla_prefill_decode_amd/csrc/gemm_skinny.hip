@@ -1,10 +1,12 @@
-// Skinny bf16 GEMM for decode-sized batches (at most 64 rows): C[M, N] = A[M, K] . B[K, N] with
+// Skinny bf16 GEMM for decode-sized batches (at most 256 rows): C[M, N] = A[M, K] . B[K, N] with
 // the weights B in their stored [K, N] layout, for the projections of one decode step (Motif 3
 // Technical Report, picx.dev summary section 2.2: Eq.(1)-(3), (7), (9) and the output projection
 // of Eq.(10)).  With so few rows the product is bound by streaming the weights once from HBM, so
 // the work is cut into many workgroups: 64 columns each, and, when the column tiles alone do not
 // fill the chip, split along K into `splits` slices whose fp32 partial sums a second kernel adds
-// in a fixed order (deterministic).
+// in a fixed order (deterministic).  More than 64 rows take up to 4 row blocks of 64; the row
+// blocks of one weight tile are neighbouring workgroups, so they stream that tile at about the
+// same time.
 //
 // One workgroup = 4 waves; per 64-deep k-step it stages the weight tile B[k0:+64, n0:+64] and the
 // activation tile A[0:64, k0:+64] (8 KB each) by direct global -> LDS 16-byte loads into a 4-stage
@@ -25,6 +27,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int SM = 64;          // rows (M) per workgroup
+constexpr int MAX_MB = 4;       // row blocks: at most 256 rows
 constexpr int SN = 64;          // columns per workgroup
 constexpr int SK = 64;          // k per stage
 constexpr int NST = 4;          // ring stages
@@ -55,20 +58,21 @@ __device__ __forceinline__ int aslot(int m, int c) { return c ^ (m & 7); }
 struct SkinnyArgs {
   GemmBatch g;
   float *partial;   // [splits, M, n_total] fp32 when splits > 1
-  int32_t splits, n_total;
+  int32_t splits, n_total, mblocks;
   int32_t col0[kMaxGemmProblems];  // column offset of each problem in the partial rows
 };
 
 __global__ void __launch_bounds__(256) gemm_skinny_kernel(const SkinnyArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t ring[NST * (TILE_B + TILE_A)];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tile = (int)blockIdx.x / a.mblocks;
   int pi = 0;
 #pragma unroll 1
   for (int i = 1; i < a.g.n; ++i)
-    if ((int)blockIdx.x >= a.g.p[i].tile0) pi = i;
+    if (tile >= a.g.p[i].tile0) pi = i;
   const GemmProblem &P = a.g.p[pi];
-  const int n0 = ((int)blockIdx.x - P.tile0) * SN;
-  const int m0 = (int)blockIdx.z * SM;
+  const int n0 = (tile - P.tile0) * SN;
+  const int m0 = ((int)blockIdx.x % a.mblocks) * SM;
   const int ks = P.K / a.splits;
   const int kbeg = (int)blockIdx.y * ks;
   const int nsteps = ks / SK;
@@ -186,14 +190,15 @@ __global__ void __launch_bounds__(256) skinny_reduce_kernel(const SkinnyArgs a) 
 }
 
 // split count: double while the workgroups do not cover the chip (256 compute units), every K
-// splits into whole stages and the slices stay at least 4 stages deep.  So splits * tiles < 512,
-// which bounds the partial sums (skinny_gemm_partial_bound).
+// splits into whole stages and the slices stay at least 4 stages deep.  So splits * tiles * row
+// blocks < 512, which bounds the partial sums (skinny_gemm_partial_bound).
 int choose_splits(const GemmBatch &g) {
   int tiles = 0;
   for (int i = 0; i < g.n; ++i) tiles += g.p[i].N / SN;
+  const int mb = (g.p[0].M + SM - 1) / SM;
   int s = 1;
   for (;;) {
-    bool ok = tiles * s < 256;
+    bool ok = tiles * mb * s < 256;
     for (int i = 0; i < g.n && ok; ++i) ok = g.p[i].K % (2 * s * SK) == 0 && g.p[i].K / (2 * s) >= 4 * SK;
     if (!ok) return s;
     s *= 2;
@@ -203,7 +208,7 @@ int choose_splits(const GemmBatch &g) {
 }  // namespace
 
 bool skinny_problem_ok(const GemmProblem &p) {
-  return p.M >= 1 && p.M <= SM && p.N % SN == 0 && p.K % SK == 0 && p.K >= SK && p.a_f16 == 0 &&
+  return p.M >= 1 && p.M <= SM * MAX_MB && p.N % SN == 0 && p.K % SK == 0 && p.K >= SK && p.a_f16 == 0 &&
          p.epi == EPI_NONE && !p.c_trans && (p.c_dt == CD_F32 || p.c_dt == CD_IN) && p.lda % 8 == 0 &&
          p.ldb % 8 == 0 && p.ldc % 4 == 0 && ((uintptr_t)p.A & 15) == 0 && ((uintptr_t)p.B & 15) == 0 &&
          ((uintptr_t)p.C & 15) == 0 && p.hw == p.N && p.hs == 0 && p.ho == 0 &&
@@ -241,11 +246,12 @@ hipError_t launch_gemm_skinny(const GemmBatch &g, void *partial, size_t partial_
     cols += g.p[i].N;
   }
   a.n_total = cols;
+  a.mblocks = (g.p[0].M + SM - 1) / SM;
   if (a.splits > 1) {
     if (!partial || partial_bytes < (size_t)a.splits * g.p[0].M * cols * 4) return hipErrorInvalidValue;
     a.partial = (float *)partial;
   }
-  hipLaunchKernelGGL(gemm_skinny_kernel, dim3(tiles, a.splits, 1), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(gemm_skinny_kernel, dim3(tiles * a.mblocks, a.splits, 1), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   const int64_t quads = (int64_t)g.p[0].M * cols / 4;

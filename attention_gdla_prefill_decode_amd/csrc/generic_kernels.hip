@@ -361,14 +361,14 @@ constexpr int kMaxLatentChunks = 16;  // d_c + d_r <= 1024
 template <typename T>
 __global__ void __launch_bounds__(256) latent_attention_kernel(const float *qabs, const T *cache,
                                                                float *o, const int32_t *pos,
-                                                               int32_t B, int32_t max_len,
-                                                               LayerDims d) {
+                                                               int32_t B, int32_t q_len,
+                                                               int32_t max_len, LayerDims d) {
   const int lane = threadIdx.x & 63;
-  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (wid >= (int64_t)B * d.n_heads) return;
-  const int b = (int)(wid / d.n_heads);
+  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b q_len + i) n_H + h
+  if (wid >= (int64_t)B * q_len * d.n_heads) return;
+  const int v = (int)(wid / d.n_heads), b = v / q_len;
   const int row = d.d_c + d.d_r;
-  const int p = pos[b];
+  const int p = pos[b] + v % q_len;
   const int lo = d.window > 0 ? max(0, p - d.window + 1) : 0;
   const float *q = qabs + wid * row;
   const T *c = cache + (int64_t)b * max_len * row;
@@ -408,17 +408,18 @@ __global__ void __launch_bounds__(256) latent_attention_kernel(const float *qabs
 }
 
 hipError_t launch_latent_attention_generic(const float *qabs, const void *cache, float *o,
-                                           const int32_t *pos, int32_t B, int32_t max_len,
-                                           const LayerDims &d, DT dt, hipStream_t s) {
-  const int64_t waves = (int64_t)B * d.n_heads;
+                                           const int32_t *pos, int32_t B, int32_t q_len,
+                                           int32_t max_len, const LayerDims &d, DT dt,
+                                           hipStream_t s) {
+  const int64_t waves = (int64_t)B * q_len * d.n_heads;
   if (waves == 0) return hipSuccess;
   const dim3 grid((unsigned)((waves + 3) / 4));
   if (dt == DT::F32)
     hipLaunchKernelGGL(latent_attention_kernel<float>, grid, dim3(256), 0, s, qabs,
-                       (const float *)cache, o, pos, B, max_len, d);
+                       (const float *)cache, o, pos, B, q_len, max_len, d);
   else
     hipLaunchKernelGGL(latent_attention_kernel<bf16_t>, grid, dim3(256), 0, s, qabs,
-                       (const bf16_t *)cache, o, pos, B, max_len, d);
+                       (const bf16_t *)cache, o, pos, B, q_len, max_len, d);
   return hipGetLastError();
 }
 

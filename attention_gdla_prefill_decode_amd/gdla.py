@@ -22,7 +22,9 @@ WEIGHT_FIELDS = ("w_qa", "gamma_q", "w_qc", "w_qr", "w_dkv", "w_kr", "gamma_kv",
                  "w_lambda", "w_gate", "w_o")
 
 EXPORTED = ("gdla_workspace_bytes", "gdla_latent_append", "gdla_prefill", "gdla_decode",
-            "gdla_status_string", "gdla_last_error")
+            "gdla_decode_tokens", "gdla_status_string", "gdla_last_error")
+
+MAX_DECODE_TOKENS = 16  # GDLA_MAX_DECODE_TOKENS
 
 
 class GdlaDims(ctypes.Structure):
@@ -120,6 +122,11 @@ def lib():
                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                   P(GdlaDebug), ctypes.c_void_p]
+        L.gdla_decode_tokens.restype = ctypes.c_int
+        L.gdla_decode_tokens.argtypes = [P(GdlaDims), P(GdlaWeights), ctypes.c_void_p, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_size_t, P(GdlaDebug), ctypes.c_void_p]
         L.gdla_status_string.restype = ctypes.c_char_p
         L.gdla_status_string.argtypes = [ctypes.c_int]
         L.gdla_last_error.restype = ctypes.c_char_p
@@ -225,4 +232,21 @@ def gdla_decode(dims, weights, x, pos, cache, out=None, ws=None, lambda_override
     _check(lib().gdla_decode(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B,
                              _pos_array(pos), _ptr(cache), max_len, _ptr(out), _ptr(ws), nbytes,
                              None if dbg is None else ctypes.byref(dbg), _stream(stream)))
+    return out
+
+
+def gdla_decode_tokens(dims, weights, x, pos, cache, out=None, ws=None, lambda_override=None,
+                       out_heads=None, stream=None, timer=None):
+    """x [B, T, d_model], token i of sequence b at position pos[b] + i (T <= MAX_DECODE_TOKENS);
+    appends to cache; returns out [B, T, d_model] (absorbed decode path)."""
+    B, T = x.shape[0], x.shape[1]
+    max_len = cache.shape[1]
+    if out is None:
+        out = torch.empty_like(x)
+    ws, nbytes = _workspace(dims, GDLA_OP_DECODE, B, T, pos, max_len, ws, x.device)
+    dbg = _debug(lambda_override, out_heads, timer)
+    _check(lib().gdla_decode_tokens(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B, T,
+                                    _pos_array(pos), _ptr(cache), max_len, _ptr(out), _ptr(ws),
+                                    nbytes, None if dbg is None else ctypes.byref(dbg),
+                                    _stream(stream)))
     return out

@@ -8,10 +8,13 @@ library around it), and the fp64 CPU oracle timed on a bounded sample of the sam
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode] [--no-cpu-baseline]
                     [--workload prefill_8k|swa_prefill_2x32k|chunked_prefill_4k_256k|decode_64x64k]
+                    [--tokens T]
 
 --workload picks another workload for the timed line (2 x 32K prefill with a 4096 window; a
 4096-token chunk against a 256K cache; one decode step of 64 sequences at 64K context, reported
-in GB/s of latent cache); --decode appends the decode measurement to the 8K line.
+in GB/s of latent cache); --decode appends the decode measurement to the 8K line.  With the
+decode workload, --tokens T > 1 times the multi-token decode (T draft tokens per sequence,
+ending at position 65535) instead of the single-token step.
 """
 
 import argparse
@@ -108,27 +111,35 @@ def cpu_baseline(rows=2048):
                       f"{flops / 1e12:.3f} TFLOP of algorithmic work"}
 
 
-def bench_decode(steps, warmup):
+def bench_decode(steps, warmup, tokens=1):
+    """64 sequences with a 65536-position context.  tokens = 1: one decode step (gdla_decode, the
+    new token at position 65535); tokens = T > 1: T draft tokens per sequence at positions
+    65536 - T .. 65535 in one gdla_decode_tokens call."""
     import torch
     import synth
     import attention_gdla_prefill_decode_amd as gd
     cfg = synth.WORKLOADS["decode_64x64k"]
-    inp = synth.make_inputs(cfg, "cuda")
+    inp = synth.make_inputs(cfg, "cuda", seq=tokens, p0=cfg["max_len"] - tokens)
     w = gd.make_weights(inp["weights"])
     dims = gd.make_dims(cfg)
-    x = inp["x"][:, 0].contiguous()
     pos = inp["p0"]
-    ws = torch.empty(gd.gdla_workspace_bytes(dims, gd.GDLA_OP_DECODE, len(pos), 1, pos, cfg["max_len"]),
+    if tokens == 1:
+        x = inp["x"][:, 0].contiguous()
+        run = gd.gdla_decode
+    else:
+        x = inp["x"]
+        run = gd.gdla_decode_tokens
+    ws = torch.empty(gd.gdla_workspace_bytes(dims, gd.GDLA_OP_DECODE, len(pos), tokens, pos, cfg["max_len"]),
                      dtype=torch.uint8, device="cuda")
     out = torch.empty_like(x)
     timers = [gd.StageTimer() for _ in range(steps)]
     for _ in range(warmup):
-        gd.gdla_decode(dims, w, x, pos, inp["cache"], out=out, ws=ws)
+        run(dims, w, x, pos, inp["cache"], out=out, ws=ws)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(steps):
-        gd.gdla_decode(dims, w, x, pos, inp["cache"], out=out, ws=ws, timer=timers[i])
+        run(dims, w, x, pos, inp["cache"], out=out, ws=ws, timer=timers[i])
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
@@ -136,23 +147,38 @@ def bench_decode(steps, warmup):
     for tm in timers:
         for k, v in tm.elapsed().items():
             stages[k] += v / steps
-    # Algorithmic bytes of the latent-attention kernel: every visible cache row once, the absorbed
-    # query of every head (bf16) and the attended latent o of every head (fp32).
-    keys = sum(min(p + 1, cfg["window"]) if cfg["window"] > 0 else p + 1 for p in pos)
+    # Algorithmic bytes of the latent-attention kernel: every cache row visible to the last token
+    # once per sequence, the absorbed query of every head and token (bf16) and the attended
+    # latent o of every head and token (fp32).
+    last = [p + tokens - 1 for p in pos]
+    keys = sum(min(p + 1, cfg["window"]) if cfg["window"] > 0 else p + 1 for p in last)
     row = cfg["d_kv_latent"] + cfg["d_rope"]
-    nbytes = keys * row * 2 + len(pos) * cfg["n_heads"] * (row * 2 + cfg["d_kv_latent"] * 4)
+    nbytes = keys * row * 2 + len(pos) * tokens * cfg["n_heads"] * (row * 2 + cfg["d_kv_latent"] * 4)
     kern_ms = stages["attn_noise"]
     gbs = nbytes / kern_ms / 1e6
-    return {"workload": "decode_64x64k", "batch": len(pos), "context": int(pos[0]) + 1,
+    # Algorithmic FLOP: per head, token and visible key a 576-long score dot product and a
+    # 512-long weighted sum.  Above the ridge (312.5 FLOP/B) the kernel is MFMA-bound: from two
+    # tokens per sequence on, since every token multiplies the work on each cache row.
+    vis = sum(min(p + i + 1, cfg["window"]) if cfg["window"] > 0 else p + i + 1
+              for p in pos for i in range(tokens))
+    flop = 2.0 * cfg["n_heads"] * vis * (row + cfg["d_kv_latent"])
+    if flop / nbytes > PEAK_MFMA_TFLOPS * 1e3 / PEAK_HBM_GBS:
+        tfs = flop / kern_ms / 1e9
+        roof = {"bound": "mfma", "achieved": round(tfs, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tfs / PEAK_MFMA_TFLOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    name = "decode_64x64k" if tokens == 1 else f"decode_tokens_64x64k_t{tokens}"
+    return {"workload": name, "batch": len(pos), "tokens": tokens, "context": int(last[0]) + 1,
             "ms_per_step": round(ms, 4),
             "latent_GBps_whole_step": round(nbytes / ms / 1e6, 1),
-            "tokens_per_s": round(len(pos) / ms * 1e3, 1),
-            "roofline": {"kernel": "latent_decode_kernel<shared>", "bound": "hbm",
-                         "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": traffic_from_profile("latent_decode_64x64k_traffic.json"),
-                         "bytes_per_launch": nbytes,
-                         "avg_launch_ms": round(kern_ms, 4)},
+            "tokens_per_s": round(len(pos) * tokens / ms * 1e3, 1),
+            "roofline": dict({"kernel": "latent_decode_kernel<shared>"}, **roof,
+                             traffic=(traffic_from_profile("latent_decode_64x64k_traffic.json")
+                                      if tokens == 1 else None),
+                             bytes_per_launch=nbytes, flop_per_launch=flop,
+                             avg_launch_ms=round(kern_ms, 4)),
             "stages_ms": {k: round(v, 4) for k, v in stages.items()}}
 
 
@@ -167,6 +193,9 @@ def main():
     ap.add_argument("--workload", default="prefill_8k",
                     choices=["prefill_8k", "swa_prefill_2x32k", "chunked_prefill_4k_256k", "decode_64x64k"],
                     help="workload of the timed line (default: the 8K prefill)")
+    ap.add_argument("--tokens", type=int, default=1,
+                    help="with --workload decode_64x64k or --decode-only: draft tokens per sequence "
+                         "(T > 1 times gdla_decode_tokens, the multi-token verification step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 1 GiB device to device three times (a known-size reference "
@@ -192,18 +221,18 @@ def main():
         return
 
     if args.decode_only:
-        print(json.dumps(bench_decode(args.steps, args.warmup)), flush=True)
+        print(json.dumps(bench_decode(args.steps, args.warmup, args.tokens)), flush=True)
         return
 
     if args.workload == "decode_64x64k":
-        d = bench_decode(args.steps, args.warmup)
+        d = bench_decode(args.steps, args.warmup, args.tokens)
         result = {
             "metric": METRIC, "value": round(d["latent_GBps_whole_step"], 1), "unit": "GB/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": d["ms_per_step"],
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "bf16 (fp32 accumulate)", "data": "synthetic",
-            "config": {"workload": "decode_64x64k", "batch": 64, "context": 65536,
-                       "parallelism": "none (1 GPU)"},
+            "config": {"workload": d["workload"], "batch": 64, "tokens_per_sequence": args.tokens,
+                       "context": 65536, "parallelism": "none (1 GPU)"},
             "roofline": d["roofline"], "stages_ms": d["stages_ms"], "tokens_per_s": d["tokens_per_s"],
         }
         print(json.dumps(result), flush=True)

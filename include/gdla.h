@@ -68,6 +68,9 @@ typedef enum { GDLA_F32 = 0, GDLA_BF16 = 1 } gdla_dtype;
 
 typedef enum { GDLA_OP_PREFILL = 0, GDLA_OP_DECODE = 1, GDLA_OP_APPEND = 2 } gdla_op;
 
+/* Most new tokens per sequence that gdla_decode_tokens takes in one call. */
+#define GDLA_MAX_DECODE_TOKENS 16
+
 /* Layer sizes (picx.dev summary section 2.2).  n_heads = n_signal + n_noise, n_signal is a
  * multiple g of n_noise (Eq.(6)), and n_kv_heads divides n_noise. */
 typedef struct {
@@ -131,7 +134,8 @@ enum {
   GDLA_N_STAGES
 };
 
-/* Bytes of workspace that op needs for B sequences of T new tokens each (T = 1 for decode).
+/* Bytes of workspace that op needs for B sequences of T new tokens each (GDLA_OP_DECODE: T = 1
+ * for gdla_decode, 1 .. GDLA_MAX_DECODE_TOKENS for gdla_decode_tokens).
  * pos_host (host, [B], may be NULL) gives the first new position of each sequence; with NULL the
  * size is an upper bound for any positions with pos + T <= max_len.  Returns 0 for invalid
  * dims or sizes.  The workspace must be 256-byte aligned. */
@@ -160,6 +164,21 @@ gdla_status gdla_prefill(const gdla_dims *dims, const gdla_weights *w, const voi
 gdla_status gdla_decode(const gdla_dims *dims, const gdla_weights *w, const void *x, int32_t B,
                         const int32_t *pos_host, void *cache, int32_t max_len, void *out,
                         void *ws, size_t ws_bytes, const gdla_debug *dbg, hipStream_t stream);
+
+/* Several new tokens per sequence on the absorbed decode path: the verification step of
+ * self-speculative decoding with a multi-token-prediction head (picx.dev summary section 2.1, the
+ * MTP component; alphasignal.ai news page, "A wall of custom parts").  The T tokens of sequence b
+ * (x [B, T, d_model], 0 <= T <= GDLA_MAX_DECODE_TOKENS) sit at positions pos_host[b] ..
+ * pos_host[b] + T - 1.  Their latent rows are appended, then token i attends over cache rows
+ * [0, pos_host[b] + i] (window permitting), so the draft tokens see each other causally.  The
+ * result is that of gdla_prefill on the same arguments, computed in the absorbed form: every
+ * cache row is read from HBM once per sequence for all T tokens.  out [B, T, d_model].  T = 1 is
+ * gdla_decode.  Workspace: gdla_workspace_bytes(dims, GDLA_OP_DECODE, B, T, ...).  Errors as
+ * gdla_decode, plus GDLA_ERR_INVALID_ARG for T outside 0 .. GDLA_MAX_DECODE_TOKENS. */
+gdla_status gdla_decode_tokens(const gdla_dims *dims, const gdla_weights *w, const void *x,
+                               int32_t B, int32_t T, const int32_t *pos_host, void *cache,
+                               int32_t max_len, void *out, void *ws, size_t ws_bytes,
+                               const gdla_debug *dbg, hipStream_t stream);
 
 /* Static description of a status code. */
 const char *gdla_status_string(gdla_status s);

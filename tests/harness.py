@@ -69,8 +69,9 @@ def device_inputs(inp, device="cuda"):
 
 
 def prefill_case(cfg, seq, p0, window=0, seed=None, random_gamma=True, lam_zero=False,
-                 want_heads=False):
-    """Runs gdla_prefill on GPU and the oracle on CPU for every sequence; returns both outputs."""
+                 want_heads=False, entry="prefill"):
+    """Runs gdla_prefill (or, with entry="decode_tokens", the multi-token absorbed decode) on GPU
+    and the oracle's one-call forward on CPU for every sequence; returns both outputs."""
     batch = len(p0)
     inp = synth.make_inputs(cfg, "cpu", seed=seed, batch=batch, seq=seq, p0=p0,
                             random_gamma=random_gamma)
@@ -83,8 +84,9 @@ def prefill_case(cfg, seq, p0, window=0, seed=None, random_gamma=True, lam_zero=
     if want_heads:
         heads = torch.empty((batch, seq, cfg["n_heads"], cfg["d_head"]), dtype=torch.float32,
                             device="cuda")
-    out = gd.gdla_prefill(dims, dev["wstruct"], dev["x"], inp["p0"], dev["cache"],
-                          lambda_override=lam, out_heads=heads)
+    run = gd.gdla_prefill if entry == "prefill" else gd.gdla_decode_tokens
+    out = run(dims, dev["wstruct"], dev["x"], inp["p0"], dev["cache"], lambda_override=lam,
+              out_heads=heads)
     torch.cuda.synchronize()
     w = oracle_weights(inp)
     od = oracle_dims(cfg, window)

@@ -61,7 +61,12 @@ def test_workspace_bytes():
         gd.gdla_workspace_bytes(d, gd.GDLA_OP_PREFILL, 1, 4096, [100000], 262144)
     # invalid requests report 0
     assert gd.gdla_workspace_bytes(d, gd.GDLA_OP_PREFILL, 1, 10, [8190], 8192) == 0
-    assert gd.gdla_workspace_bytes(d, gd.GDLA_OP_DECODE, 4, 2, None, 64) == 0
+    # several tokens per sequence on the decode path: workspace grows with B T
+    dec4 = gd.gdla_workspace_bytes(d, gd.GDLA_OP_DECODE, 64, 4, [65532] * 64, 65536)
+    assert dec4 > dec
+    assert gd.gdla_workspace_bytes(d, gd.GDLA_OP_DECODE, 4, gd.MAX_DECODE_TOKENS, None, 64) > 0
+    assert gd.gdla_workspace_bytes(d, gd.GDLA_OP_DECODE, 4, gd.MAX_DECODE_TOKENS + 1, None, 64) == 0
+    assert gd.gdla_workspace_bytes(d, gd.GDLA_OP_DECODE, 1, 4, [61], 64) == 0
     assert gd.gdla_workspace_bytes(d, 7, 1, 1, None, 64) == 0
     assert gd.gdla_workspace_bytes(big_dims(n_noise=15), gd.GDLA_OP_PREFILL, 1, 1, None, 8) == 0
 
@@ -168,3 +173,23 @@ def test_decode_and_append_argument_errors():
     st = lib.gdla_latent_append(ctypes.byref(d), ctypes.byref(w), FAKE, 2, 3, pos, FAKE, 64, FAKE,
                                 16, None)
     assert st == gb.GDLA_ERR_WORKSPACE
+
+
+def test_decode_tokens_argument_errors():
+    lib = gd.lib()
+    d = big_dims()
+    w = gb.GdlaWeights(*([FAKE] * 12))
+    pos = (ctypes.c_int32 * 2)(5, 60)
+
+    def call(T, pos=pos, ws_bytes=1 << 40):
+        return lib.gdla_decode_tokens(ctypes.byref(d), ctypes.byref(w), FAKE, 2, T, pos, FAKE, 64,
+                                      FAKE, FAKE, ws_bytes, None, None)
+
+    assert call(gd.MAX_DECODE_TOKENS + 1) == gb.GDLA_ERR_INVALID_ARG
+    assert lib.gdla_last_error().decode()
+    assert call(-1) == gb.GDLA_ERR_INVALID_ARG
+    assert call(5) == gb.GDLA_ERR_OUT_OF_RANGE  # 60 + 5 > 64
+    assert call(4, ws_bytes=16) == gb.GDLA_ERR_WORKSPACE
+    # T = 0: nothing to do
+    assert lib.gdla_decode_tokens(ctypes.byref(d), ctypes.byref(w), None, 2, 0, pos, None, 64, None,
+                                  None, 0, None, None) == gb.GDLA_OK

@@ -149,10 +149,62 @@ def test_bf16_decode(p0):
 
 
 def test_bf16_decode_batch_over_64():
-    # 72 sequences: more rows than the skinny projection kernel takes (general GEMM)
+    # 72 sequences: the skinny projection kernel's second row block holds 8 rows
     r = H.decode_case(BF, [(37 * b) % 500 for b in range(72)], seed=41)
     _say(H.check(r["out"], r["exp_out"], "bf16", "bf16 decode B=72"))
     H.check_rows(r["rows"], r["exp_rows"], "bf16", "bf16 decode cache rows")
+
+
+# ---------------------------------------------------------------- multi-token decode
+# T draft tokens per sequence on the absorbed path (token i at position p0 + i sees the cache and
+# tokens 0..i), against the oracle's one-call forward over the same T tokens.
+@pytest.mark.parametrize("T,p0,window", [(3, [0, 5, 120], 0), (2, [64], 0), (16, [40], 0), (4, [90, 7], 9)])
+def test_fp32_decode_tokens(T, p0, window):
+    r = H.prefill_case(TINY, T, p0, window=window, seed=29, want_heads=True, entry="decode_tokens")
+    _say(H.check(r["out"], r["exp_out"], "f32", f"fp32 decode_tokens T={T} p0={p0} W={window}"))
+    err = float(np.max(np.abs(r["heads"] - r["exp_heads"])))
+    assert err <= 1e-5, f"per-head H max-abs {err:.3e}"
+    for b in range(len(p0)):
+        H.check_rows(r["rows"][b], r["exp_rows"][b], "f32", "fp32 cache rows")
+
+
+@pytest.mark.parametrize("cfg,T,p0", [
+    (BF, 2, [0, 33, 1000]),            # ten heads (one head block), first token at position 0
+    (BF, 4, [4095, 31, 64]),           # tokens across a tile boundary
+    (H.BF80, 4, [0, 700, 2047]),       # five head blocks, the fifth shared
+    (H.BF72, 3, [3000, 5]),            # partly filled fifth block
+    (dict(H.BF80, window=1000), 4, [2500, 40, 998]),  # window edge inside the draft
+    (BF, 16, [100, 4, 300, 50]),       # 64 query rows (one row block of the skinny projection)
+    (BF, 5, [10] * 13),                # 65 query rows (a second row block of one row)
+    (BF, 16, [3 * b for b in range(17)]),  # 272 query rows (general projection GEMM)
+])
+def test_bf16_decode_tokens(cfg, T, p0):
+    r = H.prefill_case(cfg, T, p0, window=cfg.get("window", 0), seed=31, want_heads=True,
+                       entry="decode_tokens")
+    _say(H.check(r["out"], r["exp_out"], "bf16", f"bf16 decode_tokens n_H={cfg['n_heads']} T={T}"))
+    H.check(r["heads"], r["exp_heads"], "bf16", "per-head H")
+    for b in range(len(p0)):
+        H.check_rows(r["rows"][b], r["exp_rows"][b], "bf16", "bf16 cache rows")
+
+
+def test_decode_tokens_matches_decode_and_prefill():
+    """T = 1 is gdla_decode bit for bit; T = 4 agrees with gdla_prefill of the same tokens."""
+    cfg = H.BF80
+    inp = synth.make_inputs(cfg, "cpu", batch=3, seq=4, p0=[500, 9, 1999], random_gamma=True)
+    dev = H.device_inputs(inp)
+    dims = gd.make_dims(cfg)
+    c1, c2 = dev["cache"].clone(), dev["cache"].clone()
+    one = gd.gdla_decode(dims, dev["wstruct"], dev["x"][:, 0].contiguous(), inp["p0"], c1)
+    tok = gd.gdla_decode_tokens(dims, dev["wstruct"], dev["x"][:, :1].contiguous(), inp["p0"], c2)
+    torch.cuda.synchronize()
+    assert torch.equal(one, tok[:, 0]) and torch.equal(c1, c2)
+    c3, c4 = dev["cache"].clone(), dev["cache"].clone()
+    pre = gd.gdla_prefill(dims, dev["wstruct"], dev["x"], inp["p0"], c3)
+    dec = gd.gdla_decode_tokens(dims, dev["wstruct"], dev["x"], inp["p0"], c4)
+    torch.cuda.synchronize()
+    _say(H.check(H.to_np(dec), H.to_np(pre), "bf16", "decode_tokens vs prefill"))
+    for bi, p in enumerate(inp["p0"]):  # the same rows, up to the projection GEMMs' rounding
+        H.check_rows(H.to_np(c4[bi, p:p + 4]), H.to_np(c3[bi, p:p + 4]), "bf16", "appended rows")
 
 
 def test_bf16_lambda_zero_is_gated_mla():
