@@ -57,15 +57,16 @@ constexpr int DMA_PER_WAVE = TILE_CH / 64 / MAX_WAVES;  // 16-byte loads per lan
 constexpr int MAX_HEADS = 16 * (MAX_WAVES + 1);
 constexpr int WDB = NDB / MAX_WAVES;    // dim blocks of 16 owned by each wave (8)
 constexpr int NHB = MAX_WAVES + 1;      // head blocks of 16 (at most)
+constexpr int PG_CAP = 1024;            // pages of a split's block-table slice kept in LDS
 
 // Queries are indexed by v = b q_len + i: token i of sequence b, at position pos[b] + i.
 struct DecodeArgs {
   const bf16_t *qabs;  // [B q_len, n_H, 576] bf16
-  const bf16_t *cache; // [B, max_len, 576] bf16
+  CacheRef cache;      // bf16 rows of 576 (contiguous or paged in pages of a multiple of 32 rows)
   const int32_t *pos;  // [B] position of the first new token (token i sees keys 0 .. pos + i)
   float *part_o;       // [B q_len, splits, n_H, 512]
   float *part_ml;      // [B q_len, splits, n_H, 2]
-  int32_t B, q_len, n_heads, max_len, window, splits;
+  int32_t B, q_len, n_heads, window, splits;
   float c;             // softmax scale * log2(e)
 };
 
@@ -118,14 +119,17 @@ struct SoftmaxState {
 };
 
 // Scores -> probabilities for one tile (score of key s0 + 16 kb + 4 g + j in S[kb][j]); `lim` =
-// k_end - s0 - 4 g masks the keys past the split.  Returns P^T as the B operand of the 32-key step
-// (slot e <-> key 16 (e / 4) + 4 g + e % 4).  Branch-free, so it stays in the MFMA block.
-__device__ __forceinline__ void softmax_tile(f32x4 (&S)[2], SoftmaxState &st, int lim, float c, bf16x8 &P) {
+// k_end - s0 - 4 g masks the keys past the split and, with LOWER (paged cache with a window: the
+// first tile, aligned to the pages, may start below it), `llim` = lo - s0 - 4 g those before it.  Returns P^T as the B operand of the 32-key
+// step (slot e <-> key 16 (e / 4) + 4 g + e % 4).  Branch-free, so it stays in the MFMA block.
+template <bool LOWER>
+__device__ __forceinline__ void softmax_tile(f32x4 (&S)[2], SoftmaxState &st, int llim, int lim, float c,
+                                             bf16x8 &P) {
   float v[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int kidx = 16 * (i >> 2) + (i & 3);
-    v[i] = kidx < lim ? S[i >> 2][i & 3] * c : -INFINITY;
+    v[i] = kidx < lim && (!LOWER || kidx >= llim) ? S[i >> 2][i & 3] * c : -INFINITY;
   }
   float mt = v[0];
 #pragma unroll
@@ -160,9 +164,9 @@ __device__ __forceinline__ uint32_t lds_u32(const void *p) {
 // whole block (so its P^T needs no further exchange).
 constexpr int K4N = NKST / 2;  // k-steps of the shared block per wave (9)
 
-template <bool SHARED, int ROLE>
+template <bool SHARED, bool PAGED, bool LOWER, int ROLE>
 __device__ __forceinline__ void decode_body(const DecodeArgs &a, bf16_t *CB, bf16x8 (*PB)[64], f32x4 (*S4B)[64],
-                                            int wave) {
+                                            int32_t *PG, int wave) {
   constexpr int KB4 = ROLE >> 1, K4LO = (ROLE & 1) * K4N;
   const int lane = threadIdx.x & 63;
   int b, tok, sp;
@@ -170,9 +174,12 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, bf16_t *CB, bf1
   const int v = b * a.q_len + tok;  // query row set
   const int p = a.pos[b] + tok;
   const int lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
-  const int span = p + 1 - lo;
+  // PAGED: tiles start on multiples of KT (so a tile never crosses a page) and the keys below lo
+  // of the first tile are masked; contiguous: tiles start at lo
+  const int kbase = PAGED ? lo & ~(KT - 1) : lo;
+  const int span = p + 1 - kbase;
   const int kps = ((span + a.splits - 1) / a.splits + KT - 1) / KT * KT;  // keys per split
-  const int k_begin = lo + sp * kps, k_end = min(p + 1, k_begin + kps);
+  const int k_begin = kbase + sp * kps, k_end = min(p + 1, k_begin + kps);
   const int ntiles = k_end > k_begin ? (k_end - k_begin + KT - 1) / KT : 0;
   const int col = lane & 15, g = lane >> 4;
   const int head = 16 * wave + col, head4 = 16 * MAX_WAVES + col;
@@ -199,10 +206,40 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, bf16_t *CB, bf1
     }
   }
 
-  const bf16_t *cb = a.cache + (int64_t)b * a.max_len * ROW;
+  // PAGED: the physical pages of the split's blocks are copied to LDS once (when there are at
+  // most PG_CAP of them), so a tile's page costs an LDS read, not a scalar memory load (whose wait
+  // the compiler would merge with the next LDS wait of the tile loop).
+  const CacheRef &cr = a.cache;
+  const bf16_t *cb = (const bf16_t *)cr.base + (PAGED ? 0 : (int64_t)b * cr.max_len * ROW);
+  int blk0 = 0;
+  bool pg_lds = false;
+  if (PAGED) {
+    blk0 = k_begin / cr.page_rows;
+    const int nblk = ntiles > 0 ? (k_begin + ntiles * KT - 1) / cr.page_rows - blk0 + 1 : 0;
+    pg_lds = nblk > 0 && nblk <= PG_CAP;
+    if (pg_lds) {
+      const int32_t *bt = cr.block_table + (int64_t)b * cr.max_blocks + blk0;
+      for (int i = threadIdx.x; i < nblk; i += 64 * MAX_WAVES) PG[i] = min(max(bt[i], 0), cr.n_pages - 1);
+    }
+    __syncthreads();
+  }
+  // first cache row (relative to cb) of the tile at s0; paged, the tiles are visited in order
+  // and (blk, off) = (s0 / page_rows, s0 % page_rows) is advanced without a division
+  int blk = blk0, off = PAGED ? k_begin - blk0 * cr.page_rows : 0;
+  auto tile_row = [&](int s0) -> int64_t {
+    if (!PAGED) return s0;
+    const int64_t r = pg_lds ? (int64_t)PG[blk - blk0] * cr.page_rows + off : cache_row(cr, b, s0);
+    off += KT;
+    if (off == cr.page_rows) {
+      off = 0;
+      ++blk;
+    }
+    return r;
+  };
   // Tile t goes to ring slot t % NBUF; wave w issues wave-instructions w, w + 4, ... of the tile
   // (DMA_PER_WAVE of them).  rowoff[i] is this lane's source offset (bytes) inside the tile.
-  // Keys past k_end are clamped to k_end - 1 (masked later, and always inside the cache).
+  // Keys past k_end (and, paged, before lo) are read from row k_end - 1 (lo) instead: masked later,
+  // and never a row outside the visible range, which a paged cache may no longer map.
   const uint32_t ring = lds_u32(CB);
   int rowoff[DMA_PER_WAVE];
 #pragma unroll
@@ -211,11 +248,14 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, bf16_t *CB, bf1
     const int row = sl / RCH;
     rowoff[i] = row * RB + (((sl % RCH) ^ swz(row)) * 16);
   }
+  // first cache row of the next tile to issue (one block-table lookup ahead when paged)
+  int64_t row_next = 0;
   auto issue = [&](int t) {
     const int s0 = k_begin + t * KT;
     const uint32_t base = ring + (uint32_t)((t % NBUF) * TILE * 2) + wave * 1024;
-    const char *src = (const char *)(cb + (int64_t)s0 * ROW);
-    if (s0 + KT <= k_end) {
+    const char *src = (const char *)(cb + (PAGED ? row_next : (int64_t)s0) * ROW);
+    if (PAGED && t + 1 < ntiles) row_next = tile_row(s0 + KT);
+    if ((!PAGED || s0 >= lo) && s0 + KT <= k_end) {
 #pragma unroll
       for (int i = 0; i < DMA_PER_WAVE; ++i)
         dma16(src + rowoff[i], __builtin_amdgcn_readfirstlane(base + i * MAX_WAVES * 1024));
@@ -223,7 +263,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, bf16_t *CB, bf1
 #pragma unroll
       for (int i = 0; i < DMA_PER_WAVE; ++i) {
         const int row = rowoff[i] / RB;
-        const int off = rowoff[i] - row * RB + (min(s0 + row, k_end - 1) - s0) * RB;
+        const int off = rowoff[i] - row * RB + (min(PAGED ? max(s0 + row, lo) : s0 + row, k_end - 1) - s0) * RB;
         dma16(src + off, __builtin_amdgcn_readfirstlane(base + i * MAX_WAVES * 1024));
       }
     }
@@ -281,8 +321,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, bf16_t *CB, bf1
       else __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
     bf16x8 P;
-    const int lim = k_end - s0 - 4 * g;
-    softmax_tile(S, st, lim, a.c, P);
+    const int lim = k_end - s0 - 4 * g, llim = lo - s0 - 4 * g;
+    softmax_tile<LOWER>(S, st, llim, lim, a.c, P);
     if (SHARED) S4B[wave][lane] = S4p;
     PB[wave][lane] = P;
     __syncthreads();  // P^T of blocks 0..3 and the shared block's partial scores visible to every wave
@@ -293,7 +333,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, bf16_t *CB, bf1
       f32x4 S4[2];
       S4[0] = S4B[0][lane] + S4B[1][lane];
       S4[1] = S4B[2][lane] + S4B[3][lane];
-      softmax_tile(S4, st4, lim, a.c, PH[HB - 1]);
+      softmax_tile<LOWER>(S4, st4, llim, lim, a.c, PH[HB - 1]);
     }
     // PV phase over this wave's dim blocks, pipelined two ahead: [reads of dd + 2][MFMAs of dd]
     bf16x8 vf[3];
@@ -320,6 +360,11 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, bf16_t *CB, bf1
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
   for (;;) {
+    if (PAGED && ntiles > 0) {
+      blk = blk0;
+      off = k_begin - blk0 * cr.page_rows;
+      row_next = tile_row(k_begin);
+    }
     for (int t = 0; t < NBUF - 1 && t < ntiles; ++t) issue(t);
     for (int t = 0; t < ntiles; ++t) {
       wait_tiles_after(min(ntiles - 1 - t, NBUF - 2));
@@ -375,24 +420,26 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, bf16_t *CB, bf1
   }
 }
 
-template <bool SHARED>
+// PAGED: paged cache; LOWER: with a window (paged tiles may then start below it)
+template <bool SHARED, bool PAGED, bool LOWER>
 __global__ void __launch_bounds__(256, 1) latent_decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t CB[NBUF * TILE];
   __shared__ __attribute__((aligned(16))) bf16x8 PB[MAX_WAVES][64];   // P^T of head blocks 0..3
   __shared__ __attribute__((aligned(16))) f32x4 S4B[MAX_WAVES][64];   // partial scores, shared block
+  __shared__ int32_t PG[PAGED ? PG_CAP : 1];                           // physical pages of the split
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   {
     int b, tok, sp;
     if (!decode_unit(a, b, tok, sp)) return;  // uniform over the workgroup, before any barrier
   }
   if (!SHARED) {
-    decode_body<false, 0>(a, CB, PB, S4B, wave);
+    decode_body<false, PAGED, LOWER, 0>(a, CB, PB, S4B, PG, wave);
   } else {
     switch (wave) {  // wave-uniform: each wave runs the code of its part of the shared block
-      case 0: decode_body<true, 0>(a, CB, PB, S4B, 0); break;
-      case 1: decode_body<true, 1>(a, CB, PB, S4B, 1); break;
-      case 2: decode_body<true, 2>(a, CB, PB, S4B, 2); break;
-      default: decode_body<true, 3>(a, CB, PB, S4B, 3); break;
+      case 0: decode_body<true, PAGED, LOWER, 0>(a, CB, PB, S4B, PG, 0); break;
+      case 1: decode_body<true, PAGED, LOWER, 1>(a, CB, PB, S4B, PG, 1); break;
+      case 2: decode_body<true, PAGED, LOWER, 2>(a, CB, PB, S4B, PG, 2); break;
+      default: decode_body<true, PAGED, LOWER, 3>(a, CB, PB, S4B, PG, 3); break;
     }
   }
 }
@@ -551,7 +598,7 @@ int32_t fast_decode_splits(int32_t B, int32_t max_len) {
 }
 
 gdla_status run_fast_decode(const LayerDims &d, const gdla_weights *w, int32_t B, int32_t T,
-                            const int32_t *pos_dev, void *cache, int32_t max_len, const float *qc,
+                            const int32_t *pos_dev, const CacheRef &cache, const float *qc,
                             const float *qr, float *heads, const FastDecodeLayout &L, void *ws, hipStream_t s,
                             StageEvents &se) {
   const int32_t BT = B * T;  // query rows sets: token i of sequence b is row set b T + i
@@ -565,17 +612,21 @@ gdla_status run_fast_decode(const LayerDims &d, const gdla_weights *w, int32_t B
   if (hipGetLastError() != hipSuccess) return GDLA_ERR_HIP;
   se.end(GDLA_STAGE_PROJ_Q);
   DecodeArgs a{};
-  a.qabs = qabs; a.cache = (const bf16_t *)cache; a.pos = pos_dev; a.part_o = part_o; a.part_ml = part_ml;
+  a.qabs = qabs; a.cache = cache; a.pos = pos_dev; a.part_o = part_o; a.part_ml = part_ml;
   const int nblk = (d.n_heads + 15) / 16;
   a.B = B; a.q_len = T;
-  a.n_heads = d.n_heads; a.max_len = max_len; a.window = d.window; a.splits = L.splits;
+  a.n_heads = d.n_heads; a.window = d.window; a.splits = L.splits;
   a.c = d.scale * 1.4426950408889634f;
   se.begin(GDLA_STAGE_ATTN_NOISE);
   const dim3 grid((unsigned)decode_grid(B, T, L.splits));
-  if (nblk > MAX_WAVES)
-    hipLaunchKernelGGL(latent_decode_kernel<true>, grid, dim3(64 * MAX_WAVES), 0, s, a);
-  else
-    hipLaunchKernelGGL(latent_decode_kernel<false>, grid, dim3(64 * MAX_WAVES), 0, s, a);
+  const bool shared = nblk > MAX_WAVES, paged = cache.page_rows > 0, lower = paged && d.window > 0;
+  const dim3 block(64 * MAX_WAVES);
+  if (shared && lower) hipLaunchKernelGGL((latent_decode_kernel<true, true, true>), grid, block, 0, s, a);
+  else if (shared && paged) hipLaunchKernelGGL((latent_decode_kernel<true, true, false>), grid, block, 0, s, a);
+  else if (shared) hipLaunchKernelGGL((latent_decode_kernel<true, false, false>), grid, block, 0, s, a);
+  else if (lower) hipLaunchKernelGGL((latent_decode_kernel<false, true, true>), grid, block, 0, s, a);
+  else if (paged) hipLaunchKernelGGL((latent_decode_kernel<false, true, false>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((latent_decode_kernel<false, false, false>), grid, block, 0, s, a);
   if (hipGetLastError() != hipSuccess) return GDLA_ERR_HIP;
   se.end(GDLA_STAGE_ATTN_NOISE);
   se.begin(GDLA_STAGE_ATTN_SIGNAL);

@@ -103,7 +103,7 @@ bool fast_decode_supported(const LayerDims &d, gdla_dtype dt);
 // T new tokens per sequence (token i of sequence b at position pos_dev[b] + i, already appended);
 // qc, qr, heads hold B T row sets of n_H heads.
 gdla_status run_fast_decode(const LayerDims &d, const gdla_weights *w, int32_t B, int32_t T,
-                            const int32_t *pos_dev, void *cache, int32_t max_len, const float *qc,
+                            const int32_t *pos_dev, const CacheRef &cache, const float *qc,
                             const float *qr, float *heads, const FastDecodeLayout &L, void *ws,
                             hipStream_t s, StageEvents &se);
 

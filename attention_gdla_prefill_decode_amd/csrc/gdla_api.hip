@@ -196,6 +196,33 @@ AppendLayout plan_append(const LayerDims &d, int32_t B, int32_t T) {
   return L;
 }
 
+// Workspace of a paged prefill: the contiguous prefill's (over stage_len positions), then the
+// positions and the staging cache [B, stage_len, d_c + d_r] that the visible rows are gathered into.
+struct PagedPrefillLayout {
+  PrefillLayout pre;
+  size_t pos, stage, total;
+  int32_t stage_len, max_gather;
+};
+
+PagedPrefillLayout plan_prefill_paged(const LayerDims &d, gdla_dtype dt, int32_t B, int32_t T,
+                                      const int32_t *pos, int32_t max_len) {
+  PagedPrefillLayout L{};
+  L.stage_len = pos ? 0 : max_len;
+  L.max_gather = pos ? 0 : max_len - T;
+  if (pos)
+    for (int32_t b = 0; b < B; ++b) {
+      L.stage_len = std::max(L.stage_len, pos[b] + T);
+      L.max_gather = std::max(L.max_gather, pos[b] - key_lo(pos[b], d.window));
+    }
+  L.pre = plan_prefill(d, dt, B, T, pos, L.stage_len);
+  Plan p;
+  p.bytes = L.pre.total;
+  L.pos = p.add(sizeof(int32_t) * B);
+  L.stage = p.add(esize(dt) * (size_t)B * L.stage_len * (d.d_c + d.d_r));
+  L.total = p.bytes;
+  return L;
+}
+
 // ---------------------------------------------------------------------------------------------
 gdla_status check_call(const gdla_dims *dims, const gdla_weights *w, const void *x, int32_t B,
                        int32_t T, const int32_t *pos, const void *cache, int32_t max_len,
@@ -268,8 +295,8 @@ hipError_t launch_gemm_rows(GemmBatch &g, DT dt, void *partial, size_t partial_b
 // First projection, Eq.(1), (3), (7) (x W_qa, x W_dkv, x W_kr, x W_lambda) and the row-wise
 // normalisation / RoPE / cache append / sigmoid step.
 gdla_status project_and_append(const LayerDims &d, DT dt, const gdla_weights *w, const void *x,
-                               int32_t M, int32_t T, const int32_t *pos_dev, void *cache,
-                               int32_t max_len, float *aq, float *ckv, float *krp, float *laml,
+                               int32_t M, int32_t T, const int32_t *pos_dev, const CacheRef &cache,
+                               float *aq, float *ckv, float *krp, float *laml,
                                void *cq, float *lam, const float *lam_override, hipStream_t s,
                                StageEvents &se, bool cq_f16 = false, const NtWeights *nt = nullptr,
                                void *partial = nullptr, size_t partial_bytes = 0) {
@@ -305,7 +332,7 @@ gdla_status project_and_append(const LayerDims &d, DT dt, const gdla_weights *w,
   PrepArgs a{};
   a.aq = aq; a.ckv = ckv; a.kr = krp; a.lam_logit = laml; a.lam_override = lam_override;
   a.gamma_q = w->gamma_q; a.gamma_kv = w->gamma_kv; a.cq = cq; a.lam = lam; a.cache = cache;
-  a.pos = pos_dev; a.M = M; a.T = T; a.max_len = max_len; a.cq_f16 = cq_f16 ? 1 : 0;
+  a.pos = pos_dev; a.M = M; a.T = T; a.cq_f16 = cq_f16 ? 1 : 0;
   se.begin(GDLA_STAGE_NORM_APPEND);
   HIP_TRY(launch_prep(a, d, dt, s));
   se.end(GDLA_STAGE_NORM_APPEND);
@@ -367,17 +394,39 @@ GDLA_EXPORT size_t gdla_workspace_bytes(const gdla_dims *dims, int32_t op, int32
     case GDLA_OP_PREFILL: return plan_prefill(d, dims->dtype, B, T, pos_host, max_len).total;
     case GDLA_OP_DECODE: return plan_decode(d, dims->dtype, B, T, max_len).total;
     case GDLA_OP_APPEND: return plan_append(d, B, T).total;
+    case GDLA_OP_PREFILL_PAGED: return plan_prefill_paged(d, dims->dtype, B, T, pos_host, max_len).total;
     default: return 0;
   }
 }
 
-GDLA_EXPORT gdla_status gdla_latent_append(const gdla_dims *dims, const gdla_weights *w,
-                                           const void *x, int32_t B, int32_t T,
-                                           const int32_t *pos_host, void *cache, int32_t max_len,
-                                           void *ws, size_t ws_bytes, hipStream_t stream) {
-  g_err[0] = 0;
+namespace {
+
+// Validates a paged cache and describes it for the kernels.
+gdla_status paged_ref(const gdla_paged_cache *pc, CacheRef &c) {
+  if (!pc) return fail(GDLA_ERR_INVALID_ARG, "paged cache is NULL");
+  if (pc->page_rows <= 0 || pc->page_rows % 32 != 0)
+    return fail(GDLA_ERR_INVALID_ARG, "page_rows = %d must be a positive multiple of 32", pc->page_rows);
+  if (pc->n_pages <= 0 || pc->max_blocks <= 0)
+    return fail(GDLA_ERR_INVALID_ARG, "n_pages and max_blocks must be positive");
+  if ((int64_t)pc->max_blocks * pc->page_rows > INT32_MAX)
+    return fail(GDLA_ERR_INVALID_ARG, "max_blocks * page_rows exceeds the int32 position range");
+  if (!pc->pages || !pc->block_table) return fail(GDLA_ERR_INVALID_ARG, "pages or block_table is NULL");
+  if (((uintptr_t)pc->block_table & 3u) != 0) return fail(GDLA_ERR_INVALID_ARG, "block_table must be 4-byte aligned");
+  c = CacheRef{};
+  c.base = pc->pages;
+  c.block_table = pc->block_table;
+  c.max_len = pc->max_blocks * pc->page_rows;
+  c.page_rows = pc->page_rows;
+  c.max_blocks = pc->max_blocks;
+  c.n_pages = pc->n_pages;
+  return GDLA_OK;
+}
+
+gdla_status append_impl(const gdla_dims *dims, const gdla_weights *w, const void *x, int32_t B, int32_t T,
+                        const int32_t *pos_host, const CacheRef &cache, void *ws, size_t ws_bytes,
+                        hipStream_t stream) {
   LayerDims d;
-  gdla_status st = check_call(dims, w, x, B, T, pos_host, cache, max_len, nullptr, false, d);
+  gdla_status st = check_call(dims, w, x, B, T, pos_host, cache.base, cache.max_len, nullptr, false, d);
   if (st != GDLA_OK || B == 0 || T == 0) return st;
   const AppendLayout L = plan_append(d, B, T);
   if ((st = check_ws(ws, ws_bytes, L.total)) != GDLA_OK) return st;
@@ -385,16 +434,36 @@ GDLA_EXPORT gdla_status gdla_latent_append(const gdla_dims *dims, const gdla_wei
   int32_t *pos_dev = at<int32_t>(ws, L.pos);
   HIP_TRY(launch_set_i32(pos_dev, pos_host, B, stream));
   StageEvents se;
-  return project_and_append(d, dt, w, x, B * T, T, pos_dev, cache, max_len, nullptr,
-                            at<float>(ws, L.ckv), at<float>(ws, L.krp), nullptr, nullptr, nullptr,
-                            nullptr, stream, se);
+  return project_and_append(d, dt, w, x, B * T, T, pos_dev, cache, nullptr, at<float>(ws, L.ckv),
+                            at<float>(ws, L.krp), nullptr, nullptr, nullptr, nullptr, stream, se);
 }
 
-GDLA_EXPORT gdla_status gdla_prefill(const gdla_dims *dims, const gdla_weights *w, const void *x,
-                                     int32_t B, int32_t T, const int32_t *pos_host, void *cache,
-                                     int32_t max_len, void *out, void *ws, size_t ws_bytes,
-                                     const gdla_debug *dbg, hipStream_t stream) {
+}  // namespace
+
+GDLA_EXPORT gdla_status gdla_latent_append(const gdla_dims *dims, const gdla_weights *w,
+                                           const void *x, int32_t B, int32_t T,
+                                           const int32_t *pos_host, void *cache, int32_t max_len,
+                                           void *ws, size_t ws_bytes, hipStream_t stream) {
   g_err[0] = 0;
+  return append_impl(dims, w, x, B, T, pos_host, contiguous_cache(cache, max_len), ws, ws_bytes, stream);
+}
+
+GDLA_EXPORT gdla_status gdla_latent_append_paged(const gdla_dims *dims, const gdla_weights *w, const void *x,
+                                                 int32_t B, int32_t T, const int32_t *pos_host,
+                                                 const gdla_paged_cache *cache, void *ws, size_t ws_bytes,
+                                                 hipStream_t stream) {
+  g_err[0] = 0;
+  CacheRef c;
+  const gdla_status st = paged_ref(cache, c);
+  if (st != GDLA_OK) return st;
+  return append_impl(dims, w, x, B, T, pos_host, c, ws, ws_bytes, stream);
+}
+
+namespace {
+
+gdla_status prefill_impl(const gdla_dims *dims, const gdla_weights *w, const void *x, int32_t B, int32_t T,
+                         const int32_t *pos_host, void *cache, int32_t max_len, void *out, void *ws,
+                         size_t ws_bytes, const gdla_debug *dbg, hipStream_t stream) {
   LayerDims d;
   gdla_status st = check_call(dims, w, x, B, T, pos_host, cache, max_len, out, true, d);
   if (st != GDLA_OK || B == 0 || T == 0) return st;
@@ -435,7 +504,7 @@ GDLA_EXPORT gdla_status gdla_prefill(const gdla_dims *dims, const gdla_weights *
            at<void>(ws, L.wt_uv), at<void>(ws, L.wt_o)};
   }
   // Eq.(1), (3), (4), (7) and the cache append of this chunk's rows.
-  st = project_and_append(d, dt, w, x, M, T, pos_dev, cache, max_len, at<float>(ws, L.aq),
+  st = project_and_append(d, dt, w, x, M, T, pos_dev, contiguous_cache(cache, max_len), at<float>(ws, L.aq),
                           at<float>(ws, L.ckv), at<float>(ws, L.krp), at<float>(ws, L.laml),
                           at<void>(ws, L.cq), at<float>(ws, L.lam), lam_override, stream, se,
                           L.use_fast, L.use_nt ? &ntw : nullptr);
@@ -533,18 +602,53 @@ GDLA_EXPORT gdla_status gdla_prefill(const gdla_dims *dims, const gdla_weights *
   return GDLA_OK;
 }
 
+}  // namespace
+
+GDLA_EXPORT gdla_status gdla_prefill(const gdla_dims *dims, const gdla_weights *w, const void *x,
+                                     int32_t B, int32_t T, const int32_t *pos_host, void *cache,
+                                     int32_t max_len, void *out, void *ws, size_t ws_bytes,
+                                     const gdla_debug *dbg, hipStream_t stream) {
+  g_err[0] = 0;
+  return prefill_impl(dims, w, x, B, T, pos_host, cache, max_len, out, ws, ws_bytes, dbg, stream);
+}
+
+GDLA_EXPORT gdla_status gdla_prefill_paged(const gdla_dims *dims, const gdla_weights *w, const void *x,
+                                           int32_t B, int32_t T, const int32_t *pos_host,
+                                           const gdla_paged_cache *cache, void *out, void *ws, size_t ws_bytes,
+                                           const gdla_debug *dbg, hipStream_t stream) {
+  g_err[0] = 0;
+  CacheRef pc;
+  gdla_status st = paged_ref(cache, pc);
+  if (st != GDLA_OK) return st;
+  LayerDims d;
+  st = check_call(dims, w, x, B, T, pos_host, pc.base, pc.max_len, out, true, d);
+  if (st != GDLA_OK || B == 0 || T == 0) return st;
+  const PagedPrefillLayout L = plan_prefill_paged(d, dims->dtype, B, T, pos_host, pc.max_len);
+  if ((st = check_ws(ws, ws_bytes, L.total)) != GDLA_OK) return st;
+  const int64_t row_bytes = (int64_t)(d.d_c + d.d_r) * esize(dims->dtype);
+  int32_t *pos_dev = at<int32_t>(ws, L.pos);
+  const CacheRef stage = contiguous_cache(at<void>(ws, L.stage), L.stage_len);
+  HIP_TRY(launch_set_i32(pos_dev, pos_host, B, stream));
+  // visible rows before the chunk -> staging; the chunk as a contiguous prefill there (which
+  // appends its rows to the staging cache); its new rows -> their pages
+  HIP_TRY(launch_copy_cache_rows(pc, stage, pos_dev, B, L.max_gather, false, T, d.window, row_bytes, stream));
+  st = prefill_impl(dims, w, x, B, T, pos_host, stage.base, L.stage_len, out, ws, L.pre.total, dbg, stream);
+  if (st != GDLA_OK) return st;
+  HIP_TRY(launch_copy_cache_rows(stage, pc, pos_dev, B, T, true, T, d.window, row_bytes, stream));
+  return GDLA_OK;
+}
+
 namespace gdla {
 namespace {
 
 // Absorbed decode of T new tokens per sequence (row m = b T + i: token i of sequence b).
 gdla_status decode_impl(const gdla_dims *dims, const gdla_weights *w, const void *x, int32_t B, int32_t T,
-                        const int32_t *pos_host, void *cache, int32_t max_len, void *out, void *ws,
+                        const int32_t *pos_host, const CacheRef &cache, void *out, void *ws,
                         size_t ws_bytes, const gdla_debug *dbg, hipStream_t stream) {
-  g_err[0] = 0;
   LayerDims d;
-  gdla_status st = check_call(dims, w, x, B, T, pos_host, cache, max_len, out, true, d);
+  gdla_status st = check_call(dims, w, x, B, T, pos_host, cache.base, cache.max_len, out, true, d);
   if (st != GDLA_OK || B == 0 || T == 0) return st;
-  const DecodeLayout L = plan_decode(d, dims->dtype, B, T, max_len);
+  const DecodeLayout L = plan_decode(d, dims->dtype, B, T, cache.max_len);
   if ((st = check_ws(ws, ws_bytes, L.total)) != GDLA_OK) return st;
   const DT dt = dims->dtype == GDLA_F32 ? DT::F32 : DT::BF16;
   const int32_t M = B * T;
@@ -557,7 +661,7 @@ gdla_status decode_impl(const gdla_dims *dims, const gdla_weights *w, const void
   int32_t *pos_dev = at<int32_t>(ws, L.pos);
   HIP_TRY(launch_set_i32(pos_dev, pos_host, B, stream));
   void *partial = at<void>(ws, L.skinny);
-  st = project_and_append(d, dt, w, x, M, T, pos_dev, cache, max_len, at<float>(ws, L.aq),
+  st = project_and_append(d, dt, w, x, M, T, pos_dev, cache, at<float>(ws, L.aq),
                           at<float>(ws, L.ckv), at<float>(ws, L.krp), at<float>(ws, L.laml),
                           at<void>(ws, L.cq), at<float>(ws, L.lam), lam_override, stream, se, false, nullptr,
                           partial, L.skinny_bytes);
@@ -576,7 +680,7 @@ gdla_status decode_impl(const gdla_dims *dims, const gdla_weights *w, const void
                             M, T, d.n_heads, d.d_r, pos_dev, d.theta, DT::F32, stream));
   if (L.use_fast) {
     // ends GDLA_STAGE_PROJ_Q after the absorbed query; leaves GDLA_STAGE_ATTN_SIGNAL open
-    st = run_fast_decode(d, w, B, T, pos_dev, cache, max_len, at<float>(ws, L.qc), at<float>(ws, L.qr),
+    st = run_fast_decode(d, w, B, T, pos_dev, cache, at<float>(ws, L.qc), at<float>(ws, L.qr),
                          at<float>(ws, L.heads), L.fast, ws, stream, se);
     if (st != GDLA_OK) return fail(st, "fast decode path failed: %s", hipGetErrorString(hipGetLastError()));
   } else {
@@ -585,7 +689,7 @@ gdla_status decode_impl(const gdla_dims *dims, const gdla_weights *w, const void
     HIP_TRY(launch_absorb_generic(at<float>(ws, L.qc), at<float>(ws, L.qr), w->w_uk, at<float>(ws, L.qabs),
                                   M, d, dt, stream));
     HIP_TRY(launch_latent_attention_generic(at<float>(ws, L.qabs), cache, at<float>(ws, L.o), pos_dev, B, T,
-                                            max_len, d, dt, stream));
+                                            d, dt, stream));
     se.end(GDLA_STAGE_ATTN_NOISE);
     se.begin(GDLA_STAGE_ATTN_SIGNAL);
     HIP_TRY(launch_unabsorb_generic(at<float>(ws, L.o), w->w_uv, at<float>(ws, L.heads), M, d, dt, stream));
@@ -613,16 +717,31 @@ GDLA_EXPORT gdla_status gdla_decode(const gdla_dims *dims, const gdla_weights *w
                                     int32_t B, const int32_t *pos_host, void *cache,
                                     int32_t max_len, void *out, void *ws, size_t ws_bytes,
                                     const gdla_debug *dbg, hipStream_t stream) {
-  return decode_impl(dims, w, x, B, 1, pos_host, cache, max_len, out, ws, ws_bytes, dbg, stream);
+  g_err[0] = 0;
+  return decode_impl(dims, w, x, B, 1, pos_host, contiguous_cache(cache, max_len), out, ws, ws_bytes, dbg,
+                     stream);
 }
 
 GDLA_EXPORT gdla_status gdla_decode_tokens(const gdla_dims *dims, const gdla_weights *w, const void *x,
                                            int32_t B, int32_t T, const int32_t *pos_host, void *cache,
                                            int32_t max_len, void *out, void *ws, size_t ws_bytes,
                                            const gdla_debug *dbg, hipStream_t stream) {
-  if (T < 0 || T > GDLA_MAX_DECODE_TOKENS) {
-    g_err[0] = 0;
+  g_err[0] = 0;
+  if (T < 0 || T > GDLA_MAX_DECODE_TOKENS)
     return fail(GDLA_ERR_INVALID_ARG, "T = %d outside 0 .. %d", T, GDLA_MAX_DECODE_TOKENS);
-  }
-  return decode_impl(dims, w, x, B, T, pos_host, cache, max_len, out, ws, ws_bytes, dbg, stream);
+  return decode_impl(dims, w, x, B, T, pos_host, contiguous_cache(cache, max_len), out, ws, ws_bytes, dbg,
+                     stream);
+}
+
+GDLA_EXPORT gdla_status gdla_decode_paged(const gdla_dims *dims, const gdla_weights *w, const void *x,
+                                          int32_t B, int32_t T, const int32_t *pos_host,
+                                          const gdla_paged_cache *cache, void *out, void *ws, size_t ws_bytes,
+                                          const gdla_debug *dbg, hipStream_t stream) {
+  g_err[0] = 0;
+  if (T < 0 || T > GDLA_MAX_DECODE_TOKENS)
+    return fail(GDLA_ERR_INVALID_ARG, "T = %d outside 0 .. %d", T, GDLA_MAX_DECODE_TOKENS);
+  CacheRef c;
+  const gdla_status st = paged_ref(cache, c);
+  if (st != GDLA_OK) return st;
+  return decode_impl(dims, w, x, B, T, pos_host, c, out, ws, ws_bytes, dbg, stream);
 }

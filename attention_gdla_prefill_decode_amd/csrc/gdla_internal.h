@@ -60,6 +60,31 @@ struct LayerDims {
   float eps, theta, scale;
 };
 
+// Where the latent cache keeps row `pos` of sequence b.  Contiguous (page_rows == 0): row
+// b max_len + pos of [B, max_len, d_c + d_r].  Paged: row pos % page_rows of physical page
+// block_table[b max_blocks + pos / page_rows] of [n_pages, page_rows, d_c + d_r]; a table entry
+// outside [0, n_pages) is clamped into it, so a bad table gives wrong rows, never a fault.
+struct CacheRef {
+  void *base;
+  const int32_t *block_table;  // device [B, max_blocks] (paged only)
+  int32_t max_len;             // positions per sequence (paged: max_blocks * page_rows)
+  int32_t page_rows, max_blocks, n_pages;
+};
+
+__host__ __device__ inline int64_t cache_row(const CacheRef &c, int b, int pos) {
+  if (c.page_rows == 0) return (int64_t)b * c.max_len + pos;
+  int pg = c.block_table[(int64_t)b * c.max_blocks + pos / c.page_rows];
+  pg = pg < 0 ? 0 : (pg >= c.n_pages ? c.n_pages - 1 : pg);
+  return (int64_t)pg * c.page_rows + pos % c.page_rows;
+}
+
+inline CacheRef contiguous_cache(void *base, int32_t max_len) {
+  CacheRef c{};
+  c.base = base;
+  c.max_len = max_len;
+  return c;
+}
+
 __host__ __device__ inline int kv_head_of(int h, int n_signal, int n_kv) {
   return h < n_signal ? (h % n_kv) : ((h - n_signal) % n_kv);
 }
@@ -100,9 +125,9 @@ struct PrepArgs {
   const void *gamma_q, *gamma_kv;
   void *cq;               // [M, d_cq] in the input dtype, or fp16 when cq_f16
   float *lam;             // [M, n_S]
-  void *cache;            // [B, max_len, d_c + d_r]
+  CacheRef cache;
   const int32_t *pos;     // [B] device
-  int32_t M, T, max_len;
+  int32_t M, T;
   int32_t cq_f16;
 };
 hipError_t launch_prep(const PrepArgs &a, const LayerDims &d, DT dt, hipStream_t s);
@@ -137,14 +162,19 @@ hipError_t launch_absorb_generic(const float *qc, const float *qr, const void *w
                                  int32_t B, const LayerDims &d, DT dt, hipStream_t s);
 //   o[v, h] = sum_s softmax_s(tau qabs[v, h] . cache[b, s]) cache[b, s, 0:d_c]   (fp32), s over the
 //   visible keys of position pos[b] + i
-hipError_t launch_latent_attention_generic(const float *qabs, const void *cache, float *o,
+hipError_t launch_latent_attention_generic(const float *qabs, const CacheRef &cache, float *o,
                                            const int32_t *pos, int32_t B, int32_t q_len,
-                                           int32_t max_len, const LayerDims &d, DT dt,
-                                           hipStream_t s);
+                                           const LayerDims &d, DT dt, hipStream_t s);
 //   heads[b, h] = o[b, h] W_uv[:, kv(h)]   (fp32 [B, n_H, d_h])
 hipError_t launch_unabsorb_generic(const float *o, const void *w_uv, float *heads, int32_t B,
                                    const LayerDims &d, DT dt, hipStream_t s);
 
+// Cache rows of every sequence b from src to dst (either may be paged): the visible keys before
+// the new tokens [lo(pos_b), pos_b) (scatter = false; lo from the window), or the new rows
+// [pos_b, pos_b + T) (scatter = true).  max_rows bounds the rows of any sequence.
+hipError_t launch_copy_cache_rows(const CacheRef &src, const CacheRef &dst, const int32_t *pos_dev, int32_t B,
+                                  int32_t max_rows, bool scatter, int32_t T, int32_t window, int64_t row_bytes,
+                                  hipStream_t s);
 // Copies up to 128 host values into a device int32 array through kernel arguments, so that no
 // host-to-device copy (and no pinned host buffer) is needed.
 hipError_t launch_set_i32(int32_t *dst, const int32_t *src_host, int32_t n, hipStream_t s);

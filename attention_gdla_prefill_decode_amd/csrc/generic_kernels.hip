@@ -152,7 +152,7 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs a, LayerDims d) {
       else st<T>((T *)a.cq, (int64_t)m * d.d_cq + j, v);
     }
   }
-  T *crow = (T *)a.cache + ((int64_t)b * a.max_len + p) * (d.d_c + d.d_r);
+  T *crow = (T *)a.cache.base + cache_row(a.cache, b, p) * (d.d_c + d.d_r);
   {
     const float *row = a.ckv + (int64_t)m * d.d_c;
     float ss = 0.f;
@@ -359,10 +359,9 @@ hipError_t launch_absorb_generic(const float *qc, const float *qr, const void *w
 constexpr int kMaxLatentChunks = 16;  // d_c + d_r <= 1024
 
 template <typename T>
-__global__ void __launch_bounds__(256) latent_attention_kernel(const float *qabs, const T *cache,
+__global__ void __launch_bounds__(256) latent_attention_kernel(const float *qabs, CacheRef cache,
                                                                float *o, const int32_t *pos,
-                                                               int32_t B, int32_t q_len,
-                                                               int32_t max_len, LayerDims d) {
+                                                               int32_t B, int32_t q_len, LayerDims d) {
   const int lane = threadIdx.x & 63;
   const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b q_len + i) n_H + h
   if (wid >= (int64_t)B * q_len * d.n_heads) return;
@@ -371,7 +370,7 @@ __global__ void __launch_bounds__(256) latent_attention_kernel(const float *qabs
   const int p = pos[b] + v % q_len;
   const int lo = d.window > 0 ? max(0, p - d.window + 1) : 0;
   const float *q = qabs + wid * row;
-  const T *c = cache + (int64_t)b * max_len * row;
+  const T *c = (const T *)cache.base;
   float qv[kMaxLatentChunks], acc[kMaxLatentChunks];
 #pragma unroll
   for (int i = 0; i < kMaxLatentChunks; ++i) {
@@ -381,7 +380,7 @@ __global__ void __launch_bounds__(256) latent_attention_kernel(const float *qabs
   }
   float mx = -INFINITY, l = 0.f;
   for (int s = lo; s <= p; ++s) {
-    const T *cr = c + (int64_t)s * row;
+    const T *cr = c + cache_row(cache, b, s) * row;
     float dot = 0.f;
 #pragma unroll
     for (int i = 0; i < kMaxLatentChunks; ++i) {
@@ -407,19 +406,18 @@ __global__ void __launch_bounds__(256) latent_attention_kernel(const float *qabs
   }
 }
 
-hipError_t launch_latent_attention_generic(const float *qabs, const void *cache, float *o,
+hipError_t launch_latent_attention_generic(const float *qabs, const CacheRef &cache, float *o,
                                            const int32_t *pos, int32_t B, int32_t q_len,
-                                           int32_t max_len, const LayerDims &d, DT dt,
-                                           hipStream_t s) {
+                                           const LayerDims &d, DT dt, hipStream_t s) {
   const int64_t waves = (int64_t)B * q_len * d.n_heads;
   if (waves == 0) return hipSuccess;
   const dim3 grid((unsigned)((waves + 3) / 4));
   if (dt == DT::F32)
-    hipLaunchKernelGGL(latent_attention_kernel<float>, grid, dim3(256), 0, s, qabs,
-                       (const float *)cache, o, pos, B, q_len, max_len, d);
+    hipLaunchKernelGGL(latent_attention_kernel<float>, grid, dim3(256), 0, s, qabs, cache, o, pos, B,
+                       q_len, d);
   else
-    hipLaunchKernelGGL(latent_attention_kernel<bf16_t>, grid, dim3(256), 0, s, qabs,
-                       (const bf16_t *)cache, o, pos, B, q_len, max_len, d);
+    hipLaunchKernelGGL(latent_attention_kernel<bf16_t>, grid, dim3(256), 0, s, qabs, cache, o, pos, B,
+                       q_len, d);
   return hipGetLastError();
 }
 
@@ -489,6 +487,42 @@ hipError_t launch_copy_rows_f32(const float *src, int64_t src_ld, float *dst, in
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(copy_rows_f32_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 65536)),
                      dim3(256), 0, s, src, src_ld, dst, dst_ld, rows, cols);
+  return hipGetLastError();
+}
+
+// Rows of every sequence b copied between two caches (either may be paged): scatter = false
+// copies the visible keys before the new tokens, [lo(pos_b), pos_b), with lo = pos_b - window + 1
+// (at least 0) for a windowed layer and 0 otherwise; scatter = true copies the new rows
+// [pos_b, pos_b + T).  Block (x, b) takes 16 rows; U is the copy unit (16, 4 or 2 bytes).
+template <typename U>
+__global__ void __launch_bounds__(256) copy_cache_rows_kernel(CacheRef src, CacheRef dst, const int32_t *pos,
+                                                              int32_t scatter, int32_t T, int32_t window,
+                                                              int32_t row_units) {
+  const int b = blockIdx.y, p = pos[b];
+  const int lo = scatter ? p : (window > 0 ? max(0, p - window + 1) : 0);
+  const int hi = scatter ? p + T : p;
+  const int r0 = lo + (int)blockIdx.x * 16;
+  const int nr = min(16, hi - r0);
+  for (int i = threadIdx.x; i < nr * row_units; i += 256) {
+    const int r = r0 + i / row_units, u = i % row_units;
+    ((U *)dst.base)[cache_row(dst, b, r) * row_units + u] = ((const U *)src.base)[cache_row(src, b, r) * row_units + u];
+  }
+}
+
+hipError_t launch_copy_cache_rows(const CacheRef &src, const CacheRef &dst, const int32_t *pos_dev, int32_t B,
+                                  int32_t max_rows, bool scatter, int32_t T, int32_t window, int64_t row_bytes,
+                                  hipStream_t s) {
+  if (B == 0 || max_rows <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((max_rows + 15) / 16), (unsigned)B);
+  if (row_bytes % 16 == 0)
+    hipLaunchKernelGGL(copy_cache_rows_kernel<uint4>, grid, dim3(256), 0, s, src, dst, pos_dev, scatter ? 1 : 0, T,
+                       window, (int32_t)(row_bytes / 16));
+  else if (row_bytes % 4 == 0)
+    hipLaunchKernelGGL(copy_cache_rows_kernel<uint32_t>, grid, dim3(256), 0, s, src, dst, pos_dev, scatter ? 1 : 0,
+                       T, window, (int32_t)(row_bytes / 4));
+  else
+    hipLaunchKernelGGL(copy_cache_rows_kernel<uint16_t>, grid, dim3(256), 0, s, src, dst, pos_dev, scatter ? 1 : 0,
+                       T, window, (int32_t)(row_bytes / 2));
   return hipGetLastError();
 }
 

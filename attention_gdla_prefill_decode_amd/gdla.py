@@ -16,13 +16,14 @@ LIB_PATH = os.path.join(_PKG, "libgdla.so")
 GDLA_OK, GDLA_ERR_INVALID_ARG, GDLA_ERR_UNSUPPORTED, GDLA_ERR_WORKSPACE, GDLA_ERR_OUT_OF_RANGE, \
     GDLA_ERR_HIP = range(6)
 GDLA_F32, GDLA_BF16 = 0, 1
-GDLA_OP_PREFILL, GDLA_OP_DECODE, GDLA_OP_APPEND = 0, 1, 2
+GDLA_OP_PREFILL, GDLA_OP_DECODE, GDLA_OP_APPEND, GDLA_OP_PREFILL_PAGED = 0, 1, 2, 3
 
 WEIGHT_FIELDS = ("w_qa", "gamma_q", "w_qc", "w_qr", "w_dkv", "w_kr", "gamma_kv", "w_uk", "w_uv",
                  "w_lambda", "w_gate", "w_o")
 
 EXPORTED = ("gdla_workspace_bytes", "gdla_latent_append", "gdla_prefill", "gdla_decode",
-            "gdla_decode_tokens", "gdla_status_string", "gdla_last_error")
+            "gdla_decode_tokens", "gdla_latent_append_paged", "gdla_prefill_paged",
+            "gdla_decode_paged", "gdla_status_string", "gdla_last_error")
 
 MAX_DECODE_TOKENS = 16  # GDLA_MAX_DECODE_TOKENS
 
@@ -39,6 +40,12 @@ class GdlaDims(ctypes.Structure):
 
 class GdlaWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_FIELDS]
+
+
+class GdlaPagedCache(ctypes.Structure):
+    _fields_ = [("pages", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("n_pages", ctypes.c_int32), ("page_rows", ctypes.c_int32),
+                ("max_blocks", ctypes.c_int32)]
 
 
 class GdlaDebug(ctypes.Structure):
@@ -127,6 +134,17 @@ def lib():
                                          ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_size_t, P(GdlaDebug), ctypes.c_void_p]
+        L.gdla_latent_append_paged.restype = ctypes.c_int
+        L.gdla_latent_append_paged.argtypes = [P(GdlaDims), P(GdlaWeights), ctypes.c_void_p,
+                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                               P(GdlaPagedCache), ctypes.c_void_p, ctypes.c_size_t,
+                                               ctypes.c_void_p]
+        for name in ("gdla_prefill_paged", "gdla_decode_paged"):
+            f = getattr(L, name)
+            f.restype = ctypes.c_int
+            f.argtypes = [P(GdlaDims), P(GdlaWeights), ctypes.c_void_p, ctypes.c_int32,
+                          ctypes.c_int32, ctypes.c_void_p, P(GdlaPagedCache), ctypes.c_void_p,
+                          ctypes.c_void_p, ctypes.c_size_t, P(GdlaDebug), ctypes.c_void_p]
         L.gdla_status_string.restype = ctypes.c_char_p
         L.gdla_status_string.argtypes = [ctypes.c_int]
         L.gdla_last_error.restype = ctypes.c_char_p
@@ -249,4 +267,58 @@ def gdla_decode_tokens(dims, weights, x, pos, cache, out=None, ws=None, lambda_o
                                     _pos_array(pos), _ptr(cache), max_len, _ptr(out), _ptr(ws),
                                     nbytes, None if dbg is None else ctypes.byref(dbg),
                                     _stream(stream)))
+    return out
+
+
+class PagedCache:
+    """A paged latent cache: `pages` [n_pages, page_rows, d_kv_latent + d_rope] and `block_table`
+    [B, max_blocks] int32 (both device tensors, owned by the caller)."""
+
+    def __init__(self, pages, block_table):
+        assert block_table.dtype == torch.int32 and block_table.dim() == 2
+        self.pages, self.block_table = pages, block_table
+        self.struct = GdlaPagedCache(pages.data_ptr(), block_table.data_ptr(), pages.shape[0],
+                                     pages.shape[1], block_table.shape[1])
+
+    @property
+    def max_len(self):
+        return self.struct.max_blocks * self.struct.page_rows
+
+
+def gdla_latent_append_paged(dims, weights, x, pos, cache, ws=None, stream=None):
+    """gdla_latent_append into a PagedCache."""
+    B, T = x.shape[0], x.shape[1]
+    ws, nbytes = _workspace(dims, GDLA_OP_APPEND, B, T, pos, cache.max_len, ws, x.device)
+    _check(lib().gdla_latent_append_paged(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B, T,
+                                          _pos_array(pos), ctypes.byref(cache.struct), _ptr(ws),
+                                          nbytes, _stream(stream)))
+
+
+def gdla_prefill_paged(dims, weights, x, pos, cache, out=None, ws=None, lambda_override=None,
+                       out_heads=None, stream=None, timer=None):
+    """gdla_prefill over a PagedCache: x [B, T, d_model] -> out [B, T, d_model]."""
+    B, T = x.shape[0], x.shape[1]
+    if out is None:
+        out = torch.empty_like(x)
+    ws, nbytes = _workspace(dims, GDLA_OP_PREFILL_PAGED, B, T, pos, cache.max_len, ws, x.device)
+    dbg = _debug(lambda_override, out_heads, timer)
+    _check(lib().gdla_prefill_paged(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B, T,
+                                    _pos_array(pos), ctypes.byref(cache.struct), _ptr(out),
+                                    _ptr(ws), nbytes, None if dbg is None else ctypes.byref(dbg),
+                                    _stream(stream)))
+    return out
+
+
+def gdla_decode_paged(dims, weights, x, pos, cache, out=None, ws=None, lambda_override=None,
+                      out_heads=None, stream=None, timer=None):
+    """Multi-token decode over a PagedCache: x [B, T, d_model] -> out [B, T, d_model]."""
+    B, T = x.shape[0], x.shape[1]
+    if out is None:
+        out = torch.empty_like(x)
+    ws, nbytes = _workspace(dims, GDLA_OP_DECODE, B, T, pos, cache.max_len, ws, x.device)
+    dbg = _debug(lambda_override, out_heads, timer)
+    _check(lib().gdla_decode_paged(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B, T,
+                                   _pos_array(pos), ctypes.byref(cache.struct), _ptr(out), _ptr(ws),
+                                   nbytes, None if dbg is None else ctypes.byref(dbg),
+                                   _stream(stream)))
     return out

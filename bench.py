@@ -111,10 +111,25 @@ def cpu_baseline(rows=2048):
                       f"{flops / 1e12:.3f} TFLOP of algorithmic work"}
 
 
-def bench_decode(steps, warmup, tokens=1):
+def paged_copy(cache, page_rows, seed=0):
+    """The cache [B, L, row] in a pool of B L / page_rows pages in shuffled order (the block table
+    of a serving system after many allocations)."""
+    import torch
+    import attention_gdla_prefill_decode_amd as gd
+    B, L, row = cache.shape
+    blocks = L // page_rows
+    gen = torch.Generator().manual_seed(seed)
+    table = torch.randperm(B * blocks, generator=gen).to(torch.int32).reshape(B, blocks).to(cache.device)
+    pages = torch.empty((B * blocks, page_rows, row), dtype=cache.dtype, device=cache.device)
+    pages[table.reshape(-1).long()] = cache.reshape(B * blocks, page_rows, row)
+    return gd.PagedCache(pages, table.contiguous())
+
+
+def bench_decode(steps, warmup, tokens=1, page_rows=0):
     """64 sequences with a 65536-position context.  tokens = 1: one decode step (gdla_decode, the
     new token at position 65535); tokens = T > 1: T draft tokens per sequence at positions
-    65536 - T .. 65535 in one gdla_decode_tokens call."""
+    65536 - T .. 65535 in one gdla_decode_tokens call.  page_rows > 0: the same over a paged
+    cache (gdla_decode_paged, shuffled pages of page_rows rows)."""
     import torch
     import synth
     import attention_gdla_prefill_decode_amd as gd
@@ -123,7 +138,13 @@ def bench_decode(steps, warmup, tokens=1):
     w = gd.make_weights(inp["weights"])
     dims = gd.make_dims(cfg)
     pos = inp["p0"]
-    if tokens == 1:
+    cache = inp["cache"]
+    if page_rows > 0:
+        x = inp["x"]
+        cache = paged_copy(inp["cache"], page_rows)
+        del inp["cache"]
+        run = gd.gdla_decode_paged
+    elif tokens == 1:
         x = inp["x"][:, 0].contiguous()
         run = gd.gdla_decode
     else:
@@ -134,12 +155,12 @@ def bench_decode(steps, warmup, tokens=1):
     out = torch.empty_like(x)
     timers = [gd.StageTimer() for _ in range(steps)]
     for _ in range(warmup):
-        run(dims, w, x, pos, inp["cache"], out=out, ws=ws)
+        run(dims, w, x, pos, cache, out=out, ws=ws)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(steps):
-        run(dims, w, x, pos, inp["cache"], out=out, ws=ws, timer=timers[i])
+        run(dims, w, x, pos, cache, out=out, ws=ws, timer=timers[i])
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
@@ -170,6 +191,8 @@ def bench_decode(steps, warmup, tokens=1):
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4)}
     name = "decode_64x64k" if tokens == 1 else f"decode_tokens_64x64k_t{tokens}"
+    if page_rows > 0:
+        name += f"_paged{page_rows}"
     return {"workload": name, "batch": len(pos), "tokens": tokens, "context": int(last[0]) + 1,
             "ms_per_step": round(ms, 4),
             "latent_GBps_whole_step": round(nbytes / ms / 1e6, 1),
@@ -196,6 +219,9 @@ def main():
     ap.add_argument("--tokens", type=int, default=1,
                     help="with --workload decode_64x64k or --decode-only: draft tokens per sequence "
                          "(T > 1 times gdla_decode_tokens, the multi-token verification step)")
+    ap.add_argument("--page-rows", type=int, default=0,
+                    help="with the decode workload: run over a paged cache of this page size "
+                         "(gdla_decode_paged)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 1 GiB device to device three times (a known-size reference "
@@ -221,11 +247,11 @@ def main():
         return
 
     if args.decode_only:
-        print(json.dumps(bench_decode(args.steps, args.warmup, args.tokens)), flush=True)
+        print(json.dumps(bench_decode(args.steps, args.warmup, args.tokens, args.page_rows)), flush=True)
         return
 
     if args.workload == "decode_64x64k":
-        d = bench_decode(args.steps, args.warmup, args.tokens)
+        d = bench_decode(args.steps, args.warmup, args.tokens, args.page_rows)
         result = {
             "metric": METRIC, "value": round(d["latent_GBps_whole_step"], 1), "unit": "GB/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": d["ms_per_step"],

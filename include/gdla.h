@@ -66,7 +66,12 @@ typedef enum {
 
 typedef enum { GDLA_F32 = 0, GDLA_BF16 = 1 } gdla_dtype;
 
-typedef enum { GDLA_OP_PREFILL = 0, GDLA_OP_DECODE = 1, GDLA_OP_APPEND = 2 } gdla_op;
+typedef enum {
+  GDLA_OP_PREFILL = 0,
+  GDLA_OP_DECODE = 1,        /* gdla_decode, gdla_decode_tokens and gdla_decode_paged */
+  GDLA_OP_APPEND = 2,        /* gdla_latent_append and gdla_latent_append_paged */
+  GDLA_OP_PREFILL_PAGED = 3  /* gdla_prefill_paged (max_len = max_blocks * page_rows) */
+} gdla_op;
 
 /* Most new tokens per sequence that gdla_decode_tokens takes in one call. */
 #define GDLA_MAX_DECODE_TOKENS 16
@@ -179,6 +184,49 @@ gdla_status gdla_decode_tokens(const gdla_dims *dims, const gdla_weights *w, con
                                int32_t B, int32_t T, const int32_t *pos_host, void *cache,
                                int32_t max_len, void *out, void *ws, size_t ws_bytes,
                                const gdla_debug *dbg, hipStream_t stream);
+
+/* Paged latent cache, for serving several sequences out of one pool of fixed-size pages (the
+ * multi-token decode path above is where serving systems use it).  Logical block j of sequence b
+ * (positions j * page_rows .. j * page_rows + page_rows - 1) lives in physical page
+ * block_table[b * max_blocks + j]; a page holds page_rows cache rows laid out as in the contiguous
+ * cache.  The caller owns the pages and the table and may map any page to any block (a sliding-
+ * window layer can recycle the pages of positions that have left the window).
+ *   - pages: device, [n_pages, page_rows, d_kv_latent + d_rope] in dims->dtype, 16-byte aligned.
+ *   - block_table: device int32 [B, max_blocks].  Every block that a call reads or writes (the
+ *     visible positions of every new token, and the new positions) must map to a page in
+ *     [0, n_pages); the kernels clamp other entries into that range (wrong rows, never a fault).
+ *   - page_rows: a positive multiple of 32.
+ * Positions run from 0 to max_blocks * page_rows - 1, which plays the role of max_len. */
+typedef struct {
+  void *pages;
+  const int32_t *block_table;
+  int32_t n_pages;
+  int32_t page_rows;
+  int32_t max_blocks;
+} gdla_paged_cache;
+
+/* gdla_latent_append over a paged cache. */
+gdla_status gdla_latent_append_paged(const gdla_dims *dims, const gdla_weights *w, const void *x,
+                                     int32_t B, int32_t T, const int32_t *pos_host,
+                                     const gdla_paged_cache *cache, void *ws, size_t ws_bytes,
+                                     hipStream_t stream);
+
+/* gdla_prefill over a paged cache: the visible rows of every sequence are gathered into the
+ * workspace, the chunk runs as gdla_prefill there, and its new rows are written back to their
+ * pages.  Workspace: gdla_workspace_bytes(dims, GDLA_OP_PREFILL_PAGED, B, T, pos_host,
+ * max_blocks * page_rows). */
+gdla_status gdla_prefill_paged(const gdla_dims *dims, const gdla_weights *w, const void *x,
+                               int32_t B, int32_t T, const int32_t *pos_host,
+                               const gdla_paged_cache *cache, void *out, void *ws, size_t ws_bytes,
+                               const gdla_debug *dbg, hipStream_t stream);
+
+/* gdla_decode_tokens over a paged cache: x [B, T, d_model], 0 <= T <= GDLA_MAX_DECODE_TOKENS
+ * (T = 1 is one decode step).  The split-L kernel reads the cache in 32-row tiles, each inside
+ * one page.  Workspace: gdla_workspace_bytes(dims, GDLA_OP_DECODE, B, T, ...). */
+gdla_status gdla_decode_paged(const gdla_dims *dims, const gdla_weights *w, const void *x,
+                              int32_t B, int32_t T, const int32_t *pos_host,
+                              const gdla_paged_cache *cache, void *out, void *ws, size_t ws_bytes,
+                              const gdla_debug *dbg, hipStream_t stream);
 
 /* Static description of a status code. */
 const char *gdla_status_string(gdla_status s);

@@ -144,3 +144,26 @@ def check_rows(got, exp, dtype, what):
         bound = np.abs(exp) * 2.0 ** -7 + 1e-5
         bad = np.abs(got - exp) > bound
         assert not bad.any(), f"{what}: {int(bad.sum())} cache entries beyond one bf16 rounding"
+
+
+def to_pages(cache, page_rows, seed=0, spare=3):
+    """Copies a contiguous cache [B, L, row] into a shuffled pool of pages: returns a
+    gd.PagedCache whose block table maps every block of every sequence to a distinct page (plus
+    `spare` unused pages, so page indices are not dense)."""
+    B, L, row = cache.shape
+    blocks = (L + page_rows - 1) // page_rows
+    n_pages = B * blocks + spare
+    gen = torch.Generator().manual_seed(seed)
+    perm = torch.randperm(n_pages, generator=gen)[:B * blocks].to(torch.int32)
+    table = perm.reshape(B, blocks).contiguous()
+    pages = torch.zeros((n_pages, page_rows, row), dtype=cache.dtype, device=cache.device)
+    padded = torch.zeros((B, blocks * page_rows, row), dtype=cache.dtype, device=cache.device)
+    padded[:, :L] = cache
+    pages[table.reshape(-1).long().to(cache.device)] = padded.reshape(B * blocks, page_rows, row)
+    return gd.PagedCache(pages, table.to(cache.device))
+
+
+def from_pages(pc, B, L):
+    """The contiguous [B, L, row] view of a paged cache (a copy)."""
+    rows = pc.pages[pc.block_table.long()]  # [B, blocks, page_rows, row]
+    return rows.reshape(B, -1, pc.pages.shape[-1])[:, :L]

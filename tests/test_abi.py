@@ -193,3 +193,39 @@ def test_decode_tokens_argument_errors():
     # T = 0: nothing to do
     assert lib.gdla_decode_tokens(ctypes.byref(d), ctypes.byref(w), None, 2, 0, pos, None, 64, None,
                                   None, 0, None, None) == gb.GDLA_OK
+
+
+def test_paged_argument_errors():
+    lib = gd.lib()
+    d = big_dims()
+    w = gb.GdlaWeights(*([FAKE] * 12))
+    pos = (ctypes.c_int32 * 2)(5, 60)
+
+    def paged(page_rows=64, n_pages=8, max_blocks=2, pages=FAKE, table=FAKE):
+        return gb.GdlaPagedCache(pages, table, n_pages, page_rows, max_blocks)
+
+    def dec(pc, T=1, ws_bytes=1 << 40):
+        return lib.gdla_decode_paged(ctypes.byref(d), ctypes.byref(w), FAKE, 2, T, pos,
+                                     None if pc is None else ctypes.byref(pc), FAKE, FAKE, ws_bytes,
+                                     None, None)
+
+    assert dec(None) == gb.GDLA_ERR_INVALID_ARG
+    assert dec(paged(page_rows=48)) == gb.GDLA_ERR_INVALID_ARG      # not a multiple of 32
+    assert dec(paged(n_pages=0)) == gb.GDLA_ERR_INVALID_ARG
+    assert dec(paged(table=None)) == gb.GDLA_ERR_INVALID_ARG
+    assert dec(paged(table=FAKE + 2)) == gb.GDLA_ERR_INVALID_ARG    # misaligned block table
+    assert dec(paged(max_blocks=1), T=5) == gb.GDLA_ERR_OUT_OF_RANGE  # 60 + 5 > 1 * 64
+    assert dec(paged(), T=gd.MAX_DECODE_TOKENS + 1) == gb.GDLA_ERR_INVALID_ARG
+    assert dec(paged(), T=2, ws_bytes=16) == gb.GDLA_ERR_WORKSPACE
+    assert lib.gdla_last_error().decode()
+    pc = paged()
+    st = lib.gdla_prefill_paged(ctypes.byref(d), ctypes.byref(w), FAKE, 2, 8, pos, ctypes.byref(pc), FAKE,
+                                FAKE, 16, None, None)
+    assert st == gb.GDLA_ERR_WORKSPACE
+    st = lib.gdla_latent_append_paged(ctypes.byref(d), ctypes.byref(w), FAKE, 2, 70, pos, ctypes.byref(pc),
+                                      FAKE, 1 << 40, None)
+    assert st == gb.GDLA_ERR_OUT_OF_RANGE  # 60 + 70 > 2 * 64
+    # a paged prefill stages the visible rows: more workspace than the contiguous prefill
+    pre = gd.gdla_workspace_bytes(d, gd.GDLA_OP_PREFILL, 2, 8, [5, 60], 128)
+    prp = gd.gdla_workspace_bytes(d, gd.GDLA_OP_PREFILL_PAGED, 2, 8, [5, 60], 128)
+    assert prp >= pre + 2 * 68 * 576 * 2

@@ -207,6 +207,70 @@ def test_decode_tokens_matches_decode_and_prefill():
         H.check_rows(H.to_np(c4[bi, p:p + 4]), H.to_np(c3[bi, p:p + 4]), "bf16", "appended rows")
 
 
+# ---------------------------------------------------------------- paged latent cache
+# The same calls over a shuffled pool of pages: the kernels read and write exactly the rows of the
+# contiguous layout, so the outputs must equal the contiguous path's bit for bit (windowed decode
+# excepted: its paged tiles are aligned to the pages, so the sums run in another order), and the
+# rows written through the block table must land in the right pages.
+@pytest.mark.parametrize("cfg,T,p0,page_rows", [
+    (H.BF80, 1, [0, 700, 2047], 64),
+    (H.BF80, 4, [31, 1000, 2], 32),
+    (dict(H.BF80, window=1000), 3, [2500, 40, 998], 96),
+    (TINY, 2, [0, 50, 127], 32),
+])
+def test_paged_decode_matches_contiguous(cfg, T, p0, page_rows):
+    dt = cfg["dtype"]
+    inp = synth.make_inputs(cfg, "cpu", batch=len(p0), seq=T, p0=p0, random_gamma=True, seed=37)
+    dev = H.device_inputs(inp)
+    dims = gd.make_dims(cfg, window=cfg.get("window", 0))
+    B, L = dev["cache"].shape[0], dev["cache"].shape[1]
+    pc = H.to_pages(dev["cache"], page_rows, seed=5)
+    ref = gd.gdla_decode_tokens(dims, dev["wstruct"], dev["x"], inp["p0"], dev["cache"])
+    out = gd.gdla_decode_paged(dims, dev["wstruct"], dev["x"], inp["p0"], pc)
+    torch.cuda.synchronize()
+    if cfg.get("window", 0) == 0:
+        assert torch.equal(out, ref), "paged and contiguous decode must agree bit for bit"
+    else:  # paged tiles start on page boundaries, contiguous ones at the window start
+        H.check(H.to_np(out), H.to_np(ref), dt, "paged vs contiguous decode")
+    assert torch.equal(H.from_pages(pc, B, L), dev["cache"]), "appended rows must land in their pages"
+    # and against the oracle's one-call forward
+    r = H.prefill_case(cfg, T, p0, window=cfg.get("window", 0), seed=37, entry="decode_tokens")
+    _say(H.check(H.to_np(out), r["exp_out"], dt, f"paged decode {dt} T={T} page_rows={page_rows}"))
+
+
+@pytest.mark.parametrize("cfg,T,p0,window,page_rows", [
+    (BF, 100, [0, 150], 0, 32),
+    (BF, 64, [300, 7], 40, 64),
+    (TINY, 37, [0, 11], 0, 32),
+])
+def test_paged_prefill_matches_contiguous(cfg, T, p0, window, page_rows):
+    inp = synth.make_inputs(cfg, "cpu", batch=len(p0), seq=T, p0=p0, random_gamma=True, seed=41)
+    dev = H.device_inputs(inp)
+    dims = gd.make_dims(cfg, window=window)
+    B, L = dev["cache"].shape[0], dev["cache"].shape[1]
+    pc = H.to_pages(dev["cache"], page_rows, seed=9)
+    ref = gd.gdla_prefill(dims, dev["wstruct"], dev["x"], inp["p0"], dev["cache"])
+    out = gd.gdla_prefill_paged(dims, dev["wstruct"], dev["x"], inp["p0"], pc)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref), "paged and contiguous prefill must agree bit for bit"
+    assert torch.equal(H.from_pages(pc, B, L), dev["cache"])
+    r = H.prefill_case(cfg, T, p0, window=window, seed=41)
+    _say(H.check(H.to_np(out), r["exp_out"], cfg["dtype"], f"paged prefill T={T} W={window}"))
+
+
+def test_paged_append():
+    cfg = BF
+    inp = synth.make_inputs(cfg, "cpu", batch=3, seq=45, p0=[0, 20, 99], seed=43)
+    dev = H.device_inputs(inp)
+    dims = gd.make_dims(cfg)
+    B, L = dev["cache"].shape[0], dev["cache"].shape[1]
+    pc = H.to_pages(dev["cache"], 32, seed=11)
+    gd.gdla_latent_append(dims, dev["wstruct"], dev["x"], inp["p0"], dev["cache"])
+    gd.gdla_latent_append_paged(dims, dev["wstruct"], dev["x"], inp["p0"], pc)
+    torch.cuda.synchronize()
+    assert torch.equal(H.from_pages(pc, B, L), dev["cache"])
+
+
 def test_bf16_lambda_zero_is_gated_mla():
     r = H.prefill_case(BF, 96, [0, 20], window=32, lam_zero=True)
     inp = r["inp"]
