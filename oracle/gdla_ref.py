@@ -36,6 +36,9 @@ Where the pages are silent the oracle takes these readings (the GPU library take
   positions p = P0 + t.
 * Softmax scale 1/sqrt(d_head + d_rope); key s is visible from query p iff s <= p and, when a
   window W > 0 is set, p - s < W.
+* Packed documents (paperglide reader, Figure 4 (a): a training sequence holding 473 documents,
+  drawn on the QK^T score matrix): when a token's document start d(p) is given, key s is visible
+  from query p only if also s >= d(p), i.e. attention stays inside the document.
 * A cache row is [cbar^KV (after norm and gamma) ; k^R (after RoPE)].
 
 The softmax is evaluated exactly per row in two passes (max, then exp / sum); a matmul is used as
@@ -171,18 +174,23 @@ def expand_kv(c_bar, w, dims):
     return k_c, v
 
 
-def visible_mask(qpos, kpos, window):
-    """Key s is visible from query p iff s <= p and (window == 0 or p - s < window)."""
+def visible_mask(qpos, kpos, window, qdoc=None):
+    """Key s is visible from query p iff s <= p and (window == 0 or p - s < window) and, with
+    document starts qdoc, s >= qdoc[p's row]."""
     p = np.asarray(qpos)[:, None]
     s = np.asarray(kpos)[None, :]
     m = s <= p
     if window > 0:
         m &= (p - s) < window
+    if qdoc is not None:
+        m &= s >= np.asarray(qdoc)[:, None]
     return m
 
 
-def _key_range(qpos, window):
+def _key_range(qpos, window, qdoc=None):
     lo = 0 if window <= 0 else max(0, int(np.min(qpos)) - window + 1)
+    if qdoc is not None:
+        lo = max(lo, int(np.min(qdoc)))
     return lo, int(np.max(qpos)) + 1
 
 
@@ -197,11 +205,12 @@ def _softmax_rows(scores, mask):
     return p
 
 
-def attention_expanded(q_c, q_r, k_c, k_r, v, qpos, dims, block=256):
+def attention_expanded(q_c, q_r, k_c, k_r, v, qpos, dims, block=256, qdoc=None):
     """Per-head softmax attention over expanded keys [K^C ; k^R] and values V.
 
     q_c [T, n_H, d_h], q_r [T, n_H, d_R]; k_c, v [L, n_KV, d_h]; k_r [L, d_R] (shared by all
-    heads); qpos [T] absolute positions; keys are positions 0..L-1.  Returns H [T, n_H, d_h].
+    heads); qpos [T] absolute positions; qdoc [T] optional document starts; keys are positions
+    0..L-1.  Returns H [T, n_H, d_h].
     """
     q_c, q_r, k_c, k_r, v = map(_f64, (q_c, q_r, k_c, k_r, v))
     qpos = np.asarray(qpos)
@@ -210,8 +219,9 @@ def attention_expanded(q_c, q_r, k_c, k_r, v, qpos, dims, block=256):
     for t0 in range(0, t, block):
         t1 = min(t, t0 + block)
         p = qpos[t0:t1]
-        lo, hi = _key_range(p, dims.window)
-        mask = visible_mask(p, np.arange(lo, hi), dims.window)
+        qd = None if qdoc is None else np.asarray(qdoc)[t0:t1]
+        lo, hi = _key_range(p, dims.window, qd)
+        mask = visible_mask(p, np.arange(lo, hi), dims.window, qd)
         for h in range(dims.n_heads):
             j = kv_head_of(h, dims)
             s = dims.scale * (q_c[t0:t1, h] @ k_c[lo:hi, j].T + q_r[t0:t1, h] @ k_r[lo:hi].T)
@@ -219,7 +229,7 @@ def attention_expanded(q_c, q_r, k_c, k_r, v, qpos, dims, block=256):
     return out
 
 
-def attention_absorbed(q_c, q_r, c_bar, k_r, w, dims, qpos, block=256):
+def attention_absorbed(q_c, q_r, c_bar, k_r, w, dims, qpos, block=256, qdoc=None):
     """The same attention evaluated on the latent cache (the MLA 'reconstruct inside attention').
 
     q~ = q^C_h W_uk[:, j]^T scores against cbar directly, o = sum_s P_s cbar_s, H = o W_uv[:, j].
@@ -233,8 +243,9 @@ def attention_absorbed(q_c, q_r, c_bar, k_r, w, dims, qpos, block=256):
     for t0 in range(0, t, block):
         t1 = min(t, t0 + block)
         p = qpos[t0:t1]
-        lo, hi = _key_range(p, dims.window)
-        mask = visible_mask(p, np.arange(lo, hi), dims.window)
+        qd = None if qdoc is None else np.asarray(qdoc)[t0:t1]
+        lo, hi = _key_range(p, dims.window, qd)
+        mask = visible_mask(p, np.arange(lo, hi), dims.window, qd)
         for h in range(dims.n_heads):
             j = kv_head_of(h, dims)
             q_abs = q_c[t0:t1, h] @ w_uk[:, j * dh:(j + 1) * dh].T
@@ -263,12 +274,15 @@ def output_projection(y, w_o):
     return y.reshape(y.shape[0], -1) @ _f64(w_o)
 
 
-def gdla_forward(x, w, dims, prefix=None, p0=0, lam_override=None, form="expanded", rows=None):
+def gdla_forward(x, w, dims, prefix=None, p0=0, lam_override=None, form="expanded", rows=None,
+                 doc_start=None):
     """GDLA layer forward for one sequence: T new tokens at positions p0 .. p0+T-1.
 
     prefix: [p0, d_c + d_R] cache rows already present (None when p0 == 0).
     rows:   optional indices of the query rows to evaluate (all rows by default); the cache rows of
             all T tokens are always produced, since later rows attend to them.
+    doc_start: optional [T] position of the first token of each new token's document (packed
+            documents); attention then stays inside the document.
     Returns a dict with out [R, d_model], cache_rows [T, d_c + d_R], heads H [R, n_H, d_h],
     lam [R, n_S], and the intermediates of the R evaluated rows.
     """
@@ -291,12 +305,15 @@ def gdla_forward(x, w, dims, prefix=None, p0=0, lam_override=None, form="expande
         keys = cache_rows
     c_bar_all, k_r_all = keys[:, :d_c], keys[:, d_c:]
     qpos = pos[sel]
+    qdoc = None if doc_start is None else np.asarray(doc_start)[sel]
+    if qdoc is not None and np.any((qdoc < 0) | (qdoc > qpos)):
+        raise ValueError("a document must start at or before its token")
     hi = int(np.max(qpos)) + 1
     if form == "expanded":
         k_c, v = expand_kv(c_bar_all[:hi], w, dims)
-        heads = attention_expanded(q_c, q_r, k_c, k_r_all[:hi], v, qpos, dims)
+        heads = attention_expanded(q_c, q_r, k_c, k_r_all[:hi], v, qpos, dims, qdoc=qdoc)
     elif form == "absorbed":
-        heads = attention_absorbed(q_c, q_r, c_bar_all[:hi], k_r_all[:hi], w, dims, qpos)
+        heads = attention_absorbed(q_c, q_r, c_bar_all[:hi], k_r_all[:hi], w, dims, qpos, qdoc=qdoc)
     else:
         raise ValueError("form must be 'expanded' or 'absorbed'")
     d = differential_combine(heads, lam, dims)

@@ -48,8 +48,9 @@ def _sig(z):
 
 
 def brute_gdla(x, w, n_signal, n_noise, n_kv, d_head, d_rope, window=0, eps=1e-6,
-               theta=10000.0, prefix=None, p0=0, lam_override=None):
-    """Returns (out [T][d_model], heads [T][n_H][d_head]) as nested lists of mpf."""
+               theta=10000.0, prefix=None, p0=0, lam_override=None, doc_start=None):
+    """Returns (out [T][d_model], heads [T][n_H][d_head]) as nested lists of mpf.  doc_start[t]
+    (optional) is the first position of token t's document: keys before it are not visible."""
     n_heads = n_signal + n_noise
     g = n_signal // n_noise
     eps, theta = mpf(eps), mpf(theta)
@@ -88,7 +89,8 @@ def brute_gdla(x, w, n_signal, n_noise, n_kv, d_head, d_rope, window=0, eps=1e-6
     heads = []
     for t in range(T):
         p = p0 + t
-        vis = [s for s in range(L) if s <= p and (window == 0 or p - s < window)]
+        first = 0 if doc_start is None else doc_start[t]
+        vis = [s for s in range(L) if first <= s <= p and (window == 0 or p - s < window)]
         ht = []
         for h in range(n_heads):
             j = (h % n_kv) if h < n_signal else ((h - n_signal) % n_kv)

@@ -267,7 +267,56 @@ def pin_row_sums(ref):
     _close(h, np.ones_like(h), 1e-14, "row sums")
 
 
+def _doc_starts(lengths, first=0):
+    """Per-token document start for documents of the given lengths packed from position `first`."""
+    out, start = [], first
+    for n in lengths:
+        out += [start] * n
+        start += n
+    return np.array(out)
+
+
+def pin_documents_brute_force(ref):
+    """Packed documents: the layer equals the 50-digit brute force whose visible set also starts
+    at the token's document (tiny shapes; with a window; a document that began in the prefix)."""
+    cases = [  # (seq, p0, window, document lengths of the new tokens, first document start)
+        (6, 0, 0, (2, 3, 1), 0), (5, 3, 2, (2, 3), 1), (4, 2, 0, (3, 1), 0),
+    ]
+    for i, (t, p0, win, lens, first) in enumerate(cases):
+        cfg, w, x, prefix = small_problem(4, 3, 1, 1, d_model=6, d_q_latent=5, d_kv_latent=4,
+                                          d_head=4, d_rope=2, seq=t, p0=p0, seed=140 + i)
+        ds = _doc_starts(lens, p0)
+        ds[:lens[0]] = first  # the first document may have started before the new tokens
+        got = ref.gdla_forward(x, w, make_dims(ref, cfg, win), prefix, p0, doc_start=ds)
+        out, heads = brute_gdla(x, w, 3, 1, 1, 4, 2, win, prefix=prefix, p0=p0, doc_start=list(ds))
+        exp_out = np.array([[float(v) for v in r] for r in out])
+        _close(got["out"], exp_out, 1e-12, f"documents brute force case {i}")
+
+
+def pin_documents_are_separate_sequences(ref):
+    """A packed sequence of documents gives, on each document's rows, the forward of that document
+    alone from position 0: attention stays inside the document and RoPE scores depend only on
+    relative positions (the pages' packed training sequence, paperglide Figure 4 (a))."""
+    lens = (5, 1, 7, 3)
+    cfg, w, x, _ = small_problem(6, 4, 2, 2, seq=sum(lens), seed=77)
+    for win in (0, 3):
+        dims = make_dims(ref, cfg, win)
+        packed = ref.gdla_forward(x, w, dims, doc_start=_doc_starts(lens))
+        absorbed = ref.gdla_forward(x, w, dims, doc_start=_doc_starts(lens), form="absorbed")
+        _close(absorbed["out"], packed["out"], 1e-12, "documents absorbed vs expanded")
+        start = 0
+        for n in lens:
+            alone = ref.gdla_forward(x[start:start + n], w, dims)
+            _close(packed["out"][start:start + n], alone["out"], 1e-11,
+                   f"document at {start} (W={win}) vs the document alone")
+            start += n
+    # no document boundary inside the new tokens: the same as no documents
+    plain = ref.gdla_forward(x, w, make_dims(ref, cfg, 0))
+    one = ref.gdla_forward(x, w, make_dims(ref, cfg, 0), doc_start=np.zeros(sum(lens), dtype=int))
+    _close(one["out"], plain["out"], 0.0, "one document vs no documents")
+
+
 ALL_PINS = [pin_worked_example, pin_rmsnorm_library, pin_attention_sdpa, pin_brute_force,
             pin_lambda_zero_is_mla, pin_absorbed_equals_expanded, pin_window_special_cases,
             pin_closed_forms, pin_chunk_consistency, pin_pairing, pin_rope_mechanics,
-            pin_row_sums]
+            pin_row_sums, pin_documents_brute_force, pin_documents_are_separate_sequences]

@@ -32,6 +32,9 @@ MUTATIONS = {
     "gamma_ignored": ("return r if gamma is None else r * _f64(gamma)", "return r"),
     "absorbed_wrong_value_proj": ("out[t0:t1, h] = o @ w_uv[:, j * dh:(j + 1) * dh]",
                                   "out[t0:t1, h] = o @ w_uk[:, j * dh:(j + 1) * dh]"),
+    "document_mask_ignored": ("m &= s >= np.asarray(qdoc)[:, None]", "pass"),
+    "document_off_by_one": ("m &= s >= np.asarray(qdoc)[:, None]", "m &= s > np.asarray(qdoc)[:, None]"),
+    "document_key_range_from_last_row": ("lo = max(lo, int(np.min(qdoc)))", "lo = max(lo, int(np.max(qdoc)))"),
 }
 
 
