@@ -25,8 +25,9 @@
 // The values arrive transposed from the expansion GEMM ([n_kv][128][keys], keys of every 16-group
 // in the order vt_slot), which is the order in which the S accumulators hold the keys of P^T: the
 // accumulators serve as the P operand without any shuffle and no transposing LDS read is needed.
-// Causal / sliding-window tiles are classified per wave as skipped, full or partial; only partial
-// tiles evaluate the per-element mask s <= p && (W == 0 || p - s < W).
+// Causal / sliding-window / packed-document tiles are classified per wave as skipped, full or
+// partial; only partial tiles evaluate the per-element mask lo(p) <= s <= p, lo(p) the first key
+// of the window and of the token's document.
 #include "fast_paths.h"
 
 #include <algorithm>
@@ -53,6 +54,7 @@ struct AttnArgs {
   const f16_t *kx;        // [B, n_kv, lcap, 192] fp16: [K^C ; k^R] of keys base_b .. base_b + lcap - 1
   const f16_t *vx;        // [B, n_kv, 128, lcap] fp16: V^T, keys in vt_slot order per 16-group
   const int32_t *pos;     // [B] first position of the chunk
+  const int32_t *doc;     // [M] first position of each token's document (packed documents) or null
   const float *lam;       // [M, n_S]
   const void *gate;       // [M, n_S, 128]: sigmoid(G) in fp16 (gate_f16) or the logits G in fp32
   int32_t gate_f16;
@@ -138,13 +140,36 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
   const int W = a.window;
   const int p0 = a.pos[b];
   const int base = W > 0 ? max(0, p0 - W + 1) : 0;
-  // first key tile: aligned to 16 keys past `base` (the value layout's key groups); the extra keys
-  // in front are outside the window and masked
-  const int klo = W > 0 ? base + ((max(0, p0 + tlo - W + 1) - base) & ~15) : 0;
+  const int64_t mrow0 = (int64_t)b * a.T;
+  // lowest visible key of query t: the window's and (packed documents) its document's first key
+  auto qlo = [&](int t) {
+    int lo = W > 0 ? max(0, p0 + t - W + 1) : 0;
+    if (a.doc) lo = max(lo, min(max(a.doc[mrow0 + t], 0), p0 + t));
+    return lo;
+  };
+  // first key tile: from the block's first query (document starts never decrease along a packed
+  // sequence), aligned to 16 keys past `base` (the value layout's key groups); the extra keys in
+  // front are masked
+  const int klo = base + ((qlo(tlo) - base) & ~15);
   const int khi = p0 + thi + 1;
   const int ntiles = (khi - klo + KT - 1) / KT;
   const int wp_lo = p0 + t0w, wp_hi = p0 + min(t0w + 31, a.T - 1);
-  const int64_t mrow0 = (int64_t)b * a.T;
+  // this lane's query (column lane % 32 of the score tiles): key s is visible iff
+  // 0 <= p - s < wlim; wlo_min / wlo_max: lowest visible key over the wave's queries
+  int wlim, wlo_min, wlo_max;
+  {
+    const int tq = min(t0w + (lane & 31), a.T - 1);
+    const int lo = qlo(tq);
+    wlim = p0 + tq - lo + 1;
+    int mn = lo, mx = lo;
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+      mn = min(mn, __shfl_xor(mn, o, 64));
+      mx = max(mx, __shfl_xor(mx, o, 64));
+    }
+    wlo_min = __builtin_amdgcn_readfirstlane(mn);
+    wlo_max = __builtin_amdgcn_readfirstlane(mx);
+  }
 
   // ---- Q fragments: Qf[ks] holds dims 16 ks + 8 (lane / 32) .. + 7 of query column lane % 32
   f16x8 Qf[12];
@@ -208,9 +233,9 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
   }
 
   auto compute = [&](const f16_t *ks, const f16_t *vs, int s0) {
-    const bool skip = !active || s0 > wp_hi || (W > 0 && wp_lo - (s0 + KT - 1) >= W);
+    const bool skip = !active || s0 > wp_hi || s0 + KT - 1 < wlo_min;
     if (skip) return;
-    const bool full = (s0 + KT - 1 <= wp_lo) && (W == 0 || wp_hi - s0 < W);
+    const bool full = s0 + KT - 1 <= wp_lo && s0 >= wlo_max;
     const char *kb8 = (const char *)ks;
     const char *vb8 = (const char *)vs;
     // S phase, software-pipelined one k-step ahead: [reads of step kst + 1][MFMAs of step kst]
@@ -238,13 +263,12 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) v[kb * 16 + e] = S[kb][e];
     if (!full) {
-      // branch-free mask: visible iff 0 <= p - s < W (W = 0: no upper bound)
+      // branch-free mask: visible iff 0 <= p - s < wlim (negative p - s wraps above it)
       const int d0 = wp_lo + (lane & 31) - s0 - 4 * hgrp;
-      const unsigned wlim = W > 0 ? (unsigned)W : 0x7fffffffu;  // negative p - s wraps above it
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
         const int off = (i >> 4) * 32 + 8 * ((i & 15) >> 2) + (i & 3);
-        v[i] = (unsigned)(d0 - off) < wlim ? v[i] : -INFINITY;
+        v[i] = (unsigned)(d0 - off) < (unsigned)wlim ? v[i] : -INFINITY;
       }
     }
     float mt = v[0];
@@ -423,7 +447,7 @@ gdla_status run_fast_prefill(const LayerDims &d, const gdla_weights *w, int32_t 
                              int32_t max_len, void *cq, float *lam, float *gate, void *kx,
                              void *vx, int32_t lcap, void *y, float *out_heads,
                              const FastPrefillLayout &L, void *ws, hipStream_t s, StageEvents &se,
-                             const NtWeights *nt) {
+                             const NtWeights *nt, const int32_t *doc) {
   (void)pos_host;
   (void)cache;
   (void)max_len;
@@ -469,7 +493,7 @@ gdla_status run_fast_prefill(const LayerDims &d, const gdla_weights *w, int32_t 
 
   AttnArgs a{};
   a.q = q; a.kx = (const f16_t *)kx; a.vx = (const f16_t *)vx;
-  a.pos = pos_dev; a.lam = lam; a.gate = gate; a.gate_f16 = nt ? 1 : 0; a.hn = hn; a.y = (f16_t *)y; a.out_heads = out_heads;
+  a.pos = pos_dev; a.doc = doc; a.lam = lam; a.gate = gate; a.gate_f16 = nt ? 1 : 0; a.hn = hn; a.y = (f16_t *)y; a.out_heads = out_heads;
   a.T = T; a.lcap = lcap;
   a.n_heads = d.n_heads; a.n_signal = d.n_signal; a.n_noise = d.n_noise; a.n_kv = d.n_kv;
   a.window = d.window;

@@ -74,7 +74,7 @@ gdla_status run_fast_prefill(const LayerDims &d, const gdla_weights *w, int32_t 
                              int32_t max_len, void *cq, float *lam, float *gate, void *kx,
                              void *vx, int32_t lcap, void *y, float *out_heads,
                              const FastPrefillLayout &L, void *ws, hipStream_t s, StageEvents &se,
-                             const NtWeights *nt);
+                             const NtWeights *nt, const int32_t *doc);
 
 // ---- absorbed split-L decode ----
 // Sizes are per query row set: BT = B T for T new tokens per sequence.

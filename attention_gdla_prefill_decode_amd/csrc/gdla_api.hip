@@ -461,9 +461,11 @@ GDLA_EXPORT gdla_status gdla_latent_append_paged(const gdla_dims *dims, const gd
 
 namespace {
 
+// doc: device [B, T] first position of each token's document (packed documents), or null
 gdla_status prefill_impl(const gdla_dims *dims, const gdla_weights *w, const void *x, int32_t B, int32_t T,
                          const int32_t *pos_host, void *cache, int32_t max_len, void *out, void *ws,
-                         size_t ws_bytes, const gdla_debug *dbg, hipStream_t stream) {
+                         size_t ws_bytes, const gdla_debug *dbg, hipStream_t stream,
+                         const int32_t *doc = nullptr) {
   LayerDims d;
   gdla_status st = check_call(dims, w, x, B, T, pos_host, cache, max_len, out, true, d);
   if (st != GDLA_OK || B == 0 || T == 0) return st;
@@ -554,7 +556,7 @@ gdla_status prefill_impl(const gdla_dims *dims, const gdla_weights *w, const voi
     st = run_fast_prefill(d, w, B, T, pos_dev, pos_host, cache, max_len, at<void>(ws, L.cq),
                           at<float>(ws, L.lam), at<float>(ws, L.gate), at<void>(ws, L.kx),
                           at<void>(ws, L.vx), L.lcap, at<void>(ws, L.y), out_heads, L.fast, ws,
-                          stream, se, L.use_nt ? &ntw : nullptr);
+                          stream, se, L.use_nt ? &ntw : nullptr, doc);
     if (st != GDLA_OK) return fail(st, "fast prefill path failed: %s", hipGetErrorString(hipGetLastError()));
   } else {
     // Eq.(2), (9): q^C, pre-RoPE q^R and gate logits.
@@ -572,7 +574,7 @@ gdla_status prefill_impl(const gdla_dims *dims, const gdla_weights *w, const voi
     se.end(GDLA_STAGE_PROJ_Q);
     AttnGenericArgs a{};
     a.qc = at<void>(ws, L.qc); a.qr = at<void>(ws, L.qr); a.kx = at<void>(ws, L.kx);
-    a.vx = at<void>(ws, L.vx); a.cache = cache; a.heads = at<float>(ws, L.heads); a.pos = pos_dev;
+    a.vx = at<void>(ws, L.vx); a.cache = cache; a.heads = at<float>(ws, L.heads); a.pos = pos_dev; a.doc = doc;
     a.M = M; a.T = T; a.max_len = max_len; a.lcap = L.lcap;
     se.begin(GDLA_STAGE_ATTN_NOISE);
     HIP_TRY(launch_attention_generic(a, d, dt, stream));
@@ -610,6 +612,16 @@ GDLA_EXPORT gdla_status gdla_prefill(const gdla_dims *dims, const gdla_weights *
                                      const gdla_debug *dbg, hipStream_t stream) {
   g_err[0] = 0;
   return prefill_impl(dims, w, x, B, T, pos_host, cache, max_len, out, ws, ws_bytes, dbg, stream);
+}
+
+GDLA_EXPORT gdla_status gdla_prefill_packed(const gdla_dims *dims, const gdla_weights *w, const void *x,
+                                            int32_t B, int32_t T, const int32_t *pos_host,
+                                            const int32_t *doc_start, void *cache, int32_t max_len, void *out,
+                                            void *ws, size_t ws_bytes, const gdla_debug *dbg, hipStream_t stream) {
+  g_err[0] = 0;
+  if (B > 0 && T > 0 && !doc_start) return fail(GDLA_ERR_INVALID_ARG, "doc_start is NULL");
+  if (((uintptr_t)doc_start & 3u) != 0) return fail(GDLA_ERR_INVALID_ARG, "doc_start must be 4-byte aligned");
+  return prefill_impl(dims, w, x, B, T, pos_host, cache, max_len, out, ws, ws_bytes, dbg, stream, doc_start);
 }
 
 GDLA_EXPORT gdla_status gdla_prefill_paged(const gdla_dims *dims, const gdla_weights *w, const void *x,

@@ -145,6 +145,7 @@ struct AttnGenericArgs {
   const void *qc, *qr, *kx, *vx, *cache;
   float *heads;
   const int32_t *pos;
+  const int32_t *doc;  // [M] first position of each token's document, or null (no documents)
   int32_t M, T, max_len, lcap;
 };
 hipError_t launch_attention_generic(const AttnGenericArgs &a, const LayerDims &d, DT dt,

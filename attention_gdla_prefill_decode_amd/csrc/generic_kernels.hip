@@ -235,7 +235,8 @@ __global__ void __launch_bounds__(256) attention_generic_kernel(AttnGenericArgs 
   const int b = m / a.T, t = m % a.T;
   const int p = a.pos[b] + t;
   const int base = d.window > 0 ? max(0, a.pos[b] - d.window + 1) : 0;
-  const int lo = d.window > 0 ? max(0, p - d.window + 1) : 0;
+  int lo = d.window > 0 ? max(0, p - d.window + 1) : 0;
+  if (a.doc) lo = max(lo, min(max(a.doc[m], 0), p));  // packed documents: keys from the token's document
   const int kv = kv_head_of(h, d.n_signal, d.n_kv);
   const T *qc = (const T *)a.qc + ((int64_t)m * d.n_heads + h) * d.d_h;
   const T *qr = (const T *)a.qr + ((int64_t)m * d.n_heads + h) * d.d_r;

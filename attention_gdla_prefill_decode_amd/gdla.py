@@ -22,8 +22,8 @@ WEIGHT_FIELDS = ("w_qa", "gamma_q", "w_qc", "w_qr", "w_dkv", "w_kr", "gamma_kv",
                  "w_lambda", "w_gate", "w_o")
 
 EXPORTED = ("gdla_workspace_bytes", "gdla_latent_append", "gdla_prefill", "gdla_decode",
-            "gdla_decode_tokens", "gdla_latent_append_paged", "gdla_prefill_paged",
-            "gdla_decode_paged", "gdla_status_string", "gdla_last_error")
+            "gdla_decode_tokens", "gdla_prefill_packed", "gdla_latent_append_paged",
+            "gdla_prefill_paged", "gdla_decode_paged", "gdla_status_string", "gdla_last_error")
 
 MAX_DECODE_TOKENS = 16  # GDLA_MAX_DECODE_TOKENS
 
@@ -134,6 +134,12 @@ def lib():
                                          ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_size_t, P(GdlaDebug), ctypes.c_void_p]
+        L.gdla_prefill_packed.restype = ctypes.c_int
+        L.gdla_prefill_packed.argtypes = [P(GdlaDims), P(GdlaWeights), ctypes.c_void_p, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_size_t, P(GdlaDebug),
+                                          ctypes.c_void_p]
         L.gdla_latent_append_paged.restype = ctypes.c_int
         L.gdla_latent_append_paged.argtypes = [P(GdlaDims), P(GdlaWeights), ctypes.c_void_p,
                                                ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
@@ -267,6 +273,25 @@ def gdla_decode_tokens(dims, weights, x, pos, cache, out=None, ws=None, lambda_o
                                     _pos_array(pos), _ptr(cache), max_len, _ptr(out), _ptr(ws),
                                     nbytes, None if dbg is None else ctypes.byref(dbg),
                                     _stream(stream)))
+    return out
+
+
+def gdla_prefill_packed(dims, weights, x, pos, doc_start, cache, out=None, ws=None,
+                        lambda_override=None, out_heads=None, stream=None, timer=None):
+    """gdla_prefill over packed documents: doc_start [B, T] int32 (device) holds the position of
+    the first token of each token's document."""
+    B, T = x.shape[0], x.shape[1]
+    max_len = cache.shape[1]
+    assert doc_start.dtype == torch.int32 and tuple(doc_start.shape) == (B, T)
+    doc_start = doc_start.contiguous()
+    if out is None:
+        out = torch.empty_like(x)
+    ws, nbytes = _workspace(dims, GDLA_OP_PREFILL, B, T, pos, max_len, ws, x.device)
+    dbg = _debug(lambda_override, out_heads, timer)
+    _check(lib().gdla_prefill_packed(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B, T,
+                                     _pos_array(pos), _ptr(doc_start), _ptr(cache), max_len,
+                                     _ptr(out), _ptr(ws), nbytes,
+                                     None if dbg is None else ctypes.byref(dbg), _stream(stream)))
     return out
 
 

@@ -32,20 +32,37 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "GDLA prefill TFLOP/s (% bf16 MFMA peak); decode latent-KV GB/s (% HBM peak)"
 
 
-def visible_pairs(p0, t, window):
-    """Number of (query, key) pairs with key <= query position and, for window W, within W."""
+def visible_pairs(p0, t, window, docs=None):
+    """Number of (query, key) pairs with key <= query position and, for window W, within W (and,
+    with packed documents, inside the query's document: docs[i] = first position of its document)."""
     total = 0
     for i in range(t):
         p = p0 + i
-        total += min(p + 1, window) if window > 0 else p + 1
+        lo = max(0, p - window + 1) if window > 0 else 0
+        if docs is not None:
+            lo = max(lo, docs[i])
+        total += p + 1 - lo
     return total
 
 
-def layer_flops(cfg, t, p0, window):
+def packed_documents(t, mean, seed=0):
+    """Document starts of t packed tokens, document lengths drawn from a seeded exponential
+    distribution of the given mean (at least one token each)."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    starts, pos = [], 0
+    while pos < t:
+        n = max(1, int(round(rng.exponential(mean))))
+        starts += [pos] * min(n, t - pos)
+        pos += n
+    return starts
+
+
+def layer_flops(cfg, t, p0, window, docs=None):
     """Algorithmic FLOP of one GDLA layer call on one sequence (attention counts visible pairs)."""
     d, dcq, dc, nh, ns = cfg["d_model"], cfg["d_q_latent"], cfg["d_kv_latent"], cfg["n_heads"], cfg["n_signal"]
     nkv, dh, dr = cfg["n_kv"], cfg["d_head"], cfg["d_rope"]
-    pairs = visible_pairs(p0, t, window)
+    pairs = visible_pairs(p0, t, window, docs)
     attn_signal = 2.0 * ns * pairs * (2 * dh + dr)
     attn_noise = 2.0 * (nh - ns) * pairs * (2 * dh + dr)
     keys = p0 + t - (max(0, p0 - window + 1) if window > 0 else 0)
@@ -222,6 +239,9 @@ def main():
     ap.add_argument("--page-rows", type=int, default=0,
                     help="with the decode workload: run over a paged cache of this page size "
                          "(gdla_decode_paged)")
+    ap.add_argument("--docs", type=float, default=0,
+                    help="prefill workloads: pack the tokens into documents of this mean length "
+                         "(seeded exponential lengths; gdla_prefill_packed)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 1 GiB device to device three times (a known-size reference "
@@ -274,17 +294,25 @@ def main():
     ws = torch.empty(gd.gdla_workspace_bytes(dims, gd.GDLA_OP_PREFILL, bsz, t, pos, cfg["max_len"]),
                      dtype=torch.uint8, device="cuda")
     out = torch.empty_like(x)
+    docs = None
+    run = gd.gdla_prefill
+    if args.docs > 0:  # documents packed from the chunk's first token
+        docs = [p0 + v for v in packed_documents(t, args.docs)]
+        doc_t = torch.tensor([docs] * bsz, dtype=torch.int32, device="cuda")
+
+        def run(*a, **k):
+            return gd.gdla_prefill_packed(a[0], a[1], a[2], a[3], doc_t, a[4], **k)
     # one set of stage events per timed step, read after the timed region (no host sync inside)
     timers = [gd.StageTimer() for _ in range(args.steps)]
     for _ in range(args.warmup):
-        gd.gdla_prefill(dims, w, x, pos, cache, out=out, ws=ws)
+        run(dims, w, x, pos, cache, out=out, ws=ws)
     torch.cuda.synchronize()
 
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
     for i in range(args.steps):
-        gd.gdla_prefill(dims, w, x, pos, cache, out=out, ws=ws, timer=timers[i])
+        run(dims, w, x, pos, cache, out=out, ws=ws, timer=timers[i])
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
@@ -293,7 +321,7 @@ def main():
         for k, v in tm.elapsed().items():
             stage_tot[k] += v
     stages = {k: round(v / args.steps, 4) for k, v in stage_tot.items()}
-    fl = {k: v * bsz for k, v in layer_flops(cfg, t, p0, win).items()}
+    fl = {k: v * bsz for k, v in layer_flops(cfg, t, p0, win, docs).items()}
     value = fl["total"] / (ms * 1e-3) / 1e12
     attn_ms = stages["attn_signal"]
     achieved = fl["attn_signal"] / (attn_ms * 1e-3) / 1e12
@@ -306,13 +334,14 @@ def main():
         "config": {"workload": args.workload, "batch": bsz, "seq_len": t, "cached_before": p0,
                    "d_model": cfg["d_model"], "heads": "64 signal + 16 noise, 16 KV",
                    "latents": "1024 / 512", "head_dim": cfg["d_head"], "rope_dim": cfg["d_rope"],
-                   "window": win, "parallelism": "none (1 GPU)"},
+                   "window": win, "parallelism": "none (1 GPU)",
+                   **({"documents": len(set(docs)), "mean_document": args.docs} if docs else {})},
         "frac_of_mfma_peak_whole_step": round(value / PEAK_MFMA_TFLOPS, 4),
         "roofline": {"kernel": "attn_prefill_kernel<signal>", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
                      "traffic": (traffic_from_profile("attn_signal_prefill_8k_traffic.json")
-                                 if args.workload == "prefill_8k" else None),
+                                 if args.workload == "prefill_8k" and not docs else None),
                      "flop_per_launch": fl["attn_signal"], "avg_launch_ms": attn_ms},
         "attention_core": {"kernels": "noise + signal attention", "ms": round(attn_ms + noise_ms, 4),
                            "TFLOPs": round((fl["attn_signal"] + fl["attn_noise"])
@@ -322,7 +351,7 @@ def main():
     }
     if args.decode:
         result["decode"] = bench_decode(max(3, args.steps // 4), 2)
-    if not args.no_cpu_baseline and args.workload == "prefill_8k":
+    if not args.no_cpu_baseline and args.workload == "prefill_8k" and not docs:
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result), flush=True)
 

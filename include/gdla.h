@@ -170,6 +170,20 @@ gdla_status gdla_decode(const gdla_dims *dims, const gdla_weights *w, const void
                         const int32_t *pos_host, void *cache, int32_t max_len, void *out,
                         void *ws, size_t ws_bytes, const gdla_debug *dbg, hipStream_t stream);
 
+/* gdla_prefill over packed documents (paperglide reader, Figure 4 (a): a training sequence that
+ * holds 473 documents, drawn on the QK^T score matrix): every token attends only to keys of its own
+ * document, inside the window.  doc_start is a device int32 array [B, T]: for token t of sequence
+ * b, the position of the first token of its document (0 <= doc_start <= pos_host[b] + t; a
+ * document may have started in an earlier chunk).  Within a sequence doc_start must not decrease
+ * (documents are contiguous); the kernels clamp out-of-range values into [0, position].  All other
+ * arguments, the workspace (GDLA_OP_PREFILL) and the errors are those of gdla_prefill, plus
+ * GDLA_ERR_INVALID_ARG for a NULL or misaligned doc_start. */
+gdla_status gdla_prefill_packed(const gdla_dims *dims, const gdla_weights *w, const void *x,
+                                int32_t B, int32_t T, const int32_t *pos_host,
+                                const int32_t *doc_start, void *cache, int32_t max_len, void *out,
+                                void *ws, size_t ws_bytes, const gdla_debug *dbg,
+                                hipStream_t stream);
+
 /* Several new tokens per sequence on the absorbed decode path: the verification step of
  * self-speculative decoding with a multi-token-prediction head (picx.dev summary section 2.1, the
  * MTP component; alphasignal.ai news page, "A wall of custom parts").  The T tokens of sequence b

@@ -68,10 +68,23 @@ def device_inputs(inp, device="cuda"):
     return d
 
 
+def doc_starts(p0, lens, first=None):
+    """Per-token document starts of one sequence whose new tokens (from position p0) hold documents
+    of the given lengths; the first document began at `first` (default p0)."""
+    out, start = [], p0
+    for n in lens:
+        out += [start] * n
+        start += n
+    if first is not None:
+        out[:lens[0]] = [first] * lens[0]
+    return out
+
+
 def prefill_case(cfg, seq, p0, window=0, seed=None, random_gamma=True, lam_zero=False,
-                 want_heads=False, entry="prefill"):
+                 want_heads=False, entry="prefill", docs=None):
     """Runs gdla_prefill (or, with entry="decode_tokens", the multi-token absorbed decode) on GPU
-    and the oracle's one-call forward on CPU for every sequence; returns both outputs."""
+    and the oracle's one-call forward on CPU for every sequence; returns both outputs.  docs: per
+    sequence, the document start of every new token (gdla_prefill_packed)."""
     batch = len(p0)
     inp = synth.make_inputs(cfg, "cpu", seed=seed, batch=batch, seq=seq, p0=p0,
                             random_gamma=random_gamma)
@@ -84,9 +97,14 @@ def prefill_case(cfg, seq, p0, window=0, seed=None, random_gamma=True, lam_zero=
     if want_heads:
         heads = torch.empty((batch, seq, cfg["n_heads"], cfg["d_head"]), dtype=torch.float32,
                             device="cuda")
-    run = gd.gdla_prefill if entry == "prefill" else gd.gdla_decode_tokens
-    out = run(dims, dev["wstruct"], dev["x"], inp["p0"], dev["cache"], lambda_override=lam,
-              out_heads=heads)
+    if docs is not None:
+        ds = torch.tensor(docs, dtype=torch.int32, device="cuda")
+        out = gd.gdla_prefill_packed(dims, dev["wstruct"], dev["x"], inp["p0"], ds, dev["cache"],
+                                     lambda_override=lam, out_heads=heads)
+    else:
+        run = gd.gdla_prefill if entry == "prefill" else gd.gdla_decode_tokens
+        out = run(dims, dev["wstruct"], dev["x"], inp["p0"], dev["cache"], lambda_override=lam,
+                  out_heads=heads)
     torch.cuda.synchronize()
     w = oracle_weights(inp)
     od = oracle_dims(cfg, window)
@@ -94,7 +112,8 @@ def prefill_case(cfg, seq, p0, window=0, seed=None, random_gamma=True, lam_zero=
     for b in range(batch):
         pre = to_np(inp["cache"][b, :inp["p0"][b]]) if inp["p0"][b] > 0 else None
         r = ref.gdla_forward(to_np(inp["x"][b]), w, od, pre, inp["p0"][b],
-                             None if lam is None else np.zeros((seq, cfg["n_signal"])))
+                             None if lam is None else np.zeros((seq, cfg["n_signal"])),
+                             doc_start=None if docs is None else np.array(docs[b]))
         exp_out.append(r["out"])
         exp_rows.append(r["cache_rows"])
         exp_heads.append(r["heads"])

@@ -229,3 +229,20 @@ def test_paged_argument_errors():
     pre = gd.gdla_workspace_bytes(d, gd.GDLA_OP_PREFILL, 2, 8, [5, 60], 128)
     prp = gd.gdla_workspace_bytes(d, gd.GDLA_OP_PREFILL_PAGED, 2, 8, [5, 60], 128)
     assert prp >= pre + 2 * 68 * 576 * 2
+
+
+def test_packed_prefill_argument_errors():
+    lib = gd.lib()
+    d = big_dims()
+    w = gb.GdlaWeights(*([FAKE] * 12))
+    pos = (ctypes.c_int32 * 1)(0)
+
+    def call(doc, ws_bytes=1 << 40, T=4):
+        return lib.gdla_prefill_packed(ctypes.byref(d), ctypes.byref(w), FAKE, 1, T, pos, doc, FAKE, 64,
+                                       FAKE, FAKE, ws_bytes, None, None)
+
+    assert call(None) == gb.GDLA_ERR_INVALID_ARG
+    assert lib.gdla_last_error().decode()
+    assert call(FAKE + 2) == gb.GDLA_ERR_INVALID_ARG
+    assert call(FAKE, ws_bytes=16) == gb.GDLA_ERR_WORKSPACE
+    assert call(FAKE, T=65) == gb.GDLA_ERR_OUT_OF_RANGE

@@ -207,6 +207,39 @@ def test_decode_tokens_matches_decode_and_prefill():
         H.check_rows(H.to_np(c4[bi, p:p + 4]), H.to_np(c3[bi, p:p + 4]), "bf16", "appended rows")
 
 
+# ---------------------------------------------------------------- packed documents
+@pytest.mark.parametrize("cfg,T,p0,window,lens,first", [
+    (BF, 300, [0], 0, (37, 113, 150), None),          # document edges inside query blocks and tiles
+    (BF, 200, [0, 77], 40, (1, 64, 135), None),       # a one-token document; window inside documents
+    (BF, 160, [300], 0, (100, 60), 120),              # the first document began in the cached prefix
+    (H.BF80, 130, [0], 0, (65, 65), None),
+    (TINY, 70, [0, 9], 12, (20, 3, 47), None),        # fp32 generic path
+])
+def test_packed_prefill(cfg, T, p0, window, lens, first):
+    docs = [H.doc_starts(p, lens, first) for p in p0]
+    r = H.prefill_case(cfg, T, p0, window=window, seed=47, want_heads=True, docs=docs)
+    dt = cfg["dtype"]
+    _say(H.check(r["out"], r["exp_out"], dt, f"packed prefill {dt} lens={lens} W={window}"))
+    if dt == "f32":
+        err = float(np.max(np.abs(r["heads"] - r["exp_heads"])))
+        assert err <= 1e-5, f"per-head H max-abs {err:.3e}"
+    else:
+        H.check(r["heads"], r["exp_heads"], dt, "per-head H")
+
+
+def test_packed_prefill_single_document_is_prefill():
+    """One document from position 0 masks nothing: bit for bit the plain prefill."""
+    inp = synth.make_inputs(BF, "cpu", batch=2, seq=150, p0=[0, 40], random_gamma=True, seed=53)
+    dev = H.device_inputs(inp)
+    dims = gd.make_dims(BF, window=70)
+    c2 = dev["cache"].clone()
+    ref_out = gd.gdla_prefill(dims, dev["wstruct"], dev["x"], inp["p0"], dev["cache"])
+    zero = torch.zeros((2, 150), dtype=torch.int32, device="cuda")
+    out = gd.gdla_prefill_packed(dims, dev["wstruct"], dev["x"], inp["p0"], zero, c2)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out)
+
+
 # ---------------------------------------------------------------- paged latent cache
 # The same calls over a shuffled pool of pages: the kernels read and write exactly the rows of the
 # contiguous layout, so the outputs must equal the contiguous path's bit for bit (windowed decode
