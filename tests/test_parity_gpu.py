@@ -291,6 +291,34 @@ def test_paged_prefill_matches_contiguous(cfg, T, p0, window, page_rows):
     _say(H.check(H.to_np(out), r["exp_out"], cfg["dtype"], f"paged prefill T={T} W={window}"))
 
 
+@pytest.mark.parametrize("entry", ["decode", "prefill"])
+def test_paged_window_never_reads_recycled_pages(entry):
+    """Sliding-window layer over a ring of pages: the blocks wholly before every new token's window
+    are remapped to a page of NaNs (as a serving system would recycle them).  Neither path may read
+    them: the outputs stay finite and equal the contiguous cache's."""
+    cfg, W, page = dict(H.BF80, window=96), 96, 32
+    T = 3 if entry == "decode" else 40
+    p0 = [500, 1000, 130]
+    inp = synth.make_inputs(cfg, "cpu", batch=3, seq=T, p0=p0, random_gamma=True, seed=59)
+    dev = H.device_inputs(inp)
+    dims = gd.make_dims(cfg, window=W)
+    pc = H.to_pages(dev["cache"], page, seed=13)
+    poison = pc.pages.shape[0] - 1  # a spare page: no block maps to it yet
+    pc.pages[poison] = float("nan")
+    for b, p in enumerate(p0):
+        first_visible = max(0, p - W + 1)  # the first new token's window start (later ones start later)
+        pc.block_table[b, :first_visible // page] = poison
+    if entry == "decode":
+        ref = gd.gdla_decode_tokens(dims, dev["wstruct"], dev["x"], p0, dev["cache"])
+        out = gd.gdla_decode_paged(dims, dev["wstruct"], dev["x"], p0, pc)
+    else:
+        ref = gd.gdla_prefill(dims, dev["wstruct"], dev["x"], p0, dev["cache"])
+        out = gd.gdla_prefill_paged(dims, dev["wstruct"], dev["x"], p0, pc)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all()), "a recycled (NaN) page was read"
+    _say(H.check(H.to_np(out), H.to_np(ref), "bf16", f"ring of pages, {entry}"))
+
+
 def test_paged_append():
     cfg = BF
     inp = synth.make_inputs(cfg, "cpu", batch=3, seq=45, p0=[0, 20, 99], seed=43)
