@@ -1,0 +1,168 @@
+"""Plain fp64 CPU oracle of the GDLA layer's backward pass (gradients of a training step).
+
+TEST INFRASTRUCTURE ONLY, like gdla_ref.py: only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import it; the GPU product path never does.
+
+The pages train Motif 3 with GDLA layers and recompute each block's forward pass during the
+backward pass (paperglide reader, section "Distributed Training System": activation recomputation);
+they give no gradient formulas.  This module differentiates the forward of gdla_ref.py
+(picx.dev summary section 2.2, Eq.(1)-(10), with the same readings) by the chain rule, one
+equation at a time, in the reverse order of the forward:
+
+    out = vec(Y) W_O                       Eq.(10)   -> dW_O, dY
+    Y = sigmoid(G) (.) D                   Eq.(10)   -> dD, dG
+    D_i = H_i - lambda_i H_(n_S + i mod n_N)   Eq.(8) -> dH (signal and noise), dlambda
+    H_h = softmax(tau S_h) V                (two softmax maps, both kinds of head)
+                                                     -> dq^C, dq^R, dK^C, dk^R, dV
+    lambda = sigmoid(x W_lambda)           Eq.(7)
+    [K^C ; V] = cbar [W_uk | W_uv]         Eq.(5)    -> dcbar, dW_uk, dW_uv
+    cbar = RMSNorm(c^KV) gamma_KV          Eq.(4)
+    k^R = RoPE(x W_kr)                     Eq.(3)
+    q^C, q^R = c^Q W_qc, RoPE(c^Q W_qr)    Eq.(2);  G = c^Q W_gate  Eq.(9)
+    c^Q = RMSNorm(x W_qa) gamma_Q          Eq.(1)
+
+Softmax backward: with P = softmax(s) and dH = P V's upstream gradient, dP = dH V^T and
+ds = P (.) (dP - rowsum(dP (.) P)); masked keys have P = 0 and so receive no gradient.  RoPE is a
+rotation, so its backward rotates by the negative angle.  RMSNorm backward of y = v / r (.) gamma,
+r = sqrt(mean(v^2) + eps): with u = dy (.) gamma, dv = u / r - v (sum_j u_j v_j) / (n r^3) and
+dgamma = sum over rows of dy (.) v / r.
+
+The reference is the loss L = sum(out (.) dout) for a given upstream gradient dout; every returned
+gradient is dL/d(that input).  Only new-token sequences starting at position 0 are covered (a
+training sequence), with the optional window and packed documents of the forward.
+"""
+
+import numpy as np
+
+from oracle import gdla_ref as ref
+
+__all__ = ["rms_norm_backward", "rope_backward", "gdla_backward"]
+
+
+def _f64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+def rms_norm_backward(v, gamma, dy, eps):
+    """Gradient of y = v / sqrt(mean(v^2) + eps) (.) gamma over the last axis: returns (dv, dgamma);
+    dgamma is None when gamma is None (a fixed gain of 1)."""
+    v, dy = _f64(v), _f64(dy)
+    n = v.shape[-1]
+    r = np.sqrt(np.mean(v * v, axis=-1, keepdims=True) + eps)
+    u = dy if gamma is None else dy * _f64(gamma)
+    dv = u / r - v * np.sum(u * v, axis=-1, keepdims=True) / (n * r ** 3)
+    dgamma = None if gamma is None else np.sum(dy * v / r, axis=tuple(range(v.ndim - 1)))
+    return dv, dgamma
+
+
+def rope_backward(du, pos, theta):
+    """Gradient through RoPE: the transpose of a rotation is the rotation by the negative angle."""
+    return ref.rope(du, -_f64(pos), theta)
+
+
+def gdla_backward(x, w, dims, dout, doc_start=None, lam_override=None):
+    """Gradients of L = sum(out (.) dout) for one sequence x [T, d_model] at positions 0..T-1.
+
+    Returns a dict: dx [T, d_model]; dw_qa, dw_qc, dw_qr, dw_dkv, dw_kr, dw_uk, dw_uv, dw_lambda,
+    dw_gate, dw_o (shaped like the weights); dgamma_q, dgamma_kv (None for fixed gains of 1); and
+    the intermediate gradients dY, dH (per head), dlam, dq_c, dq_r, dk_c, dk_r, dv.
+    """
+    x, dout = _f64(x), _f64(dout)
+    t = x.shape[0]
+    pos = np.arange(t)
+    nh, ns, nn, nkv = dims.n_heads, dims.n_signal, dims.n_noise, dims.n_kv
+    dh, dr, tau = dims.d_head, dims.d_rope, dims.scale
+    W = {k: _f64(v) for k, v in w.items() if k.startswith("w_")}
+    gq = None if w.get("gamma_q") is None else _f64(w["gamma_q"])
+    gkv = None if w.get("gamma_kv") is None else _f64(w["gamma_kv"])
+
+    # ---- forward, keeping what the backward needs (the recomputation)
+    a_q = x @ W["w_qa"]
+    c_q = ref.rms_norm(a_q, gq, dims.eps)                                        # Eq.(1)
+    q_c = (c_q @ W["w_qc"]).reshape(t, nh, dh)                                   # Eq.(2)
+    q_r = ref.rope((c_q @ W["w_qr"]).reshape(t, nh, dr), pos, dims.theta)
+    g_logit = (c_q @ W["w_gate"]).reshape(t, ns, dh)                             # Eq.(9)
+    c_kv = x @ W["w_dkv"]
+    c_bar = ref.rms_norm(c_kv, gkv, dims.eps)                                    # Eq.(3), (4)
+    k_r = ref.rope(x @ W["w_kr"], pos, dims.theta)
+    k_c = (c_bar @ W["w_uk"]).reshape(t, nkv, dh)                                # Eq.(5)
+    v = (c_bar @ W["w_uv"]).reshape(t, nkv, dh)
+    lam = ref.sigmoid(x @ W["w_lambda"]) if lam_override is None else _f64(lam_override)  # Eq.(7)
+    mask = ref.visible_mask(pos, pos, dims.window, None if doc_start is None else doc_start)
+    probs = np.zeros((nh, t, t))
+    heads = np.zeros((t, nh, dh))
+    for h in range(nh):
+        j = ref.kv_head_of(h, dims)
+        s = tau * (q_c[:, h] @ k_c[:, j].T + q_r[:, h] @ k_r.T)
+        s = np.where(mask, s, -np.inf)
+        e = np.where(mask, np.exp(s - np.max(s, axis=1, keepdims=True)), 0.0)
+        probs[h] = e / np.sum(e, axis=1, keepdims=True)
+        heads[:, h] = probs[h] @ v[:, j]
+    h_s, h_n = heads[:, :ns], heads[:, ns:]
+    partner = np.arange(ns) % nn                                                 # Repeat_g tiles
+    d = h_s - lam[:, :, None] * h_n[:, partner]                                  # Eq.(8)
+    sg = ref.sigmoid(g_logit)
+    y = sg * d                                                                   # Eq.(10)
+
+    # ---- Eq.(10): out = vec(Y) W_O and the gate
+    dw_o = y.reshape(t, ns * dh).T @ dout
+    d_y = (dout @ W["w_o"].T).reshape(t, ns, dh)
+    d_d = d_y * sg
+    d_g = d_y * d * sg * (1.0 - sg)
+
+    # ---- Eq.(8): signal heads take dD, the noise head of pair i takes -lambda_i dD_i
+    d_heads = np.zeros((t, nh, dh))
+    d_heads[:, :ns] = d_d
+    for i in range(ns):
+        d_heads[:, ns + partner[i]] -= lam[:, i:i + 1] * d_d[:, i]
+    d_lam = -np.sum(d_d * h_n[:, partner], axis=2)
+
+    # ---- the softmax maps of every head
+    d_qc = np.zeros_like(q_c)
+    d_qr = np.zeros_like(q_r)
+    d_kc = np.zeros_like(k_c)
+    d_kr = np.zeros_like(k_r)
+    d_v = np.zeros_like(v)
+    for h in range(nh):
+        j = ref.kv_head_of(h, dims)
+        p = probs[h]
+        dp = d_heads[:, h] @ v[:, j].T
+        ds = p * (dp - np.sum(dp * p, axis=1, keepdims=True))
+        d_v[:, j] += p.T @ d_heads[:, h]
+        d_qc[:, h] = tau * ds @ k_c[:, j]
+        d_qr[:, h] = tau * ds @ k_r
+        d_kc[:, j] += tau * ds.T @ q_c[:, h]
+        d_kr += tau * ds.T @ q_r[:, h]
+
+    # ---- Eq.(5), (4), (3): back into the latent and the rotary key
+    dw_uk = c_bar.T @ d_kc.reshape(t, nkv * dh)
+    dw_uv = c_bar.T @ d_v.reshape(t, nkv * dh)
+    d_cbar = d_kc.reshape(t, nkv * dh) @ W["w_uk"].T + d_v.reshape(t, nkv * dh) @ W["w_uv"].T
+    d_ckv, dgamma_kv = rms_norm_backward(c_kv, gkv, d_cbar, dims.eps)
+    d_kr_pre = rope_backward(d_kr, pos, dims.theta)
+
+    # ---- Eq.(2), (9), (1): back into the query latent
+    d_qr_pre = rope_backward(d_qr, pos, dims.theta).reshape(t, nh * dr)
+    d_qc_flat = d_qc.reshape(t, nh * dh)
+    d_g_flat = d_g.reshape(t, ns * dh)
+    dw_qc = c_q.T @ d_qc_flat
+    dw_qr = c_q.T @ d_qr_pre
+    dw_gate = c_q.T @ d_g_flat
+    d_cq = d_qc_flat @ W["w_qc"].T + d_qr_pre @ W["w_qr"].T + d_g_flat @ W["w_gate"].T
+    d_aq, dgamma_q = rms_norm_backward(a_q, gq, d_cq, dims.eps)
+
+    # ---- Eq.(7): lambda (a fixed override receives no gradient path into x)
+    d_lam_logit = d_lam * lam * (1.0 - lam) if lam_override is None else np.zeros_like(d_lam)
+
+    # ---- x and the x-side weights
+    dw_qa = x.T @ d_aq
+    dw_dkv = x.T @ d_ckv
+    dw_kr = x.T @ d_kr_pre
+    dw_lambda = x.T @ d_lam_logit
+    dx = (d_aq @ W["w_qa"].T + d_ckv @ W["w_dkv"].T + d_kr_pre @ W["w_kr"].T
+          + d_lam_logit @ W["w_lambda"].T)
+    return {"dx": dx, "dw_qa": dw_qa, "dw_qc": dw_qc, "dw_qr": dw_qr, "dw_dkv": dw_dkv,
+            "dw_kr": dw_kr, "dw_uk": dw_uk, "dw_uv": dw_uv, "dw_lambda": dw_lambda,
+            "dw_gate": dw_gate, "dw_o": dw_o, "dgamma_q": dgamma_q, "dgamma_kv": dgamma_kv,
+            "dY": d_y, "dH": d_heads, "dlam": d_lam, "dq_c": d_qc, "dq_r": d_qr, "dk_c": d_kc,
+            "dk_r": d_kr, "dv": d_v}

@@ -320,3 +320,75 @@ ALL_PINS = [pin_worked_example, pin_rmsnorm_library, pin_attention_sdpa, pin_bru
             pin_lambda_zero_is_mla, pin_absorbed_equals_expanded, pin_window_special_cases,
             pin_closed_forms, pin_chunk_consistency, pin_pairing, pin_rope_mechanics,
             pin_row_sums, pin_documents_brute_force, pin_documents_are_separate_sequences]
+
+
+# -------------------------------------------------------------------------------- backward
+# Pins of the backward oracle (oracle/gdla_grad.py).  Each takes the backward module `gg`; the
+# forward they differentiate is oracle.gdla_ref, pinned above.
+def _loss_fd(ref_fwd, x, w, dims, dout, docs, name, direction, eps=1e-6):
+    """Central difference of L = sum(out (.) dout) along `direction` of input `name`."""
+    def f(xx, ww):
+        return float(np.sum(ref_fwd.gdla_forward(xx, ww, dims, doc_start=docs)["out"] * dout))
+    if name == "x":
+        return (f(x + eps * direction, w) - f(x - eps * direction, w)) / (2 * eps)
+    wp, wm = dict(w), dict(w)
+    wp[name] = w[name] + eps * direction
+    wm[name] = w[name] - eps * direction
+    return (f(x, wp) - f(x, wm)) / (2 * eps)
+
+
+def pin_backward_finite_differences(gg):
+    """Every gradient matches the central finite difference of the pinned forward along a random
+    direction (full causal; with a window and packed documents)."""
+    import oracle.gdla_ref as ref_fwd
+    for i, (win, docs) in enumerate(((0, None), (3, [0, 0, 0, 3, 3, 3, 3, 7]))):
+        cfg, w, x, _ = small_problem(6, 4, 2, 2, seq=8, seed=61 + i)
+        dims = make_dims(ref_fwd, cfg, win)
+        rng = np.random.default_rng(70 + i)
+        dout = rng.standard_normal((8, cfg["d_model"]))
+        g = gg.gdla_backward(x, w, dims, dout, doc_start=None if docs is None else np.array(docs))
+        names = ["x"] + sorted(k for k in w if w[k] is not None)
+        for name in names:
+            base = x if name == "x" else w[name]
+            direction = rng.standard_normal(base.shape)
+            fd = _loss_fd(ref_fwd, x, w, dims, dout, docs, name, direction)
+            an = float(np.sum(g["d" + name] * direction))
+            if not abs(fd - an) <= 1e-7 * max(1.0, abs(fd)):
+                raise AssertionError(f"backward vs finite difference, {name} (case {i}): {an} vs {fd}")
+
+
+def pin_backward_entries(gg):
+    """Single entries of dx and of several weight gradients against one-coordinate differences."""
+    import oracle.gdla_ref as ref_fwd
+    cfg, w, x, _ = small_problem(4, 3, 1, 1, seq=5, seed=83)
+    dims = make_dims(ref_fwd, cfg, 0)
+    dout = np.random.default_rng(84).standard_normal((5, cfg["d_model"]))
+    g = gg.gdla_backward(x, w, dims, dout)
+    for name, idx in (("x", (4, 3)), ("x", (0, 0)), ("w_qc", (2, 5)), ("w_uk", (1, 2)),
+                      ("w_kr", (3, 1)), ("w_lambda", (0, 2)), ("gamma_kv", (5,))):
+        base = x if name == "x" else w[name]
+        e = np.zeros(base.shape)
+        e[idx] = 1.0
+        fd = _loss_fd(ref_fwd, x, w, dims, dout, None, name, e)
+        an = float(g["d" + name][idx])
+        if not abs(fd - an) <= 1e-7 * max(1.0, abs(fd)):
+            raise AssertionError(f"d{name}{idx}: {an} vs finite difference {fd}")
+
+
+def pin_backward_lambda_zero(gg):
+    """With lambda fixed at 0 the noise heads do not reach the output: the columns of W_qc and W_qr
+    that feed the noise heads get exactly zero gradient, and so does every noise head's dH."""
+    import oracle.gdla_ref as ref_fwd
+    cfg, w, x, _ = small_problem(6, 4, 2, 2, seq=6, seed=91)
+    dims = make_dims(ref_fwd, cfg, 0)
+    dout = np.random.default_rng(92).standard_normal((6, cfg["d_model"]))
+    g = gg.gdla_backward(x, w, dims, dout, lam_override=np.zeros((6, 4)))
+    dh, dr = cfg["d_head"], cfg["d_rope"]
+    _close(g["dH"][:, 4:], np.zeros_like(g["dH"][:, 4:]), 0.0, "noise dH with lambda = 0")
+    _close(g["dw_qc"][:, 4 * dh:], np.zeros((cfg["d_q_latent"], 2 * dh)), 0.0, "noise W_qc grad")
+    _close(g["dw_qr"][:, 4 * dr:], np.zeros((cfg["d_q_latent"], 2 * dr)), 0.0, "noise W_qr grad")
+    if not np.all(np.abs(g["dw_qc"][:, :4 * dh]) > 0):
+        raise AssertionError("signal W_qc grad vanished")
+
+
+GRAD_PINS = [pin_backward_finite_differences, pin_backward_entries, pin_backward_lambda_zero]

@@ -7,7 +7,7 @@ import types
 
 import pytest
 
-from tests.oracle_pins import ALL_PINS
+from tests.oracle_pins import ALL_PINS, GRAD_PINS
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle",
                    "gdla_ref.py")
@@ -57,3 +57,38 @@ def test_planted_mistake_is_caught(name):
         except Exception as e:  # any failure of a pin counts as catching the mistake
             caught.append(f"{pin.__name__}: {type(e).__name__}")
     assert caught, f"planted mistake {name} escaped every pin"
+
+
+GRAD_SRC = os.path.join(os.path.dirname(SRC), "gdla_grad.py")
+
+GRAD_MUTATIONS = {
+    "softmax_backward_no_rowsum": ("ds = p * (dp - np.sum(dp * p, axis=1, keepdims=True))", "ds = p * dp"),
+    "rope_backward_same_angle": ("return ref.rope(du, -_f64(pos), theta)", "return ref.rope(du, _f64(pos), theta)"),
+    "rms_backward_first_term_only": ("dv = u / r - v * np.sum(u * v, axis=-1, keepdims=True) / (n * r ** 3)", "dv = u / r"),
+    "lambda_grad_sign": ("d_lam = -np.sum(d_d * h_n[:, partner], axis=2)", "d_lam = np.sum(d_d * h_n[:, partner], axis=2)"),
+    "noise_grad_missing": ("d_heads[:, ns + partner[i]] -= lam[:, i:i + 1] * d_d[:, i]", "pass"),
+    "gate_grad_without_sigmoid_slope": ("d_g = d_y * d * sg * (1.0 - sg)", "d_g = d_y * d"),
+    "shared_rotary_key_grad_last_head_only": ("d_kr += tau * ds.T @ q_r[:, h]", "d_kr = tau * ds.T @ q_r[:, h]"),
+    "value_grad_transposed": ("d_v[:, j] += p.T @ d_heads[:, h]", "d_v[:, j] += p @ d_heads[:, h]"),
+}
+
+
+def _grad_mutant(old, new):
+    with open(GRAD_SRC) as f:
+        src = f.read()
+    assert src.count(old) == 1, f"mutation anchor not unique/found: {old!r}"
+    mod = types.ModuleType("gdla_grad_mutant")
+    exec(compile(src.replace(old, new), "gdla_grad_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(GRAD_MUTATIONS))
+def test_planted_backward_mistake_is_caught(name):
+    mod = _grad_mutant(*GRAD_MUTATIONS[name])
+    caught = []
+    for pin in GRAD_PINS:
+        try:
+            pin(mod)
+        except Exception as e:
+            caught.append(f"{pin.__name__}: {type(e).__name__}")
+    assert caught, f"planted mistake {name} escaped every backward pin"
