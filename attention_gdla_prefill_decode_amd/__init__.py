@@ -4,8 +4,9 @@ The compute lives in libgdla.so (C ABI, include/gdla.h): hand-written HIP kernel
 This package is its thin Python binding; see gdla.py.
 """
 
-from .gdla import (EXPORTED, GDLA_BF16, GDLA_F32, GDLA_OP_APPEND, GDLA_OP_DECODE,  # noqa: F401
-                   GDLA_OP_PREFILL, GDLA_OP_PREFILL_PAGED, STAGES, GdlaDebug, StageTimer, GdlaDims,
+from .gdla import (EXPORTED, GDLA_BF16, GDLA_F32, GDLA_OP_APPEND, GDLA_OP_BACKWARD,  # noqa: F401
+                   GDLA_OP_DECODE, GDLA_OP_PREFILL, GDLA_OP_PREFILL_PAGED, GRAD_FIELDS, GdlaGrads,
+                   gdla_backward, STAGES, GdlaDebug, StageTimer, GdlaDims,
                    GdlaError, GdlaPagedCache, GdlaWeights, LIB_PATH, MAX_DECODE_TOKENS, PagedCache,
                    gdla_decode, gdla_decode_paged, gdla_decode_tokens, gdla_latent_append,
                    gdla_latent_append_paged, gdla_prefill, gdla_prefill_packed, gdla_prefill_paged,

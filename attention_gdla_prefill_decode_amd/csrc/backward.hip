@@ -1,0 +1,578 @@
+// Backward pass of one GDLA layer over training sequences (positions 0 .. T-1, no cached prefix):
+// the gradients of L = sum(out (.) dout) with respect to x and every weight.
+//
+// The pages train with GDLA layers and recompute each block's forward during the backward pass
+// (Motif 3 Technical Report, paperglide reader, section "Distributed Training System": activation
+// recomputation).  The forward is that of picx.dev summary section 2.2, Eq.(1)-(10); the
+// backward is its chain rule, taken in reverse order:
+//   Eq.(10)  out = vec(Y) W_O, Y = sigmoid(G) (.) D      -> dW_O, dY, dD, dG
+//   Eq.(8)   D_i = H_i - lambda_i H_(n_S + i mod n_N)    -> dH (signal and noise heads), dlambda
+//   both softmax maps, per head h with KV head kv(h):
+//            P = softmax(tau (q^C K^C^T + q^R k^R^T)) (masked), H = P V
+//            dP = dH V^T, dS = P (.) (dP - rowsum(dH (.) H)),
+//            dq^C = tau dS K^C, dq^R = tau dS k^R, dK^C += tau dS^T q^C, dk^R += tau dS^T q^R,
+//            dV += P^T dH  (K^C, V summed over the heads of a KV group; k^R over all heads)
+//   Eq.(5)   [K^C ; V] = cbar [W_uk | W_uv]              -> dcbar, dW_uk, dW_uv
+//   Eq.(4), (1)  RMSNorm: with u = dy (.) gamma, dv = u / r - v (u . v) / (n r^3)
+//   Eq.(2), (3)  RoPE: the backward rotates by the negative angle
+//   Eq.(7)   lambda = sigmoid(x W_lambda)
+//   Eq.(1)-(3), (7), (9)  the projections                -> dW_qa, dW_qc, dW_qr, dW_gate, dW_dkv,
+//                                                           dW_kr, dW_lambda, dx
+// This file is the general path: every step in fp32 (the recomputed forward included), any layer
+// sizes the forward's generic path takes, fp32 or bf16 storage.
+#include "gdla_internal.h"
+
+#include <math.h>
+
+namespace gdla {
+namespace {
+
+template <typename T> __device__ __forceinline__ float ldv(const T *p, int64_t i) { return (float)p[i]; }
+
+__device__ __forceinline__ float wsum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ------------------------------------------------------------------------------------------
+// C[M, N] (fp32, row stride ldc) = (beta ? C : 0) + op(A) op(B), op(A)[m, k] = A[m lda + k] or, with
+// a_t, A[k lda + m]; op(B)[k, n] = B[k ldb + n] or, with b_t, B[n ldb + k].  64 x 64 tiles,
+// 16-deep K slices in LDS, 4 x 4 outputs per thread.
+template <typename TA, typename TB>
+__global__ void __launch_bounds__(256) grad_gemm_kernel(const TA *A, int64_t lda, int a_t, const TB *B, int64_t ldb,
+                                                        int b_t, float *C, int64_t ldc, int M, int N, int K, int beta,
+                                                        int tiles_n) {
+  __shared__ float As[16][64 + 1];
+  __shared__ float Bs[16][64 + 1];
+  const int m0 = ((int)blockIdx.x / tiles_n) * 64, n0 = ((int)blockIdx.x % tiles_n) * 64;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    for (int i = threadIdx.x; i < 64 * 16; i += 256) {
+      // A tile: with a_t the 64 rows of op(A) are contiguous in memory, so threads run along m
+      int r, c;
+      if (a_t) { r = i & 63; c = i >> 6; } else { r = i >> 4; c = i & 15; }
+      const int gm = m0 + r, gk = k0 + c;
+      As[c][r] = (gm < M && gk < K) ? ldv(A, a_t ? (int64_t)gk * lda + gm : (int64_t)gm * lda + gk) : 0.f;
+      int kr, nc;
+      if (b_t) { kr = i & 15; nc = i >> 4; } else { kr = i >> 6; nc = i & 63; }
+      const int bk = k0 + kr, bn = n0 + nc;
+      Bs[kr][nc] = (bk < K && bn < N) ? ldv(B, b_t ? (int64_t)bn * ldb + bk : (int64_t)bk * ldb + bn) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + ty * 4 + i;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx * 4 + j;
+      if (n >= N) continue;
+      float *c = C + (int64_t)m * ldc + n;
+      *c = beta ? *c + acc[i][j] : acc[i][j];
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Recomputed forward, row-wise: c^Q = RMSNorm(aq) gamma_q, cbar = RMSNorm(ckv) gamma_kv (and the
+// inverse RMS of both rows), k^R = RoPE(krp, t), lambda = sigmoid(laml) or the override.
+__device__ __forceinline__ void rope_angle(int p, int j, int d_r, float theta, float &c, float &s) {
+  const double freq = pow((double)theta, -2.0 * (double)j / (double)d_r);
+  double a = (double)p * freq;
+  const double two_pi = 6.283185307179586476925286766559;
+  a -= floor(a / two_pi) * two_pi;
+  sincosf((float)a, &s, &c);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(64) bwd_prep_kernel(const float *aq, const float *ckv, const float *krp,
+                                                      const float *laml, const float *lam_override, const T *gq,
+                                                      const T *gkv, float *cq, float *cbar, float *kr, float *lam,
+                                                      float *rinv_q, float *rinv_kv, int32_t T_, LayerDims d) {
+  const int m = blockIdx.x, lane = threadIdx.x, t = m % T_;
+  float ss = 0.f;
+  for (int j = lane; j < d.d_cq; j += 64) ss += aq[(int64_t)m * d.d_cq + j] * aq[(int64_t)m * d.d_cq + j];
+  const float rq = 1.0f / sqrtf(wsum(ss) / d.d_cq + d.eps);
+  for (int j = lane; j < d.d_cq; j += 64)
+    cq[(int64_t)m * d.d_cq + j] = aq[(int64_t)m * d.d_cq + j] * rq * (gq ? ldv(gq, j) : 1.f);
+  ss = 0.f;
+  for (int j = lane; j < d.d_c; j += 64) ss += ckv[(int64_t)m * d.d_c + j] * ckv[(int64_t)m * d.d_c + j];
+  const float rk = 1.0f / sqrtf(wsum(ss) / d.d_c + d.eps);
+  for (int j = lane; j < d.d_c; j += 64)
+    cbar[(int64_t)m * d.d_c + j] = ckv[(int64_t)m * d.d_c + j] * rk * (gkv ? ldv(gkv, j) : 1.f);
+  const int half = d.d_r / 2;
+  for (int j = lane; j < half; j += 64) {
+    float c, s;
+    rope_angle(t, j, d.d_r, d.theta, c, s);
+    const float u = krp[(int64_t)m * d.d_r + j], v = krp[(int64_t)m * d.d_r + j + half];
+    kr[(int64_t)m * d.d_r + j] = u * c - v * s;
+    kr[(int64_t)m * d.d_r + j + half] = u * s + v * c;
+  }
+  for (int i = lane; i < d.n_signal; i += 64)
+    lam[(int64_t)m * d.n_signal + i] = lam_override ? lam_override[(int64_t)m * d.n_signal + i]
+                                                    : 1.0f / (1.0f + expf(-laml[(int64_t)m * d.n_signal + i]));
+  if (lane == 0) {
+    rinv_q[m] = rq;
+    rinv_kv[m] = rk;
+  }
+}
+
+// v [M, n_heads, d_r] rotated in place by +angle (sign = 1, RoPE) or -angle (sign = -1, its
+// backward); row m sits at position m % T.
+__global__ void __launch_bounds__(256) bwd_rope_kernel(float *v, int32_t M, int32_t T_, int32_t n_heads, int32_t d_r,
+                                                       float theta, float sign) {
+  const int half = d_r / 2;
+  const int64_t n = (int64_t)M * n_heads * half;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int j = (int)(i % half);
+    const int64_t mh = i / half;
+    const int t = (int)((mh / n_heads) % T_);
+    float c, s;
+    rope_angle(t, j, d_r, theta, c, s);
+    s *= sign;
+    float *r = v + mh * d_r;
+    const float u = r[j], w = r[j + half];
+    r[j] = u * c - w * s;
+    r[j + half] = u * s + w * c;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Attention (fp32, one wave per query row and head).  Visible keys of token t of a sequence:
+// lo(t) .. t with lo(t) = max(window start, document start).
+struct BwdAttn {
+  const float *qc, *qr;       // [M, n_H, d_h], [M, n_H, d_r]
+  const float *kc, *v;        // [M, n_kv, d_h]
+  const float *kr;            // [M, d_r]
+  const int32_t *doc;         // [M] or null
+  float *heads, *lse;         // [M, n_H, d_h], [M, n_H]
+  const float *dheads;        // [M, n_H, d_h]
+  const float *drow;          // [M, n_H]: rowsum(dH (.) H)
+  float *dqc, *dqr;           // [M, n_H, d_h], [M, n_H, d_r]
+  float *dkc, *dv;            // [M, n_kv, d_h]
+  float *dkr_part;            // [M, n_kv, d_r]: dk^R summed over the heads of each KV group
+  int32_t M, T;
+};
+
+constexpr int kMaxHd = 4;  // d_head <= 256 (chunks of 64 lanes)
+
+__device__ __forceinline__ int vis_lo(const BwdAttn &a, const LayerDims &d, int m, int t) {
+  int lo = d.window > 0 ? max(0, t - d.window + 1) : 0;
+  if (a.doc) lo = max(lo, min(max(a.doc[m], 0), t));
+  return lo;
+}
+
+// score of query row m (head h) against key row ms, scaled by tau
+__device__ __forceinline__ float score(const BwdAttn &a, const LayerDims &d, const float (&q)[kMaxHd], float qr,
+                                       int h, int ms, int lane) {
+  const int kv = kv_head_of(h, d.n_signal, d.n_kv);
+  const float *k = a.kc + ((int64_t)ms * d.n_kv + kv) * d.d_h;
+  float dot = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxHd; ++i) {
+    const int e = lane + 64 * i;
+    if (e < d.d_h) dot = fmaf(q[i], k[e], dot);
+  }
+  if (lane < d.d_r) dot = fmaf(qr, a.kr[(int64_t)ms * d.d_r + lane], dot);
+  return wsum(dot) * d.scale;
+}
+
+// H and the log-sum-exp of every (row, head)
+__global__ void __launch_bounds__(256) bwd_attn_fwd_kernel(BwdAttn a, LayerDims d) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wid >= (int64_t)a.M * d.n_heads) return;
+  const int m = (int)(wid / d.n_heads), h = (int)(wid % d.n_heads);
+  const int t = m % a.T, m0 = m - t;
+  const int kv = kv_head_of(h, d.n_signal, d.n_kv);
+  float q[kMaxHd], acc[kMaxHd];
+#pragma unroll
+  for (int i = 0; i < kMaxHd; ++i) {
+    const int e = lane + 64 * i;
+    q[i] = e < d.d_h ? a.qc[wid * d.d_h + e] : 0.f;
+    acc[i] = 0.f;
+  }
+  const float qr = lane < d.d_r ? a.qr[wid * d.d_r + lane] : 0.f;
+  float mx = -INFINITY, l = 0.f;
+  for (int s = vis_lo(a, d, m, t); s <= t; ++s) {
+    const float sc = score(a, d, q, qr, h, m0 + s, lane);
+    const float mn = fmaxf(mx, sc);
+    const float corr = expf(mx - mn), w = expf(sc - mn);
+    l = l * corr + w;
+    const float *vr = a.v + ((int64_t)(m0 + s) * d.n_kv + kv) * d.d_h;
+#pragma unroll
+    for (int i = 0; i < kMaxHd; ++i) {
+      const int e = lane + 64 * i;
+      if (e < d.d_h) acc[i] = acc[i] * corr + w * vr[e];
+    }
+    mx = mn;
+  }
+#pragma unroll
+  for (int i = 0; i < kMaxHd; ++i) {
+    const int e = lane + 64 * i;
+    if (e < d.d_h) a.heads[wid * d.d_h + e] = acc[i] / l;
+  }
+  if (lane == 0) a.lse[wid] = mx + logf(l);
+}
+
+// dq^C and dq^R of every (row, head): loop over the row's visible keys
+__global__ void __launch_bounds__(256) bwd_attn_dq_kernel(BwdAttn a, LayerDims d) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wid >= (int64_t)a.M * d.n_heads) return;
+  const int m = (int)(wid / d.n_heads), h = (int)(wid % d.n_heads);
+  const int t = m % a.T, m0 = m - t;
+  const int kv = kv_head_of(h, d.n_signal, d.n_kv);
+  float q[kMaxHd], dh[kMaxHd], dq[kMaxHd];
+#pragma unroll
+  for (int i = 0; i < kMaxHd; ++i) {
+    const int e = lane + 64 * i;
+    q[i] = e < d.d_h ? a.qc[wid * d.d_h + e] : 0.f;
+    dh[i] = e < d.d_h ? a.dheads[wid * d.d_h + e] : 0.f;
+    dq[i] = 0.f;
+  }
+  const float qr = lane < d.d_r ? a.qr[wid * d.d_r + lane] : 0.f;
+  const float lse = a.lse[wid], drow = a.drow[wid];
+  float dqr = 0.f;
+  for (int s = vis_lo(a, d, m, t); s <= t; ++s) {
+    const int ms = m0 + s;
+    const float p = expf(score(a, d, q, qr, h, ms, lane) - lse);
+    const float *vr = a.v + ((int64_t)ms * d.n_kv + kv) * d.d_h;
+    float dp = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxHd; ++i) {
+      const int e = lane + 64 * i;
+      if (e < d.d_h) dp = fmaf(dh[i], vr[e], dp);
+    }
+    const float ds = p * (wsum(dp) - drow) * d.scale;
+    const float *kr = a.kc + ((int64_t)ms * d.n_kv + kv) * d.d_h;
+#pragma unroll
+    for (int i = 0; i < kMaxHd; ++i) {
+      const int e = lane + 64 * i;
+      if (e < d.d_h) dq[i] = fmaf(ds, kr[e], dq[i]);
+    }
+    if (lane < d.d_r) dqr = fmaf(ds, a.kr[(int64_t)ms * d.d_r + lane], dqr);
+  }
+#pragma unroll
+  for (int i = 0; i < kMaxHd; ++i) {
+    const int e = lane + 64 * i;
+    if (e < d.d_h) a.dqc[wid * d.d_h + e] = dq[i];
+  }
+  if (lane < d.d_r) a.dqr[wid * d.d_r + lane] = dqr;
+}
+
+// dK^C, dV and the group's share of dk^R of every (key row, KV head): loop over the heads of the
+// group and the query rows that see the key
+__global__ void __launch_bounds__(256) bwd_attn_dkv_kernel(BwdAttn a, LayerDims d) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wid >= (int64_t)a.M * d.n_kv) return;
+  const int ms = (int)(wid / d.n_kv), kv = (int)(wid % d.n_kv);
+  const int s = ms % a.T, m0 = ms - s;
+  float k[kMaxHd], vv[kMaxHd], dk[kMaxHd], dvv[kMaxHd];
+#pragma unroll
+  for (int i = 0; i < kMaxHd; ++i) {
+    const int e = lane + 64 * i;
+    k[i] = e < d.d_h ? a.kc[wid * d.d_h + e] : 0.f;
+    vv[i] = e < d.d_h ? a.v[wid * d.d_h + e] : 0.f;
+    dk[i] = dvv[i] = 0.f;
+  }
+  const float kr = lane < d.d_r ? a.kr[(int64_t)ms * d.d_r + lane] : 0.f;
+  float dkr = 0.f;
+  const int t_end = d.window > 0 ? min(a.T - 1, s + d.window - 1) : a.T - 1;
+  for (int h = 0; h < d.n_heads; ++h) {
+    if (kv_head_of(h, d.n_signal, d.n_kv) != kv) continue;
+    for (int t = s; t <= t_end; ++t) {
+      const int m = m0 + t;
+      if (a.doc && min(max(a.doc[m], 0), t) > s) break;  // later tokens' documents start later still
+      const int64_t mh = (int64_t)m * d.n_heads + h;
+      float dot = 0.f, dp = 0.f;
+#pragma unroll
+      for (int i = 0; i < kMaxHd; ++i) {
+        const int e = lane + 64 * i;
+        if (e < d.d_h) {
+          dot = fmaf(a.qc[mh * d.d_h + e], k[i], dot);
+          dp = fmaf(a.dheads[mh * d.d_h + e], vv[i], dp);
+        }
+      }
+      if (lane < d.d_r) dot = fmaf(a.qr[mh * d.d_r + lane], kr, dot);
+      const float p = expf(wsum(dot) * d.scale - a.lse[mh]);
+      const float ds = p * (wsum(dp) - a.drow[mh]) * d.scale;
+#pragma unroll
+      for (int i = 0; i < kMaxHd; ++i) {
+        const int e = lane + 64 * i;
+        if (e < d.d_h) {
+          dk[i] = fmaf(ds, a.qc[mh * d.d_h + e], dk[i]);
+          dvv[i] = fmaf(p, a.dheads[mh * d.d_h + e], dvv[i]);
+        }
+      }
+      if (lane < d.d_r) dkr = fmaf(ds, a.qr[mh * d.d_r + lane], dkr);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kMaxHd; ++i) {
+    const int e = lane + 64 * i;
+    if (e < d.d_h) {
+      a.dkc[wid * d.d_h + e] = dk[i];
+      a.dv[wid * d.d_h + e] = dvv[i];
+    }
+  }
+  if (lane < d.d_r) a.dkr_part[wid * d.d_r + lane] = dkr;
+}
+
+// dk^R[m] = sum over KV groups of their shares
+__global__ void __launch_bounds__(256) bwd_sum_groups_kernel(const float *part, float *out, int32_t M, int32_t n_kv,
+                                                             int32_t d_r) {
+  const int64_t n = (int64_t)M * d_r;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t m = i / d_r;
+    const int j = (int)(i % d_r);
+    float acc = 0.f;
+    for (int g = 0; g < n_kv; ++g) acc += part[(m * n_kv + g) * d_r + j];
+    out[i] = acc;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Eq.(8)-(10) forward and backward per row, element (i, e) of the signal heads:
+//   sg = sigmoid(G), D = H_i - lambda_i H_(n_S + i mod n_N), Y = sg D;
+//   dD = dY sg, dG = dY D sg (1 - sg), dH_i = dD.
+// Y goes out in fp32 (the W_O gradient's operand); noise-head dH and dlambda are reduced below.
+__global__ void __launch_bounds__(256) bwd_combine_kernel(const float *heads, const float *lam, const float *g,
+                                                          const float *dy, float *y, float *dheads, float *dd,
+                                                          float *dg, int32_t M, LayerDims d) {
+  const int64_t n = (int64_t)M * d.n_signal * d.d_h;
+  for (int64_t idx = blockIdx.x * 256ll + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * 256) {
+    const int e = (int)(idx % d.d_h);
+    const int64_t r = idx / d.d_h;
+    const int i = (int)(r % d.n_signal);
+    const int64_t m = r / d.n_signal;
+    const float hs = heads[(m * d.n_heads + i) * d.d_h + e];
+    const float hn = heads[(m * d.n_heads + d.n_signal + i % d.n_noise) * d.d_h + e];
+    const float dval = hs - lam[m * d.n_signal + i] * hn;
+    const float sg = 1.0f / (1.0f + expf(-g[idx]));
+    y[idx] = sg * dval;
+    const float ddv = dy[idx] * sg;
+    dd[idx] = ddv;
+    dg[idx] = dy[idx] * dval * sg * (1.0f - sg);
+    dheads[(m * d.n_heads + i) * d.d_h + e] = ddv;
+  }
+}
+
+// noise head j: dH = -sum over the signal heads i = j (mod n_N) of lambda_i dD_i; and
+// dlambda_i = -sum_e dD_i,e H_(n_S + i mod n_N),e, then through the sigmoid unless overridden
+__global__ void __launch_bounds__(256) bwd_noise_lambda_kernel(const float *heads, const float *lam, const float *dd,
+                                                               float *dheads, float *dlam_logit, int override_lam,
+                                                               int32_t M, LayerDims d) {
+  const int64_t nn = (int64_t)M * d.n_noise * d.d_h;
+  const int64_t nl = (int64_t)M * d.n_signal;
+  for (int64_t idx = blockIdx.x * 256ll + threadIdx.x; idx < nn + nl; idx += (int64_t)gridDim.x * 256) {
+    if (idx < nn) {
+      const int e = (int)(idx % d.d_h);
+      const int64_t r = idx / d.d_h;
+      const int j = (int)(r % d.n_noise);
+      const int64_t m = r / d.n_noise;
+      float acc = 0.f;
+      for (int i = j; i < d.n_signal; i += d.n_noise)
+        acc -= lam[m * d.n_signal + i] * dd[(m * d.n_signal + i) * d.d_h + e];
+      dheads[(m * d.n_heads + d.n_signal + j) * d.d_h + e] = acc;
+    } else {
+      const int64_t r = idx - nn;
+      const int i = (int)(r % d.n_signal);
+      const int64_t m = r / d.n_signal;
+      const float *hn = heads + (m * d.n_heads + d.n_signal + i % d.n_noise) * d.d_h;
+      const float *ddi = dd + r * d.d_h;
+      float acc = 0.f;
+      for (int e = 0; e < d.d_h; ++e) acc -= ddi[e] * hn[e];
+      const float l = lam[r];
+      dlam_logit[r] = override_lam ? 0.f : acc * l * (1.0f - l);
+    }
+  }
+}
+
+// drow[m, h] = sum_e dH (.) H
+__global__ void __launch_bounds__(256) bwd_drow_kernel(const float *heads, const float *dheads, float *drow,
+                                                       int64_t rows, int32_t d_h) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  float acc = 0.f;
+  for (int e = lane; e < d_h; e += 64) acc += heads[r * d_h + e] * dheads[r * d_h + e];
+  acc = wsum(acc);
+  if (lane == 0) drow[r] = acc;
+}
+
+// RMSNorm backward of y = v rinv (.) gamma per row: dv = rinv (u - v rinv^2 (u . v) / n), u = dy (.) gamma
+template <typename T>
+__global__ void __launch_bounds__(64) bwd_rms_kernel(const float *v, const float *rinv, const T *gamma, const float *dy,
+                                                     float *dv, int32_t n) {
+  const int64_t m = blockIdx.x;
+  const int lane = threadIdx.x;
+  const float r = rinv[m];
+  float uv = 0.f;
+  for (int j = lane; j < n; j += 64) uv += dy[m * n + j] * (gamma ? ldv(gamma, j) : 1.f) * v[m * n + j];
+  uv = wsum(uv);
+  for (int j = lane; j < n; j += 64) {
+    const float u = dy[m * n + j] * (gamma ? ldv(gamma, j) : 1.f);
+    dv[m * n + j] = r * (u - v[m * n + j] * r * r * uv / n);
+  }
+}
+
+// dgamma[j] = sum over rows of dy (.) v rinv (column sums, fixed order)
+__global__ void __launch_bounds__(256) bwd_dgamma_kernel(const float *v, const float *rinv, const float *dy,
+                                                         float *dgamma, int32_t M, int32_t n) {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= n) return;
+  float acc = 0.f;
+  for (int m = 0; m < M; ++m) acc += dy[(int64_t)m * n + j] * v[(int64_t)m * n + j] * rinv[m];
+  dgamma[j] = acc;
+}
+
+unsigned grid_for(int64_t n) { return (unsigned)std::min<int64_t>((n + 255) / 256, 65536); }
+
+template <typename TA, typename TB>
+hipError_t gg(const TA *A, int64_t lda, bool a_t, const TB *B, int64_t ldb, bool b_t, float *C, int64_t ldc, int M,
+              int N, int K, bool beta, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  const int tn = (N + 63) / 64, tm = (M + 63) / 64;
+  hipLaunchKernelGGL((grad_gemm_kernel<TA, TB>), dim3((unsigned)(tm * tn)), dim3(256), 0, s, A, lda, a_t ? 1 : 0, B,
+                     ldb, b_t ? 1 : 0, C, ldc, M, N, K, beta ? 1 : 0, tn);
+  return hipGetLastError();
+}
+
+#define BWD_TRY(expr)                       \
+  do {                                      \
+    const hipError_t e_ = (expr);           \
+    if (e_ != hipSuccess) return e_;        \
+  } while (0)
+
+template <typename T>
+hipError_t backward_t(const BackwardArgs &ba, const LayerDims &d, hipStream_t s) {
+  const int M = ba.M, T_ = ba.T;
+  const T *x = (const T *)ba.x;
+  const gdla_weights &w = *ba.w;
+  const T *Wqa = (const T *)w.w_qa, *Wqc = (const T *)w.w_qc, *Wqr = (const T *)w.w_qr;
+  const T *Wdkv = (const T *)w.w_dkv, *Wkr = (const T *)w.w_kr, *Wuk = (const T *)w.w_uk, *Wuv = (const T *)w.w_uv;
+  const T *Wl = (const T *)w.w_lambda, *Wg = (const T *)w.w_gate, *Wo = (const T *)w.w_o;
+  const T *gq = (const T *)w.gamma_q, *gkv = (const T *)w.gamma_kv;
+  const int dm = d.d_model, dcq = d.d_cq, dc = d.d_c, dr = d.d_r, dh = d.d_h;
+  const int nH = d.n_heads, nS = d.n_signal, nKV = d.n_kv;
+  const BwdBuffers &b = ba.buf;
+
+  // ---- recomputed forward (fp32)
+  BWD_TRY(gg(x, dm, false, Wqa, dcq, false, b.aq, dcq, M, dcq, dm, false, s));
+  BWD_TRY(gg(x, dm, false, Wdkv, dc, false, b.ckv, dc, M, dc, dm, false, s));
+  BWD_TRY(gg(x, dm, false, Wkr, dr, false, b.krp, dr, M, dr, dm, false, s));
+  BWD_TRY(gg(x, dm, false, Wl, nS, false, b.laml, nS, M, nS, dm, false, s));
+  hipLaunchKernelGGL((bwd_prep_kernel<T>), dim3(M), dim3(64), 0, s, b.aq, b.ckv, b.krp, b.laml, ba.lam_override, gq,
+                     gkv, b.cq, b.cbar, b.kr, b.lam, b.rq, b.rkv, T_, d);
+  BWD_TRY(hipGetLastError());
+  BWD_TRY(gg(b.cq, dcq, false, Wqc, (int64_t)nH * dh, false, b.qc, (int64_t)nH * dh, M, nH * dh, dcq, false, s));
+  BWD_TRY(gg(b.cq, dcq, false, Wqr, (int64_t)nH * dr, false, b.qr, (int64_t)nH * dr, M, nH * dr, dcq, false, s));
+  hipLaunchKernelGGL(bwd_rope_kernel, dim3(grid_for((int64_t)M * nH * dr / 2)), dim3(256), 0, s, b.qr, M, T_, nH, dr,
+                     d.theta, 1.0f);
+  BWD_TRY(hipGetLastError());
+  BWD_TRY(gg(b.cq, dcq, false, Wg, (int64_t)nS * dh, false, b.g, (int64_t)nS * dh, M, nS * dh, dcq, false, s));
+  BWD_TRY(gg(b.cbar, dc, false, Wuk, (int64_t)nKV * dh, false, b.kc, (int64_t)nKV * dh, M, nKV * dh, dc, false, s));
+  BWD_TRY(gg(b.cbar, dc, false, Wuv, (int64_t)nKV * dh, false, b.v, (int64_t)nKV * dh, M, nKV * dh, dc, false, s));
+  BwdAttn at{};
+  at.qc = b.qc; at.qr = b.qr; at.kc = b.kc; at.v = b.v; at.kr = b.kr; at.doc = ba.doc;
+  at.heads = b.heads; at.lse = b.lse; at.dheads = b.dheads; at.drow = b.drow;
+  at.dqc = b.dqc; at.dqr = b.dqr; at.dkc = b.dkc; at.dv = b.dv; at.dkr_part = b.dkr_part;
+  at.M = M; at.T = T_;
+  const unsigned gh = (unsigned)(((int64_t)M * nH + 3) / 4);
+  hipLaunchKernelGGL(bwd_attn_fwd_kernel, dim3(gh), dim3(256), 0, s, at, d);
+  BWD_TRY(hipGetLastError());
+
+  // ---- Eq.(10): dY = dout W_O^T, and dW_O = Y^T dout once Y is known
+  const T *dout = (const T *)ba.dout;
+  BWD_TRY(gg(dout, dm, false, Wo, dm, true, b.dy, (int64_t)nS * dh, M, nS * dh, dm, false, s));
+  const int64_t nsig = (int64_t)M * nS * dh;
+  hipLaunchKernelGGL(bwd_combine_kernel, dim3(grid_for(nsig)), dim3(256), 0, s, b.heads, b.lam, b.g, b.dy, b.y,
+                     b.dheads, b.dd, b.dg, M, d);
+  BWD_TRY(hipGetLastError());
+  BWD_TRY(gg(b.y, (int64_t)nS * dh, true, dout, dm, false, ba.grads.dw_o, dm, nS * dh, dm, M, false, s));
+  // ---- Eq.(8): noise-head dH and dlambda
+  hipLaunchKernelGGL(bwd_noise_lambda_kernel, dim3(grid_for((int64_t)M * d.n_noise * dh + (int64_t)M * nS)), dim3(256),
+                     0, s, b.heads, b.lam, b.dd, b.dheads, b.dlaml, ba.lam_override ? 1 : 0, M, d);
+  BWD_TRY(hipGetLastError());
+  // ---- the softmax maps
+  hipLaunchKernelGGL(bwd_drow_kernel, dim3(gh), dim3(256), 0, s, b.heads, b.dheads, b.drow, (int64_t)M * nH, dh);
+  BWD_TRY(hipGetLastError());
+  hipLaunchKernelGGL(bwd_attn_dq_kernel, dim3(gh), dim3(256), 0, s, at, d);
+  BWD_TRY(hipGetLastError());
+  hipLaunchKernelGGL(bwd_attn_dkv_kernel, dim3((unsigned)(((int64_t)M * nKV + 3) / 4)), dim3(256), 0, s, at, d);
+  BWD_TRY(hipGetLastError());
+  hipLaunchKernelGGL(bwd_sum_groups_kernel, dim3(grid_for((int64_t)M * dr)), dim3(256), 0, s, b.dkr_part, b.dkr, M,
+                     nKV, dr);
+  BWD_TRY(hipGetLastError());
+  // RoPE backward of dq^R and dk^R (in place)
+  hipLaunchKernelGGL(bwd_rope_kernel, dim3(grid_for((int64_t)M * nH * dr / 2)), dim3(256), 0, s, b.dqr, M, T_, nH, dr,
+                     d.theta, -1.0f);
+  BWD_TRY(hipGetLastError());
+  hipLaunchKernelGGL(bwd_rope_kernel, dim3(grid_for((int64_t)M * dr / 2)), dim3(256), 0, s, b.dkr, M, T_, 1, dr,
+                     d.theta, -1.0f);
+  BWD_TRY(hipGetLastError());
+
+  // ---- Eq.(5), (4): the latent
+  const gdla_grads &G = ba.grads;
+  BWD_TRY(gg(b.cbar, dc, true, b.dkc, (int64_t)nKV * dh, false, G.dw_uk, (int64_t)nKV * dh, dc, nKV * dh, M, false, s));
+  BWD_TRY(gg(b.cbar, dc, true, b.dv, (int64_t)nKV * dh, false, G.dw_uv, (int64_t)nKV * dh, dc, nKV * dh, M, false, s));
+  BWD_TRY(gg(b.dkc, (int64_t)nKV * dh, false, Wuk, (int64_t)nKV * dh, true, b.dcbar, dc, M, dc, nKV * dh, false, s));
+  BWD_TRY(gg(b.dv, (int64_t)nKV * dh, false, Wuv, (int64_t)nKV * dh, true, b.dcbar, dc, M, dc, nKV * dh, true, s));
+  hipLaunchKernelGGL((bwd_rms_kernel<T>), dim3(M), dim3(64), 0, s, b.ckv, b.rkv, gkv, b.dcbar, b.dckv, dc);
+  BWD_TRY(hipGetLastError());
+  if (G.dgamma_kv) {
+    hipLaunchKernelGGL(bwd_dgamma_kernel, dim3((dc + 255) / 256), dim3(256), 0, s, b.ckv, b.rkv, b.dcbar,
+                       G.dgamma_kv, M, dc);
+    BWD_TRY(hipGetLastError());
+  }
+  // ---- Eq.(2), (9), (1): the query latent
+  BWD_TRY(gg(b.cq, dcq, true, b.dqc, (int64_t)nH * dh, false, G.dw_qc, (int64_t)nH * dh, dcq, nH * dh, M, false, s));
+  BWD_TRY(gg(b.cq, dcq, true, b.dqr, (int64_t)nH * dr, false, G.dw_qr, (int64_t)nH * dr, dcq, nH * dr, M, false, s));
+  BWD_TRY(gg(b.cq, dcq, true, b.dg, (int64_t)nS * dh, false, G.dw_gate, (int64_t)nS * dh, dcq, nS * dh, M, false, s));
+  BWD_TRY(gg(b.dqc, (int64_t)nH * dh, false, Wqc, (int64_t)nH * dh, true, b.dcq, dcq, M, dcq, nH * dh, false, s));
+  BWD_TRY(gg(b.dqr, (int64_t)nH * dr, false, Wqr, (int64_t)nH * dr, true, b.dcq, dcq, M, dcq, nH * dr, true, s));
+  BWD_TRY(gg(b.dg, (int64_t)nS * dh, false, Wg, (int64_t)nS * dh, true, b.dcq, dcq, M, dcq, nS * dh, true, s));
+  hipLaunchKernelGGL((bwd_rms_kernel<T>), dim3(M), dim3(64), 0, s, b.aq, b.rq, gq, b.dcq, b.daq, dcq);
+  BWD_TRY(hipGetLastError());
+  if (G.dgamma_q) {
+    hipLaunchKernelGGL(bwd_dgamma_kernel, dim3((dcq + 255) / 256), dim3(256), 0, s, b.aq, b.rq, b.dcq, G.dgamma_q, M,
+                       dcq);
+    BWD_TRY(hipGetLastError());
+  }
+  // ---- x and the x-side weights
+  BWD_TRY(gg(x, dm, true, b.daq, dcq, false, G.dw_qa, dcq, dm, dcq, M, false, s));
+  BWD_TRY(gg(x, dm, true, b.dckv, dc, false, G.dw_dkv, dc, dm, dc, M, false, s));
+  BWD_TRY(gg(x, dm, true, b.dkr, dr, false, G.dw_kr, dr, dm, dr, M, false, s));
+  BWD_TRY(gg(x, dm, true, b.dlaml, nS, false, G.dw_lambda, nS, dm, nS, M, false, s));
+  BWD_TRY(gg(b.daq, dcq, false, Wqa, dcq, true, G.dx, dm, M, dm, dcq, false, s));
+  BWD_TRY(gg(b.dckv, dc, false, Wdkv, dc, true, G.dx, dm, M, dm, dc, true, s));
+  BWD_TRY(gg(b.dkr, dr, false, Wkr, dr, true, G.dx, dm, M, dm, dr, true, s));
+  BWD_TRY(gg(b.dlaml, nS, false, Wl, nS, true, G.dx, dm, M, dm, nS, true, s));
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_backward_generic(const BackwardArgs &a, const LayerDims &d, DT dt, hipStream_t s) {
+  return dt == DT::F32 ? backward_t<float>(a, d, s) : backward_t<bf16_t>(a, d, s);
+}
+
+}  // namespace gdla

@@ -223,6 +223,29 @@ PagedPrefillLayout plan_prefill_paged(const LayerDims &d, gdla_dtype dt, int32_t
   return L;
 }
 
+// Workspace of the backward: fp32 buffers of M = B T rows (fields of BwdBuffers, in order).
+struct BackwardLayout {
+  size_t off[34];
+  size_t total;
+};
+
+BackwardLayout plan_backward(const LayerDims &d, int32_t B, int32_t T) {
+  const size_t M = (size_t)B * T;
+  const size_t nH = d.n_heads, nS = d.n_signal, nKV = d.n_kv;
+  const size_t cols[34] = {
+      (size_t)d.d_cq, (size_t)d.d_c, (size_t)d.d_r, nS, (size_t)d.d_cq, (size_t)d.d_c, (size_t)d.d_r, nS, 1, 1,
+      nH * d.d_h, nH * d.d_r, nS * d.d_h, nKV * d.d_h, nKV * d.d_h, nH * d.d_h, nH,
+      nS * d.d_h, nS * d.d_h, nH * d.d_h, nS * d.d_h, nS * d.d_h, nS, nH,
+      nH * d.d_h, nH * d.d_r, nKV * d.d_h, nKV * d.d_h, nKV * d.d_r, (size_t)d.d_r, (size_t)d.d_c, (size_t)d.d_c,
+      (size_t)d.d_cq, (size_t)d.d_cq};
+  static_assert(sizeof(BwdBuffers) == 34 * sizeof(float *), "one column count per buffer");
+  BackwardLayout L{};
+  Plan p;
+  for (int i = 0; i < 34; ++i) L.off[i] = p.add(4 * M * cols[i]);
+  L.total = p.bytes;
+  return L;
+}
+
 // ---------------------------------------------------------------------------------------------
 gdla_status check_call(const gdla_dims *dims, const gdla_weights *w, const void *x, int32_t B,
                        int32_t T, const int32_t *pos, const void *cache, int32_t max_len,
@@ -395,6 +418,7 @@ GDLA_EXPORT size_t gdla_workspace_bytes(const gdla_dims *dims, int32_t op, int32
     case GDLA_OP_DECODE: return plan_decode(d, dims->dtype, B, T, max_len).total;
     case GDLA_OP_APPEND: return plan_append(d, B, T).total;
     case GDLA_OP_PREFILL_PAGED: return plan_prefill_paged(d, dims->dtype, B, T, pos_host, max_len).total;
+    case GDLA_OP_BACKWARD: return plan_backward(d, B, T).total;
     default: return 0;
   }
 }
@@ -756,4 +780,47 @@ GDLA_EXPORT gdla_status gdla_decode_paged(const gdla_dims *dims, const gdla_weig
   const gdla_status st = paged_ref(cache, c);
   if (st != GDLA_OK) return st;
   return decode_impl(dims, w, x, B, T, pos_host, c, out, ws, ws_bytes, dbg, stream);
+}
+
+GDLA_EXPORT gdla_status gdla_backward(const gdla_dims *dims, const gdla_weights *w, const void *x, int32_t B,
+                                      int32_t T, const int32_t *doc_start, const void *dout,
+                                      const gdla_grads *grads, void *ws, size_t ws_bytes, const gdla_debug *dbg,
+                                      hipStream_t stream) {
+  g_err[0] = 0;
+  LayerDims d;
+  gdla_status st = check_dims(dims, d);
+  if (st != GDLA_OK) return st;
+  if (B < 0 || T < 0) return fail(GDLA_ERR_INVALID_ARG, "negative B or T");
+  if (B == 0 || T == 0) return GDLA_OK;
+  if (!w || !grads) return fail(GDLA_ERR_INVALID_ARG, "weights or grads is NULL");
+  if (!x || !dout) return fail(GDLA_ERR_INVALID_ARG, "x or dout is NULL");
+  const void *req[] = {w->w_qa, w->w_qc, w->w_qr, w->w_dkv, w->w_kr, w->w_uk, w->w_uv, w->w_lambda, w->w_gate, w->w_o};
+  for (const void *p : req)
+    if (!p) return fail(GDLA_ERR_INVALID_ARG, "a required weight pointer is NULL");
+  const void *al[] = {x, dout, w->w_qa, w->w_qc, w->w_qr, w->w_dkv, w->w_kr, w->w_uk, w->w_uv, w->w_lambda,
+                      w->w_gate, w->w_o, w->gamma_q, w->gamma_kv};
+  for (const void *p : al)
+    if (p && !aligned16(p)) return fail(GDLA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  const float *gp_[] = {grads->dx, grads->dw_qa, grads->dw_qc, grads->dw_qr, grads->dw_dkv, grads->dw_kr,
+                        grads->dw_uk, grads->dw_uv, grads->dw_lambda, grads->dw_gate, grads->dw_o};
+  for (const float *p : gp_)
+    if (!p) return fail(GDLA_ERR_INVALID_ARG, "a gradient pointer is NULL");
+  if ((w->gamma_q && !grads->dgamma_q) || (w->gamma_kv && !grads->dgamma_kv))
+    return fail(GDLA_ERR_INVALID_ARG, "dgamma_q / dgamma_kv are required with gamma_q / gamma_kv");
+  if (((uintptr_t)doc_start & 3u) != 0) return fail(GDLA_ERR_INVALID_ARG, "doc_start must be 4-byte aligned");
+  if (d.d_h > 256) return fail(GDLA_ERR_UNSUPPORTED, "d_head > 256");
+  const BackwardLayout L = plan_backward(d, B, T);
+  if ((st = check_ws(ws, ws_bytes, L.total)) != GDLA_OK) return st;
+  BackwardArgs a{};
+  a.x = x; a.dout = dout; a.w = w; a.doc = doc_start;
+  a.lam_override = dbg ? dbg->lambda_override : nullptr;
+  a.grads = *grads;
+  if (!w->gamma_q) a.grads.dgamma_q = nullptr;
+  if (!w->gamma_kv) a.grads.dgamma_kv = nullptr;
+  float **bufs = (float **)&a.buf;
+  for (int i = 0; i < 34; ++i) bufs[i] = at<float>(ws, L.off[i]);
+  a.M = B * T;
+  a.T = T;
+  HIP_TRY(launch_backward_generic(a, d, dims->dtype == GDLA_F32 ? DT::F32 : DT::BF16, stream));
+  return GDLA_OK;
 }

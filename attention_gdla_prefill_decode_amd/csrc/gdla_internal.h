@@ -176,6 +176,25 @@ hipError_t launch_unabsorb_generic(const float *o, const void *w_uv, float *head
 hipError_t launch_copy_cache_rows(const CacheRef &src, const CacheRef &dst, const int32_t *pos_dev, int32_t B,
                                   int32_t max_rows, bool scatter, int32_t T, int32_t window, int64_t row_bytes,
                                   hipStream_t s);
+// ---------------- backward (training sequences at positions 0 .. T-1) ----------------------
+// fp32 work buffers of the general backward path, each [M, ...] with M = B T rows.
+struct BwdBuffers {
+  float *aq, *ckv, *krp, *laml, *cq, *cbar, *kr, *lam, *rq, *rkv;
+  float *qc, *qr, *g, *kc, *v, *heads, *lse;
+  float *dy, *y, *dheads, *dd, *dg, *dlaml, *drow;
+  float *dqc, *dqr, *dkc, *dv, *dkr_part, *dkr, *dcbar, *dckv, *dcq, *daq;
+};
+struct BackwardArgs {
+  const void *x, *dout;        // [M, d_model] in the layer dtype
+  const gdla_weights *w;
+  const int32_t *doc;          // [M] document starts or null
+  const float *lam_override;   // [M, n_S] or null
+  gdla_grads grads;
+  BwdBuffers buf;
+  int32_t M, T;
+};
+hipError_t launch_backward_generic(const BackwardArgs &a, const LayerDims &d, DT dt, hipStream_t s);
+
 // Copies up to 128 host values into a device int32 array through kernel arguments, so that no
 // host-to-device copy (and no pinned host buffer) is needed.
 hipError_t launch_set_i32(int32_t *dst, const int32_t *src_host, int32_t n, hipStream_t s);

@@ -16,14 +16,18 @@ LIB_PATH = os.path.join(_PKG, "libgdla.so")
 GDLA_OK, GDLA_ERR_INVALID_ARG, GDLA_ERR_UNSUPPORTED, GDLA_ERR_WORKSPACE, GDLA_ERR_OUT_OF_RANGE, \
     GDLA_ERR_HIP = range(6)
 GDLA_F32, GDLA_BF16 = 0, 1
-GDLA_OP_PREFILL, GDLA_OP_DECODE, GDLA_OP_APPEND, GDLA_OP_PREFILL_PAGED = 0, 1, 2, 3
+GDLA_OP_PREFILL, GDLA_OP_DECODE, GDLA_OP_APPEND, GDLA_OP_PREFILL_PAGED, GDLA_OP_BACKWARD = 0, 1, 2, 3, 4
+
+GRAD_FIELDS = ("dx", "dw_qa", "dw_qc", "dw_qr", "dw_dkv", "dw_kr", "dw_uk", "dw_uv", "dw_lambda",
+               "dw_gate", "dw_o", "dgamma_q", "dgamma_kv")
 
 WEIGHT_FIELDS = ("w_qa", "gamma_q", "w_qc", "w_qr", "w_dkv", "w_kr", "gamma_kv", "w_uk", "w_uv",
                  "w_lambda", "w_gate", "w_o")
 
 EXPORTED = ("gdla_workspace_bytes", "gdla_latent_append", "gdla_prefill", "gdla_decode",
             "gdla_decode_tokens", "gdla_prefill_packed", "gdla_latent_append_paged",
-            "gdla_prefill_paged", "gdla_decode_paged", "gdla_status_string", "gdla_last_error")
+            "gdla_prefill_paged", "gdla_decode_paged", "gdla_backward", "gdla_status_string",
+            "gdla_last_error")
 
 MAX_DECODE_TOKENS = 16  # GDLA_MAX_DECODE_TOKENS
 
@@ -46,6 +50,10 @@ class GdlaPagedCache(ctypes.Structure):
     _fields_ = [("pages", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
                 ("n_pages", ctypes.c_int32), ("page_rows", ctypes.c_int32),
                 ("max_blocks", ctypes.c_int32)]
+
+
+class GdlaGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in GRAD_FIELDS]
 
 
 class GdlaDebug(ctypes.Structure):
@@ -151,6 +159,10 @@ def lib():
             f.argtypes = [P(GdlaDims), P(GdlaWeights), ctypes.c_void_p, ctypes.c_int32,
                           ctypes.c_int32, ctypes.c_void_p, P(GdlaPagedCache), ctypes.c_void_p,
                           ctypes.c_void_p, ctypes.c_size_t, P(GdlaDebug), ctypes.c_void_p]
+        L.gdla_backward.restype = ctypes.c_int
+        L.gdla_backward.argtypes = [P(GdlaDims), P(GdlaWeights), ctypes.c_void_p, ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, P(GdlaGrads),
+                                    ctypes.c_void_p, ctypes.c_size_t, P(GdlaDebug), ctypes.c_void_p]
         L.gdla_status_string.restype = ctypes.c_char_p
         L.gdla_status_string.argtypes = [ctypes.c_int]
         L.gdla_last_error.restype = ctypes.c_char_p
@@ -347,3 +359,30 @@ def gdla_decode_paged(dims, weights, x, pos, cache, out=None, ws=None, lambda_ov
                                    nbytes, None if dbg is None else ctypes.byref(dbg),
                                    _stream(stream)))
     return out
+
+
+def gdla_backward(dims, weights, tensors, x, dout, doc_start=None, ws=None, lambda_override=None,
+                  stream=None, timer=None):
+    """Gradients of sum(out * dout) for training sequences x [B, T, d_model] at positions 0..T-1.
+    `tensors` maps the weight names (as for make_weights) to the weight tensors, which give the
+    gradient shapes.  Returns a dict of fp32 gradients (GRAD_FIELDS; the gamma gradients only for
+    the gains that are set)."""
+    B, T = x.shape[0], x.shape[1]
+    dev = x.device
+    grads = {"dx": torch.empty((B, T, x.shape[2]), dtype=torch.float32, device=dev)}
+    for name in ("w_qa", "w_qc", "w_qr", "w_dkv", "w_kr", "w_uk", "w_uv", "w_lambda", "w_gate", "w_o"):
+        grads["d" + name] = torch.empty(tuple(tensors[name].shape), dtype=torch.float32, device=dev)
+    for name in ("gamma_q", "gamma_kv"):
+        if tensors.get(name) is not None:
+            grads["d" + name] = torch.empty(tuple(tensors[name].shape), dtype=torch.float32, device=dev)
+    gs = GdlaGrads(*[None if grads.get(n) is None else grads[n].data_ptr() for n in GRAD_FIELDS])
+    ws, nbytes = _workspace(dims, GDLA_OP_BACKWARD, B, T, None, T, ws, dev)
+    if doc_start is not None:
+        assert doc_start.dtype == torch.int32 and tuple(doc_start.shape) == (B, T)
+        doc_start = doc_start.contiguous()
+    dbg = _debug(lambda_override, None, timer)
+    _check(lib().gdla_backward(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B, T,
+                               None if doc_start is None else _ptr(doc_start), _ptr(dout),
+                               ctypes.byref(gs), _ptr(ws), nbytes,
+                               None if dbg is None else ctypes.byref(dbg), _stream(stream)))
+    return grads

@@ -70,7 +70,8 @@ typedef enum {
   GDLA_OP_PREFILL = 0,
   GDLA_OP_DECODE = 1,        /* gdla_decode, gdla_decode_tokens and gdla_decode_paged */
   GDLA_OP_APPEND = 2,        /* gdla_latent_append and gdla_latent_append_paged */
-  GDLA_OP_PREFILL_PAGED = 3  /* gdla_prefill_paged (max_len = max_blocks * page_rows) */
+  GDLA_OP_PREFILL_PAGED = 3, /* gdla_prefill_paged (max_len = max_blocks * page_rows) */
+  GDLA_OP_BACKWARD = 4       /* gdla_backward (pos_host NULL, max_len = T) */
 } gdla_op;
 
 /* Most new tokens per sequence that gdla_decode_tokens takes in one call. */
@@ -241,6 +242,31 @@ gdla_status gdla_decode_paged(const gdla_dims *dims, const gdla_weights *w, cons
                               int32_t B, int32_t T, const int32_t *pos_host,
                               const gdla_paged_cache *cache, void *out, void *ws, size_t ws_bytes,
                               const gdla_debug *dbg, hipStream_t stream);
+
+/* Gradient outputs of gdla_backward: fp32 device buffers shaped like the corresponding input,
+ * fully overwritten (weight gradients are sums over all B * T tokens). */
+typedef struct {
+  float *dx;                                       /* [B, T, d_model] */
+  float *dw_qa, *dw_qc, *dw_qr, *dw_dkv, *dw_kr;   /* shaped like w_qa, w_qc, w_qr, w_dkv, w_kr */
+  float *dw_uk, *dw_uv, *dw_lambda, *dw_gate, *dw_o;
+  float *dgamma_q, *dgamma_kv;                     /* [d_q_latent], [d_kv_latent]: required when
+                                                      the weights carry gamma_q / gamma_kv, else
+                                                      ignored (a fixed gain has no gradient) */
+} gdla_grads;
+
+/* Backward pass of the layer for training: B sequences of T tokens at positions 0 .. T-1 (no
+ * cached prefix), with the layer's window and, optionally, packed documents (doc_start as in
+ * gdla_prefill_packed, or NULL).  Given dout [B, T, d_model] (layer dtype), it writes the
+ * gradients of L = sum(out (.) dout) with respect to x and every weight.  The forward is
+ * recomputed inside the call (the pages train with activation recomputation: paperglide reader,
+ * section "Distributed Training System"); nothing from an earlier forward is needed.
+ * dbg->lambda_override, when given, fixes lambda as in the forward (then no gradient flows
+ * through W_lambda).  Workspace: gdla_workspace_bytes(dims, GDLA_OP_BACKWARD, B, T, NULL, T).
+ * Errors as gdla_prefill, plus GDLA_ERR_INVALID_ARG for a NULL gradient pointer. */
+gdla_status gdla_backward(const gdla_dims *dims, const gdla_weights *w, const void *x, int32_t B,
+                          int32_t T, const int32_t *doc_start, const void *dout,
+                          const gdla_grads *grads, void *ws, size_t ws_bytes,
+                          const gdla_debug *dbg, hipStream_t stream);
 
 /* Static description of a status code. */
 const char *gdla_status_string(gdla_status s);

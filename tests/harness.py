@@ -4,6 +4,7 @@ fp64 oracle on the same seeded inputs and measure the difference."""
 import numpy as np
 import torch
 
+import oracle.gdla_grad as grad_ref
 import oracle.gdla_ref as ref
 import synth
 import attention_gdla_prefill_decode_amd as gd
@@ -186,3 +187,51 @@ def from_pages(pc, B, L):
     """The contiguous [B, L, row] view of a paged cache (a copy)."""
     rows = pc.pages[pc.block_table.long()]  # [B, blocks, page_rows, row]
     return rows.reshape(B, -1, pc.pages.shape[-1])[:, :L]
+
+
+def backward_case(cfg, seq, batch, window=0, docs=None, seed=None, random_gamma=True, lam_zero=False):
+    """gdla_backward on GPU and the oracle's backward on CPU (sequences at positions 0..T-1) for
+    a seeded upstream gradient dout; weight gradients are summed over the batch."""
+    inp = synth.make_inputs(cfg, "cpu", seed=seed, batch=batch, seq=seq, p0=0, random_gamma=random_gamma)
+    gen = torch.Generator().manual_seed(1000 + (cfg["seed"] if seed is None else seed))
+    dout = torch.randn((batch, seq, cfg["d_model"]), generator=gen).to(inp["x"].dtype)
+    dev = device_inputs(inp)
+    dims = gd.make_dims(cfg, window=window)
+    tensors = dict(dev["weights"], gamma_q=dev["gamma_q"], gamma_kv=dev["gamma_kv"])
+    ds = None if docs is None else torch.tensor(docs, dtype=torch.int32, device="cuda")
+    lam = torch.zeros((batch, seq, cfg["n_signal"]), dtype=torch.float32, device="cuda") if lam_zero else None
+    got = gd.gdla_backward(dims, dev["wstruct"], tensors, dev["x"], dout.to("cuda"), doc_start=ds,
+                           lambda_override=lam)
+    torch.cuda.synchronize()
+    w = oracle_weights(inp)
+    od = oracle_dims(cfg, window)
+    exp = {}
+    for b in range(batch):
+        r = grad_ref.gdla_backward(to_np(inp["x"][b]), w, od, to_np(dout[b]),
+                                   doc_start=None if docs is None else np.array(docs[b]),
+                                   lam_override=np.zeros((seq, cfg["n_signal"])) if lam_zero else None)
+        for k, v in r.items():
+            if v is None or not (k == "dx" or k.startswith("dw_") or k.startswith("dgamma")):
+                continue
+            if k == "dx":
+                exp.setdefault(k, []).append(v)
+            else:
+                exp[k] = exp.get(k, 0) + v
+    exp["dx"] = np.stack(exp["dx"])
+    return {k: to_np(v) for k, v in got.items()}, exp
+
+
+def check_grads(got, exp, rel_l2, what):
+    """Every gradient within rel_l2 of the oracle's (relative L2 over the tensor), and its max-abs
+    error within 10 rel_l2 of the tensor's largest entry; returns one line per gradient."""
+    lines = []
+    for k in sorted(exp):
+        g, e = np.asarray(got[k], dtype=np.float64), np.asarray(exp[k], dtype=np.float64)
+        assert g.shape == e.shape, f"{what} {k}: shape {g.shape} vs {e.shape}"
+        den = float(np.linalg.norm(e))
+        rel = float(np.linalg.norm(g - e)) / (den if den > 0 else 1.0)
+        mx = float(np.max(np.abs(g - e)))
+        big = float(np.max(np.abs(e))) if e.size else 0.0
+        lines.append(f"{k}: rel-L2 {rel:.2e}, max-abs {mx:.2e} (max |ref| {big:.2e})")
+        assert rel <= rel_l2 and mx <= 10 * rel_l2 * max(big, 1e-30), f"{what} {k}: " + lines[-1]
+    return lines

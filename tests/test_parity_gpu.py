@@ -240,6 +240,28 @@ def test_packed_prefill_single_document_is_prefill():
     assert torch.equal(out, ref_out)
 
 
+# ---------------------------------------------------------------- backward
+# The general backward path recomputes the forward and runs every step in fp32 from the stored
+# (fp32 or bf16) values, which the oracle reads exactly: fp32 rounding alone, 1e-5 relative.
+@pytest.mark.parametrize("cfg,T,batch,window,lens", [
+    (TINY, 40, 2, 0, None),
+    (TINY, 33, 1, 7, (10, 1, 22)),
+    (BF, 64, 1, 0, None),
+    (BF, 70, 2, 20, (30, 40)),
+])
+def test_backward_matches_oracle(cfg, T, batch, window, lens):
+    docs = None if lens is None else [H.doc_starts(0, lens) for _ in range(batch)]
+    got, exp = H.backward_case(cfg, T, batch, window=window, docs=docs, seed=67)
+    for line in H.check_grads(got, exp, 1e-5, f"backward {cfg['dtype']} T={T} W={window}"):
+        _say(line)
+
+
+def test_backward_lambda_zero():
+    got, exp = H.backward_case(BF, 48, 1, seed=71, lam_zero=True)
+    H.check_grads(got, exp, 1e-5, "backward, lambda = 0")
+    assert float(np.max(np.abs(got["dw_lambda"]))) == 0.0
+
+
 # ---------------------------------------------------------------- paged latent cache
 # The same calls over a shuffled pool of pages: the kernels read and write exactly the rows of the
 # contiguous layout, so the outputs must equal the contiguous path's bit for bit (windowed decode
