@@ -61,6 +61,7 @@ struct AttnArgs {
   float *hn;              // [M, n_N, 128] normalised noise-head outputs
   f16_t *y;               // [M, n_S * 128] fp16
   float *out_heads;       // [M, n_H, 128] or null
+  float *lse;             // [M, n_H] or null: log2 of the softmax denominator of the log2e-scaled scores
   int32_t T, lcap;
   int32_t n_heads, n_signal, n_noise, n_kv, window;
   int32_t sig_per_kv, chunks, n_qblk;
@@ -331,10 +332,13 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
 
   if (!active) return;
   // ---- epilogue: lane holds query column lane % 32 and dims db*32 + 8 i + 4 (lane / 32) + j
-  const float inv = 1.0f / pair_sum(l);
+  const float lsum = pair_sum(l);
+  const float inv = 1.0f / lsum;
   const int t = t0w + (lane & 31);
   if (t >= a.T) return;
   const int64_t mr = mrow0 + t;
+  // the probabilities are exp2(c s - lse) for raw scores s (what a backward pass recomputes)
+  if (a.lse && hgrp == 0) a.lse[mr * a.n_heads + head] = m * a.c + __log2f(lsum);
   float *oh = a.out_heads ? a.out_heads + (mr * a.n_heads + head) * DH : nullptr;
   if (!SIGNAL) {
     float *hn = a.hn + (mr * a.n_noise + (head - a.n_signal)) * DH;
@@ -447,7 +451,7 @@ gdla_status run_fast_prefill(const LayerDims &d, const gdla_weights *w, int32_t 
                              int32_t max_len, void *cq, float *lam, float *gate, void *kx,
                              void *vx, int32_t lcap, void *y, float *out_heads,
                              const FastPrefillLayout &L, void *ws, hipStream_t s, StageEvents &se,
-                             const NtWeights *nt, const int32_t *doc) {
+                             const NtWeights *nt, const int32_t *doc, float *lse) {
   (void)pos_host;
   (void)cache;
   (void)max_len;
@@ -493,7 +497,7 @@ gdla_status run_fast_prefill(const LayerDims &d, const gdla_weights *w, int32_t 
 
   AttnArgs a{};
   a.q = q; a.kx = (const f16_t *)kx; a.vx = (const f16_t *)vx;
-  a.pos = pos_dev; a.doc = doc; a.lam = lam; a.gate = gate; a.gate_f16 = nt ? 1 : 0; a.hn = hn; a.y = (f16_t *)y; a.out_heads = out_heads;
+  a.pos = pos_dev; a.doc = doc; a.lse = lse; a.lam = lam; a.gate = gate; a.gate_f16 = nt ? 1 : 0; a.hn = hn; a.y = (f16_t *)y; a.out_heads = out_heads;
   a.T = T; a.lcap = lcap;
   a.n_heads = d.n_heads; a.n_signal = d.n_signal; a.n_noise = d.n_noise; a.n_kv = d.n_kv;
   a.window = d.window;

@@ -20,7 +20,7 @@
 //                                                           dW_kr, dW_lambda, dx
 // This file is the general path: every step in fp32 (the recomputed forward included), any layer
 // sizes the forward's generic path takes, fp32 or bf16 storage.
-#include "gdla_internal.h"
+#include "fast_paths.h"
 
 #include <math.h>
 
@@ -573,6 +573,312 @@ hipError_t backward_t(const BackwardArgs &ba, const LayerDims &d, hipStream_t s)
 
 hipError_t launch_backward_generic(const BackwardArgs &a, const LayerDims &d, DT dt, hipStream_t s) {
   return dt == DT::F32 ? backward_t<float>(a, d, s) : backward_t<bf16_t>(a, d, s);
+}
+
+}  // namespace gdla
+
+// ==============================================================================================
+// Fast path (bf16 layer, d_head 128, d_rope 64, after the fused forward): the attention maps run in
+// bwd_attn.hip and every product on the transposed-weight MFMA GEMM with fp16 operands: data
+// gradients take the stored weights [in, out] as the K-major operand directly (converted to fp16,
+// and concatenated so that dc^Q and dx are one GEMM each), weight gradients take transposed
+// copies of the activations and gradients (tokens as K, padded with zeros to a multiple of 64).
+namespace gdla {
+namespace {
+
+__device__ __forceinline__ f16_t f16s(float v) { return (f16_t)fminf(fmaxf(v, -65504.f), 65504.f); }
+
+// dst[r, col_off + c] = fp16(src[r, c])  (r < rows, c < cols)
+template <typename TS>
+__global__ void __launch_bounds__(256) pack_f16_kernel(const TS *src, int64_t lds, int32_t rows, int32_t cols,
+                                                       f16_t *dst, int64_t ldd, int32_t col_off) {
+  const int64_t n = (int64_t)rows * cols;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / cols;
+    const int c = (int)(i % cols);
+    dst[r * ldd + col_off + c] = f16s((float)src[r * lds + c]);
+  }
+}
+
+// dst[row_off + c, r] = fp16(src[r, c]) for r < R, 0 for R <= r < R_pad (64 x 64 tiles through LDS)
+template <typename TS>
+__global__ void __launch_bounds__(256) tpack_f16_kernel(const TS *src, int64_t lds, int32_t R, int32_t C, int32_t R_pad,
+                                                        f16_t *dst, int64_t ldd, int32_t row_off) {
+  __shared__ float tile[64][65];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int rr = i / 64, cc = i % 64;
+    const int r = r0 + rr, c = c0 + cc;
+    tile[rr][cc] = (r < R && c < C) ? (float)src[(int64_t)r * lds + c] : 0.f;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int cc = i / 64, rr = i % 64;
+    const int r = r0 + rr, c = c0 + cc;
+    if (c < C && r < R_pad) dst[(int64_t)(row_off + c) * ldd + r] = f16s(tile[rr][cc]);
+  }
+}
+
+// Eq.(10) backward with sigmoid(G) from the forward (fp16): per element (m, i, e)
+//   D = H_i - lambda_i H_(n_S + i mod n_N);  dD = dY sg;  dG = dY D sg (1 - sg);  dH_i = dD
+// dG goes straight into the fp16 operand of the query-latent GEMM (columns g_off ...).
+__global__ void __launch_bounds__(256) combine_fast_kernel(const float *heads, const float *lam, const f16_t *sg16,
+                                                           const float *dy, float *dheads, float *dd, f16_t *a6,
+                                                           int64_t lda6, int32_t g_off, int32_t M, LayerDims d) {
+  const int64_t n = (int64_t)M * d.n_signal * d.d_h;
+  for (int64_t idx = blockIdx.x * 256ll + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * 256) {
+    const int e = (int)(idx % d.d_h);
+    const int64_t r = idx / d.d_h;
+    const int i = (int)(r % d.n_signal);
+    const int64_t m = r / d.n_signal;
+    const float hs = heads[(m * d.n_heads + i) * d.d_h + e];
+    const float hn = heads[(m * d.n_heads + d.n_signal + i % d.n_noise) * d.d_h + e];
+    const float dval = hs - lam[m * d.n_signal + i] * hn;
+    const float sg = (float)sg16[idx];
+    const float ddv = dy[idx] * sg;
+    dd[idx] = ddv;
+    dheads[(m * d.n_heads + i) * d.d_h + e] = ddv;
+    a6[m * lda6 + g_off + (idx - m * d.n_signal * d.d_h)] = f16s(dy[idx] * dval * sg * (1.0f - sg));
+  }
+}
+
+// dq [M, n_H, 192] (fp32) -> the query-latent operand: columns h d_h + e (dq^C) and
+// q_off + h d_r + j (dq^R rotated back by RoPE's negative angle), row m at position m % T
+__global__ void __launch_bounds__(256) pack_dq_kernel(const float *dq, f16_t *a6, int64_t lda6, int32_t q_off,
+                                                      int32_t M, int32_t T_, LayerDims d) {
+  const int dqk = d.d_h + d.d_r, half = d.d_r / 2;
+  const int per = d.d_h + half;  // elements handled per (m, h): d_h copies and d_r / 2 rotations
+  const int64_t n = (int64_t)M * d.n_heads * per;
+  for (int64_t idx = blockIdx.x * 256ll + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * 256) {
+    const int k = (int)(idx % per);
+    const int64_t mh = idx / per;
+    const int h = (int)(mh % d.n_heads);
+    const int64_t m = mh / d.n_heads;
+    const float *src = dq + mh * dqk;
+    if (k < d.d_h) {
+      a6[m * lda6 + (int64_t)h * d.d_h + k] = f16s(src[k]);
+    } else {
+      const int j = k - d.d_h;
+      float c, s;
+      rope_angle((int)(m % T_), j, d.d_r, d.theta, c, s);
+      const float u = src[d.d_h + j], w = src[d.d_h + j + half];
+      f16_t *o = a6 + m * lda6 + q_off + (int64_t)h * d.d_r;
+      o[j] = f16s(u * c + w * s);          // rotation by -angle
+      o[j + half] = f16s(-u * s + w * c);
+    }
+  }
+}
+
+// dk [B, n_kv, T, 192], dv [B, n_kv, T, 128] -> [dK^C | dV] as the latent operand a3 [M, 2 n_kv d_h]
+// (fp16) and dk^R summed over the KV groups, rotated back (fp32 [M, d_r])
+__global__ void __launch_bounds__(256) pack_dkv_kernel(const float *dk, const float *dv, f16_t *a3, float *dkr,
+                                                       int32_t M, int32_t T_, LayerDims d) {
+  const int dqk = d.d_h + d.d_r, half = d.d_r / 2;
+  const int64_t nkv = (int64_t)M * d.n_kv * d.d_h;
+  const int64_t nr = (int64_t)M * half;
+  const int64_t lda3 = 2ll * d.n_kv * d.d_h;
+  for (int64_t idx = blockIdx.x * 256ll + threadIdx.x; idx < nkv + nr; idx += (int64_t)gridDim.x * 256) {
+    if (idx < nkv) {
+      const int e = (int)(idx % d.d_h);
+      const int64_t r = idx / d.d_h;
+      const int j = (int)(r % d.n_kv);
+      const int64_t m = r / d.n_kv, b = m / T_, t = m % T_;
+      const int64_t src = ((b * d.n_kv + j) * T_ + t);
+      a3[m * lda3 + (int64_t)j * d.d_h + e] = f16s(dk[src * dqk + e]);
+      a3[m * lda3 + (int64_t)(d.n_kv + j) * d.d_h + e] = f16s(dv[src * d.d_h + e]);
+    } else {
+      const int64_t r = idx - nkv;
+      const int jj = (int)(r % half);
+      const int64_t m = r / half, b = m / T_, t = m % T_;
+      float u = 0.f, w = 0.f;
+      for (int g = 0; g < d.n_kv; ++g) {
+        const float *s = dk + ((b * d.n_kv + g) * T_ + t) * dqk + d.d_h;
+        u += s[jj];
+        w += s[jj + half];
+      }
+      float c, s;
+      rope_angle((int)t, jj, d.d_r, d.theta, c, s);
+      dkr[m * d.d_r + jj] = u * c + w * s;
+      dkr[m * d.d_r + jj + half] = -u * s + w * c;
+    }
+  }
+}
+
+// RMSNorm backward per row with the inverse RMS recomputed from v: writes dv and rinv[m]
+template <typename T>
+__global__ void __launch_bounds__(64) rms_bwd_kernel(const float *v, const T *gamma, const float *dy, float *dv,
+                                                     float *rinv, int32_t n, float eps) {
+  const int64_t m = blockIdx.x;
+  const int lane = threadIdx.x;
+  float ss = 0.f, uv = 0.f;
+  for (int j = lane; j < n; j += 64) {
+    const float x = v[m * n + j];
+    ss += x * x;
+    uv += dy[m * n + j] * (gamma ? (float)gamma[j] : 1.f) * x;
+  }
+  ss = wsum(ss);
+  uv = wsum(uv);
+  const float r = 1.0f / sqrtf(ss / n + eps);
+  for (int j = lane; j < n; j += 64) {
+    const float u = dy[m * n + j] * (gamma ? (float)gamma[j] : 1.f);
+    dv[m * n + j] = r * (u - v[m * n + j] * r * r * uv / n);
+  }
+  if (lane == 0) rinv[m] = r;
+}
+
+// dst[r, c] = 0 for r < rows, c0 <= c < c1 (the K padding of a concatenated operand)
+__global__ void __launch_bounds__(256) zero_cols_kernel(f16_t *dst, int64_t ldd, int32_t rows, int32_t c0, int32_t c1) {
+  const int w = c1 - c0;
+  const int64_t n = (int64_t)rows * w;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    dst[(i / w) * ldd + c0 + i % w] = (f16_t)0.f;
+}
+
+__global__ void __launch_bounds__(256) to_f16_kernel(const float *src, f16_t *dst, int64_t n) {
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) dst[i] = f16s(src[i]);
+}
+
+template <typename TS>
+hipError_t pack(const TS *src, int64_t lds, int rows, int cols, f16_t *dst, int64_t ldd, int col_off, hipStream_t s) {
+  hipLaunchKernelGGL(pack_f16_kernel<TS>, dim3(grid_for((int64_t)rows * cols)), dim3(256), 0, s, src, lds, rows, cols,
+                     dst, ldd, col_off);
+  return hipGetLastError();
+}
+template <typename TS>
+hipError_t tpack(const TS *src, int64_t lds, int R, int C, int R_pad, f16_t *dst, int64_t ldd, int row_off,
+                 hipStream_t s) {
+  hipLaunchKernelGGL(tpack_f16_kernel<TS>, dim3((C + 63) / 64, (R_pad + 63) / 64), dim3(256), 0, s, src, lds, R, C,
+                     R_pad, dst, ldd, row_off);
+  return hipGetLastError();
+}
+
+// C[M, N] (fp32, ldc) = A[M, K] Bt[N, K]^T, fp16 operands with K-contiguous rows
+hipError_t nt(const f16_t *A, int64_t lda, const f16_t *Bt, int64_t ldb, float *C, int64_t ldc, int M, int N, int K,
+              hipStream_t s) {
+  GemmBatch g{};
+  GemmProblem &p = g.p[g.n++];
+  p.A = A; p.lda = lda; p.B = Bt; p.ldb = ldb; p.C = C; p.ldc = ldc;
+  p.M = M; p.N = N; p.K = K; p.hw = N; p.hs = 0; p.ho = 0; p.c_dt = CD_F32; p.a_f16 = 1; p.epi = EPI_NONE;
+  return launch_gemm_nt(g, true, s);
+}
+
+}  // namespace
+
+hipError_t launch_backward_fast(const FastBwdArgs &a, const LayerDims &d, hipStream_t s) {
+  const int M = a.M, T_ = a.T, Mp = a.M_pad;
+  const int dm = d.d_model, dcq = d.d_cq, dc = d.d_c, dr = d.d_r, dh = d.d_h;
+  const int nH = d.n_heads, nS = d.n_signal, nKV = d.n_kv;
+  const gdla_weights &w = *a.w;
+  const gdla_grads &G = a.grads;
+  const FastBwdBuffers &b = a.buf;
+  const int ny = nS * dh;                        // Y columns
+  const int k6 = nH * dh + nH * dr + nS * dh;    // query-latent operand: [dq^C | dq^R | dG]
+  const int k3 = 2 * nKV * dh;                   // latent operand: [dK^C | dV]
+  const int k8 = a.k8;                           // x operand: [da^Q | dc^KV | dk^R | dlambda | 0]
+
+  // fp16 weights, concatenated along K as the data-gradient GEMMs read them
+  BWD_TRY(pack((const bf16_t *)w.w_o, dm, ny, dm, b.wo16, dm, 0, s));
+  BWD_TRY(pack((const bf16_t *)w.w_uk, (int64_t)nKV * dh, dc, nKV * dh, b.w3, k3, 0, s));
+  BWD_TRY(pack((const bf16_t *)w.w_uv, (int64_t)nKV * dh, dc, nKV * dh, b.w3, k3, nKV * dh, s));
+  BWD_TRY(pack((const bf16_t *)w.w_qc, (int64_t)nH * dh, dcq, nH * dh, b.w6, k6, 0, s));
+  BWD_TRY(pack((const bf16_t *)w.w_qr, (int64_t)nH * dr, dcq, nH * dr, b.w6, k6, nH * dh, s));
+  BWD_TRY(pack((const bf16_t *)w.w_gate, (int64_t)nS * dh, dcq, nS * dh, b.w6, k6, nH * dh + nH * dr, s));
+  BWD_TRY(pack((const bf16_t *)w.w_qa, dcq, dm, dcq, b.w8, k8, 0, s));
+  BWD_TRY(pack((const bf16_t *)w.w_dkv, dc, dm, dc, b.w8, k8, dcq, s));
+  BWD_TRY(pack((const bf16_t *)w.w_kr, dr, dm, dr, b.w8, k8, dcq + dc, s));
+  BWD_TRY(pack((const bf16_t *)w.w_lambda, nS, dm, nS, b.w8, k8, dcq + dc + dr, s));
+  const int k8_used = dcq + dc + dr + nS;
+  if (k8 > k8_used) {
+    hipLaunchKernelGGL(zero_cols_kernel, dim3(grid_for((int64_t)dm * (k8 - k8_used))), dim3(256), 0, s, b.w8,
+                       (int64_t)k8, dm, k8_used, k8);
+    BWD_TRY(hipGetLastError());
+    hipLaunchKernelGGL(zero_cols_kernel, dim3(grid_for((int64_t)M * (k8 - k8_used))), dim3(256), 0, s, b.a8,
+                       (int64_t)k8, M, k8_used, k8);
+    BWD_TRY(hipGetLastError());
+  }
+
+  // ---- Eq.(10): dY = dout W_O^T; dW_O = Y^T dout
+  BWD_TRY(pack((const bf16_t *)a.dout, dm, M, dm, b.dout16, dm, 0, s));
+  BWD_TRY(nt(b.dout16, dm, b.wo16, dm, b.dy, ny, M, ny, dm, s));
+  BWD_TRY(tpack(a.y16, ny, M, ny, Mp, b.ta, Mp, 0, s));
+  BWD_TRY(tpack((const bf16_t *)a.dout, dm, M, dm, Mp, b.tb, Mp, 0, s));
+  BWD_TRY(nt(b.ta, Mp, b.tb, Mp, G.dw_o, dm, ny, dm, Mp, s));
+  // gate and differential combine; noise-head dH and dlambda
+  hipLaunchKernelGGL(combine_fast_kernel, dim3(grid_for((int64_t)M * ny)), dim3(256), 0, s, a.heads, a.lam, a.sg16,
+                     b.dy, b.dheads, b.dd, b.a6, (int64_t)k6, nH * dh + nH * dr, M, d);
+  BWD_TRY(hipGetLastError());
+  hipLaunchKernelGGL(bwd_noise_lambda_kernel, dim3(grid_for((int64_t)M * d.n_noise * dh + (int64_t)M * nS)), dim3(256),
+                     0, s, a.heads, a.lam, b.dd, b.dheads, b.dlaml, a.lam_overridden ? 1 : 0, M, d);
+  BWD_TRY(hipGetLastError());
+  hipLaunchKernelGGL(bwd_drow_kernel, dim3((unsigned)(((int64_t)M * nH + 3) / 4)), dim3(256), 0, s, a.heads,
+                     b.dheads, b.drow, (int64_t)M * nH, dh);
+  BWD_TRY(hipGetLastError());
+  hipLaunchKernelGGL(to_f16_kernel, dim3(grid_for((int64_t)M * nH * dh)), dim3(256), 0, s, b.dheads, b.dh16,
+                     (int64_t)M * nH * dh);
+  BWD_TRY(hipGetLastError());
+
+  // ---- the softmax maps
+  BwdAttnArgs at{};
+  at.q = a.q16; at.k = a.kx; at.v = a.vk; at.dh = b.dh16; at.lse = a.lse; at.drow = b.drow; at.doc = a.doc;
+  at.dq = b.dq; at.dk = b.dk; at.dv = b.dv;
+  at.B = a.B; at.T = T_; at.lcap = a.lcap; at.n_heads = nH; at.n_signal = nS; at.n_noise = d.n_noise;
+  at.n_kv = nKV; at.window = d.window; at.c = d.scale * 1.4426950408889634f; at.tau = d.scale;
+  BWD_TRY(launch_bwd_attention(at, s));
+  hipLaunchKernelGGL(pack_dq_kernel, dim3(grid_for((int64_t)M * nH * (dh + dr / 2))), dim3(256), 0, s, b.dq, b.a6,
+                     (int64_t)k6, nH * dh, M, T_, d);
+  BWD_TRY(hipGetLastError());
+  hipLaunchKernelGGL(pack_dkv_kernel, dim3(grid_for((int64_t)M * nKV * dh + (int64_t)M * dr / 2)), dim3(256), 0, s,
+                     b.dk, b.dv, b.a3, b.dkr, M, T_, d);
+  BWD_TRY(hipGetLastError());
+
+  // ---- Eq.(5), (4): dcbar = [dK^C | dV] [W_uk | W_uv]^T; dW_uk, dW_uv = cbar^T [dK^C | dV]
+  BWD_TRY(nt(b.a3, k3, b.w3, k3, b.dcbar, dc, M, dc, k3, s));
+  BWD_TRY(tpack(a.cache, (int64_t)dc + dr, M, dc, Mp, b.ta, Mp, 0, s));
+  BWD_TRY(tpack(b.a3, k3, M, k3, Mp, b.tb, Mp, 0, s));
+  BWD_TRY(nt(b.ta, Mp, b.tb, Mp, G.dw_uk, (int64_t)nKV * dh, dc, nKV * dh, Mp, s));
+  BWD_TRY(nt(b.ta, Mp, b.tb + (int64_t)nKV * dh * Mp, Mp, G.dw_uv, (int64_t)nKV * dh, dc, nKV * dh, Mp, s));
+  hipLaunchKernelGGL((rms_bwd_kernel<bf16_t>), dim3(M), dim3(64), 0, s, a.ckv, (const bf16_t *)w.gamma_kv, b.dcbar,
+                     b.dckv, b.rkv, dc, d.eps);
+  BWD_TRY(hipGetLastError());
+  if (G.dgamma_kv) {
+    hipLaunchKernelGGL(bwd_dgamma_kernel, dim3((dc + 255) / 256), dim3(256), 0, s, a.ckv, b.rkv, b.dcbar, G.dgamma_kv,
+                       M, dc);
+    BWD_TRY(hipGetLastError());
+  }
+
+  // ---- Eq.(2), (9), (1): dc^Q = [dq^C | dq^R | dG] [W_qc | W_qr | W_gate]^T; their weight grads
+  BWD_TRY(nt(b.a6, k6, b.w6, k6, b.dcq, dcq, M, dcq, k6, s));
+  BWD_TRY(tpack(a.cq16, dcq, M, dcq, Mp, b.ta, Mp, 0, s));
+  BWD_TRY(tpack(b.a6, k6, M, k6, Mp, b.tb, Mp, 0, s));
+  BWD_TRY(nt(b.ta, Mp, b.tb, Mp, G.dw_qc, (int64_t)nH * dh, dcq, nH * dh, Mp, s));
+  BWD_TRY(nt(b.ta, Mp, b.tb + (int64_t)nH * dh * Mp, Mp, G.dw_qr, (int64_t)nH * dr, dcq, nH * dr, Mp, s));
+  BWD_TRY(nt(b.ta, Mp, b.tb + (int64_t)(nH * dh + nH * dr) * Mp, Mp, G.dw_gate, (int64_t)nS * dh, dcq, nS * dh, Mp, s));
+  hipLaunchKernelGGL((rms_bwd_kernel<bf16_t>), dim3(M), dim3(64), 0, s, a.aq, (const bf16_t *)w.gamma_q, b.dcq, b.daq,
+                     b.rq, dcq, d.eps);
+  BWD_TRY(hipGetLastError());
+  if (G.dgamma_q) {
+    hipLaunchKernelGGL(bwd_dgamma_kernel, dim3((dcq + 255) / 256), dim3(256), 0, s, a.aq, b.rq, b.dcq, G.dgamma_q, M,
+                       dcq);
+    BWD_TRY(hipGetLastError());
+  }
+
+  // ---- x: dx = [da^Q | dc^KV | dk^R | dlambda] [W_qa | W_dkv | W_kr | W_lambda]^T; x-side weights
+  BWD_TRY(pack(b.daq, dcq, M, dcq, b.a8, k8, 0, s));
+  BWD_TRY(pack(b.dckv, dc, M, dc, b.a8, k8, dcq, s));
+  BWD_TRY(pack(b.dkr, dr, M, dr, b.a8, k8, dcq + dc, s));
+  BWD_TRY(pack(b.dlaml, nS, M, nS, b.a8, k8, dcq + dc + dr, s));
+  BWD_TRY(nt(b.a8, k8, b.w8, k8, G.dx, dm, M, dm, k8, s));
+  BWD_TRY(tpack((const bf16_t *)a.x, dm, M, dm, Mp, b.ta, Mp, 0, s));
+  BWD_TRY(tpack(b.a8, k8, M, k8, Mp, b.tb, Mp, 0, s));
+  BWD_TRY(nt(b.ta, Mp, b.tb, Mp, G.dw_qa, dcq, dm, dcq, Mp, s));
+  BWD_TRY(nt(b.ta, Mp, b.tb + (int64_t)dcq * Mp, Mp, G.dw_dkv, dc, dm, dc, Mp, s));
+  BWD_TRY(nt(b.ta, Mp, b.tb + (int64_t)(dcq + dc) * Mp, Mp, G.dw_kr, dr, dm, dr, Mp, s));
+  if (nS % 8 == 0) {
+    BWD_TRY(nt(b.ta, Mp, b.tb + (int64_t)(dcq + dc + dr) * Mp, Mp, G.dw_lambda, nS, dm, nS, Mp, s));
+  } else {  // too few columns for the MFMA GEMM's 16-byte stores
+    BWD_TRY(gg((const bf16_t *)a.x, dm, true, b.dlaml, nS, false, G.dw_lambda, nS, dm, nS, M, false, s));
+  }
+  return hipSuccess;
 }
 
 }  // namespace gdla

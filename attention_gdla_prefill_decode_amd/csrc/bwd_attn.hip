@@ -1,0 +1,395 @@
+// Fused backward of the GDLA attention maps for gfx950 (d_head 128, d_rope 64, fp16 operands, fp32
+// accumulation), training sequences at positions 0 .. T-1.
+//
+// Per head h with KV head kv(h) (picx.dev summary section 2.2: the two softmax maps of the signal
+// and noise heads, both on the KV heads of Eq.(5)), with raw scores s = q . k over [q^C ; q^R] and
+// [K^C ; k^R], P = exp2(c s - lse) (c = tau log2 e, lse from the forward) on the visible keys:
+//   dP = dH V^T,  dS = tau P (.) (dP - rowsum(dH (.) H)),
+//   dq = dS K,    dK += dS^T q,   dV += P^T dH.
+// Two kernels, so that every output has one writer and no atomics are needed:
+//   bwd_dq_kernel   query-major, like the forward: a wave holds 32 queries of one head, streams
+//                   the KV head's key tiles and accumulates dQ^T = K^T dS^T;
+//   bwd_dkv_kernel  key-major: a wave holds 32 keys of one KV head, streams the query blocks of
+//                   every head of the group and accumulates dK^T = Q^T dS and dV^T = dH^T P.
+// All products run on v_mfma_f32_32x32x16_f16 (A[m = l % 32][k = 8 (l / 32) + i],
+// B[k = 8 (l / 32) + i][n = l % 32], acc[j] = C[8 (j / 4) + 4 (l / 32) + j % 4][l % 32]).  Where
+// an accumulator (whose rows run in that j order) feeds the next product as its B operand, the
+// matching A fragments are read with ds_read_b64_tr_b16 from a row-major tile: each 4-row group of
+// the transposing read covers one run of four consecutive rows in that order.
+#include "fast_paths.h"
+
+namespace gdla {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int DH = 128, DR = 64, DQK = DH + DR;
+constexpr int KP = DQK + 8;  // LDS row pitch (elements) of [q ; k] rows
+constexpr int VP = DH + 8;   // LDS row pitch of value / dH rows
+
+__device__ __forceinline__ f32x16 mfma(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f16x4 tr4(const f16_t *p) {
+  return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p));
+}
+__device__ __forceinline__ f16_t h16(float v) { return (f16_t)fminf(fmaxf(v, -65504.f), 65504.f); }
+
+// A fragment of a transposed row-major tile (rows r, columns c, pitch `pitch` elements): lane l
+// gets column c0 + l % 32 at the 8 rows r0 + 8 (i / 4) + 4 (l / 32) + i % 4, i = 0..7 (the row
+// order of an accumulator's 16-row half).
+__device__ __forceinline__ f16x8 tr_frag(const f16_t *tile, int pitch, int r0, int c0, int lane) {
+  const int G = lane >> 4, s = lane & 15;
+  const f16_t *p = tile + (r0 + 4 * (G >> 1) + (s >> 2)) * pitch + c0 + 16 * (G & 1) + 4 * (s & 3);
+  const f16x4 lo = tr4(p), hi = tr4(p + 8 * pitch);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+}  // namespace
+
+
+
+namespace {
+
+// lowest visible key of token t of sequence b (window and document)
+__device__ __forceinline__ int qlo(const BwdAttnArgs &a, int b, int t) {
+  int lo = a.window > 0 ? max(0, t - a.window + 1) : 0;
+  if (a.doc) lo = max(lo, min(max(a.doc[(int64_t)b * a.T + t], 0), t));
+  return lo;
+}
+
+// ------------------------------------------------------------------------------------------
+// dq.  SIGNAL: workgroup (q block of 32, KV head, chunk of 4 signal heads, sequence), wave w =
+// signal head kv + n_kv (4 chunk + w).  Noise: workgroup (q block of 128, noise head, sequence),
+// wave w = queries 32 w ... of that head.  Key tiles of 64 rows are staged in LDS (K and V,
+// double-buffered through registers).
+template <bool SIGNAL>
+__global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdAttnArgs a) {
+  __shared__ __attribute__((aligned(16))) f16_t KS[2][64 * KP];
+  __shared__ __attribute__((aligned(16))) f16_t VS[2][64 * VP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int QB = SIGNAL ? 32 : 128;
+  const int n_qblk = (a.T + QB - 1) / QB;
+  const int ny = SIGNAL ? a.n_kv * a.sig_chunks : a.n_noise;
+  const int per_q = ny * a.B;
+  const int qblk = n_qblk - 1 - (int)blockIdx.x / per_q;  // longest work first
+  const int yy = (int)blockIdx.x % per_q % ny, b = (int)blockIdx.x % per_q / ny;
+  int head, kvh, q0;
+  const int q_first = qblk * QB;
+  if (SIGNAL) {
+    kvh = yy / a.sig_chunks;
+    const int r = (yy % a.sig_chunks) * 4 + wave;
+    head = r < a.n_signal / a.n_kv ? kvh + a.n_kv * r : -1;
+    q0 = q_first;
+  } else {
+    head = a.n_signal + yy;
+    kvh = yy % a.n_kv;
+    q0 = q_first + 32 * wave;
+  }
+  const int q_last = min(q_first + QB, a.T) - 1;
+  const bool active = head >= 0 && q0 < a.T;
+  const int klo = qlo(a, b, q_first) & ~63, khi = q_last + 1;
+  const int ntiles = (khi - klo + 63) / 64;
+  const int wq_hi = min(q0 + 31, a.T - 1);
+  const int wlo_min = qlo(a, b, min(q0, a.T - 1)), wlo_max = qlo(a, b, wq_hi);
+
+  // this lane's query (column l % 32)
+  const int tq = q0 + (lane & 31);
+  const bool qok = active && tq < a.T;
+  const int tqc = min(tq, a.T - 1);
+  const int64_t mh = ((int64_t)b * a.T + tqc) * a.n_heads + (head >= 0 ? head : 0);
+  const int wlim = qok ? tqc - qlo(a, b, tqc) + 1 : 0;  // key s visible iff 0 <= t - s < wlim
+  const float lse = qok ? a.lse[mh] : 0.f, drow = qok ? a.drow[mh] : 0.f;
+  f16x8 Qf[12], Hf[8];
+#pragma unroll
+  for (int k = 0; k < 12; ++k) Qf[k] = *(const f16x8 *)(a.q + mh * DQK + 16 * k + 8 * (lane >> 5));
+#pragma unroll
+  for (int k = 0; k < 8; ++k) Hf[k] = *(const f16x8 *)(a.dh + mh * DH + 16 * k + 8 * (lane >> 5));
+  f32x16 dQ[6];
+#pragma unroll
+  for (int i = 0; i < 6; ++i) dQ[i] = f32x16{};
+
+  const f16_t *kg = a.k + ((int64_t)b * a.n_kv + kvh) * a.lcap * DQK;
+  const f16_t *vg = a.v + ((int64_t)b * a.n_kv + kvh) * a.lcap * DH;
+  // tile staging: thread tid moves chunks tid, tid + 256, ... (K: 64 x 24, V: 64 x 16 chunks);
+  // rows past the last query's key read the last valid row instead (finite, never visible)
+  uint4 kr[6], vr[4];
+  auto load = [&](int t) {
+    const int s0 = klo + 64 * t;
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      const int c = tid + 256 * i, row = c / 24, ch = c % 24;
+      kr[i] = *(const uint4 *)(kg + (int64_t)min(s0 + row, a.T - 1) * DQK + 8 * ch);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i, row = c / 16, ch = c % 16;
+      vr[i] = *(const uint4 *)(vg + (int64_t)min(s0 + row, a.T - 1) * DH + 8 * ch);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      const int c = tid + 256 * i, row = c / 24, ch = c % 24;
+      *(uint4 *)(KS[buf] + row * KP + 8 * ch) = kr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i, row = c / 16, ch = c % 16;
+      *(uint4 *)(VS[buf] + row * VP + 8 * ch) = vr[i];
+    }
+  };
+
+  if (ntiles > 0) {
+    load(0);
+    store(0);
+  }
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles) load(t + 1);
+    const int s0 = klo + 64 * t;
+    const f16_t *ks = KS[t & 1], *vs = VS[t & 1];
+    const bool skip = !active || s0 > wq_hi || s0 + 63 < wlo_min;
+    if (!skip) {
+      const bool full = s0 + 63 <= q0 && s0 >= wlo_max;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16 S = {}, dP = {};
+#pragma unroll
+        for (int k = 0; k < 12; ++k)
+          S = mfma(*(const f16x8 *)(ks + (32 * kb + (lane & 31)) * KP + 16 * k + 8 * (lane >> 5)), Qf[k], S);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          dP = mfma(*(const f16x8 *)(vs + (32 * kb + (lane & 31)) * VP + 16 * k + 8 * (lane >> 5)), Hf[k], dP);
+        // acc[j]: key s0 + 32 kb + 8 (j / 4) + 4 (l / 32) + j % 4, query tq
+        const int d0 = tq - s0 - 32 * kb - 4 * (lane >> 5);
+        f16x8 dsf[2];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int off = 8 * (j >> 2) + (j & 3);
+          const bool vis = full ? qok : (unsigned)(d0 - off) < (unsigned)wlim;
+          const float p = vis ? __builtin_amdgcn_exp2f(S[j] * a.c - lse) : 0.f;
+          dsf[j >> 3][j & 7] = h16(vis ? p * (dP[j] - drow) : 0.f);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int db = 0; db < 6; ++db)
+            dQ[db] = mfma(tr_frag(ks, KP, 32 * kb + 16 * kk, 32 * db, lane), dsf[kk], dQ[db]);
+      }
+    }
+    // the other buffer was last read in iteration t - 1, which every wave has left
+    if (t + 1 < ntiles) store((t + 1) & 1);
+    __syncthreads();
+  }
+  if (!qok) return;
+  // dQ[db][j] = dQ^T[dim 32 db + 8 (j / 4) + 4 (l / 32) + j % 4][query tq]
+  float *o = a.dq + mh * DQK;
+#pragma unroll
+  for (int db = 0; db < 6; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *(float4 *)(o + 32 * db + 8 * i + 4 * (lane >> 5)) =
+          make_float4(dQ[db][4 * i] * a.tau, dQ[db][4 * i + 1] * a.tau, dQ[db][4 * i + 2] * a.tau,
+                      dQ[db][4 * i + 3] * a.tau);
+}
+
+// ------------------------------------------------------------------------------------------
+// dK, dV.  Workgroup (key block of 64, KV head, sequence); wave w takes keys 32 (w & 1) .. of the
+// block and the query blocks of parity w >> 1, over every head of the KV group.  The two parities
+// are added through LDS at the end.
+constexpr int QT_BYTES = 32 * KP * 2 + 32 * VP * 2 + 3 * 32 * 4;  // Q, dH, lse, drow, lo of 32 queries
+
+__global__ void __launch_bounds__(256, 1) bwd_dkv_kernel(BwdAttnArgs a) {
+  __shared__ __attribute__((aligned(16))) char SM[2 * 2 * QT_BYTES];  // [buffer][parity]
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kh = wave & 1, par = wave >> 1;
+  const int per_k = a.n_kv * a.B;
+  const int kblk = (int)blockIdx.x / per_k;  // longest work (first keys) first
+  const int kvh = (int)blockIdx.x % per_k % a.n_kv, b = (int)blockIdx.x % per_k / a.n_kv;
+  const int kb0 = 64 * kblk;
+  // queries kb0 .. q_end - 1 can see a key of the block: lowest visible keys never decrease
+  int lo_q = kb0, hi_q = a.T;
+  while (lo_q < hi_q) {
+    const int mid = (lo_q + hi_q) >> 1;
+    if (qlo(a, b, mid) > kb0 + 63) hi_q = mid;
+    else lo_q = mid + 1;
+  }
+  const int q_end = lo_q;
+  const int qb0 = kb0 / 32, nqb = max(0, (q_end - kb0 + 31) / 32);
+  const int its = (nqb + 1) / 2;
+  const int sig_g = a.n_signal / a.n_kv, n_g = a.n_heads / a.n_kv;
+  const int n_it = n_g * its;
+
+  // this wave's keys: K^T and V^T as B operands (B[k = dim][n = key])
+  const int key = kb0 + 32 * kh + (lane & 31);
+  const int keyc = min(key, a.T - 1);
+  const f16_t *kg = a.k + (((int64_t)b * a.n_kv + kvh) * a.lcap + keyc) * DQK;
+  const f16_t *vg = a.v + (((int64_t)b * a.n_kv + kvh) * a.lcap + keyc) * DH;
+  f16x8 Kf[12], Vf[8];
+#pragma unroll
+  for (int k = 0; k < 12; ++k) Kf[k] = *(const f16x8 *)(kg + 16 * k + 8 * (lane >> 5));
+#pragma unroll
+  for (int k = 0; k < 8; ++k) Vf[k] = *(const f16x8 *)(vg + 16 * k + 8 * (lane >> 5));
+  f32x16 dK[6], dV[4];
+#pragma unroll
+  for (int i = 0; i < 6; ++i) dK[i] = f32x16{};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dV[i] = f32x16{};
+
+  // staging of one query block by the 128 threads of its parity (u = tid & 127)
+  const int u = tid & 127;
+  uint4 qr[6], hr[4];
+  float sr = 0.f, dr = 0.f;
+  int lr = 0;
+  auto head_of = [&](int gi) { return gi < sig_g ? kvh + a.n_kv * gi : a.n_signal + kvh + a.n_kv * (gi - sig_g); };
+  auto load = [&](int it) {
+    const int h = head_of(it / its), qb = qb0 + 2 * (it % its) + par;
+    const int qbase = 32 * qb;
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      const int c = u + 128 * i, row = c / 24, ch = c % 24;
+      const int t = min(qbase + row, a.T - 1);
+      qr[i] = *(const uint4 *)(a.q + (((int64_t)b * a.T + t) * a.n_heads + h) * DQK + 8 * ch);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = u + 128 * i, row = c / 16, ch = c % 16;
+      const int t = min(qbase + row, a.T - 1);
+      hr[i] = *(const uint4 *)(a.dh + (((int64_t)b * a.T + t) * a.n_heads + h) * DH + 8 * ch);
+    }
+    if (u < 32) {
+      const int t = min(qbase + u, a.T - 1);
+      const int64_t mh = ((int64_t)b * a.T + t) * a.n_heads + h;
+      sr = a.lse[mh];
+      dr = a.drow[mh];
+      lr = qbase + u < a.T ? qlo(a, b, t) : 0x7fffffff;  // rows past T see nothing
+    }
+  };
+  auto tile = [&](int buf, int p) { return SM + (2 * buf + p) * QT_BYTES; };
+  auto store = [&](int buf) {
+    char *base = tile(buf, par);
+    f16_t *qs = (f16_t *)base, *hs = (f16_t *)(base + 32 * KP * 2);
+    float *ls = (float *)(base + 32 * KP * 2 + 32 * VP * 2);
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      const int c = u + 128 * i, row = c / 24, ch = c % 24;
+      *(uint4 *)(qs + row * KP + 8 * ch) = qr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = u + 128 * i, row = c / 16, ch = c % 16;
+      *(uint4 *)(hs + row * VP + 8 * ch) = hr[i];
+    }
+    if (u < 32) {
+      ls[u] = sr;
+      ls[32 + u] = dr;
+      ((int *)ls)[64 + u] = lr;
+    }
+  };
+
+  if (n_it > 0) {
+    load(0);
+    store(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < n_it; ++it) {
+    if (it + 1 < n_it) load(it + 1);
+    const int qb = qb0 + 2 * (it % its) + par;
+    if (qb < qb0 + nqb) {
+      const char *base = tile(it & 1, par);
+      const f16_t *qs = (const f16_t *)base, *hs = (const f16_t *)(base + 32 * KP * 2);
+      const float *ls = (const float *)(base + 32 * KP * 2 + 32 * VP * 2);
+      f32x16 S = {}, dP = {};
+#pragma unroll
+      for (int k = 0; k < 12; ++k) S = mfma(*(const f16x8 *)(qs + (lane & 31) * KP + 16 * k + 8 * (lane >> 5)), Kf[k], S);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) dP = mfma(*(const f16x8 *)(hs + (lane & 31) * VP + 16 * k + 8 * (lane >> 5)), Vf[k], dP);
+      // acc[j]: query 32 qb + qi, qi = 8 (j / 4) + 4 (l / 32) + j % 4; key `key`
+      f16x8 pf[2], dsf[2];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int qi = 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+        const int t = 32 * qb + qi;
+        const bool vis = key <= t && key >= ((const int *)ls)[64 + qi];
+        const float p = vis ? __builtin_amdgcn_exp2f(S[j] * a.c - ls[qi]) : 0.f;
+        pf[j >> 3][j & 7] = h16(p);
+        dsf[j >> 3][j & 7] = h16(vis ? p * (dP[j] - ls[32 + qi]) : 0.f);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int eb = 0; eb < 4; ++eb) dV[eb] = mfma(tr_frag(hs, VP, 16 * kk, 32 * eb, lane), pf[kk], dV[eb]);
+#pragma unroll
+        for (int db = 0; db < 6; ++db) dK[db] = mfma(tr_frag(qs, KP, 16 * kk, 32 * db, lane), dsf[kk], dK[db]);
+      }
+    }
+    if (it + 1 < n_it) store((it + 1) & 1);  // last read in iteration it - 1
+    __syncthreads();
+  }
+
+  // parity 1 hands its sums to parity 0 through LDS (the tile buffers are free now)
+  float *red = (float *)SM + kh * (10 * 16 * 64);
+  if (par == 1) {
+#pragma unroll
+    for (int db = 0; db < 6; ++db)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) red[(db * 16 + j) * 64 + lane] = dK[db][j];
+#pragma unroll
+    for (int eb = 0; eb < 4; ++eb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) red[((6 + eb) * 16 + j) * 64 + lane] = dV[eb][j];
+  }
+  __syncthreads();
+  if (par == 1 || key >= a.T) return;
+  // dK[db][j] = dK^T[dim 32 db + 8 (j / 4) + 4 (l / 32) + j % 4][key]
+  const int64_t ko = ((int64_t)b * a.n_kv + kvh) * a.T + key;
+  float *dk = a.dk + ko * DQK, *dv = a.dv + ko * DH;
+#pragma unroll
+  for (int db = 0; db < 6; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float4 v;
+      v.x = (dK[db][4 * i] + red[(db * 16 + 4 * i) * 64 + lane]) * a.tau;
+      v.y = (dK[db][4 * i + 1] + red[(db * 16 + 4 * i + 1) * 64 + lane]) * a.tau;
+      v.z = (dK[db][4 * i + 2] + red[(db * 16 + 4 * i + 2) * 64 + lane]) * a.tau;
+      v.w = (dK[db][4 * i + 3] + red[(db * 16 + 4 * i + 3) * 64 + lane]) * a.tau;
+      *(float4 *)(dk + 32 * db + 8 * i + 4 * (lane >> 5)) = v;
+    }
+#pragma unroll
+  for (int eb = 0; eb < 4; ++eb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float4 v;
+      v.x = dV[eb][4 * i] + red[((6 + eb) * 16 + 4 * i) * 64 + lane];
+      v.y = dV[eb][4 * i + 1] + red[((6 + eb) * 16 + 4 * i + 1) * 64 + lane];
+      v.z = dV[eb][4 * i + 2] + red[((6 + eb) * 16 + 4 * i + 2) * 64 + lane];
+      v.w = dV[eb][4 * i + 3] + red[((6 + eb) * 16 + 4 * i + 3) * 64 + lane];
+      *(float4 *)(dv + 32 * eb + 8 * i + 4 * (lane >> 5)) = v;
+    }
+}
+
+}  // namespace
+
+bool fast_backward_supported(const LayerDims &d, gdla_dtype dt) {
+  return dt == GDLA_BF16 && d.d_h == DH && d.d_r == DR && d.n_noise % d.n_kv == 0 && d.n_signal % d.n_kv == 0;
+}
+
+hipError_t launch_bwd_attention(const BwdAttnArgs &a0, hipStream_t s) {
+  BwdAttnArgs a = a0;
+  a.sig_chunks = (a.n_signal / a.n_kv + 3) / 4;
+  const int nq32 = (a.T + 31) / 32, nq128 = (a.T + 127) / 128, nk = (a.T + 63) / 64;
+  hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3((unsigned)(nq32 * a.n_kv * a.sig_chunks * a.B)), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3((unsigned)(nq128 * a.n_noise * a.B)), dim3(256), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dkv_kernel, dim3((unsigned)(nk * a.n_kv * a.B)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace gdla

@@ -74,7 +74,7 @@ gdla_status run_fast_prefill(const LayerDims &d, const gdla_weights *w, int32_t 
                              int32_t max_len, void *cq, float *lam, float *gate, void *kx,
                              void *vx, int32_t lcap, void *y, float *out_heads,
                              const FastPrefillLayout &L, void *ws, hipStream_t s, StageEvents &se,
-                             const NtWeights *nt, const int32_t *doc);
+                             const NtWeights *nt, const int32_t *doc, float *lse = nullptr);
 
 // ---- absorbed split-L decode ----
 // Sizes are per query row set: BT = B T for T new tokens per sequence.
@@ -107,4 +107,52 @@ gdla_status run_fast_decode(const LayerDims &d, const gdla_weights *w, int32_t B
                             const float *qr, float *heads, const FastDecodeLayout &L, void *ws,
                             hipStream_t s, StageEvents &se);
 
+// ---- fused backward (bf16 layer, d_head 128, d_rope 64; training sequences from position 0) ----
+struct BwdAttnArgs {
+  const f16_t *q;      // [M, n_H, 192]: q^C ; RoPE(q^R)
+  const f16_t *k;      // [B, n_kv, lcap, 192]: K^C ; k^R of keys 0 .. lcap - 1
+  const f16_t *v;      // [B, n_kv, lcap, 128]: V, key-major
+  const f16_t *dh;     // [M, n_H, 128]
+  const float *lse;    // [M, n_H]: log2 softmax denominators of c s
+  const float *drow;   // [M, n_H]: rowsum(dH (.) H)
+  const int32_t *doc;  // [M] document starts or null
+  float *dq;           // [M, n_H, 192]
+  float *dk;           // [B, n_kv, T, 192]: the k^R part summed over this KV group's heads only
+  float *dv;           // [B, n_kv, T, 128]
+  int32_t B, T, lcap, n_heads, n_signal, n_noise, n_kv, window;
+  int32_t sig_chunks;  // dq, signal heads: workgroups of 4 heads per KV head
+  float c, tau;
+};
+bool fast_backward_supported(const LayerDims &d, gdla_dtype dt);
+hipError_t launch_bwd_attention(const BwdAttnArgs &a, hipStream_t s);
+
+struct FastBwdBuffers {
+  f16_t *wo16, *w3, *w6, *w8;   // fp16 weights, K-concatenated: [n_S d_h, d], [d_c, k3], [d_cq, k6], [d, k8]
+  f16_t *dout16;                // [M, d]
+  float *dy;                    // [M, n_S d_h]
+  f16_t *ta, *tb;               // transposed operands [rows, M_pad]
+  float *dheads, *dd, *dlaml, *drow;
+  f16_t *dh16;                  // [M, n_H, d_h]
+  float *dq, *dk, *dv;          // attention gradients
+  f16_t *a6, *a3, *a8;          // gradient operands [M, k6], [M, k3], [M, k8]
+  float *dkr, *dcbar, *dckv, *rkv, *dcq, *daq, *rq;
+};
+struct FastBwdArgs {
+  const void *x, *dout;
+  const gdla_weights *w;
+  const int32_t *doc;
+  gdla_grads grads;
+  const f16_t *cq16;            // [M, d_cq] c^Q of the forward
+  const float *aq, *ckv;        // [M, d_cq], [M, d_c] before RMSNorm
+  const bf16_t *cache;          // [B, T, d_c + d_r] cache rows of the forward
+  const f16_t *q16, *kx, *vk;   // forward operands (see BwdAttnArgs)
+  const float *heads, *lse, *lam;
+  const f16_t *sg16, *y16;      // sigmoid(G), Y of the forward [M, n_S d_h]
+  int32_t lam_overridden;
+  FastBwdBuffers buf;
+  int32_t B, T, M, M_pad, lcap, k8;
+};
+hipError_t launch_backward_fast(const FastBwdArgs &a, const LayerDims &d, hipStream_t s);
+
 }  // namespace gdla
+

@@ -246,6 +246,53 @@ BackwardLayout plan_backward(const LayerDims &d, int32_t B, int32_t T) {
   return L;
 }
 
+// Fast backward (bf16, the fused forward with transposed weights): the forward's workspace over T
+// positions from 0, its cache, output, per-head H, log-sum-exp and key-major V, then the buffers
+// of FastBwdBuffers.
+struct FastBackwardLayout {
+  PrefillLayout pre;
+  size_t cache, out, heads, lse, vk;
+  size_t fb[26];  // FastBwdBuffers fields, in order
+  size_t total;
+  int32_t M_pad, k8;
+  bool ok;
+};
+
+FastBackwardLayout plan_backward_fast(const LayerDims &d, int32_t B, int32_t T) {
+  FastBackwardLayout L{};
+  std::vector<int32_t> zeros((size_t)B, 0);
+  L.pre = plan_prefill(d, GDLA_BF16, B, T, zeros.data(), T);
+  L.ok = L.pre.use_fast && L.pre.use_nt && fast_backward_supported(d, GDLA_BF16);
+  if (!L.ok) return L;
+  const size_t M = (size_t)B * T, nH = d.n_heads, nS = d.n_signal, nKV = d.n_kv;
+  L.M_pad = (int32_t)((M + 63) / 64 * 64);
+  L.k8 = (d.d_cq + d.d_c + d.d_r + d.n_signal + 63) / 64 * 64;
+  const size_t Mp = L.M_pad, dm = d.d_model, dh = d.d_h, dr = d.d_r;
+  const size_t k3 = 2 * nKV * dh, k6 = nH * dh + nH * dr + nS * dh, k8 = L.k8;
+  Plan p;
+  p.bytes = L.pre.total;
+  L.cache = p.add(2 * M * (d.d_c + d.d_r));
+  L.out = p.add(2 * M * dm);
+  L.heads = p.add(4 * M * nH * dh);
+  L.lse = p.add(4 * M * nH);
+  L.vk = p.add(2 * (size_t)B * nKV * L.pre.lcap * dh);
+  const size_t trows_a = std::max({nS * dh, (size_t)d.d_c, (size_t)d.d_cq, dm});
+  const size_t trows_b = std::max({dm, k3, k6, k8});
+  const size_t bytes[26] = {
+      2 * nS * dh * dm, 2 * d.d_c * k3, 2 * d.d_cq * k6, 2 * dm * k8,      // wo16 w3 w6 w8
+      2 * M * dm, 4 * M * nS * dh,                                          // dout16 dy
+      2 * trows_a * Mp, 2 * trows_b * Mp,                                   // ta tb
+      4 * M * nH * dh, 4 * M * nS * dh, 4 * M * nS, 4 * M * nH,             // dheads dd dlaml drow
+      2 * M * nH * dh,                                                      // dh16
+      4 * M * nH * (dh + dr), 4 * M * nKV * (dh + dr), 4 * M * nKV * dh,    // dq dk dv
+      2 * M * k6, 2 * M * k3, 2 * M * k8,                                   // a6 a3 a8
+      4 * M * dr, 4 * M * d.d_c, 4 * M * d.d_c, 4 * M, 4 * M * d.d_cq, 4 * M * d.d_cq, 4 * M};
+  static_assert(sizeof(FastBwdBuffers) == 26 * sizeof(void *), "one size per buffer");
+  for (int i = 0; i < 26; ++i) L.fb[i] = p.add(bytes[i]);
+  L.total = p.bytes;
+  return L;
+}
+
 // ---------------------------------------------------------------------------------------------
 gdla_status check_call(const gdla_dims *dims, const gdla_weights *w, const void *x, int32_t B,
                        int32_t T, const int32_t *pos, const void *cache, int32_t max_len,
@@ -418,7 +465,13 @@ GDLA_EXPORT size_t gdla_workspace_bytes(const gdla_dims *dims, int32_t op, int32
     case GDLA_OP_DECODE: return plan_decode(d, dims->dtype, B, T, max_len).total;
     case GDLA_OP_APPEND: return plan_append(d, B, T).total;
     case GDLA_OP_PREFILL_PAGED: return plan_prefill_paged(d, dims->dtype, B, T, pos_host, max_len).total;
-    case GDLA_OP_BACKWARD: return plan_backward(d, B, T).total;
+    case GDLA_OP_BACKWARD: {
+      if (dims->dtype == GDLA_BF16) {
+        const FastBackwardLayout F = plan_backward_fast(d, B, T);
+        if (F.ok) return F.total;
+      }
+      return plan_backward(d, B, T).total;
+    }
     default: return 0;
   }
 }
@@ -489,7 +542,7 @@ namespace {
 gdla_status prefill_impl(const gdla_dims *dims, const gdla_weights *w, const void *x, int32_t B, int32_t T,
                          const int32_t *pos_host, void *cache, int32_t max_len, void *out, void *ws,
                          size_t ws_bytes, const gdla_debug *dbg, hipStream_t stream,
-                         const int32_t *doc = nullptr) {
+                         const int32_t *doc = nullptr, float *lse = nullptr) {
   LayerDims d;
   gdla_status st = check_call(dims, w, x, B, T, pos_host, cache, max_len, out, true, d);
   if (st != GDLA_OK || B == 0 || T == 0) return st;
@@ -580,7 +633,7 @@ gdla_status prefill_impl(const gdla_dims *dims, const gdla_weights *w, const voi
     st = run_fast_prefill(d, w, B, T, pos_dev, pos_host, cache, max_len, at<void>(ws, L.cq),
                           at<float>(ws, L.lam), at<float>(ws, L.gate), at<void>(ws, L.kx),
                           at<void>(ws, L.vx), L.lcap, at<void>(ws, L.y), out_heads, L.fast, ws,
-                          stream, se, L.use_nt ? &ntw : nullptr, doc);
+                          stream, se, L.use_nt ? &ntw : nullptr, doc, lse);
     if (st != GDLA_OK) return fail(st, "fast prefill path failed: %s", hipGetErrorString(hipGetLastError()));
   } else {
     // Eq.(2), (9): q^C, pre-RoPE q^R and gate logits.
@@ -782,6 +835,67 @@ GDLA_EXPORT gdla_status gdla_decode_paged(const gdla_dims *dims, const gdla_weig
   return decode_impl(dims, w, x, B, T, pos_host, c, out, ws, ws_bytes, dbg, stream);
 }
 
+namespace gdla {
+namespace {
+
+gdla_status backward_fast(const gdla_dims *dims, const gdla_weights *w, const void *x, int32_t B, int32_t T,
+                          const int32_t *doc, const void *dout, const gdla_grads *grads, void *ws,
+                          const gdla_debug *dbg, hipStream_t stream, const LayerDims &d, const FastBackwardLayout &F) {
+  const PrefillLayout &PL = F.pre;
+  const int32_t M = B * T;
+  // the forward again, keeping per-head H and the log-sum-exp of every row and head
+  std::vector<int32_t> zeros((size_t)B, 0);
+  gdla_debug fdbg{};
+  fdbg.lambda_override = dbg ? dbg->lambda_override : nullptr;
+  fdbg.out_heads = at<float>(ws, F.heads);
+  gdla_status st = prefill_impl(dims, w, x, B, T, zeros.data(), at<void>(ws, F.cache), T, at<void>(ws, F.out), ws,
+                                PL.total, &fdbg, stream, doc, at<float>(ws, F.lse));
+  if (st != GDLA_OK) return st;
+  // V key-major per KV head: cbar W_uv (the forward keeps V transposed)
+  {
+    const int64_t row = d.d_c + d.d_r;
+    GemmBatch g{};
+    for (int32_t b0 = 0; b0 < B; b0 += kMaxGemmProblems) {
+      g = GemmBatch{};
+      for (int32_t b = b0; b < std::min(B, b0 + kMaxGemmProblems); ++b) {
+        GemmProblem pv = gp(at<char>(ws, F.cache) + (int64_t)b * T * row * 2, row, at<void>(ws, PL.wt_uv), d.d_c,
+                            at<char>(ws, F.vk) + (int64_t)b * d.n_kv * PL.lcap * d.d_h * 2, d.d_h, T,
+                            d.n_kv * d.d_h, d.d_c, false);
+        pv.hw = d.d_h;
+        pv.hs = (int64_t)PL.lcap * d.d_h;
+        pv.c_dt = CD_F16;
+        g.p[g.n++] = pv;
+      }
+      HIP_TRY(launch_gemm_nt(g, false, stream));
+    }
+  }
+  FastBwdArgs a{};
+  a.x = x; a.dout = dout; a.w = w; a.doc = doc; a.grads = *grads;
+  if (!w->gamma_q) a.grads.dgamma_q = nullptr;
+  if (!w->gamma_kv) a.grads.dgamma_kv = nullptr;
+  a.cq16 = at<f16_t>(ws, PL.cq);
+  a.aq = at<float>(ws, PL.aq);
+  a.ckv = at<float>(ws, PL.ckv);
+  a.cache = at<bf16_t>(ws, F.cache);
+  a.q16 = at<f16_t>(ws, PL.fast.q);
+  a.kx = at<f16_t>(ws, PL.kx);
+  a.vk = at<f16_t>(ws, F.vk);
+  a.heads = at<float>(ws, F.heads);
+  a.lse = at<float>(ws, F.lse);
+  a.lam = at<float>(ws, PL.lam);
+  a.sg16 = at<f16_t>(ws, PL.gate);
+  a.y16 = at<f16_t>(ws, PL.y);
+  a.lam_overridden = fdbg.lambda_override ? 1 : 0;
+  void **bufs = (void **)&a.buf;
+  for (int i = 0; i < 26; ++i) bufs[i] = at<void>(ws, F.fb[i]);
+  a.B = B; a.T = T; a.M = M; a.M_pad = F.M_pad; a.lcap = PL.lcap; a.k8 = F.k8;
+  HIP_TRY(launch_backward_fast(a, d, stream));
+  return GDLA_OK;
+}
+
+}  // namespace
+}  // namespace gdla
+
 GDLA_EXPORT gdla_status gdla_backward(const gdla_dims *dims, const gdla_weights *w, const void *x, int32_t B,
                                       int32_t T, const int32_t *doc_start, const void *dout,
                                       const gdla_grads *grads, void *ws, size_t ws_bytes, const gdla_debug *dbg,
@@ -809,6 +923,13 @@ GDLA_EXPORT gdla_status gdla_backward(const gdla_dims *dims, const gdla_weights 
     return fail(GDLA_ERR_INVALID_ARG, "dgamma_q / dgamma_kv are required with gamma_q / gamma_kv");
   if (((uintptr_t)doc_start & 3u) != 0) return fail(GDLA_ERR_INVALID_ARG, "doc_start must be 4-byte aligned");
   if (d.d_h > 256) return fail(GDLA_ERR_UNSUPPORTED, "d_head > 256");
+  if (dims->dtype == GDLA_BF16) {
+    const FastBackwardLayout F = plan_backward_fast(d, B, T);
+    if (F.ok) {
+      if ((st = check_ws(ws, ws_bytes, F.total)) != GDLA_OK) return st;
+      return backward_fast(dims, w, x, B, T, doc_start, dout, grads, ws, dbg, stream, d, F);
+    }
+  }
   const BackwardLayout L = plan_backward(d, B, T);
   if ((st = check_ws(ws, ws_bytes, L.total)) != GDLA_OK) return st;
   BackwardArgs a{};

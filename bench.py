@@ -72,6 +72,53 @@ def layer_flops(cfg, t, p0, window, docs=None):
             "total": attn_signal + attn_noise + proj + expand, "pairs": pairs}
 
 
+def backward_flops(cfg, t, window, docs=None):
+    """Algorithmic FLOP of one backward call on one sequence at positions 0..t-1: the forward it
+    recomputes plus the gradients (per visible pair and head: the score, dP = dH V^T, dq, dK and
+    dV products; every projection and the expansion twice, for the data and the weight gradient)."""
+    f = layer_flops(cfg, t, 0, window, docs)
+    dqk, dh = cfg["d_head"] + cfg["d_rope"], cfg["d_head"]
+    attn = 2.0 * cfg["n_heads"] * f["pairs"] * (3 * dqk + 2 * dh)
+    return {"forward": f["total"], "attention": attn, "proj": 2.0 * (f["proj"] + f["expand"]),
+            "total": f["total"] + attn + 2.0 * (f["proj"] + f["expand"])}
+
+
+def bench_backward(args):
+    """Times gdla_backward on the workload's shape (training sequences from position 0)."""
+    import torch
+    import synth
+    import attention_gdla_prefill_decode_amd as gd
+    cfg = synth.WORKLOADS[args.workload]
+    bsz, t, win = cfg["batch"], cfg["seq"], cfg["window"]
+    inp = synth.make_inputs(cfg, "cuda", p0=0)
+    dims = gd.make_dims(cfg)
+    w = gd.make_weights(inp["weights"])
+    tensors = dict(inp["weights"], gamma_q=None, gamma_kv=None)
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    dout = torch.randn(inp["x"].shape, generator=gen, device="cuda").to(inp["x"].dtype)
+    docs = None
+    doc_t = None
+    if args.docs > 0:
+        docs = packed_documents(t, args.docs)
+        doc_t = torch.tensor([docs] * bsz, dtype=torch.int32, device="cuda")
+    ws = torch.empty(gd.gdla_workspace_bytes(dims, gd.GDLA_OP_BACKWARD, bsz, t, None, t), dtype=torch.uint8,
+                     device="cuda")
+    for _ in range(args.warmup):
+        g = gd.gdla_backward(dims, w, tensors, inp["x"], dout, doc_start=doc_t, ws=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        g = gd.gdla_backward(dims, w, tensors, inp["x"], dout, doc_start=doc_t, ws=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    fl = {k: v * bsz for k, v in backward_flops(cfg, t, win, docs).items()}
+    return {"workload": args.workload + "_backward", "batch": bsz, "seq_len": t, "window": win,
+            "ms_per_call": round(ms, 3), "TFLOPs": round(fl["total"] / (ms * 1e-3) / 1e12, 2),
+            "flop_per_call": fl, "grads_finite": bool(all(torch.isfinite(v).all().item() for v in g.values()))}
+
+
 def source_sha(rel):
     h = hashlib.sha256()
     with open(os.path.join(ROOT, rel), "rb") as f:
@@ -242,6 +289,9 @@ def main():
     ap.add_argument("--docs", type=float, default=0,
                     help="prefill workloads: pack the tokens into documents of this mean length "
                          "(seeded exponential lengths; gdla_prefill_packed)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time gdla_backward (training sequences from position 0) on the workload's "
+                         "shape instead of the forward; prints its JSON object")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 1 GiB device to device three times (a known-size reference "
@@ -264,6 +314,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes_per_launch": n, "launches": 3}), flush=True)
+        return
+
+    if args.backward:
+        print(json.dumps(bench_backward(args)), flush=True)
         return
 
     if args.decode_only:

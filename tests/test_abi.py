@@ -246,3 +246,27 @@ def test_packed_prefill_argument_errors():
     assert call(FAKE + 2) == gb.GDLA_ERR_INVALID_ARG
     assert call(FAKE, ws_bytes=16) == gb.GDLA_ERR_WORKSPACE
     assert call(FAKE, T=65) == gb.GDLA_ERR_OUT_OF_RANGE
+
+
+def test_backward_argument_errors():
+    lib = gd.lib()
+    d = big_dims()
+    w = gb.GdlaWeights(*([FAKE] * 12))
+    full = gb.GdlaGrads(*([FAKE] * 13))
+
+    def call(grads=full, x=FAKE, dout=FAKE, doc=None, ws_bytes=1 << 40, T=16):
+        return lib.gdla_backward(ctypes.byref(d), ctypes.byref(w), x, 1, T, doc, dout, ctypes.byref(grads), FAKE,
+                                 ws_bytes, None, None)
+
+    assert call(x=None) == gb.GDLA_ERR_INVALID_ARG
+    assert call(dout=None) == gb.GDLA_ERR_INVALID_ARG
+    no_dx = gb.GdlaGrads(*([None] + [FAKE] * 12))
+    assert call(grads=no_dx) == gb.GDLA_ERR_INVALID_ARG
+    no_dgamma = gb.GdlaGrads(*([FAKE] * 11 + [None, FAKE]))  # gamma_q is set, dgamma_q missing
+    assert call(grads=no_dgamma) == gb.GDLA_ERR_INVALID_ARG
+    assert call(doc=FAKE + 2) == gb.GDLA_ERR_INVALID_ARG
+    assert call(x=FAKE + 2) == gb.GDLA_ERR_INVALID_ARG
+    assert call(ws_bytes=16) == gb.GDLA_ERR_WORKSPACE
+    assert lib.gdla_last_error().decode()
+    assert call(T=0, x=None, dout=None) == gb.GDLA_OK
+    assert gd.gdla_workspace_bytes(d, gd.GDLA_OP_BACKWARD, 1, 16, None, 16) > 0

@@ -256,6 +256,23 @@ def test_backward_matches_oracle(cfg, T, batch, window, lens):
         _say(line)
 
 
+# With at least 256 rows the backward runs fused: fp16 MFMA operands (gradients, activations and
+# weights each rounded once to fp16, 2^-11 relative), fp32 accumulation, on top of the forward's
+# own roundings (bf16 cache rows, 2^-9).  The deepest gradients pass about eight such roundings:
+# about 2.3e-3 in quadrature, so 1e-2 leaves a factor of four.
+@pytest.mark.parametrize("cfg,T,batch,window,lens", [
+    (BF, 300, 1, 0, None),
+    (BF, 160, 2, 20, (37, 90, 33)),
+    (H.BF80, 256, 1, 0, None),
+    (H.BF72, 270, 1, 64, (200, 70)),
+])
+def test_backward_fused_matches_oracle(cfg, T, batch, window, lens):
+    docs = None if lens is None else [H.doc_starts(0, lens) for _ in range(batch)]
+    got, exp = H.backward_case(cfg, T, batch, window=window, docs=docs, seed=73)
+    for line in H.check_grads(got, exp, 1e-2, f"fused backward n_H={cfg['n_heads']} T={T} W={window}"):
+        _say(line)
+
+
 def test_backward_lambda_zero():
     got, exp = H.backward_case(BF, 48, 1, seed=71, lam_zero=True)
     H.check_grads(got, exp, 1e-5, "backward, lambda = 0")
