@@ -61,7 +61,7 @@ struct AttnArgs {
   float *hn;              // [M, n_N, 128] normalised noise-head outputs
   f16_t *y;               // [M, n_S * 128] fp16
   float *out_heads;       // [M, n_H, 128] or null
-  float *lse;             // [M, n_H] or null: log2 of the softmax denominator of the log2e-scaled scores
+  float *lse;             // [n_H, M] or null: log2 of the softmax denominator of the log2e-scaled scores
   int32_t T, lcap;
   int32_t n_heads, n_signal, n_noise, n_kv, window;
   int32_t sig_per_kv, chunks, n_qblk;
@@ -338,7 +338,7 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
   if (t >= a.T) return;
   const int64_t mr = mrow0 + t;
   // the probabilities are exp2(c s - lse) for raw scores s (what a backward pass recomputes)
-  if (a.lse && hgrp == 0) a.lse[mr * a.n_heads + head] = m * a.c + __log2f(lsum);
+  if (a.lse && hgrp == 0) a.lse[(int64_t)head * a.nb * a.T + mr] = m * a.c + __log2f(lsum);  // head-major
   float *oh = a.out_heads ? a.out_heads + (mr * a.n_heads + head) * DH : nullptr;
   if (!SIGNAL) {
     float *hn = a.hn + (mr * a.n_noise + (head - a.n_signal)) * DH;

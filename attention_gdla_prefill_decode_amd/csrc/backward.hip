@@ -406,16 +406,20 @@ __global__ void __launch_bounds__(256) bwd_noise_lambda_kernel(const float *head
   }
 }
 
-// drow[m, h] = sum_e dH (.) H
+// drow[m, h] = sum_e dH (.) H, row r = m n_H + h stored at r, or (head_major, n_heads given) at
+// h M + m
 __global__ void __launch_bounds__(256) bwd_drow_kernel(const float *heads, const float *dheads, float *drow,
-                                                       int64_t rows, int32_t d_h) {
+                                                       int64_t rows, int32_t d_h, int32_t head_major_nh) {
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
   float acc = 0.f;
   for (int e = lane; e < d_h; e += 64) acc += heads[r * d_h + e] * dheads[r * d_h + e];
   acc = wsum(acc);
-  if (lane == 0) drow[r] = acc;
+  if (lane == 0) {
+    if (head_major_nh > 0) drow[(r % head_major_nh) * (rows / head_major_nh) + r / head_major_nh] = acc;
+    else drow[r] = acc;
+  }
 }
 
 // RMSNorm backward of y = v rinv (.) gamma per row: dv = rinv (u - v rinv^2 (u . v) / n), u = dy (.) gamma
@@ -513,7 +517,7 @@ hipError_t backward_t(const BackwardArgs &ba, const LayerDims &d, hipStream_t s)
                      0, s, b.heads, b.lam, b.dd, b.dheads, b.dlaml, ba.lam_override ? 1 : 0, M, d);
   BWD_TRY(hipGetLastError());
   // ---- the softmax maps
-  hipLaunchKernelGGL(bwd_drow_kernel, dim3(gh), dim3(256), 0, s, b.heads, b.dheads, b.drow, (int64_t)M * nH, dh);
+  hipLaunchKernelGGL(bwd_drow_kernel, dim3(gh), dim3(256), 0, s, b.heads, b.dheads, b.drow, (int64_t)M * nH, dh, 0);
   BWD_TRY(hipGetLastError());
   hipLaunchKernelGGL(bwd_attn_dq_kernel, dim3(gh), dim3(256), 0, s, at, d);
   BWD_TRY(hipGetLastError());
@@ -734,6 +738,16 @@ __global__ void __launch_bounds__(256) zero_cols_kernel(f16_t *dst, int64_t ldd,
     dst[(i / w) * ldd + c0 + i % w] = (f16_t)0.f;
 }
 
+// lo[m] = lowest visible key of token t = m % T (window and document start)
+__global__ void __launch_bounds__(256) qlo_kernel(const int32_t *doc, int32_t *lo, int32_t M, int32_t T_, int32_t window) {
+  const int m = blockIdx.x * 256 + threadIdx.x;
+  if (m >= M) return;
+  const int t = m % T_;
+  int v = window > 0 ? max(0, t - window + 1) : 0;
+  if (doc) v = max(v, min(max(doc[m], 0), t));
+  lo[m] = v;
+}
+
 __global__ void __launch_bounds__(256) to_f16_kernel(const float *src, f16_t *dst, int64_t n) {
   for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) dst[i] = f16s(src[i]);
 }
@@ -811,7 +825,9 @@ hipError_t launch_backward_fast(const FastBwdArgs &a, const LayerDims &d, hipStr
                      0, s, a.heads, a.lam, b.dd, b.dheads, b.dlaml, a.lam_overridden ? 1 : 0, M, d);
   BWD_TRY(hipGetLastError());
   hipLaunchKernelGGL(bwd_drow_kernel, dim3((unsigned)(((int64_t)M * nH + 3) / 4)), dim3(256), 0, s, a.heads,
-                     b.dheads, b.drow, (int64_t)M * nH, dh);
+                     b.dheads, b.drow, (int64_t)M * nH, dh, nH);
+  BWD_TRY(hipGetLastError());
+  hipLaunchKernelGGL(qlo_kernel, dim3(grid_for(M)), dim3(256), 0, s, a.doc, b.lo, M, T_, d.window);
   BWD_TRY(hipGetLastError());
   hipLaunchKernelGGL(to_f16_kernel, dim3(grid_for((int64_t)M * nH * dh)), dim3(256), 0, s, b.dheads, b.dh16,
                      (int64_t)M * nH * dh);
@@ -819,7 +835,8 @@ hipError_t launch_backward_fast(const FastBwdArgs &a, const LayerDims &d, hipStr
 
   // ---- the softmax maps
   BwdAttnArgs at{};
-  at.q = a.q16; at.k = a.kx; at.v = a.vk; at.dh = b.dh16; at.lse = a.lse; at.drow = b.drow; at.doc = a.doc;
+  at.q = a.q16; at.k = a.kx; at.v = a.vk; at.dh = b.dh16; at.lse = a.lse; at.drow = b.drow; at.lo = b.lo;
+  at.doc = a.doc;
   at.dq = b.dq; at.dk = b.dk; at.dv = b.dv;
   at.B = a.B; at.T = T_; at.lcap = a.lcap; at.n_heads = nH; at.n_signal = nS; at.n_noise = d.n_noise;
   at.n_kv = nKV; at.window = d.window; at.c = d.scale * 1.4426950408889634f; at.tau = d.scale;

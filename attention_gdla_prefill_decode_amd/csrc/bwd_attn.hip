@@ -103,7 +103,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdAttnArgs a) {
   const int tqc = min(tq, a.T - 1);
   const int64_t mh = ((int64_t)b * a.T + tqc) * a.n_heads + (head >= 0 ? head : 0);
   const int wlim = qok ? tqc - qlo(a, b, tqc) + 1 : 0;  // key s visible iff 0 <= t - s < wlim
-  const float lse = qok ? a.lse[mh] : 0.f, drow = qok ? a.drow[mh] : 0.f;
+  const int64_t hm = (int64_t)(head >= 0 ? head : 0) * a.B * a.T + (int64_t)b * a.T + tqc;  // head-major
+  const float lse = qok ? a.lse[hm] : 0.f, drow = qok ? a.drow[hm] : 0.f;
   f16x8 Qf[12], Hf[8];
 #pragma unroll
   for (int k = 0; k < 12; ++k) Qf[k] = *(const f16x8 *)(a.q + mh * DQK + 16 * k + 8 * (lane >> 5));
@@ -199,34 +200,48 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdAttnArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// dK, dV.  Workgroup (key block of 64, KV head, sequence); wave w takes keys 32 (w & 1) .. of the
-// block and the query blocks of parity w >> 1, over every head of the KV group.  The two parities
-// are added through LDS at the end.
-constexpr int QT_BYTES = 32 * KP * 2 + 32 * VP * 2 + 3 * 32 * 4;  // Q, dH, lse, drow, lo of 32 queries
+// dK, dV.  Workgroup (key block of 128, KV head, sequence); wave w holds keys 32 w .. 32 w + 31 of
+// the block.  The waves walk the query blocks of 32 of every head of the group together: each
+// block's Q, dH, log-sum-exp, row sum and lowest visible keys come by direct global -> LDS loads
+// (M0 + 16 lane per wave-instruction, no compiler tracking) into three buffers, two blocks in
+// flight while one is read.  A buffer is 24 wave-instructions of 64 slots of 16 bytes:
+//   Q rows 0..31 at 25 slots per row (24 of data, one of padding), then dH rows at 17 slots per
+//   row, then lse, row sum (fp32) and lowest visible key (int32) of the 32 queries, 8 slots each;
+//   padding slots receive a copy of a neighbouring chunk.
+constexpr int DMA_W = 6;                       // wave-instructions per wave and block
+constexpr int TB_SLOTS = 4 * DMA_W * 64;       // 1536 slots
+constexpr int TB_BYTES = TB_SLOTS * 16;        // 24 KB
+constexpr int Q_SLOTS = 32 * 25, H_SLOTS = 32 * 17;
+constexpr int S_OFF = (Q_SLOTS + H_SLOTS) * 16;  // bytes: lse [32], drow [32], lo [32]
+
+__device__ __forceinline__ void dma16v(const void *gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(lds_addr) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_u32(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
 
 __global__ void __launch_bounds__(256, 1) bwd_dkv_kernel(BwdAttnArgs a) {
-  __shared__ __attribute__((aligned(16))) char SM[2 * 2 * QT_BYTES];  // [buffer][parity]
+  __shared__ __attribute__((aligned(16))) char SM[3 * TB_BYTES];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kh = wave & 1, par = wave >> 1;
   const int per_k = a.n_kv * a.B;
   const int kblk = (int)blockIdx.x / per_k;  // longest work (first keys) first
   const int kvh = (int)blockIdx.x % per_k % a.n_kv, b = (int)blockIdx.x % per_k / a.n_kv;
-  const int kb0 = 64 * kblk;
+  const int kb0 = 128 * kblk;
+  const int64_t M = (int64_t)a.B * a.T;
   // queries kb0 .. q_end - 1 can see a key of the block: lowest visible keys never decrease
   int lo_q = kb0, hi_q = a.T;
   while (lo_q < hi_q) {
     const int mid = (lo_q + hi_q) >> 1;
-    if (qlo(a, b, mid) > kb0 + 63) hi_q = mid;
+    if (qlo(a, b, mid) > kb0 + 127) hi_q = mid;
     else lo_q = mid + 1;
   }
-  const int q_end = lo_q;
-  const int qb0 = kb0 / 32, nqb = max(0, (q_end - kb0 + 31) / 32);
-  const int its = (nqb + 1) / 2;
+  const int qb0 = kb0 / 32, nqb = max(0, (lo_q - kb0 + 31) / 32);
   const int sig_g = a.n_signal / a.n_kv, n_g = a.n_heads / a.n_kv;
-  const int n_it = n_g * its;
+  const int n_it = n_g * nqb;
 
   // this wave's keys: K^T and V^T as B operands (B[k = dim][n = key])
-  const int key = kb0 + 32 * kh + (lane & 31);
+  const int key = kb0 + 32 * wave + (lane & 31);
   const int keyc = min(key, a.T - 1);
   const f16_t *kg = a.k + (((int64_t)b * a.n_kv + kvh) * a.lcap + keyc) * DQK;
   const f16_t *vg = a.v + (((int64_t)b * a.n_kv + kvh) * a.lcap + keyc) * DH;
@@ -235,142 +250,98 @@ __global__ void __launch_bounds__(256, 1) bwd_dkv_kernel(BwdAttnArgs a) {
   for (int k = 0; k < 12; ++k) Kf[k] = *(const f16x8 *)(kg + 16 * k + 8 * (lane >> 5));
 #pragma unroll
   for (int k = 0; k < 8; ++k) Vf[k] = *(const f16x8 *)(vg + 16 * k + 8 * (lane >> 5));
+  // the key fragments have landed before any block load is issued (the block waits below count
+  // only those loads)
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   f32x16 dK[6], dV[4];
 #pragma unroll
   for (int i = 0; i < 6; ++i) dK[i] = f32x16{};
 #pragma unroll
   for (int i = 0; i < 4; ++i) dV[i] = f32x16{};
 
-  // staging of one query block by the 128 threads of its parity (u = tid & 127)
-  const int u = tid & 127;
-  uint4 qr[6], hr[4];
-  float sr = 0.f, dr = 0.f;
-  int lr = 0;
   auto head_of = [&](int gi) { return gi < sig_g ? kvh + a.n_kv * gi : a.n_signal + kvh + a.n_kv * (gi - sig_g); };
-  auto load = [&](int it) {
-    const int h = head_of(it / its), qb = qb0 + 2 * (it % its) + par;
-    const int qbase = 32 * qb;
+  // block `it` into buffer it % 3: this lane's DMA_W slots are (wave + 4 i) * 64 + lane
+  const uint32_t lds0 = lds_u32(SM);
+  auto issue = [&](int it) {
+    const int h = head_of(it / nqb), qbase = 32 * (qb0 + it % nqb);
+    const int64_t mrow = (int64_t)b * a.T;
+    const uint32_t buf = lds0 + (uint32_t)((it % 3) * TB_BYTES);
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      const int c = u + 128 * i, row = c / 24, ch = c % 24;
-      const int t = min(qbase + row, a.T - 1);
-      qr[i] = *(const uint4 *)(a.q + (((int64_t)b * a.T + t) * a.n_heads + h) * DQK + 8 * ch);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = u + 128 * i, row = c / 16, ch = c % 16;
-      const int t = min(qbase + row, a.T - 1);
-      hr[i] = *(const uint4 *)(a.dh + (((int64_t)b * a.T + t) * a.n_heads + h) * DH + 8 * ch);
-    }
-    if (u < 32) {
-      const int t = min(qbase + u, a.T - 1);
-      const int64_t mh = ((int64_t)b * a.T + t) * a.n_heads + h;
-      sr = a.lse[mh];
-      dr = a.drow[mh];
-      lr = qbase + u < a.T ? qlo(a, b, t) : 0x7fffffff;  // rows past T see nothing
-    }
-  };
-  auto tile = [&](int buf, int p) { return SM + (2 * buf + p) * QT_BYTES; };
-  auto store = [&](int buf) {
-    char *base = tile(buf, par);
-    f16_t *qs = (f16_t *)base, *hs = (f16_t *)(base + 32 * KP * 2);
-    float *ls = (float *)(base + 32 * KP * 2 + 32 * VP * 2);
-#pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      const int c = u + 128 * i, row = c / 24, ch = c % 24;
-      *(uint4 *)(qs + row * KP + 8 * ch) = qr[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = u + 128 * i, row = c / 16, ch = c % 16;
-      *(uint4 *)(hs + row * VP + 8 * ch) = hr[i];
-    }
-    if (u < 32) {
-      ls[u] = sr;
-      ls[32 + u] = dr;
-      ((int *)ls)[64 + u] = lr;
+    for (int i = 0; i < DMA_W; ++i) {
+      const int slot = (wave + 4 * i) * 64 + lane;
+      const void *src;
+      if (slot < Q_SLOTS) {
+        const int r = slot / 25, c = min(slot % 25, 23);
+        const int t = min(qbase + r, a.T - 1);
+        src = a.q + ((mrow + t) * a.n_heads + h) * DQK + 8 * c;
+      } else if (slot < Q_SLOTS + H_SLOTS) {
+        const int s2 = slot - Q_SLOTS, r = s2 / 17, c = min(s2 % 17, 15);
+        const int t = min(qbase + r, a.T - 1);
+        src = a.dh + ((mrow + t) * a.n_heads + h) * DH + 8 * c;
+      } else {
+        const int s3 = min(slot - Q_SLOTS - H_SLOTS, 23), part = s3 >> 3, k4 = 4 * (s3 & 7);
+        // the three arrays carry 32 entries of padding past their end
+        if (part == 0) src = a.lse + (int64_t)h * M + mrow + qbase + k4;
+        else if (part == 1) src = a.drow + (int64_t)h * M + mrow + qbase + k4;
+        else src = a.lo + mrow + qbase + k4;
+      }
+      dma16v(src, __builtin_amdgcn_readfirstlane(buf + (uint32_t)((wave + 4 * i) * 64 * 16)));
     }
   };
 
-  if (n_it > 0) {
-    load(0);
-    store(0);
-  }
-  __syncthreads();
+  for (int it = 0; it < 2 && it < n_it; ++it) issue(it);
   for (int it = 0; it < n_it; ++it) {
-    if (it + 1 < n_it) load(it + 1);
-    const int qb = qb0 + 2 * (it % its) + par;
-    if (qb < qb0 + nqb) {
-      const char *base = tile(it & 1, par);
-      const f16_t *qs = (const f16_t *)base, *hs = (const f16_t *)(base + 32 * KP * 2);
-      const float *ls = (const float *)(base + 32 * KP * 2 + 32 * VP * 2);
-      f32x16 S = {}, dP = {};
+    // at most this wave's loads of block it + 1 still in flight
+    if (it + 1 < n_it) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_W) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // block it has landed for every wave; every wave is done with block it - 1
+    if (it + 2 < n_it) issue(it + 2);
+    const int qbase = 32 * (qb0 + it % nqb);
+    const char *base = SM + (it % 3) * TB_BYTES;
+    const f16_t *qs = (const f16_t *)base, *hs = (const f16_t *)(base + Q_SLOTS * 16);
+    const float *ls = (const float *)(base + S_OFF);
+    const int *los = (const int *)(base + S_OFF + 64 * 4);
+    f32x16 S = {}, dP = {};
 #pragma unroll
-      for (int k = 0; k < 12; ++k) S = mfma(*(const f16x8 *)(qs + (lane & 31) * KP + 16 * k + 8 * (lane >> 5)), Kf[k], S);
+    for (int k = 0; k < 12; ++k) S = mfma(*(const f16x8 *)(qs + (lane & 31) * KP + 16 * k + 8 * (lane >> 5)), Kf[k], S);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) dP = mfma(*(const f16x8 *)(hs + (lane & 31) * VP + 16 * k + 8 * (lane >> 5)), Vf[k], dP);
-      // acc[j]: query 32 qb + qi, qi = 8 (j / 4) + 4 (l / 32) + j % 4; key `key`
-      f16x8 pf[2], dsf[2];
+    for (int k = 0; k < 8; ++k) dP = mfma(*(const f16x8 *)(hs + (lane & 31) * VP + 16 * k + 8 * (lane >> 5)), Vf[k], dP);
+    // acc[j]: query qbase + qi, qi = 8 (j / 4) + 4 (l / 32) + j % 4; key `key`
+    f16x8 pf[2], dsf[2];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int qi = 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
-        const int t = 32 * qb + qi;
-        const bool vis = key <= t && key >= ((const int *)ls)[64 + qi];
-        const float p = vis ? __builtin_amdgcn_exp2f(S[j] * a.c - ls[qi]) : 0.f;
-        pf[j >> 3][j & 7] = h16(p);
-        dsf[j >> 3][j & 7] = h16(vis ? p * (dP[j] - ls[32 + qi]) : 0.f);
-      }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-        for (int eb = 0; eb < 4; ++eb) dV[eb] = mfma(tr_frag(hs, VP, 16 * kk, 32 * eb, lane), pf[kk], dV[eb]);
-#pragma unroll
-        for (int db = 0; db < 6; ++db) dK[db] = mfma(tr_frag(qs, KP, 16 * kk, 32 * db, lane), dsf[kk], dK[db]);
-      }
+    for (int j = 0; j < 16; ++j) {
+      const int qi = 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+      const int t = qbase + qi;
+      const bool vis = key <= t && t < a.T && key >= los[qi];
+      const float p = vis ? __builtin_amdgcn_exp2f(S[j] * a.c - ls[qi]) : 0.f;
+      pf[j >> 3][j & 7] = h16(p);
+      dsf[j >> 3][j & 7] = h16(vis ? p * (dP[j] - ls[32 + qi]) : 0.f);
     }
-    if (it + 1 < n_it) store((it + 1) & 1);  // last read in iteration it - 1
-    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int eb = 0; eb < 4; ++eb) dV[eb] = mfma(tr_frag(hs, VP, 16 * kk, 32 * eb, lane), pf[kk], dV[eb]);
+#pragma unroll
+      for (int db = 0; db < 6; ++db) dK[db] = mfma(tr_frag(qs, KP, 16 * kk, 32 * db, lane), dsf[kk], dK[db]);
+    }
   }
-
-  // parity 1 hands its sums to parity 0 through LDS (the tile buffers are free now)
-  float *red = (float *)SM + kh * (10 * 16 * 64);
-  if (par == 1) {
-#pragma unroll
-    for (int db = 0; db < 6; ++db)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) red[(db * 16 + j) * 64 + lane] = dK[db][j];
-#pragma unroll
-    for (int eb = 0; eb < 4; ++eb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) red[((6 + eb) * 16 + j) * 64 + lane] = dV[eb][j];
-  }
-  __syncthreads();
-  if (par == 1 || key >= a.T) return;
+  if (key >= a.T) return;
   // dK[db][j] = dK^T[dim 32 db + 8 (j / 4) + 4 (l / 32) + j % 4][key]
   const int64_t ko = ((int64_t)b * a.n_kv + kvh) * a.T + key;
   float *dk = a.dk + ko * DQK, *dv = a.dv + ko * DH;
 #pragma unroll
   for (int db = 0; db < 6; ++db)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float4 v;
-      v.x = (dK[db][4 * i] + red[(db * 16 + 4 * i) * 64 + lane]) * a.tau;
-      v.y = (dK[db][4 * i + 1] + red[(db * 16 + 4 * i + 1) * 64 + lane]) * a.tau;
-      v.z = (dK[db][4 * i + 2] + red[(db * 16 + 4 * i + 2) * 64 + lane]) * a.tau;
-      v.w = (dK[db][4 * i + 3] + red[(db * 16 + 4 * i + 3) * 64 + lane]) * a.tau;
-      *(float4 *)(dk + 32 * db + 8 * i + 4 * (lane >> 5)) = v;
-    }
+    for (int i = 0; i < 4; ++i)
+      *(float4 *)(dk + 32 * db + 8 * i + 4 * (lane >> 5)) =
+          make_float4(dK[db][4 * i] * a.tau, dK[db][4 * i + 1] * a.tau, dK[db][4 * i + 2] * a.tau,
+                      dK[db][4 * i + 3] * a.tau);
 #pragma unroll
   for (int eb = 0; eb < 4; ++eb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float4 v;
-      v.x = dV[eb][4 * i] + red[((6 + eb) * 16 + 4 * i) * 64 + lane];
-      v.y = dV[eb][4 * i + 1] + red[((6 + eb) * 16 + 4 * i + 1) * 64 + lane];
-      v.z = dV[eb][4 * i + 2] + red[((6 + eb) * 16 + 4 * i + 2) * 64 + lane];
-      v.w = dV[eb][4 * i + 3] + red[((6 + eb) * 16 + 4 * i + 3) * 64 + lane];
-      *(float4 *)(dv + 32 * eb + 8 * i + 4 * (lane >> 5)) = v;
-    }
+    for (int i = 0; i < 4; ++i)
+      *(float4 *)(dv + 32 * eb + 8 * i + 4 * (lane >> 5)) =
+          make_float4(dV[eb][4 * i], dV[eb][4 * i + 1], dV[eb][4 * i + 2], dV[eb][4 * i + 3]);
 }
 
 }  // namespace
@@ -382,13 +353,13 @@ bool fast_backward_supported(const LayerDims &d, gdla_dtype dt) {
 hipError_t launch_bwd_attention(const BwdAttnArgs &a0, hipStream_t s) {
   BwdAttnArgs a = a0;
   a.sig_chunks = (a.n_signal / a.n_kv + 3) / 4;
-  const int nq32 = (a.T + 31) / 32, nq128 = (a.T + 127) / 128, nk = (a.T + 63) / 64;
+  const int nq32 = (a.T + 31) / 32, nq128 = (a.T + 127) / 128, nk = (a.T + 127) / 128;
   hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3((unsigned)(nq32 * a.n_kv * a.sig_chunks * a.B)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3((unsigned)(nq128 * a.n_noise * a.B)), dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dkv_kernel, dim3((unsigned)(nk * a.n_kv * a.B)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(bwd_dkv_kernel, dim3((unsigned)(nk * a.n_kv * a.B)), dim3(256), 0, s, a);  // 128-key blocks
   return hipGetLastError();
 }
 

@@ -113,8 +113,9 @@ struct BwdAttnArgs {
   const f16_t *k;      // [B, n_kv, lcap, 192]: K^C ; k^R of keys 0 .. lcap - 1
   const f16_t *v;      // [B, n_kv, lcap, 128]: V, key-major
   const f16_t *dh;     // [M, n_H, 128]
-  const float *lse;    // [M, n_H]: log2 softmax denominators of c s
-  const float *drow;   // [M, n_H]: rowsum(dH (.) H)
+  const float *lse;    // [n_H, M] (+32 padding): log2 softmax denominators of c s
+  const float *drow;   // [n_H, M] (+32 padding): rowsum(dH (.) H)
+  const int32_t *lo;   // [M] (+32 padding): lowest visible key of every token
   const int32_t *doc;  // [M] document starts or null
   float *dq;           // [M, n_H, 192]
   float *dk;           // [B, n_kv, T, 192]: the k^R part summed over this KV group's heads only
@@ -136,6 +137,7 @@ struct FastBwdBuffers {
   float *dq, *dk, *dv;          // attention gradients
   f16_t *a6, *a3, *a8;          // gradient operands [M, k6], [M, k3], [M, k8]
   float *dkr, *dcbar, *dckv, *rkv, *dcq, *daq, *rq;
+  int32_t *lo;                  // [M + 32]
 };
 struct FastBwdArgs {
   const void *x, *dout;
@@ -146,7 +148,7 @@ struct FastBwdArgs {
   const float *aq, *ckv;        // [M, d_cq], [M, d_c] before RMSNorm
   const bf16_t *cache;          // [B, T, d_c + d_r] cache rows of the forward
   const f16_t *q16, *kx, *vk;   // forward operands (see BwdAttnArgs)
-  const float *heads, *lse, *lam;
+  const float *heads, *lse, *lam;  // lse: [n_H, M] (+32), from the forward
   const f16_t *sg16, *y16;      // sigmoid(G), Y of the forward [M, n_S d_h]
   int32_t lam_overridden;
   FastBwdBuffers buf;
