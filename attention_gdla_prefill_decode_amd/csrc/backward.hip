@@ -649,7 +649,7 @@ __global__ void __launch_bounds__(256) combine_fast_kernel(const float *heads, c
 // dq [M, n_H, 192] (fp32) -> the query-latent operand: columns h d_h + e (dq^C) and
 // q_off + h d_r + j (dq^R rotated back by RoPE's negative angle), row m at position m % T
 __global__ void __launch_bounds__(256) pack_dq_kernel(const float *dq, f16_t *a6, int64_t lda6, int32_t q_off,
-                                                      int32_t M, int32_t T_, LayerDims d) {
+                                                      int32_t M, int32_t T_, LayerDims d, const float2 *cs) {
   const int dqk = d.d_h + d.d_r, half = d.d_r / 2;
   const int per = d.d_h + half;  // elements handled per (m, h): d_h copies and d_r / 2 rotations
   const int64_t n = (int64_t)M * d.n_heads * per;
@@ -663,8 +663,8 @@ __global__ void __launch_bounds__(256) pack_dq_kernel(const float *dq, f16_t *a6
       a6[m * lda6 + (int64_t)h * d.d_h + k] = f16s(src[k]);
     } else {
       const int j = k - d.d_h;
-      float c, s;
-      rope_angle((int)(m % T_), j, d.d_r, d.theta, c, s);
+      const float2 r = cs[(m % T_) * half + j];
+      const float c = r.x, s = r.y;
       const float u = src[d.d_h + j], w = src[d.d_h + j + half];
       f16_t *o = a6 + m * lda6 + q_off + (int64_t)h * d.d_r;
       o[j] = f16s(u * c + w * s);          // rotation by -angle
@@ -676,7 +676,7 @@ __global__ void __launch_bounds__(256) pack_dq_kernel(const float *dq, f16_t *a6
 // dk [B, n_kv, T, 192], dv [B, n_kv, T, 128] -> [dK^C | dV] as the latent operand a3 [M, 2 n_kv d_h]
 // (fp16) and dk^R summed over the KV groups, rotated back (fp32 [M, d_r])
 __global__ void __launch_bounds__(256) pack_dkv_kernel(const float *dk, const float *dv, f16_t *a3, float *dkr,
-                                                       int32_t M, int32_t T_, LayerDims d) {
+                                                       int32_t M, int32_t T_, LayerDims d, const float2 *cs) {
   const int dqk = d.d_h + d.d_r, half = d.d_r / 2;
   const int64_t nkv = (int64_t)M * d.n_kv * d.d_h;
   const int64_t nr = (int64_t)M * half;
@@ -700,8 +700,8 @@ __global__ void __launch_bounds__(256) pack_dkv_kernel(const float *dk, const fl
         u += s[jj];
         w += s[jj + half];
       }
-      float c, s;
-      rope_angle((int)t, jj, d.d_r, d.theta, c, s);
+      const float2 rc = cs[t * half + jj];
+      const float c = rc.x, s = rc.y;
       dkr[m * d.d_r + jj] = u * c + w * s;
       dkr[m * d.d_r + jj + half] = -u * s + w * c;
     }
@@ -736,6 +736,44 @@ __global__ void __launch_bounds__(256) zero_cols_kernel(f16_t *dst, int64_t ldd,
   const int64_t n = (int64_t)rows * w;
   for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
     dst[(i / w) * ldd + c0 + i % w] = (f16_t)0.f;
+}
+
+// Eq.(8) backward of one row per workgroup: noise head j gets dH = -sum over the signal heads
+// i = j (mod n_N) of lambda_i dD_i; dlambda_i = -sum_e dD_i,e H_(n_S + i mod n_N),e, through the
+// sigmoid unless lambda is fixed.  Reads are contiguous along e.
+__global__ void __launch_bounds__(256) noise_lambda_fast_kernel(const float *heads, const float *lam, const float *dd,
+                                                                float *dheads, float *dlam_logit, int override_lam,
+                                                                LayerDims d) {
+  const int64_t m = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float *ddm = dd + m * d.n_signal * d.d_h;
+  const float *hm = heads + m * d.n_heads * d.d_h;
+  for (int idx = threadIdx.x; idx < d.n_noise * d.d_h; idx += 256) {
+    const int j = idx / d.d_h, e = idx % d.d_h;
+    float acc = 0.f;
+    for (int i = j; i < d.n_signal; i += d.n_noise) acc -= lam[m * d.n_signal + i] * ddm[i * d.d_h + e];
+    dheads[(m * d.n_heads + d.n_signal + j) * d.d_h + e] = acc;
+  }
+  for (int i = wave; i < d.n_signal; i += 4) {
+    const float *hn = hm + (int64_t)(d.n_signal + i % d.n_noise) * d.d_h;
+    float acc = 0.f;
+    for (int e = lane; e < d.d_h; e += 64) acc -= ddm[i * d.d_h + e] * hn[e];
+    acc = wsum(acc);
+    if (lane == 0) {
+      const float l = lam[m * d.n_signal + i];
+      dlam_logit[m * d.n_signal + i] = override_lam ? 0.f : acc * l * (1.0f - l);
+    }
+  }
+}
+
+// cs[t][j] = (cos, sin) of RoPE's angle for position t and pair j
+__global__ void __launch_bounds__(256) rope_table_kernel(float2 *cs, int32_t T_, int32_t d_r, float theta) {
+  const int half = d_r / 2;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= T_ * half) return;
+  float c, s;
+  rope_angle(i / half, i % half, d_r, theta, c, s);
+  cs[i] = make_float2(c, s);
 }
 
 // lo[m] = lowest visible key of token t = m % T (window and document start)
@@ -821,8 +859,8 @@ hipError_t launch_backward_fast(const FastBwdArgs &a, const LayerDims &d, hipStr
   hipLaunchKernelGGL(combine_fast_kernel, dim3(grid_for((int64_t)M * ny)), dim3(256), 0, s, a.heads, a.lam, a.sg16,
                      b.dy, b.dheads, b.dd, b.a6, (int64_t)k6, nH * dh + nH * dr, M, d);
   BWD_TRY(hipGetLastError());
-  hipLaunchKernelGGL(bwd_noise_lambda_kernel, dim3(grid_for((int64_t)M * d.n_noise * dh + (int64_t)M * nS)), dim3(256),
-                     0, s, a.heads, a.lam, b.dd, b.dheads, b.dlaml, a.lam_overridden ? 1 : 0, M, d);
+  hipLaunchKernelGGL(noise_lambda_fast_kernel, dim3(M), dim3(256), 0, s, a.heads, a.lam, b.dd, b.dheads, b.dlaml,
+                     a.lam_overridden ? 1 : 0, d);
   BWD_TRY(hipGetLastError());
   hipLaunchKernelGGL(bwd_drow_kernel, dim3((unsigned)(((int64_t)M * nH + 3) / 4)), dim3(256), 0, s, a.heads,
                      b.dheads, b.drow, (int64_t)M * nH, dh, nH);
@@ -841,11 +879,14 @@ hipError_t launch_backward_fast(const FastBwdArgs &a, const LayerDims &d, hipStr
   at.B = a.B; at.T = T_; at.lcap = a.lcap; at.n_heads = nH; at.n_signal = nS; at.n_noise = d.n_noise;
   at.n_kv = nKV; at.window = d.window; at.c = d.scale * 1.4426950408889634f; at.tau = d.scale;
   BWD_TRY(launch_bwd_attention(at, s));
+  hipLaunchKernelGGL(rope_table_kernel, dim3((T_ * (dr / 2) + 255) / 256), dim3(256), 0, s, b.rope_cs, T_, dr,
+                     d.theta);
+  BWD_TRY(hipGetLastError());
   hipLaunchKernelGGL(pack_dq_kernel, dim3(grid_for((int64_t)M * nH * (dh + dr / 2))), dim3(256), 0, s, b.dq, b.a6,
-                     (int64_t)k6, nH * dh, M, T_, d);
+                     (int64_t)k6, nH * dh, M, T_, d, (const float2 *)b.rope_cs);
   BWD_TRY(hipGetLastError());
   hipLaunchKernelGGL(pack_dkv_kernel, dim3(grid_for((int64_t)M * nKV * dh + (int64_t)M * dr / 2)), dim3(256), 0, s,
-                     b.dk, b.dv, b.a3, b.dkr, M, T_, d);
+                     b.dk, b.dv, b.a3, b.dkr, M, T_, d, (const float2 *)b.rope_cs);
   BWD_TRY(hipGetLastError());
 
   // ---- Eq.(5), (4): dcbar = [dK^C | dV] [W_uk | W_uv]^T; dW_uk, dW_uv = cbar^T [dK^C | dV]

@@ -55,6 +55,13 @@ __device__ __forceinline__ f16x8 tr_frag(const f16_t *tile, int pitch, int r0, i
 
 namespace {
 
+__device__ __forceinline__ void dma16v(const void *gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(lds_addr) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_u32(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
 // lowest visible key of token t of sequence b (window and document)
 __device__ __forceinline__ int qlo(const BwdAttnArgs &a, int b, int t) {
   int lo = a.window > 0 ? max(0, t - a.window + 1) : 0;
@@ -65,12 +72,15 @@ __device__ __forceinline__ int qlo(const BwdAttnArgs &a, int b, int t) {
 // ------------------------------------------------------------------------------------------
 // dq.  SIGNAL: workgroup (q block of 32, KV head, chunk of 4 signal heads, sequence), wave w =
 // signal head kv + n_kv (4 chunk + w).  Noise: workgroup (q block of 128, noise head, sequence),
-// wave w = queries 32 w ... of that head.  Key tiles of 64 rows are staged in LDS (K and V,
-// double-buffered through registers).
+// wave w = queries 32 w ... of that head.  Key tiles of 64 rows (K at 25 slots of 16 bytes per
+// row, V at 17, one slot of padding each) come by direct global -> LDS loads into three buffers.
+constexpr int KT_W = 11;                        // wave-instructions per wave and key tile
+constexpr int KT_BYTES = 4 * KT_W * 64 * 16;    // 44 KB
+constexpr int K_SLOTS = 64 * 25, V_SLOTS = 64 * 17;
+
 template <bool SIGNAL>
 __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdAttnArgs a) {
-  __shared__ __attribute__((aligned(16))) f16_t KS[2][64 * KP];
-  __shared__ __attribute__((aligned(16))) f16_t VS[2][64 * VP];
+  __shared__ __attribute__((aligned(16))) char KV[3 * KT_BYTES];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int QB = SIGNAL ? 32 : 128;
   const int n_qblk = (a.T + QB - 1) / QB;
@@ -116,44 +126,41 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdAttnArgs a) {
 
   const f16_t *kg = a.k + ((int64_t)b * a.n_kv + kvh) * a.lcap * DQK;
   const f16_t *vg = a.v + ((int64_t)b * a.n_kv + kvh) * a.lcap * DH;
-  // tile staging: thread tid moves chunks tid, tid + 256, ... (K: 64 x 24, V: 64 x 16 chunks);
-  // rows past the last query's key read the last valid row instead (finite, never visible)
-  uint4 kr[6], vr[4];
-  auto load = [&](int t) {
+  // the query fragments have landed before any tile load is issued (the tile waits below count
+  // only those loads)
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  // tile t into buffer t % 3; rows past the last key read the last valid row instead (finite,
+  // never visible)
+  const uint32_t lds0 = lds_u32(KV);
+  auto issue = [&](int t) {
     const int s0 = klo + 64 * t;
+    const uint32_t buf = lds0 + (uint32_t)((t % 3) * KT_BYTES);
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      const int c = tid + 256 * i, row = c / 24, ch = c % 24;
-      kr[i] = *(const uint4 *)(kg + (int64_t)min(s0 + row, a.T - 1) * DQK + 8 * ch);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, row = c / 16, ch = c % 16;
-      vr[i] = *(const uint4 *)(vg + (int64_t)min(s0 + row, a.T - 1) * DH + 8 * ch);
-    }
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      const int c = tid + 256 * i, row = c / 24, ch = c % 24;
-      *(uint4 *)(KS[buf] + row * KP + 8 * ch) = kr[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, row = c / 16, ch = c % 16;
-      *(uint4 *)(VS[buf] + row * VP + 8 * ch) = vr[i];
+    for (int i = 0; i < KT_W; ++i) {
+      const int slot = (wave + 4 * i) * 64 + lane;
+      const void *src;
+      if (slot < K_SLOTS) {
+        const int r = slot / 25, c = min(slot % 25, 23);
+        src = kg + (int64_t)min(s0 + r, a.T - 1) * DQK + 8 * c;
+      } else if (slot < K_SLOTS + V_SLOTS) {
+        const int s2 = slot - K_SLOTS, r = s2 / 17, c = min(s2 % 17, 15);
+        src = vg + (int64_t)min(s0 + r, a.T - 1) * DH + 8 * c;
+      } else {
+        src = kg;
+      }
+      dma16v(src, __builtin_amdgcn_readfirstlane(buf + (uint32_t)((wave + 4 * i) * 64 * 16)));
     }
   };
 
-  if (ntiles > 0) {
-    load(0);
-    store(0);
-  }
-  __syncthreads();
+  for (int t = 0; t < 2 && t < ntiles; ++t) issue(t);
   for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) load(t + 1);
+    if (t + 1 < ntiles) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KT_W) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // tile t has landed for every wave; every wave is done with tile t - 1
+    if (t + 2 < ntiles) issue(t + 2);
     const int s0 = klo + 64 * t;
-    const f16_t *ks = KS[t & 1], *vs = VS[t & 1];
+    const f16_t *ks = (const f16_t *)(KV + (t % 3) * KT_BYTES);
+    const f16_t *vs = (const f16_t *)(KV + (t % 3) * KT_BYTES + K_SLOTS * 16);
     const bool skip = !active || s0 > wq_hi || s0 + 63 < wlo_min;
     if (!skip) {
       const bool full = s0 + 63 <= q0 && s0 >= wlo_max;
@@ -183,9 +190,6 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdAttnArgs a) {
             dQ[db] = mfma(tr_frag(ks, KP, 32 * kb + 16 * kk, 32 * db, lane), dsf[kk], dQ[db]);
       }
     }
-    // the other buffer was last read in iteration t - 1, which every wave has left
-    if (t + 1 < ntiles) store((t + 1) & 1);
-    __syncthreads();
   }
   if (!qok) return;
   // dQ[db][j] = dQ^T[dim 32 db + 8 (j / 4) + 4 (l / 32) + j % 4][query tq]
@@ -201,25 +205,19 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdAttnArgs a) {
 
 // ------------------------------------------------------------------------------------------
 // dK, dV.  Workgroup (key block of 128, KV head, sequence); wave w holds keys 32 w .. 32 w + 31 of
-// the block.  The waves walk the query blocks of 32 of every head of the group together: each
+// the block.  The waves walk the query blocks of 64 of every head of the group together: each
 // block's Q, dH, log-sum-exp, row sum and lowest visible keys come by direct global -> LDS loads
 // (M0 + 16 lane per wave-instruction, no compiler tracking) into three buffers, two blocks in
-// flight while one is read.  A buffer is 24 wave-instructions of 64 slots of 16 bytes:
-//   Q rows 0..31 at 25 slots per row (24 of data, one of padding), then dH rows at 17 slots per
-//   row, then lse, row sum (fp32) and lowest visible key (int32) of the 32 queries, 8 slots each;
+// flight while one is read.  A buffer is 44 wave-instructions of 64 slots of 16 bytes:
+//   Q rows 0..63 at 25 slots per row (24 of data, one of padding), then dH rows at 17 slots per
+//   row, then lse, row sum (fp32) and lowest visible key (int32) of the 64 queries, 16 slots each;
 //   padding slots receive a copy of a neighbouring chunk.
-constexpr int DMA_W = 6;                       // wave-instructions per wave and block
-constexpr int TB_SLOTS = 4 * DMA_W * 64;       // 1536 slots
-constexpr int TB_BYTES = TB_SLOTS * 16;        // 24 KB
-constexpr int Q_SLOTS = 32 * 25, H_SLOTS = 32 * 17;
-constexpr int S_OFF = (Q_SLOTS + H_SLOTS) * 16;  // bytes: lse [32], drow [32], lo [32]
-
-__device__ __forceinline__ void dma16v(const void *gptr, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(lds_addr) : "memory");
-}
-__device__ __forceinline__ uint32_t lds_u32(const void *p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
-}
+constexpr int QB64 = 64;                       // queries per block
+constexpr int DMA_W = 11;                      // wave-instructions per wave and block
+constexpr int TB_SLOTS = 4 * DMA_W * 64;       // 2816 slots
+constexpr int TB_BYTES = TB_SLOTS * 16;        // 44 KB
+constexpr int Q_SLOTS = QB64 * 25, H_SLOTS = QB64 * 17;
+constexpr int S_OFF = (Q_SLOTS + H_SLOTS) * 16;  // bytes: lse [64], drow [64], lo [64]
 
 __global__ void __launch_bounds__(256, 1) bwd_dkv_kernel(BwdAttnArgs a) {
   __shared__ __attribute__((aligned(16))) char SM[3 * TB_BYTES];
@@ -236,7 +234,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkv_kernel(BwdAttnArgs a) {
     if (qlo(a, b, mid) > kb0 + 127) hi_q = mid;
     else lo_q = mid + 1;
   }
-  const int qb0 = kb0 / 32, nqb = max(0, (lo_q - kb0 + 31) / 32);
+  const int qb0 = kb0 / QB64, nqb = max(0, (lo_q - kb0 + QB64 - 1) / QB64);
   const int sig_g = a.n_signal / a.n_kv, n_g = a.n_heads / a.n_kv;
   const int n_it = n_g * nqb;
 
@@ -263,7 +261,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkv_kernel(BwdAttnArgs a) {
   // block `it` into buffer it % 3: this lane's DMA_W slots are (wave + 4 i) * 64 + lane
   const uint32_t lds0 = lds_u32(SM);
   auto issue = [&](int it) {
-    const int h = head_of(it / nqb), qbase = 32 * (qb0 + it % nqb);
+    const int h = head_of(it / nqb), qbase = QB64 * (qb0 + it % nqb);
     const int64_t mrow = (int64_t)b * a.T;
     const uint32_t buf = lds0 + (uint32_t)((it % 3) * TB_BYTES);
 #pragma unroll
@@ -279,8 +277,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dkv_kernel(BwdAttnArgs a) {
         const int t = min(qbase + r, a.T - 1);
         src = a.dh + ((mrow + t) * a.n_heads + h) * DH + 8 * c;
       } else {
-        const int s3 = min(slot - Q_SLOTS - H_SLOTS, 23), part = s3 >> 3, k4 = 4 * (s3 & 7);
-        // the three arrays carry 32 entries of padding past their end
+        const int s3 = min(slot - Q_SLOTS - H_SLOTS, 47), part = s3 >> 4, k4 = 4 * (s3 & 15);
+        // the three arrays carry 64 entries of padding past their end
         if (part == 0) src = a.lse + (int64_t)h * M + mrow + qbase + k4;
         else if (part == 1) src = a.drow + (int64_t)h * M + mrow + qbase + k4;
         else src = a.lo + mrow + qbase + k4;
@@ -296,33 +294,51 @@ __global__ void __launch_bounds__(256, 1) bwd_dkv_kernel(BwdAttnArgs a) {
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // block it has landed for every wave; every wave is done with block it - 1
     if (it + 2 < n_it) issue(it + 2);
-    const int qbase = 32 * (qb0 + it % nqb);
+    const int qblock = QB64 * (qb0 + it % nqb);
     const char *base = SM + (it % 3) * TB_BYTES;
-    const f16_t *qs = (const f16_t *)base, *hs = (const f16_t *)(base + Q_SLOTS * 16);
+    const f16_t *qs0 = (const f16_t *)base, *hs0 = (const f16_t *)(base + Q_SLOTS * 16);
     const float *ls = (const float *)(base + S_OFF);
-    const int *los = (const int *)(base + S_OFF + 64 * 4);
-    f32x16 S = {}, dP = {};
+    const int *los = (const int *)(base + S_OFF + 2 * QB64 * 4);
 #pragma unroll
-    for (int k = 0; k < 12; ++k) S = mfma(*(const f16x8 *)(qs + (lane & 31) * KP + 16 * k + 8 * (lane >> 5)), Kf[k], S);
+    for (int qh = 0; qh < QB64 / 32; ++qh) {
+      const int qbase = qblock + 32 * qh;
+      const f16_t *qs = qs0 + 32 * qh * KP, *hs = hs0 + 32 * qh * VP;
+      f32x16 S = {}, dP = {};
 #pragma unroll
-    for (int k = 0; k < 8; ++k) dP = mfma(*(const f16x8 *)(hs + (lane & 31) * VP + 16 * k + 8 * (lane >> 5)), Vf[k], dP);
-    // acc[j]: query qbase + qi, qi = 8 (j / 4) + 4 (l / 32) + j % 4; key `key`
-    f16x8 pf[2], dsf[2];
+      for (int k = 0; k < 12; ++k) S = mfma(*(const f16x8 *)(qs + (lane & 31) * KP + 16 * k + 8 * (lane >> 5)), Kf[k], S);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int qi = 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
-      const int t = qbase + qi;
-      const bool vis = key <= t && t < a.T && key >= los[qi];
-      const float p = vis ? __builtin_amdgcn_exp2f(S[j] * a.c - ls[qi]) : 0.f;
-      pf[j >> 3][j & 7] = h16(p);
-      dsf[j >> 3][j & 7] = h16(vis ? p * (dP[j] - ls[32 + qi]) : 0.f);
-    }
+      for (int k = 0; k < 8; ++k) dP = mfma(*(const f16x8 *)(hs + (lane & 31) * VP + 16 * k + 8 * (lane >> 5)), Vf[k], dP);
+      // acc[j]: query qbase + qi, qi = 8 (j / 4) + 4 (l / 32) + j % 4; key `key`.  The 16 queries
+      // of a lane are four runs of four: their lse, row sums and lowest keys are 16-byte reads.
+      float4 lv[4], dv4[4];
+      int4 lov[4];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+      for (int g = 0; g < 4; ++g) {
+        const int q4 = 32 * qh + 8 * g + 4 * (lane >> 5);
+        lv[g] = *(const float4 *)(ls + q4);
+        dv4[g] = *(const float4 *)(ls + QB64 + q4);
+        lov[g] = *(const int4 *)(los + q4);
+      }
+      f16x8 pf[2], dsf[2];
 #pragma unroll
-      for (int eb = 0; eb < 4; ++eb) dV[eb] = mfma(tr_frag(hs, VP, 16 * kk, 32 * eb, lane), pf[kk], dV[eb]);
+      for (int j = 0; j < 16; ++j) {
+        const int g = j >> 2, e = j & 3;
+        const int t = qbase + 8 * g + 4 * (lane >> 5) + e;
+        const float lse_q = e == 0 ? lv[g].x : e == 1 ? lv[g].y : e == 2 ? lv[g].z : lv[g].w;
+        const float dr_q = e == 0 ? dv4[g].x : e == 1 ? dv4[g].y : e == 2 ? dv4[g].z : dv4[g].w;
+        const int lo_q = e == 0 ? lov[g].x : e == 1 ? lov[g].y : e == 2 ? lov[g].z : lov[g].w;
+        const bool vis = key <= t && t < a.T && key >= lo_q;
+        const float p = vis ? __builtin_amdgcn_exp2f(S[j] * a.c - lse_q) : 0.f;
+        pf[j >> 3][j & 7] = h16(p);
+        dsf[j >> 3][j & 7] = h16(vis ? p * (dP[j] - dr_q) : 0.f);
+      }
 #pragma unroll
-      for (int db = 0; db < 6; ++db) dK[db] = mfma(tr_frag(qs, KP, 16 * kk, 32 * db, lane), dsf[kk], dK[db]);
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int eb = 0; eb < 4; ++eb) dV[eb] = mfma(tr_frag(hs, VP, 16 * kk, 32 * eb, lane), pf[kk], dV[eb]);
+#pragma unroll
+        for (int db = 0; db < 6; ++db) dK[db] = mfma(tr_frag(qs, KP, 16 * kk, 32 * db, lane), dsf[kk], dK[db]);
+      }
     }
   }
   if (key >= a.T) return;

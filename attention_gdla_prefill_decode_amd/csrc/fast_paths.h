@@ -138,6 +138,7 @@ struct FastBwdBuffers {
   f16_t *a6, *a3, *a8;          // gradient operands [M, k6], [M, k3], [M, k8]
   float *dkr, *dcbar, *dckv, *rkv, *dcq, *daq, *rq;
   int32_t *lo;                  // [M + 32]
+  float2 *rope_cs;              // [T, d_r / 2] (cos, sin)
 };
 struct FastBwdArgs {
   const void *x, *dout;
