@@ -805,12 +805,24 @@ hipError_t tpack(const TS *src, int64_t lds, int R, int C, int R_pad, f16_t *dst
 }
 
 // C[M, N] (fp32, ldc) = A[M, K] Bt[N, K]^T, fp16 operands with K-contiguous rows
+// C = A . Bt^T in fp32.  A product with fewer 256 x 256 tiles than the chip has CUs (the weight
+// gradients reduce over all tokens: few tiles, long K) is split along K into up to 16 slices of
+// at least 512, as long as the partials fit `part` (kSplitKBytes); the slices are summed in order.
 hipError_t nt(const f16_t *A, int64_t lda, const f16_t *Bt, int64_t ldb, float *C, int64_t ldc, int M, int N, int K,
-              hipStream_t s) {
+              hipStream_t s, float *part = nullptr) {
   GemmBatch g{};
   GemmProblem &p = g.p[g.n++];
   p.A = A; p.lda = lda; p.B = Bt; p.ldb = ldb; p.C = C; p.ldc = ldc;
   p.M = M; p.N = N; p.K = K; p.hw = N; p.hs = 0; p.ho = 0; p.c_dt = CD_F32; p.a_f16 = 1; p.epi = EPI_NONE;
+  const int64_t tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+  int ks = 1;
+  while (part && N % 4 == 0 && ks < 16 && tiles * ks < 256 && K % (64 * 2 * ks) == 0 && K / (2 * ks) >= 512 &&
+         (size_t)(2 * ks) * M * N * 4 <= kSplitKBytes)
+    ks *= 2;
+  if (ks > 1) {
+    p.ksplit = ks;
+    p.part = part;
+  }
   return launch_gemm_nt(g, true, s);
 }
 
@@ -851,10 +863,10 @@ hipError_t launch_backward_fast(const FastBwdArgs &a, const LayerDims &d, hipStr
 
   // ---- Eq.(10): dY = dout W_O^T; dW_O = Y^T dout
   BWD_TRY(pack((const bf16_t *)a.dout, dm, M, dm, b.dout16, dm, 0, s));
-  BWD_TRY(nt(b.dout16, dm, b.wo16, dm, b.dy, ny, M, ny, dm, s));
+  BWD_TRY(nt(b.dout16, dm, b.wo16, dm, b.dy, ny, M, ny, dm, s, b.splitk));
   BWD_TRY(tpack(a.y16, ny, M, ny, Mp, b.ta, Mp, 0, s));
   BWD_TRY(tpack((const bf16_t *)a.dout, dm, M, dm, Mp, b.tb, Mp, 0, s));
-  BWD_TRY(nt(b.ta, Mp, b.tb, Mp, G.dw_o, dm, ny, dm, Mp, s));
+  BWD_TRY(nt(b.ta, Mp, b.tb, Mp, G.dw_o, dm, ny, dm, Mp, s, b.splitk));
   // gate and differential combine; noise-head dH and dlambda
   hipLaunchKernelGGL(combine_fast_kernel, dim3(grid_for((int64_t)M * ny)), dim3(256), 0, s, a.heads, a.lam, a.sg16,
                      b.dy, b.dheads, b.dd, b.a6, (int64_t)k6, nH * dh + nH * dr, M, d);
@@ -890,11 +902,11 @@ hipError_t launch_backward_fast(const FastBwdArgs &a, const LayerDims &d, hipStr
   BWD_TRY(hipGetLastError());
 
   // ---- Eq.(5), (4): dcbar = [dK^C | dV] [W_uk | W_uv]^T; dW_uk, dW_uv = cbar^T [dK^C | dV]
-  BWD_TRY(nt(b.a3, k3, b.w3, k3, b.dcbar, dc, M, dc, k3, s));
+  BWD_TRY(nt(b.a3, k3, b.w3, k3, b.dcbar, dc, M, dc, k3, s, b.splitk));
   BWD_TRY(tpack(a.cache, (int64_t)dc + dr, M, dc, Mp, b.ta, Mp, 0, s));
   BWD_TRY(tpack(b.a3, k3, M, k3, Mp, b.tb, Mp, 0, s));
-  BWD_TRY(nt(b.ta, Mp, b.tb, Mp, G.dw_uk, (int64_t)nKV * dh, dc, nKV * dh, Mp, s));
-  BWD_TRY(nt(b.ta, Mp, b.tb + (int64_t)nKV * dh * Mp, Mp, G.dw_uv, (int64_t)nKV * dh, dc, nKV * dh, Mp, s));
+  BWD_TRY(nt(b.ta, Mp, b.tb, Mp, G.dw_uk, (int64_t)nKV * dh, dc, nKV * dh, Mp, s, b.splitk));
+  BWD_TRY(nt(b.ta, Mp, b.tb + (int64_t)nKV * dh * Mp, Mp, G.dw_uv, (int64_t)nKV * dh, dc, nKV * dh, Mp, s, b.splitk));
   hipLaunchKernelGGL((rms_bwd_kernel<bf16_t>), dim3(M), dim3(64), 0, s, a.ckv, (const bf16_t *)w.gamma_kv, b.dcbar,
                      b.dckv, b.rkv, dc, d.eps);
   BWD_TRY(hipGetLastError());
@@ -905,12 +917,12 @@ hipError_t launch_backward_fast(const FastBwdArgs &a, const LayerDims &d, hipStr
   }
 
   // ---- Eq.(2), (9), (1): dc^Q = [dq^C | dq^R | dG] [W_qc | W_qr | W_gate]^T; their weight grads
-  BWD_TRY(nt(b.a6, k6, b.w6, k6, b.dcq, dcq, M, dcq, k6, s));
+  BWD_TRY(nt(b.a6, k6, b.w6, k6, b.dcq, dcq, M, dcq, k6, s, b.splitk));
   BWD_TRY(tpack(a.cq16, dcq, M, dcq, Mp, b.ta, Mp, 0, s));
   BWD_TRY(tpack(b.a6, k6, M, k6, Mp, b.tb, Mp, 0, s));
-  BWD_TRY(nt(b.ta, Mp, b.tb, Mp, G.dw_qc, (int64_t)nH * dh, dcq, nH * dh, Mp, s));
-  BWD_TRY(nt(b.ta, Mp, b.tb + (int64_t)nH * dh * Mp, Mp, G.dw_qr, (int64_t)nH * dr, dcq, nH * dr, Mp, s));
-  BWD_TRY(nt(b.ta, Mp, b.tb + (int64_t)(nH * dh + nH * dr) * Mp, Mp, G.dw_gate, (int64_t)nS * dh, dcq, nS * dh, Mp, s));
+  BWD_TRY(nt(b.ta, Mp, b.tb, Mp, G.dw_qc, (int64_t)nH * dh, dcq, nH * dh, Mp, s, b.splitk));
+  BWD_TRY(nt(b.ta, Mp, b.tb + (int64_t)nH * dh * Mp, Mp, G.dw_qr, (int64_t)nH * dr, dcq, nH * dr, Mp, s, b.splitk));
+  BWD_TRY(nt(b.ta, Mp, b.tb + (int64_t)(nH * dh + nH * dr) * Mp, Mp, G.dw_gate, (int64_t)nS * dh, dcq, nS * dh, Mp, s, b.splitk));
   hipLaunchKernelGGL((rms_bwd_kernel<bf16_t>), dim3(M), dim3(64), 0, s, a.aq, (const bf16_t *)w.gamma_q, b.dcq, b.daq,
                      b.rq, dcq, d.eps);
   BWD_TRY(hipGetLastError());
@@ -925,14 +937,14 @@ hipError_t launch_backward_fast(const FastBwdArgs &a, const LayerDims &d, hipStr
   BWD_TRY(pack(b.dckv, dc, M, dc, b.a8, k8, dcq, s));
   BWD_TRY(pack(b.dkr, dr, M, dr, b.a8, k8, dcq + dc, s));
   BWD_TRY(pack(b.dlaml, nS, M, nS, b.a8, k8, dcq + dc + dr, s));
-  BWD_TRY(nt(b.a8, k8, b.w8, k8, G.dx, dm, M, dm, k8, s));
+  BWD_TRY(nt(b.a8, k8, b.w8, k8, G.dx, dm, M, dm, k8, s, b.splitk));
   BWD_TRY(tpack((const bf16_t *)a.x, dm, M, dm, Mp, b.ta, Mp, 0, s));
   BWD_TRY(tpack(b.a8, k8, M, k8, Mp, b.tb, Mp, 0, s));
-  BWD_TRY(nt(b.ta, Mp, b.tb, Mp, G.dw_qa, dcq, dm, dcq, Mp, s));
-  BWD_TRY(nt(b.ta, Mp, b.tb + (int64_t)dcq * Mp, Mp, G.dw_dkv, dc, dm, dc, Mp, s));
-  BWD_TRY(nt(b.ta, Mp, b.tb + (int64_t)(dcq + dc) * Mp, Mp, G.dw_kr, dr, dm, dr, Mp, s));
+  BWD_TRY(nt(b.ta, Mp, b.tb, Mp, G.dw_qa, dcq, dm, dcq, Mp, s, b.splitk));
+  BWD_TRY(nt(b.ta, Mp, b.tb + (int64_t)dcq * Mp, Mp, G.dw_dkv, dc, dm, dc, Mp, s, b.splitk));
+  BWD_TRY(nt(b.ta, Mp, b.tb + (int64_t)(dcq + dc) * Mp, Mp, G.dw_kr, dr, dm, dr, Mp, s, b.splitk));
   if (nS % 8 == 0) {
-    BWD_TRY(nt(b.ta, Mp, b.tb + (int64_t)(dcq + dc + dr) * Mp, Mp, G.dw_lambda, nS, dm, nS, Mp, s));
+    BWD_TRY(nt(b.ta, Mp, b.tb + (int64_t)(dcq + dc + dr) * Mp, Mp, G.dw_lambda, nS, dm, nS, Mp, s, b.splitk));
   } else {  // too few columns for the MFMA GEMM's 16-byte stores
     BWD_TRY(gg((const bf16_t *)a.x, dm, true, b.dlaml, nS, false, G.dw_lambda, nS, dm, nS, M, false, s));
   }

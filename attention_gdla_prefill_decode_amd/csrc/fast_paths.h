@@ -127,6 +127,9 @@ struct BwdAttnArgs {
 bool fast_backward_supported(const LayerDims &d, gdla_dtype dt);
 hipError_t launch_bwd_attention(const BwdAttnArgs &a, hipStream_t s);
 
+// Partials of the split-K products of the fused backward (at most this many bytes per product).
+constexpr size_t kSplitKBytes = (size_t)128 << 20;
+
 struct FastBwdBuffers {
   f16_t *wo16, *w3, *w6, *w8;   // fp16 weights, K-concatenated: [n_S d_h, d], [d_c, k3], [d_cq, k6], [d, k8]
   f16_t *dout16;                // [M, d]
@@ -139,6 +142,7 @@ struct FastBwdBuffers {
   float *dkr, *dcbar, *dckv, *rkv, *dcq, *daq, *rq;
   int32_t *lo;                  // [M + 32]
   float2 *rope_cs;              // [T, d_r / 2] (cos, sin)
+  float *splitk;                // kSplitKBytes: K-slice partials of the small-grid products
 };
 struct FastBwdArgs {
   const void *x, *dout;

@@ -252,7 +252,7 @@ BackwardLayout plan_backward(const LayerDims &d, int32_t B, int32_t T) {
 struct FastBackwardLayout {
   PrefillLayout pre;
   size_t cache, out, heads, lse, vk;
-  size_t fb[28];  // FastBwdBuffers fields, in order
+  size_t fb[29];  // FastBwdBuffers fields, in order
   size_t total;
   int32_t M_pad, k8;
   bool ok;
@@ -278,7 +278,7 @@ FastBackwardLayout plan_backward_fast(const LayerDims &d, int32_t B, int32_t T) 
   L.vk = p.add(2 * (size_t)B * nKV * L.pre.lcap * dh);
   const size_t trows_a = std::max({nS * dh, (size_t)d.d_c, (size_t)d.d_cq, dm});
   const size_t trows_b = std::max({dm, k3, k6, k8});
-  const size_t bytes[28] = {
+  const size_t bytes[29] = {
       2 * nS * dh * dm, 2 * d.d_c * k3, 2 * d.d_cq * k6, 2 * dm * k8,      // wo16 w3 w6 w8
       2 * M * dm, 4 * M * nS * dh,                                          // dout16 dy
       2 * trows_a * Mp, 2 * trows_b * Mp,                                   // ta tb
@@ -287,9 +287,10 @@ FastBackwardLayout plan_backward_fast(const LayerDims &d, int32_t B, int32_t T) 
       4 * M * nH * (dh + dr), 4 * M * nKV * (dh + dr), 4 * M * nKV * dh,    // dq dk dv
       2 * M * k6, 2 * M * k3, 2 * M * k8,                                   // a6 a3 a8
       4 * M * dr, 4 * M * d.d_c, 4 * M * d.d_c, 4 * M, 4 * M * d.d_cq, 4 * M * d.d_cq, 4 * M,
-      4 * (M + 32), 8 * (size_t)T * (dr / 2)};                            // lo rope_cs
-  static_assert(sizeof(FastBwdBuffers) == 28 * sizeof(void *), "one size per buffer");
-  for (int i = 0; i < 28; ++i) L.fb[i] = p.add(bytes[i]);
+      4 * (M + 32), 8 * (size_t)T * (dr / 2),                             // lo rope_cs
+      kSplitKBytes};                                                        // splitk
+  static_assert(sizeof(FastBwdBuffers) == 29 * sizeof(void *), "one size per buffer");
+  for (int i = 0; i < 29; ++i) L.fb[i] = p.add(bytes[i]);
   L.total = p.bytes;
   return L;
 }
@@ -888,7 +889,7 @@ gdla_status backward_fast(const gdla_dims *dims, const gdla_weights *w, const vo
   a.y16 = at<f16_t>(ws, PL.y);
   a.lam_overridden = fdbg.lambda_override ? 1 : 0;
   void **bufs = (void **)&a.buf;
-  for (int i = 0; i < 28; ++i) bufs[i] = at<void>(ws, F.fb[i]);
+  for (int i = 0; i < 29; ++i) bufs[i] = at<void>(ws, F.fb[i]);
   a.B = B; a.T = T; a.M = M; a.M_pad = F.M_pad; a.lcap = PL.lcap; a.k8 = F.k8;
   HIP_TRY(launch_backward_fast(a, d, stream));
   return GDLA_OK;

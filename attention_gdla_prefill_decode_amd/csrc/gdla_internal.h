@@ -40,6 +40,11 @@ struct GemmProblem {
   float rope_theta;
   int32_t tile0;   // first linear tile index of this problem (filled by the launcher)
   int32_t tiles_n; // tiles along N (filled by the launcher)
+  // Split-K (transposed-weight GEMM, plain fp32 outputs only): ksplit > 1 slices K into ksplit
+  // equal ranges, each workgroup writes its slice's product to part[slice] ([M, N] fp32, dense) and
+  // a second kernel sums the slices in order into C (deterministic).
+  int32_t ksplit;
+  float *part;
 };
 
 enum { EPI_NONE = 0, EPI_SIGMOID = 1, EPI_ROPE = 2 };

@@ -143,7 +143,13 @@ __global__ void __launch_bounds__(512, 1) gemm_nt_kernel(GemmBatch batch) {
   int pi = 0;
   while (pi + 1 < batch.n && bid >= batch.p[pi + 1].tile0) ++pi;
   const GemmProblem &P = batch.p[pi];
-  const int tile = bid - P.tile0;
+  int tile = bid - P.tile0, kc = 0;
+  if (P.ksplit > 1) {  // slice kc of K; the tiles of one slice are consecutive
+    const int per_slice = ((P.M + BM - 1) / BM) * P.tiles_n;
+    kc = tile / per_slice;
+    tile -= kc * per_slice;
+  }
+  const int kbeg = P.ksplit > 1 ? kc * (P.K / P.ksplit) : 0;
   const int m0 = (tile / P.tiles_n) * BM, n0 = (tile % P.tiles_n) * BN;
   const T *A = (const T *)P.A;
   const T *Bt = (const T *)P.B;
@@ -160,8 +166,8 @@ __global__ void __launch_bounds__(512, 1) gemm_nt_kernel(GemmBatch batch) {
     const int jj = j & 31;
     const int sl = jj * 64 + lane;
     const int row = sl >> 3, c = (sl & 7) ^ ((row >> 1) & 7);
-    if (j < 32) src[i] = A + (int64_t)min(m0 + row, P.M - 1) * P.lda + c * 8;
-    else src[i] = Bt + (int64_t)min(n0 + row, P.N - 1) * P.ldb + c * 8;
+    if (j < 32) src[i] = A + (int64_t)min(m0 + row, P.M - 1) * P.lda + kbeg + c * 8;
+    else src[i] = Bt + (int64_t)min(n0 + row, P.N - 1) * P.ldb + kbeg + c * 8;
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)smem;
   auto issue = [&](int stage, int k0) {
@@ -211,7 +217,7 @@ __global__ void __launch_bounds__(512, 1) gemm_nt_kernel(GemmBatch batch) {
     }
   };
 
-  const int nk = P.K / BK;
+  const int nk = (P.ksplit > 1 ? P.K / P.ksplit : P.K) / BK;
   issue(0, 0);
   for (int ks = 0; ks < nk; ++ks) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -223,6 +229,14 @@ __global__ void __launch_bounds__(512, 1) gemm_nt_kernel(GemmBatch batch) {
   // epilogue: lane holds column (lane & 31) and rows 8 (j / 4) + 4 (lane / 32) + j % 4 of a block
   // output kinds of the staged epilogue: 0 fp32, 1 fp16, 2 bf16
   const int okind = P.c_dt == CD_F32 ? 0 : (P.c_dt == CD_F16 || (P.c_dt == CD_IN && __is_same(T, f16_t))) ? 1 : 2;
+  if (P.ksplit > 1) {  // this slice's partial product, dense fp32 [M, N]
+    __syncthreads();  // every wave is done with the stage buffers
+    GemmProblem Q = P;
+    Q.C = P.part + (int64_t)kc * P.M * P.N;
+    Q.ldc = P.N; Q.hw = P.N; Q.hs = 0; Q.ho = 0; Q.epi = EPI_NONE;
+    staged_epilogue<0>(Q, acc, smem + wave * 32 * 272, m0 + wm * 128, n0 + wn * 64, lane);
+    return;
+  }
   if (!P.c_trans) {  // row-major outputs: 16-byte storable (nt_gemm_problem_ok)
     __syncthreads();  // every wave is done with the stage buffers
     unsigned char *wt = smem + wave * 32 * 272;
@@ -257,6 +271,23 @@ __global__ void __launch_bounds__(512, 1) gemm_nt_kernel(GemmBatch batch) {
         }
     }
   }
+}
+
+// C[m][n] = sum over the K slices s = 0 .. ks - 1 (in that order) of part[s][m][n]; four columns
+// per thread.
+__global__ void __launch_bounds__(256) splitk_sum_kernel(const float *part, int32_t ks, int32_t M, int32_t N, float *C,
+                                                         int64_t ldc) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= (int64_t)M * (N / 4)) return;
+  const int64_t m = q / (N / 4), n = 4 * (q % (N / 4));
+  const int64_t slice = (int64_t)M * N;
+  float4 acc = *(const float4 *)(part + m * N + n);
+  for (int s = 1; s < ks; ++s) {
+    const float4 v = *(const float4 *)(part + s * slice + m * N + n);
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  float *c = C + m * ldc + n;
+  c[0] = acc.x; c[1] = acc.y; c[2] = acc.z; c[3] = acc.w;
 }
 
 // Wt[n][k] = W[k][n] for a [K, N] bf16 weight, converted to fp16 (exact in the fp16 normal range,
@@ -331,15 +362,27 @@ hipError_t launch_gemm_nt(GemmBatch &g, bool f16, hipStream_t s) {
   for (int i = 0; i < g.n; ++i) {
     GemmProblem &p = g.p[i];
     if (!nt_gemm_problem_ok(p)) return hipErrorInvalidValue;
+    if (p.ksplit > 1 && (p.c_dt != CD_F32 || p.epi != EPI_NONE || p.c_trans || !p.part || p.N % 4 != 0 ||
+                         p.K % (BK * p.ksplit) != 0))
+      return hipErrorInvalidValue;
     p.tile0 = t;
     p.tiles_n = (p.N + BN - 1) / BN;
-    t += ((p.M + BM - 1) / BM) * p.tiles_n;
+    t += ((p.M + BM - 1) / BM) * p.tiles_n * (p.ksplit > 1 ? p.ksplit : 1);
   }
   g.total_tiles = t;
   if (t == 0) return hipSuccess;
   if (f16) hipLaunchKernelGGL(gemm_nt_kernel<f16_t>, dim3(t), dim3(64 * WAVES), 0, s, g);
   else hipLaunchKernelGGL(gemm_nt_kernel<bf16_t>, dim3(t), dim3(64 * WAVES), 0, s, g);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  for (int i = 0; i < g.n && e == hipSuccess; ++i) {
+    const GemmProblem &p = g.p[i];
+    if (p.ksplit <= 1) continue;
+    const int64_t quads = (int64_t)p.M * (p.N / 4);
+    hipLaunchKernelGGL(splitk_sum_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s, p.part, p.ksplit,
+                       p.M, p.N, (float *)p.C, p.ldc);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 hipError_t launch_transpose_weight(const void *w, void *wt, int32_t K, int32_t N, bool to_f16, hipStream_t s) {

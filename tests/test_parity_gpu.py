@@ -273,6 +273,14 @@ def test_backward_fused_matches_oracle(cfg, T, batch, window, lens):
         _say(line)
 
 
+# Enough tokens that the weight-gradient products are split along the token axis (8192 rows: up
+# to 8 slices of 1024, summed in order) on the fused path.
+def test_backward_fused_split_k():
+    got, exp = H.backward_case(BF, 2048, 4, window=300, seed=79)
+    for line in H.check_grads(got, exp, 1e-2, "fused backward, 4 x 2048 tokens (split-K products)"):
+        _say(line)
+
+
 def test_backward_lambda_zero():
     got, exp = H.backward_case(BF, 48, 1, seed=71, lam_zero=True)
     H.check_grads(got, exp, 1e-5, "backward, lambda = 0")
