@@ -298,7 +298,7 @@ def main():
                          "for the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build runs on a single MI355X and has no "
+        print(f"bench.py measures one GPU only: the library runs on a single MI355X and has no "
               f"multi-GPU path (asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
 

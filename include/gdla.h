@@ -58,7 +58,7 @@ extern "C" {
 typedef enum {
   GDLA_OK = 0,
   GDLA_ERR_INVALID_ARG = 1,   /* null pointer, inconsistent sizes, bad alignment */
-  GDLA_ERR_UNSUPPORTED = 2,   /* valid layer, but a size or dtype this build does not serve */
+  GDLA_ERR_UNSUPPORTED = 2,   /* valid layer, but a size or dtype the library does not serve */
   GDLA_ERR_WORKSPACE = 3,     /* ws_bytes smaller than gdla_workspace_bytes(...) */
   GDLA_ERR_OUT_OF_RANGE = 4,  /* a position + T exceeds max_len, or a negative position */
   GDLA_ERR_HIP = 5            /* a HIP runtime call or kernel launch failed */
