@@ -72,14 +72,17 @@ __device__ __forceinline__ int qlo(const BwdAttnArgs &a, int b, int t) {
 // ------------------------------------------------------------------------------------------
 // dq.  SIGNAL: workgroup (q block of 32, KV head, chunk of 4 signal heads, sequence), wave w =
 // signal head kv + n_kv (4 chunk + w).  Noise: workgroup (q block of 128, noise head, sequence),
-// wave w = queries 32 w ... of that head.  Key tiles of 64 rows (K at 25 slots of 16 bytes per
-// row, V at 17, one slot of padding each) come by direct global -> LDS loads into three buffers.
-constexpr int KT_W = 11;                        // wave-instructions per wave and key tile
-constexpr int KT_BYTES = 4 * KT_W * 64 * 16;    // 44 KB
-constexpr int K_SLOTS = 64 * 25, V_SLOTS = 64 * 17;
+// wave w = queries 32 w ... of that head.  Key tiles of 32 rows (K at 25 slots of 16 bytes per
+// row, V at 17, one slot of padding each) come by direct global -> LDS loads into three buffers
+// of 24 KB, so two workgroups (two waves per SIMD, at most 256 registers each) share a CU and
+// one's softmax and waits overlap the other's matrix work.
+constexpr int DQ_KT = 32;                       // keys per tile
+constexpr int KT_W = 6;                         // wave-instructions per wave and key tile
+constexpr int KT_BYTES = 4 * KT_W * 64 * 16;    // 24 KB
+constexpr int K_SLOTS = DQ_KT * 25, V_SLOTS = DQ_KT * 17;
 
 template <bool SIGNAL>
-__global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdAttnArgs a) {
+__global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdAttnArgs a) {
   __shared__ __attribute__((aligned(16))) char KV[3 * KT_BYTES];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int QB = SIGNAL ? 32 : 128;
@@ -102,8 +105,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdAttnArgs a) {
   }
   const int q_last = min(q_first + QB, a.T) - 1;
   const bool active = head >= 0 && q0 < a.T;
-  const int klo = qlo(a, b, q_first) & ~63, khi = q_last + 1;
-  const int ntiles = (khi - klo + 63) / 64;
+  const int klo = qlo(a, b, q_first) & ~(DQ_KT - 1), khi = q_last + 1;
+  const int ntiles = (khi - klo + DQ_KT - 1) / DQ_KT;
   const int wq_hi = min(q0 + 31, a.T - 1);
   const int wlo_min = qlo(a, b, min(q0, a.T - 1)), wlo_max = qlo(a, b, wq_hi);
 
@@ -133,7 +136,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdAttnArgs a) {
   // never visible)
   const uint32_t lds0 = lds_u32(KV);
   auto issue = [&](int t) {
-    const int s0 = klo + 64 * t;
+    const int s0 = klo + DQ_KT * t;
     const uint32_t buf = lds0 + (uint32_t)((t % 3) * KT_BYTES);
 #pragma unroll
     for (int i = 0; i < KT_W; ++i) {
@@ -158,14 +161,14 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdAttnArgs a) {
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // tile t has landed for every wave; every wave is done with tile t - 1
     if (t + 2 < ntiles) issue(t + 2);
-    const int s0 = klo + 64 * t;
+    const int s0 = klo + DQ_KT * t;
     const f16_t *ks = (const f16_t *)(KV + (t % 3) * KT_BYTES);
     const f16_t *vs = (const f16_t *)(KV + (t % 3) * KT_BYTES + K_SLOTS * 16);
-    const bool skip = !active || s0 > wq_hi || s0 + 63 < wlo_min;
+    const bool skip = !active || s0 > wq_hi || s0 + DQ_KT - 1 < wlo_min;
     if (!skip) {
-      const bool full = s0 + 63 <= q0 && s0 >= wlo_max;
+      const bool full = s0 + DQ_KT - 1 <= q0 && s0 >= wlo_max;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < DQ_KT / 32; ++kb) {
         f32x16 S = {}, dP = {};
 #pragma unroll
         for (int k = 0; k < 12; ++k)
