@@ -604,22 +604,47 @@ __global__ void __launch_bounds__(256) pack_f16_kernel(const TS *src, int64_t ld
   }
 }
 
-// dst[row_off + c, r] = fp16(src[r, c]) for r < R, 0 for R <= r < R_pad (64 x 64 tiles through LDS)
+// dst[row_off + c, r] = fp16(src[r, c]) for r < R, 0 for R <= r < R_pad (64 x 64 tiles through LDS).
+// Each thread moves runs of 8: 16-byte row reads of the source (when aligned and inside the
+// matrix) and 16-byte column runs of the destination.
 template <typename TS>
 __global__ void __launch_bounds__(256) tpack_f16_kernel(const TS *src, int64_t lds, int32_t R, int32_t C, int32_t R_pad,
                                                         f16_t *dst, int64_t ldd, int32_t row_off) {
-  __shared__ float tile[64][65];
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  __shared__ __attribute__((aligned(16))) f16_t tile[64][72];  // row pitch 144 bytes
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int rr = i / 64, cc = i % 64;
-    const int r = r0 + rr, c = c0 + cc;
-    tile[rr][cc] = (r < R && c < C) ? (float)src[(int64_t)r * lds + c] : 0.f;
+  for (int i = threadIdx.x; i < 64 * 8; i += 256) {
+    const int rr = i >> 3, c8 = (i & 7) * 8;
+    const int r = r0 + rr, c = c0 + c8;
+    h8 v;
+    const TS *p = src + (int64_t)r * lds + c;
+    if (r < R && c + 8 <= C && ((uintptr_t)p & 15) == 0) {
+      const uint4 raw = *(const uint4 *)p;
+      const TS *e = (const TS *)&raw;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = f16s((float)e[k]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = (r < R && c + k < C) ? f16s((float)p[k]) : (f16_t)0.f;
+    }
+    *(h8 *)&tile[rr][c8] = v;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int cc = i / 64, rr = i % 64;
-    const int r = r0 + rr, c = c0 + cc;
-    if (c < C && r < R_pad) dst[(int64_t)(row_off + c) * ldd + r] = f16s(tile[rr][cc]);
+  for (int i = threadIdx.x; i < 64 * 8; i += 256) {
+    const int cc = i >> 3, r8 = (i & 7) * 8;
+    const int c = c0 + cc, r = r0 + r8;
+    if (c >= C || r >= R_pad) continue;
+    h8 v;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = tile[r8 + k][cc];
+    f16_t *q = dst + (int64_t)(row_off + c) * ldd + r;
+    if (r + 8 <= R_pad && ((uintptr_t)q & 15) == 0) {
+      *(h8 *)q = v;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (r + k < R_pad) q[k] = v[k];
+    }
   }
 }
 
