@@ -671,33 +671,6 @@ __global__ void __launch_bounds__(256) combine_fast_kernel(const float *heads, c
   }
 }
 
-// dq [M, n_H, 192] (fp32) -> the query-latent operand: columns h d_h + e (dq^C) and
-// q_off + h d_r + j (dq^R rotated back by RoPE's negative angle), row m at position m % T
-__global__ void __launch_bounds__(256) pack_dq_kernel(const float *dq, f16_t *a6, int64_t lda6, int32_t q_off,
-                                                      int32_t M, int32_t T_, LayerDims d, const float2 *cs) {
-  const int dqk = d.d_h + d.d_r, half = d.d_r / 2;
-  const int per = d.d_h + half;  // elements handled per (m, h): d_h copies and d_r / 2 rotations
-  const int64_t n = (int64_t)M * d.n_heads * per;
-  for (int64_t idx = blockIdx.x * 256ll + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * 256) {
-    const int k = (int)(idx % per);
-    const int64_t mh = idx / per;
-    const int h = (int)(mh % d.n_heads);
-    const int64_t m = mh / d.n_heads;
-    const float *src = dq + mh * dqk;
-    if (k < d.d_h) {
-      a6[m * lda6 + (int64_t)h * d.d_h + k] = f16s(src[k]);
-    } else {
-      const int j = k - d.d_h;
-      const float2 r = cs[(m % T_) * half + j];
-      const float c = r.x, s = r.y;
-      const float u = src[d.d_h + j], w = src[d.d_h + j + half];
-      f16_t *o = a6 + m * lda6 + q_off + (int64_t)h * d.d_r;
-      o[j] = f16s(u * c + w * s);          // rotation by -angle
-      o[j + half] = f16s(-u * s + w * c);
-    }
-  }
-}
-
 // dk [B, n_kv, T, 192], dv [B, n_kv, T, 128] -> [dK^C | dV] as the latent operand a3 [M, 2 n_kv d_h]
 // (fp16) and dk^R summed over the KV groups, rotated back (fp32 [M, d_r])
 __global__ void __launch_bounds__(256) pack_dkv_kernel(const float *dk, const float *dv, f16_t *a3, float *dkr,
@@ -915,13 +888,13 @@ hipError_t launch_backward_fast(const FastBwdArgs &a, const LayerDims &d, hipStr
   at.dq = b.dq; at.dk = b.dk; at.dv = b.dv;
   at.B = a.B; at.T = T_; at.lcap = a.lcap; at.n_heads = nH; at.n_signal = nS; at.n_noise = d.n_noise;
   at.n_kv = nKV; at.window = d.window; at.c = d.scale * 1.4426950408889634f; at.tau = d.scale;
-  BWD_TRY(launch_bwd_attention(at, s));
   hipLaunchKernelGGL(rope_table_kernel, dim3((T_ * (dr / 2) + 255) / 256), dim3(256), 0, s, b.rope_cs, T_, dr,
                      d.theta);
   BWD_TRY(hipGetLastError());
-  hipLaunchKernelGGL(pack_dq_kernel, dim3(grid_for((int64_t)M * nH * (dh + dr / 2))), dim3(256), 0, s, b.dq, b.a6,
-                     (int64_t)k6, nH * dh, M, T_, d, (const float2 *)b.rope_cs);
-  BWD_TRY(hipGetLastError());
+  // dq leaves the attention kernel already packed into a6 (dq^C, and dq^R rotated back)
+  at.dq = nullptr;
+  at.a6 = b.a6; at.lda6 = k6; at.q_off = nH * dh; at.rope_cs = (const float2 *)b.rope_cs;
+  BWD_TRY(launch_bwd_attention(at, s));
   hipLaunchKernelGGL(pack_dkv_kernel, dim3(grid_for((int64_t)M * nKV * dh + (int64_t)M * dr / 2)), dim3(256), 0, s,
                      b.dk, b.dv, b.a3, b.dkr, M, T_, d, (const float2 *)b.rope_cs);
   BWD_TRY(hipGetLastError());

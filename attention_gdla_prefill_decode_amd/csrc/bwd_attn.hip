@@ -196,6 +196,38 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdAttnArgs a) {
   }
   if (!qok) return;
   // dQ[db][j] = dQ^T[dim 32 db + 8 (j / 4) + 4 (l / 32) + j % 4][query tq]
+  if (a.a6) {
+    // packed: dims 0..127 as they are; rope dims r and r + 32 (blocks 4 and 5, same lane and
+    // index) rotated by the negative angle of token tq
+    f16_t *oc = a.a6 + ((int64_t)b * a.T + tq) * a.lda6 + (int64_t)head * DH;
+    f16_t *orr = a.a6 + ((int64_t)b * a.T + tq) * a.lda6 + a.q_off + (int64_t)head * DR;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = h16(dQ[db][4 * i + e] * a.tau);
+        *(f16x4 *)(oc + 32 * db + 8 * i + 4 * (lane >> 5)) = v;
+      }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 8 * i + 4 * (lane >> 5);
+      const float4 c01 = *(const float4 *)(a.rope_cs + (int64_t)tq * (DR / 2) + r);
+      const float4 c23 = *(const float4 *)(a.rope_cs + (int64_t)tq * (DR / 2) + r + 2);
+      const float cs[4] = {c01.x, c01.z, c23.x, c23.z}, sn[4] = {c01.y, c01.w, c23.y, c23.w};
+      f16x4 lo4, hi4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float u = dQ[4][4 * i + e] * a.tau, w = dQ[5][4 * i + e] * a.tau;
+        lo4[e] = h16(u * cs[e] + w * sn[e]);
+        hi4[e] = h16(-u * sn[e] + w * cs[e]);
+      }
+      *(f16x4 *)(orr + r) = lo4;
+      *(f16x4 *)(orr + r + 32) = hi4;
+    }
+    return;
+  }
   float *o = a.dq + mh * DQK;
 #pragma unroll
   for (int db = 0; db < 6; ++db)

@@ -117,7 +117,14 @@ struct BwdAttnArgs {
   const float *drow;   // [n_H, M] (+32 padding): rowsum(dH (.) H)
   const int32_t *lo;   // [M] (+32 padding): lowest visible key of every token
   const int32_t *doc;  // [M] document starts or null
-  float *dq;           // [M, n_H, 192]
+  float *dq;           // [M, n_H, 192], or (a6 non-null) not written
+  // a6 non-null: dq leaves packed instead, in fp16 rows of the query-latent operand: dq^C of head
+  // h at columns h d_h .., dq^R rotated back by RoPE's angle at q_off + h d_r .. (cos, sin of
+  // token t and frequency j in rope_cs[t d_r / 2 + j])
+  f16_t *a6;
+  int64_t lda6;
+  int32_t q_off;
+  const float2 *rope_cs;
   float *dk;           // [B, n_kv, T, 192]: the k^R part summed over this KV group's heads only
   float *dv;           // [B, n_kv, T, 128]
   int32_t B, T, lcap, n_heads, n_signal, n_noise, n_kv, window;
@@ -137,7 +144,7 @@ struct FastBwdBuffers {
   f16_t *ta, *tb;               // transposed operands [rows, M_pad]
   float *dheads, *dd, *dlaml, *drow;
   f16_t *dh16;                  // [M, n_H, d_h]
-  float *dq, *dk, *dv;          // attention gradients
+  float *dq, *dk, *dv;          // attention gradients (dq unused: the dq kernel packs into a6)
   f16_t *a6, *a3, *a8;          // gradient operands [M, k6], [M, k3], [M, k8]
   float *dkr, *dcbar, *dckv, *rkv, *dcq, *daq, *rq;
   int32_t *lo;                  // [M + 32]

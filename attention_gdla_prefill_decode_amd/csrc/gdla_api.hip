@@ -284,7 +284,7 @@ FastBackwardLayout plan_backward_fast(const LayerDims &d, int32_t B, int32_t T) 
       2 * trows_a * Mp, 2 * trows_b * Mp,                                   // ta tb
       4 * M * nH * dh, 4 * M * nS * dh, 4 * M * nS, 4 * (M * nH + 32),      // dheads dd dlaml drow
       2 * M * nH * dh,                                                      // dh16
-      4 * M * nH * (dh + dr), 4 * M * nKV * (dh + dr), 4 * M * nKV * dh,    // dq dk dv
+      0, 4 * M * nKV * (dh + dr), 4 * M * nKV * dh,                         // dq (packed by the kernel) dk dv
       2 * M * k6, 2 * M * k3, 2 * M * k8,                                   // a6 a3 a8
       4 * M * dr, 4 * M * d.d_c, 4 * M * d.d_c, 4 * M, 4 * M * d.d_cq, 4 * M * d.d_cq, 4 * M,
       4 * (M + 32), 8 * (size_t)T * (dr / 2),                             // lo rope_cs
