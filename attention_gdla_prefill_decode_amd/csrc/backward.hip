@@ -648,29 +648,6 @@ __global__ void __launch_bounds__(256) tpack_f16_kernel(const TS *src, int64_t l
   }
 }
 
-// Eq.(10) backward with sigmoid(G) from the forward (fp16): per element (m, i, e)
-//   D = H_i - lambda_i H_(n_S + i mod n_N);  dD = dY sg;  dG = dY D sg (1 - sg);  dH_i = dD
-// dG goes straight into the fp16 operand of the query-latent GEMM (columns g_off ...).
-__global__ void __launch_bounds__(256) combine_fast_kernel(const float *heads, const float *lam, const f16_t *sg16,
-                                                           const float *dy, float *dheads, float *dd, f16_t *a6,
-                                                           int64_t lda6, int32_t g_off, int32_t M, LayerDims d) {
-  const int64_t n = (int64_t)M * d.n_signal * d.d_h;
-  for (int64_t idx = blockIdx.x * 256ll + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * 256) {
-    const int e = (int)(idx % d.d_h);
-    const int64_t r = idx / d.d_h;
-    const int i = (int)(r % d.n_signal);
-    const int64_t m = r / d.n_signal;
-    const float hs = heads[(m * d.n_heads + i) * d.d_h + e];
-    const float hn = heads[(m * d.n_heads + d.n_signal + i % d.n_noise) * d.d_h + e];
-    const float dval = hs - lam[m * d.n_signal + i] * hn;
-    const float sg = (float)sg16[idx];
-    const float ddv = dy[idx] * sg;
-    dd[idx] = ddv;
-    dheads[(m * d.n_heads + i) * d.d_h + e] = ddv;
-    a6[m * lda6 + g_off + (idx - m * d.n_signal * d.d_h)] = f16s(dy[idx] * dval * sg * (1.0f - sg));
-  }
-}
-
 // dk [B, n_kv, T, 192], dv [B, n_kv, T, 128] -> [dK^C | dV] as the latent operand a3 [M, 2 n_kv d_h]
 // (fp16) and dk^R summed over the KV groups, rotated back (fp32 [M, d_r])
 __global__ void __launch_bounds__(256) pack_dkv_kernel(const float *dk, const float *dv, f16_t *a3, float *dkr,
@@ -739,28 +716,58 @@ __global__ void __launch_bounds__(256) zero_cols_kernel(f16_t *dst, int64_t ldd,
 // Eq.(8) backward of one row per workgroup: noise head j gets dH = -sum over the signal heads
 // i = j (mod n_N) of lambda_i dD_i; dlambda_i = -sum_e dD_i,e H_(n_S + i mod n_N),e, through the
 // sigmoid unless lambda is fixed.  Reads are contiguous along e.
-__global__ void __launch_bounds__(256) noise_lambda_fast_kernel(const float *heads, const float *lam, const float *dd,
-                                                                float *dheads, float *dlam_logit, int override_lam,
-                                                                LayerDims d) {
+// Eq.(10) and Eq.(8) backward of one token row m in one workgroup (d_h = 128), everything the
+// attention backward and the query-latent GEMM need from the gate and the differential combine:
+//   dD_i = dY_i sg_i,  dG_i = dY_i D_i sg_i (1 - sg_i) (fp16 into a6),  dH_i = dD_i,
+//   dH_(n_S + j) = -sum over the signal heads i of partner j of lambda_i dD_i,
+//   dlambda-logit_i = -(dD_i . H_(n_S + j)) lambda_i (1 - lambda_i)  (0 with a fixed lambda),
+//   drow_h = dH_h . H_h (head-major), dH in fp16.
+// Wave w takes the noise heads j = w, w + 4, ... and, for each, its signal heads i = j + n_N k;
+// lane l holds dims 2 l and 2 l + 1.
+__global__ void __launch_bounds__(256) combine_row_kernel(const float *heads, const float *lam, const f16_t *sg16,
+                                                          const float *dy, f16_t *dh16, f16_t *a6, int64_t lda6,
+                                                          int32_t g_off, float *drow, float *dlam_logit,
+                                                          int override_lam, int32_t M, LayerDims d) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
   const int64_t m = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const float *ddm = dd + m * d.n_signal * d.d_h;
-  const float *hm = heads + m * d.n_heads * d.d_h;
-  for (int idx = threadIdx.x; idx < d.n_noise * d.d_h; idx += 256) {
-    const int j = idx / d.d_h, e = idx % d.d_h;
-    float acc = 0.f;
-    for (int i = j; i < d.n_signal; i += d.n_noise) acc -= lam[m * d.n_signal + i] * ddm[i * d.d_h + e];
-    dheads[(m * d.n_heads + d.n_signal + j) * d.d_h + e] = acc;
-  }
-  for (int i = wave; i < d.n_signal; i += 4) {
-    const float *hn = hm + (int64_t)(d.n_signal + i % d.n_noise) * d.d_h;
-    float acc = 0.f;
-    for (int e = lane; e < d.d_h; e += 64) acc -= ddm[i * d.d_h + e] * hn[e];
-    acc = wsum(acc);
-    if (lane == 0) {
-      const float l = lam[m * d.n_signal + i];
-      dlam_logit[m * d.n_signal + i] = override_lam ? 0.f : acc * l * (1.0f - l);
+  const int e = 2 * lane;
+  const int nS = d.n_signal, nN = d.n_noise, nH = d.n_heads;
+  const float *hm = heads + m * nH * 128;
+  for (int j = wave; j < nN; j += 4) {
+    const float2 hn = *(const float2 *)(hm + (int64_t)(nS + j) * 128 + e);
+    float2 dn = make_float2(0.f, 0.f);
+    for (int i = j; i < nS; i += nN) {
+      const int64_t yi = (m * nS + i) * 128 + e;
+      const float2 hs = *(const float2 *)(hm + (int64_t)i * 128 + e);
+      const float2 yv = *(const float2 *)(dy + yi);
+      const h2 sgh = *(const h2 *)(sg16 + yi);
+      const float l = lam[m * nS + i];
+      const float s0 = (float)sgh[0], s1 = (float)sgh[1];
+      const float d0 = yv.x * s0, d1 = yv.y * s1;  // dD = dH_i
+      h2 g;
+      g[0] = f16s(yv.x * (hs.x - l * hn.x) * s0 * (1.0f - s0));
+      g[1] = f16s(yv.y * (hs.y - l * hn.y) * s1 * (1.0f - s1));
+      *(h2 *)(a6 + m * lda6 + g_off + (int64_t)i * 128 + e) = g;
+      h2 dh;
+      dh[0] = f16s(d0);
+      dh[1] = f16s(d1);
+      *(h2 *)(dh16 + (m * nH + i) * 128 + e) = dh;
+      dn.x -= l * d0;
+      dn.y -= l * d1;
+      const float rs = wsum(d0 * hs.x + d1 * hs.y);
+      const float dl = wsum(d0 * hn.x + d1 * hn.y);
+      if (lane == 0) {
+        drow[(int64_t)i * M + m] = rs;
+        dlam_logit[m * nS + i] = override_lam ? 0.f : -dl * l * (1.0f - l);
+      }
     }
+    h2 dh;
+    dh[0] = f16s(dn.x);
+    dh[1] = f16s(dn.y);
+    *(h2 *)(dh16 + (m * nH + nS + j) * 128 + e) = dh;
+    const float rn = wsum(dn.x * hn.x + dn.y * hn.y);
+    if (lane == 0) drow[(int64_t)(nS + j) * M + m] = rn;
   }
 }
 
@@ -782,10 +789,6 @@ __global__ void __launch_bounds__(256) qlo_kernel(const int32_t *doc, int32_t *l
   int v = window > 0 ? max(0, t - window + 1) : 0;
   if (doc) v = max(v, min(max(doc[m], 0), t));
   lo[m] = v;
-}
-
-__global__ void __launch_bounds__(256) to_f16_kernel(const float *src, f16_t *dst, int64_t n) {
-  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) dst[i] = f16s(src[i]);
 }
 
 template <typename TS>
@@ -865,20 +868,11 @@ hipError_t launch_backward_fast(const FastBwdArgs &a, const LayerDims &d, hipStr
   BWD_TRY(tpack(a.y16, ny, M, ny, Mp, b.ta, Mp, 0, s));
   BWD_TRY(tpack((const bf16_t *)a.dout, dm, M, dm, Mp, b.tb, Mp, 0, s));
   BWD_TRY(nt(b.ta, Mp, b.tb, Mp, G.dw_o, dm, ny, dm, Mp, s, b.splitk));
-  // gate and differential combine; noise-head dH and dlambda
-  hipLaunchKernelGGL(combine_fast_kernel, dim3(grid_for((int64_t)M * ny)), dim3(256), 0, s, a.heads, a.lam, a.sg16,
-                     b.dy, b.dheads, b.dd, b.a6, (int64_t)k6, nH * dh + nH * dr, M, d);
-  BWD_TRY(hipGetLastError());
-  hipLaunchKernelGGL(noise_lambda_fast_kernel, dim3(M), dim3(256), 0, s, a.heads, a.lam, b.dd, b.dheads, b.dlaml,
-                     a.lam_overridden ? 1 : 0, d);
-  BWD_TRY(hipGetLastError());
-  hipLaunchKernelGGL(bwd_drow_kernel, dim3((unsigned)(((int64_t)M * nH + 3) / 4)), dim3(256), 0, s, a.heads,
-                     b.dheads, b.drow, (int64_t)M * nH, dh, nH);
+  // gate and differential combine: dG, dH (fp16), noise-head dH, dlambda and the row sums, per row
+  hipLaunchKernelGGL(combine_row_kernel, dim3(M), dim3(256), 0, s, a.heads, a.lam, a.sg16, b.dy, b.dh16, b.a6,
+                     (int64_t)k6, nH * dh + nH * dr, b.drow, b.dlaml, a.lam_overridden ? 1 : 0, M, d);
   BWD_TRY(hipGetLastError());
   hipLaunchKernelGGL(qlo_kernel, dim3(grid_for(M)), dim3(256), 0, s, a.doc, b.lo, M, T_, d.window);
-  BWD_TRY(hipGetLastError());
-  hipLaunchKernelGGL(to_f16_kernel, dim3(grid_for((int64_t)M * nH * dh)), dim3(256), 0, s, b.dheads, b.dh16,
-                     (int64_t)M * nH * dh);
   BWD_TRY(hipGetLastError());
 
   // ---- the softmax maps

@@ -142,7 +142,7 @@ struct FastBwdBuffers {
   f16_t *dout16;                // [M, d]
   float *dy;                    // [M, n_S d_h]
   f16_t *ta, *tb;               // transposed operands [rows, M_pad]
-  float *dheads, *dd, *dlaml, *drow;
+  float *dheads, *dd, *dlaml, *drow;  // dheads, dd unused (combine_row_kernel writes dH in fp16)
   f16_t *dh16;                  // [M, n_H, d_h]
   float *dq, *dk, *dv;          // attention gradients (dq unused: the dq kernel packs into a6)
   f16_t *a6, *a3, *a8;          // gradient operands [M, k6], [M, k3], [M, k8]

@@ -282,7 +282,7 @@ FastBackwardLayout plan_backward_fast(const LayerDims &d, int32_t B, int32_t T) 
       2 * nS * dh * dm, 2 * d.d_c * k3, 2 * d.d_cq * k6, 2 * dm * k8,      // wo16 w3 w6 w8
       2 * M * dm, 4 * M * nS * dh,                                          // dout16 dy
       2 * trows_a * Mp, 2 * trows_b * Mp,                                   // ta tb
-      4 * M * nH * dh, 4 * M * nS * dh, 4 * M * nS, 4 * (M * nH + 32),      // dheads dd dlaml drow
+      0, 0, 4 * M * nS, 4 * (M * nH + 32),                                  // (dheads dd: unused) dlaml drow
       2 * M * nH * dh,                                                      // dh16
       0, 4 * M * nKV * (dh + dr), 4 * M * nKV * dh,                         // dq (packed by the kernel) dk dv
       2 * M * k6, 2 * M * k3, 2 * M * k8,                                   // a6 a3 a8
