@@ -596,6 +596,24 @@ __device__ __forceinline__ f16_t f16s(float v) { return (f16_t)fminf(fmaxf(v, -6
 template <typename TS>
 __global__ void __launch_bounds__(256) pack_f16_kernel(const TS *src, int64_t lds, int32_t rows, int32_t cols,
                                                        f16_t *dst, int64_t ldd, int32_t col_off) {
+  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+  // runs of 4 columns when every run is aligned on both sides (the usual case), else one by one
+  const bool quads = cols % 4 == 0 && lds % 4 == 0 && ldd % 4 == 0 && col_off % 4 == 0 &&
+                     ((uintptr_t)src & (4 * sizeof(TS) - 1)) == 0 && ((uintptr_t)dst & 7) == 0;
+  if (quads) {
+    const int c4 = cols / 4;
+    const int64_t n = (int64_t)rows * c4;
+    for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+      const int64_t r = i / c4;
+      const int c = 4 * (int)(i % c4);
+      const TS *p = src + r * lds + c;
+      h4 v;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = f16s((float)p[k]);
+      *(h4 *)(dst + r * ldd + col_off + c) = v;
+    }
+    return;
+  }
   const int64_t n = (int64_t)rows * cols;
   for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
     const int64_t r = i / cols;
