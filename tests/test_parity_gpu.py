@@ -274,10 +274,13 @@ def test_backward_fused_matches_oracle(cfg, T, batch, window, lens):
 
 
 # Enough tokens that the weight-gradient products are split along the token axis (8192 rows: up
-# to 8 slices of 1024, summed in order) on the fused path.
-def test_backward_fused_split_k():
-    got, exp = H.backward_case(BF, 2048, 4, window=300, seed=79)
-    for line in H.check_grads(got, exp, 1e-2, "fused backward, 4 x 2048 tokens (split-K products)"):
+# to 8 slices of 1024; 4096 rows: up to 4), summed in order, on the fused path; with a window, and
+# with packed documents (a one-token document among them).
+@pytest.mark.parametrize("batch,window,lens", [(4, 300, None), (2, 0, (700, 1, 900, 447))])
+def test_backward_fused_split_k(batch, window, lens):
+    docs = None if lens is None else [H.doc_starts(0, lens) for _ in range(batch)]
+    got, exp = H.backward_case(BF, 2048, batch, window=window, docs=docs, seed=79)
+    for line in H.check_grads(got, exp, 1e-2, f"fused backward, {batch} x 2048 tokens (split-K products)"):
         _say(line)
 
 
