@@ -96,6 +96,30 @@ __device__ __forceinline__ bf16x4 tr_read(const char *p) {
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4 mfma16h(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ _Float16 sat16(float v) { return (_Float16)fminf(fmaxf(v, -65504.f), 65504.f); }
+// 8 fp32 -> hi = fp16(v) (saturating), lo = fp16(v - hi): hi + lo carries about 21 bits of v
+__device__ __forceinline__ void split16(const float *v, f16x8 &hi, f16x8 &lo) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    hi[i] = sat16(v[i]);
+    lo[i] = (_Float16)(v[i] - (float)hi[i]);
+  }
+}
+// 8 bf16 (16 bytes) -> fp16: exact in the fp16 normal range, saturating beyond it
+__device__ __forceinline__ f16x8 bf16_to_f16x8(uint4 w) {
+  const unsigned u[4] = {w.x, w.y, w.z, w.w};
+  f16x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[2 * i] = (_Float16)fminf(fmaxf(__uint_as_float(u[i] << 16), -65504.f), 65504.f);
+    r[2 * i + 1] = (_Float16)fminf(fmaxf(__uint_as_float(u[i] & 0xffff0000u), -65504.f), 65504.f);
+  }
+  return r;
+}
 
 __device__ __forceinline__ float head_max(float v) {  // over lanes l, l^16, l^32, l^48
   v = fmaxf(v, __shfl_xor(v, 16, 64));
@@ -504,39 +528,44 @@ __global__ void __launch_bounds__(256) absorb_kernel(const float *qc, const floa
     const int r = i / DR, e = i % DR;
     qabs[rowq[r] * ROW + DC + e] = (bf16_t)qr[rowq[r] * DR + e];
   }
+  for (int i = nr * 32 + tid; i < R * 32; i += 256) {  // rows past the list: zeros
+    const int r = i >> 5, e = (i & 31) * 4;
+    *(float4 *)&qs[r][e] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   __syncthreads();
+  // q~[r][c] = sum_e q^C[r][e] W_uk[c][128 kv + e] on v_mfma_f32_16x16x32_f16 (A[m = r][k = e],
+  // B[k = e][n = c], acc[j] = C[4 (l / 16) + j][l % 16]); wave w takes c = 128 w .. 128 w + 127
+  const int lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g = lane >> 4;
   const int64_t ldw = (int64_t)d.n_kv * 128;
-  for (int c = tid; c < DC; c += 256) {
-    uint4 w[16];
-    const bf16_t *wr = w_uk + (int64_t)c * ldw + kv * 128;
+  // q^C as the sum of two fp16 parts (hi + lo carry about 21 bits), so the product keeps the
+  // fp32 query's precision; the weights are exact in fp16
+  f16x8 qa[4], ql[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) w[i] = *(const uint4 *)(wr + 8 * i);
-    for (int r = 0; r < nr; ++r) {
-      float acc = 0.f;
+  for (int k = 0; k < 4; ++k) split16(&qs[l16][32 * k + 8 * g], qa[k], ql[k]);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float4 qa = *(const float4 *)&qs[r][8 * i], qb = *(const float4 *)&qs[r][8 * i + 4];
-        const unsigned u[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
-        acc = fmaf(qa.x, __uint_as_float(u[0] << 16), acc);
-        acc = fmaf(qa.y, __uint_as_float(u[0] & 0xffff0000u), acc);
-        acc = fmaf(qa.z, __uint_as_float(u[1] << 16), acc);
-        acc = fmaf(qa.w, __uint_as_float(u[1] & 0xffff0000u), acc);
-        acc = fmaf(qb.x, __uint_as_float(u[2] << 16), acc);
-        acc = fmaf(qb.y, __uint_as_float(u[2] & 0xffff0000u), acc);
-        acc = fmaf(qb.z, __uint_as_float(u[3] << 16), acc);
-        acc = fmaf(qb.w, __uint_as_float(u[3] & 0xffff0000u), acc);
-      }
-      qabs[rowq[r] * ROW + c] = (bf16_t)acc;
+  for (int nb = 0; nb < 8; ++nb) {
+    const int c = 128 * wave + 16 * nb + l16;
+    const bf16_t *wr = w_uk + (int64_t)c * ldw + kv * 128 + 8 * g;
+    f32x4 acc = {};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f16x8 wb = bf16_to_f16x8(*(const uint4 *)(wr + 32 * k));
+      acc = mfma16h(qa[k], wb, acc);
+      acc = mfma16h(ql[k], wb, acc);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * g + j;
+      if (r < nr) qabs[rowq[r] * ROW + c] = (bf16_t)acc[j];
     }
   }
 }
 
 // H_h = o_h W_uv[:, kv(h)] in fp32, for the block's R rows.  Thread (half, e) sums latent
 // dimensions half * 256 .. + 255 for output column e; the two halves are added through LDS.
-__global__ void __launch_bounds__(256) unabsorb_kernel(const float *o, const bf16_t *w_uv, float *heads,
+__global__ void __launch_bounds__(256) unabsorb_kernel(const float *o, const f16_t *wuvt, float *heads,
                                                        int32_t B, LayerDims d) {
   __shared__ __attribute__((aligned(16))) float os[R][DC];
-  __shared__ float red[R][128];
   __shared__ int64_t rowq[R];
   const int kv = blockIdx.y, tid = threadIdx.x;
   int ns;
@@ -557,31 +586,30 @@ __global__ void __launch_bounds__(256) unabsorb_kernel(const float *o, const bf1
     *(float4 *)&os[r][c] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   __syncthreads();
-  const int e = tid & 127, half = tid >> 7;
-  const int64_t ldw = (int64_t)d.n_kv * 128;
-  const bf16_t *wc = w_uv + kv * 128 + e;
-  float acc[R];
+  // H[r][e] = sum_c o[r][c] W_uv[c][128 kv + e] on v_mfma_f32_16x16x32_f16 (A[m = r][k = c],
+  // B[k = c][n = e]); wave w takes e = 32 w .. 32 w + 31 (two blocks of 16), K = 512 in 16 steps
+  const int lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g = lane >> 4;
+  f32x4 acc[2] = {};
+#pragma unroll 4
+  for (int k = 0; k < DC / 32; ++k) {
+    const int c0 = 32 * k + 8 * g;
+    f16x8 oa, ol;  // o as hi + lo fp16 parts
+    split16(&os[l16][c0], oa, ol);
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = 0.f;
-  for (int c = half * 256; c < half * 256 + 256; c += 4) {
-    const float w0 = (float)wc[(int64_t)c * ldw], w1 = (float)wc[(int64_t)(c + 1) * ldw];
-    const float w2 = (float)wc[(int64_t)(c + 2) * ldw], w3 = (float)wc[(int64_t)(c + 3) * ldw];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float4 v = *(const float4 *)&os[r][c];
-      acc[r] = fmaf(v.x, w0, fmaf(v.y, w1, fmaf(v.z, w2, fmaf(v.w, w3, acc[r]))));
+    for (int nb = 0; nb < 2; ++nb) {
+      // W_uv^T row 128 kv + e, latent dims c0 .. c0 + 7
+      const f16x8 wb = *(const f16x8 *)(wuvt + (int64_t)(kv * 128 + 32 * wave + 16 * nb + l16) * DC + c0);
+      acc[nb] = mfma16h(oa, wb, acc[nb]);
+      acc[nb] = mfma16h(ol, wb, acc[nb]);
     }
   }
-  if (half) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) red[r][e] = acc[r];
-  }
-  __syncthreads();
-  if (!half) {
+  for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (r < nr) heads[rowq[r] * 128 + e] = acc[r] + red[r][e];
-  }
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * g + j;
+      if (r < nr) heads[rowq[r] * 128 + 32 * wave + 16 * nb + l16] = acc[nb][j];
+    }
 }
 
 }  // namespace
@@ -633,7 +661,9 @@ gdla_status run_fast_decode(const LayerDims &d, const gdla_weights *w, int32_t B
   hipLaunchKernelGGL(merge_splits_kernel, dim3(BT * d.n_heads), dim3(128), 0, s, part_o, part_ml, o, d.n_heads,
                      L.splits);
   if (hipGetLastError() != hipSuccess) return GDLA_ERR_HIP;
-  hipLaunchKernelGGL(unabsorb_kernel, gk, dim3(256), 0, s, o, (const bf16_t *)w->w_uv, heads, BT, d);
+  f16_t *wuvt = (f16_t *)((char *)ws + L.wuvt);
+  if (launch_transpose_weight(w->w_uv, wuvt, DC, d.n_kv * 128, true, s) != hipSuccess) return GDLA_ERR_HIP;
+  hipLaunchKernelGGL(unabsorb_kernel, gk, dim3(256), 0, s, o, (const f16_t *)wuvt, heads, BT, d);
   if (hipGetLastError() != hipSuccess) return GDLA_ERR_HIP;
   return GDLA_OK;
 }
