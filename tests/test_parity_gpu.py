@@ -284,6 +284,24 @@ def test_backward_fused_split_k(batch, window, lens):
         _say(line)
 
 
+# Every gradient has one writer and the K slices are summed in order: repeated calls (fused path
+# with split products, and the general path) give identical bits.
+@pytest.mark.parametrize("cfg,T,batch", [(BF, 2048, 2), (BF, 64, 1)])
+def test_backward_is_deterministic(cfg, T, batch):
+    inp = synth.make_inputs(cfg, "cpu", seed=83, batch=batch, seq=T, p0=0, random_gamma=True)
+    gen = torch.Generator().manual_seed(84)
+    dout = torch.randn((batch, T, cfg["d_model"]), generator=gen).to(inp["x"].dtype).to("cuda")
+    dev = H.device_inputs(inp)
+    dims = gd.make_dims(cfg)
+    tensors = dict(dev["weights"], gamma_q=dev["gamma_q"], gamma_kv=dev["gamma_kv"])
+    first = gd.gdla_backward(dims, dev["wstruct"], tensors, dev["x"], dout)
+    first = {k: v.clone() for k, v in first.items()}
+    second = gd.gdla_backward(dims, dev["wstruct"], tensors, dev["x"], dout)
+    torch.cuda.synchronize()
+    for k in first:
+        assert torch.equal(first[k], second[k]), f"backward {k} differs between two calls"
+
+
 def test_backward_lambda_zero():
     got, exp = H.backward_case(BF, 48, 1, seed=71, lam_zero=True)
     H.check_grads(got, exp, 1e-5, "backward, lambda = 0")
