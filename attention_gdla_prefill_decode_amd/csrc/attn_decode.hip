@@ -23,10 +23,9 @@
 //   softmax against a fixed reference (see SoftmaxState), P^T -> LDS, barrier,
 //   O^T[dim, head] += cbar^T[dim, key] . P^T[key, head]    (A = cbar^T by ds_read_b64_tr_b16,
 //                                                           B = P^T of each head block)
-// Rows are unpadded; chunk c of row r sits at c ^ f(r) with f(r) = 4 r_1 + 2 (r_0 ^ r_2) +
-// (r_0 ^ r_3) (r_i = bit i of r).  The 16-byte row reads (consecutive rows, one chunk) and the
-// transposing reads (4 consecutive rows, an aligned pair of chunks) then hit distinct banks whether
-// the LDS serves 32 or 64 banks of 4 bytes per clock.
+// Rows are unpadded; chunk c of row r sits at c ^ (r mod 8).  With it the hardware counter reads no
+// LDS bank conflicts for the 16-byte row reads (16 consecutive rows, one chunk) or the transposing
+// reads (4 consecutive rows, an aligned pair of chunks).
 // Each split writes its unnormalised O, its reference m (log2 units) and sum l; merge_splits
 // combines them.
 #include "fast_paths.h"
@@ -85,9 +84,7 @@ __device__ __forceinline__ bool decode_unit(const DecodeArgs &a, int &b, int &to
 
 int decode_grid(int B, int q_len, int splits) { return (B * splits + 7) / 8 * 8 * q_len; }
 
-__host__ __device__ constexpr int swz(int r) {
-  return 4 * ((r >> 1) & 1) + 2 * ((r & 1) ^ ((r >> 2) & 1)) + ((r & 1) ^ ((r >> 3) & 1));
-}
+__host__ __device__ constexpr int swz(int r) { return r & 7; }
 
 __device__ __forceinline__ bf16x4 tr_read(const char *p) {
   return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p));
