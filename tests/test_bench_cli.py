@@ -1,0 +1,36 @@
+"""Host-side checks of bench.py's command line (no GPU): the single-GPU contract and the
+algorithmic FLOP and byte counts the roofline figures divide by."""
+
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import synth  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
+
+
+def test_attention_flop_of_the_8k_prefill():
+    # causal pairs of 8192 tokens, 64 signal heads, 2 (2 d_h + d_r) per pair and head
+    cfg = synth.WORKLOADS["prefill_8k"]
+    f = bench.layer_flops(cfg, 8192, 0, 0)
+    pairs = 8192 * 8193 // 2
+    assert f["pairs"] == pairs
+    assert f["attn_signal"] == 2.0 * 64 * pairs * (2 * 128 + 64)
+
+
+def test_backward_flop_counts_five_products_per_pair():
+    cfg = synth.WORKLOADS["prefill_8k"]
+    f = bench.layer_flops(cfg, 8192, 0, 0)
+    bw = bench.backward_flops(cfg, 8192, 0)
+    assert bw["attention"] == 2.0 * 80 * f["pairs"] * (3 * 192 + 2 * 128)
+    assert bw["total"] == f["total"] + bw["attention"] + bw["proj"]
