@@ -5,6 +5,7 @@ of the GDLA forward runs in the library's HIP kernels.  There is no fallback: if
 missing, or a call fails, an exception is raised.
 """
 
+import contextlib
 import ctypes
 import os
 
@@ -185,13 +186,16 @@ def _ptr(t):
 
 
 def make_weights(weights, gamma_q=None, gamma_kv=None):
-    """gdla_weights from a dict of device tensors ([in, out] row-major, contiguous)."""
+    """gdla_weights from a dict of device tensors ([in, out] row-major, contiguous).  The returned
+    struct keeps references to the tensors, so their memory lives as long as the struct does."""
     vals = dict(weights)
     vals["gamma_q"], vals["gamma_kv"] = gamma_q, gamma_kv
     for k, v in vals.items():
         if v is not None and not v.is_contiguous():
             raise ValueError(f"weight {k} must be contiguous")
-    return GdlaWeights(*[None if vals.get(n) is None else vals[n].data_ptr() for n in WEIGHT_FIELDS])
+    w = GdlaWeights(*[None if vals.get(n) is None else vals[n].data_ptr() for n in WEIGHT_FIELDS])
+    w._tensors = {n: vals.get(n) for n in WEIGHT_FIELDS}
+    return w
 
 
 def _pos_array(pos):
@@ -202,6 +206,13 @@ def _pos_array(pos):
 def _stream(stream):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _on(stream):
+    """Context for the memory a call allocates (workspace, outputs): with an explicit stream they
+    are allocated on that stream, so the caching allocator hands their blocks to no other work
+    before the call's kernels on that stream have finished with them."""
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
 
 
 def _check(status):
@@ -235,7 +246,8 @@ def gdla_latent_append(dims, weights, x, pos, cache, ws=None, stream=None):
     """Writes cache rows [pos[b], pos[b] + T) from x [B, T, d_model]."""
     B, T = x.shape[0], x.shape[1]
     max_len = cache.shape[1]
-    ws, nbytes = _workspace(dims, GDLA_OP_APPEND, B, T, pos, max_len, ws, x.device)
+    with _on(stream):
+        ws, nbytes = _workspace(dims, GDLA_OP_APPEND, B, T, pos, max_len, ws, x.device)
     _check(lib().gdla_latent_append(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B, T,
                                     _pos_array(pos), _ptr(cache), max_len, _ptr(ws), nbytes,
                                     _stream(stream)))
@@ -246,9 +258,10 @@ def gdla_prefill(dims, weights, x, pos, cache, out=None, ws=None, lambda_overrid
     """x [B, T, d_model] at positions pos[b] + t; appends to cache; returns out [B, T, d_model]."""
     B, T = x.shape[0], x.shape[1]
     max_len = cache.shape[1]
-    if out is None:
-        out = torch.empty_like(x)
-    ws, nbytes = _workspace(dims, GDLA_OP_PREFILL, B, T, pos, max_len, ws, x.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(x)
+        ws, nbytes = _workspace(dims, GDLA_OP_PREFILL, B, T, pos, max_len, ws, x.device)
     dbg = _debug(lambda_override, out_heads, timer)
     _check(lib().gdla_prefill(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B, T,
                               _pos_array(pos), _ptr(cache), max_len, _ptr(out), _ptr(ws), nbytes,
@@ -261,9 +274,10 @@ def gdla_decode(dims, weights, x, pos, cache, out=None, ws=None, lambda_override
     """x [B, d_model], token b at position pos[b]; appends to cache; returns out [B, d_model]."""
     B = x.shape[0]
     max_len = cache.shape[1]
-    if out is None:
-        out = torch.empty_like(x)
-    ws, nbytes = _workspace(dims, GDLA_OP_DECODE, B, 1, pos, max_len, ws, x.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(x)
+        ws, nbytes = _workspace(dims, GDLA_OP_DECODE, B, 1, pos, max_len, ws, x.device)
     dbg = _debug(lambda_override, out_heads, timer)
     _check(lib().gdla_decode(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B,
                              _pos_array(pos), _ptr(cache), max_len, _ptr(out), _ptr(ws), nbytes,
@@ -277,9 +291,10 @@ def gdla_decode_tokens(dims, weights, x, pos, cache, out=None, ws=None, lambda_o
     appends to cache; returns out [B, T, d_model] (absorbed decode path)."""
     B, T = x.shape[0], x.shape[1]
     max_len = cache.shape[1]
-    if out is None:
-        out = torch.empty_like(x)
-    ws, nbytes = _workspace(dims, GDLA_OP_DECODE, B, T, pos, max_len, ws, x.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(x)
+        ws, nbytes = _workspace(dims, GDLA_OP_DECODE, B, T, pos, max_len, ws, x.device)
     dbg = _debug(lambda_override, out_heads, timer)
     _check(lib().gdla_decode_tokens(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B, T,
                                     _pos_array(pos), _ptr(cache), max_len, _ptr(out), _ptr(ws),
@@ -296,9 +311,10 @@ def gdla_prefill_packed(dims, weights, x, pos, doc_start, cache, out=None, ws=No
     max_len = cache.shape[1]
     assert doc_start.dtype == torch.int32 and tuple(doc_start.shape) == (B, T)
     doc_start = doc_start.contiguous()
-    if out is None:
-        out = torch.empty_like(x)
-    ws, nbytes = _workspace(dims, GDLA_OP_PREFILL, B, T, pos, max_len, ws, x.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(x)
+        ws, nbytes = _workspace(dims, GDLA_OP_PREFILL, B, T, pos, max_len, ws, x.device)
     dbg = _debug(lambda_override, out_heads, timer)
     _check(lib().gdla_prefill_packed(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B, T,
                                      _pos_array(pos), _ptr(doc_start), _ptr(cache), max_len,
@@ -325,7 +341,8 @@ class PagedCache:
 def gdla_latent_append_paged(dims, weights, x, pos, cache, ws=None, stream=None):
     """gdla_latent_append into a PagedCache."""
     B, T = x.shape[0], x.shape[1]
-    ws, nbytes = _workspace(dims, GDLA_OP_APPEND, B, T, pos, cache.max_len, ws, x.device)
+    with _on(stream):
+        ws, nbytes = _workspace(dims, GDLA_OP_APPEND, B, T, pos, cache.max_len, ws, x.device)
     _check(lib().gdla_latent_append_paged(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B, T,
                                           _pos_array(pos), ctypes.byref(cache.struct), _ptr(ws),
                                           nbytes, _stream(stream)))
@@ -335,9 +352,10 @@ def gdla_prefill_paged(dims, weights, x, pos, cache, out=None, ws=None, lambda_o
                        out_heads=None, stream=None, timer=None):
     """gdla_prefill over a PagedCache: x [B, T, d_model] -> out [B, T, d_model]."""
     B, T = x.shape[0], x.shape[1]
-    if out is None:
-        out = torch.empty_like(x)
-    ws, nbytes = _workspace(dims, GDLA_OP_PREFILL_PAGED, B, T, pos, cache.max_len, ws, x.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(x)
+        ws, nbytes = _workspace(dims, GDLA_OP_PREFILL_PAGED, B, T, pos, cache.max_len, ws, x.device)
     dbg = _debug(lambda_override, out_heads, timer)
     _check(lib().gdla_prefill_paged(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B, T,
                                     _pos_array(pos), ctypes.byref(cache.struct), _ptr(out),
@@ -350,9 +368,10 @@ def gdla_decode_paged(dims, weights, x, pos, cache, out=None, ws=None, lambda_ov
                       out_heads=None, stream=None, timer=None):
     """Multi-token decode over a PagedCache: x [B, T, d_model] -> out [B, T, d_model]."""
     B, T = x.shape[0], x.shape[1]
-    if out is None:
-        out = torch.empty_like(x)
-    ws, nbytes = _workspace(dims, GDLA_OP_DECODE, B, T, pos, cache.max_len, ws, x.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(x)
+        ws, nbytes = _workspace(dims, GDLA_OP_DECODE, B, T, pos, cache.max_len, ws, x.device)
     dbg = _debug(lambda_override, out_heads, timer)
     _check(lib().gdla_decode_paged(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B, T,
                                    _pos_array(pos), ctypes.byref(cache.struct), _ptr(out), _ptr(ws),
@@ -369,14 +388,15 @@ def gdla_backward(dims, weights, tensors, x, dout, doc_start=None, ws=None, lamb
     the gains that are set)."""
     B, T = x.shape[0], x.shape[1]
     dev = x.device
-    grads = {"dx": torch.empty((B, T, x.shape[2]), dtype=torch.float32, device=dev)}
-    for name in ("w_qa", "w_qc", "w_qr", "w_dkv", "w_kr", "w_uk", "w_uv", "w_lambda", "w_gate", "w_o"):
-        grads["d" + name] = torch.empty(tuple(tensors[name].shape), dtype=torch.float32, device=dev)
-    for name in ("gamma_q", "gamma_kv"):
-        if tensors.get(name) is not None:
+    with _on(stream):
+        grads = {"dx": torch.empty((B, T, x.shape[2]), dtype=torch.float32, device=dev)}
+        for name in ("w_qa", "w_qc", "w_qr", "w_dkv", "w_kr", "w_uk", "w_uv", "w_lambda", "w_gate", "w_o"):
             grads["d" + name] = torch.empty(tuple(tensors[name].shape), dtype=torch.float32, device=dev)
+        for name in ("gamma_q", "gamma_kv"):
+            if tensors.get(name) is not None:
+                grads["d" + name] = torch.empty(tuple(tensors[name].shape), dtype=torch.float32, device=dev)
+        ws, nbytes = _workspace(dims, GDLA_OP_BACKWARD, B, T, None, T, ws, dev)
     gs = GdlaGrads(*[None if grads.get(n) is None else grads[n].data_ptr() for n in GRAD_FIELDS])
-    ws, nbytes = _workspace(dims, GDLA_OP_BACKWARD, B, T, None, T, ws, dev)
     if doc_start is not None:
         assert doc_start.dtype == torch.int32 and tuple(doc_start.shape) == (B, T)
         doc_start = doc_start.contiguous()
