@@ -97,23 +97,23 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ f32x4 mfma16h(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ _Float16 sat16(float v) { return (_Float16)fminf(fmaxf(v, -65504.f), 65504.f); }
-// 8 fp32 -> hi = fp16(v) (saturating), lo = fp16(v - hi): hi + lo carries about 21 bits of v
+// 8 fp32 -> hi = fp16(v), lo = fp16(v - hi): hi + lo carries about 21 bits of v.  Round to nearest
+// even: beyond fp16's range hi is +-inf and the product non-finite, and a NaN stays a NaN.
 __device__ __forceinline__ void split16(const float *v, f16x8 &hi, f16x8 &lo) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    hi[i] = sat16(v[i]);
+    hi[i] = (_Float16)v[i];
     lo[i] = (_Float16)(v[i] - (float)hi[i]);
   }
 }
-// 8 bf16 (16 bytes) -> fp16: exact in the fp16 normal range, saturating beyond it
+// 8 bf16 (16 bytes) -> fp16: exact in the fp16 normal range, +-inf beyond it, NaN kept
 __device__ __forceinline__ f16x8 bf16_to_f16x8(uint4 w) {
   const unsigned u[4] = {w.x, w.y, w.z, w.w};
   f16x8 r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    r[2 * i] = (_Float16)fminf(fmaxf(__uint_as_float(u[i] << 16), -65504.f), 65504.f);
-    r[2 * i + 1] = (_Float16)fminf(fmaxf(__uint_as_float(u[i] & 0xffff0000u), -65504.f), 65504.f);
+    r[2 * i] = (_Float16)(__uint_as_float(u[i] << 16));
+    r[2 * i + 1] = (_Float16)(__uint_as_float(u[i] & 0xffff0000u));
   }
   return r;
 }

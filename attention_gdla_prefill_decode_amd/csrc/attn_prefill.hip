@@ -37,6 +37,7 @@ namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int DH = 128, DR = 64, DQK = DH + DR;
@@ -96,8 +97,6 @@ __device__ __forceinline__ uint32_t lds_u32(const void *p) {
 __device__ __forceinline__ f32x16 mfma(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
-
-__device__ __forceinline__ f16_t to_f16(float v) { return (f16_t)fminf(fmaxf(v, -65504.f), 65504.f); }
 
 // (own, partner) exchange between lanes l and l ^ 32
 __device__ __forceinline__ float pair_max(float v) {
@@ -379,17 +378,17 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
         const float o2 = O[db][4 * i + 2] * inv, o3 = O[db][4 * i + 3] * inv;
         if (oh) *(float4 *)(oh + dim) = make_float4(o0, o1, o2, o3);
         f16x4 yv;
-        yv[0] = to_f16((o0 - lam * nv.x) * sg[0]);
-        yv[1] = to_f16((o1 - lam * nv.y) * sg[1]);
-        yv[2] = to_f16((o2 - lam * nv.z) * sg[2]);
-        yv[3] = to_f16((o3 - lam * nv.w) * sg[3]);
+        yv[0] = (f16_t)((o0 - lam * nv.x) * sg[0]);
+        yv[1] = (f16_t)((o1 - lam * nv.y) * sg[1]);
+        yv[2] = (f16_t)((o2 - lam * nv.z) * sg[2]);
+        yv[3] = (f16_t)((o3 - lam * nv.w) * sg[3]);
         *(f16x4 *)(y + dim) = yv;
       }
   }
 }
 
 // k^R of keys lo_b .. lo_b + nk_b - 1, converted from the bf16 cache to fp16 (exact in the fp16
-// normal range, saturating beyond it), into columns 128 .. 191 of every KV head's key rows.
+// normal range, +-inf beyond it, NaN kept), into columns 128 .. 191 of every KV head's key rows.
 __global__ void __launch_bounds__(256) kr_fill_kernel(const bf16_t *cache, f16_t *kx, const int32_t *pos,
                                                       int32_t T, int32_t window, int32_t max_len,
                                                       int32_t row, int32_t d_c, int32_t n_kv, int32_t lcap) {
@@ -402,7 +401,7 @@ __global__ void __launch_bounds__(256) kr_fill_kernel(const bf16_t *cache, f16_t
   const int r = i / (DR / 8), ch = i % (DR / 8);
   const uint4 v = *(const uint4 *)(cache + ((int64_t)b * max_len + lo + r) * row + d_c + ch * 8);
   auto cv = [](unsigned w) {
-    const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+    const f16x2 h = {(f16_t)__uint_as_float(w << 16), (f16_t)__uint_as_float(w & 0xffff0000u)};
     return __builtin_bit_cast(unsigned, h);
   };
   const uint4 o = make_uint4(cv(v.x), cv(v.y), cv(v.z), cv(v.w));

@@ -24,6 +24,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 namespace gdla {
 namespace {
 
@@ -590,13 +592,14 @@ hipError_t launch_backward_generic(const BackwardArgs &a, const LayerDims &d, DT
 namespace gdla {
 namespace {
 
-__device__ __forceinline__ f16_t f16s(float v) { return (f16_t)fminf(fmaxf(v, -65504.f), 65504.f); }
+__device__ __forceinline__ f16_t f16s(float v) { return (f16_t)(v); }
 
 // dst[r, col_off + c] = fp16(src[r, c])  (r < rows, c < cols)
 template <typename TS>
 __global__ void __launch_bounds__(256) pack_f16_kernel(const TS *src, int64_t lds, int32_t rows, int32_t cols,
-                                                       f16_t *dst, int64_t ldd, int32_t col_off) {
+                                                       f16_t *dst, int64_t ldd, int32_t col_off, const float *scale) {
   typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+  const float sc = scale ? scale[0] : 1.0f;
   // runs of 4 columns when every run is aligned on both sides (the usual case), else one by one
   const bool quads = cols % 4 == 0 && lds % 4 == 0 && ldd % 4 == 0 && col_off % 4 == 0 &&
                      ((uintptr_t)src & (4 * sizeof(TS) - 1)) == 0 && ((uintptr_t)dst & 7) == 0;
@@ -609,7 +612,7 @@ __global__ void __launch_bounds__(256) pack_f16_kernel(const TS *src, int64_t ld
       const TS *p = src + r * lds + c;
       h4 v;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) v[k] = f16s((float)p[k]);
+      for (int k = 0; k < 4; ++k) v[k] = f16s((float)p[k] * sc);
       *(h4 *)(dst + r * ldd + col_off + c) = v;
     }
     return;
@@ -618,7 +621,7 @@ __global__ void __launch_bounds__(256) pack_f16_kernel(const TS *src, int64_t ld
   for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
     const int64_t r = i / cols;
     const int c = (int)(i % cols);
-    dst[r * ldd + col_off + c] = f16s((float)src[r * lds + c]);
+    dst[r * ldd + col_off + c] = f16s((float)src[r * lds + c] * sc);
   }
 }
 
@@ -627,8 +630,9 @@ __global__ void __launch_bounds__(256) pack_f16_kernel(const TS *src, int64_t ld
 // matrix) and 16-byte column runs of the destination.
 template <typename TS>
 __global__ void __launch_bounds__(256) tpack_f16_kernel(const TS *src, int64_t lds, int32_t R, int32_t C, int32_t R_pad,
-                                                        f16_t *dst, int64_t ldd, int32_t row_off) {
+                                                        f16_t *dst, int64_t ldd, int32_t row_off, const float *scale) {
   typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  const float sc = scale ? scale[0] : 1.0f;
   __shared__ __attribute__((aligned(16))) f16_t tile[64][72];  // row pitch 144 bytes
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   for (int i = threadIdx.x; i < 64 * 8; i += 256) {
@@ -640,10 +644,10 @@ __global__ void __launch_bounds__(256) tpack_f16_kernel(const TS *src, int64_t l
       const uint4 raw = *(const uint4 *)p;
       const TS *e = (const TS *)&raw;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = f16s((float)e[k]);
+      for (int k = 0; k < 8; ++k) v[k] = f16s((float)e[k] * sc);
     } else {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = (r < R && c + k < C) ? f16s((float)p[k]) : (f16_t)0.f;
+      for (int k = 0; k < 8; ++k) v[k] = (r < R && c + k < C) ? f16s((float)p[k] * sc) : (f16_t)0.f;
     }
     *(h8 *)&tile[rr][c8] = v;
   }
@@ -724,6 +728,54 @@ __global__ void __launch_bounds__(64) rms_bwd_kernel(const float *v, const T *ga
 }
 
 // dst[r, c] = 0 for r < rows, c0 <= c < c1 (the K padding of a concatenated operand)
+// Gradient scaling of the fp16 path.  The backward is linear in dout, so dout may enter the fp16
+// operands multiplied by any power of two s and every fp32 gradient divided by s at the end, with
+// no rounding of its own.  s puts the largest |dout| in [4, 8), where gradients of every size the
+// layer produces stay inside fp16's normal range (an upstream gradient of 1e-6 would otherwise sit
+// among fp16's subnormals after the first product, and a very large one overflow).
+// Block maxima of |dout| (fmaxf skips a NaN, which then reaches the gradients through the data).
+__global__ void __launch_bounds__(256) absmax_part_kernel(const bf16_t *v, int64_t n, float *part) {
+  __shared__ float red[4];
+  float m = 0.f;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    m = fmaxf(m, fabsf((float)v[i]));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) part[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+// sc[0] = s = 2^(3 - e) for the largest |dout| = f 2^e (f in [0.5, 1)), sc[1] = 1 / s; s = 1 when
+// dout is all zeros (or not finite).  The exponent is clamped so both stay normal fp32 numbers.
+__global__ void __launch_bounds__(256) grad_scale_kernel(const float *part, int32_t n, float *sc) {
+  __shared__ float red[4];
+  float m = 0.f;
+  for (int i = threadIdx.x; i < n; i += 256) m = fmaxf(m, part[i]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    int e = 0;
+    if (m > 0.f && m <= 3.0e38f) frexpf(m, &e);
+    const int k = min(max(3 - e, -100), 100);
+    sc[0] = ldexpf(1.0f, k);
+    sc[1] = ldexpf(1.0f, -k);
+  }
+}
+// Every fp32 gradient of the call times 1 / s (exact: a power of two).
+struct GradList {
+  float *p[16];
+  int64_t n[16];
+};
+__global__ void __launch_bounds__(256) unscale_grads_kernel(GradList g, const float *sc) {
+  float *p = g.p[blockIdx.y];
+  const int64_t n = g.n[blockIdx.y];
+  const float inv = sc[1];
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] *= inv;
+}
+
 __global__ void __launch_bounds__(256) zero_cols_kernel(f16_t *dst, int64_t ldd, int32_t rows, int32_t c0, int32_t c1) {
   const int w = c1 - c0;
   const int64_t n = (int64_t)rows * w;
@@ -810,16 +862,17 @@ __global__ void __launch_bounds__(256) qlo_kernel(const int32_t *doc, int32_t *l
 }
 
 template <typename TS>
-hipError_t pack(const TS *src, int64_t lds, int rows, int cols, f16_t *dst, int64_t ldd, int col_off, hipStream_t s) {
+hipError_t pack(const TS *src, int64_t lds, int rows, int cols, f16_t *dst, int64_t ldd, int col_off, hipStream_t s,
+                const float *scale = nullptr) {
   hipLaunchKernelGGL(pack_f16_kernel<TS>, dim3(grid_for((int64_t)rows * cols)), dim3(256), 0, s, src, lds, rows, cols,
-                     dst, ldd, col_off);
+                     dst, ldd, col_off, scale);
   return hipGetLastError();
 }
 template <typename TS>
 hipError_t tpack(const TS *src, int64_t lds, int R, int C, int R_pad, f16_t *dst, int64_t ldd, int row_off,
-                 hipStream_t s) {
+                 hipStream_t s, const float *scale = nullptr) {
   hipLaunchKernelGGL(tpack_f16_kernel<TS>, dim3((C + 63) / 64, (R_pad + 63) / 64), dim3(256), 0, s, src, lds, R, C,
-                     R_pad, dst, ldd, row_off);
+                     R_pad, dst, ldd, row_off, scale);
   return hipGetLastError();
 }
 
@@ -880,11 +933,19 @@ hipError_t launch_backward_fast(const FastBwdArgs &a, const LayerDims &d, hipStr
     BWD_TRY(hipGetLastError());
   }
 
+  // ---- gradient scale s from the largest |dout| (see grad_scale_kernel); dout enters as s dout
+  const float *gsc = b.gscale + kGradScaleBlocks;
+  hipLaunchKernelGGL(absmax_part_kernel, dim3(kGradScaleBlocks), dim3(256), 0, s, (const bf16_t *)a.dout,
+                     (int64_t)M * dm, b.gscale);
+  BWD_TRY(hipGetLastError());
+  hipLaunchKernelGGL(grad_scale_kernel, dim3(1), dim3(256), 0, s, b.gscale, kGradScaleBlocks, b.gscale + kGradScaleBlocks);
+  BWD_TRY(hipGetLastError());
+
   // ---- Eq.(10): dY = dout W_O^T; dW_O = Y^T dout
-  BWD_TRY(pack((const bf16_t *)a.dout, dm, M, dm, b.dout16, dm, 0, s));
+  BWD_TRY(pack((const bf16_t *)a.dout, dm, M, dm, b.dout16, dm, 0, s, gsc));
   BWD_TRY(nt(b.dout16, dm, b.wo16, dm, b.dy, ny, M, ny, dm, s, b.splitk));
   BWD_TRY(tpack(a.y16, ny, M, ny, Mp, b.ta, Mp, 0, s));
-  BWD_TRY(tpack((const bf16_t *)a.dout, dm, M, dm, Mp, b.tb, Mp, 0, s));
+  BWD_TRY(tpack((const bf16_t *)a.dout, dm, M, dm, Mp, b.tb, Mp, 0, s, gsc));
   BWD_TRY(nt(b.ta, Mp, b.tb, Mp, G.dw_o, dm, ny, dm, Mp, s, b.splitk));
   // gate and differential combine: dG, dH (fp16), noise-head dH, dlambda and the row sums, per row
   hipLaunchKernelGGL(combine_row_kernel, dim3(M), dim3(256), 0, s, a.heads, a.lam, a.sg16, b.dy, b.dh16, b.a6,
@@ -958,6 +1019,33 @@ hipError_t launch_backward_fast(const FastBwdArgs &a, const LayerDims &d, hipStr
   } else {  // too few columns for the MFMA GEMM's 16-byte stores
     BWD_TRY(gg((const bf16_t *)a.x, dm, true, b.dlaml, nS, false, G.dw_lambda, nS, dm, nS, M, false, s));
   }
+
+  // ---- every gradient back to dout's scale
+  GradList gl{};
+  int ng = 0;
+  int64_t most = 0;
+  auto add = [&](float *p, int64_t n) {
+    if (!p || n <= 0) return;
+    gl.p[ng] = p;
+    gl.n[ng++] = n;
+    most = std::max(most, n);
+  };
+  add(G.dx, (int64_t)M * dm);
+  add(G.dw_qa, (int64_t)dm * dcq);
+  add(G.dw_qc, (int64_t)dcq * nH * dh);
+  add(G.dw_qr, (int64_t)dcq * nH * dr);
+  add(G.dw_dkv, (int64_t)dm * dc);
+  add(G.dw_kr, (int64_t)dm * dr);
+  add(G.dw_uk, (int64_t)dc * nKV * dh);
+  add(G.dw_uv, (int64_t)dc * nKV * dh);
+  add(G.dw_lambda, (int64_t)dm * nS);
+  add(G.dw_gate, (int64_t)dcq * ny);
+  add(G.dw_o, (int64_t)ny * dm);
+  add(G.dgamma_q, dcq);
+  add(G.dgamma_kv, dc);
+  hipLaunchKernelGGL(unscale_grads_kernel, dim3((unsigned)std::min<int64_t>((most + 255) / 256, 1024), ng), dim3(256),
+                     0, s, gl, gsc);
+  BWD_TRY(hipGetLastError());
   return hipSuccess;
 }
 

@@ -37,7 +37,7 @@ __device__ __forceinline__ f32x16 mfma(f16x8 a, f16x8 b, f32x16 c) {
 __device__ __forceinline__ f16x4 tr4(const f16_t *p) {
   return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p));
 }
-__device__ __forceinline__ f16_t h16(float v) { return (f16_t)fminf(fmaxf(v, -65504.f), 65504.f); }
+__device__ __forceinline__ f16_t h16(float v) { return (f16_t)(v); }
 
 // A fragment of a transposed row-major tile (rows r, columns c, pitch `pitch` elements): lane l
 // gets column c0 + l % 32 at the 8 rows r0 + 8 (i / 4) + 4 (l / 32) + i % 4, i = 0..7 (the row

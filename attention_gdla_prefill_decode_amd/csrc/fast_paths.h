@@ -139,12 +139,14 @@ hipError_t launch_bwd_attention(const BwdAttnArgs &a, hipStream_t s);
 // Partials of the split-K products of the fused backward (at most this many bytes per product).
 constexpr size_t kSplitKBytes = (size_t)128 << 20;
 
+constexpr int kGradScaleBlocks = 512;  // blocks of the |dout| maximum
 struct FastBwdBuffers {
   f16_t *wo16, *w3, *w6, *w8;   // fp16 weights, K-concatenated: [n_S d_h, d], [d_c, k3], [d_cq, k6], [d, k8]
   f16_t *dout16;                // [M, d]
   float *dy;                    // [M, n_S d_h]
   f16_t *ta, *tb;               // transposed operands [rows, M_pad]
-  float *dheads, *dd, *dlaml, *drow;  // dheads, dd unused (combine_row_kernel writes dH in fp16)
+  float *dheads, *gscale, *dlaml, *drow;  // dheads unused (combine_row_kernel writes dH in fp16);
+                                         // gscale: kGradScaleBlocks maxima of |dout|, then (s, 1/s)
   f16_t *dh16;                  // [M, n_H, d_h]
   float *dq, *dk, *dv;          // attention gradients (dq unused: the dq kernel packs into a6)
   f16_t *a6, *a3, *a8;          // gradient operands [M, k6], [M, k3], [M, k8]

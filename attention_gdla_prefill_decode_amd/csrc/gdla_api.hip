@@ -144,6 +144,7 @@ PrefillLayout plan_prefill(const LayerDims &d, gdla_dtype dt, int32_t B, int32_t
 
 struct DecodeLayout {
   size_t pos, aq, ckv, krp, laml, cq, lam, qc, qrp, qr, gate, qabs, o, heads, y, skinny, total;
+  size_t cq_lo, y_lo;   // bf16 rounding remainders of c^Q and Y (skinny projections), or 0 bytes
   size_t skinny_bytes;  // split-K partial sums of the skinny projection GEMMs (0: not used)
   FastDecodeLayout fast;
   bool use_fast;
@@ -171,6 +172,10 @@ DecodeLayout plan_decode(const LayerDims &d, gdla_dtype dt, int32_t B, int32_t T
   L.y = p.add(es * M * d.n_signal * d.d_h);
   L.skinny_bytes = (dt == GDLA_BF16 && M <= 256) ? skinny_gemm_partial_bound((int32_t)M) : 0;
   L.skinny = p.add(L.skinny_bytes);
+  // c^Q and Y enter the skinny projections as bf16 + bf16 remainder (about 16 bits)
+  const bool two_part = L.skinny_bytes > 0;
+  L.cq_lo = p.add(two_part ? 2 * M * d.d_cq : 0);
+  L.y_lo = p.add(two_part ? 2 * M * d.n_signal * d.d_h : 0);
   if (L.use_fast) {
     L.fast = plan_fast_decode(d, (int32_t)M, max_len, [&](size_t n) { return p.add(n); });
   } else {
@@ -282,7 +287,7 @@ FastBackwardLayout plan_backward_fast(const LayerDims &d, int32_t B, int32_t T) 
       2 * nS * dh * dm, 2 * d.d_c * k3, 2 * d.d_cq * k6, 2 * dm * k8,      // wo16 w3 w6 w8
       2 * M * dm, 4 * M * nS * dh,                                          // dout16 dy
       2 * trows_a * Mp, 2 * trows_b * Mp,                                   // ta tb
-      0, 0, 4 * M * nS, 4 * (M * nH + 32),                                  // (dheads dd: unused) dlaml drow
+      0, 4 * (kGradScaleBlocks + 2), 4 * M * nS, 4 * (M * nH + 32),         // (dheads: unused) gscale dlaml drow
       2 * M * nH * dh,                                                      // dh16
       0, 4 * M * nKV * (dh + dr), 4 * M * nKV * dh,                         // dq (packed by the kernel) dk dv
       2 * M * k6, 2 * M * k3, 2 * M * k8,                                   // a6 a3 a8
@@ -371,7 +376,7 @@ gdla_status project_and_append(const LayerDims &d, DT dt, const gdla_weights *w,
                                float *aq, float *ckv, float *krp, float *laml,
                                void *cq, float *lam, const float *lam_override, hipStream_t s,
                                StageEvents &se, bool cq_f16 = false, const NtWeights *nt = nullptr,
-                               void *partial = nullptr, size_t partial_bytes = 0) {
+                               void *partial = nullptr, size_t partial_bytes = 0, void *cq_lo = nullptr) {
   GemmBatch g{};
   // with nt, B is the transposed weight [N, K] (row stride K = d_model)
   auto wb = [&](const void *w_, const void *wt) { return nt ? wt : w_; };
@@ -404,7 +409,7 @@ gdla_status project_and_append(const LayerDims &d, DT dt, const gdla_weights *w,
   PrepArgs a{};
   a.aq = aq; a.ckv = ckv; a.kr = krp; a.lam_logit = laml; a.lam_override = lam_override;
   a.gamma_q = w->gamma_q; a.gamma_kv = w->gamma_kv; a.cq = cq; a.lam = lam; a.cache = cache;
-  a.pos = pos_dev; a.M = M; a.T = T; a.cq_f16 = cq_f16 ? 1 : 0;
+  a.pos = pos_dev; a.M = M; a.T = T; a.cq_f16 = cq_f16 ? 1 : 0; a.cq_lo = cq_lo;
   se.begin(GDLA_STAGE_NORM_APPEND);
   HIP_TRY(launch_prep(a, d, dt, s));
   se.end(GDLA_STAGE_NORM_APPEND);
@@ -752,10 +757,12 @@ gdla_status decode_impl(const gdla_dims *dims, const gdla_weights *w, const void
   int32_t *pos_dev = at<int32_t>(ws, L.pos);
   HIP_TRY(launch_set_i32(pos_dev, pos_host, B, stream));
   void *partial = at<void>(ws, L.skinny);
+  void *cq_lo = L.skinny_bytes > 0 ? at<void>(ws, L.cq_lo) : nullptr;
+  void *y_lo = L.skinny_bytes > 0 ? at<void>(ws, L.y_lo) : nullptr;
   st = project_and_append(d, dt, w, x, M, T, pos_dev, cache, at<float>(ws, L.aq),
                           at<float>(ws, L.ckv), at<float>(ws, L.krp), at<float>(ws, L.laml),
                           at<void>(ws, L.cq), at<float>(ws, L.lam), lam_override, stream, se, false, nullptr,
-                          partial, L.skinny_bytes);
+                          partial, L.skinny_bytes, cq_lo);
   if (st != GDLA_OK) return st;
   // Eq.(2), (9) in fp32 (decode keeps the query in fp32 until it is mapped into the latent).
   se.begin(GDLA_STAGE_PROJ_Q);
@@ -766,6 +773,7 @@ gdla_status decode_impl(const gdla_dims *dims, const gdla_weights *w, const void
                   (int64_t)d.n_heads * d.d_r, M, d.n_heads * d.d_r, d.d_cq, true);
   g.p[g.n++] = gp(at<void>(ws, L.cq), d.d_cq, w->w_gate, (int64_t)d.n_signal * d.d_h, at<float>(ws, L.gate),
                   (int64_t)d.n_signal * d.d_h, M, d.n_signal * d.d_h, d.d_cq, true);
+  for (int i = 0; i < g.n; ++i) g.p[i].A_lo = cq_lo;
   HIP_TRY(launch_gemm_rows(g, dt, partial, L.skinny_bytes, stream));
   HIP_TRY(launch_rope_heads(at<float>(ws, L.qrp), at<float>(ws, L.qr), (int64_t)d.n_heads * d.d_r, d.d_r, 0,
                             M, T, d.n_heads, d.d_r, pos_dev, d.theta, DT::F32, stream));
@@ -789,11 +797,12 @@ gdla_status decode_impl(const gdla_dims *dims, const gdla_weights *w, const void
     HIP_TRY(launch_copy_rows_f32(at<float>(ws, L.heads), (int64_t)d.n_heads * d.d_h, out_heads,
                                  (int64_t)d.n_heads * d.d_h, M, d.n_heads * d.d_h, stream));
   HIP_TRY(launch_combine(at<float>(ws, L.heads), at<float>(ws, L.lam), at<float>(ws, L.gate),
-                         at<void>(ws, L.y), M, d, dt, stream));
+                         at<void>(ws, L.y), M, d, dt, stream, y_lo));
   se.end(GDLA_STAGE_ATTN_SIGNAL);
   g = GemmBatch{};
   g.p[g.n++] = gp(at<void>(ws, L.y), (int64_t)d.n_signal * d.d_h, w->w_o, d.d_model, out, d.d_model, M,
                   d.d_model, d.n_signal * d.d_h, false);
+  g.p[0].A_lo = y_lo;
   se.begin(GDLA_STAGE_PROJ_OUT);
   HIP_TRY(launch_gemm_rows(g, dt, partial, L.skinny_bytes, stream));
   se.end(GDLA_STAGE_PROJ_OUT);

@@ -45,6 +45,10 @@ struct GemmProblem {
   // a second kernel sums the slices in order into C (deterministic).
   int32_t ksplit;
   float *part;
+  // Skinny GEMM only: the bf16 rounding remainder of A (same layout and lda), or null.  A + A_lo
+  // carries about 16 significant bits of an fp32 activation; the kernel adds A_lo B to the
+  // product.  The other kernels ignore it.
+  const void *A_lo;
 };
 
 enum { EPI_NONE = 0, EPI_SIGMOID = 1, EPI_ROPE = 2 };
@@ -129,6 +133,7 @@ struct PrepArgs {
   const float *lam_override;
   const void *gamma_q, *gamma_kv;
   void *cq;               // [M, d_cq] in the input dtype, or fp16 when cq_f16
+  void *cq_lo;            // bf16 layers: [M, d_cq] bf16 remainder cq_exact - cq, or null
   float *lam;             // [M, n_S]
   CacheRef cache;
   const int32_t *pos;     // [B] device
@@ -159,7 +164,7 @@ hipError_t launch_attention_generic(const AttnGenericArgs &a, const LayerDims &d
 // Eq.(8)-(10) before W_o: y[m, i, e] = sigmoid(g[m, i, e]) * (H[m, i, e] - lam[m, i] *
 // H[m, n_S + i mod n_N, e]) in the input dtype.
 hipError_t launch_combine(const float *heads, const float *lam, const float *gate, void *y,
-                          int32_t M, const LayerDims &d, DT dt, hipStream_t s);
+                          int32_t M, const LayerDims &d, DT dt, hipStream_t s, void *y_lo = nullptr);
 
 // Absorbed decode.  The absorb / un-absorb steps work on any number of query row sets; the
 // attention step takes q_len tokens per sequence, row set v = b q_len + i at position pos[b] + i.

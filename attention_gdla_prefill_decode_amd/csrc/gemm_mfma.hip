@@ -1,7 +1,7 @@
 // Grouped GEMM on gfx950 matrix cores: C = A[M, K] B[K, N], fp32 accumulation.  Two operand
 // modes: bf16 x bf16, or fp16 A x bf16 B, where B is converted to fp16 while it is staged (bf16
-// values convert exactly unless they fall outside the fp16 range, where the conversion rounds
-// toward zero, i.e. saturates).  Outputs are fp32, bf16 or fp16.
+// values convert exactly unless they fall outside the fp16 range, where they become +-inf; NaN
+// stays NaN).  Outputs are fp32, bf16 or fp16 (round to nearest even, +-inf beyond fp16's range).
 //
 // Used for every projection of the GDLA layer (Motif 3 Technical Report, picx.dev summary,
 // section 2.2: x W^Q_a, x W^KV_a, x W^lambda in Eq.(1), (3), (7); c^Q W^Q_b, c^Q W^G in Eq.(2),
@@ -51,10 +51,11 @@ __device__ __forceinline__ f32x16 mfma(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-// 8 bf16 -> 8 fp16 (exact in the fp16 normal range; v_cvt_pkrtz saturates beyond it).
+// 8 bf16 -> 8 fp16 (exact in the fp16 normal range, +-inf beyond it, NaN kept).
 __device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 v) {
   auto cv = [](unsigned w) {
-    const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 h = {(_Float16)__uint_as_float(w << 16), (_Float16)__uint_as_float(w & 0xffff0000u)};
     return __builtin_bit_cast(unsigned, h);
   };
   return make_uint4(cv(v.x), cv(v.y), cv(v.z), cv(v.w));
@@ -168,7 +169,7 @@ __global__ void __launch_bounds__(256, 4) gemm_mfma_kernel(GemmBatch batch) {
           if (m >= P.M) continue;
           f16x4 v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (f16_t)fminf(fmaxf(acc[r][c][4 * q + e], -65504.f), 65504.f);
+          for (int e = 0; e < 4; ++e) v[e] = (f16_t)(acc[r][c][4 * q + e]);
           if (m + 3 < P.M) {
             *(f16x4 *)(base + vt_slot(m)) = v;
           } else {
@@ -189,7 +190,7 @@ __global__ void __launch_bounds__(256, 4) gemm_mfma_kernel(GemmBatch batch) {
         const int64_t off = (int64_t)m * P.ldc + coff;
         if (P.c_dt == CD_F32) ((float *)P.C)[off] = v;
         else if (P.c_dt == CD_F16 || (P.c_dt == CD_IN && CONVERT_B))
-          ((f16_t *)P.C)[off] = (f16_t)fminf(fmaxf(v, -65504.f), 65504.f);
+          ((f16_t *)P.C)[off] = (f16_t)(v);
         else ((bf16_t *)P.C)[off] = (bf16_t)v;
       }
     }

@@ -112,8 +112,8 @@ __device__ __forceinline__ void staged_epilogue(const GemmProblem &P, const f32x
         *(float *)q = v0[j];
         *(float *)(q + 32 * ESZ) = v1[j];
       } else if constexpr (KIND == 1) {
-        *(f16_t *)q = (f16_t)fminf(fmaxf(v0[j], -65504.f), 65504.f);
-        *(f16_t *)(q + 32 * ESZ) = (f16_t)fminf(fmaxf(v1[j], -65504.f), 65504.f);
+        *(f16_t *)q = (f16_t)(v0[j]);
+        *(f16_t *)(q + 32 * ESZ) = (f16_t)(v1[j]);
       } else {
         *(bf16_t *)q = (bf16_t)v0[j];
         *(bf16_t *)(q + 32 * ESZ) = (bf16_t)v1[j];
@@ -260,7 +260,7 @@ __global__ void __launch_bounds__(512, 1) gemm_nt_kernel(GemmBatch batch) {
           if (m >= P.M) continue;
           f16x4 v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (f16_t)fminf(fmaxf(acc[mb][nb][4 * q + e], -65504.f), 65504.f);
+          for (int e = 0; e < 4; ++e) v[e] = (f16_t)(acc[mb][nb][4 * q + e]);
           if (m + 3 < P.M) {
             *(f16x4 *)(base + vt_slot(m)) = v;
           } else {
@@ -291,7 +291,7 @@ __global__ void __launch_bounds__(256) splitk_sum_kernel(const float *part, int3
 }
 
 // Wt[n][k] = W[k][n] for a [K, N] bf16 weight, converted to fp16 (exact in the fp16 normal range,
-// round-to-nearest below it, saturating above) or kept in bf16.  64 x 64 tiles through LDS with
+// round-to-nearest below it, +-inf above) or kept in bf16.  64 x 64 tiles through LDS with
 // 16-byte global loads and stores (K and N multiples of 8; the scalar kernel serves the rest).
 template <typename TO>
 __global__ void __launch_bounds__(256) transpose16_kernel(const bf16_t *W, TO *Wt, int32_t K, int32_t N) {
@@ -315,7 +315,7 @@ __global__ void __launch_bounds__(256) transpose16_kernel(const bf16_t *W, TO *W
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float v = (float)t[kc + e][rn];
-      if constexpr (__is_same(TO, f16_t)) o[e] = (f16_t)fminf(fmaxf(v, -65504.f), 65504.f);
+      if constexpr (__is_same(TO, f16_t)) o[e] = (f16_t)(v);
       else o[e] = (bf16_t)v;
     }
     *(uint4 *)(Wt + (int64_t)(n0 + rn) * K + k0 + kc) = *(const uint4 *)o;
@@ -336,7 +336,7 @@ __global__ void __launch_bounds__(256) transpose_kernel(const bf16_t *W, TO *Wt,
     const int n = n0 + r, k = k0 + tx;
     if (n < N && k < K) {
       const float v = t[tx][r];
-      if constexpr (__is_same(TO, f16_t)) Wt[(int64_t)n * K + k] = (f16_t)fminf(fmaxf(v, -65504.f), 65504.f);
+      if constexpr (__is_same(TO, f16_t)) Wt[(int64_t)n * K + k] = (f16_t)(v);
       else Wt[(int64_t)n * K + k] = (bf16_t)v;
     }
   }

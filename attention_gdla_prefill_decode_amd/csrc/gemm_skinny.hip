@@ -12,6 +12,9 @@
 // activation tile A[0:64, k0:+64] (8 KB each) by direct global -> LDS 16-byte loads into a 4-stage
 // ring (three k-steps in flight).  Wave w owns columns n0 + 16 w .. + 15 and all 64 rows:
 //   C^T[n, m] += B^T[n, k] . A^T[k, m]   with v_mfma_f32_16x16x32_bf16,
+// With a two-part activation (A_lo: the bf16 rounding remainder of an fp32 activation) the stage
+// also holds the A_lo tile, the ring has 3 stages (two in flight, 72 KB, still two workgroups per
+// CU) and every weight fragment meets both parts, so the product keeps about 16 bits of A.
 // the B^T fragments read by the transposing ds_read_b64_tr_b16 from the row-major weight tile,
 // the A^T fragments by 16-byte reads of activation rows.  Both tiles are XOR-swizzled so the reads
 // are free of bank conflicts.  Rows past M read row M - 1 (always inside A) and are not stored.
@@ -62,8 +65,12 @@ struct SkinnyArgs {
   int32_t col0[kMaxGemmProblems];  // column offset of each problem in the partial rows
 };
 
+template <bool SPLIT>
 __global__ void __launch_bounds__(256) gemm_skinny_kernel(const SkinnyArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t ring[NST * (TILE_B + TILE_A)];
+  constexpr int NS = SPLIT ? 3 : NST;                           // ring stages
+  constexpr int NL = SPLIT ? LOADS + 2 : LOADS;                 // 16-byte loads per lane and stage
+  constexpr int STAGE = TILE_B + (SPLIT ? 2 : 1) * TILE_A;      // elements per stage
+  __shared__ __attribute__((aligned(16))) bf16_t ring[NS * STAGE];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tile = (int)blockIdx.x / a.mblocks;
   int pi = 0;
@@ -77,14 +84,16 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(const SkinnyArgs a) {
   const int kbeg = (int)blockIdx.y * ks;
   const int nsteps = ks / SK;
   const bf16_t *Ab = (const bf16_t *)P.A;
+  const bf16_t *Al = (const bf16_t *)P.A_lo;
   const bf16_t *Bb = (const bf16_t *)P.B;
 
-  // this lane's source offsets (bytes) for its 4 loads of a stage: loads 0..7 of the workgroup
-  // fill weight rows 8 q .. 8 q + 7, loads 8..15 activation rows 8 (q - 8) ..; wave w issues
-  // loads w, w + 4, w + 8, w + 12
-  uint32_t soff[LOADS];
+  // this lane's source offsets (bytes) for its loads of a stage: loads 0..7 of the workgroup fill
+  // weight rows 8 q .. 8 q + 7, loads 8..15 activation rows 8 (q - 8) .., and (SPLIT) loads 16..23
+  // the same rows of A_lo; wave w issues loads w, w + 4, w + 8, ...  Load q lands at 1 KB q of the
+  // stage (weight tile, then A, then A_lo).
+  uint32_t soff[NL];
 #pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
+  for (int i = 0; i < NL; ++i) {
     const int q = wave + 4 * i;
     const int r = (q & 7) * 8 + (lane >> 3), cp = lane & 7;
     if (q < 8) {
@@ -97,12 +106,13 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(const SkinnyArgs a) {
   const uint32_t rbase = lds_u32(ring);
   auto issue = [&](int st) {
     const int k0 = kbeg + st * SK;
-    const uint32_t slot = rbase + (uint32_t)((st % NST) * (TILE_B + TILE_A) * 2);
+    const uint32_t slot = rbase + (uint32_t)((st % NS) * STAGE * 2);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
+    for (int i = 0; i < NL; ++i) {
       const int q = wave + 4 * i;
       if (q < 8) dma16(Bb + (int64_t)k0 * P.ldb + n0, soff[i], slot + q * 1024);
-      else dma16(Ab + k0, soff[i], slot + TILE_B * 2 + (q - 8) * 1024);
+      else if (q < 16) dma16(Ab + k0, soff[i], slot + q * 1024);
+      else dma16(Al + k0, soff[i], slot + q * 1024);
     }
   };
 
@@ -121,15 +131,15 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(const SkinnyArgs a) {
   }
 
   f32x4 acc[4] = {};
-  for (int st = 0; st < NST - 1 && st < nsteps; ++st) issue(st);
+  for (int st = 0; st < NS - 1 && st < nsteps; ++st) issue(st);
   for (int st = 0; st < nsteps; ++st) {
-    const int ahead = min(nsteps - 1 - st, NST - 2);
-    if (ahead >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LOADS) : "memory");
-    else if (ahead == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
+    const int ahead = min(nsteps - 1 - st, NS - 2);
+    if (ahead >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NL) : "memory");
+    else if (ahead == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NL) : "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // stage st has landed for every wave; every wave is done with stage st - 1
-    if (st + NST - 1 < nsteps) issue(st + NST - 1);
-    const char *sb = (const char *)(ring + (st % NST) * (TILE_B + TILE_A));
+    if (st + NS - 1 < nsteps) issue(st + NS - 1);
+    const char *sb = (const char *)(ring + (st % NS) * STAGE);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const bf16x4 lo = tr_read(sb + offW[kk]);
@@ -139,6 +149,10 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(const SkinnyArgs a) {
       for (int mb = 0; mb < 4; ++mb) {
         const bf16x8 af = *(const bf16x8 *)(sb + offA[kk][mb]);
         acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, af, acc[mb], 0, 0, 0);
+        if (SPLIT) {
+          const bf16x8 al = *(const bf16x8 *)(sb + offA[kk][mb] + TILE_A * 2);
+          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, al, acc[mb], 0, 0, 0);
+        }
       }
     }
   }
@@ -211,14 +225,15 @@ bool skinny_problem_ok(const GemmProblem &p) {
   return p.M >= 1 && p.M <= SM * MAX_MB && p.N % SN == 0 && p.K % SK == 0 && p.K >= SK && p.a_f16 == 0 &&
          p.epi == EPI_NONE && !p.c_trans && (p.c_dt == CD_F32 || p.c_dt == CD_IN) && p.lda % 8 == 0 &&
          p.ldb % 8 == 0 && p.ldc % 4 == 0 && ((uintptr_t)p.A & 15) == 0 && ((uintptr_t)p.B & 15) == 0 &&
-         ((uintptr_t)p.C & 15) == 0 && p.hw == p.N && p.hs == 0 && p.ho == 0 &&
+         ((uintptr_t)p.C & 15) == 0 && ((uintptr_t)p.A_lo & 15) == 0 && p.hw == p.N && p.hs == 0 && p.ho == 0 &&
          (int64_t)(p.M - 1) * p.lda + p.K < (int64_t)1 << 30 && (int64_t)63 * p.ldb + 64 < (int64_t)1 << 30;
 }
 
 bool skinny_gemm_ok(const GemmBatch &g) {
   if (g.n < 1) return false;
   for (int i = 0; i < g.n; ++i)
-    if (!skinny_problem_ok(g.p[i]) || g.p[i].M != g.p[0].M) return false;
+    if (!skinny_problem_ok(g.p[i]) || g.p[i].M != g.p[0].M || (g.p[i].A_lo == nullptr) != (g.p[0].A_lo == nullptr))
+      return false;
   return true;
 }
 
@@ -251,7 +266,10 @@ hipError_t launch_gemm_skinny(const GemmBatch &g, void *partial, size_t partial_
     if (!partial || partial_bytes < (size_t)a.splits * g.p[0].M * cols * 4) return hipErrorInvalidValue;
     a.partial = (float *)partial;
   }
-  hipLaunchKernelGGL(gemm_skinny_kernel, dim3(tiles * a.mblocks, a.splits, 1), dim3(256), 0, s, a);
+  if (g.p[0].A_lo)
+    hipLaunchKernelGGL(gemm_skinny_kernel<true>, dim3(tiles * a.mblocks, a.splits, 1), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(gemm_skinny_kernel<false>, dim3(tiles * a.mblocks, a.splits, 1), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   const int64_t quads = (int64_t)g.p[0].M * cols / 4;

@@ -22,9 +22,10 @@ template <> __device__ __forceinline__ void st<float>(float *p, int64_t i, float
 template <> __device__ __forceinline__ void st<bf16_t>(bf16_t *p, int64_t i, float v) {
   p[i] = (bf16_t)v;
 }
-// fp16 stores saturate to the finite range (+-65504) instead of producing infinities.
+// fp16 stores round to nearest even: a value beyond fp16's range becomes +-inf and a NaN stays a
+// NaN, so an out-of-range or corrupted input surfaces as a non-finite output.
 template <> __device__ __forceinline__ void st<f16_t>(f16_t *p, int64_t i, float v) {
-  p[i] = (f16_t)fminf(fmaxf(v, -65504.f), 65504.f);
+  p[i] = (f16_t)(v);
 }
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
@@ -148,8 +149,12 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs a, LayerDims d) {
     const float r = rsqrtf(block_sum256(ss, red) / d.d_cq + d.eps);
     for (int j = threadIdx.x; j < d.d_cq; j += 256) {
       const float v = row[j] * r * (gq ? ld<T>(gq, j) : 1.f);
-      if (a.cq_f16) st<f16_t>((f16_t *)a.cq, (int64_t)m * d.d_cq + j, v);
-      else st<T>((T *)a.cq, (int64_t)m * d.d_cq + j, v);
+      if (a.cq_f16) {
+        st<f16_t>((f16_t *)a.cq, (int64_t)m * d.d_cq + j, v);
+      } else {
+        st<T>((T *)a.cq, (int64_t)m * d.d_cq + j, v);
+        if (a.cq_lo) st<bf16_t>((bf16_t *)a.cq_lo, (int64_t)m * d.d_cq + j, v - (float)(bf16_t)v);
+      }
     }
   }
   T *crow = (T *)a.cache.base + cache_row(a.cache, b, p) * (d.d_c + d.d_r);
@@ -291,9 +296,11 @@ hipError_t launch_attention_generic(const AttnGenericArgs &a, const LayerDims &d
 }
 
 // ------------------------------------------------------------------------------------------
+// y_lo (bf16 layers, or null): the bf16 rounding remainder of each Y value, for the two-part
+// output projection.
 template <typename T>
 __global__ void __launch_bounds__(256) combine_kernel(const float *heads, const float *lam,
-                                                      const float *gate, T *y, int32_t M,
+                                                      const float *gate, T *y, bf16_t *y_lo, int32_t M,
                                                       LayerDims d) {
   const int64_t n = (int64_t)M * d.n_signal * d.d_h;
   for (int64_t idx = blockIdx.x * 256ll + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * 256) {
@@ -304,19 +311,22 @@ __global__ void __launch_bounds__(256) combine_kernel(const float *heads, const 
     const float hs = heads[(m * d.n_heads + i) * d.d_h + e];
     const float hn = heads[(m * d.n_heads + d.n_signal + i % d.n_noise) * d.d_h + e];
     const float dv = hs - lam[m * d.n_signal + i] * hn;
-    st<T>(y, idx, sigmoidf_(gate[idx]) * dv);
+    const float v = sigmoidf_(gate[idx]) * dv;
+    st<T>(y, idx, v);
+    if (y_lo) y_lo[idx] = (bf16_t)(v - (float)(bf16_t)v);
   }
 }
 
 hipError_t launch_combine(const float *heads, const float *lam, const float *gate, void *y,
-                          int32_t M, const LayerDims &d, DT dt, hipStream_t s) {
+                          int32_t M, const LayerDims &d, DT dt, hipStream_t s, void *y_lo) {
   const int64_t n = (int64_t)M * d.n_signal * d.d_h;
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)std::min<int64_t>((n + 255) / 256, 65536));
   if (dt == DT::F32)
-    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, heads, lam, gate, (float *)y, M, d);
+    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, heads, lam, gate, (float *)y, nullptr, M, d);
   else
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, dim3(256), 0, s, heads, lam, gate, (bf16_t *)y, M, d);
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, dim3(256), 0, s, heads, lam, gate, (bf16_t *)y,
+                       (bf16_t *)y_lo, M, d);
   return hipGetLastError();
 }
 

@@ -43,6 +43,13 @@
  *     buffer is written.  A HIP launch failure returns GDLA_ERR_HIP (work already queued on the
  *     stream by the same call may then have run).  No C++ exception crosses this interface.
  *   - gdla_last_error() returns a short description of the last failure on the calling thread.
+ *   - Numerical range of the bf16 layers: the fast paths feed the matrix cores fp16 operands
+ *     (c^Q, q^C/q^R, K^C/k^R, V, P, Y and, in the backward, the gradients), each rounded once to
+ *     nearest even.  An operand beyond fp16's range (|v| > 65504) becomes +-inf and a NaN stays a
+ *     NaN, so such inputs give non-finite outputs, never finite wrong ones; the library itself
+ *     checks no values.  c^Q and cbar are RMS-normalised, so the range binds only through the
+ *     weights' and gains' magnitudes, k^R (linear in x) and V.  A NaN in a key may also reach the
+ *     outputs of the earlier queries of its 64-key tile (a masked probability of 0 times NaN).
  */
 #ifndef GDLA_H_
 #define GDLA_H_
@@ -264,7 +271,8 @@ typedef struct {
  * through W_lambda).  Workspace: gdla_workspace_bytes(dims, GDLA_OP_BACKWARD, B, T, NULL, T).
  * bf16 layers with d_head 128, d_rope 64 and at least 256 rows take the fused path (fp16 MFMA
  * operands, fp32 accumulation: about 3e-3 relative error per gradient); the rest compute in
- * fp32.  Every gradient has a single writer (no atomics), so repeated calls give identical bits.
+ * fp32.  The fused path scales dout by a power of two computed on the device from its largest
+ * magnitude (and the gradients back), so upstream gradients of any scale keep fp16 precision.  Every gradient has a single writer (no atomics), so repeated calls give identical bits.
  * Errors as gdla_prefill, plus GDLA_ERR_INVALID_ARG for a NULL gradient pointer. */
 gdla_status gdla_backward(const gdla_dims *dims, const gdla_weights *w, const void *x, int32_t B,
                           int32_t T, const int32_t *doc_start, const void *dout,

@@ -483,3 +483,26 @@ def test_workspace_reuse_and_explicit_stream():
     o2 = gd.gdla_prefill(dims, dev["wstruct"], dev["x"], [0], dev["cache"].clone())
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
+
+
+def test_explicit_stream_without_workspace():
+    """stream= with neither ws= nor out=, called outside any stream context: the binding allocates
+    the workspace and the output on that stream, so memory freed when the call returns is not handed
+    to work queued meanwhile on the current stream while the call's kernels still run on the other."""
+    inp = synth.make_inputs(BF, "cpu", batch=1, seq=300, p0=0, seed=61)
+    dev = H.device_inputs(inp)
+    dims = gd.make_dims(BF)
+    ref = gd.gdla_prefill(dims, dev["wstruct"], dev["x"], [0], dev["cache"].clone())
+    need = gd.gdla_workspace_bytes(dims, gd.GDLA_OP_PREFILL, 1, 300, [0], dev["cache"].shape[1])
+    cache = dev["cache"].clone()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        torch.cuda._sleep(20_000_000)  # keep the side stream busy so its kernels run late
+    out = gd.gdla_prefill(dims, dev["wstruct"], dev["x"], [0], cache, stream=s)
+    # blocks of exactly the workspace's size, filled on the current stream right away
+    junk = [torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    s.synchronize()
+    torch.cuda.synchronize()
+    del junk
+    assert torch.equal(out, ref)
