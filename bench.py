@@ -5,16 +5,20 @@ latents 1024 / 512, head dim 128, rotary dim 64, full causal), inputs seeded and
 Prints one JSON line: whole-step throughput (algorithmic FLOP of the layer / step time), the
 roofline of the dominant kernel (signal-head attention, timed with HIP events recorded by the
 library around it), and the fp64 CPU oracle timed on a bounded sample of the same workload.
+The line also carries the other half of the metric, `decode`: one decode step of 64 sequences at
+65536 positions (latent-cache GB/s, the roofline of the split-L attention kernel against HBM and
+its own CPU-oracle baseline), and `ceilings`: the fp16 matrix-core rate with random operands and
+the HBM read rate measured on this GPU, against which both fractions are also given.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-ceilings]
+                    [--no-cpu-baseline]
                     [--workload prefill_8k|swa_prefill_2x32k|chunked_prefill_4k_256k|decode_64x64k]
                     [--tokens T]
 
 --workload picks another workload for the timed line (2 x 32K prefill with a 4096 window; a
 4096-token chunk against a 256K cache; one decode step of 64 sequences at 64K context, reported
-in GB/s of latent cache); --decode appends the decode measurement to the 8K line.  With the
-decode workload, --tokens T > 1 times the multi-token decode (T draft tokens per sequence,
-ending at position 65535) instead of the single-token step.
+in GB/s of latent cache).  With the decode workload, --tokens T > 1 times the multi-token decode
+(T draft tokens per sequence, ending at position 65535) instead of the single-token step.
 """
 
 import argparse
@@ -137,6 +141,92 @@ def traffic_from_profile(name):
     if t.get("kernel_source_sha") != source_sha(t["kernel_source"]):
         return None
     return t.get("bytes_per_launch")
+
+
+def traffic_source(name):
+    """Where `traffic` comes from: the committed counter summary, taken on this kernel source."""
+    return (f"profiles/{name}: rocprofv3 FETCH_SIZE / WRITE_SIZE of the kernel, scaled by a 1 GiB "
+            f"copy's counts, taken on the committed kernel source (its SHA-256 matches the current "
+            f"file); not measured in this run")
+
+
+def ceilings(reps=3):
+    """Measured ceilings of this GPU (libgdla_ceiling.so): v_mfma_f32_32x32x16_f16 back to back
+    on pseudo-random operands (8 chains per wave, 8 waves per workgroup); a plain streaming read of
+    4 GiB with non-temporal 16-byte loads.
+    Returns the best of `reps` runs of each, timed with HIP events on the current stream."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "attention_gdla_prefill_decode_amd", "libgdla_ceiling.so")
+    L = ctypes.CDLL(path)
+    L.ceiling_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    L.ceiling_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    blocks, iters = 1024, 2000
+    out = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+    flop = float(blocks) * 8 * iters * 8 * 32768
+
+    def timed(fn):
+        best = None
+        for _ in range(reps + 1):  # the first run warms up
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            if fn() != 0:
+                raise RuntimeError("ceiling probe launch failed")
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        return best
+
+    ms_mfma = timed(lambda: L.ceiling_mfma(ctypes.c_void_p(out.data_ptr()), blocks, iters, stream))
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    rblocks = 8192
+    ms_read = timed(lambda: L.ceiling_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(out.data_ptr()),
+                                           rblocks, stream))
+    del buf
+    return {"mfma_f16_random_TFLOPs": round(flop / ms_mfma / 1e9, 1),
+            "hbm_read_GBps": round(nbytes / ms_read / 1e6, 1),
+            "how": "libgdla_ceiling.so: ceiling_mfma (1024 x 512 threads, 8 x 2000 v_mfma_f32_32x32x16_f16 "
+                   "per wave on random fp16 operands) and ceiling_read (4 GiB, non-temporal 16-byte loads, "
+                   "8 in flight per lane, 8192 x 256 threads); best of 3 after a warm-up"}
+
+
+def cpu_baseline_decode(nseq=8):
+    """The fp64 oracle (absorbed form, as it stands) on nseq sequences drawn with the recipe of the
+    64 x 64K decode workload: each a 65535-row N(0, 1) latent prefix and one new token at position
+    65535.  Returns latent-cache GB/s of the oracle (the bytes of the GPU metric: each cached row of
+    576 bf16 values read once per sequence)."""
+    import numpy as np
+    import synth
+    import oracle.gdla_ref as ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        threads = os.cpu_count()
+    cfg = synth.WORKLOADS["decode_64x64k"]
+    inp = synth.make_inputs(cfg, "cpu", batch=nseq)
+    w = {k: v.double().numpy() for k, v in inp["weights"].items()}
+    dims = ref.Dims(cfg["n_heads"], cfg["n_signal"], cfg["n_noise"], cfg["n_kv"], cfg["d_head"],
+                    cfg["d_rope"], 0)
+    p0 = cfg["p0"]
+    dt = 0.0
+    for b in range(nseq):
+        prefix = inp["cache"][b, :p0].double().numpy()
+        x = inp["x"][b, :1].double().numpy()
+        t0 = time.perf_counter()
+        ref.gdla_decode(x, w, dims, [prefix], [p0])
+        dt += time.perf_counter() - t0
+        del prefix
+    row = cfg["d_kv_latent"] + cfg["d_rope"]
+    nbytes = nseq * (p0 + 1) * row * 2
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"fp64 NumPy oracle, absorbed form, {nseq} sequences of the 64 x 64K decode step "
+                      f"(same recipe, seed of the workload, drawn as a batch of {nseq}): 65535-row "
+                      f"prefix + 1 new token each, {nbytes / 1e9:.3f} GB of latent cache"}
 
 
 def cpu_baseline(rows=2048):
@@ -263,7 +353,8 @@ def bench_decode(steps, warmup, tokens=1, page_rows=0):
             "tokens_per_s": round(len(pos) * tokens / ms * 1e3, 1),
             "roofline": dict({"kernel": "latent_decode_kernel<shared>"}, **roof,
                              traffic=(traffic_from_profile("latent_decode_64x64k_traffic.json")
-                                      if tokens == 1 else None),
+                                      if tokens == 1 and page_rows == 0 else None),
+                             traffic_source=traffic_source("latent_decode_64x64k_traffic.json"),
                              bytes_per_launch=nbytes, flop_per_launch=flop,
                              avg_launch_ms=round(kern_ms, 4)),
             "stages_ms": {k: round(v, 4) for k, v in stages.items()}}
@@ -274,7 +365,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--decode", action="store_true", help="also time the 64 x 64K decode workload")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="leave the 64 x 64K decode step out of the prefill line")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured MFMA / HBM ceilings")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the 64 x 64K decode workload (prints its JSON object)")
     ap.add_argument("--workload", default="prefill_8k",
@@ -396,6 +490,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
                      "traffic": (traffic_from_profile("attn_signal_prefill_8k_traffic.json")
                                  if args.workload == "prefill_8k" and not docs else None),
+                     "traffic_source": traffic_source("attn_signal_prefill_8k_traffic.json"),
                      "flop_per_launch": fl["attn_signal"], "avg_launch_ms": attn_ms},
         "attention_core": {"kernels": "noise + signal attention", "ms": round(attn_ms + noise_ms, 4),
                            "TFLOPs": round((fl["attn_signal"] + fl["attn_noise"])
@@ -403,10 +498,25 @@ def main():
         "stages_ms": stages,
         "out_finite": bool(torch.isfinite(out).all().item()),
     }
-    if args.decode:
-        result["decode"] = bench_decode(max(3, args.steps // 4), 2)
+    del inp, x, cache, ws, out
+    torch.cuda.empty_cache()
+    if not args.no_decode and args.workload == "prefill_8k" and not docs:
+        result["decode"] = bench_decode(max(5, args.steps), 3)
+    if not args.no_ceilings:
+        c = ceilings()
+        result["ceilings"] = c
+        roof = result["roofline"]
+        roof["measured_ceiling"] = c["mfma_f16_random_TFLOPs"]
+        roof["frac_of_measured_ceiling"] = round(roof["achieved"] / c["mfma_f16_random_TFLOPs"], 4)
+        if "decode" in result:
+            droof = result["decode"]["roofline"]
+            if droof["bound"] == "hbm":
+                droof["measured_ceiling"] = c["hbm_read_GBps"]
+                droof["frac_of_measured_ceiling"] = round(droof["achieved"] / c["hbm_read_GBps"], 4)
     if not args.no_cpu_baseline and args.workload == "prefill_8k" and not docs:
         result["cpu_baseline"] = cpu_baseline()
+        if "decode" in result:
+            result["decode"]["cpu_baseline"] = cpu_baseline_decode()
     print(json.dumps(result), flush=True)
 
 

@@ -34,3 +34,21 @@ def test_backward_flop_counts_five_products_per_pair():
     bw = bench.backward_flops(cfg, 8192, 0)
     assert bw["attention"] == 2.0 * 80 * f["pairs"] * (3 * 192 + 2 * 128)
     assert bw["total"] == f["total"] + bw["attention"] + bw["proj"]
+
+
+def test_ceiling_library_exports_its_probes():
+    # the measured-ceiling probes live in a library of their own next to libgdla.so (no launch here)
+    import ctypes
+    path = os.path.join(ROOT, "attention_gdla_prefill_decode_amd", "libgdla_ceiling.so")
+    assert os.path.exists(path), "build the libraries first (__graft_entry__.build())"
+    lib = ctypes.CDLL(path)
+    for name in ("ceiling_mfma", "ceiling_read"):
+        assert hasattr(lib, name), name
+
+
+def test_decode_cpu_baseline_counts_the_latent_cache_bytes():
+    # the decode baseline's bytes: every cached row (576 bf16 values) of each sampled sequence once
+    cfg = synth.WORKLOADS["decode_64x64k"]
+    row = cfg["d_kv_latent"] + cfg["d_rope"]
+    assert row * 2 == 1152
+    assert (cfg["p0"] + 1) * row * 2 == 65536 * 1152
