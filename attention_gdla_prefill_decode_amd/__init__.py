@@ -8,6 +8,6 @@ from .gdla import (EXPORTED, GDLA_BF16, GDLA_F32, GDLA_OP_APPEND, GDLA_OP_BACKWA
                    GDLA_OP_DECODE, GDLA_OP_PREFILL, GDLA_OP_PREFILL_PAGED, GRAD_FIELDS, GdlaGrads,
                    gdla_backward, STAGES, GdlaDebug, StageTimer, GdlaDims,
                    GdlaError, GdlaPagedCache, GdlaWeights, LIB_PATH, MAX_DECODE_TOKENS, PagedCache,
-                   gdla_decode, gdla_decode_paged, gdla_decode_tokens, gdla_latent_append,
+                   NOALLOC_SCRATCH_BYTES, gdla_decode, gdla_decode_noalloc, gdla_decode_paged, gdla_decode_tokens, gdla_latent_append,
                    gdla_latent_append_paged, gdla_prefill, gdla_prefill_packed, gdla_prefill_paged,
                    gdla_workspace_bytes, lib, make_dims, make_weights)

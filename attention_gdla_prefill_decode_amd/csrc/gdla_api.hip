@@ -524,6 +524,10 @@ gdla_status append_impl(const gdla_dims *dims, const gdla_weights *w, const void
 
 }  // namespace
 
+namespace gdla {
+gdla_status report_error(gdla_status st, const char *msg) { return fail(st, "%s", msg); }
+}  // namespace gdla
+
 GDLA_EXPORT gdla_status gdla_latent_append(const gdla_dims *dims, const gdla_weights *w,
                                            const void *x, int32_t B, int32_t T,
                                            const int32_t *pos_host, void *cache, int32_t max_len,

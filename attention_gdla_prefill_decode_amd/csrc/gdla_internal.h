@@ -87,6 +87,9 @@ __host__ __device__ inline int64_t cache_row(const CacheRef &c, int b, int pos) 
   return (int64_t)pg * c.page_rows + pos % c.page_rows;
 }
 
+// Records `msg` as the calling thread's last error (gdla_last_error) and returns st.
+gdla_status report_error(gdla_status st, const char *msg);
+
 inline CacheRef contiguous_cache(void *base, int32_t max_len) {
   CacheRef c{};
   c.base = base;

@@ -27,10 +27,11 @@ WEIGHT_FIELDS = ("w_qa", "gamma_q", "w_qc", "w_qr", "w_dkv", "w_kr", "gamma_kv",
 
 EXPORTED = ("gdla_workspace_bytes", "gdla_latent_append", "gdla_prefill", "gdla_decode",
             "gdla_decode_tokens", "gdla_prefill_packed", "gdla_latent_append_paged",
-            "gdla_prefill_paged", "gdla_decode_paged", "gdla_backward", "gdla_status_string",
-            "gdla_last_error")
+            "gdla_prefill_paged", "gdla_decode_paged", "gdla_backward", "gdla_decode_noalloc",
+            "gdla_status_string", "gdla_last_error")
 
 MAX_DECODE_TOKENS = 16  # GDLA_MAX_DECODE_TOKENS
+NOALLOC_SCRATCH_BYTES = 96 * 1024 * 1024  # GDLA_NOALLOC_SCRATCH_BYTES
 
 
 class GdlaDims(ctypes.Structure):
@@ -138,6 +139,10 @@ def lib():
                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                   P(GdlaDebug), ctypes.c_void_p]
+        L.gdla_decode_noalloc.restype = ctypes.c_int
+        L.gdla_decode_noalloc.argtypes = [P(GdlaDims), P(GdlaWeights), ctypes.c_void_p, ctypes.c_int32,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                          ctypes.c_void_p, P(GdlaDebug), ctypes.c_void_p]
         L.gdla_decode_tokens.restype = ctypes.c_int
         L.gdla_decode_tokens.argtypes = [P(GdlaDims), P(GdlaWeights), ctypes.c_void_p, ctypes.c_int32,
                                          ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
@@ -282,6 +287,20 @@ def gdla_decode(dims, weights, x, pos, cache, out=None, ws=None, lambda_override
     _check(lib().gdla_decode(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B,
                              _pos_array(pos), _ptr(cache), max_len, _ptr(out), _ptr(ws), nbytes,
                              None if dbg is None else ctypes.byref(dbg), _stream(stream)))
+    return out
+
+
+def gdla_decode_noalloc(dims, weights, x, pos, cache, out, lambda_override=None, out_heads=None,
+                        stream=None, timer=None):
+    """gdla_decode on the library's static device scratch (no workspace argument): x [B, d_model],
+    token b at position pos[b]; appends to cache; writes out [B, d_model] (caller-allocated) and
+    returns it.  Calls on one GPU share the scratch: the caller orders them."""
+    B = x.shape[0]
+    max_len = cache.shape[1]
+    dbg = _debug(lambda_override, out_heads, timer)
+    _check(lib().gdla_decode_noalloc(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B,
+                                     _pos_array(pos), _ptr(cache), max_len, _ptr(out),
+                                     None if dbg is None else ctypes.byref(dbg), _stream(stream)))
     return out
 
 

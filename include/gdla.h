@@ -84,6 +84,10 @@ typedef enum {
 /* Most new tokens per sequence that gdla_decode_tokens takes in one call. */
 #define GDLA_MAX_DECODE_TOKENS 16
 
+/* Size of gdla_decode_noalloc's static device scratch (96 MiB): enough for a decode step of 64
+ * sequences of the 4096-wide, 80-head layer at any context length (78 MiB). */
+#define GDLA_NOALLOC_SCRATCH_BYTES (96u * 1024u * 1024u)
+
 /* Layer sizes (picx.dev summary section 2.2).  n_heads = n_signal + n_noise, n_signal is a
  * multiple g of n_noise (Eq.(6)), and n_kv_heads divides n_noise. */
 typedef struct {
@@ -177,6 +181,20 @@ gdla_status gdla_prefill(const gdla_dims *dims, const gdla_weights *w, const voi
 gdla_status gdla_decode(const gdla_dims *dims, const gdla_weights *w, const void *x, int32_t B,
                         const int32_t *pos_host, void *cache, int32_t max_len, void *out,
                         void *ws, size_t ws_bytes, const gdla_debug *dbg, hipStream_t stream);
+
+/* gdla_decode for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  It takes no workspace: the library uses
+ * a static device array of GDLA_NOALLOC_SCRATCH_BYTES instead, one per GPU, held from the first
+ * call on that GPU until the process ends.  The caller still passes x, the cache and out (as for
+ * gdla_decode); the call allocates nothing and clears nothing (every scratch byte it reads it has
+ * written).  All calls on one GPU share that GPU's array, so calls that overlap on one GPU (other
+ * streams, other host threads) race: the caller orders them.  The stream must belong to the
+ * current device.  Errors as gdla_decode, plus GDLA_ERR_WORKSPACE (nothing launched) when the
+ * call needs more than GDLA_NOALLOC_SCRATCH_BYTES (gdla_workspace_bytes(dims, GDLA_OP_DECODE, B,
+ * 1, pos_host, max_len) tells), and GDLA_ERR_HIP when the scratch has no address on the device. */
+gdla_status gdla_decode_noalloc(const gdla_dims *dims, const gdla_weights *w, const void *x, int32_t B,
+                                const int32_t *pos_host, void *cache, int32_t max_len, void *out,
+                                const gdla_debug *dbg, hipStream_t stream);
 
 /* gdla_prefill over packed documents (paperglide reader, Figure 4 (a): a training sequence that
  * holds 473 documents, drawn on the QK^T score matrix): every token attends only to keys of its own

@@ -175,6 +175,25 @@ def test_decode_and_append_argument_errors():
     assert st == gb.GDLA_ERR_WORKSPACE
 
 
+def test_decode_noalloc_refuses_calls_beyond_its_scratch():
+    # 256 sequences of the 80-head layer need about 185 MiB of workspace, above the 96 MiB static
+    # scratch: refused with GDLA_ERR_WORKSPACE before any GPU call (so this runs without a GPU)
+    lib = gd.lib()
+    d = big_dims()
+    w = gb.GdlaWeights(*([FAKE] * 12))
+    B = 256
+    pos = (ctypes.c_int32 * B)(*([100] * B))
+    need = lib.gdla_workspace_bytes(ctypes.byref(d), gb.GDLA_OP_DECODE, B, 1, pos, 4096)
+    assert need > gd.NOALLOC_SCRATCH_BYTES
+    st = lib.gdla_decode_noalloc(ctypes.byref(d), ctypes.byref(w), FAKE, B, pos, FAKE, 4096, FAKE, None, None)
+    assert st == gb.GDLA_ERR_WORKSPACE
+    assert b"static scratch" in lib.gdla_last_error()
+    # and 64 sequences at the 64K context fit
+    B = 64
+    pos = (ctypes.c_int32 * B)(*([65535] * B))
+    assert lib.gdla_workspace_bytes(ctypes.byref(d), gb.GDLA_OP_DECODE, B, 1, pos, 65536) <= gd.NOALLOC_SCRATCH_BYTES
+
+
 def test_decode_tokens_argument_errors():
     lib = gd.lib()
     d = big_dims()
