@@ -10,4 +10,5 @@ from .gdla import (EXPORTED, GDLA_BF16, GDLA_F32, GDLA_OP_APPEND, GDLA_OP_BACKWA
                    GdlaError, GdlaPagedCache, GdlaWeights, LIB_PATH, MAX_DECODE_TOKENS, PagedCache,
                    NOALLOC_SCRATCH_BYTES, gdla_decode, gdla_decode_noalloc, gdla_decode_paged, gdla_decode_tokens, gdla_latent_append,
                    gdla_latent_append_paged, gdla_prefill, gdla_prefill_packed, gdla_prefill_paged,
+                   gdla_prepare_weights, gdla_prepared_weights_bytes, gdla_prefill_prepared,
                    gdla_workspace_bytes, lib, make_dims, make_weights)

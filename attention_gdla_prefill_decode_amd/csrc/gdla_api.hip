@@ -86,6 +86,52 @@ struct PrefillLayout {
 // Rows from which the transposed-weight GEMM pays for transposing the weights once per call.
 constexpr int32_t kNtMinRows = 256;
 
+// Prepared weights (gdla_prepare_weights): the transposed copies the K-contiguous GEMM reads,
+// x-side and expansion weights in bf16, the weights applied to fp16 activations in fp16.
+struct PreparedLayout {
+  size_t qa, dkv, kr, lam, qc, qr, gate, uk, uv, o, total;
+};
+
+PreparedLayout plan_prepared(const LayerDims &d) {
+  PreparedLayout L{};
+  Plan p;
+  L.qa = p.add(2 * (size_t)d.d_model * d.d_cq);
+  L.dkv = p.add(2 * (size_t)d.d_model * d.d_c);
+  L.kr = p.add(2 * (size_t)d.d_model * d.d_r);
+  L.lam = p.add(2 * (size_t)d.d_model * d.n_signal);
+  L.qc = p.add(2 * (size_t)d.d_cq * d.n_heads * d.d_h);
+  L.qr = p.add(2 * (size_t)d.d_cq * d.n_heads * d.d_r);
+  L.gate = p.add(2 * (size_t)d.d_cq * d.n_signal * d.d_h);
+  L.uk = p.add(2 * (size_t)d.d_c * d.n_kv * d.d_h);
+  L.uv = p.add(2 * (size_t)d.d_c * d.n_kv * d.d_h);
+  L.o = p.add(2 * (size_t)d.n_signal * d.d_h * d.d_model);
+  L.total = p.bytes;
+  return L;
+}
+
+// The 10 transposed weight copies of one layer into `dst` at the offsets of `off` (a prefill
+// workspace's wt_* fields or a prepared-weight buffer's).
+hipError_t transpose_layer_weights(const LayerDims &d, const gdla_weights *w, char *dst, const size_t (&off)[10],
+                                   hipStream_t stream) {
+  struct { const void *w; int32_t K, N; bool f16; } tw[] = {
+      {w->w_qa, d.d_model, d.d_cq, false},
+      {w->w_dkv, d.d_model, d.d_c, false},
+      {w->w_kr, d.d_model, d.d_r, false},
+      {w->w_lambda, d.d_model, d.n_signal, false},
+      {w->w_qc, d.d_cq, d.n_heads * d.d_h, true},
+      {w->w_qr, d.d_cq, d.n_heads * d.d_r, true},
+      {w->w_gate, d.d_cq, d.n_signal * d.d_h, true},
+      {w->w_uk, d.d_c, d.n_kv * d.d_h, false},
+      {w->w_uv, d.d_c, d.n_kv * d.d_h, false},
+      {w->w_o, d.n_signal * d.d_h, d.d_model, true},
+  };
+  for (int i = 0; i < 10; ++i) {
+    const hipError_t e = launch_transpose_weight(tw[i].w, dst + off[i], tw[i].K, tw[i].N, tw[i].f16, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 int32_t key_capacity(const LayerDims &d, int32_t B, int32_t T, const int32_t *pos, int32_t max_len) {
   int32_t lcap = 0;
   for (int32_t b = 0; b < B; ++b) {
@@ -550,10 +596,12 @@ GDLA_EXPORT gdla_status gdla_latent_append_paged(const gdla_dims *dims, const gd
 namespace {
 
 // doc: device [B, T] first position of each token's document (packed documents), or null
+// prepared: the layer's transposed weights from gdla_prepare_weights, or null (then the call
+// transposes them into its workspace)
 gdla_status prefill_impl(const gdla_dims *dims, const gdla_weights *w, const void *x, int32_t B, int32_t T,
                          const int32_t *pos_host, void *cache, int32_t max_len, void *out, void *ws,
                          size_t ws_bytes, const gdla_debug *dbg, hipStream_t stream,
-                         const int32_t *doc = nullptr, float *lse = nullptr) {
+                         const int32_t *doc = nullptr, float *lse = nullptr, const void *prepared = nullptr) {
   LayerDims d;
   gdla_status st = check_call(dims, w, x, B, T, pos_host, cache, max_len, out, true, d);
   if (st != GDLA_OK || B == 0 || T == 0) return st;
@@ -574,24 +622,19 @@ gdla_status prefill_impl(const gdla_dims *dims, const gdla_weights *w, const voi
   if (L.use_nt) {
     // Transposed weights for the K-contiguous GEMM: weights applied to x and to the bf16 cache stay
     // bf16, those applied to the fp16 c^Q and Y become fp16 (the conversion the other MFMA GEMM
-    // does while staging).
+    // does while staging).  Prepared once by the caller, or written here into the workspace.
     se.begin(GDLA_STAGE_PROJ_IN);
-    struct { const void *w; size_t off; int32_t K, N; bool f16; } tw[] = {
-        {w->w_qa, L.wt_qa, d.d_model, d.d_cq, false},
-        {w->w_dkv, L.wt_dkv, d.d_model, d.d_c, false},
-        {w->w_kr, L.wt_kr, d.d_model, d.d_r, false},
-        {w->w_lambda, L.wt_lam, d.d_model, d.n_signal, false},
-        {w->w_qc, L.wt_qc, d.d_cq, d.n_heads * d.d_h, true},
-        {w->w_qr, L.wt_qr, d.d_cq, d.n_heads * d.d_r, true},
-        {w->w_gate, L.wt_gate, d.d_cq, d.n_signal * d.d_h, true},
-        {w->w_uk, L.wt_uk, d.d_c, d.n_kv * d.d_h, false},
-        {w->w_uv, L.wt_uv, d.d_c, d.n_kv * d.d_h, false},
-        {w->w_o, L.wt_o, d.n_signal * d.d_h, d.d_model, true},
-    };
-    for (const auto &t : tw) HIP_TRY(launch_transpose_weight(t.w, at<void>(ws, t.off), t.K, t.N, t.f16, stream));
-    ntw = {at<void>(ws, L.wt_qa), at<void>(ws, L.wt_dkv), at<void>(ws, L.wt_kr), at<void>(ws, L.wt_lam),
-           at<void>(ws, L.wt_qc), at<void>(ws, L.wt_qr), at<void>(ws, L.wt_gate), at<void>(ws, L.wt_uk),
-           at<void>(ws, L.wt_uv), at<void>(ws, L.wt_o)};
+    if (prepared) {
+      const PreparedLayout P = plan_prepared(d);
+      const char *b = (const char *)prepared;
+      ntw = {b + P.qa, b + P.dkv, b + P.kr, b + P.lam, b + P.qc, b + P.qr, b + P.gate, b + P.uk, b + P.uv, b + P.o};
+    } else {
+      const size_t off[10] = {L.wt_qa, L.wt_dkv, L.wt_kr, L.wt_lam, L.wt_qc, L.wt_qr, L.wt_gate, L.wt_uk, L.wt_uv, L.wt_o};
+      HIP_TRY(transpose_layer_weights(d, w, (char *)ws, off, stream));
+      ntw = {at<void>(ws, L.wt_qa), at<void>(ws, L.wt_dkv), at<void>(ws, L.wt_kr), at<void>(ws, L.wt_lam),
+             at<void>(ws, L.wt_qc), at<void>(ws, L.wt_qr), at<void>(ws, L.wt_gate), at<void>(ws, L.wt_uk),
+             at<void>(ws, L.wt_uv), at<void>(ws, L.wt_o)};
+    }
   }
   // Eq.(1), (3), (4), (7) and the cache append of this chunk's rows.
   st = project_and_append(d, dt, w, x, M, T, pos_dev, contiguous_cache(cache, max_len), at<float>(ws, L.aq),
@@ -700,6 +743,50 @@ GDLA_EXPORT gdla_status gdla_prefill(const gdla_dims *dims, const gdla_weights *
                                      const gdla_debug *dbg, hipStream_t stream) {
   g_err[0] = 0;
   return prefill_impl(dims, w, x, B, T, pos_host, cache, max_len, out, ws, ws_bytes, dbg, stream);
+}
+
+GDLA_EXPORT size_t gdla_prepared_weights_bytes(const gdla_dims *dims) {
+  LayerDims d;
+  if (check_dims(dims, d) != GDLA_OK) return 0;
+  if (!fast_prefill_supported(d, dims->dtype) || d.d_c % 64 != 0) return 0;
+  return plan_prepared(d).total;
+}
+
+GDLA_EXPORT gdla_status gdla_prepare_weights(const gdla_dims *dims, const gdla_weights *w, void *prepared,
+                                             size_t prepared_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  LayerDims d;
+  gdla_status st = check_dims(dims, d);
+  if (st != GDLA_OK) return st;
+  const size_t need = gdla_prepared_weights_bytes(dims);
+  if (need == 0) return fail(GDLA_ERR_UNSUPPORTED, "this layer's prefill takes no prepared weights");
+  if (!w) return fail(GDLA_ERR_INVALID_ARG, "weights is NULL");
+  const void *req[] = {w->w_qa, w->w_qc, w->w_qr, w->w_dkv, w->w_kr, w->w_uk, w->w_uv, w->w_lambda, w->w_gate, w->w_o};
+  for (const void *p : req) {
+    if (!p) return fail(GDLA_ERR_INVALID_ARG, "a required weight pointer is NULL");
+    if (!aligned16(p)) return fail(GDLA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  }
+  if ((st = check_ws(prepared, prepared_bytes, need)) != GDLA_OK) return st;
+  const PreparedLayout P = plan_prepared(d);
+  const size_t off[10] = {P.qa, P.dkv, P.kr, P.lam, P.qc, P.qr, P.gate, P.uk, P.uv, P.o};
+  HIP_TRY(transpose_layer_weights(d, w, (char *)prepared, off, stream));
+  return GDLA_OK;
+}
+
+GDLA_EXPORT gdla_status gdla_prefill_prepared(const gdla_dims *dims, const gdla_weights *w, const void *prepared,
+                                              size_t prepared_bytes, const void *x, int32_t B, int32_t T,
+                                              const int32_t *pos_host, void *cache, int32_t max_len, void *out,
+                                              void *ws, size_t ws_bytes, const gdla_debug *dbg,
+                                              hipStream_t stream) {
+  g_err[0] = 0;
+  const size_t need = gdla_prepared_weights_bytes(dims);
+  if (need == 0) return fail(GDLA_ERR_UNSUPPORTED, "this layer's prefill takes no prepared weights");
+  if (!prepared) return fail(GDLA_ERR_INVALID_ARG, "prepared is NULL");
+  if (((uintptr_t)prepared & 255u) != 0) return fail(GDLA_ERR_INVALID_ARG, "prepared must be 256-byte aligned");
+  if (prepared_bytes < need)
+    return fail(GDLA_ERR_WORKSPACE, "prepared weights %zu bytes < %zu needed", prepared_bytes, need);
+  return prefill_impl(dims, w, x, B, T, pos_host, cache, max_len, out, ws, ws_bytes, dbg, stream, nullptr, nullptr,
+                      prepared);
 }
 
 GDLA_EXPORT gdla_status gdla_prefill_packed(const gdla_dims *dims, const gdla_weights *w, const void *x,

@@ -28,6 +28,7 @@ WEIGHT_FIELDS = ("w_qa", "gamma_q", "w_qc", "w_qr", "w_dkv", "w_kr", "gamma_kv",
 EXPORTED = ("gdla_workspace_bytes", "gdla_latent_append", "gdla_prefill", "gdla_decode",
             "gdla_decode_tokens", "gdla_prefill_packed", "gdla_latent_append_paged",
             "gdla_prefill_paged", "gdla_decode_paged", "gdla_backward", "gdla_decode_noalloc",
+            "gdla_prepared_weights_bytes", "gdla_prepare_weights", "gdla_prefill_prepared",
             "gdla_status_string", "gdla_last_error")
 
 MAX_DECODE_TOKENS = 16  # GDLA_MAX_DECODE_TOKENS
@@ -139,6 +140,16 @@ def lib():
                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                   P(GdlaDebug), ctypes.c_void_p]
+        L.gdla_prepared_weights_bytes.restype = ctypes.c_size_t
+        L.gdla_prepared_weights_bytes.argtypes = [P(GdlaDims)]
+        L.gdla_prepare_weights.restype = ctypes.c_int
+        L.gdla_prepare_weights.argtypes = [P(GdlaDims), P(GdlaWeights), ctypes.c_void_p, ctypes.c_size_t,
+                                           ctypes.c_void_p]
+        L.gdla_prefill_prepared.restype = ctypes.c_int
+        L.gdla_prefill_prepared.argtypes = [P(GdlaDims), P(GdlaWeights), ctypes.c_void_p, ctypes.c_size_t,
+                                            ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_size_t, P(GdlaDebug), ctypes.c_void_p]
         L.gdla_decode_noalloc.restype = ctypes.c_int
         L.gdla_decode_noalloc.argtypes = [P(GdlaDims), P(GdlaWeights), ctypes.c_void_p, ctypes.c_int32,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
@@ -287,6 +298,37 @@ def gdla_decode(dims, weights, x, pos, cache, out=None, ws=None, lambda_override
     _check(lib().gdla_decode(ctypes.byref(dims), ctypes.byref(weights), _ptr(x), B,
                              _pos_array(pos), _ptr(cache), max_len, _ptr(out), _ptr(ws), nbytes,
                              None if dbg is None else ctypes.byref(dbg), _stream(stream)))
+    return out
+
+
+def gdla_prepared_weights_bytes(dims):
+    return int(lib().gdla_prepared_weights_bytes(ctypes.byref(dims)))
+
+
+def gdla_prepare_weights(dims, weights, prepared=None, stream=None, device="cuda"):
+    """The layer's prepared (transposed) weights for gdla_prefill_prepared, in `prepared` (a
+    uint8 device tensor of at least gdla_prepared_weights_bytes(dims) bytes) or a new tensor."""
+    with _on(stream):
+        if prepared is None:
+            prepared = torch.empty(max(gdla_prepared_weights_bytes(dims), 256), dtype=torch.uint8, device=device)
+    _check(lib().gdla_prepare_weights(ctypes.byref(dims), ctypes.byref(weights), _ptr(prepared),
+                                      prepared.numel(), _stream(stream)))
+    return prepared
+
+
+def gdla_prefill_prepared(dims, weights, prepared, x, pos, cache, out=None, ws=None, lambda_override=None,
+                          out_heads=None, stream=None, timer=None):
+    """gdla_prefill reading the weights' transposed copies from `prepared` (gdla_prepare_weights)."""
+    B, T = x.shape[0], x.shape[1]
+    max_len = cache.shape[1]
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(x)
+        ws, nbytes = _workspace(dims, GDLA_OP_PREFILL, B, T, pos, max_len, ws, x.device)
+    dbg = _debug(lambda_override, out_heads, timer)
+    _check(lib().gdla_prefill_prepared(ctypes.byref(dims), ctypes.byref(weights), _ptr(prepared), prepared.numel(),
+                                       _ptr(x), B, T, _pos_array(pos), _ptr(cache), max_len, _ptr(out), _ptr(ws),
+                                       nbytes, None if dbg is None else ctypes.byref(dbg), _stream(stream)))
     return out
 
 

@@ -386,6 +386,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time gdla_backward (training sequences from position 0) on the workload's "
                          "shape instead of the forward; prints its JSON object")
+    ap.add_argument("--transpose-per-call", action="store_true",
+                    help="time gdla_prefill (weights transposed inside every call) instead of "
+                         "gdla_prefill_prepared (transposed once beforehand)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 1 GiB device to device three times (a known-size reference "
@@ -443,7 +446,13 @@ def main():
                      dtype=torch.uint8, device="cuda")
     out = torch.empty_like(x)
     docs = None
-    run = gd.gdla_prefill
+    if args.transpose_per_call:
+        run = gd.gdla_prefill
+    else:  # the layer's weights transposed once, as a deployment keeps them resident
+        prepared = gd.gdla_prepare_weights(dims, w)
+
+        def run(*a, **k):
+            return gd.gdla_prefill_prepared(a[0], a[1], prepared, *a[2:], **k)
     if args.docs > 0:  # documents packed from the chunk's first token
         docs = [p0 + v for v in packed_documents(t, args.docs)]
         doc_t = torch.tensor([docs] * bsz, dtype=torch.int32, device="cuda")
@@ -483,6 +492,8 @@ def main():
                    "d_model": cfg["d_model"], "heads": "64 signal + 16 noise, 16 KV",
                    "latents": "1024 / 512", "head_dim": cfg["d_head"], "rope_dim": cfg["d_rope"],
                    "window": win, "parallelism": "none (1 GPU)",
+                   "weights": ("transposed inside every call" if args.transpose_per_call or docs
+                               else "transposed once beforehand (gdla_prepare_weights)"),
                    **({"documents": len(set(docs)), "mean_document": args.docs} if docs else {})},
         "frac_of_mfma_peak_whole_step": round(value / PEAK_MFMA_TFLOPS, 4),
         "roofline": {"kernel": "attn_prefill_kernel<signal>", "bound": "mfma",
@@ -499,6 +510,8 @@ def main():
         "out_finite": bool(torch.isfinite(out).all().item()),
     }
     del inp, x, cache, ws, out
+    if not args.transpose_per_call:
+        del prepared
     torch.cuda.empty_cache()
     if not args.no_decode and args.workload == "prefill_8k" and not docs:
         result["decode"] = bench_decode(max(5, args.steps), 3)

@@ -174,6 +174,34 @@ gdla_status gdla_prefill(const gdla_dims *dims, const gdla_weights *w, const voi
                          void *out, void *ws, size_t ws_bytes, const gdla_debug *dbg,
                          hipStream_t stream);
 
+/* Prepared weights for prefill: the transposed copies of the ten projection weights that the
+ * prefill's large GEMMs read (K-contiguous; the weights applied to x and to the cache in bf16, those
+ * applied to fp16 activations, W_qc / W_qr / W_gate / W_o, converted to fp16).  gdla_prefill makes
+ * them in its workspace on every call; a caller that keeps a layer's weights resident makes them
+ * once with gdla_prepare_weights and passes them to gdla_prefill_prepared instead (Eq.(1)-(5),
+ * (9), (10) of picx.dev summary section 2.2 are unchanged; only where the weights' copies come
+ * from differs).  gdla_prepared_weights_bytes returns the buffer size, or 0 for layers whose
+ * prefill reads no transposed weights (fp32 layers, head sizes other than 128 + 64). */
+size_t gdla_prepared_weights_bytes(const gdla_dims *dims);
+
+/* Writes the prepared weights of w into `prepared` (device, 256-byte aligned, at least
+ * gdla_prepared_weights_bytes(dims) bytes, owned by the caller), asynchronously on `stream`.
+ * Call again whenever the weights change.  Errors: GDLA_ERR_UNSUPPORTED when the layer takes none,
+ * GDLA_ERR_INVALID_ARG for NULL or misaligned pointers, GDLA_ERR_WORKSPACE when prepared_bytes is
+ * too small; nothing is launched on error. */
+gdla_status gdla_prepare_weights(const gdla_dims *dims, const gdla_weights *w, void *prepared,
+                                 size_t prepared_bytes, hipStream_t stream);
+
+/* gdla_prefill with prepared weights (the same arguments, plus the buffer gdla_prepare_weights
+ * filled from the same w): identical results, without the per-call transposes.  w is still read
+ * (gains, and the projections of calls too small for the transposed-weight GEMM).  Workspace:
+ * gdla_workspace_bytes(dims, GDLA_OP_PREFILL, ...), as for gdla_prefill.  Errors as gdla_prefill,
+ * plus those of the prepared buffer (as gdla_prepare_weights). */
+gdla_status gdla_prefill_prepared(const gdla_dims *dims, const gdla_weights *w, const void *prepared,
+                                  size_t prepared_bytes, const void *x, int32_t B, int32_t T,
+                                  const int32_t *pos_host, void *cache, int32_t max_len, void *out,
+                                  void *ws, size_t ws_bytes, const gdla_debug *dbg, hipStream_t stream);
+
 /* One decode step per sequence: token b (x [B, d_model]) sits at position pos_host[b] (= number
  * of rows already cached).  Its latent row is appended, then it attends over cache rows
  * [0, pos_host[b]] in the absorbed form (queries mapped into the latent space, values mapped out

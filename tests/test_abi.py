@@ -289,3 +289,32 @@ def test_backward_argument_errors():
     assert lib.gdla_last_error().decode()
     assert call(T=0, x=None, dout=None) == gb.GDLA_OK
     assert gd.gdla_workspace_bytes(d, gd.GDLA_OP_BACKWARD, 1, 16, None, 16) > 0
+
+
+def test_prepared_weights_sizes_and_errors():
+    lib = gd.lib()
+    d = big_dims()
+    need = gd.gdla_prepared_weights_bytes(d)
+    # ten transposed weights of the 80-head layer, 2 bytes per value
+    vals = (4096 * (1024 + 512 + 64 + 64) + 1024 * (80 * 128 + 80 * 64 + 64 * 128) + 512 * 2 * 16 * 128
+            + 64 * 128 * 4096)
+    assert need >= 2 * vals and need < 2 * vals + 10 * 256
+    assert gd.gdla_prepared_weights_bytes(big_dims(dtype="f32")) == 0
+    w = gb.GdlaWeights(*([FAKE] * 12))
+    st = lib.gdla_prepare_weights(ctypes.byref(big_dims(dtype="f32")), ctypes.byref(w), FAKE, 1 << 40, None)
+    assert st == gb.GDLA_ERR_UNSUPPORTED
+    st = lib.gdla_prepare_weights(ctypes.byref(d), ctypes.byref(w), None, 1 << 40, None)
+    assert st == gb.GDLA_ERR_INVALID_ARG
+    st = lib.gdla_prepare_weights(ctypes.byref(d), ctypes.byref(w), FAKE, need - 1, None)
+    assert st == gb.GDLA_ERR_WORKSPACE
+    w.w_o = None
+    st = lib.gdla_prepare_weights(ctypes.byref(d), ctypes.byref(w), FAKE, need, None)
+    assert st == gb.GDLA_ERR_INVALID_ARG
+    w.w_o = FAKE
+    pos = (ctypes.c_int32 * 1)(0)
+    st = lib.gdla_prefill_prepared(ctypes.byref(d), ctypes.byref(w), None, need, FAKE, 1, 8, pos, FAKE, 8, FAKE,
+                                   FAKE, 1 << 40, None, None)
+    assert st == gb.GDLA_ERR_INVALID_ARG
+    st = lib.gdla_prefill_prepared(ctypes.byref(d), ctypes.byref(w), FAKE, 16, FAKE, 1, 8, pos, FAKE, 8, FAKE,
+                                   FAKE, 1 << 40, None, None)
+    assert st == gb.GDLA_ERR_WORKSPACE

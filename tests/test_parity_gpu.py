@@ -506,3 +506,21 @@ def test_explicit_stream_without_workspace():
     torch.cuda.synchronize()
     del junk
     assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("cfg,T,p0,window", [(H.BF80, 300, [0], 0), (BF, 260, [40, 0], 64), (BF, 64, [5], 0)],
+                         ids=["80h", "10h-window", "short"])
+def test_prefill_prepared_weights_match_prefill(cfg, T, p0, window):
+    """gdla_prefill_prepared (weights transposed once by gdla_prepare_weights) gives gdla_prefill's
+    output and cache rows bit for bit; below 256 rows the prepared copies are not read at all."""
+    inp = synth.make_inputs(cfg, "cpu", batch=len(p0), seq=T, p0=p0, random_gamma=True, seed=131)
+    dev = H.device_inputs(inp)
+    dims = gd.make_dims(cfg, window=window)
+    prepared = gd.gdla_prepare_weights(dims, dev["wstruct"])
+    c1, c2 = dev["cache"].clone(), dev["cache"].clone()
+    ref = gd.gdla_prefill(dims, dev["wstruct"], dev["x"], inp["p0"], c1)
+    out = gd.gdla_prefill_prepared(dims, dev["wstruct"], prepared, dev["x"], inp["p0"], c2)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref) and torch.equal(c1, c2)
+    r = H.prefill_case(cfg, T, p0, window=window, seed=131)
+    _say(H.check(H.to_np(out), r["exp_out"], "bf16", f"prepared-weight prefill T={T}"))
