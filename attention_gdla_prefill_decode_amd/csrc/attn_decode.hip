@@ -10,9 +10,11 @@
 //
 // Kernel layout: one workgroup per (sequence, key split), one wave per SIMD.  Query heads come in
 // blocks of 16 (the N side of v_mfma_f32_16x16x32_bf16).
-//   Scores: wave w computes the scores of block w and, when there are five blocks (65..80 heads),
-//   also those of block 4 (every wave, from the fragments it already reads), so q~ of two blocks
-//   (2 x 72 registers) stays in registers.
+//   Scores: wave w computes the scores of key block w % 2 (16 of the tile's 32 keys) for head
+//   blocks 2 (w / 2) and 2 (w / 2) + 1, so every cache fragment it reads from LDS feeds two MFMAs
+//   (the S phase is bound by these LDS reads); when there are five blocks (65..80 heads) it also
+//   computes a quarter of block 4's partial scores from the same fragments.  q~ of two blocks and
+//   the quarter of block 4 (2 x 72 + 36 registers) stay in registers.
 //   Values: wave w accumulates output dims 128 w .. 128 w + 127 of every head block (160 registers),
 //   so each wave transposes only its quarter of the tile (the transposing LDS reads are about 3x
 //   slower per byte than plain ones).  The probabilities of blocks 0..3 go through a 4 KB LDS
@@ -20,7 +22,7 @@
 // Cache tiles of 32 rows (576 bf16 = 72 chunks of 16 bytes each) stream through a 4-slot LDS ring
 // by direct global -> LDS 16-byte loads; every tile serves all heads.  Per tile and wave:
 //   S^T[key, head] = cache[key, 0:576] . q~[head, 0:576]   (A = cache rows, B = q~ from registers)
-//   softmax against a fixed reference (see SoftmaxState), P^T -> LDS, barrier,
+//   softmax against a fixed reference (see SoftmaxState), each wave's half of P^T -> LDS, barrier,
 //   O^T[dim, head] += cbar^T[dim, key] . P^T[key, head]    (A = cbar^T by ds_read_b64_tr_b16,
 //                                                           B = P^T of each head block)
 // Rows are unpadded; chunk c of row r sits at c ^ (r mod 8).  With it the hardware counter reads no
@@ -132,36 +134,32 @@ __device__ __forceinline__ float head_sum(float v) {
 // tile loop needs no cross-lane reduction.  A score more than 64 above the reference (overflow
 // risk), or a split whose maximum stays more than 64 below it (underflow risk), raises `redo`, and
 // the split is then computed again against its exact maximum, so neither can happen.  mrun and l
-// are kept per lane (each lane sees a quarter of the keys of its head) and reduced over the 4 lanes
-// of a head at the end.
+// are kept per lane (each lane sees a quarter of the keys of its head in its wave's key block) and
+// reduced over the 4 lanes of a head, and over the waves holding the other key block, at the end.
 struct SoftmaxState {
   float mref = 0.f, mrun = -INFINITY, l = 0.f;
   bool redo = false;
 };
 
-// Scores -> probabilities for one tile (score of key s0 + 16 kb + 4 g + j in S[kb][j]); `lim` =
-// k_end - s0 - 4 g masks the keys past the split and, with LOWER (paged cache with a window: the
-// first tile, aligned to the pages, may start below it), `llim` = lo - s0 - 4 g those before it.  Returns P^T as the B operand of the 32-key
-// step (slot e <-> key 16 (e / 4) + 4 g + e % 4).  Branch-free, so it stays in the MFMA block.
+// Scores -> probabilities of one block of 16 keys (score of key s0 + 16 kb + 4 g + j in S[j]);
+// `lim` = k_end - s0 - 16 kb - 4 g masks the keys past the split and, with LOWER (paged cache with
+// a window: the first tile, aligned to the pages, may start below it), `llim` = lo - s0 - 16 kb - 4 g
+// those before it.  P[j] is slot 4 kb + j of the B operand of the 32-key PV step (slot e <-> key
+// 16 (e / 4) + 4 g + e % 4).  Branch-free, so it stays in the MFMA block.
 template <bool LOWER>
-__device__ __forceinline__ void softmax_tile(f32x4 (&S)[2], SoftmaxState &st, int llim, int lim, float c,
-                                             bf16x8 &P) {
-  float v[8];
+__device__ __forceinline__ void softmax_keys16(f32x4 S, SoftmaxState &st, int llim, int lim, float c,
+                                               bf16x4 &P) {
+  float v[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int kidx = 16 * (i >> 2) + (i & 3);
-    v[i] = kidx < lim && (!LOWER || kidx >= llim) ? S[i >> 2][i & 3] * c : -INFINITY;
-  }
-  float mt = v[0];
-#pragma unroll
-  for (int i = 1; i < 8; ++i) mt = fmaxf(mt, v[i]);
+  for (int j = 0; j < 4; ++j) v[j] = j < lim && (!LOWER || j >= llim) ? S[j] * c : -INFINITY;
+  const float mt = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
   st.mrun = fmaxf(st.mrun, mt);
   st.redo |= mt - st.mref > 64.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    v[i] = __builtin_amdgcn_exp2f(v[i] - st.mref);
-    st.l += v[i];
-    P[i] = (bf16_t)v[i];
+  for (int j = 0; j < 4; ++j) {
+    v[j] = __builtin_amdgcn_exp2f(v[j] - st.mref);
+    st.l += v[j];
+    P[j] = (bf16_t)v[j];
   }
 }
 
@@ -180,16 +178,20 @@ __device__ __forceinline__ uint32_t lds_u32(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
 
-// Shared head block (heads 64..79): its 36 score MFMAs per tile are split over the waves, wave
-// ROLE taking key block ROLE / 2 and k-steps 9 (ROLE % 2) .. + 8 with the fragments it reads for its
-// own block anyway; the partial sums meet in LDS and every wave then takes the same softmax of the
-// whole block (so its P^T needs no further exchange).
+// Scores: wave w takes the keys of key block KB = w % 2 (16 of the tile's 32) for head blocks
+// 2 (w / 2) and 2 (w / 2) + 1, so each wave reads half of the tile's rows once and applies every
+// fragment to two head blocks.  Shared head block (heads 64..79): its 36 score MFMAs per tile are
+// split over the waves, wave w taking key block w % 2 and k-steps 9 (w / 2) .. + 8 with the
+// fragments it reads anyway; the partial sums meet in LDS and every wave then takes the same
+// softmax of the whole block (so its P^T needs no further exchange).
 constexpr int K4N = NKST / 2;  // k-steps of the shared block per wave (9)
 
 template <bool SHARED, bool PAGED, bool LOWER, int ROLE>
 __device__ __forceinline__ void decode_body(const DecodeArgs &a, bf16_t *CB, bf16x8 (*PB)[64], f32x4 (*S4B)[64],
                                             int32_t *PG, int wave) {
-  constexpr int KB4 = ROLE >> 1, K4LO = (ROLE & 1) * K4N;
+  // ROLE = wave: key block KB of the scores, head blocks 2 HP and 2 HP + 1, k-steps K4LO .. of the
+  // shared block
+  constexpr int KB = ROLE & 1, HP = ROLE >> 1, K4LO = HP * K4N;
   const int lane = threadIdx.x & 63;
   int b, tok, sp;
   decode_unit(a, b, tok, sp);
@@ -204,19 +206,23 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, bf16_t *CB, bf1
   const int k_begin = kbase + sp * kps, k_end = min(p + 1, k_begin + kps);
   const int ntiles = k_end > k_begin ? (k_end - k_begin + KT - 1) / KT : 0;
   const int col = lane & 15, g = lane >> 4;
-  const int head = 16 * wave + col, head4 = 16 * MAX_WAVES + col;
-  const bool head_ok = head < a.n_heads, head4_ok = SHARED && head4 < a.n_heads;
+  const int head4 = 16 * MAX_WAVES + col;
+  const bool head4_ok = SHARED && head4 < a.n_heads;
 
-  // q~ fragments (B operand): Qf[kst] = dims 32 kst + 8 g .. + 7 of head `head`; Q4[k] those of
-  // head `head4` at k-step K4LO + k
-  bf16x8 Qf[NKST], Q4[SHARED ? K4N : 1];
+  // q~ fragments (B operand): Qf[i][kst] = dims 32 kst + 8 g .. + 7 of head 16 (2 HP + i) + col;
+  // Q4[k] those of head `head4` at k-step K4LO + k
+  bf16x8 Qf[2][NKST], Q4[SHARED ? K4N : 1];
   {
     const bf16_t *qb = a.qabs + (int64_t)v * a.n_heads * ROW + 8 * g;
-    const bf16_t *qp = qb + (int64_t)(head_ok ? head : 0) * ROW;
 #pragma unroll
-    for (int k = 0; k < NKST; ++k) {
-      Qf[k] = *(const bf16x8 *)(qp + 32 * k);
-      if (!head_ok) Qf[k] = bf16x8{};
+    for (int i = 0; i < 2; ++i) {
+      const int head = 16 * (2 * HP + i) + col;
+      const bf16_t *qp = qb + (int64_t)(head < a.n_heads ? head : 0) * ROW;
+#pragma unroll
+      for (int k = 0; k < NKST; ++k) {
+        Qf[i][k] = *(const bf16x8 *)(qp + 32 * k);
+        if (head >= a.n_heads) Qf[i][k] = bf16x8{};
+      }
     }
     if (SHARED) {
       const bf16_t *q4 = qb + (int64_t)(head4_ok ? head4 : 0) * ROW;
@@ -298,14 +304,14 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, bf16_t *CB, bf1
   for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
     for (int d = 0; d < WDB; ++d) O[hb][d] = f32x4{};
-  SoftmaxState st, st4;
+  SoftmaxState st[2], st4;  // head blocks 2 HP + i over this wave's keys; the shared block
   int pass = 0;
 
   // Lane-dependent byte offsets of the LDS reads; everything else is an immediate.
-  // S phase: row 16 kb + col, logical chunk 4 kst + g; swz(row) = swz(col) for every kb.
+  // S phase: row 16 KB + col, logical chunk 4 kst + g; swz(row) = swz(col).
   int offS[2];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) offS[q] = col * RB + (((4 * q + g) ^ swz(col)) * 16);
+  for (int q = 0; q < 2; ++q) offS[q] = (16 * KB + col) * RB + (((4 * q + g) ^ swz(col)) * 16);
   // PV phase: lane (g, jj, qq) of a transposing read addresses row 16 hi + 4 g + jj and dims
   // 16 d + 4 qq .. + 3 with d = WDB wave + dd, i.e. logical chunk 16 wave + 2 dd + (qq >> 1), half
   // qq & 1; swz(row) = swz(4 g + jj) and the XOR only touches the low 3 bits of the chunk.
@@ -320,42 +326,46 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, bf16_t *CB, bf1
   auto compute = [&](const bf16_t *cs, int s0) {
     const char *cbyte = (const char *)cs;
     f32x4 S[2], S4p;
-    // S phase, key block by key block, software-pipelined two k-steps ahead:
-    // [reads of step n + 2][MFMAs of step n]; the own block and this wave's part of the shared
-    // block use the same fragment
+    // S phase over this wave's 16 keys, software-pipelined two k-steps ahead:
+    // [read of step n + 2][MFMAs of step n]; both own head blocks and this wave's part of the
+    // shared block use the same fragment
     bf16x8 af[3];
-    auto ldA = [&](bf16x8 &f, int n) {  // n = 18 kb + kst
-      const int kb = n / NKST, kst = n % NKST;
-      f = *(const bf16x8 *)(cbyte + offS[kst & 1] + kb * 16 * RB + (kst >> 1) * 128);
-    };
+    auto ldA = [&](bf16x8 &f, int kst) { f = *(const bf16x8 *)(cbyte + offS[kst & 1] + (kst >> 1) * 128); };
     ldA(af[0], 0);
     ldA(af[1], 1);
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-    for (int n = 0; n < 2 * NKST; ++n) {
-      const int kb = n / NKST, kst = n % NKST;
-      if (n + 2 < 2 * NKST) ldA(af[(n + 2) % 3], n + 2);
-      const bool part4 = SHARED && kb == KB4 && kst >= K4LO && kst < K4LO + K4N;
-      S[kb] = mfma16(af[n % 3], Qf[kst], kst == 0 ? f32x4{} : S[kb]);
-      if (part4) S4p = mfma16(af[n % 3], Q4[kst - K4LO], kst == K4LO ? f32x4{} : S4p);
-      if (n + 2 < 2 * NKST) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (part4) __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      else __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    for (int kst = 0; kst < NKST; ++kst) {
+      if (kst + 2 < NKST) ldA(af[(kst + 2) % 3], kst + 2);
+      const bool part4 = SHARED && kst >= K4LO && kst < K4LO + K4N;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) S[i] = mfma16(af[kst % 3], Qf[i][kst], kst == 0 ? f32x4{} : S[i]);
+      if (part4) S4p = mfma16(af[kst % 3], Q4[kst - K4LO], kst == K4LO ? f32x4{} : S4p);
+      if (kst + 2 < NKST) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (part4) __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+      else __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
-    bf16x8 P;
     const int lim = k_end - s0 - 4 * g, llim = lo - s0 - 4 * g;
-    softmax_tile<LOWER>(S, st, llim, lim, a.c, P);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      bf16x4 P;
+      softmax_keys16<LOWER>(S[i], st[i], llim - 16 * KB, lim - 16 * KB, a.c, P);
+      *((bf16x4 *)&PB[2 * HP + i][lane] + KB) = P;
+    }
     if (SHARED) S4B[wave][lane] = S4p;
-    PB[wave][lane] = P;
     __syncthreads();  // P^T of blocks 0..3 and the shared block's partial scores visible to every wave
     bf16x8 PH[HB];
 #pragma unroll
     for (int hb = 0; hb < MAX_WAVES; ++hb) PH[hb] = PB[hb][lane];
     if (SHARED) {
-      f32x4 S4[2];
-      S4[0] = S4B[0][lane] + S4B[1][lane];
-      S4[1] = S4B[2][lane] + S4B[3][lane];
-      softmax_tile<LOWER>(S4, st4, llim, lim, a.c, PH[HB - 1]);
+      // key block kb of the shared block: k-steps 0..8 from wave kb, 9..17 from wave kb + 2
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        bf16x4 P;
+        softmax_keys16<LOWER>(S4B[kb][lane] + S4B[kb + 2][lane], st4, llim - 16 * kb, lim - 16 * kb, a.c, P);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) PH[HB - 1][4 * kb + j] = P[j];
+      }
     }
     // PV phase over this wave's dim blocks, pipelined two ahead: [reads of dd + 2][MFMAs of dd]
     bf16x8 vf[3];
@@ -394,19 +404,42 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, bf16_t *CB, bf1
       if (t + NBUF - 1 < ntiles) issue(t + NBUF - 1);
       compute(CB + (t % NBUF) * TILE, k_begin + t * KT);
     }
-    __syncthreads();
-    // reduce the per-lane maxima over the 4 lanes of each head; check for underflow
-    st.mrun = head_max(st.mrun);
-    st.redo |= ntiles > 0 && st.mrun - st.mref < -64.0f;
+    __syncthreads();  // every wave is done with the last tile (and with S4B)
+    // reduce the per-lane maxima and sums over the 4 lanes of each head, then over the two waves
+    // that hold the two key blocks of the same heads (waves w and w ^ 1, through S4B); check for
+    // underflow against the maximum over all keys
+    {
+      f32x4 x;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        x[i] = head_max(st[i].mrun);
+        x[2 + i] = head_sum(st[i].l);
+      }
+      S4B[wave][lane] = x;
+      __syncthreads();
+      const f32x4 y = S4B[wave ^ 1][lane];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        st[i].mrun = fmaxf(x[i], y[i]);
+        st[i].l = x[2 + i] + y[2 + i];
+      }
+    }
+    bool redo = false;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) redo |= st[i].redo || (ntiles > 0 && st[i].mrun - st[i].mref < -64.0f);
     if (SHARED) {
       st4.mrun = head_max(st4.mrun);
       st4.redo |= ntiles > 0 && st4.mrun - st4.mref < -64.0f;
+      redo |= st4.redo;
     }
-    if (pass == 1 || !__syncthreads_or(st.redo || st4.redo)) break;
+    if (pass == 1 || !__syncthreads_or(redo)) break;
     // second pass against the exact maximum
     pass = 1;
-    st.mref = st.mrun;
-    st.l = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      st[i].mref = st[i].mrun;
+      st[i].l = 0.f;
+    }
     st4.mref = st4.mrun;
     st4.l = 0.f;
 #pragma unroll
@@ -415,12 +448,16 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, bf16_t *CB, bf1
       for (int d = 0; d < WDB; ++d) O[hb][d] = f32x4{};
   }
 
-  // (m, l) of head block hb come from the wave that owns its scores (wave 0 for block 4)
-  const float lt = head_sum(st.l);
-  if (head_ok && g == 0) {
-    const int64_t ph = ((int64_t)v * a.splits + sp) * a.n_heads + head;
-    a.part_ml[ph * 2] = ntiles > 0 ? st.mref : -INFINITY;
-    a.part_ml[ph * 2 + 1] = lt;
+  // (m, l) of head blocks 0..3 come from the waves of key block 0 (st[i].l already holds the
+  // sum over both key blocks), those of block 4 from wave 0
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int head = 16 * (2 * HP + i) + col;
+    if (KB == 0 && head < a.n_heads && g == 0) {
+      const int64_t ph = ((int64_t)v * a.splits + sp) * a.n_heads + head;
+      a.part_ml[ph * 2] = ntiles > 0 ? st[i].mref : -INFINITY;
+      a.part_ml[ph * 2 + 1] = st[i].l;
+    }
   }
   if (SHARED) {
     const float lt4 = head_sum(st4.l);
@@ -454,15 +491,11 @@ __global__ void __launch_bounds__(256, 1) latent_decode_kernel(DecodeArgs a) {
     int b, tok, sp;
     if (!decode_unit(a, b, tok, sp)) return;  // uniform over the workgroup, before any barrier
   }
-  if (!SHARED) {
-    decode_body<false, PAGED, LOWER, 0>(a, CB, PB, S4B, PG, wave);
-  } else {
-    switch (wave) {  // wave-uniform: each wave runs the code of its part of the shared block
-      case 0: decode_body<true, PAGED, LOWER, 0>(a, CB, PB, S4B, PG, 0); break;
-      case 1: decode_body<true, PAGED, LOWER, 1>(a, CB, PB, S4B, PG, 1); break;
-      case 2: decode_body<true, PAGED, LOWER, 2>(a, CB, PB, S4B, PG, 2); break;
-      default: decode_body<true, PAGED, LOWER, 3>(a, CB, PB, S4B, PG, 3); break;
-    }
+  switch (wave) {  // wave-uniform: each wave runs the code of its key block and head blocks
+    case 0: decode_body<SHARED, PAGED, LOWER, 0>(a, CB, PB, S4B, PG, 0); break;
+    case 1: decode_body<SHARED, PAGED, LOWER, 1>(a, CB, PB, S4B, PG, 1); break;
+    case 2: decode_body<SHARED, PAGED, LOWER, 2>(a, CB, PB, S4B, PG, 2); break;
+    default: decode_body<SHARED, PAGED, LOWER, 3>(a, CB, PB, S4B, PG, 3); break;
   }
 }
 
