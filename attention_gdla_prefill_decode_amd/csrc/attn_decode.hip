@@ -33,6 +33,7 @@
 #include "fast_paths.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace gdla {
 namespace {
@@ -163,14 +164,21 @@ __device__ __forceinline__ void softmax_keys16(f32x4 S, SoftmaxState &st, int ll
   }
 }
 
-// 16 bytes global -> LDS (M0 + 16 lane) without the compiler's LDS-DMA tracking: the waits for
+// 16 bytes global (wave-uniform base + this lane's 32-bit byte offset) -> LDS (M0 + 16 lane),
+// without the compiler's LDS-DMA tracking: the waits for
 // these loads are explicit (s_waitcnt vmcnt before the barrier that publishes a tile).  M0 is set
 // right before the load (one wait state between them); nothing else in the kernel uses M0.  The
 // cache rows are read once per call, so the loads are non-temporal (nt): about 2% faster here.
-__device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+__device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds_addr) {
+  // readfirstlane returns int: each half goes through uint32_t, or the low half would be
+  // sign-extended into the high one
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  const uint64_t sbase = (uint64_t)hi << 32 | (uint64_t)lo;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                :
-               : "v"(gptr), "s"(lds_addr)
+               : "v"(voff), "s"(sbase), "s"(lds_addr)
                : "memory");
 }
 
@@ -178,20 +186,28 @@ __device__ __forceinline__ uint32_t lds_u32(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
 
-// Scores: wave w takes the keys of key block KB = w % 2 (16 of the tile's 32) for head blocks
-// 2 (w / 2) and 2 (w / 2) + 1, so each wave reads half of the tile's rows once and applies every
-// fragment to two head blocks.  Shared head block (heads 64..79): its 36 score MFMAs per tile are
-// split over the waves, wave w taking key block w % 2 and k-steps 9 (w / 2) .. + 8 with the
-// fragments it reads anyway; the partial sums meet in LDS and every wave then takes the same
-// softmax of the whole block (so its P^T needs no further exchange).
-constexpr int K4N = NKST / 2;  // k-steps of the shared block per wave (9)
+// Two kinds of waves share each SIMD, and the tile loop is pipelined across them: while the score
+// waves compute the probabilities of tile t + 1, the value waves accumulate tile t, so each SIMD
+// interleaves two independent instruction streams on its matrix core and one hides the other's
+// LDS and MFMA latencies.  Both kinds issue about the same number of MFMAs per tile.
+//   Score wave w (0..3): the keys of key block KB = w % 2 (16 of the tile's 32) for head blocks
+//     2 (w / 2) and 2 (w / 2) + 1, so every cache fragment it reads from LDS feeds two MFMAs; with
+//     five head blocks also k-steps 9 (w / 2) .. + 8 of the shared block (heads 64..79) for its
+//     keys, whose partial sums meet in LDS.  Holds q~ of its blocks in registers.
+//   Value wave w (4..7): output dims 128 (w - 4) .. + 127 of every head block (accumulators in
+//     registers), so it transposes only a quarter of the tile; takes the shared block's softmax
+//     from the partial sums; issues the tile loads.
+constexpr int K4N = NKST / 2;  // k-steps of the shared block per score wave (9)
+constexpr int NWAVES = 2 * MAX_WAVES;
 
 template <bool SHARED, bool PAGED, bool LOWER, int ROLE>
-__device__ __forceinline__ void decode_body(const DecodeArgs &a, bf16_t *CB, bf16x8 (*PB)[64], f32x4 (*S4B)[64],
-                                            int32_t *PG, int wave) {
-  // ROLE = wave: key block KB of the scores, head blocks 2 HP and 2 HP + 1, k-steps K4LO .. of the
-  // shared block
-  constexpr int KB = ROLE & 1, HP = ROLE >> 1, K4LO = HP * K4N;
+__device__ __forceinline__ void decode_body(const DecodeArgs &a, bf16_t *CB, bf16x8 (*PB)[MAX_WAVES][64],
+                                            f32x4 (*S4B)[MAX_WAVES][64], int32_t *PG) {
+  constexpr bool SW = ROLE < MAX_WAVES;                  // score wave
+  constexpr int KB = ROLE & 1, HP = (ROLE >> 1) & 1;     // score wave: key block, head-block pair
+  constexpr int K4LO = HP * K4N;
+  constexpr int VW = ROLE - MAX_WAVES;                   // value wave: dims 16 WDB VW ..
+  constexpr int HB = SHARED ? NHB : MAX_WAVES;
   const int lane = threadIdx.x & 63;
   int b, tok, sp;
   decode_unit(a, b, tok, sp);
@@ -207,12 +223,11 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, bf16_t *CB, bf1
   const int ntiles = k_end > k_begin ? (k_end - k_begin + KT - 1) / KT : 0;
   const int col = lane & 15, g = lane >> 4;
   const int head4 = 16 * MAX_WAVES + col;
-  const bool head4_ok = SHARED && head4 < a.n_heads;
 
-  // q~ fragments (B operand): Qf[i][kst] = dims 32 kst + 8 g .. + 7 of head 16 (2 HP + i) + col;
-  // Q4[k] those of head `head4` at k-step K4LO + k
-  bf16x8 Qf[2][NKST], Q4[SHARED ? K4N : 1];
-  {
+  // Score wave: q~ fragments (B operand): Qf[i][kst] = dims 32 kst + 8 g .. + 7 of head
+  // 16 (2 HP + i) + col; Q4[k] those of head `head4` at k-step K4LO + k
+  bf16x8 Qf[SW ? 2 : 1][SW ? NKST : 1], Q4[SW && SHARED ? K4N : 1];
+  if constexpr (SW) {
     const bf16_t *qb = a.qabs + (int64_t)v * a.n_heads * ROW + 8 * g;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -225,6 +240,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, bf16_t *CB, bf1
       }
     }
     if (SHARED) {
+      const bool head4_ok = head4 < a.n_heads;
       const bf16_t *q4 = qb + (int64_t)(head4_ok ? head4 : 0) * ROW;
 #pragma unroll
       for (int k = 0; k < K4N; ++k) {
@@ -232,11 +248,21 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, bf16_t *CB, bf1
         if (!head4_ok) Q4[k] = bf16x8{};
       }
     }
+    // Wait for these loads here: a wait the compiler placed at their first use inside the tile
+    // loop would count only its own loads (vmcnt(0)) and so also drain the tile loads in flight.
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int k = 0; k < NKST; ++k) asm volatile("" : "+v"(Qf[i][k]));
+    if (SHARED)
+#pragma unroll
+      for (int k = 0; k < K4N; ++k) asm volatile("" : "+v"(Q4[k]));
   }
 
   // PAGED: the physical pages of the split's blocks are copied to LDS once (when there are at
-  // most PG_CAP of them), so a tile's page costs an LDS read, not a scalar memory load (whose wait
-  // the compiler would merge with the next LDS wait of the tile loop).
+  // most PG_CAP of them and the LDS has room: four head blocks), so a tile's page costs an LDS
+  // read, not a scalar memory load (whose wait the compiler would merge with the next LDS wait of
+  // the tile loop).
   const CacheRef &cr = a.cache;
   const bf16_t *cb = (const bf16_t *)cr.base + (PAGED ? 0 : (int64_t)b * cr.max_len * ROW);
   int blk0 = 0;
@@ -244,10 +270,10 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, bf16_t *CB, bf1
   if (PAGED) {
     blk0 = k_begin / cr.page_rows;
     const int nblk = ntiles > 0 ? (k_begin + ntiles * KT - 1) / cr.page_rows - blk0 + 1 : 0;
-    pg_lds = nblk > 0 && nblk <= PG_CAP;
+    pg_lds = !SHARED && nblk > 0 && nblk <= PG_CAP;
     if (pg_lds) {
       const int32_t *bt = cr.block_table + (int64_t)b * cr.max_blocks + blk0;
-      for (int i = threadIdx.x; i < nblk; i += 64 * MAX_WAVES) PG[i] = min(max(bt[i], 0), cr.n_pages - 1);
+      for (int i = threadIdx.x; i < nblk; i += 64 * NWAVES) PG[i] = min(max(bt[i], 0), cr.n_pages - 1);
     }
     __syncthreads();
   }
@@ -264,47 +290,62 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, bf16_t *CB, bf1
     }
     return r;
   };
-  // Tile t goes to ring slot t % NBUF; wave w issues wave-instructions w, w + 4, ... of the tile
-  // (DMA_PER_WAVE of them).  rowoff[i] is this lane's source offset (bytes) inside the tile.
-  // Keys past k_end (and, paged, before lo) are read from row k_end - 1 (lo) instead: masked later,
-  // and never a row outside the visible range, which a paged cache may no longer map.
+  // Value waves load the tiles: tile t goes to ring slot t % NBUF, value wave VW issuing
+  // wave-instructions VW, VW + 4, ... of the tile (DMA_PER_WAVE of them).  rowoff(i) is this lane's
+  // source offset (bytes) inside the tile, recomputed at each tile (a few VALU operations; kept in
+  // registers the offsets would cost nine of them).  Keys past k_end (and, paged, before lo) are
+  // read from row k_end - 1 (lo) instead: masked later, and never a row outside the visible range,
+  // which a paged cache may no longer map.
   const uint32_t ring = lds_u32(CB);
-  int rowoff[DMA_PER_WAVE];
-#pragma unroll
-  for (int i = 0; i < DMA_PER_WAVE; ++i) {
-    const int sl = (wave + MAX_WAVES * i) * 64 + lane;
-    const int row = sl / RCH;
-    rowoff[i] = row * RB + (((sl % RCH) ^ swz(row)) * 16);
-  }
   // first cache row of the next tile to issue (one block-table lookup ahead when paged)
   int64_t row_next = 0;
   auto issue = [&](int t) {
-    const int s0 = k_begin + t * KT;
-    const uint32_t base = ring + (uint32_t)((t % NBUF) * TILE * 2) + wave * 1024;
-    const char *src = (const char *)(cb + (PAGED ? row_next : (int64_t)s0) * ROW);
-    if (PAGED && t + 1 < ntiles) row_next = tile_row(s0 + KT);
-    if ((!PAGED || s0 >= lo) && s0 + KT <= k_end) {
+    if constexpr (!SW) {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));  // keeps the offsets below inside the loop
+      auto rowoff = [&](int i) {
+        const int sl = (VW + MAX_WAVES * i) * 64 + ln;
+        const int row = sl / RCH;
+        return row * RB + (((sl - row * RCH) ^ swz(row)) * 16);
+      };
+      const int s0 = k_begin + t * KT;
+      const uint32_t base = ring + (uint32_t)((t % NBUF) * TILE * 2) + VW * 1024;
+      const char *src = (const char *)(cb + (PAGED ? row_next : (int64_t)s0) * ROW);
+      if (PAGED && t + 1 < ntiles) row_next = tile_row(s0 + KT);
+      if ((!PAGED || s0 >= lo) && s0 + KT <= k_end) {
 #pragma unroll
-      for (int i = 0; i < DMA_PER_WAVE; ++i)
-        dma16(src + rowoff[i], __builtin_amdgcn_readfirstlane(base + i * MAX_WAVES * 1024));
-    } else {
+        for (int i = 0; i < DMA_PER_WAVE; ++i)
+          dma16(src, rowoff(i), __builtin_amdgcn_readfirstlane(base + i * MAX_WAVES * 1024));
+      } else {
 #pragma unroll
-      for (int i = 0; i < DMA_PER_WAVE; ++i) {
-        const int row = rowoff[i] / RB;
-        const int off = rowoff[i] - row * RB + (min(PAGED ? max(s0 + row, lo) : s0 + row, k_end - 1) - s0) * RB;
-        dma16(src + off, __builtin_amdgcn_readfirstlane(base + i * MAX_WAVES * 1024));
+        for (int i = 0; i < DMA_PER_WAVE; ++i) {
+          const int ro = rowoff(i), row = ro / RB;
+          const int off = ro - row * RB + (min(PAGED ? max(s0 + row, lo) : s0 + row, k_end - 1) - s0) * RB;
+          dma16(src, off, __builtin_amdgcn_readfirstlane(base + i * MAX_WAVES * 1024));
+        }
       }
     }
   };
+  // vmcnt(n): at most n of this wave's tile loads still in flight (n = 0, one tile, two tiles)
+  auto wait_tiles_after = [&](int n_after) {
+    if constexpr (!SW) {
+      if (n_after >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DMA_PER_WAVE) : "memory");
+      else if (n_after == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_PER_WAVE) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+  };
 
-  // O[hb][dd] = O^T[dims 16 (WDB wave + dd) + 4 g + j][heads 16 hb + col]
-  constexpr int HB = SHARED ? NHB : MAX_WAVES;
-  f32x4 O[HB][WDB];
+  // Value wave: O[hb][dd] = O^T[dims 16 (WDB VW + dd) + 4 g + j][heads 16 hb + col]
+  f32x4 O[SW ? 1 : HB][SW ? 1 : WDB];
+  auto clear_o = [&]() {
+    if constexpr (!SW) {
 #pragma unroll
-  for (int hb = 0; hb < HB; ++hb)
+      for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-    for (int d = 0; d < WDB; ++d) O[hb][d] = f32x4{};
-  SoftmaxState st[2], st4;  // head blocks 2 HP + i over this wave's keys; the shared block
+        for (int d = 0; d < WDB; ++d) O[hb][d] = f32x4{};
+    }
+  };
+  SoftmaxState st[2], st4;  // score wave: head blocks 2 HP + i over its keys; value wave: shared block
   int pass = 0;
 
   // Lane-dependent byte offsets of the LDS reads; everything else is an immediate.
@@ -313,126 +354,150 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, bf16_t *CB, bf1
 #pragma unroll
   for (int q = 0; q < 2; ++q) offS[q] = (16 * KB + col) * RB + (((4 * q + g) ^ swz(col)) * 16);
   // PV phase: lane (g, jj, qq) of a transposing read addresses row 16 hi + 4 g + jj and dims
-  // 16 d + 4 qq .. + 3 with d = WDB wave + dd, i.e. logical chunk 16 wave + 2 dd + (qq >> 1), half
+  // 16 d + 4 qq .. + 3 with d = WDB VW + dd, i.e. logical chunk 16 VW + 2 dd + (qq >> 1), half
   // qq & 1; swz(row) = swz(4 g + jj) and the XOR only touches the low 3 bits of the chunk.
   const int jj = (lane & 15) >> 2, qq = lane & 3;
   int offP[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int r = 4 * g + jj;
-    offP[q] = r * RB + wave * (2 * WDB * 16) + (((2 * q + (qq >> 1)) ^ swz(r)) * 16) + (qq & 1) * 8;
+    offP[q] = r * RB + (SW ? 0 : VW) * (2 * WDB * 16) + (((2 * q + (qq >> 1)) ^ swz(r)) * 16) + (qq & 1) * 8;
   }
 
-  auto compute = [&](const bf16_t *cs, int s0) {
-    const char *cbyte = (const char *)cs;
-    f32x4 S[2], S4p;
-    // S phase over this wave's 16 keys, software-pipelined two k-steps ahead:
-    // [read of step n + 2][MFMAs of step n]; both own head blocks and this wave's part of the
-    // shared block use the same fragment
-    bf16x8 af[3];
-    auto ldA = [&](bf16x8 &f, int kst) { f = *(const bf16x8 *)(cbyte + offS[kst & 1] + (kst >> 1) * 128); };
-    ldA(af[0], 0);
-    ldA(af[1], 1);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  // Score wave, tile at c (keys s0 ..): S phase over its 16 keys, software-pipelined two k-steps
+  // ahead ([read of step n + 2][MFMAs of step n]; both own head blocks and its part of the shared
+  // block use the same fragment), then the softmax; its halves of P^T (and its partial scores of
+  // the shared block) go to exchange buffer `buf`.
+  auto score_tile = [&](const char *c, int s0, int buf) {
+    if constexpr (SW) {
+      f32x4 S[2], S4p;
+      bf16x8 af[3];
+      auto ldA = [&](bf16x8 &f, int kst) { f = *(const bf16x8 *)(c + offS[kst & 1] + (kst >> 1) * 128); };
+      ldA(af[0], 0);
+      ldA(af[1], 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-    for (int kst = 0; kst < NKST; ++kst) {
-      if (kst + 2 < NKST) ldA(af[(kst + 2) % 3], kst + 2);
-      const bool part4 = SHARED && kst >= K4LO && kst < K4LO + K4N;
+      for (int kst = 0; kst < NKST; ++kst) {
+        if (kst + 2 < NKST) ldA(af[(kst + 2) % 3], kst + 2);
+        const bool part4 = SHARED && kst >= K4LO && kst < K4LO + K4N;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) S[i] = mfma16(af[kst % 3], Qf[i][kst], kst == 0 ? f32x4{} : S[i]);
-      if (part4) S4p = mfma16(af[kst % 3], Q4[kst - K4LO], kst == K4LO ? f32x4{} : S4p);
-      if (kst + 2 < NKST) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (part4) __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
-      else __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    }
-    const int lim = k_end - s0 - 4 * g, llim = lo - s0 - 4 * g;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      bf16x4 P;
-      softmax_keys16<LOWER>(S[i], st[i], llim - 16 * KB, lim - 16 * KB, a.c, P);
-      *((bf16x4 *)&PB[2 * HP + i][lane] + KB) = P;
-    }
-    if (SHARED) S4B[wave][lane] = S4p;
-    __syncthreads();  // P^T of blocks 0..3 and the shared block's partial scores visible to every wave
-    bf16x8 PH[HB];
-#pragma unroll
-    for (int hb = 0; hb < MAX_WAVES; ++hb) PH[hb] = PB[hb][lane];
-    if (SHARED) {
-      // key block kb of the shared block: k-steps 0..8 from wave kb, 9..17 from wave kb + 2
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        bf16x4 P;
-        softmax_keys16<LOWER>(S4B[kb][lane] + S4B[kb + 2][lane], st4, llim - 16 * kb, lim - 16 * kb, a.c, P);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) PH[HB - 1][4 * kb + j] = P[j];
+        for (int i = 0; i < 2; ++i) S[i] = mfma16(af[kst % 3], Qf[i][kst], kst == 0 ? f32x4{} : S[i]);
+        if (part4) S4p = mfma16(af[kst % 3], Q4[kst - K4LO], kst == K4LO ? f32x4{} : S4p);
+        if (kst + 2 < NKST) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (part4) __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+        else __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
+      const int lim = k_end - s0 - 4 * g - 16 * KB, llim = lo - s0 - 4 * g - 16 * KB;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        bf16x4 P;
+        softmax_keys16<LOWER>(S[i], st[i], llim, lim, a.c, P);
+        *((bf16x4 *)&PB[buf][2 * HP + i][lane] + KB) = P;
+      }
+      if (SHARED) S4B[buf][ROLE][lane] = S4p;
     }
-    // PV phase over this wave's dim blocks, pipelined two ahead: [reads of dd + 2][MFMAs of dd]
-    bf16x8 vf[3];
-    auto ldV = [&](bf16x8 &f, int dd) {
-      const char *p0 = cbyte + offP[dd & 3] + (dd >> 2) * 128;
-      const bf16x4 lo4 = tr_read(p0);
-      const bf16x4 hi4 = tr_read(p0 + 16 * RB);
-      f = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-    };
-    ldV(vf[0], 0);
-    ldV(vf[1], 1);
+  };
+  // Value wave, tile at c (keys s0 ..), after the barrier that published buffer `buf`: P^T of
+  // every head block (the shared block's from its two partial sums per key block, the same
+  // softmax in every value wave), then the PV phase over its dims, pipelined two ahead:
+  // [reads of dd + 2][MFMAs of dd].
+  auto value_tile = [&](const char *c, int s0, int buf) {
+    if constexpr (!SW) {
+      bf16x8 PH[HB];
 #pragma unroll
-    for (int dd = 0; dd < WDB; ++dd) {
-      if (dd + 2 < WDB) ldV(vf[(dd + 2) % 3], dd + 2);
+      for (int hb = 0; hb < MAX_WAVES; ++hb) PH[hb] = PB[buf][hb][lane];
+      if (SHARED) {
+        const int lim = k_end - s0 - 4 * g, llim = lo - s0 - 4 * g;
+        // key block kb of the shared block: k-steps 0..8 from score wave kb, 9..17 from kb + 2
 #pragma unroll
-      for (int hb = 0; hb < HB; ++hb) O[hb][dd] = mfma16(vf[dd % 3], PH[hb], O[hb][dd]);
+        for (int kb = 0; kb < 2; ++kb) {
+          bf16x4 P;
+          softmax_keys16<LOWER>(S4B[buf][kb][lane] + S4B[buf][kb + 2][lane], st4, llim - 16 * kb, lim - 16 * kb,
+                                a.c, P);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) PH[HB - 1][4 * kb + j] = P[j];
+        }
+      }
+      bf16x8 vf[3];
+      auto ldV = [&](bf16x8 &f, int dd) {
+        const char *p0 = c + offP[dd & 3] + (dd >> 2) * 128;
+        const bf16x4 lo4 = tr_read(p0);
+        const bf16x4 hi4 = tr_read(p0 + 16 * RB);
+        f = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      ldV(vf[0], 0);
+      ldV(vf[1], 1);
+#pragma unroll
+      for (int dd = 0; dd < WDB; ++dd) {
+        if (dd + 2 < WDB) ldV(vf[(dd + 2) % 3], dd + 2);
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) O[hb][dd] = mfma16(vf[dd % 3], PH[hb], O[hb][dd]);
+      }
     }
   };
 
-  // vmcnt(n): at most n of this wave's loads still in flight (n = 0, one tile, two tiles)
-  auto wait_tiles_after = [&](int n_after) {
-    if (n_after >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * DMA_PER_WAVE) : "memory");
-    else if (n_after == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_PER_WAVE) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  };
+  // Tile t sits in ring slot t % NBUF.  Iteration t: the value waves accumulate tile t, the score
+  // waves take the probabilities of tile t + 1, and the loads of tiles t + 2 and t + 3 are in
+  // flight.  The barrier at its top publishes tile t + 1 and the probabilities of tile t, and
+  // frees the slot of tile t - 1 (and exchange buffer (t + 1) % 2) for reuse.
+  auto slot = [&](int t) { return (const char *)(CB + (t % NBUF) * TILE); };
   for (;;) {
+    clear_o();
     if (PAGED && ntiles > 0) {
       blk = blk0;
       off = k_begin - blk0 * cr.page_rows;
       row_next = tile_row(k_begin);
     }
     for (int t = 0; t < NBUF - 1 && t < ntiles; ++t) issue(t);
-    for (int t = 0; t < ntiles; ++t) {
-      wait_tiles_after(min(ntiles - 1 - t, NBUF - 2));
-      __syncthreads();  // tile t has landed for every wave; every wave is done with tile t - 1
-      if (t + NBUF - 1 < ntiles) issue(t + NBUF - 1);
-      compute(CB + (t % NBUF) * TILE, k_begin + t * KT);
+    if (ntiles > 0) {
+      wait_tiles_after(min(ntiles - 1, NBUF - 2));
+      __syncthreads();  // tile 0 has landed
+      score_tile(slot(0), k_begin, 0);
     }
-    __syncthreads();  // every wave is done with the last tile (and with S4B)
-    // reduce the per-lane maxima and sums over the 4 lanes of each head, then over the two waves
-    // that hold the two key blocks of the same heads (waves w and w ^ 1, through S4B); check for
-    // underflow against the maximum over all keys
-    {
-      f32x4 x;
+    for (int t = 0; t < ntiles; ++t) {
+      if (t + 1 < ntiles) wait_tiles_after(t + 2 < ntiles ? 1 : 0);  // tile t + 1 has landed
+      __syncthreads();
+      if (t + NBUF - 1 < ntiles) issue(t + NBUF - 1);
+      if (t + 1 < ntiles) score_tile(slot(t + 1), k_begin + (t + 1) * KT, (t + 1) & 1);
+      value_tile(slot(t), k_begin + t * KT, t & 1);
+    }
+    __syncthreads();  // every wave is done with the last tile and the exchange buffers
+    // Score waves: reduce the per-lane maxima and sums over the 4 lanes of each head, then over
+    // the two score waves that hold the two key blocks of the same heads (ROLE, ROLE ^ 1, through
+    // S4B).  Value waves: the shared block's maximum over the 4 lanes of each head.
+    f32x4 x;
+    if constexpr (SW) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         x[i] = head_max(st[i].mrun);
         x[2 + i] = head_sum(st[i].l);
       }
-      S4B[wave][lane] = x;
-      __syncthreads();
-      const f32x4 y = S4B[wave ^ 1][lane];
+      S4B[0][ROLE][lane] = x;
+    } else if (SHARED) {
+      st4.mrun = head_max(st4.mrun);
+    }
+    __syncthreads();
+    bool redo = false;
+    if constexpr (SW) {
+      const f32x4 y = S4B[0][ROLE ^ 1][lane];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         st[i].mrun = fmaxf(x[i], y[i]);
         st[i].l = x[2 + i] + y[2 + i];
+        redo |= st[i].redo || (ntiles > 0 && st[i].mrun - st[i].mref < -64.0f);
       }
+    } else if (SHARED) {
+      redo = st4.redo || (ntiles > 0 && st4.mrun - st4.mref < -64.0f);
     }
-    bool redo = false;
+    // workgroup vote through PB (idle until the next pass publishes its first tile, after a barrier)
+    int *vote = (int *)&PB[0][0][0];
+    const int wave_redo = __any(redo);  // over all lanes: taken before the one-lane branch
+    if (lane == 0) vote[ROLE] = wave_redo;
+    __syncthreads();
+    int any_redo = 0;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) redo |= st[i].redo || (ntiles > 0 && st[i].mrun - st[i].mref < -64.0f);
-    if (SHARED) {
-      st4.mrun = head_max(st4.mrun);
-      st4.redo |= ntiles > 0 && st4.mrun - st4.mref < -64.0f;
-      redo |= st4.redo;
-    }
-    if (pass == 1 || !__syncthreads_or(redo)) break;
+    for (int w = 0; w < NWAVES; ++w) any_redo |= vote[w];
+    if (pass == 1 || !any_redo) break;
     // second pass against the exact maximum
     pass = 1;
 #pragma unroll
@@ -442,60 +507,70 @@ __device__ __forceinline__ void decode_body(const DecodeArgs &a, bf16_t *CB, bf1
     }
     st4.mref = st4.mrun;
     st4.l = 0.f;
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-      for (int d = 0; d < WDB; ++d) O[hb][d] = f32x4{};
   }
 
-  // (m, l) of head blocks 0..3 come from the waves of key block 0 (st[i].l already holds the
-  // sum over both key blocks), those of block 4 from wave 0
+  if constexpr (SW) {
+    // (m, l) of head blocks 0..3 from the score waves of key block 0 (st[i].l holds the sum over
+    // both key blocks)
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int head = 16 * (2 * HP + i) + col;
-    if (KB == 0 && head < a.n_heads && g == 0) {
-      const int64_t ph = ((int64_t)v * a.splits + sp) * a.n_heads + head;
-      a.part_ml[ph * 2] = ntiles > 0 ? st[i].mref : -INFINITY;
-      a.part_ml[ph * 2 + 1] = st[i].l;
+    for (int i = 0; i < 2; ++i) {
+      const int head = 16 * (2 * HP + i) + col;
+      if (KB == 0 && head < a.n_heads && g == 0) {
+        const int64_t ph = ((int64_t)v * a.splits + sp) * a.n_heads + head;
+        a.part_ml[ph * 2] = ntiles > 0 ? st[i].mref : -INFINITY;
+        a.part_ml[ph * 2 + 1] = st[i].l;
+      }
     }
-  }
-  if (SHARED) {
-    const float lt4 = head_sum(st4.l);
-    if (head4_ok && wave == 0 && g == 0) {
-      const int64_t ph = ((int64_t)v * a.splits + sp) * a.n_heads + head4;
-      a.part_ml[ph * 2] = ntiles > 0 ? st4.mref : -INFINITY;
-      a.part_ml[ph * 2 + 1] = lt4;
+  } else {
+    // (m, l) of the shared block from value wave 0
+    if (SHARED) {
+      const float lt4 = head_sum(st4.l);
+      if (VW == 0 && head4 < a.n_heads && g == 0) {
+        const int64_t ph = ((int64_t)v * a.splits + sp) * a.n_heads + head4;
+        a.part_ml[ph * 2] = ntiles > 0 ? st4.mref : -INFINITY;
+        a.part_ml[ph * 2 + 1] = lt4;
+      }
     }
-  }
-  // this wave's dims of every head: O[hb][dd][j] = O^T[dim 16 (WDB wave + dd) + 4 g + j][16 hb + col]
+    // this wave's dims of every head: O[hb][dd][j] = O^T[dim 16 (WDB VW + dd) + 4 g + j][16 hb + col]
 #pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    const int h = 16 * hb + col;
-    if (h >= a.n_heads) continue;
-    float *po = a.part_o + (((int64_t)v * a.splits + sp) * a.n_heads + h) * DC + 16 * WDB * wave + 4 * g;
+    for (int hb = 0; hb < HB; ++hb) {
+      const int h = 16 * hb + col;
+      if (h >= a.n_heads) continue;
+      float *po = a.part_o + (((int64_t)v * a.splits + sp) * a.n_heads + h) * DC + 16 * WDB * VW + 4 * g;
 #pragma unroll
-    for (int dd = 0; dd < WDB; ++dd)
-      *(float4 *)(po + 16 * dd) = make_float4(O[hb][dd][0], O[hb][dd][1], O[hb][dd][2], O[hb][dd][3]);
+      for (int dd = 0; dd < WDB; ++dd)
+        *(float4 *)(po + 16 * dd) = make_float4(O[hb][dd][0], O[hb][dd][1], O[hb][dd][2], O[hb][dd][3]);
+    }
   }
 }
 
 // PAGED: paged cache; LOWER: with a window (paged tiles may then start below it)
 template <bool SHARED, bool PAGED, bool LOWER>
-__global__ void __launch_bounds__(256, 1) latent_decode_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(64 * NWAVES, 1) latent_decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t CB[NBUF * TILE];
-  __shared__ __attribute__((aligned(16))) bf16x8 PB[MAX_WAVES][64];   // P^T of head blocks 0..3
-  __shared__ __attribute__((aligned(16))) f32x4 S4B[MAX_WAVES][64];   // partial scores, shared block
-  __shared__ int32_t PG[PAGED ? PG_CAP : 1];                           // physical pages of the split
+  // Two exchange buffers each (tile t uses buffer t % 2): P^T of head blocks 0..3, and with five
+  // head blocks the partial scores of the shared block.  With four, S4B[0] serves only the final
+  // reduction and S4B[1] holds the split's physical pages when the cache is paged; with five the
+  // LDS is full (the ring and these buffers take all 160 KB), so a paged tile looks its page up in
+  // the block table.
+  __shared__ __attribute__((aligned(16))) bf16x8 PB[2][MAX_WAVES][64];
+  __shared__ __attribute__((aligned(16))) f32x4 S4B[2][MAX_WAVES][64];
+  static_assert(sizeof(S4B[1]) == PG_CAP * sizeof(int32_t), "page table slice fills one buffer");
+  int32_t *PG = PAGED && !SHARED ? (int32_t *)&S4B[1][0][0] : nullptr;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   {
     int b, tok, sp;
     if (!decode_unit(a, b, tok, sp)) return;  // uniform over the workgroup, before any barrier
   }
-  switch (wave) {  // wave-uniform: each wave runs the code of its key block and head blocks
-    case 0: decode_body<SHARED, PAGED, LOWER, 0>(a, CB, PB, S4B, PG, 0); break;
-    case 1: decode_body<SHARED, PAGED, LOWER, 1>(a, CB, PB, S4B, PG, 1); break;
-    case 2: decode_body<SHARED, PAGED, LOWER, 2>(a, CB, PB, S4B, PG, 2); break;
-    default: decode_body<SHARED, PAGED, LOWER, 3>(a, CB, PB, S4B, PG, 3); break;
+  switch (wave) {  // wave-uniform: each wave runs the code of its role
+    case 0: decode_body<SHARED, PAGED, LOWER, 0>(a, CB, PB, S4B, PG); break;
+    case 1: decode_body<SHARED, PAGED, LOWER, 1>(a, CB, PB, S4B, PG); break;
+    case 2: decode_body<SHARED, PAGED, LOWER, 2>(a, CB, PB, S4B, PG); break;
+    case 3: decode_body<SHARED, PAGED, LOWER, 3>(a, CB, PB, S4B, PG); break;
+    case 4: decode_body<SHARED, PAGED, LOWER, 4>(a, CB, PB, S4B, PG); break;
+    case 5: decode_body<SHARED, PAGED, LOWER, 5>(a, CB, PB, S4B, PG); break;
+    case 6: decode_body<SHARED, PAGED, LOWER, 6>(a, CB, PB, S4B, PG); break;
+    default: decode_body<SHARED, PAGED, LOWER, 7>(a, CB, PB, S4B, PG); break;
   }
 }
 
@@ -679,7 +754,7 @@ gdla_status run_fast_decode(const LayerDims &d, const gdla_weights *w, int32_t B
   se.begin(GDLA_STAGE_ATTN_NOISE);
   const dim3 grid((unsigned)decode_grid(B, T, L.splits));
   const bool shared = nblk > MAX_WAVES, paged = cache.page_rows > 0, lower = paged && d.window > 0;
-  const dim3 block(64 * MAX_WAVES);
+  const dim3 block(64 * NWAVES);
   if (shared && lower) hipLaunchKernelGGL((latent_decode_kernel<true, true, true>), grid, block, 0, s, a);
   else if (shared && paged) hipLaunchKernelGGL((latent_decode_kernel<true, true, false>), grid, block, 0, s, a);
   else if (shared) hipLaunchKernelGGL((latent_decode_kernel<true, false, false>), grid, block, 0, s, a);
