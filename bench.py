@@ -279,15 +279,18 @@ def paged_copy(cache, page_rows, seed=0):
     return gd.PagedCache(pages, table.contiguous())
 
 
-def bench_decode(steps, warmup, tokens=1, page_rows=0):
+def bench_decode(steps, warmup, tokens=1, page_rows=0, window=0):
     """64 sequences with a 65536-position context.  tokens = 1: one decode step (gdla_decode, the
     new token at position 65535); tokens = T > 1: T draft tokens per sequence at positions
     65536 - T .. 65535 in one gdla_decode_tokens call.  page_rows > 0: the same over a paged
-    cache (gdla_decode_paged, shuffled pages of page_rows rows)."""
+    cache (gdla_decode_paged, shuffled pages of page_rows rows).  window > 0: sliding-window
+    attention over the last `window` positions (the same cache, a layer with that window)."""
     import torch
     import synth
     import attention_gdla_prefill_decode_amd as gd
     cfg = synth.WORKLOADS["decode_64x64k"]
+    if window > 0:
+        cfg = dict(cfg, window=window)
     inp = synth.make_inputs(cfg, "cuda", seq=tokens, p0=cfg["max_len"] - tokens)
     w = gd.make_weights(inp["weights"])
     dims = gd.make_dims(cfg)
@@ -347,13 +350,15 @@ def bench_decode(steps, warmup, tokens=1, page_rows=0):
     name = "decode_64x64k" if tokens == 1 else f"decode_tokens_64x64k_t{tokens}"
     if page_rows > 0:
         name += f"_paged{page_rows}"
+    if window > 0:
+        name += f"_window{window}"
     return {"workload": name, "batch": len(pos), "tokens": tokens, "context": int(last[0]) + 1,
             "ms_per_step": round(ms, 4),
             "latent_GBps_whole_step": round(nbytes / ms / 1e6, 1),
             "tokens_per_s": round(len(pos) * tokens / ms * 1e3, 1),
             "roofline": dict({"kernel": "latent_decode_kernel<shared>"}, **roof,
                              traffic=(traffic_from_profile("latent_decode_64x64k_traffic.json")
-                                      if tokens == 1 and page_rows == 0 else None),
+                                      if tokens == 1 and page_rows == 0 and window == 0 else None),
                              traffic_source=traffic_source("latent_decode_64x64k_traffic.json"),
                              bytes_per_launch=nbytes, flop_per_launch=flop,
                              avg_launch_ms=round(kern_ms, 4)),
@@ -380,6 +385,9 @@ def main():
     ap.add_argument("--page-rows", type=int, default=0,
                     help="with the decode workload: run over a paged cache of this page size "
                          "(gdla_decode_paged)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="with the decode workload: a layer with this sliding window (decode over "
+                         "the last W positions of the 64K cache)")
     ap.add_argument("--docs", type=float, default=0,
                     help="prefill workloads: pack the tokens into documents of this mean length "
                          "(seeded exponential lengths; gdla_prefill_packed)")
@@ -418,18 +426,18 @@ def main():
         return
 
     if args.decode_only:
-        print(json.dumps(bench_decode(args.steps, args.warmup, args.tokens, args.page_rows)), flush=True)
+        print(json.dumps(bench_decode(args.steps, args.warmup, args.tokens, args.page_rows, args.window)), flush=True)
         return
 
     if args.workload == "decode_64x64k":
-        d = bench_decode(args.steps, args.warmup, args.tokens, args.page_rows)
+        d = bench_decode(args.steps, args.warmup, args.tokens, args.page_rows, args.window)
         result = {
             "metric": METRIC, "value": round(d["latent_GBps_whole_step"], 1), "unit": "GB/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": d["ms_per_step"],
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "bf16 (fp32 accumulate)", "data": "synthetic",
             "config": {"workload": d["workload"], "batch": 64, "tokens_per_sequence": args.tokens,
-                       "context": 65536, "parallelism": "none (1 GPU)"},
+                       "context": 65536, "window": args.window, "parallelism": "none (1 GPU)"},
             "roofline": d["roofline"], "stages_ms": d["stages_ms"], "tokens_per_s": d["tokens_per_s"],
         }
         print(json.dumps(result), flush=True)
