@@ -152,8 +152,8 @@ def traffic_source(name):
 
 def ceilings(reps=3):
     """Measured ceilings of this GPU (libgdla_ceiling.so): v_mfma_f32_32x32x16_f16 back to back
-    on pseudo-random operands (8 chains per wave, 8 waves per workgroup); a plain streaming read of
-    4 GiB with non-temporal 16-byte loads.
+    on pseudo-random operands (8 chains per wave, 8 waves per workgroup); a streaming read of 4 GiB
+    through LDS rings of direct global-to-LDS loads, one workgroup per CU.
     Returns the best of `reps` runs of each, timed with HIP events on the current stream."""
     import ctypes
     import torch
@@ -182,15 +182,16 @@ def ceilings(reps=3):
     ms_mfma = timed(lambda: L.ceiling_mfma(ctypes.c_void_p(out.data_ptr()), blocks, iters, stream))
     nbytes = 4 << 30
     buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
-    rblocks = 8192
+    rblocks = 256  # one workgroup per CU
     ms_read = timed(lambda: L.ceiling_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(out.data_ptr()),
                                            rblocks, stream))
     del buf
     return {"mfma_f16_random_TFLOPs": round(flop / ms_mfma / 1e9, 1),
             "hbm_read_GBps": round(nbytes / ms_read / 1e6, 1),
             "how": "libgdla_ceiling.so: ceiling_mfma (1024 x 512 threads, 8 x 2000 v_mfma_f32_32x32x16_f16 "
-                   "per wave on random fp16 operands) and ceiling_read (4 GiB, non-temporal 16-byte loads, "
-                   "8 in flight per lane, 8192 x 256 threads); best of 3 after a warm-up"}
+                   "per wave on random fp16 operands) and ceiling_read (4 GiB: 256 workgroups, one per CU, each "
+                   "streaming 16 MiB through a 4-slot LDS ring of 32 KiB with direct global-to-LDS 16-byte "
+                   "loads, three slots in flight); best of 3 after a warm-up"}
 
 
 def cpu_baseline_decode(nseq=8):
