@@ -51,9 +51,10 @@ constexpr int K_LOADS = K_TILE * 2 / 16 / 64 / 8;  // 16-byte K loads per wave p
 constexpr int V_LOADS = V_TILE * 2 / 16 / 64 / 8;  // 16-byte V^T loads per wave per tile (2)
 
 struct AttnArgs {
-  const f16_t *q;         // [M, n_H, 192] fp16: q^C then rotated q^R of each head
-  const f16_t *kx;        // [B, n_kv, lcap, 192] fp16: [K^C ; k^R] of keys base_b .. base_b + lcap - 1
-  const f16_t *vx;        // [B, n_kv, 128, lcap] fp16: V^T, keys in vt_slot order per 16-group
+  // q, kx, vx hold fp16, or bf16 in the kernel's BF instantiation (16-bit lanes either way)
+  const f16_t *q;         // [M, n_H, 192]: q^C then rotated q^R of each head
+  const f16_t *kx;        // [B, n_kv, lcap, 192]: [K^C ; k^R] of keys base_b .. base_b + lcap - 1
+  const f16_t *vx;        // [B, n_kv, 128, lcap]: V^T, keys in vt_slot order per 16-group
   const int32_t *pos;     // [B] first position of the chunk
   const int32_t *doc;     // [M] first position of each token's document (packed documents) or null
   const float *lam;       // [M, n_S]
@@ -94,8 +95,21 @@ __device__ __forceinline__ uint32_t lds_u32(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
 
+// The 16-bit operands are fp16 or, with BF, bf16 (held in the same 16-bit lanes).
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+template <bool BF>
 __device__ __forceinline__ f32x16 mfma(f16x8 a, f16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  if constexpr (BF)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                   0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+// fp32 -> the 16-bit operand type, rounding to nearest even
+template <bool BF>
+__device__ __forceinline__ f16_t to_op(float v) {
+  if constexpr (BF) return __builtin_bit_cast(f16_t, (bf16_t)v);
+  else return (f16_t)v;
 }
 
 // (own, partner) exchange between lanes l and l ^ 32
@@ -108,7 +122,8 @@ __device__ __forceinline__ float pair_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <bool SIGNAL>
+// BF: q, K and V (and so P) are bf16, else fp16.
+template <bool SIGNAL, bool BF>
 __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
   // NBUF buffers of one key tile each: K rows, then V^T rows
   __shared__ __attribute__((aligned(16))) f16_t KV[NBUF * (K_TILE + V_TILE)];
@@ -252,7 +267,7 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
     for (int kst = 0; kst < 12; ++kst) {
       if (kst + 1 < 12) ldK(kf[(kst + 1) & 1], kst + 1);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) S[kb] = mfma(kf[kst & 1][kb], Qf[kst], kst == 0 ? f32x16{} : S[kb]);
+      for (int kb = 0; kb < 2; ++kb) S[kb] = mfma<BF>(kf[kst & 1][kb], Qf[kst], kst == 0 ? f32x16{} : S[kb]);
       if (kst + 1 < 12) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
@@ -297,7 +312,7 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) P[k4][e] = (f16_t)v[8 * k4 + e];
+      for (int e = 0; e < 8; ++e) P[k4][e] = to_op<BF>(v[8 * k4 + e]);
     l += rs;
     // PV phase, pipelined one dim block ahead: [reads of block db + 1][MFMAs of block db]
     f16x8 vf[2][4];
@@ -311,7 +326,7 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
     for (int db = 0; db < 4; ++db) {
       if (db + 1 < 4) ldV(vf[(db + 1) & 1], db + 1);
 #pragma unroll
-      for (int kst = 0; kst < 4; ++kst) O[db] = mfma(vf[db & 1][kst], P[kst], O[db]);
+      for (int kst = 0; kst < 4; ++kst) O[db] = mfma<BF>(vf[db & 1][kst], P[kst], O[db]);
       if (db + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
@@ -387,8 +402,10 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
   }
 }
 
-// k^R of keys lo_b .. lo_b + nk_b - 1, converted from the bf16 cache to fp16 (exact in the fp16
-// normal range, +-inf beyond it, NaN kept), into columns 128 .. 191 of every KV head's key rows.
+// k^R of keys lo_b .. lo_b + nk_b - 1 into columns 128 .. 191 of every KV head's key rows: copied
+// from the bf16 cache (BF), or converted to fp16 (exact in the fp16 normal range, +-inf beyond it,
+// NaN kept).
+template <bool BF>
 __global__ void __launch_bounds__(256) kr_fill_kernel(const bf16_t *cache, f16_t *kx, const int32_t *pos,
                                                       int32_t T, int32_t window, int32_t max_len,
                                                       int32_t row, int32_t d_c, int32_t n_kv, int32_t lcap) {
@@ -404,7 +421,7 @@ __global__ void __launch_bounds__(256) kr_fill_kernel(const bf16_t *cache, f16_t
     const f16x2 h = {(f16_t)__uint_as_float(w << 16), (f16_t)__uint_as_float(w & 0xffff0000u)};
     return __builtin_bit_cast(unsigned, h);
   };
-  const uint4 o = make_uint4(cv(v.x), cv(v.y), cv(v.z), cv(v.w));
+  const uint4 o = BF ? v : make_uint4(cv(v.x), cv(v.y), cv(v.z), cv(v.w));
   for (int h = 0; h < n_kv; ++h)
     *(uint4 *)(kx + (((int64_t)b * n_kv + h) * lcap + r) * DQK + DH + ch * 8) = o;
 }
@@ -438,10 +455,14 @@ bool fast_prefill_supported(const LayerDims &d, gdla_dtype dt) {
 int32_t fast_prefill_key_row() { return DQK; }
 
 hipError_t launch_kr_fill(const void *cache, void *kx, const int32_t *pos_dev, int32_t B, int32_t T,
-                          int32_t lcap, int32_t max_len, const LayerDims &d, hipStream_t s) {
+                          int32_t lcap, int32_t max_len, const LayerDims &d, bool bf16, hipStream_t s) {
   const dim3 grid((lcap * (DR / 8) + 255) / 256, B);
-  hipLaunchKernelGGL(kr_fill_kernel, grid, dim3(256), 0, s, (const bf16_t *)cache, (f16_t *)kx, pos_dev,
-                     T, d.window, max_len, d.d_c + d.d_r, d.d_c, d.n_kv, lcap);
+  if (bf16)
+    hipLaunchKernelGGL(kr_fill_kernel<true>, grid, dim3(256), 0, s, (const bf16_t *)cache, (f16_t *)kx, pos_dev,
+                       T, d.window, max_len, d.d_c + d.d_r, d.d_c, d.n_kv, lcap);
+  else
+    hipLaunchKernelGGL(kr_fill_kernel<false>, grid, dim3(256), 0, s, (const bf16_t *)cache, (f16_t *)kx, pos_dev,
+                       T, d.window, max_len, d.d_c + d.d_r, d.d_c, d.n_kv, lcap);
   return hipGetLastError();
 }
 
@@ -450,11 +471,12 @@ gdla_status run_fast_prefill(const LayerDims &d, const gdla_weights *w, int32_t 
                              int32_t max_len, void *cq, float *lam, float *gate, void *kx,
                              void *vx, int32_t lcap, void *y, float *out_heads,
                              const FastPrefillLayout &L, void *ws, hipStream_t s, StageEvents &se,
-                             const NtWeights *nt, const int32_t *doc, float *lse) {
+                             const NtWeights *nt, const int32_t *doc, float *lse, bool bf_ops) {
   (void)pos_host;
   (void)cache;
   (void)max_len;
   const int32_t M = B * T;
+  bf_ops = bf_ops && nt;  // bf16 operands come from the transposed-weight GEMM's epilogues only
   f16_t *q = (f16_t *)((char *)ws + L.q);
   float *qrp = (float *)((char *)ws + L.qrp);
   float *hn = (float *)((char *)ws + L.hn);
@@ -470,10 +492,12 @@ gdla_status run_fast_prefill(const LayerDims &d, const gdla_weights *w, int32_t 
     p.epi = EPI_NONE;
     g.p[g.n++] = p;
   };
-  add(nt ? nt->qc : w->w_qc, d.n_heads * DH, q, (int64_t)d.n_heads * DQK, CD_F16, DH, DQK);
+  // q leaves the GEMM in the attention's operand type
+  const int q_dt = bf_ops ? CD_BF16 : CD_F16;
+  add(nt ? nt->qc : w->w_qc, d.n_heads * DH, q, (int64_t)d.n_heads * DQK, q_dt, DH, DQK);
   if (nt) {
     // q^R rotated in the GEMM epilogue, straight into columns 128 .. 191 of every head's q row
-    add(nt->qr, d.n_heads * DR, q, (int64_t)d.n_heads * DQK, CD_F16, DR, DQK);
+    add(nt->qr, d.n_heads * DR, q, (int64_t)d.n_heads * DQK, q_dt, DR, DQK);
     GemmProblem &pr = g.p[g.n - 1];
     pr.ho = DH;
     pr.epi = EPI_ROPE;
@@ -507,13 +531,15 @@ gdla_status run_fast_prefill(const LayerDims &d, const gdla_weights *w, int32_t 
   a.ny = d.n_noise;
   se.begin(GDLA_STAGE_ATTN_NOISE);
   a.nb = B;
-  hipLaunchKernelGGL(attn_prefill_kernel<false>, dim3(a.n_qblk * a.ny * B), dim3(512), 0, s, a);
+  if (bf_ops) hipLaunchKernelGGL((attn_prefill_kernel<false, true>), dim3(a.n_qblk * a.ny * B), dim3(512), 0, s, a);
+  else hipLaunchKernelGGL((attn_prefill_kernel<false, false>), dim3(a.n_qblk * a.ny * B), dim3(512), 0, s, a);
   if (hipGetLastError() != hipSuccess) return GDLA_ERR_HIP;
   se.end(GDLA_STAGE_ATTN_NOISE);
   a.n_qblk = (T + 63) / 64;
   a.ny = d.n_kv * a.chunks;
   se.begin(GDLA_STAGE_ATTN_SIGNAL);
-  hipLaunchKernelGGL(attn_prefill_kernel<true>, dim3(a.n_qblk * a.ny * B), dim3(512), 0, s, a);
+  if (bf_ops) hipLaunchKernelGGL((attn_prefill_kernel<true, true>), dim3(a.n_qblk * a.ny * B), dim3(512), 0, s, a);
+  else hipLaunchKernelGGL((attn_prefill_kernel<true, false>), dim3(a.n_qblk * a.ny * B), dim3(512), 0, s, a);
   if (hipGetLastError() != hipSuccess) return GDLA_ERR_HIP;
   se.end(GDLA_STAGE_ATTN_SIGNAL);
   return GDLA_OK;

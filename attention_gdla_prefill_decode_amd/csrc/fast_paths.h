@@ -34,8 +34,11 @@ struct NtWeights {
 };
 
 // ---- fused prefill attention ----
+// The attention's 16-bit operands (q, expanded K and V) are bf16 when the transposed-weight GEMMs
+// produce them (bf_ops) and the caller does not ask for fp16 (the fused backward's recompute,
+// whose kernels pair them with fp16 gradients); fp16 otherwise.
 struct FastPrefillLayout {
-  size_t q;      // [M, n_H, d_h + d_r] fp16: q^C and rotated q^R of every head, one row per head
+  size_t q;      // [M, n_H, d_h + d_r] fp16 or bf16: q^C and rotated q^R of every head, one row per head
   size_t qrp;    // [M, n_H, d_r] fp32: q^R before RoPE
   size_t hn;     // [M, n_N, d_h] fp32: normalised noise-head outputs
 };
@@ -65,16 +68,16 @@ hipError_t launch_vt_tail_zero(void *vx, const int32_t *pos_dev, int32_t B, int3
 bool fast_prefill_supported(const LayerDims &d, gdla_dtype dt);
 // Elements per expanded key row on the MFMA path: [K^C (d_h) ; k^R (d_rope)] in fp16.
 int32_t fast_prefill_key_row();
-// Copies k^R of the visible keys from the bf16 cache (converted to fp16) into columns d_h ..
-// d_h + d_rope - 1 of every KV head's expanded key rows.
+// Copies k^R of the visible keys from the bf16 cache (kept in bf16, or converted to fp16) into
+// columns d_h .. d_h + d_rope - 1 of every KV head's expanded key rows.
 hipError_t launch_kr_fill(const void *cache, void *kx, const int32_t *pos_dev, int32_t B, int32_t T,
-                          int32_t lcap, int32_t max_len, const LayerDims &d, hipStream_t s);
+                          int32_t lcap, int32_t max_len, const LayerDims &d, bool bf16, hipStream_t s);
 gdla_status run_fast_prefill(const LayerDims &d, const gdla_weights *w, int32_t B, int32_t T,
                              const int32_t *pos_dev, const int32_t *pos_host, void *cache,
                              int32_t max_len, void *cq, float *lam, float *gate, void *kx,
                              void *vx, int32_t lcap, void *y, float *out_heads,
                              const FastPrefillLayout &L, void *ws, hipStream_t s, StageEvents &se,
-                             const NtWeights *nt, const int32_t *doc, float *lse = nullptr);
+                             const NtWeights *nt, const int32_t *doc, float *lse = nullptr, bool bf_ops = false);
 
 // ---- absorbed split-L decode ----
 // Sizes are per query row set: BT = B T for T new tokens per sequence.

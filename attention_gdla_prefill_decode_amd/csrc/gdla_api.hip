@@ -601,7 +601,8 @@ namespace {
 gdla_status prefill_impl(const gdla_dims *dims, const gdla_weights *w, const void *x, int32_t B, int32_t T,
                          const int32_t *pos_host, void *cache, int32_t max_len, void *out, void *ws,
                          size_t ws_bytes, const gdla_debug *dbg, hipStream_t stream,
-                         const int32_t *doc = nullptr, float *lse = nullptr, const void *prepared = nullptr) {
+                         const int32_t *doc = nullptr, float *lse = nullptr, const void *prepared = nullptr,
+                         bool attn_f16 = false) {
   LayerDims d;
   gdla_status st = check_call(dims, w, x, B, T, pos_host, cache, max_len, out, true, d);
   if (st != GDLA_OK || B == 0 || T == 0) return st;
@@ -648,6 +649,8 @@ gdla_status prefill_impl(const gdla_dims *dims, const gdla_weights *w, const voi
   // head's rows); the generic path keeps K^C rows of d_h values in the layer dtype.
   const int64_t row = d.d_c + d.d_r;
   const int64_t krow = L.use_fast ? fast_prefill_key_row() : d.d_h;
+  // bf16 attention operands on the transposed-weight path, unless the caller needs fp16 ones
+  const bool bf_ops = L.use_fast && L.use_nt && !attn_f16;
   const int64_t k_seq = (int64_t)d.n_kv * L.lcap * krow;
   const int64_t v_seq = (int64_t)d.n_kv * L.lcap * d.d_h;
   se.begin(GDLA_STAGE_EXPAND_KV);
@@ -661,7 +664,7 @@ gdla_status prefill_impl(const gdla_dims *dims, const gdla_weights *w, const voi
                           at<char>(ws, L.kx) + b * k_seq * es, krow, nk, d.n_kv * d.d_h, d.d_c, false);
       pk.hw = d.d_h;
       pk.hs = (int64_t)L.lcap * krow;
-      if (L.use_fast) pk.c_dt = CD_F16;
+      if (L.use_fast) pk.c_dt = bf_ops ? CD_BF16 : CD_F16;
       GemmProblem pv = pk;
       pv.B = L.use_nt ? ntw.uv : w->w_uv;
       pv.C = at<char>(ws, L.vx) + b * v_seq * es;
@@ -678,7 +681,7 @@ gdla_status prefill_impl(const gdla_dims *dims, const gdla_weights *w, const voi
     else HIP_TRY(launch_gemm(g, dt, stream));
   }
   if (L.use_fast) {
-    HIP_TRY(launch_kr_fill(cache, at<void>(ws, L.kx), pos_dev, B, T, L.lcap, max_len, d, stream));
+    HIP_TRY(launch_kr_fill(cache, at<void>(ws, L.kx), pos_dev, B, T, L.lcap, max_len, d, bf_ops, stream));
     HIP_TRY(launch_vt_tail_zero(at<void>(ws, L.vx), pos_dev, B, T, L.lcap, d, stream));
   }
   se.end(GDLA_STAGE_EXPAND_KV);
@@ -687,7 +690,7 @@ gdla_status prefill_impl(const gdla_dims *dims, const gdla_weights *w, const voi
     st = run_fast_prefill(d, w, B, T, pos_dev, pos_host, cache, max_len, at<void>(ws, L.cq),
                           at<float>(ws, L.lam), at<float>(ws, L.gate), at<void>(ws, L.kx),
                           at<void>(ws, L.vx), L.lcap, at<void>(ws, L.y), out_heads, L.fast, ws,
-                          stream, se, L.use_nt ? &ntw : nullptr, doc, lse);
+                          stream, se, L.use_nt ? &ntw : nullptr, doc, lse, bf_ops);
     if (st != GDLA_OK) return fail(st, "fast prefill path failed: %s", hipGetErrorString(hipGetLastError()));
   } else {
     // Eq.(2), (9): q^C, pre-RoPE q^R and gate logits.
@@ -950,8 +953,9 @@ gdla_status backward_fast(const gdla_dims *dims, const gdla_weights *w, const vo
   gdla_debug fdbg{};
   fdbg.lambda_override = dbg ? dbg->lambda_override : nullptr;
   fdbg.out_heads = at<float>(ws, F.heads);
+  // fp16 attention operands: the backward kernels pair q, K and V with fp16 gradients
   gdla_status st = prefill_impl(dims, w, x, B, T, zeros.data(), at<void>(ws, F.cache), T, at<void>(ws, F.out), ws,
-                                PL.total, &fdbg, stream, doc, at<float>(ws, F.lse));
+                                PL.total, &fdbg, stream, doc, at<float>(ws, F.lse), nullptr, true);
   if (st != GDLA_OK) return st;
   // V key-major per KV head: cbar W_uv (the forward keeps V transposed)
   {

@@ -56,6 +56,38 @@ __device__ __forceinline__ int remap_xcd(int bid, int total) {
   return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
 }
 
+// Transposed per-head store of a 128 x 64 block of the value expansion (V^T, keys in vt_slot
+// order), 4 consecutive keys per 8-byte store; E is the 16-bit output type.
+template <typename E>
+__device__ __forceinline__ void trans_store(const GemmProblem &P, const f32x16 (&acc)[4][2], int r0, int c0, int lane) {
+  typedef E e4 __attribute__((ext_vector_type(4)));
+  const int r32 = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int n = c0 + nb * 32 + r32;
+      if (n >= P.N) continue;
+      E *base = (E *)P.C + (int64_t)(n / P.hw) * P.hs + P.ho + (int64_t)(n % P.hw) * P.ldc;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = r0 + mb * 32 + 8 * q + 4 * h;
+        if (m >= P.M) continue;
+        e4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (E)(acc[mb][nb][4 * q + e]);
+        if (m + 3 < P.M) {
+          *(e4 *)(base + vt_slot(m)) = v;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (m + e < P.M) base[vt_slot(m + e)] = v[e];
+        }
+      }
+    }
+  }
+}
+
 // Epilogue through LDS: the wave stages 32 rows x its 64 columns at a time (after the epilogue
 // function, in the output type: KIND 0 fp32, 1 fp16, 2 bf16) in its own area `wt` and writes them
 // back as 16-byte row segments, which lie inside one head since head widths are multiples of 8.
@@ -74,7 +106,7 @@ __device__ __forceinline__ void staged_epilogue(const GemmProblem &P, const f32x
   for (int mb = 0; mb < 4; ++mb) {
     const int mrow0 = r0 + mb * 32;
     float v0[16], v1[16];  // columns r32 and r32 + 32
-    if (KIND == 1 && P.epi == EPI_ROPE) {
+    if (KIND != 0 && P.epi == EPI_ROPE) {
       // heads of 64 columns: the wave's 64 columns are one head, and column j of block 0 pairs
       // with column j + 32 of block 1 in the same lane.  Row m is token m % T of sequence m / T;
       // the 32 rows of this block span at most two sequences (T >= 32 is checked on the host).
@@ -246,31 +278,9 @@ __global__ void __launch_bounds__(512, 1) gemm_nt_kernel(GemmBatch batch) {
     return;
   }
   // transposed per-head store of the value expansion (V^T, keys in vt_slot order): 8-byte stores
-  // along the rows
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int n = n0 + wn * 64 + nb * 32 + r32;
-      if (n >= P.N) continue;
-      f16_t *base = (f16_t *)P.C + (int64_t)(n / P.hw) * P.hs + P.ho + (int64_t)(n % P.hw) * P.ldc;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int m = m0 + wm * 128 + mb * 32 + 8 * q + 4 * h;
-          if (m >= P.M) continue;
-          f16x4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (f16_t)(acc[mb][nb][4 * q + e]);
-          if (m + 3 < P.M) {
-            *(f16x4 *)(base + vt_slot(m)) = v;
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (m + e < P.M) base[vt_slot(m + e)] = v[e];
-          }
-        }
-    }
-  }
+  // along the rows, in fp16 or bf16
+  if (P.c_dt == CD_BF16) trans_store<bf16_t>(P, acc, m0 + wm * 128, n0 + wn * 64, lane);
+  else trans_store<f16_t>(P, acc, m0 + wm * 128, n0 + wn * 64, lane);
 }
 
 // C[m][n] = sum over the K slices s = 0 .. ks - 1 (in that order) of part[s][m][n]; four columns
@@ -347,9 +357,9 @@ __global__ void __launch_bounds__(256) transpose_kernel(const bf16_t *W, TO *Wt,
 bool nt_gemm_problem_ok(const GemmProblem &p) {
   return p.K % BK == 0 && p.K > 0 && p.M > 0 && p.N > 0 && p.lda % 8 == 0 && p.ldb % 8 == 0 &&
          ((uintptr_t)p.A & 15) == 0 && ((uintptr_t)p.B & 15) == 0 && p.hw > 0 &&
-         (p.epi != EPI_ROPE || (p.rope_d == 64 && p.hw % 64 == 0 && p.N % 64 == 0 && p.c_dt == CD_F16 &&
-                                p.rope_pos && p.rope_T >= 32)) &&
-         (!p.c_trans || (p.c_dt == CD_F16 && p.ldc % 4 == 0 && (p.hs + p.ho) % 4 == 0 &&
+         (p.epi != EPI_ROPE || (p.rope_d == 64 && p.hw % 64 == 0 && p.N % 64 == 0 &&
+                                (p.c_dt == CD_F16 || p.c_dt == CD_BF16) && p.rope_pos && p.rope_T >= 32)) &&
+         (!p.c_trans || ((p.c_dt == CD_F16 || p.c_dt == CD_BF16) && p.ldc % 4 == 0 && (p.hs + p.ho) % 4 == 0 &&
                          ((uintptr_t)p.C & 7) == 0)) &&
          // row-major outputs leave as 16-byte row segments inside one head
          (p.c_trans || (p.N % 8 == 0 && p.hw % 8 == 0 && ((uintptr_t)p.C & 15) == 0 &&
