@@ -30,13 +30,18 @@ dgamma = sum over rows of dy (.) v / r.
 The reference is the loss L = sum(out (.) dout) for a given upstream gradient dout; every returned
 gradient is dL/d(that input).  Only new-token sequences starting at position 0 are covered (a
 training sequence), with the optional window and packed documents of the forward.
+
+dH of every head is known before any head's map is evaluated (dY = dout W_O^T does not depend on
+the maps; Eq.(8) routes it with lambda and sigmoid(G)), so each head's probability matrix is formed
+once, used for its output and its gradients, and dropped: one T x T matrix at a time.  The heads are
+independent, and gdla_backward can map them over worker processes (`map_fn`).
 """
 
 import numpy as np
 
 from oracle import gdla_ref as ref
 
-__all__ = ["rms_norm_backward", "rope_backward", "gdla_backward"]
+__all__ = ["rms_norm_backward", "rope_backward", "head_attention_backward", "gdla_backward"]
 
 
 def _f64(a):
@@ -60,12 +65,38 @@ def rope_backward(du, pos, theta):
     return ref.rope(du, -_f64(pos), theta)
 
 
-def gdla_backward(x, w, dims, dout, doc_start=None, lam_override=None):
+def head_attention_backward(q_c, q_r, k_c, k_r, v, d_h, tau, pos, window, doc_start):
+    """One head's softmax map, forward and backward, for queries and keys at positions `pos`:
+    s = tau (q_c k_c^T + q_r k_r^T) on the visible (query, key) pairs, P = softmax(s) per row,
+    H = P v; dP = d_h v^T, ds = P (.) (dP - rowsum(dP (.) P)).
+    Returns (H, dq_c, dq_r, dk_c, dk_r, dv); the last three are this head's contributions to its KV
+    head's K^C and V and to the shared rotary key."""
+    hidden = ~ref.visible_mask(pos, pos, window, doc_start)
+    s = q_c @ k_c.T
+    s += q_r @ k_r.T
+    s *= tau
+    np.copyto(s, -np.inf, where=hidden)
+    s -= np.max(s, axis=1, keepdims=True)
+    p = np.exp(s, out=s)  # masked keys: exp(-inf) = 0
+    p /= np.sum(p, axis=1, keepdims=True)
+    h = p @ v
+    ds = d_h @ v.T  # dP
+    ds -= np.einsum("ij,ij->i", ds, p)[:, None]  # rowsum(dP (.) P)
+    ds *= p
+    return h, tau * ds @ k_c, tau * ds @ k_r, tau * ds.T @ q_c, tau * ds.T @ q_r, p.T @ d_h
+
+
+def _head_task(args):
+    return head_attention_backward(*args)
+
+
+def gdla_backward(x, w, dims, dout, doc_start=None, lam_override=None, map_fn=map):
     """Gradients of L = sum(out (.) dout) for one sequence x [T, d_model] at positions 0..T-1.
 
     Returns a dict: dx [T, d_model]; dw_qa, dw_qc, dw_qr, dw_dkv, dw_kr, dw_uk, dw_uv, dw_lambda,
     dw_gate, dw_o (shaped like the weights); dgamma_q, dgamma_kv (None for fixed gains of 1); and
     the intermediate gradients dY, dH (per head), dlam, dq_c, dq_r, dk_c, dk_r, dv.
+    map_fn(f, tasks) evaluates the heads' maps (in head order), e.g. a process pool's map.
     """
     x, dout = _f64(x), _f64(dout)
     t = x.shape[0]
@@ -88,51 +119,45 @@ def gdla_backward(x, w, dims, dout, doc_start=None, lam_override=None):
     k_c = (c_bar @ W["w_uk"]).reshape(t, nkv, dh)                                # Eq.(5)
     v = (c_bar @ W["w_uv"]).reshape(t, nkv, dh)
     lam = ref.sigmoid(x @ W["w_lambda"]) if lam_override is None else _f64(lam_override)  # Eq.(7)
-    mask = ref.visible_mask(pos, pos, dims.window, None if doc_start is None else doc_start)
-    probs = np.zeros((nh, t, t))
-    heads = np.zeros((t, nh, dh))
-    for h in range(nh):
-        j = ref.kv_head_of(h, dims)
-        s = tau * (q_c[:, h] @ k_c[:, j].T + q_r[:, h] @ k_r.T)
-        s = np.where(mask, s, -np.inf)
-        e = np.where(mask, np.exp(s - np.max(s, axis=1, keepdims=True)), 0.0)
-        probs[h] = e / np.sum(e, axis=1, keepdims=True)
-        heads[:, h] = probs[h] @ v[:, j]
-    h_s, h_n = heads[:, :ns], heads[:, ns:]
     partner = np.arange(ns) % nn                                                 # Repeat_g tiles
-    d = h_s - lam[:, :, None] * h_n[:, partner]                                  # Eq.(8)
     sg = ref.sigmoid(g_logit)
-    y = sg * d                                                                   # Eq.(10)
 
-    # ---- Eq.(10): out = vec(Y) W_O and the gate
-    dw_o = y.reshape(t, ns * dh).T @ dout
+    # ---- Eq.(10): out = vec(Y) W_O and the gate; dY needs no head output
     d_y = (dout @ W["w_o"].T).reshape(t, ns, dh)
     d_d = d_y * sg
-    d_g = d_y * d * sg * (1.0 - sg)
 
     # ---- Eq.(8): signal heads take dD, the noise head of pair i takes -lambda_i dD_i
     d_heads = np.zeros((t, nh, dh))
     d_heads[:, :ns] = d_d
     for i in range(ns):
         d_heads[:, ns + partner[i]] -= lam[:, i:i + 1] * d_d[:, i]
-    d_lam = -np.sum(d_d * h_n[:, partner], axis=2)
 
-    # ---- the softmax maps of every head
+    # ---- the softmax maps of every head: outputs and gradients, one head at a time
+    docs = None if doc_start is None else doc_start
+    tasks = ((q_c[:, h], q_r[:, h], k_c[:, ref.kv_head_of(h, dims)], k_r, v[:, ref.kv_head_of(h, dims)],
+              d_heads[:, h], tau, pos, dims.window, docs) for h in range(nh))
+    heads = np.zeros((t, nh, dh))
     d_qc = np.zeros_like(q_c)
     d_qr = np.zeros_like(q_r)
     d_kc = np.zeros_like(k_c)
     d_kr = np.zeros_like(k_r)
     d_v = np.zeros_like(v)
-    for h in range(nh):
+    for h, (hh, dqc, dqr, dkc, dkr, dvv) in enumerate(map_fn(_head_task, tasks)):
         j = ref.kv_head_of(h, dims)
-        p = probs[h]
-        dp = d_heads[:, h] @ v[:, j].T
-        ds = p * (dp - np.sum(dp * p, axis=1, keepdims=True))
-        d_v[:, j] += p.T @ d_heads[:, h]
-        d_qc[:, h] = tau * ds @ k_c[:, j]
-        d_qr[:, h] = tau * ds @ k_r
-        d_kc[:, j] += tau * ds.T @ q_c[:, h]
-        d_kr += tau * ds.T @ q_r[:, h]
+        heads[:, h] = hh
+        d_qc[:, h] = dqc
+        d_qr[:, h] = dqr
+        d_kc[:, j] += dkc
+        d_kr += dkr
+        d_v[:, j] += dvv
+
+    # ---- the terms that need the head outputs: Eq.(8) and (10) forward, dG, dlambda, dW_O
+    h_s, h_n = heads[:, :ns], heads[:, ns:]
+    d = h_s - lam[:, :, None] * h_n[:, partner]                                  # Eq.(8)
+    y = sg * d                                                                   # Eq.(10)
+    dw_o = y.reshape(t, ns * dh).T @ dout
+    d_g = d_y * d * sg * (1.0 - sg)
+    d_lam = -np.sum(d_d * h_n[:, partner], axis=2)
 
     # ---- Eq.(5), (4), (3): back into the latent and the rotary key
     dw_uk = c_bar.T @ d_kc.reshape(t, nkv * dh)

@@ -199,10 +199,11 @@ def from_pages(pc, B, L):
 
 
 def backward_case(cfg, seq, batch, window=0, docs=None, seed=None, random_gamma=True, lam_zero=False,
-                  prep=None, dout_scale=1.0):
+                  prep=None, dout_scale=1.0, map_fn=map):
     """gdla_backward on GPU and the oracle's backward on CPU (sequences at positions 0..T-1) for
     a seeded upstream gradient dout (N(0, 1) times dout_scale); weight gradients are summed over
-    the batch.  `prep(inp)` may rewrite the CPU inputs before both sides see them."""
+    the batch.  `prep(inp)` may rewrite the CPU inputs before both sides see them; `map_fn` maps
+    the oracle's per-head work (e.g. over worker processes)."""
     inp = synth.make_inputs(cfg, "cpu", seed=seed, batch=batch, seq=seq, p0=0, random_gamma=random_gamma)
     if prep is not None:
         prep(inp)
@@ -222,7 +223,8 @@ def backward_case(cfg, seq, batch, window=0, docs=None, seed=None, random_gamma=
     for b in range(batch):
         r = grad_ref.gdla_backward(to_np(inp["x"][b]), w, od, to_np(dout[b]),
                                    doc_start=None if docs is None else np.array(docs[b]),
-                                   lam_override=np.zeros((seq, cfg["n_signal"])) if lam_zero else None)
+                                   lam_override=np.zeros((seq, cfg["n_signal"])) if lam_zero else None,
+                                   map_fn=map_fn)
         for k, v in r.items():
             if v is None or not (k == "dx" or k.startswith("dw_") or k.startswith("dgamma")):
                 continue

@@ -391,4 +391,42 @@ def pin_backward_lambda_zero(gg):
         raise AssertionError("signal W_qc grad vanished")
 
 
-GRAD_PINS = [pin_backward_finite_differences, pin_backward_entries, pin_backward_lambda_zero]
+def pin_backward_matches_stored(gg):
+    """The oracle, which forms one head's probability matrix at a time, reproduces the gradients the
+    earlier version (every head's probabilities kept for the whole call) wrote to
+    tests/golden/backward_small.npz (tests/golden/make_backward_golden.py), on a full-causal problem
+    and on a windowed one with packed documents."""
+    import oracle.gdla_ref as ref_fwd
+    stored = np.load(os.path.join(GOLDEN, "backward_small.npz"))
+    cases = ((0, None, 101), (3, [0, 0, 0, 3, 3, 3, 3, 7, 7], 102))
+    for i, (win, docs, seed) in enumerate(cases):
+        cfg, w, x, _ = small_problem(6, 4, 2, 2, seq=9, seed=seed)
+        dims = make_dims(ref_fwd, cfg, win)
+        dout = np.random.default_rng(seed + 1000).standard_normal((9, cfg["d_model"]))
+        g = gg.gdla_backward(x, w, dims, dout, doc_start=None if docs is None else np.array(docs))
+        names = sorted(k[len(f"case{i}_"):] for k in stored.files if k.startswith(f"case{i}_"))
+        if len(names) < 15:
+            raise AssertionError(f"stored case {i} holds only {names}")
+        for name in names:
+            _close(g[name], stored[f"case{i}_{name}"], 1e-12, f"case {i} {name} vs stored")
+
+
+def pin_backward_process_map(gg):
+    """The heads' maps evaluated by two worker processes give exactly the sequential result."""
+    import multiprocessing as mp
+    import oracle.gdla_ref as ref_fwd
+    cfg, w, x, _ = small_problem(6, 4, 2, 2, seq=9, seed=111)
+    dims = make_dims(ref_fwd, cfg, 4)
+    dout = np.random.default_rng(112).standard_normal((9, cfg["d_model"]))
+    seq = gg.gdla_backward(x, w, dims, dout)
+    with mp.get_context("spawn").Pool(2) as pool:
+        par = gg.gdla_backward(x, w, dims, dout, map_fn=pool.imap)
+    for name, val in seq.items():
+        if val is not None:
+            _close(par[name], val, 0.0, f"{name}: process map vs sequential")
+
+
+# pins of the gradient values (the planted-mistake tests run these), and all backward pins
+GRAD_VALUE_PINS = [pin_backward_finite_differences, pin_backward_entries, pin_backward_lambda_zero,
+                   pin_backward_matches_stored]
+GRAD_PINS = GRAD_VALUE_PINS + [pin_backward_process_map]

@@ -89,3 +89,31 @@ def test_decode_64x64k_sampled_sequences():
     _say(H.check(H.to_np(out[seqs]), r["out"], "bf16", "decode_64x64k sampled sequences"))
     H.check_rows(np.stack([H.to_np(dev["cache"][b, inp["p0"][b]]) for b in seqs]), r["cache_rows"],
                  "bf16", "decode_64x64k appended rows")
+
+
+@pytest.mark.timeout(900)
+def test_backward_8k_full():
+    """The benchmark's backward configuration (one 8192-token training sequence of the 8K prefill
+    layer, full causal, the fused fp16 path) against the oracle's backward over every gradient.
+    The oracle forms one head's 8192 x 8192 probability matrix at a time; its 80 heads run on
+    spawned worker processes (which never touch the GPU), two BLAS threads each."""
+    import multiprocessing as mp
+    import os
+    cfg = synth.WORKLOADS["prefill_8k"]
+    workers = max(1, min(8, (os.cpu_count() or 2) // 2))
+    saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    try:
+        for k in saved:
+            os.environ[k] = "2"
+        with mp.get_context("spawn").Pool(workers) as pool:
+            _say(f"8K backward: GPU call, then the oracle's 80 heads on {workers} workers")
+            got, exp = H.backward_case(cfg, cfg["seq"], 1, map_fn=pool.imap)
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    for line in H.check_grads(got, exp, 1e-2, "8K fused backward"):
+        _say(line)
+

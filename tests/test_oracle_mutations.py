@@ -7,7 +7,7 @@ import types
 
 import pytest
 
-from tests.oracle_pins import ALL_PINS, GRAD_PINS
+from tests.oracle_pins import ALL_PINS, GRAD_VALUE_PINS
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle",
                    "gdla_ref.py")
@@ -62,14 +62,14 @@ def test_planted_mistake_is_caught(name):
 GRAD_SRC = os.path.join(os.path.dirname(SRC), "gdla_grad.py")
 
 GRAD_MUTATIONS = {
-    "softmax_backward_no_rowsum": ("ds = p * (dp - np.sum(dp * p, axis=1, keepdims=True))", "ds = p * dp"),
+    "softmax_backward_no_rowsum": ("    ds -= np.einsum(\"ij,ij->i\", ds, p)[:, None]  # rowsum(dP (.) P)\n", ""),
     "rope_backward_same_angle": ("return ref.rope(du, -_f64(pos), theta)", "return ref.rope(du, _f64(pos), theta)"),
     "rms_backward_first_term_only": ("dv = u / r - v * np.sum(u * v, axis=-1, keepdims=True) / (n * r ** 3)", "dv = u / r"),
     "lambda_grad_sign": ("d_lam = -np.sum(d_d * h_n[:, partner], axis=2)", "d_lam = np.sum(d_d * h_n[:, partner], axis=2)"),
     "noise_grad_missing": ("d_heads[:, ns + partner[i]] -= lam[:, i:i + 1] * d_d[:, i]", "pass"),
     "gate_grad_without_sigmoid_slope": ("d_g = d_y * d * sg * (1.0 - sg)", "d_g = d_y * d"),
-    "shared_rotary_key_grad_last_head_only": ("d_kr += tau * ds.T @ q_r[:, h]", "d_kr = tau * ds.T @ q_r[:, h]"),
-    "value_grad_transposed": ("d_v[:, j] += p.T @ d_heads[:, h]", "d_v[:, j] += p @ d_heads[:, h]"),
+    "shared_rotary_key_grad_last_head_only": ("d_kr += dkr", "d_kr = dkr"),
+    "value_grad_transposed": ("tau * ds.T @ q_r, p.T @ d_h", "tau * ds.T @ q_r, p @ d_h"),
 }
 
 
@@ -86,7 +86,7 @@ def _grad_mutant(old, new):
 def test_planted_backward_mistake_is_caught(name):
     mod = _grad_mutant(*GRAD_MUTATIONS[name])
     caught = []
-    for pin in GRAD_PINS:
+    for pin in GRAD_VALUE_PINS:
         try:
             pin(mod)
         except Exception as e:
