@@ -1,6 +1,7 @@
-"""Benchmark of the GDLA forward on one MI355X: one step = one gdla_prefill call over the
+"""Benchmark of the GDLA forward on one MI355X: one step = one gdla_prefill_prepared call over the
 8192-token single-layer workload (batch 1, d_model 4096, 64 signal + 16 noise heads, 16 KV heads,
-latents 1024 / 512, head dim 128, rotary dim 64, full causal), inputs seeded and resident in HBM.
+latents 1024 / 512, head dim 128, rotary dim 64, full causal; the layer's weights transposed once
+beforehand by gdla_prepare_weights), inputs seeded and resident in HBM.
 
 Prints one JSON line: whole-step throughput (algorithmic FLOP of the layer / step time), the
 roofline of the dominant kernel (signal-head attention, timed with HIP events recorded by the
@@ -11,14 +12,21 @@ its own CPU-oracle baseline), and `ceilings`: the fp16 matrix-core rate with ran
 the HBM read rate measured on this GPU, against which both fractions are also given.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-ceilings]
-                    [--no-cpu-baseline]
+                    [--no-cpu-baseline] [--transpose-per-call]
                     [--workload prefill_8k|swa_prefill_2x32k|chunked_prefill_4k_256k|decode_64x64k]
-                    [--tokens T]
+                    [--tokens T] [--page-rows R] [--window W] [--docs MEAN] [--backward]
+                    [--decode-only] [--copy-probe]
 
 --workload picks another workload for the timed line (2 x 32K prefill with a 4096 window; a
 4096-token chunk against a 256K cache; one decode step of 64 sequences at 64K context, reported
-in GB/s of latent cache).  With the decode workload, --tokens T > 1 times the multi-token decode
-(T draft tokens per sequence, ending at position 65535) instead of the single-token step.
+in GB/s of latent cache).  With the decode workload (or --decode-only, which prints only the
+decode object): --tokens T > 1 times the multi-token decode (T draft tokens per sequence, ending
+at position 65535), --page-rows R a paged cache of shuffled R-row pages, --window W a layer with
+a W-position sliding window.  --docs MEAN packs the prefill tokens into seeded documents of that
+mean length; --backward times gdla_backward on the workload's shape; --transpose-per-call times
+gdla_prefill (weights transposed inside every call); --copy-probe only copies 1 GiB three times
+(the known-size reference of the traffic counters).  bench.py measures one GPU: --gpus N > 1 exits
+with a message.
 """
 
 import argparse
