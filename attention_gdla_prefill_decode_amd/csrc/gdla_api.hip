@@ -36,12 +36,16 @@ size_t esize(gdla_dtype dt) { return dt == GDLA_F32 ? 4 : 2; }
 
 gdla_status check_dims(const gdla_dims *d, LayerDims &ld) {
   if (!d) return fail(GDLA_ERR_INVALID_ARG, "dims is NULL");
-  if (d->dtype != GDLA_F32 && d->dtype != GDLA_BF16) return fail(GDLA_ERR_INVALID_ARG, "unknown dtype");
+  // (a C caller may store any int in the enum field: read it as one)
+  int32_t dtype;
+  static_assert(sizeof(d->dtype) == sizeof(dtype), "gdla_dtype is an int");
+  memcpy(&dtype, &d->dtype, sizeof(dtype));
+  if (dtype != GDLA_F32 && dtype != GDLA_BF16) return fail(GDLA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
   if (d->d_model <= 0 || d->n_heads <= 0 || d->n_signal <= 0 || d->n_noise <= 0 ||
       d->n_kv_heads <= 0 || d->d_q_latent <= 0 || d->d_kv_latent <= 0 || d->d_head <= 0 ||
       d->d_rope <= 0 || d->window < 0)
     return fail(GDLA_ERR_INVALID_ARG, "non-positive layer size");
-  if (d->n_signal + d->n_noise != d->n_heads)
+  if ((int64_t)d->n_signal + d->n_noise != d->n_heads)
     return fail(GDLA_ERR_INVALID_ARG, "n_signal + n_noise != n_heads");
   if (d->n_signal % d->n_noise != 0) return fail(GDLA_ERR_INVALID_ARG, "n_noise must divide n_signal");
   if (d->n_noise % d->n_kv_heads != 0) return fail(GDLA_ERR_INVALID_ARG, "n_kv_heads must divide n_noise");
@@ -49,8 +53,11 @@ gdla_status check_dims(const gdla_dims *d, LayerDims &ld) {
   if (!(d->rms_eps >= 0.f) || !(d->rope_theta > 0.f) || !(d->softmax_scale >= 0.f))
     return fail(GDLA_ERR_INVALID_ARG, "rms_eps, rope_theta or softmax_scale out of range");
   // Limits of the generic kernels (per-lane register arrays and LDS tables).
-  if (d->d_head > 256 || d->d_rope > 64 || d->d_kv_latent + d->d_rope > 1024)
+  if (d->d_head > 256 || d->d_rope > 64 || (int64_t)d->d_kv_latent + d->d_rope > 1024)
     return fail(GDLA_ERR_UNSUPPORTED, "d_head <= 256, d_rope <= 64, d_kv_latent + d_rope <= 1024");
+  // Widths stay well inside the int32 column counts of the GEMMs (n_heads d_head <= 2^18).
+  if (d->d_model > 65536 || d->d_q_latent > 65536 || d->n_heads > 1024)
+    return fail(GDLA_ERR_UNSUPPORTED, "d_model <= 65536, d_q_latent <= 65536, n_heads <= 1024");
   ld.d_model = d->d_model; ld.n_heads = d->n_heads; ld.n_signal = d->n_signal;
   ld.n_noise = d->n_noise; ld.n_kv = d->n_kv_heads; ld.d_cq = d->d_q_latent;
   ld.d_c = d->d_kv_latent; ld.d_h = d->d_head; ld.d_r = d->d_rope; ld.window = d->window;
@@ -60,6 +67,13 @@ gdla_status check_dims(const gdla_dims *d, LayerDims &ld) {
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Most rows (B T tokens) of one call: row counts are int32 on the host and in the kernels, and
+// 2^30 leaves room for padding them to whole tiles.
+constexpr int64_t kMaxRows = int64_t(1) << 30;
+// Most cache positions (max_len): key counts round up to whole tiles in int32.  At 2^30 positions
+// one sequence's latent cache alone would exceed a GPU's memory many times over.
+constexpr int32_t kMaxPositions = int32_t(1) << 30;
 
 // ---------------------------------------------------------------------------------------------
 // Workspace planning.  Every buffer starts on a 256-byte boundary.
@@ -311,8 +325,8 @@ struct FastBackwardLayout {
 
 FastBackwardLayout plan_backward_fast(const LayerDims &d, int32_t B, int32_t T) {
   FastBackwardLayout L{};
-  std::vector<int32_t> zeros((size_t)B, 0);
-  L.pre = plan_prefill(d, GDLA_BF16, B, T, zeros.data(), T);
+  // (positions 0 .. T-1 of every sequence: the bound over all positions is exact here)
+  L.pre = plan_prefill(d, GDLA_BF16, B, T, nullptr, T);
   L.ok = L.pre.use_fast && L.pre.use_nt && fast_backward_supported(d, GDLA_BF16);
   if (!L.ok) return L;
   const size_t M = (size_t)B * T, nH = d.n_heads, nS = d.n_signal, nKV = d.n_kv;
@@ -353,7 +367,9 @@ gdla_status check_call(const gdla_dims *dims, const gdla_weights *w, const void 
   gdla_status st = check_dims(dims, ld);
   if (st != GDLA_OK) return st;
   if (B < 0 || T < 0 || max_len <= 0) return fail(GDLA_ERR_INVALID_ARG, "negative B/T or max_len <= 0");
+  if (max_len > kMaxPositions) return fail(GDLA_ERR_UNSUPPORTED, "max_len = %d above 2^30", max_len);
   if (B == 0 || T == 0) return GDLA_OK;
+  if ((int64_t)B * T > kMaxRows) return fail(GDLA_ERR_UNSUPPORTED, "B T = %lld rows above 2^30", (long long)B * T);
   if (!w) return fail(GDLA_ERR_INVALID_ARG, "weights is NULL");
   if (!x || !cache || !pos) return fail(GDLA_ERR_INVALID_ARG, "x, cache or pos_host is NULL");
   if (need_query_weights && !out) return fail(GDLA_ERR_INVALID_ARG, "out is NULL");
@@ -508,7 +524,7 @@ GDLA_EXPORT size_t gdla_workspace_bytes(const gdla_dims *dims, int32_t op, int32
   if (check_dims(dims, d) != GDLA_OK) return 0;
   if (B < 0 || T < 0 || max_len <= 0 || (op == GDLA_OP_DECODE && T > GDLA_MAX_DECODE_TOKENS)) return 0;
   if (B == 0 || T == 0) return 0;
-  if (T > max_len) return 0;
+  if (T > max_len || max_len > kMaxPositions || (int64_t)B * T > kMaxRows) return 0;
   if (pos_host) {
     for (int32_t b = 0; b < B; ++b)
       if (pos_host[b] < 0 || (int64_t)pos_host[b] + T > max_len) return 0;
@@ -782,6 +798,9 @@ GDLA_EXPORT gdla_status gdla_prefill_prepared(const gdla_dims *dims, const gdla_
                                               void *ws, size_t ws_bytes, const gdla_debug *dbg,
                                               hipStream_t stream) {
   g_err[0] = 0;
+  LayerDims d;
+  const gdla_status st = check_dims(dims, d);
+  if (st != GDLA_OK) return st;
   const size_t need = gdla_prepared_weights_bytes(dims);
   if (need == 0) return fail(GDLA_ERR_UNSUPPORTED, "this layer's prefill takes no prepared weights");
   if (!prepared) return fail(GDLA_ERR_INVALID_ARG, "prepared is NULL");
@@ -907,6 +926,15 @@ gdla_status decode_impl(const gdla_dims *dims, const gdla_weights *w, const void
 }  // namespace
 }  // namespace gdla
 
+namespace gdla {
+gdla_status check_decode_args(const gdla_dims *dims, const gdla_weights *w, const void *x, int32_t B,
+                              const int32_t *pos_host, const void *cache, int32_t max_len, const void *out) {
+  g_err[0] = 0;
+  LayerDims d;
+  return check_call(dims, w, x, B, 1, pos_host, cache, max_len, out, true, d);
+}
+}  // namespace gdla
+
 GDLA_EXPORT gdla_status gdla_decode(const gdla_dims *dims, const gdla_weights *w, const void *x,
                                     int32_t B, const int32_t *pos_host, void *cache,
                                     int32_t max_len, void *out, void *ws, size_t ws_bytes,
@@ -1012,6 +1040,7 @@ GDLA_EXPORT gdla_status gdla_backward(const gdla_dims *dims, const gdla_weights 
   if (st != GDLA_OK) return st;
   if (B < 0 || T < 0) return fail(GDLA_ERR_INVALID_ARG, "negative B or T");
   if (B == 0 || T == 0) return GDLA_OK;
+  if ((int64_t)B * T > kMaxRows) return fail(GDLA_ERR_UNSUPPORTED, "B T = %lld rows above 2^30", (long long)B * T);
   if (!w || !grads) return fail(GDLA_ERR_INVALID_ARG, "weights or grads is NULL");
   if (!x || !dout) return fail(GDLA_ERR_INVALID_ARG, "x or dout is NULL");
   const void *req[] = {w->w_qa, w->w_qc, w->w_qr, w->w_dkv, w->w_kr, w->w_uk, w->w_uv, w->w_lambda, w->w_gate, w->w_o};

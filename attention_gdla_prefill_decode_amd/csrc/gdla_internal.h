@@ -90,6 +90,11 @@ __host__ __device__ inline int64_t cache_row(const CacheRef &c, int b, int pos) 
 // Records `msg` as the calling thread's last error (gdla_last_error) and returns st.
 gdla_status report_error(gdla_status st, const char *msg);
 
+// The argument checks of gdla_decode alone (no workspace, nothing launched): GDLA_OK or the
+// status gdla_decode would return for these arguments, with the calling thread's error text set.
+gdla_status check_decode_args(const gdla_dims *dims, const gdla_weights *w, const void *x, int32_t B,
+                              const int32_t *pos_host, const void *cache, int32_t max_len, const void *out);
+
 inline CacheRef contiguous_cache(void *base, int32_t max_len) {
   CacheRef c{};
   c.base = base;

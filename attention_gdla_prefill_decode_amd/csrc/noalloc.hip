@@ -48,8 +48,9 @@ void *scratch_ptr(hipError_t *err) {
 GDLA_EXPORT gdla_status gdla_decode_noalloc(const gdla_dims *dims, const gdla_weights *w, const void *x,
                                             int32_t B, const int32_t *pos_host, void *cache, int32_t max_len,
                                             void *out, const gdla_debug *dbg, hipStream_t stream) {
-  // A size the scratch cannot hold is refused before anything runs.  (Invalid arguments give a
-  // workspace size of 0 here; gdla_decode then reports them.)
+  // Invalid arguments, and a size the scratch cannot hold, are refused before any HIP call.
+  const gdla_status st = gdla::check_decode_args(dims, w, x, B, pos_host, cache, max_len, out);
+  if (st != GDLA_OK || B == 0) return st;
   const size_t need = gdla_workspace_bytes(dims, GDLA_OP_DECODE, B, 1, pos_host, max_len);
   if (need > kScratchBytes) {
     char msg[200];

@@ -43,11 +43,15 @@
  *     buffer is written.  A HIP launch failure returns GDLA_ERR_HIP (work already queued on the
  *     stream by the same call may then have run).  No C++ exception crosses this interface.
  *   - gdla_last_error() returns a short description of the last failure on the calling thread.
- *   - Numerical range of the bf16 layers: the fast paths feed the matrix cores fp16 operands
- *     (c^Q, q^C/q^R, K^C/k^R, V, P, Y and, in the backward, the gradients), each rounded once to
- *     nearest even.  An operand beyond fp16's range (|v| > 65504) becomes +-inf and a NaN stays a
- *     NaN, so such inputs give non-finite outputs, never finite wrong ones; the library itself
- *     checks no values.  c^Q and cbar are RMS-normalised, so the range binds only through the
+ *   - Size limits (GDLA_ERR_UNSUPPORTED, or a workspace size of 0): B T <= 2^30 rows per call,
+ *     max_len <= 2^30, d_model and d_q_latent <= 65536, n_heads <= 1024, d_head <= 256,
+ *     d_rope <= 64, d_kv_latent + d_rope <= 1024.
+ *   - Numerical range of the bf16 layers: the fast paths round every matrix-core operand once, to
+ *     nearest even: bf16 for the attention operands (q^C/q^R, K^C/k^R, V and P of prefill; the
+ *     absorbed query, the cache and P of decode), fp16 for c^Q and Y in the projections and for
+ *     every operand of the fused backward (the gradients included).  An fp16 operand beyond
+ *     fp16's range (|v| > 65504) becomes +-inf and a NaN stays a NaN, so such inputs give
+ *     non-finite outputs, never finite wrong ones; the library itself checks no values.  c^Q and cbar are RMS-normalised, so the range binds only through the
  *     weights' and gains' magnitudes, k^R (linear in x) and V.  A NaN in a key may also reach the
  *     outputs of the earlier queries of its 64-key tile (a masked probability of 0 times NaN).
  */
