@@ -8,10 +8,13 @@
 //
 // Block tile 256 x 256, K slices of 64 staged in LDS by direct global -> LDS 16-byte loads (two
 // stages of 64 KB; one in flight while the other is consumed).  8 waves in a 2 x 4 grid, each
-// computing 128 x 64 as 4 x 2 v_mfma_f32_32x32x16 blocks.  Both operands are read from LDS with
-// 16-byte reads (8 consecutive k of one row): with K-contiguous operands no transposing read is
-// needed, and the XOR swizzle (chunk c of row r at c ^ ((r >> 1) & 7)) keeps 16 consecutive rows
-// reading one chunk on distinct banks.  Tiles are spread so that each XCD gets a contiguous range.
+// computing 128 x 64 as 8 x 4 v_mfma_f32_16x16x32 blocks (at the chip's power limit the 16 x 16
+// blocks sustain a higher rate than 32 x 32 ones for the same operand traffic: the wave tile, not
+// the block shape, sets the LDS reads per flop).  Both operands are read from LDS with 16-byte
+// reads (8 consecutive k of one row): with K-contiguous operands no transposing read is needed,
+// and the XOR swizzle (chunk c of row r at c ^ ((r >> 1) & 7)) keeps 16 consecutive rows reading
+// one chunk on distinct banks.  Tiles are spread so that each XCD gets a contiguous range, and
+// ordered in groups of row tiles within it.
 #include "fast_paths.h"
 
 #include <type_traits>
@@ -22,24 +25,25 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int ROWB = BK * 2;                  // bytes per staged row (128 = 8 chunks)
 constexpr int A_BYTES = BM * ROWB;            // 32 KB
 constexpr int STAGE_BYTES = (BM + BN) * ROWB; // 64 KB
 constexpr int WAVES = 8;
+constexpr int GROUP_M = 4;                    // row tiles per group of the tile order
 constexpr int DMA_PER_WAVE = STAGE_BYTES / 1024 / WAVES;  // 16-byte loads per lane per stage (8)
 
 template <typename T> struct V8;
 template <> struct V8<bf16_t> { typedef bf16x8 t; };
 template <> struct V8<f16_t> { typedef f16x8 t; };
 
-__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x16 mfma(f16x8 a, f16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x4 mfma(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 // 16 bytes global -> LDS (M0 + 16 lane) outside the compiler's LDS-DMA tracking; the wait is the
@@ -56,33 +60,33 @@ __device__ __forceinline__ int remap_xcd(int bid, int total) {
   return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
 }
 
-// Transposed per-head store of a 128 x 64 block of the value expansion (V^T, keys in vt_slot
-// order), 4 consecutive keys per 8-byte store; E is the 16-bit output type.
+// The wave tile is held as 8 x 4 blocks of 16 x 16:
+// acc[mb][nb][i] = C[r0 + 16 mb + 4 (lane / 16) + i][c0 + 16 nb + lane % 16].
+
+// Transposed per-head store of the wave's 128 x 64 block of the value expansion (V^T, keys in
+// vt_slot order), 4 consecutive keys per 8-byte store; E is the 16-bit output type.
 template <typename E>
-__device__ __forceinline__ void trans_store(const GemmProblem &P, const f32x16 (&acc)[4][2], int r0, int c0, int lane) {
+__device__ __forceinline__ void trans_store(const GemmProblem &P, const f32x4 (&acc)[8][4], int r0, int c0, int lane) {
   typedef E e4 __attribute__((ext_vector_type(4)));
-  const int r32 = lane & 31, h = lane >> 5;
+  const int c16 = lane & 15, q4 = lane >> 4;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+  for (int nb = 0; nb < 4; ++nb) {
+    const int n = c0 + nb * 16 + c16;
+    if (n >= P.N) continue;
+    E *base = (E *)P.C + (int64_t)(n / P.hw) * P.hs + P.ho + (int64_t)(n % P.hw) * P.ldc;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int n = c0 + nb * 32 + r32;
-      if (n >= P.N) continue;
-      E *base = (E *)P.C + (int64_t)(n / P.hw) * P.hs + P.ho + (int64_t)(n % P.hw) * P.ldc;
+    for (int mb = 0; mb < 8; ++mb) {
+      const int m = r0 + mb * 16 + 4 * q4;
+      if (m >= P.M) continue;
+      e4 v;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int m = r0 + mb * 32 + 8 * q + 4 * h;
-        if (m >= P.M) continue;
-        e4 v;
+      for (int e = 0; e < 4; ++e) v[e] = (E)(acc[mb][nb][e]);
+      if (m + 3 < P.M) {
+        *(e4 *)(base + vt_slot(m)) = v;
+      } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (E)(acc[mb][nb][4 * q + e]);
-        if (m + 3 < P.M) {
-          *(e4 *)(base + vt_slot(m)) = v;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (m + e < P.M) base[vt_slot(m + e)] = v[e];
-        }
+        for (int e = 0; e < 4; ++e)
+          if (m + e < P.M) base[vt_slot(m + e)] = v[e];
       }
     }
   }
@@ -91,66 +95,72 @@ __device__ __forceinline__ void trans_store(const GemmProblem &P, const f32x16 (
 // Epilogue through LDS: the wave stages 32 rows x its 64 columns at a time (after the epilogue
 // function, in the output type: KIND 0 fp32, 1 fp16, 2 bf16) in its own area `wt` and writes them
 // back as 16-byte row segments, which lie inside one head since head widths are multiples of 8.
-// Staged rows are padded so the two rows a staging store touches (4 apart) fall on other banks.
-// acc[mb][nb][j] = C[r0 + 32 mb + 8 (j / 4) + 4 (lane / 32) + j % 4][c0 + 32 nb + lane % 32].
+// Staged rows are padded so that the rows a staging store touches fall on other banks.
 template <int KIND>
-__device__ __forceinline__ void staged_epilogue(const GemmProblem &P, const f32x16 (&acc)[4][2], unsigned char *wt,
-                                                int r0, int c0, int lane) {
+__device__ __forceinline__ void staged_epilogue(const GemmProblem &P, const f32x4 (&acc)[8][4], unsigned char *wt,
+                                                  int r0, int c0, int lane) {
   constexpr int ESZ = KIND == 0 ? 4 : 2, EPS = 16 / ESZ, SPR = 64 / EPS;
   constexpr int PITCH = KIND == 0 ? 272 : 144;
-  const int r32 = lane & 31, h = lane >> 5;
-  const double rev = P.epi == EPI_ROPE
-                         ? pow((double)P.rope_theta, -2.0 * (double)r32 / (double)P.rope_d) * 0.15915494309189533577
-                         : 0.0;
+  const int c16 = lane & 15, q4 = lane >> 4;
+  // RoPE: column j of the wave's head (j < 32) pairs with column j + 32; this lane holds the pairs
+  // j = c16 and j = 16 + c16 (blocks nb and nb + 2), rotated by p * rope_theta^(-2 j / 64)
+  double rev[2] = {0.0, 0.0};
+  if (P.epi == EPI_ROPE) {
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    const int mrow0 = r0 + mb * 32;
-    float v0[16], v1[16];  // columns r32 and r32 + 32
+    for (int nb = 0; nb < 2; ++nb)
+      rev[nb] = pow((double)P.rope_theta, -2.0 * (double)(16 * nb + c16) / (double)P.rope_d) * 0.15915494309189533577;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {  // rows 32 q .. 32 q + 31 of the wave tile: blocks mb = 2 q, 2 q + 1
+    const int mrow0 = r0 + q * 32;
+    float v[2][4][4];  // [mb - 2 q][nb][i]
     if (KIND != 0 && P.epi == EPI_ROPE) {
-      // heads of 64 columns: the wave's 64 columns are one head, and column j of block 0 pairs
-      // with column j + 32 of block 1 in the same lane.  Row m is token m % T of sequence m / T;
-      // the 32 rows of this block span at most two sequences (T >= 32 is checked on the host).
+      // row m is token m % T of sequence m / T; 32 rows span at most two sequences (T >= 32)
       const int sb = min(mrow0, P.M - 1) / P.rope_T;
       const int sb_end = (sb + 1) * P.rope_T;
       const int pos0 = P.rope_pos[sb], pos1 = sb_end < P.M ? P.rope_pos[sb + 1] : 0;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int m = min(mrow0 + 8 * (j >> 2) + 4 * h + (j & 3), P.M - 1);
-        const int pp = m < sb_end ? pos0 + (m - sb * P.rope_T) : pos1 + (m - sb_end);
-        double turns = (double)pp * rev;
-        turns -= floor(turns);  // angle / 2 pi, reduced to [0, 1)
-        const float sn = __builtin_amdgcn_sinf((float)turns), cs = __builtin_amdgcn_cosf((float)turns);
-        const float u = acc[mb][0][j], v = acc[mb][1][j];
-        v0[j] = u * cs - v * sn;
-        v1[j] = u * sn + v * cs;
-      }
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = min(mrow0 + 16 * h2 + 4 * q4 + i, P.M - 1);
+          const int pp = m < sb_end ? pos0 + (m - sb * P.rope_T) : pos1 + (m - sb_end);
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            double turns = (double)pp * rev[nb];
+            turns -= floor(turns);  // angle / 2 pi, reduced to [0, 1)
+            const float sn = __builtin_amdgcn_sinf((float)turns), cs = __builtin_amdgcn_cosf((float)turns);
+            const float u = acc[2 * q + h2][nb][i], w = acc[2 * q + h2][nb + 2][i];
+            v[h2][nb][i] = u * cs - w * sn;
+            v[h2][nb + 2][i] = u * sn + w * cs;
+          }
+        }
     } else if (P.epi == EPI_SIGMOID) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        v0[j] = __builtin_amdgcn_rcpf(1.0f + __expf(-acc[mb][0][j]));
-        v1[j] = __builtin_amdgcn_rcpf(1.0f + __expf(-acc[mb][1][j]));
-      }
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[h2][nb][i] = __builtin_amdgcn_rcpf(1.0f + __expf(-acc[2 * q + h2][nb][i]));
     } else {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        v0[j] = acc[mb][0][j];
-        v1[j] = acc[mb][1][j];
-      }
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[h2][nb][i] = acc[2 * q + h2][nb][i];
     }
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      unsigned char *q = wt + (8 * (j >> 2) + 4 * h + (j & 3)) * PITCH + r32 * ESZ;
-      if constexpr (KIND == 0) {
-        *(float *)q = v0[j];
-        *(float *)(q + 32 * ESZ) = v1[j];
-      } else if constexpr (KIND == 1) {
-        *(f16_t *)q = (f16_t)(v0[j]);
-        *(f16_t *)(q + 32 * ESZ) = (f16_t)(v1[j]);
-      } else {
-        *(bf16_t *)q = (bf16_t)v0[j];
-        *(bf16_t *)(q + 32 * ESZ) = (bf16_t)v1[j];
-      }
-    }
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          unsigned char *a = wt + (16 * h2 + 4 * q4 + i) * PITCH + (16 * nb + c16) * ESZ;
+          if constexpr (KIND == 0) *(float *)a = v[h2][nb][i];
+          else if constexpr (KIND == 1) *(f16_t *)a = (f16_t)(v[h2][nb][i]);
+          else *(bf16_t *)a = (bf16_t)v[h2][nb][i];
+        }
     // 32 rows x SPR segments, 64 per instruction
 #pragma unroll
     for (int it = 0; it < 32 * SPR / 64; ++it) {
@@ -182,7 +192,17 @@ __global__ void __launch_bounds__(512, 1) gemm_nt_kernel(GemmBatch batch) {
     tile -= kc * per_slice;
   }
   const int kbeg = P.ksplit > 1 ? kc * (P.K / P.ksplit) : 0;
-  const int m0 = (tile / P.tiles_n) * BM, n0 = (tile % P.tiles_n) * BN;
+  // Grouped order: each run of GROUP_M row tiles walks the column tiles together, so the tiles an
+  // XCD holds at once (consecutive indices) read a few row blocks of A and a few column blocks of
+  // Bt instead of one row block and as many column blocks as there are tiles.
+  int m0, n0;
+  {
+    const int tiles_m = (P.M + BM - 1) / BM;
+    const int g = tile / (GROUP_M * P.tiles_n), r = tile - g * (GROUP_M * P.tiles_n);
+    const int gm = min(GROUP_M, tiles_m - g * GROUP_M);
+    m0 = (g * GROUP_M + r % gm) * BM;
+    n0 = (r / gm) * BN;
+  }
   const T *A = (const T *)P.A;
   const T *Bt = (const T *)P.B;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -211,41 +231,41 @@ __global__ void __launch_bounds__(512, 1) gemm_nt_kernel(GemmBatch batch) {
     }
   };
 
-  // Fragment reads: A block mb rows 128 wm + 32 mb + (lane % 32), Bt block nb rows
-  // 64 wn + 32 nb + (lane % 32); k-step kk reads chunk 2 kk + lane / 32.  The row swizzle
-  // depends on lane % 32 only, so the lane part of the offset depends on kk only.
-  const int r32 = lane & 31, h = lane >> 5;
-  int off[4];
+  // Fragment reads: A block mb rows 128 wm + 16 mb + (lane % 16), Bt block nb rows
+  // 64 wn + 16 nb + (lane % 16); k-step kk (32 k) reads chunk 4 kk + lane / 16.  The row swizzle
+  // depends on lane % 16 only, so the lane part of the offset depends on kk only.
+  const int r16 = lane & 15, q4 = lane >> 4;
+  int off[2];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) off[kk] = r32 * ROWB + (((2 * kk + h) ^ ((r32 >> 1) & 7)) * 16);
+  for (int kk = 0; kk < 2; ++kk) off[kk] = r16 * ROWB + (((4 * kk + q4) ^ ((r16 >> 1) & 7)) * 16);
   const int a_base = wm * 128 * ROWB, b_base = A_BYTES + wn * 64 * ROWB;
 
-  f32x16 acc[4][2];
+  f32x4 acc[8][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{};
 
   auto compute = [&](int stage) {
     const unsigned char *sb = smem + stage * STAGE_BYTES;
-    v8 af[2][4], bfr[2][2];
-    auto ld = [&](int kk, v8 (&a)[4], v8 (&b)[2]) {
+    v8 af[2][8], bfr[2][4];
+    auto ld = [&](int kk, v8 (&a)[8], v8 (&b)[4]) {
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) a[mb] = *(const v8 *)(sb + a_base + mb * 32 * ROWB + off[kk]);
+      for (int mb = 0; mb < 8; ++mb) a[mb] = *(const v8 *)(sb + a_base + mb * 16 * ROWB + off[kk]);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) b[nb] = *(const v8 *)(sb + b_base + nb * 32 * ROWB + off[kk]);
+      for (int nb = 0; nb < 4; ++nb) b[nb] = *(const v8 *)(sb + b_base + nb * 16 * ROWB + off[kk]);
     };
     ld(0, af[0], bfr[0]);
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      if (kk + 1 < 4) ld(kk + 1, af[(kk + 1) & 1], bfr[(kk + 1) & 1]);
+    for (int kk = 0; kk < 2; ++kk) {
+      if (kk + 1 < 2) ld(kk + 1, af[1], bfr[1]);
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma(af[kk & 1][mb], bfr[kk & 1][nb], acc[mb][nb]);
-      if (kk + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma(af[kk][mb], bfr[kk][nb], acc[mb][nb]);
+      if (kk + 1 < 2) __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);
     }
   };
 
@@ -258,7 +278,7 @@ __global__ void __launch_bounds__(512, 1) gemm_nt_kernel(GemmBatch batch) {
     compute(ks & 1);
   }
 
-  // epilogue: lane holds column (lane & 31) and rows 8 (j / 4) + 4 (lane / 32) + j % 4 of a block
+  // epilogue: acc[mb][nb][i] holds row 16 mb + 4 (lane / 16) + i, column 16 nb + lane % 16
   // output kinds of the staged epilogue: 0 fp32, 1 fp16, 2 bf16
   const int okind = P.c_dt == CD_F32 ? 0 : (P.c_dt == CD_F16 || (P.c_dt == CD_IN && __is_same(T, f16_t))) ? 1 : 2;
   if (P.ksplit > 1) {  // this slice's partial product, dense fp32 [M, N]
