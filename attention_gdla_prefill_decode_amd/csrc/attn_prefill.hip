@@ -1,5 +1,6 @@
-// Fused GDLA prefill attention for gfx950 (d_head 128, d_rope 64): fp16 MFMA operands (queries,
-// expanded keys [K^C ; k^R], values and probabilities), fp32 accumulation and fp32 online softmax.
+// Fused GDLA prefill attention for gfx950 (d_head 128, d_rope 64): 16-bit MFMA operands (queries,
+// expanded keys [K^C ; k^R], values and probabilities; bf16, or fp16 where a caller needs fp16),
+// fp32 accumulation and fp32 online softmax.
 //
 // Computes, per query head h and query token t at position p, the softmax attention over the
 // expanded keys [K^C ; k^R] and values V of its KV head (Motif 3 Technical Report, picx.dev
@@ -14,15 +15,17 @@
 // matrix work); each wave owns 32 query rows of one head.  In the signal launch the waves are 4
 // signal heads sharing one KV head times 2 halves of the same 64 tokens, so each K/V tile staged
 // in LDS serves all of them; in the noise launch the waves are 8 consecutive 32-token blocks of one
-// noise head.  Keys are processed in tiles of 64:
+// noise head.  Keys are processed in tiles of 64, all products in 16 x 16 x 32 MFMA blocks (at the
+// chip's power limit they sustain a higher rate than 32 x 32 x 16 blocks for the same operand
+// reads):
 //   staging: direct global -> LDS 16-byte loads (no staging registers) into three tile buffers,
 //     so two tiles are in flight while one is read; rows are unpadded and XOR-swizzled per 16-byte
 //     chunk so both LDS read patterns below are free of bank conflicts;
 //   S^T[key, query] = K[key, 0:192] . Q[query, 0:192]   (A = K from LDS, B = Q in registers);
-//   online softmax per query (each lane owns one query column; its partner lane l^32 the other
-//     half of the keys), with lazy rescaling, P^T taken straight from the accumulators in fp16;
+//   online softmax per query (each query's 64 keys are spread over 4 lanes, 16 each), with lazy
+//     rescaling, P^T taken straight from the accumulators;
 //   O^T[dim, query] += V^T[dim, key] . P^T[key, query]  (A = V^T rows, 16-byte LDS reads).
-// The values arrive transposed from the expansion GEMM ([n_kv][128][keys], keys of every 16-group
+// The values arrive transposed from the expansion GEMM ([n_kv][128][keys], keys of every 32-group
 // in the order vt_slot), which is the order in which the S accumulators hold the keys of P^T: the
 // accumulators serve as the P operand without any shuffle and no transposing LDS read is needed.
 // Causal / sliding-window / packed-document tiles are classified per wave as skipped, full or
@@ -38,7 +41,7 @@ namespace {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int DH = 128, DR = 64, DQK = DH + DR;
 constexpr int KT = 64;                 // keys per tile
@@ -54,7 +57,7 @@ struct AttnArgs {
   // q, kx, vx hold fp16, or bf16 in the kernel's BF instantiation (16-bit lanes either way)
   const f16_t *q;         // [M, n_H, 192]: q^C then rotated q^R of each head
   const f16_t *kx;        // [B, n_kv, lcap, 192]: [K^C ; k^R] of keys base_b .. base_b + lcap - 1
-  const f16_t *vx;        // [B, n_kv, 128, lcap]: V^T, keys in vt_slot order per 16-group
+  const f16_t *vx;        // [B, n_kv, 128, lcap]: V^T, keys in vt_slot order per 32-group
   const int32_t *pos;     // [B] first position of the chunk
   const int32_t *doc;     // [M] first position of each token's document (packed documents) or null
   const float *lam;       // [M, n_S]
@@ -98,12 +101,12 @@ __device__ __forceinline__ uint32_t lds_u32(const void *p) {
 // The 16-bit operands are fp16 or, with BF, bf16 (held in the same 16-bit lanes).
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 template <bool BF>
-__device__ __forceinline__ f32x16 mfma(f16x8 a, f16x8 b, f32x16 c) {
+__device__ __forceinline__ f32x4 mfma(f16x8 a, f16x8 b, f32x4 c) {
   if constexpr (BF)
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
                                                    0, 0);
   else
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 // fp32 -> the 16-bit operand type, rounding to nearest even
 template <bool BF>
@@ -112,12 +115,15 @@ __device__ __forceinline__ f16_t to_op(float v) {
   else return (f16_t)v;
 }
 
-// (own, partner) exchange between lanes l and l ^ 32
-__device__ __forceinline__ float pair_max(float v) {
+// Reductions over the four lanes l % 16 + 16 g (g = 0 .. 3) that hold one query's keys: an
+// exchange with lane l ^ 16, then with l ^ 32.
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float pair_sum(float v) {
+__device__ __forceinline__ float quad_sum(float v) {
+  v += __shfl_xor(v, 16, 64);
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
@@ -163,22 +169,30 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
     return lo;
   };
   // first key tile: from the block's first query (document starts never decrease along a packed
-  // sequence), aligned to 16 keys past `base` (the value layout's key groups); the extra keys in
+  // sequence), aligned to 32 keys past `base` (the value layout's key groups); the extra keys in
   // front are masked
-  const int klo = base + ((qlo(tlo) - base) & ~15);
+  const int klo = base + ((qlo(tlo) - base) & ~31);
   const int khi = p0 + thi + 1;
   const int ntiles = (khi - klo + KT - 1) / KT;
   const int wp_lo = p0 + t0w, wp_hi = p0 + min(t0w + 31, a.T - 1);
-  // this lane's query (column lane % 32 of the score tiles): key s is visible iff
-  // 0 <= p - s < wlim; wlo_min / wlo_max: lowest visible key over the wave's queries
-  int wlim, wlo_min, wlo_max;
+  // The score and output blocks are 16 x 16: lane l holds query columns 16 qb + l % 16 (qb = 0, 1)
+  // and, of each 16-row block, rows 4 (l / 16) .. + 3.
+  const int c16 = lane & 15, g4 = lane >> 4;
+  // this lane's queries: key s is visible from query qb iff 0 <= p - s < wlim[qb]; wlo_min /
+  // wlo_max: lowest visible key over the wave's queries
+  int wlim[2], wlo_min, wlo_max;
   {
-    const int tq = min(t0w + (lane & 31), a.T - 1);
-    const int lo = qlo(tq);
-    wlim = p0 + tq - lo + 1;
-    int mn = lo, mx = lo;
+    int mn = INT32_MAX, mx = INT32_MIN;
 #pragma unroll
-    for (int o = 1; o < 32; o <<= 1) {
+    for (int qb = 0; qb < 2; ++qb) {
+      const int tq = min(t0w + 16 * qb + c16, a.T - 1);
+      const int lo = qlo(tq);
+      wlim[qb] = p0 + tq - lo + 1;
+      mn = min(mn, lo);
+      mx = max(mx, lo);
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
       mn = min(mn, __shfl_xor(mn, o, 64));
       mx = max(mx, __shfl_xor(mx, o, 64));
     }
@@ -186,14 +200,17 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
     wlo_max = __builtin_amdgcn_readfirstlane(mx);
   }
 
-  // ---- Q fragments: Qf[ks] holds dims 16 ks + 8 (lane / 32) .. + 7 of query column lane % 32
-  f16x8 Qf[12];
+  // ---- Q fragments: Qf[qb][ks] holds dims 32 ks + 8 (lane / 16) .. + 7 of query 16 qb + lane % 16
+  f16x8 Qf[2][6];
   {
-    const int t = t0w + (lane & 31);
-    const bool ok = active && t < a.T;
-    const f16_t *qp = a.q + ((mrow0 + (ok ? t : 0)) * a.n_heads + (ok ? head : 0)) * DQK + 8 * (lane >> 5);
 #pragma unroll
-    for (int ks = 0; ks < 12; ++ks) Qf[ks] = ok ? *(const f16x8 *)(qp + 16 * ks) : f16x8{};
+    for (int qb = 0; qb < 2; ++qb) {
+      const int t = t0w + 16 * qb + c16;
+      const bool ok = active && t < a.T;
+      const f16_t *qp = a.q + ((mrow0 + (ok ? t : 0)) * a.n_heads + (ok ? head : 0)) * DQK + 8 * g4;
+#pragma unroll
+      for (int ks = 0; ks < 6; ++ks) Qf[qb][ks] = ok ? *(const f16x8 *)(qp + 32 * ks) : f16x8{};
+    }
     // Q has landed before any tile load is issued: the compiler does not see the tile loads, and
     // a vmcnt(0) it placed for Q inside the loop would also wait for the tiles in flight.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -229,22 +246,22 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
     for (int j = 0; j < V_LOADS; ++j) dma16(vth + (s0 - base), voff[j], vl + (wave * V_LOADS + j) * 1024);
   };
 
-  f32x16 O[4];
+  // O[db][qb][i]: output dim 16 db + 4 g4 + i of query 16 qb + c16 (unnormalised); m, l: the
+  // reference max and the running sum of each of the lane's two queries (l over this lane's keys)
+  f32x4 O[8][2];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) O[db] = f32x16{};
-  float m = -INFINITY, l = 0.f;
+  for (int db = 0; db < 8; ++db) O[db][0] = O[db][1] = f32x4{};
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
 
-  const int hgrp = lane >> 5;  // which half of each 8-key group this lane's accumulators hold
-  const int krow = lane & 31;
   // Lane-dependent byte offsets of the LDS fragment reads; the rest of each address is an
-  // immediate.  K fragment (kb, kst): row 32 kb + krow, chunk 2 kst + hgrp; the row swizzle is
-  // (krow >> 1) & 7 for both kb and only touches the low 3 bits of the chunk, so the lane part
-  // depends on kst & 3 only.  V^T fragment (db, kst): row 32 db + krow, chunk 2 kst + hgrp.
-  int offK[4], offV[4];
+  // immediate.  K fragment (kb, ks): row 16 kb + c16, chunk 4 ks + g4; the row swizzle is
+  // (c16 >> 1) & 7 for every kb and only touches the low 3 bits of the chunk, so the lane part
+  // depends on ks & 1 only.  V^T fragment (db, ks2): row 16 db + c16, chunk 4 ks2 + g4.
+  int offK[2], offV[2];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    offK[q] = krow * (K_CH * 16) + (((2 * q + hgrp) ^ ((krow >> 1) & 7)) * 16);
-    offV[q] = krow * (VT_CH * 16) + (((2 * q + hgrp) ^ ((krow >> 1) & 7)) * 16);
+  for (int q = 0; q < 2; ++q) {
+    offK[q] = c16 * (K_CH * 16) + (((4 * q + g4) ^ ((c16 >> 1) & 7)) * 16);
+    offV[q] = c16 * (VT_CH * 16) + (((4 * q + g4) ^ ((c16 >> 1) & 7)) * 16);
   }
 
   auto compute = [&](const f16_t *ks, const f16_t *vs, int s0) {
@@ -253,81 +270,104 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
     const bool full = s0 + KT - 1 <= wp_lo && s0 >= wlo_max;
     const char *kb8 = (const char *)ks;
     const char *vb8 = (const char *)vs;
-    // S phase, software-pipelined one k-step ahead: [reads of step kst + 1][MFMAs of step kst]
-    f32x16 S[2];
-    f16x8 kf[2][2];
-    auto ldK = [&](f16x8 (&f)[2], int kst) {
+    // S phase, software-pipelined one k-step ahead: [reads of step ks + 1][MFMAs of step ks].
+    // S[kb][qb][i]: score of key s0 + 16 kb + 4 g4 + i for query 16 qb + c16.
+    f32x4 S[4][2];
+    f16x8 kf[2][4];
+    auto ldK = [&](f16x8 (&f)[4], int ks) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        f[kb] = *(const f16x8 *)(kb8 + offK[kst & 3] + kb * 32 * K_CH * 16 + (kst >> 2) * 128);
+      for (int kb = 0; kb < 4; ++kb)
+        f[kb] = *(const f16x8 *)(kb8 + offK[ks & 1] + kb * 16 * K_CH * 16 + (ks >> 1) * 128);
     };
     ldK(kf[0], 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-    for (int kst = 0; kst < 12; ++kst) {
-      if (kst + 1 < 12) ldK(kf[(kst + 1) & 1], kst + 1);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) S[kb] = mfma<BF>(kf[kst & 1][kb], Qf[kst], kst == 0 ? f32x16{} : S[kb]);
-      if (kst + 1 < 12) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    }
-    // v[16 kb + e] is the score of key s0 + 32 kb + 8 (e / 4) + 4 hgrp + e % 4
-    float v[32];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) v[kb * 16 + e] = S[kb][e];
-    if (!full) {
-      // branch-free mask: visible iff 0 <= p - s < wlim (negative p - s wraps above it)
-      const int d0 = wp_lo + (lane & 31) - s0 - 4 * hgrp;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int off = (i >> 4) * 32 + 8 * ((i & 15) >> 2) + (i & 3);
-        v[i] = (unsigned)(d0 - off) < (unsigned)wlim ? v[i] : -INFINITY;
-      }
-    }
-    float mt = v[0];
-#pragma unroll
-    for (int i = 1; i < 32; ++i) mt = fmaxf(mt, v[i]);
-    mt = pair_max(mt);
-    // Lazy rescaling: the reference max m moves (and O, l are rescaled) only when some row's tile
-    // max exceeds it by more than 2^8 in the exp2 domain, so P <= 256 (fine in fp16) and the O
-    // rescale runs on few tiles.
-    if (__any((mt - m) * a.c > 8.0f)) {
-      const float mnew = fmaxf(m, mt);
-      const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m - mnew) * a.c);
-      m = mnew;
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) O[db] *= alpha;
-    }
-    const float ms = m == -INFINITY ? 0.f : m * a.c;
-    float rs = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      v[i] = __builtin_amdgcn_exp2f(v[i] * a.c - ms);
-      rs += v[i];
-    }
-    f16x8 P[4];  // P[kst]: keys 16 kst .. 16 kst + 15 of the tile, in accumulator order
-#pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) P[k4][e] = to_op<BF>(v[8 * k4 + e]);
-    l += rs;
-    // PV phase, pipelined one dim block ahead: [reads of block db + 1][MFMAs of block db]
-    f16x8 vf[2][4];
-    auto ldV = [&](f16x8 (&f)[4], int db) {
-#pragma unroll
-      for (int kst = 0; kst < 4; ++kst) f[kst] = *(const f16x8 *)(vb8 + offV[kst] + db * 32 * VT_CH * 16);
-    };
-    ldV(vf[0], 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      if (db + 1 < 4) ldV(vf[(db + 1) & 1], db + 1);
+    for (int ks = 0; ks < 6; ++ks) {
+      if (ks + 1 < 6) ldK(kf[(ks + 1) & 1], ks + 1);
 #pragma unroll
-      for (int kst = 0; kst < 4; ++kst) O[db] = mfma<BF>(vf[db & 1][kst], P[kst], O[db]);
-      if (db + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          S[kb][qb] = mfma<BF>(kf[ks & 1][kb], Qf[qb][ks], ks == 0 ? f32x4{} : S[kb][qb]);
+      if (ks + 1 < 6) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    }
+    if (!full) {
+      // branch-free mask: visible iff 0 <= p - s < wlim (negative p - s wraps above it)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int d0 = wp_lo + 16 * qb + c16 - s0 - 4 * g4;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            S[kb][qb][i] = (unsigned)(d0 - 16 * kb - i) < (unsigned)wlim[qb] ? S[kb][qb][i] : -INFINITY;
+      }
+    }
+    // this lane's share of each query's tile max
+    float mt[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      mt[qb] = S[0][qb][0];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mt[qb] = fmaxf(mt[qb], S[kb][qb][i]);
+    }
+    // Lazy rescaling: the reference max m moves (and O, l are rescaled) only when some query's tile
+    // max exceeds it by more than 2^8 in the exp2 domain, so P <= 256 and the O rescale runs on few
+    // tiles.  The lane shares suffice for the test; the move takes each query's whole-tile max, so
+    // the four lanes holding a query keep one m.
+    if (__any((mt[0] - m[0]) * a.c > 8.0f || (mt[1] - m[1]) * a.c > 8.0f)) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float mnew = fmaxf(m[qb], quad_max(mt[qb]));
+        const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m[qb] - mnew) * a.c);
+        m[qb] = mnew;
+        l[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) O[db][qb] *= alpha;
+      }
+    }
+    // P[ks2][qb]: the PV MFMA's probability operand for keys 32 ks2 .. 32 ks2 + 31: k-slot
+    // 8 g4 + e holds key 32 ks2 + 16 (e / 4) + 4 g4 + e % 4, the order of the value layout
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float ms = m[qb] == -INFINITY ? 0.f : m[qb] * a.c;
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pv = __builtin_amdgcn_exp2f(S[kb][qb][i] * a.c - ms);
+          rs += pv;
+          S[kb][qb][i] = pv;
+        }
+      l[qb] += rs;
+    }
+    f16x8 P[2][2];
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) P[ks2][qb][e] = to_op<BF>(S[2 * ks2 + (e >> 2)][qb][e & 3]);
+    // PV phase, pipelined one dim block ahead: [reads of block db + 1][MFMAs of block db]
+    f16x8 vf[2][2];
+    auto ldV = [&](f16x8 (&f)[2], int db) {
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) f[ks2] = *(const f16x8 *)(vb8 + offV[ks2] + db * 16 * VT_CH * 16);
+    };
+    ldV(vf[0], 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      if (db + 1 < 8) ldV(vf[(db + 1) & 1], db + 1);
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) O[db][qb] = mfma<BF>(vf[db & 1][ks2], P[ks2][qb], O[db][qb]);
+      if (db + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
   };
@@ -345,37 +385,36 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
   }
 
   if (!active) return;
-  // ---- epilogue: lane holds query column lane % 32 and dims db*32 + 8 i + 4 (lane / 32) + j
-  const float lsum = pair_sum(l);
-  const float inv = 1.0f / lsum;
-  const int t = t0w + (lane & 31);
-  if (t >= a.T) return;
-  const int64_t mr = mrow0 + t;
-  // the probabilities are exp2(c s - lse) for raw scores s (what a backward pass recomputes)
-  if (a.lse && hgrp == 0) a.lse[(int64_t)head * a.nb * a.T + mr] = m * a.c + __log2f(lsum);  // head-major
-  float *oh = a.out_heads ? a.out_heads + (mr * a.n_heads + head) * DH : nullptr;
-  if (!SIGNAL) {
-    float *hn = a.hn + (mr * a.n_noise + (head - a.n_signal)) * DH;
+  // ---- epilogue: lane holds queries 16 qb + c16 and dims 16 db + 4 g4 + i
+  float lsum[2];
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+  for (int qb = 0; qb < 2; ++qb) lsum[qb] = quad_sum(l[qb]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int dim = db * 32 + 8 * i + 4 * hgrp;
-        const float4 v = make_float4(O[db][4 * i] * inv, O[db][4 * i + 1] * inv, O[db][4 * i + 2] * inv,
-                                     O[db][4 * i + 3] * inv);
+  for (int qb = 0; qb < 2; ++qb) {
+    const float inv = 1.0f / lsum[qb];
+    const int t = t0w + 16 * qb + c16;
+    if (t >= a.T) continue;
+    const int64_t mr = mrow0 + t;
+    // the probabilities are exp2(c s - lse) for raw scores s (what a backward pass recomputes)
+    if (a.lse && g4 == 0) a.lse[(int64_t)head * a.nb * a.T + mr] = m[qb] * a.c + __log2f(lsum[qb]);  // head-major
+    float *oh = a.out_heads ? a.out_heads + (mr * a.n_heads + head) * DH : nullptr;
+    if (!SIGNAL) {
+      float *hn = a.hn + (mr * a.n_noise + (head - a.n_signal)) * DH;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const int dim = db * 16 + 4 * g4;
+        const float4 v = make_float4(O[db][qb][0] * inv, O[db][qb][1] * inv, O[db][qb][2] * inv, O[db][qb][3] * inv);
         *(float4 *)(hn + dim) = v;
         if (oh) *(float4 *)(oh + dim) = v;
       }
-  } else {
-    const float lam = a.lam[mr * a.n_signal + head];
-    const int64_t goff = (mr * a.n_signal + head) * DH;
-    const float *hn = a.hn + (mr * a.n_noise + head % a.n_noise) * DH;
-    f16_t *y = a.y + mr * (int64_t)a.n_signal * DH + (int64_t)head * DH;
+    } else {
+      const float lam = a.lam[mr * a.n_signal + head];
+      const int64_t goff = (mr * a.n_signal + head) * DH;
+      const float *hn = a.hn + (mr * a.n_noise + head % a.n_noise) * DH;
+      f16_t *y = a.y + mr * (int64_t)a.n_signal * DH + (int64_t)head * DH;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int dim = db * 32 + 8 * i + 4 * hgrp;
+      for (int db = 0; db < 8; ++db) {
+        const int dim = db * 16 + 4 * g4;
         float sg[4];
         if (a.gate_f16) {
           const f16x4 gh = *(const f16x4 *)((const f16_t *)a.gate + goff + dim);
@@ -389,8 +428,8 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
           sg[3] = 1.0f / (1.0f + __expf(-gv.w));
         }
         const float4 nv = *(const float4 *)(hn + dim);
-        const float o0 = O[db][4 * i] * inv, o1 = O[db][4 * i + 1] * inv;
-        const float o2 = O[db][4 * i + 2] * inv, o3 = O[db][4 * i + 3] * inv;
+        const float o0 = O[db][qb][0] * inv, o1 = O[db][qb][1] * inv;
+        const float o2 = O[db][qb][2] * inv, o3 = O[db][qb][3] * inv;
         if (oh) *(float4 *)(oh + dim) = make_float4(o0, o1, o2, o3);
         f16x4 yv;
         yv[0] = (f16_t)((o0 - lam * nv.x) * sg[0]);
@@ -399,6 +438,7 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
         yv[3] = (f16_t)((o3 - lam * nv.w) * sg[3]);
         *(f16x4 *)(y + dim) = yv;
       }
+    }
   }
 }
 
@@ -434,8 +474,8 @@ __global__ void __launch_bounds__(64) vt_tail_zero_kernel(f16_t *vx, const int32
   const int lo = window > 0 ? max(0, p0 - window + 1) : 0;
   const int nk = p0 + T - lo;
   f16_t *r = vx + ((int64_t)b * rows + blockIdx.x) * lcap;
-  for (int i = (nk & ~15) + threadIdx.x; i < lcap; i += 64)
-    if (vt_slot(i) >= nk) r[i] = (f16_t)0.0f;
+  for (int i = (nk & ~31) + threadIdx.x; i < lcap; i += 64)
+    if (vt_key(i) >= nk) r[i] = (f16_t)0.0f;
 }
 
 }  // namespace

@@ -53,10 +53,12 @@ FastPrefillLayout plan_fast_prefill(const LayerDims &d, int32_t B, int32_t T, Ad
   return L;
 }
 
-// Value layout of the MFMA prefill: V^T per KV head, [n_kv][d_head][lcap] fp16, with the keys of
-// every aligned group of 16 stored in the order the probability operand of the PV MFMA expects
-// (key k at position vt_slot(k): bits 2 and 3 swapped; the map is its own inverse).
-__host__ __device__ inline int vt_slot(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+// Value layout of the MFMA prefill: V^T per KV head, [n_kv][d_head][lcap] in 16-bit values, with
+// the keys of every aligned group of 32 stored in the order the probability operand of the PV MFMA
+// (16 x 16 x 32) takes them from the score accumulators: key 16 h + 4 g + c of a group (h < 2,
+// g < 4, c < 4) at position 8 g + 4 h + c.  vt_slot maps a key to its position, vt_key back.
+__host__ __device__ inline int vt_slot(int k) { return (k & ~28) | ((k & 12) << 1) | ((k & 16) >> 2); }
+__host__ __device__ inline int vt_key(int p) { return (p & ~28) | ((p & 24) >> 1) | ((p & 4) << 2); }
 // Key capacity of the value / key buffers on the MFMA path: whole tiles plus one spare tile, so a
 // tile that starts at any 16-key boundary before the last key stays inside the buffer.
 inline int32_t fast_prefill_lcap(int32_t keys) { return (keys + 63) / 64 * 64 + 64; }
