@@ -200,22 +200,6 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
     wlo_max = __builtin_amdgcn_readfirstlane(mx);
   }
 
-  // ---- Q fragments: Qf[qb][ks] holds dims 32 ks + 8 (lane / 16) .. + 7 of query 16 qb + lane % 16
-  f16x8 Qf[2][6];
-  {
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int t = t0w + 16 * qb + c16;
-      const bool ok = active && t < a.T;
-      const f16_t *qp = a.q + ((mrow0 + (ok ? t : 0)) * a.n_heads + (ok ? head : 0)) * DQK + 8 * g4;
-#pragma unroll
-      for (int ks = 0; ks < 6; ++ks) Qf[qb][ks] = ok ? *(const f16x8 *)(qp + 32 * ks) : f16x8{};
-    }
-    // Q has landed before any tile load is issued: the compiler does not see the tile loads, and
-    // a vmcnt(0) it placed for Q inside the loop would also wait for the tiles in flight.
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  }
-
   // ---- direct global -> LDS staging of one key tile.  The last tile may run up to 63 keys past
   // khi: the buffers hold lcap >= (keys rounded up to 64) + 64 rows, those keys are masked for
   // every valid query (any value, NaN included, is replaced), and their values are the
@@ -245,6 +229,26 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < V_LOADS; ++j) dma16(vth + (s0 - base), voff[j], vl + (wave * V_LOADS + j) * 1024);
   };
+
+  // Triple buffering: tiles t + 1 and t + 2 are in flight while tile t is read.  The first two
+  // are issued before the query fragments, so their latencies overlap.
+  for (int t = 0; t < NBUF - 1 && t < ntiles; ++t) issue(t);
+
+  // ---- Q fragments: Qf[qb][ks] holds dims 32 ks + 8 (lane / 16) .. + 7 of query 16 qb + lane % 16
+  f16x8 Qf[2][6];
+  {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int t = t0w + 16 * qb + c16;
+      const bool ok = active && t < a.T;
+      const f16_t *qp = a.q + ((mrow0 + (ok ? t : 0)) * a.n_heads + (ok ? head : 0)) * DQK + 8 * g4;
+#pragma unroll
+      for (int ks = 0; ks < 6; ++ks) Qf[qb][ks] = ok ? *(const f16x8 *)(qp + 32 * ks) : f16x8{};
+    }
+    // Q and the first tiles land before the loop: the compiler does not see the tile loads, and a
+    // vmcnt(0) it placed for Q inside the loop would also wait for the tiles in flight.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  }
 
   // O[db][qb][i]: output dim 16 db + 4 g4 + i of query 16 qb + c16 (unnormalised); m, l: the
   // reference max and the running sum of each of the lane's two queries (l over this lane's keys)
@@ -372,8 +376,6 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
     }
   };
 
-  // Triple buffering: tiles t + 1 and t + 2 are in flight while tile t is read.
-  for (int t = 0; t < NBUF - 1 && t < ntiles; ++t) issue(t);
   for (int t = 0; t < ntiles; ++t) {
     // vmcnt(n): at most n of this wave's loads still in flight (those of tile t + 1)
     if (t + 1 < ntiles) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(K_LOADS + V_LOADS) : "memory");
