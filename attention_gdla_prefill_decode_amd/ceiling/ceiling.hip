@@ -1,11 +1,12 @@
 // Measured ceilings of one MI355X for the roofline fractions the benchmark reports next to the
-// published peaks: the fp16 matrix-core rate with random operands (the chip's clock under that
-// load, not the nominal 2.4 GHz, sets what any fp16 MFMA kernel can reach) and the HBM read rate
-// of a plain streaming kernel.  Not part of the GDLA library: bench.py loads libgdla_ceiling.so.
+// published peaks: the bf16 matrix-core rate with random operands, on the instruction the prefill
+// attention runs (the chip's clock under that load, not the nominal 2.4 GHz, sets what any MFMA
+// kernel can reach) and the HBM read rate of a streaming kernel.  Not part of the GDLA library:
+// bench.py loads libgdla_ceiling.so.
 //
 //   int ceiling_mfma(float *out, int blocks, int iters, hipStream_t s)
-//     blocks x 512 threads, each wave issuing iters x 8 independent v_mfma_f32_32x32x16_f16 on
-//     pseudo-random fp16 operands; FLOP = blocks * 8 * iters * 8 * 32768.  out: blocks * 512 floats.
+//     blocks x 512 threads, each wave issuing iters x 8 independent v_mfma_f32_16x16x32_bf16 on
+//     pseudo-random bf16 operands; FLOP = blocks * 8 * iters * 8 * 16384.  out: blocks * 512 floats.
 //   int ceiling_read(const void *p, int64_t bytes, float *out, int blocks, hipStream_t s)
 //     reads `bytes` (a multiple of blocks * 32 KiB) once: each of `blocks` workgroups (one per CU:
 //     256) streams its contiguous share through a 4-slot LDS ring of 32 KiB slots with direct
@@ -17,8 +18,8 @@
 
 namespace {
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int CHAINS = 8;  // independent accumulators per wave
 constexpr int RING = 4;    // LDS slots of the read probe
@@ -35,25 +36,25 @@ __device__ __forceinline__ uint32_t mix(uint32_t x) {  // 32-bit integer hash (x
 
 __global__ void __launch_bounds__(512) mfma_kernel(float *out, int iters) {
   const uint32_t tid = blockIdx.x * 512 + threadIdx.x;
-  f16x8 a[CHAINS], b[CHAINS];
+  bf16x8 a[CHAINS], b[CHAINS];
 #pragma unroll
   for (int j = 0; j < CHAINS; ++j)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       // uniform in [-1, 1): every bit of the operands toggles like real data
-      a[j][e] = (_Float16)((float)(mix(tid * 128 + j * 8 + e) >> 8) * (2.0f / 16777216.0f) - 1.0f);
-      b[j][e] = (_Float16)((float)(mix(tid * 128 + 64 + j * 8 + e) >> 8) * (2.0f / 16777216.0f) - 1.0f);
+      a[j][e] = (__bf16)((float)(mix(tid * 128 + j * 8 + e) >> 8) * (2.0f / 16777216.0f) - 1.0f);
+      b[j][e] = (__bf16)((float)(mix(tid * 128 + 64 + j * 8 + e) >> 8) * (2.0f / 16777216.0f) - 1.0f);
     }
-  f32x16 acc[CHAINS] = {};
+  f32x4 acc[CHAINS] = {};
   for (int i = 0; i < iters; ++i) {
 #pragma unroll
-    for (int j = 0; j < CHAINS; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[j], b[j], acc[j], 0, 0, 0);
+    for (int j = 0; j < CHAINS; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], b[j], acc[j], 0, 0, 0);
   }
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < CHAINS; ++j)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) s += acc[j][e];
+    for (int e = 0; e < 4; ++e) s += acc[j][e];
   out[tid] = s;
 }
 

@@ -8,8 +8,9 @@ roofline of the dominant kernel (signal-head attention, timed with HIP events re
 library around it), and the fp64 CPU oracle timed on a bounded sample of the same workload.
 The line also carries the other half of the metric, `decode`: one decode step of 64 sequences at
 65536 positions (latent-cache GB/s, the roofline of the split-L attention kernel against HBM and
-its own CPU-oracle baseline), and `ceilings`: the fp16 matrix-core rate with random operands and
-the HBM read rate measured on this GPU, against which both fractions are also given.
+its own CPU-oracle baseline), and `ceilings`: the bf16 matrix-core rate with random operands (on
+the prefill attention's MFMA instruction) and the HBM read rate measured on this GPU, against which
+both fractions are also given.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-ceilings]
                     [--no-cpu-baseline] [--transpose-per-call]
@@ -159,8 +160,9 @@ def traffic_source(name):
 
 
 def ceilings(reps=3):
-    """Measured ceilings of this GPU (libgdla_ceiling.so): v_mfma_f32_32x32x16_f16 back to back
-    on pseudo-random operands (8 chains per wave, 8 waves per workgroup); a streaming read of 4 GiB
+    """Measured ceilings of this GPU (libgdla_ceiling.so): v_mfma_f32_16x16x32_bf16 (the prefill
+    attention's instruction) back to back on pseudo-random operands (8 chains per wave, 8 waves
+    per workgroup); a streaming read of 4 GiB
     through LDS rings of direct global-to-LDS loads, one workgroup per CU.
     Returns the best of `reps` runs of each, timed with HIP events on the current stream."""
     import ctypes
@@ -170,9 +172,9 @@ def ceilings(reps=3):
     L.ceiling_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     L.ceiling_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    blocks, iters = 1024, 2000
+    blocks, iters = 1024, 4000
     out = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
-    flop = float(blocks) * 8 * iters * 8 * 32768
+    flop = float(blocks) * 8 * iters * 8 * 16384
 
     def timed(fn):
         best = None
@@ -194,10 +196,10 @@ def ceilings(reps=3):
     ms_read = timed(lambda: L.ceiling_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(out.data_ptr()),
                                            rblocks, stream))
     del buf
-    return {"mfma_f16_random_TFLOPs": round(flop / ms_mfma / 1e9, 1),
+    return {"mfma_bf16_random_TFLOPs": round(flop / ms_mfma / 1e9, 1),
             "hbm_read_GBps": round(nbytes / ms_read / 1e6, 1),
-            "how": "libgdla_ceiling.so: ceiling_mfma (1024 x 512 threads, 8 x 2000 v_mfma_f32_32x32x16_f16 "
-                   "per wave on random fp16 operands) and ceiling_read (4 GiB: 256 workgroups, one per CU, each "
+            "how": "libgdla_ceiling.so: ceiling_mfma (1024 x 512 threads, 8 x 4000 v_mfma_f32_16x16x32_bf16 "
+                   "per wave on random bf16 operands) and ceiling_read (4 GiB: 256 workgroups, one per CU, each "
                    "streaming 16 MiB through a 4-slot LDS ring of 32 KiB with direct global-to-LDS 16-byte "
                    "loads, three slots in flight); best of 3 after a warm-up"}
 
@@ -536,8 +538,8 @@ def main():
         c = ceilings()
         result["ceilings"] = c
         roof = result["roofline"]
-        roof["measured_ceiling"] = c["mfma_f16_random_TFLOPs"]
-        roof["frac_of_measured_ceiling"] = round(roof["achieved"] / c["mfma_f16_random_TFLOPs"], 4)
+        roof["measured_ceiling"] = c["mfma_bf16_random_TFLOPs"]
+        roof["frac_of_measured_ceiling"] = round(roof["achieved"] / c["mfma_bf16_random_TFLOPs"], 4)
         if "decode" in result:
             droof = result["decode"]["roofline"]
             if droof["bound"] == "hbm":
