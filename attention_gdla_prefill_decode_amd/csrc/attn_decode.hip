@@ -28,8 +28,8 @@
 // Rows are unpadded; chunk c of row r sits at c ^ (r mod 8).  With it the hardware counter reads no
 // LDS bank conflicts for the 16-byte row reads (16 consecutive rows, one chunk) or the transposing
 // reads (4 consecutive rows, an aligned pair of chunks).
-// Each split writes its unnormalised O, its reference m (log2 units) and sum l; merge_splits
-// combines them.
+// Each split writes its unnormalised O, its reference m (log2 units) and sum l; the un-absorbing
+// kernel merges the splits of its rows as it loads them.
 #include "fast_paths.h"
 
 #include <algorithm>
@@ -574,28 +574,8 @@ __global__ void __launch_bounds__(64 * NWAVES, 1) latent_decode_kernel(DecodeArg
   }
 }
 
-// o[b, h] = sum_sp 2^(m_sp - M) o_sp / sum_sp 2^(m_sp - M) l_sp, M = max_sp m_sp (each split's
-// reference in log2 units; -inf marks an empty split).
-__global__ void __launch_bounds__(128) merge_splits_kernel(const float *part_o, const float *part_ml, float *o,
-                                                         int32_t n_heads, int32_t splits) {
-  const int bh = blockIdx.x;  // b * n_heads + h
-  const int b = bh / n_heads, h = bh % n_heads;
-  float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[(((int64_t)b * splits + s) * n_heads + h) * 2]);
-  float L = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < splits; ++s) {
-    const int64_t ph = ((int64_t)b * splits + s) * n_heads + h;
-    const float ms = part_ml[ph * 2];
-    if (ms == -INFINITY) continue;  // empty split
-    const float w = __builtin_amdgcn_exp2f(ms - M);
-    L += w * part_ml[ph * 2 + 1];
-    const float4 v = *(const float4 *)(part_o + ph * DC + 4 * threadIdx.x);
-    acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
-  }
-  const float inv = 1.0f / L;
-  *(float4 *)(o + (int64_t)bh * DC + 4 * threadIdx.x) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-}
+// Largest number of splits of one row set (fast_decode_splits: about one workgroup per CU).
+constexpr int MAX_SPLITS = 256;
 
 // Query rows that share one KV head.  Block (i, kv) takes rows i R .. i R + R - 1 of the list
 // (b, k) -> b * hk + k over sequences b and the hk heads k of kv (signal heads first).
@@ -667,11 +647,14 @@ __global__ void __launch_bounds__(256) absorb_kernel(const float *qc, const floa
   }
 }
 
-// H_h = o_h W_uv[:, kv(h)] in fp32, for the block's R rows.  Thread (half, e) sums latent
-// dimensions half * 256 .. + 255 for output column e; the two halves are added through LDS.
-__global__ void __launch_bounds__(256) unabsorb_kernel(const float *o, const f16_t *wuvt, float *heads,
-                                                       int32_t B, LayerDims d) {
+// H_h = o_h W_uv[:, kv(h)] in fp32, for the block's R rows, where o_h is the merge of the
+// row's splits: o = sum_sp 2^(m_sp - M) o_sp / sum_sp 2^(m_sp - M) l_sp, M = max_sp m_sp (each
+// split's reference in log2 units; -inf marks an empty split, which is skipped).
+__global__ void __launch_bounds__(256) unabsorb_kernel(const float *part_o, const float *part_ml, int32_t splits,
+                                                       const f16_t *wuvt, float *heads, int32_t B, LayerDims d) {
   __shared__ __attribute__((aligned(16))) float os[R][DC];
+  __shared__ float wsp[R][MAX_SPLITS];  // split weights 2^(m_sp - M), 0 for empty splits
+  __shared__ float linv[R];
   __shared__ int64_t rowq[R];
   const int kv = blockIdx.y, tid = threadIdx.x;
   int ns;
@@ -683,9 +666,43 @@ __global__ void __launch_bounds__(256) unabsorb_kernel(const float *o, const f16
     rowq[tid] = (int64_t)b * d.n_heads + kv_head(kv, L % hk, ns, d);
   }
   __syncthreads();
+  // split weights and 1 / L of each row: 16 threads per row, splits j, j + 16, ...
+  {
+    const int r = tid >> 4, j = tid & 15;
+    const bool ok = r < nr;
+    const int64_t bh = ok ? rowq[r] : 0;
+    const int64_t b = bh / d.n_heads, h = bh % d.n_heads;
+    auto ml = [&](int sp) { return part_ml + ((b * splits + sp) * d.n_heads + h) * 2; };
+    float M = -INFINITY;
+    if (ok)
+      for (int sp = j; sp < splits; sp += 16) M = fmaxf(M, ml(sp)[0]);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    float L = 0.f;
+    if (ok)
+      for (int sp = j; sp < splits; sp += 16) {
+        const float ms = ml(sp)[0];
+        const float w = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+        wsp[r][sp] = w;
+        L += w * ml(sp)[1];
+      }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) L += __shfl_xor(L, o, 64);
+    if (ok && j == 0) linv[r] = 1.0f / L;
+  }
+  __syncthreads();
   for (int i = tid; i < nr * (DC / 4); i += 256) {
     const int r = i / (DC / 4), c = (i % (DC / 4)) * 4;
-    *(float4 *)&os[r][c] = *(const float4 *)(o + rowq[r] * DC + c);
+    const int64_t b = rowq[r] / d.n_heads, h = rowq[r] % d.n_heads;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int sp = 0; sp < splits; ++sp) {
+      const float w = wsp[r][sp];
+      if (w == 0.f) continue;  // empty split (its partial is not written) or no weight
+      const float4 v = *(const float4 *)(part_o + ((b * splits + sp) * d.n_heads + h) * DC + c);
+      acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
+    }
+    const float inv = linv[r];
+    *(float4 *)&os[r][c] = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   }
   for (int i = nr * (DC / 4) + tid; i < R * (DC / 4); i += 256) {
     const int r = i / (DC / 4), c = (i % (DC / 4)) * 4;
@@ -739,7 +756,6 @@ gdla_status run_fast_decode(const LayerDims &d, const gdla_weights *w, int32_t B
   bf16_t *qabs = (bf16_t *)((char *)ws + L.qabs);
   float *part_o = (float *)((char *)ws + L.part_o);
   float *part_ml = (float *)((char *)ws + L.part_ml);
-  float *o = (float *)((char *)ws + L.o);
   const int hk_max = (d.n_signal + d.n_kv - 1) / d.n_kv + (d.n_noise + d.n_kv - 1) / d.n_kv;
   const dim3 gk((unsigned)((BT * hk_max + R - 1) / R), (unsigned)d.n_kv);
   hipLaunchKernelGGL(absorb_kernel, gk, dim3(256), 0, s, qc, qr, (const bf16_t *)w->w_uk, qabs, BT, d);
@@ -764,12 +780,11 @@ gdla_status run_fast_decode(const LayerDims &d, const gdla_weights *w, int32_t B
   if (hipGetLastError() != hipSuccess) return GDLA_ERR_HIP;
   se.end(GDLA_STAGE_ATTN_NOISE);
   se.begin(GDLA_STAGE_ATTN_SIGNAL);
-  hipLaunchKernelGGL(merge_splits_kernel, dim3(BT * d.n_heads), dim3(128), 0, s, part_o, part_ml, o, d.n_heads,
-                     L.splits);
-  if (hipGetLastError() != hipSuccess) return GDLA_ERR_HIP;
+  if (L.splits > MAX_SPLITS) return GDLA_ERR_UNSUPPORTED;
   f16_t *wuvt = (f16_t *)((char *)ws + L.wuvt);
   if (launch_transpose_weight(w->w_uv, wuvt, DC, d.n_kv * 128, true, s) != hipSuccess) return GDLA_ERR_HIP;
-  hipLaunchKernelGGL(unabsorb_kernel, gk, dim3(256), 0, s, o, (const f16_t *)wuvt, heads, BT, d);
+  hipLaunchKernelGGL(unabsorb_kernel, gk, dim3(256), 0, s, part_o, part_ml, L.splits, (const f16_t *)wuvt, heads,
+                     BT, d);
   if (hipGetLastError() != hipSuccess) return GDLA_ERR_HIP;
   return GDLA_OK;
 }

@@ -87,7 +87,6 @@ struct FastDecodeLayout {
   size_t qabs;   // [BT, n_H, d_c + d_r] bf16
   size_t part_o; // [BT, splits, n_H, d_c] fp32
   size_t part_ml;// [BT, splits, n_H, 2] fp32
-  size_t o;      // [BT, n_H, d_c] fp32
   size_t wuvt;   // [n_kv d_h, d_c] fp16: W_uv transposed (K-contiguous rows for the value MFMA)
   int32_t splits;
 };
@@ -101,7 +100,6 @@ FastDecodeLayout plan_fast_decode(const LayerDims &d, int32_t B, int32_t max_len
   L.qabs = add(2 * (size_t)B * d.n_heads * (d.d_c + d.d_r));
   L.part_o = add(4 * (size_t)B * L.splits * d.n_heads * d.d_c);
   L.part_ml = add(4 * (size_t)B * L.splits * d.n_heads * 2);
-  L.o = add(4 * (size_t)B * d.n_heads * d.d_c);
   L.wuvt = add(2 * (size_t)d.n_kv * d.d_h * d.d_c);
   return L;
 }

@@ -89,7 +89,7 @@ typedef enum {
 #define GDLA_MAX_DECODE_TOKENS 16
 
 /* Size of gdla_decode_noalloc's static device scratch (96 MiB): enough for a decode step of 64
- * sequences of the 4096-wide, 80-head layer at any context length (78 MiB). */
+ * sequences of the 4096-wide, 80-head layer at any context length (68 MiB). */
 #define GDLA_NOALLOC_SCRATCH_BYTES (96u * 1024u * 1024u)
 
 /* Layer sizes (picx.dev summary section 2.2).  n_heads = n_signal + n_noise, n_signal is a
