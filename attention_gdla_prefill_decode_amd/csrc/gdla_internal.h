@@ -112,9 +112,12 @@ struct StageEvents {
   hipEvent_t *ev = nullptr;
   hipStream_t s = nullptr;
   unsigned done = 0;
-  void begin(int k) { if (ev) (void)hipEventRecord(ev[2 * k], s); }
+  // (a NULL entry of the caller's array skips that record)
+  void begin(int k) { if (ev && ev[2 * k]) (void)hipEventRecord(ev[2 * k], s); }
   void end(int k) {
-    if (ev) { (void)hipEventRecord(ev[2 * k + 1], s); done |= 1u << k; }
+    if (!ev) return;
+    if (ev[2 * k + 1]) (void)hipEventRecord(ev[2 * k + 1], s);
+    done |= 1u << k;
   }
   void finish() {
     if (!ev) return;

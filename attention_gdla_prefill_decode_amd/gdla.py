@@ -68,26 +68,36 @@ STAGES = ("proj_in", "norm_append", "expand_kv", "proj_q", "attn_noise", "attn_s
 
 
 class StageTimer:
-    """2 x len(STAGES) HIP events for gdla_debug.stage_events; elapsed() gives per-stage ms."""
+    """2 x len(STAGES) HIP events for gdla_debug.stage_events; elapsed() gives per-stage ms.
+    stages: the stage names to time (default: all); the others' entries stay NULL, so the call
+    records no event for them."""
 
-    def __init__(self):
+    def __init__(self, stages=None):
+        self.stages = tuple(STAGES if stages is None else stages)
+        if any(n not in STAGES for n in self.stages):
+            raise ValueError(f"unknown stage in {self.stages}")
         self.hip = ctypes.CDLL("libamdhip64.so")
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.events = (ctypes.c_void_p * (2 * len(STAGES)))()
-        for i in range(2 * len(STAGES)):
-            ev = ctypes.c_void_p()
-            if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
-                raise RuntimeError("hipEventCreate failed")
-            self.events[i] = ev
+        for k, name in enumerate(STAGES):
+            if name not in self.stages:
+                continue
+            for i in (2 * k, 2 * k + 1):
+                ev = ctypes.c_void_p()
+                if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                    raise RuntimeError("hipEventCreate failed")
+                self.events[i] = ev
         self.ptr = ctypes.cast(self.events, ctypes.c_void_p).value
 
     def elapsed(self):
         """Per-stage milliseconds of the last call that recorded these events."""
         out = {}
         for k, name in enumerate(STAGES):
+            if name not in self.stages:
+                continue
             self.hip.hipEventSynchronize(self.events[2 * k + 1])
             ms = ctypes.c_float()
             if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.events[2 * k],
@@ -99,7 +109,8 @@ class StageTimer:
     def __del__(self):
         try:
             for i in range(2 * len(STAGES)):
-                self.hip.hipEventDestroy(self.events[i])
+                if self.events[i]:
+                    self.hip.hipEventDestroy(self.events[i])
         except Exception:
             pass
 

@@ -136,7 +136,8 @@ typedef struct {
   /* Host array of 2 * GDLA_N_STAGES caller-created hipEvent_t (or NULL).  When set, the call
    * records stage_events[2k] on `stream` before stage k and stage_events[2k + 1] after it, so a
    * caller can time every kernel of the call with hipEventElapsedTime.  Stages that a call does
-   * not run get both events recorded back to back. */
+   * not run get both events recorded back to back.  A NULL entry skips that record (to time some
+   * stages only: each record is a packet on the stream). */
   hipEvent_t *stage_events;
 } gdla_debug;
 
