@@ -255,7 +255,14 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
   f32x4 O[8][2];
 #pragma unroll
   for (int db = 0; db < 8; ++db) O[db][0] = O[db][1] = f32x4{};
-  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY};
+  // Lsum[qb]: the running softmax denominator of query 16 qb + c16, formed on the matrix cores as
+  // ones . P^T (every row of the block is the sum over the keys), from the rounded P the PV
+  // product uses
+  f32x4 Lsum[2] = {f32x4{}, f32x4{}};
+  f16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = to_op<BF>(1.0f);
 
   // Lane-dependent byte offsets of the LDS fragment reads; the rest of each address is an
   // immediate.  K fragment (kb, ks): row 16 kb + c16, chunk 4 ks + g4; the row swizzle is
@@ -328,7 +335,7 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
         const float mnew = fmaxf(m[qb], quad_max(mt[qb]));
         const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m[qb] - mnew) * a.c);
         m[qb] = mnew;
-        l[qb] *= alpha;
+        Lsum[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < 8; ++db) O[db][qb] *= alpha;
       }
@@ -338,16 +345,13 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const float ms = m[qb] == -INFINITY ? 0.f : m[qb] * a.c;
-      float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float pv = __builtin_amdgcn_exp2f(S[kb][qb][i] * a.c - ms);
-          rs += pv;
           S[kb][qb][i] = pv;
         }
-      l[qb] += rs;
     }
     f16x8 P[2][2];
 #pragma unroll
@@ -371,6 +375,12 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
       for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) O[db][qb] = mfma<BF>(vf[db & 1][ks2], P[ks2][qb], O[db][qb]);
+      if (db == 7) {
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) Lsum[qb] = mfma<BF>(ones, P[ks2][qb], Lsum[qb]);
+      }
       if (db + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
@@ -390,7 +400,7 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
   // ---- epilogue: lane holds queries 16 qb + c16 and dims 16 db + 4 g4 + i
   float lsum[2];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) lsum[qb] = quad_sum(l[qb]);
+  for (int qb = 0; qb < 2; ++qb) lsum[qb] = Lsum[qb][0];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float inv = 1.0f / lsum[qb];
