@@ -15,7 +15,7 @@
 // matrix work); each wave owns 32 query rows of one head.  In the signal launch the waves are 4
 // signal heads sharing one KV head times 2 halves of the same 64 tokens, so each K/V tile staged
 // in LDS serves all of them; in the noise launch the waves are 8 consecutive 32-token blocks of one
-// noise head.  Keys are processed in tiles of 64, all products in 16 x 16 x 32 MFMA blocks (at the
+// noise head.  (Packed documents: 4 waves, two workgroups per CU; see Shape.)  Keys are processed in tiles of 64, all products in 16 x 16 x 32 MFMA blocks (at the
 // chip's power limit they sustain a higher rate than 32 x 32 x 16 blocks for the same operand
 // reads):
 //   staging: direct global -> LDS 16-byte loads (no staging registers) into three tile buffers,
@@ -49,9 +49,16 @@ constexpr int K_CH = DQK / 8;          // 16-byte chunks per key row (24)
 constexpr int V_CH = DH / 8;           // 16-byte chunks per value row (16)
 constexpr int K_TILE = KT * DQK;       // elements of one K tile
 constexpr int V_TILE = KT * DH;        // elements of one V tile
-constexpr int NBUF = 3;                // LDS tile buffers: two tiles in flight while one is read
-constexpr int K_LOADS = K_TILE * 2 / 16 / 64 / 8;  // 16-byte K loads per wave per tile (3)
-constexpr int V_LOADS = V_TILE * 2 / 16 / 64 / 8;  // 16-byte V^T loads per wave per tile (2)
+// Workgroup shapes (NW waves): 8 waves with three tile buffers, one workgroup per CU; or 4 waves
+// with two buffers, two workgroups per CU, for packed documents, whose short query blocks make
+// each workgroup's start and end a large share of its time (the other workgroup of the CU works
+// meanwhile).
+template <int NW> struct Shape {
+  static constexpr int NBUF = NW == 8 ? 3 : 2;  // LDS tile buffers: NBUF - 1 tiles in flight
+  static constexpr int K_LOADS = K_TILE * 2 / 16 / 64 / NW;  // 16-byte K loads per wave per tile
+  static constexpr int V_LOADS = V_TILE * 2 / 16 / 64 / NW;  // 16-byte V^T loads per wave per tile
+  static constexpr int QB_SIGNAL = 8 * NW, QB_NOISE = 32 * NW;  // queries per workgroup
+};
 
 struct AttnArgs {
   // q, kx, vx hold fp16, or bf16 in the kernel's BF instantiation (16-bit lanes either way)
@@ -129,8 +136,10 @@ __device__ __forceinline__ float quad_sum(float v) {
 }
 
 // BF: q, K and V (and so P) are bf16, else fp16.
-template <bool SIGNAL, bool BF>
-__global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
+template <bool SIGNAL, bool BF, int NW>
+__global__ void __launch_bounds__(64 * NW, 8 / NW) attn_prefill_kernel(AttnArgs a) {
+  constexpr int NBUF = Shape<NW>::NBUF, K_LOADS = Shape<NW>::K_LOADS, V_LOADS = Shape<NW>::V_LOADS;
+  constexpr int QB_SIGNAL = Shape<NW>::QB_SIGNAL, QB_NOISE = Shape<NW>::QB_NOISE;
   // NBUF buffers of one key tile each: K rows, then V^T rows
   __shared__ __attribute__((aligned(16))) f16_t KV[NBUF * (K_TILE + V_TILE)];
 
@@ -145,17 +154,17 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
   int head, kvh, t0w, tlo, thi;
   if (SIGNAL) {
     kvh = yy / a.chunks;
-    const int r = (yy % a.chunks) * 4 + (wave >> 1);
+    const int r = (yy % a.chunks) * 4 + (NW == 8 ? wave >> 1 : wave);
     head = r < a.sig_per_kv ? kvh + a.n_kv * r : -1;
-    tlo = qblk * 64;
-    t0w = tlo + 32 * (wave & 1);
-    thi = min(tlo + 63, a.T - 1);
+    tlo = qblk * QB_SIGNAL;
+    t0w = tlo + (NW == 8 ? 32 * (wave & 1) : 0);
+    thi = min(tlo + QB_SIGNAL - 1, a.T - 1);
   } else {
     head = a.n_signal + yy;
     kvh = yy % a.n_kv;
-    tlo = qblk * 256;
+    tlo = qblk * QB_NOISE;
     t0w = tlo + 32 * wave;
-    thi = min(tlo + 255, a.T - 1);
+    thi = min(tlo + QB_NOISE - 1, a.T - 1);
   }
   const bool active = head >= 0 && t0w < a.T;
   const int W = a.window;
@@ -168,10 +177,12 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
     if (a.doc) lo = max(lo, min(max(a.doc[mrow0 + t], 0), p0 + t));
     return lo;
   };
-  // first key tile: from the block's first query (document starts never decrease along a packed
-  // sequence), aligned to 32 keys past `base` (the value layout's key groups); the extra keys in
-  // front are masked
-  const int klo = base + ((qlo(tlo) - base) & ~31);
+  // first key tile: from the first query of the 8-wave shape's block (document starts never
+  // decrease along a packed sequence; with 4 waves the tile grid stays that of the 8-wave block
+  // holding this one, so both shapes run every query over the same tiles), aligned to 32 keys
+  // past `base` (the value layout's key groups); the extra keys in front are masked
+  const int tgrid = SIGNAL ? tlo - tlo % Shape<8>::QB_SIGNAL : tlo - tlo % Shape<8>::QB_NOISE;
+  const int klo = base + ((qlo(tgrid) - base) & ~31);
   const int khi = p0 + thi + 1;
   const int ntiles = (khi - klo + KT - 1) / KT;
   const int wp_lo = p0 + t0w, wp_hi = p0 + min(t0w + 31, a.T - 1);
@@ -388,7 +399,7 @@ __global__ void __launch_bounds__(512, 1) attn_prefill_kernel(AttnArgs a) {
 
   for (int t = 0; t < ntiles; ++t) {
     // vmcnt(n): at most n of this wave's loads still in flight (those of tile t + 1)
-    if (t + 1 < ntiles) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(K_LOADS + V_LOADS) : "memory");
+    if (NBUF > 2 && t + 1 < ntiles) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NBUF - 2) * (K_LOADS + V_LOADS)) : "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // tile t has landed for every wave; every wave is done with tile t - 1
     if (t + NBUF - 1 < ntiles) issue(t + NBUF - 1);
@@ -579,19 +590,26 @@ gdla_status run_fast_prefill(const LayerDims &d, const gdla_weights *w, int32_t 
   a.sig_per_kv = d.n_signal / d.n_kv;
   a.chunks = (a.sig_per_kv + 3) / 4;
   a.c = d.scale * 1.4426950408889634f;
-  a.n_qblk = (T + 255) / 256;
+  // packed documents (bf16 operands): 4-wave workgroups, two per CU
+  const bool small = doc && bf_ops;
+  a.n_qblk = small ? (T + Shape<4>::QB_NOISE - 1) / Shape<4>::QB_NOISE : (T + Shape<8>::QB_NOISE - 1) / Shape<8>::QB_NOISE;
   a.ny = d.n_noise;
   se.begin(GDLA_STAGE_ATTN_NOISE);
   a.nb = B;
-  if (bf_ops) hipLaunchKernelGGL((attn_prefill_kernel<false, true>), dim3(a.n_qblk * a.ny * B), dim3(512), 0, s, a);
-  else hipLaunchKernelGGL((attn_prefill_kernel<false, false>), dim3(a.n_qblk * a.ny * B), dim3(512), 0, s, a);
+  const dim3 gn((unsigned)(a.n_qblk * a.ny * B));
+  if (small) hipLaunchKernelGGL((attn_prefill_kernel<false, true, 4>), gn, dim3(256), 0, s, a);
+  else if (bf_ops) hipLaunchKernelGGL((attn_prefill_kernel<false, true, 8>), gn, dim3(512), 0, s, a);
+  else hipLaunchKernelGGL((attn_prefill_kernel<false, false, 8>), gn, dim3(512), 0, s, a);
   if (hipGetLastError() != hipSuccess) return GDLA_ERR_HIP;
   se.end(GDLA_STAGE_ATTN_NOISE);
-  a.n_qblk = (T + 63) / 64;
+  a.n_qblk = small ? (T + Shape<4>::QB_SIGNAL - 1) / Shape<4>::QB_SIGNAL
+                   : (T + Shape<8>::QB_SIGNAL - 1) / Shape<8>::QB_SIGNAL;
   a.ny = d.n_kv * a.chunks;
   se.begin(GDLA_STAGE_ATTN_SIGNAL);
-  if (bf_ops) hipLaunchKernelGGL((attn_prefill_kernel<true, true>), dim3(a.n_qblk * a.ny * B), dim3(512), 0, s, a);
-  else hipLaunchKernelGGL((attn_prefill_kernel<true, false>), dim3(a.n_qblk * a.ny * B), dim3(512), 0, s, a);
+  const dim3 gs((unsigned)(a.n_qblk * a.ny * B));
+  if (small) hipLaunchKernelGGL((attn_prefill_kernel<true, true, 4>), gs, dim3(256), 0, s, a);
+  else if (bf_ops) hipLaunchKernelGGL((attn_prefill_kernel<true, true, 8>), gs, dim3(512), 0, s, a);
+  else hipLaunchKernelGGL((attn_prefill_kernel<true, false, 8>), gs, dim3(512), 0, s, a);
   if (hipGetLastError() != hipSuccess) return GDLA_ERR_HIP;
   se.end(GDLA_STAGE_ATTN_SIGNAL);
   return GDLA_OK;
