@@ -6,10 +6,13 @@
 //   2. every entry point with one argument made invalid at a time: the documented status comes
 //      back and gdla_last_error says why (so the check ran before any launch);
 //   3. only when the process sees no GPU: valid argument sets with a workspace large enough, which
-//      pass validation and planning and then fail at the first HIP runtime call.
+//      pass validation and planning and then fail at the first HIP runtime call;
+//   4. the value layout of the prefill attention (key order inside each 32-key group).
 // The pointers handed in are never dereferenced by host code; on a machine with a GPU part 3 is
 // skipped so that no fake pointer can reach a copy or a kernel.
 #include "gdla.h"
+// the value layout shared by the expansion GEMM's store and the prefill attention's PV operand
+#include "../attention_gdla_prefill_decode_amd/csrc/fast_paths.h"
 
 #include <hip/hip_runtime_api.h>
 
@@ -383,6 +386,24 @@ static void check_validation() {
   expect_status(DECODE, m, GDLA_ERR_UNSUPPORTED, "max_len above 2^30");
 }
 
+// The value layout: vt_key inverts vt_slot; every aligned group of 32 keys maps onto itself and
+// every aligned run of 4 keys onto 4 consecutive positions (the GEMM stores them with one 8-byte
+// write); and the PV operand's k-slot 8 g + e (lane group g, element e) of a 32-key group holds
+// key 16 (e / 4) + 4 g + e % 4, the order in which the 16 x 16 score blocks leave the keys.
+static void check_value_layout() {
+  for (int k = 0; k < 1 << 16; ++k) {
+    const int p = gdla::vt_slot(k);
+    expect(gdla::vt_key(p) == k, "vt_key(vt_slot(%d)) = %d", k, gdla::vt_key(p));
+    expect(p / 32 == k / 32, "key %d leaves its 32-group (position %d)", k, p);
+    if (k % 4) expect(p == gdla::vt_slot(k - k % 4) + k % 4, "keys %d..%d not consecutive", k - k % 4, k);
+  }
+  for (int g = 0; g < 4; ++g)
+    for (int e = 0; e < 8; ++e) {
+      const int key = 16 * (e / 4) + 4 * g + e % 4;
+      expect(gdla::vt_slot(key) == 8 * g + e, "operand slot %d holds key %d", 8 * g + e, key);
+    }
+}
+
 // The error text is per thread: a failure on one thread leaves another thread's text alone.
 static void check_error_text_per_thread() {
   gdla_dims bad = big_layer();
@@ -428,6 +449,7 @@ int main() {
   check_workspace_planning();
   check_validation();
   check_error_text_per_thread();
+  check_value_layout();
   check_valid_calls_without_gpu();
   printf("%d checks, %d failures\n", g_checks, g_failures);
   if (g_failures == 0) printf("all checks passed\n");
