@@ -964,6 +964,15 @@ hipError_t launch_backward_fast(const FastBwdArgs &a, const LayerDims &d, hipStr
   hipLaunchKernelGGL(rope_table_kernel, dim3((T_ * (dr / 2) + 255) / 256), dim3(256), 0, s, b.rope_cs, T_, dr,
                      d.theta);
   BWD_TRY(hipGetLastError());
+  // dim-major copies of q and dH for the dK/dV kernel, per sequence, tokens padded to Tp with zeros
+  at.Tp = (T_ + 31) / 32 * 32;
+  at.qT = b.qT; at.dhT = b.dhT;
+  for (int sq = 0; sq < a.B; ++sq) {
+    BWD_TRY(tpack(a.q16 + (int64_t)sq * T_ * nH * (dh + dr), (int64_t)nH * (dh + dr), T_, nH * (dh + dr), at.Tp,
+                  b.qT + (int64_t)sq * at.Tp, (int64_t)a.B * at.Tp, 0, s));
+    BWD_TRY(tpack((const f16_t *)(b.dh16 + (int64_t)sq * T_ * nH * dh), (int64_t)nH * dh, T_, nH * dh, at.Tp,
+                  b.dhT + (int64_t)sq * at.Tp, (int64_t)a.B * at.Tp, 0, s));
+  }
   // dq leaves the attention kernel already packed into a6 (dq^C, and dq^R rotated back)
   at.dq = nullptr;
   at.a6 = b.a6; at.lda6 = k6; at.q_off = nH * dh; at.rope_cs = (const float2 *)b.rope_cs;

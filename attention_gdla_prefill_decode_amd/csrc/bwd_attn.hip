@@ -9,13 +9,15 @@
 // Two kernels, so that every output has one writer and no atomics are needed:
 //   bwd_dq_kernel   query-major, like the forward: a wave holds 32 queries of one head, streams
 //                   the KV head's key tiles and accumulates dQ^T = K^T dS^T;
-//   bwd_dkv_kernel  key-major: a wave holds 32 keys of one KV head, streams the query blocks of
-//                   every head of the group and accumulates dK^T = Q^T dS and dV^T = dH^T P.
+//   bwd_dkv_kernel  key-major: a workgroup holds 128 keys of one KV head, streams the queries of
+//                   every head of the group and accumulates dK^T = Q^T dS and dV^T = dH^T P
+//                   (one wave per 32 keys and product: see the kernel).
 // All products run on v_mfma_f32_32x32x16_f16 (A[m = l % 32][k = 8 (l / 32) + i],
 // B[k = 8 (l / 32) + i][n = l % 32], acc[j] = C[8 (j / 4) + 4 (l / 32) + j % 4][l % 32]).  Where
-// an accumulator (whose rows run in that j order) feeds the next product as its B operand, the
-// matching A fragments are read with ds_read_b64_tr_b16 from a row-major tile: each 4-row group of
-// the transposing read covers one run of four consecutive rows in that order.
+// an accumulator (whose rows run in that j order) feeds the next product as its B operand, the dq
+// kernel reads the matching A fragments with ds_read_b64_tr_b16 from a row-major tile: each 4-row
+// group of the transposing read covers one run of four consecutive rows in that order.  The dK/dV
+// kernel stages a second, dim-major copy of its operands instead.
 #include "fast_paths.h"
 
 namespace gdla {
@@ -57,6 +59,16 @@ namespace {
 
 __device__ __forceinline__ void dma16v(const void *gptr, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(lds_addr) : "memory");
+}
+// The same with a wave-uniform base and a 32-bit per-lane byte offset.
+__device__ __forceinline__ void dma16s(const void *base, uint32_t voff, uint32_t lds_addr) {
+  // readfirstlane returns int: each half goes through uint32_t (no sign extension into the high half)
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  const uint64_t sbase = (uint64_t)hi << 32 | (uint64_t)lo;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory");
 }
 __device__ __forceinline__ uint32_t lds_u32(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
@@ -239,160 +251,246 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdAttnArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// dK, dV.  Workgroup (key block of 128, KV head, sequence); wave w holds keys 32 w .. 32 w + 31 of
-// the block.  The waves walk the query blocks of 64 of every head of the group together: each
-// block's Q, dH, log-sum-exp, row sum and lowest visible keys come by direct global -> LDS loads
-// (M0 + 16 lane per wave-instruction, no compiler tracking) into three buffers, two blocks in
-// flight while one is read.  A buffer is 44 wave-instructions of 64 slots of 16 bytes:
-//   Q rows 0..63 at 25 slots per row (24 of data, one of padding), then dH rows at 17 slots per
-//   row, then lse, row sum (fp32) and lowest visible key (int32) of the 64 queries, 16 slots each;
-//   padding slots receive a copy of a neighbouring chunk.
-constexpr int QB64 = 64;                       // queries per block
-constexpr int DMA_W = 11;                      // wave-instructions per wave and block
-constexpr int TB_SLOTS = 4 * DMA_W * 64;       // 2816 slots
-constexpr int TB_BYTES = TB_SLOTS * 16;        // 44 KB
-constexpr int Q_SLOTS = QB64 * 25, H_SLOTS = QB64 * 17;
-constexpr int S_OFF = (Q_SLOTS + H_SLOTS) * 16;  // bytes: lse [64], drow [64], lo [64]
+// dK, dV.  Workgroup (key block of 128, KV head, sequence): 8 waves in two roles on the four key
+// blocks kb of 32 keys, one wave of each role per SIMD:
+//   P wave (w = kb):      S = Q K^T, P = exp2(c S - lse) on the visible pairs, dV^T += dH^T P;
+//                         hands P (fp16) through LDS to
+//   dS wave (w = 4 + kb): dP = dH V^T, dS = P (.) (dP - rowsum), dK^T += Q^T dS,
+// one step behind: in iteration j the P waves take step j and the dS waves step j - 1, so the
+// two streams of a SIMD are independent between the one barrier per iteration, and one's softmax
+// or dS arithmetic runs beside the other's matrix products.
+// A step is 32 queries of one head: every head of the group, over the queries that can see the
+// key block, last query block first.  Each role stages its own operands of a step, by direct
+// global -> LDS loads, in its own ring of three slots of 24 chunks of 64 x 16 bytes (two steps in
+// flight while one is read):
+//   P ring:  Q query-major (rows of 25 slots, one of padding), the 32 queries' lse and lowest
+//            visible keys, dH dim-major (from the transposed copy dH^T: rows of 5 slots);
+//   dS ring: dH query-major (rows of 17 slots), the 32 row sums, Q dim-major (from q^T).
+// So every LDS read is a plain 16-byte read: the products summed over the queries (dK, dV) take
+// their query-contiguous A fragments from the dim-major copies instead of transposing reads, which
+// cost about three times as much per byte.  The query-major A fragments of S and dP read row R(m)
+// (bits 2 and 3 of m swapped) for accumulator row m, which makes each lane's 8 values of an
+// accumulator half 8 consecutive queries: the k order of the dim-major fragments and of P.
+constexpr int QS = 32;                     // queries per step
+constexpr int TP = 5 * 8;                  // dim-major row pitch (elements)
+constexpr int KV_DMA = 6;                  // wave-instructions per wave and step
+constexpr int RING_SLOT = 24 * 64 * 16;    // bytes of one ring slot (24 chunks)
+// P slot (in 16-byte units): Q rows 0..799, lse 800..807, lowest keys 808..815, dH^T from 832
+// (chunks 13..22; chunk 23 repeats chunk 22).  dS slot: dH rows 0..543, row sums 544..551, Q^T
+// from 576 (chunks 9..23).
+constexpr int P_ST = QS * 25, P_HT = 13 * 64, S_ST = QS * 17, S_QT = 9 * 64;
+static_assert(P_ST + 16 <= P_HT && P_HT + DH * 5 == 23 * 64 && S_ST + 8 <= S_QT && S_QT + DQK * 5 == 24 * 64,
+              "regions fit their slots");
+constexpr int KV_LDS = 6 * RING_SLOT;      // then the P exchange: [2 steps][4 key blocks][2][64 lanes] f16x8
 
-__global__ void __launch_bounds__(256, 1) bwd_dkv_kernel(BwdAttnArgs a) {
-  __shared__ __attribute__((aligned(16))) char SM[3 * TB_BYTES];
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int per_k = a.n_kv * a.B;
-  const int kblk = (int)blockIdx.x / per_k;  // longest work (first keys) first
-  const int kvh = (int)blockIdx.x % per_k % a.n_kv, b = (int)blockIdx.x % per_k / a.n_kv;
-  const int kb0 = 128 * kblk;
-  const int64_t M = (int64_t)a.B * a.T;
-  // queries kb0 .. q_end - 1 can see a key of the block: lowest visible keys never decrease
-  int lo_q = kb0, hi_q = a.T;
-  while (lo_q < hi_q) {
-    const int mid = (lo_q + hi_q) >> 1;
-    if (qlo(a, b, mid) > kb0 + 127) hi_q = mid;
-    else lo_q = mid + 1;
-  }
-  const int qb0 = kb0 / QB64, nqb = max(0, (lo_q - kb0 + QB64 - 1) / QB64);
-  const int sig_g = a.n_signal / a.n_kv, n_g = a.n_heads / a.n_kv;
-  const int n_it = n_g * nqb;
+struct DkvUnit {
+  int b, kvh, kb0, qb0, nqb, n_it, sig_g;
+};
 
-  // this wave's keys: K^T and V^T as B operands (B[k = dim][n = key])
-  const int key = kb0 + 32 * wave + (lane & 31);
+template <bool PW>
+__device__ __forceinline__ void dkv_body(const BwdAttnArgs &a, const DkvUnit &u, char *SM, f16x8 (*PX)[4][2][64],
+                                         int wave, int lane) {
+  const int kb = wave & 3, h2 = lane >> 5;
+  const int key = u.kb0 + 32 * kb + (lane & 31);
   const int keyc = min(key, a.T - 1);
-  const f16_t *kg = a.k + (((int64_t)b * a.n_kv + kvh) * a.lcap + keyc) * DQK;
-  const f16_t *vg = a.v + (((int64_t)b * a.n_kv + kvh) * a.lcap + keyc) * DH;
-  f16x8 Kf[12], Vf[8];
+  const int rq = (lane & 19) | ((lane & 4) << 1) | ((lane & 8) >> 1);  // R(lane % 32)
+  const int64_t kvrow = ((int64_t)u.b * a.n_kv + u.kvh) * a.lcap + keyc;
+  // this wave's keys as B operands (B[k = dim][n = key]): K^T for a P wave, V^T for a dS wave
+  constexpr int NF = PW ? 12 : 8;
+  f16x8 F[NF];
+  const f16_t *fg = PW ? a.k + kvrow * DQK : a.v + kvrow * DH;
 #pragma unroll
-  for (int k = 0; k < 12; ++k) Kf[k] = *(const f16x8 *)(kg + 16 * k + 8 * (lane >> 5));
-#pragma unroll
-  for (int k = 0; k < 8; ++k) Vf[k] = *(const f16x8 *)(vg + 16 * k + 8 * (lane >> 5));
-  // the key fragments have landed before any block load is issued (the block waits below count
-  // only those loads)
+  for (int k = 0; k < NF; ++k) F[k] = *(const f16x8 *)(fg + 16 * k + 8 * h2);
+  // the key fragments have landed before any step load is issued (the waits below count only those)
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  f32x16 dK[6], dV[4];
+  constexpr int NACC = PW ? 4 : 6;  // dV^T: 4 dim blocks of 32; dK^T: 6
+  f32x16 acc[NACC];
 #pragma unroll
-  for (int i = 0; i < 6; ++i) dK[i] = f32x16{};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) dV[i] = f32x16{};
+  for (int i = 0; i < NACC; ++i) acc[i] = f32x16{};
 
-  auto head_of = [&](int gi) { return gi < sig_g ? kvh + a.n_kv * gi : a.n_signal + kvh + a.n_kv * (gi - sig_g); };
-  // block `it` into buffer it % 3: this lane's DMA_W slots are (wave + 4 i) * 64 + lane
-  const uint32_t lds0 = lds_u32(SM);
-  auto issue = [&](int it) {
-    const int h = head_of(it / nqb), qbase = QB64 * (qb0 + it % nqb);
-    const int64_t mrow = (int64_t)b * a.T;
-    const uint32_t buf = lds0 + (uint32_t)((it % 3) * TB_BYTES);
+  auto head_of = [&](int gi) {
+    return gi < u.sig_g ? u.kvh + a.n_kv * gi : a.n_signal + u.kvh + a.n_kv * (gi - u.sig_g);
+  };
+  const int n_g = a.n_heads / a.n_kv, qlast = u.qb0 + u.nqb - 1;
+  const int64_t ldt = (int64_t)a.B * a.Tp, bT = (int64_t)u.b * a.T, bTp = (int64_t)u.b * a.Tp, M = (int64_t)a.B * a.T;
+  const uint32_t ring = lds_u32(SM) + (PW ? 0u : 3u * RING_SLOT);
+  // Staging loads: instruction i fills chunk c = kb + 4 i of the role's slot (wave-uniform region);
+  // lane l takes unit 64 c + l of it.  Most are a wave-uniform base (head, query block) plus the
+  // lane's byte offset, fixed for every step but a sequence's last block, whose rows past the last
+  // token read the last token's row instead (finite, never visible).  (The offsets stay below
+  // 2^32: the fused path takes at most 2^23 padded tokens.)  The chunk that mixes the last rows
+  // with the statistics takes full per-lane addresses.  Padding units copy a unit of the step.
+  const uint32_t rowq = (uint32_t)a.n_heads * DQK * 2, rowh = (uint32_t)a.n_heads * DH * 2, ldtb = (uint32_t)(ldt * 2);
+  auto lane_off = [&](int c, int rmax) -> uint32_t {
+    if (PW && c < 13) {
+      const int s = 64 * c + lane;
+      return (uint32_t)min(s / 25, rmax) * rowq + 16u * (uint32_t)min(s % 25, 23);
+    }
+    if (PW) {
+      const int s = 64 * (min(c, 22) - 13) + lane;
+      return (uint32_t)(s / 5) * ldtb + 16u * (uint32_t)min(s % 5, 3);
+    }
+    if (c < 9) {
+      const int s = 64 * c + lane;
+      return (uint32_t)min(s / 17, rmax) * rowh + 16u * (uint32_t)min(s % 17, 15);
+    }
+    const int s = 64 * (c - 9) + lane;
+    return (uint32_t)(s / 5) * ldtb + 16u * (uint32_t)min(s % 5, 3);
+  };
+  uint32_t off[KV_DMA];
 #pragma unroll
-    for (int i = 0; i < DMA_W; ++i) {
-      const int slot = (wave + 4 * i) * 64 + lane;
-      const void *src;
-      if (slot < Q_SLOTS) {
-        const int r = slot / 25, c = min(slot % 25, 23);
-        const int t = min(qbase + r, a.T - 1);
-        src = a.q + ((mrow + t) * a.n_heads + h) * DQK + 8 * c;
-      } else if (slot < Q_SLOTS + H_SLOTS) {
-        const int s2 = slot - Q_SLOTS, r = s2 / 17, c = min(s2 % 17, 15);
-        const int t = min(qbase + r, a.T - 1);
-        src = a.dh + ((mrow + t) * a.n_heads + h) * DH + 8 * c;
-      } else {
-        const int s3 = min(slot - Q_SLOTS - H_SLOTS, 47), part = s3 >> 4, k4 = 4 * (s3 & 15);
-        // the three arrays carry 64 entries of padding past their end
-        if (part == 0) src = a.lse + (int64_t)h * M + mrow + qbase + k4;
-        else if (part == 1) src = a.drow + (int64_t)h * M + mrow + qbase + k4;
-        else src = a.lo + mrow + qbase + k4;
+  for (int i = 0; i < KV_DMA; ++i) off[i] = lane_off(kb + 4 * i, QS - 1);
+  auto issue = [&](int st) {  // step st into slot st % 3
+    const int h = head_of(st % n_g), qbase = QS * (qlast - st / n_g);
+    const uint32_t slot = ring + (uint32_t)((st % 3) * RING_SLOT);
+    const int rmax = min(QS - 1, a.T - 1 - qbase);
+#pragma unroll
+    for (int i = 0; i < KV_DMA; ++i) {
+      const int c = kb + 4 * i;
+      const uint32_t lds = __builtin_amdgcn_readfirstlane(slot + (uint32_t)(c * 64 * 16));
+      if (c == (PW ? 12 : 8)) {  // last rows, then the statistics (their arrays carry 32 entries of padding)
+        const int s = 64 * c + lane;
+        const void *src;
+        if (PW && s < P_ST) {
+          src = a.q + ((bT + qbase + min(s / 25, rmax)) * a.n_heads + h) * DQK + 8 * min(s % 25, 23);
+        } else if (!PW && s < S_ST) {
+          src = a.dh + ((bT + qbase + min(s / 17, rmax)) * a.n_heads + h) * DH + 8 * min(s % 17, 15);
+        } else {
+          const int e = min(s - (PW ? P_ST : S_ST), PW ? 15 : 7);  // lse 0..7, lowest keys 8..15; row sums 0..7
+          src = PW ? (e < 8 ? (const void *)(a.lse + h * M + bT + qbase + 4 * e) : (const void *)(a.lo + bT + qbase + 4 * (e - 8)))
+                   : (const void *)(a.drow + h * M + bT + qbase + 4 * e);
+        }
+        dma16v(src, lds);
+        continue;
       }
-      dma16v(src, __builtin_amdgcn_readfirstlane(buf + (uint32_t)((wave + 4 * i) * 64 * 16)));
+      const f16_t *base;
+      if (PW && c < 13) base = a.q + ((bT + qbase) * a.n_heads + h) * DQK;
+      else if (PW) base = a.dhT + (int64_t)h * DH * ldt + bTp + qbase;
+      else if (c < 9) base = a.dh + ((bT + qbase) * a.n_heads + h) * DH;
+      else base = a.qT + (int64_t)h * DQK * ldt + bTp + qbase;
+      dma16s(base, rmax < QS - 1 ? lane_off(c, rmax) : off[i], lds);
     }
   };
 
-  for (int it = 0; it < 2 && it < n_it; ++it) issue(it);
-  for (int it = 0; it < n_it; ++it) {
-    // at most this wave's loads of block it + 1 still in flight
-    if (it + 1 < n_it) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DMA_W) : "memory");
+  // P waves: step j in iteration j (two steps in flight); dS waves: step j - 1 (issued one
+  // iteration later, also two in flight).  One more iteration than steps.
+  const int lag = PW ? 0 : 1;
+  for (int st = 0; st < 2 - lag && st < u.n_it; ++st) issue(st);
+  for (int j = 0; j <= u.n_it; ++j) {
+    const int st = j - lag;  // this wave's step
+    // at most this wave's loads of step st + 1 still in flight
+    if (st + 1 < u.n_it) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KV_DMA) : "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // block it has landed for every wave; every wave is done with block it - 1
-    if (it + 2 < n_it) issue(it + 2);
-    const int qblock = QB64 * (qb0 + it % nqb);
-    const char *base = SM + (it % 3) * TB_BYTES;
-    const f16_t *qs0 = (const f16_t *)base, *hs0 = (const f16_t *)(base + Q_SLOTS * 16);
-    const float *ls = (const float *)(base + S_OFF);
-    const int *los = (const int *)(base + S_OFF + 2 * QB64 * 4);
+    // steps j and j - 1 have landed for every wave; every wave is done with their previous steps
+    __syncthreads();
+    if (st + 2 < u.n_it) issue(st + 2);
+    if (st < 0 || st >= u.n_it) continue;
+    const int qbase = QS * (qlast - st / n_g);
+    const char *base = SM + (PW ? 0 : 3 * RING_SLOT) + (st % 3) * RING_SLOT;
+    // query-major product over the dims (S or dP): row m = query R(m), column = this lane's key.
+    // The 16 values of a lane are queries qbase + 16 kk + 8 h2 + i at index 8 kk + i.
+    const f16_t *rows = (const f16_t *)base + rq * (PW ? KP : VP) + 8 * h2;
+    // (at most 8 fragments in registers: the P wave reads its last four after the first products)
+    f16x8 A[NF];
 #pragma unroll
-    for (int qh = 0; qh < QB64 / 32; ++qh) {
-      const int qbase = qblock + 32 * qh;
-      const f16_t *qs = qs0 + 32 * qh * KP, *hs = hs0 + 32 * qh * VP;
-      f32x16 S = {}, dP = {};
+    for (int k = 0; k < 8; ++k) A[k] = *(const f16x8 *)(rows + 16 * k);
+    f32x16 X = {};
 #pragma unroll
-      for (int k = 0; k < 12; ++k) S = mfma(*(const f16x8 *)(qs + (lane & 31) * KP + 16 * k + 8 * (lane >> 5)), Kf[k], S);
+    for (int k = 0; k < NF - 4; ++k) X = mfma(A[k], F[k], X);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) dP = mfma(*(const f16x8 *)(hs + (lane & 31) * VP + 16 * k + 8 * (lane >> 5)), Vf[k], dP);
-      // acc[j]: query qbase + qi, qi = 8 (j / 4) + 4 (l / 32) + j % 4; key `key`.  The 16 queries
-      // of a lane are four runs of four: their lse, row sums and lowest keys are 16-byte reads.
-      float4 lv[4], dv4[4];
-      int4 lov[4];
+    for (int k = 8; k < NF; ++k) A[k] = *(const f16x8 *)(rows + 16 * k);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int q4 = 32 * qh + 8 * g + 4 * (lane >> 5);
-        lv[g] = *(const float4 *)(ls + q4);
-        dv4[g] = *(const float4 *)(ls + QB64 + q4);
-        lov[g] = *(const int4 *)(los + q4);
-      }
-      f16x8 pf[2], dsf[2];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int g = j >> 2, e = j & 3;
-        const int t = qbase + 8 * g + 4 * (lane >> 5) + e;
-        const float lse_q = e == 0 ? lv[g].x : e == 1 ? lv[g].y : e == 2 ? lv[g].z : lv[g].w;
-        const float dr_q = e == 0 ? dv4[g].x : e == 1 ? dv4[g].y : e == 2 ? dv4[g].z : dv4[g].w;
-        const int lo_q = e == 0 ? lov[g].x : e == 1 ? lov[g].y : e == 2 ? lov[g].z : lov[g].w;
-        const bool vis = key <= t && t < a.T && key >= lo_q;
-        const float p = vis ? __builtin_amdgcn_exp2f(S[j] * a.c - lse_q) : 0.f;
-        pf[j >> 3][j & 7] = h16(p);
-        dsf[j >> 3][j & 7] = h16(vis ? p * (dP[j] - dr_q) : 0.f);
-      }
+    for (int k = NF - 4; k < NF; ++k) X = mfma(A[k], F[k], X);
+    __builtin_amdgcn_sched_barrier(0);  // the second product's fragments stay below (registers)
+    f16x8 pf[2];
+    const float *stt = (const float *)(base + 16 * (PW ? P_ST : S_ST));
+    if constexpr (PW) {
+      const int *los = (const int *)(stt + QS);
+      // every pair of the step visible (wave-uniform): all queries at or after the wave's last key
+      // and inside the sequence, and the last query's lowest visible key (lowest keys never
+      // decrease) at or before the wave's first key
+      const int kfirst = u.kb0 + 32 * kb;
+      const bool full = qbase >= kfirst + 31 && qbase + QS <= a.T &&
+                        __builtin_amdgcn_readfirstlane(los[QS - 1]) <= kfirst;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
+        const int q8 = 16 * kk + 8 * h2;
+        const float4 l0 = *(const float4 *)(stt + q8), l1 = *(const float4 *)(stt + q8 + 4);
+        const float lse8[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+        if (full) {
 #pragma unroll
-        for (int eb = 0; eb < 4; ++eb) dV[eb] = mfma(tr_frag(hs, VP, 16 * kk, 32 * eb, lane), pf[kk], dV[eb]);
+          for (int i = 0; i < 8; ++i) pf[kk][i] = h16(__builtin_amdgcn_exp2f(X[8 * kk + i] * a.c - lse8[i]));
+        } else {
+          const int4 o0 = *(const int4 *)(los + q8), o1 = *(const int4 *)(los + q8 + 4);
+          const int lo8[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
 #pragma unroll
-        for (int db = 0; db < 6; ++db) dK[db] = mfma(tr_frag(qs, KP, 16 * kk, 32 * db, lane), dsf[kk], dK[db]);
+          for (int i = 0; i < 8; ++i) {
+            const int t = qbase + q8 + i;
+            const bool vis = key <= t && t < a.T && key >= lo8[i];
+            pf[kk][i] = h16(vis ? __builtin_amdgcn_exp2f(X[8 * kk + i] * a.c - lse8[i]) : 0.f);
+          }
+        }
+        PX[st & 1][kb][kk][lane] = pf[kk];
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int q8 = 16 * kk + 8 * h2;
+        const float4 d0 = *(const float4 *)(stt + q8), d1 = *(const float4 *)(stt + q8 + 4);
+        const float dr8[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+        const f16x8 p8 = PX[st & 1][kb][kk][lane];  // written by this SIMD's P wave last iteration
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float p = (float)p8[i];
+          pf[kk][i] = h16(p != 0.f ? p * (X[8 * kk + i] - dr8[i]) : 0.f);  // dS
+        }
       }
     }
+    // the product over the queries (dV or dK): dim-major A fragments, row = dim 32 blk + l % 32,
+    // queries 16 kk + 8 h2 ..
+    const f16_t *cols = (const f16_t *)(base + 16 * (PW ? P_HT : S_QT)) + (lane & 31) * TP + 8 * h2;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int blk = 0; blk < NACC; ++blk) acc[blk] = mfma(*(const f16x8 *)(cols + 32 * blk * TP + 16 * kk), pf[kk], acc[blk]);
   }
   if (key >= a.T) return;
-  // dK[db][j] = dK^T[dim 32 db + 8 (j / 4) + 4 (l / 32) + j % 4][key]
-  const int64_t ko = ((int64_t)b * a.n_kv + kvh) * a.T + key;
-  float *dk = a.dk + ko * DQK, *dv = a.dv + ko * DH;
+  // acc[blk][j] = (dK^T or dV^T)[dim 32 blk + 8 (j / 4) + 4 (l / 32) + j % 4][key]
+  const int64_t ko = ((int64_t)u.b * a.n_kv + u.kvh) * a.T + key;
+  const float sc = PW ? 1.f : a.tau;
+  float *o = PW ? a.dv + ko * DH : a.dk + ko * DQK;
 #pragma unroll
-  for (int db = 0; db < 6; ++db)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *(float4 *)(dk + 32 * db + 8 * i + 4 * (lane >> 5)) =
-          make_float4(dK[db][4 * i] * a.tau, dK[db][4 * i + 1] * a.tau, dK[db][4 * i + 2] * a.tau,
-                      dK[db][4 * i + 3] * a.tau);
-#pragma unroll
-  for (int eb = 0; eb < 4; ++eb)
+  for (int blk = 0; blk < NACC; ++blk)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      *(float4 *)(dv + 32 * eb + 8 * i + 4 * (lane >> 5)) =
-          make_float4(dV[eb][4 * i], dV[eb][4 * i + 1], dV[eb][4 * i + 2], dV[eb][4 * i + 3]);
+      *(float4 *)(o + 32 * blk + 8 * i + 4 * h2) =
+          make_float4(acc[blk][4 * i] * sc, acc[blk][4 * i + 1] * sc, acc[blk][4 * i + 2] * sc, acc[blk][4 * i + 3] * sc);
+}
+
+__global__ void __launch_bounds__(512, 1) bwd_dkv_kernel(BwdAttnArgs a) {
+  __shared__ __attribute__((aligned(16))) char SM[KV_LDS];
+  __shared__ __attribute__((aligned(16))) f16x8 PX[2][4][2][64];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int per_k = a.n_kv * a.B;
+  DkvUnit u;
+  const int kblk = (int)blockIdx.x / per_k;  // longest work (first keys) first
+  u.kvh = (int)blockIdx.x % per_k % a.n_kv;
+  u.b = (int)blockIdx.x % per_k / a.n_kv;
+  u.kb0 = 128 * kblk;
+  // queries kb0 .. lo_q - 1 can see a key of the block: lowest visible keys never decrease
+  int lo_q = u.kb0, hi_q = a.T;
+  while (lo_q < hi_q) {
+    const int mid = (lo_q + hi_q) >> 1;
+    if (qlo(a, u.b, mid) > u.kb0 + 127) hi_q = mid;
+    else lo_q = mid + 1;
+  }
+  u.qb0 = u.kb0 / QS;
+  u.nqb = max(0, (lo_q - u.kb0 + QS - 1) / QS);
+  u.sig_g = a.n_signal / a.n_kv;
+  u.n_it = (a.n_heads / a.n_kv) * u.nqb;
+  if (wave < 4) dkv_body<true>(a, u, SM, PX, wave, lane);  // wave-uniform: each wave runs its role
+  else dkv_body<false>(a, u, SM, PX, wave, lane);
 }
 
 }  // namespace
@@ -410,7 +508,7 @@ hipError_t launch_bwd_attention(const BwdAttnArgs &a0, hipStream_t s) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3((unsigned)(nq128 * a.n_noise * a.B)), dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dkv_kernel, dim3((unsigned)(nk * a.n_kv * a.B)), dim3(256), 0, s, a);  // 128-key blocks
+  hipLaunchKernelGGL(bwd_dkv_kernel, dim3((unsigned)(nk * a.n_kv * a.B)), dim3(512), 0, s, a);  // 128-key blocks
   return hipGetLastError();
 }
 

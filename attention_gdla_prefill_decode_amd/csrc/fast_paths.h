@@ -118,6 +118,9 @@ struct BwdAttnArgs {
   const f16_t *k;      // [B, n_kv, lcap, 192]: K^C ; k^R of keys 0 .. lcap - 1
   const f16_t *v;      // [B, n_kv, lcap, 128]: V, key-major
   const f16_t *dh;     // [M, n_H, 128]
+  // dim-major copies for the dK/dV kernel: element (token t of sequence b, head h, dim j) at
+  // (h 192 + j) B Tp + b Tp + t of qT (h 128 + j of dhT); tokens T .. Tp - 1 hold zeros
+  const f16_t *qT, *dhT;
   const float *lse;    // [n_H, M] (+32 padding): log2 softmax denominators of c s
   const float *drow;   // [n_H, M] (+32 padding): rowsum(dH (.) H)
   const int32_t *lo;   // [M] (+32 padding): lowest visible key of every token
@@ -133,6 +136,7 @@ struct BwdAttnArgs {
   float *dk;           // [B, n_kv, T, 192]: the k^R part summed over this KV group's heads only
   float *dv;           // [B, n_kv, T, 128]
   int32_t B, T, lcap, n_heads, n_signal, n_noise, n_kv, window;
+  int32_t Tp;          // T rounded up to a multiple of 32
   int32_t sig_chunks;  // dq, signal heads: workgroups of 4 heads per KV head
   float c, tau;
 };
@@ -151,6 +155,7 @@ struct FastBwdBuffers {
   float *dheads, *gscale, *dlaml, *drow;  // dheads unused (combine_row_kernel writes dH in fp16);
                                          // gscale: kGradScaleBlocks maxima of |dout|, then (s, 1/s)
   f16_t *dh16;                  // [M, n_H, d_h]
+  f16_t *qT, *dhT;              // dim-major copies of q and dH (see BwdAttnArgs)
   float *dq, *dk, *dv;          // attention gradients (dq unused: the dq kernel packs into a6)
   f16_t *a6, *a3, *a8;          // gradient operands [M, k6], [M, k3], [M, k8]
   float *dkr, *dcbar, *dckv, *rkv, *dcq, *daq, *rq;

@@ -317,7 +317,7 @@ BackwardLayout plan_backward(const LayerDims &d, int32_t B, int32_t T) {
 struct FastBackwardLayout {
   PrefillLayout pre;
   size_t cache, out, heads, lse, vk;
-  size_t fb[29];  // FastBwdBuffers fields, in order
+  size_t fb[31];  // FastBwdBuffers fields, in order
   size_t total;
   int32_t M_pad, k8;
   bool ok;
@@ -327,7 +327,9 @@ FastBackwardLayout plan_backward_fast(const LayerDims &d, int32_t B, int32_t T) 
   FastBackwardLayout L{};
   // (positions 0 .. T-1 of every sequence: the bound over all positions is exact here)
   L.pre = plan_prefill(d, GDLA_BF16, B, T, nullptr, T);
-  L.ok = L.pre.use_fast && L.pre.use_nt && fast_backward_supported(d, GDLA_BF16);
+  // (the dK/dV kernel addresses the dim-major copies with 32-bit offsets: at most 2^23 padded tokens)
+  L.ok = L.pre.use_fast && L.pre.use_nt && fast_backward_supported(d, GDLA_BF16) &&
+         (int64_t)B * ((T + 31) / 32 * 32) <= ((int64_t)1 << 23);
   if (!L.ok) return L;
   const size_t M = (size_t)B * T, nH = d.n_heads, nS = d.n_signal, nKV = d.n_kv;
   L.M_pad = (int32_t)((M + 63) / 64 * 64);
@@ -341,21 +343,23 @@ FastBackwardLayout plan_backward_fast(const LayerDims &d, int32_t B, int32_t T) 
   L.heads = p.add(4 * M * nH * dh);
   L.lse = p.add(4 * (M * nH + 32));  // head-major, 32 entries of padding
   L.vk = p.add(2 * (size_t)B * nKV * L.pre.lcap * dh);
+  const size_t BTp = (size_t)B * ((T + 31) / 32 * 32);  // dim-major copies: B rows of T rounded to 32
   const size_t trows_a = std::max({nS * dh, (size_t)d.d_c, (size_t)d.d_cq, dm});
   const size_t trows_b = std::max({dm, k3, k6, k8});
-  const size_t bytes[29] = {
+  const size_t bytes[31] = {
       2 * nS * dh * dm, 2 * d.d_c * k3, 2 * d.d_cq * k6, 2 * dm * k8,      // wo16 w3 w6 w8
       2 * M * dm, 4 * M * nS * dh,                                          // dout16 dy
       2 * trows_a * Mp, 2 * trows_b * Mp,                                   // ta tb
       0, 4 * (kGradScaleBlocks + 2), 4 * M * nS, 4 * (M * nH + 32),         // (dheads: unused) gscale dlaml drow
       2 * M * nH * dh,                                                      // dh16
+      2 * nH * (dh + dr) * BTp, 2 * nH * dh * BTp,                          // qT dhT
       0, 4 * M * nKV * (dh + dr), 4 * M * nKV * dh,                         // dq (packed by the kernel) dk dv
       2 * M * k6, 2 * M * k3, 2 * M * k8,                                   // a6 a3 a8
       4 * M * dr, 4 * M * d.d_c, 4 * M * d.d_c, 4 * M, 4 * M * d.d_cq, 4 * M * d.d_cq, 4 * M,
       4 * (M + 32), 8 * (size_t)T * (dr / 2),                             // lo rope_cs
       kSplitKBytes};                                                        // splitk
-  static_assert(sizeof(FastBwdBuffers) == 29 * sizeof(void *), "one size per buffer");
-  for (int i = 0; i < 29; ++i) L.fb[i] = p.add(bytes[i]);
+  static_assert(sizeof(FastBwdBuffers) == 31 * sizeof(void *), "one size per buffer");
+  for (int i = 0; i < 31; ++i) L.fb[i] = p.add(bytes[i]);
   L.total = p.bytes;
   return L;
 }
@@ -1021,7 +1025,7 @@ gdla_status backward_fast(const gdla_dims *dims, const gdla_weights *w, const vo
   a.y16 = at<f16_t>(ws, PL.y);
   a.lam_overridden = fdbg.lambda_override ? 1 : 0;
   void **bufs = (void **)&a.buf;
-  for (int i = 0; i < 29; ++i) bufs[i] = at<void>(ws, F.fb[i]);
+  for (int i = 0; i < 31; ++i) bufs[i] = at<void>(ws, F.fb[i]);
   a.B = B; a.T = T; a.M = M; a.M_pad = F.M_pad; a.lcap = PL.lcap; a.k8 = F.k8;
   HIP_TRY(launch_backward_fast(a, d, stream));
   return GDLA_OK;
