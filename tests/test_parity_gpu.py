@@ -260,11 +260,15 @@ def test_backward_matches_oracle(cfg, T, batch, window, lens):
 # weights each rounded once to fp16, 2^-11 relative), fp32 accumulation, on top of the forward's
 # own roundings (bf16 cache rows, 2^-9).  The deepest gradients pass about eight such roundings:
 # about 2.3e-3 in quadrature, so 1e-2 leaves a factor of four.
+# The short cases put one token, or a ragged 13, in each sequence's last 32-query block, with
+# the transposed copies of q and dH padded per sequence.
 @pytest.mark.parametrize("cfg,T,batch,window,lens", [
     (BF, 300, 1, 0, None),
     (BF, 160, 2, 20, (37, 90, 33)),
     (H.BF80, 256, 1, 0, None),
     (H.BF72, 270, 1, 64, (200, 70)),
+    (BF, 33, 8, 0, None),
+    (BF, 45, 6, 12, (20, 25)),
 ])
 def test_backward_fused_matches_oracle(cfg, T, batch, window, lens):
     docs = None if lens is None else [H.doc_starts(0, lens) for _ in range(batch)]
