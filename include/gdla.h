@@ -320,9 +320,10 @@ typedef struct {
  * section "Distributed Training System"); nothing from an earlier forward is needed.
  * dbg->lambda_override, when given, fixes lambda as in the forward (then no gradient flows
  * through W_lambda).  Workspace: gdla_workspace_bytes(dims, GDLA_OP_BACKWARD, B, T, NULL, T).
- * bf16 layers with d_head 128, d_rope 64 and at least 256 rows take the fused path (fp16 MFMA
- * operands, fp32 accumulation: about 3e-3 relative error per gradient); the rest compute in
- * fp32.  The fused path scales dout by a power of two computed on the device from its largest
+ * bf16 layers with d_head 128, d_rope 64, d_model, d_q_latent and d_kv_latent multiples of 64 and
+ * signal and noise head counts multiples of n_kv take the fused path when B T >= 256, T >= 32 and B times T rounded up to
+ * 32 is at most 2^23 (fp16 MFMA operands, fp32 accumulation: about 3e-3 relative error per
+ * gradient); the rest compute in fp32.  The fused path scales dout by a power of two computed on the device from its largest
  * magnitude (and the gradients back), so upstream gradients of any scale keep fp16 precision.  Every gradient has a single writer (no atomics), so repeated calls give identical bits.
  * Errors as gdla_prefill, plus GDLA_ERR_INVALID_ARG for a NULL gradient pointer. */
 gdla_status gdla_backward(const gdla_dims *dims, const gdla_weights *w, const void *x, int32_t B,
