@@ -89,9 +89,11 @@ __device__ __forceinline__ int qlo(const BwdAttnArgs &a, int b, int t) {
 // of 24 KB, so two workgroups (two waves per SIMD, at most 256 registers each) share a CU and
 // one's softmax and waits overlap the other's matrix work.
 constexpr int DQ_KT = 32;                       // keys per tile
-constexpr int KT_W = 6;                         // wave-instructions per wave and key tile
+constexpr int KT_W = 6;                         // wave-instructions per wave and key tile (at most)
 constexpr int KT_BYTES = 4 * KT_W * 64 * 16;    // 24 KB
-constexpr int K_SLOTS = DQ_KT * 25, V_SLOTS = DQ_KT * 17;
+// K rows in chunks 0..12 of 64 slots (800 slots used), V rows in chunks 13..21 (544 used)
+constexpr int VC0 = 13, KT_CHUNKS = 22;
+static_assert(DQ_KT * 25 <= VC0 * 64 && DQ_KT * 17 <= (KT_CHUNKS - VC0) * 64, "tile regions");
 
 template <bool SIGNAL>
 __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdAttnArgs a) {
@@ -144,38 +146,50 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(BwdAttnArgs a) {
   // the query fragments have landed before any tile load is issued (the tile waits below count
   // only those loads)
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  // tile t into buffer t % 3; rows past the last key read the last valid row instead (finite,
-  // never visible)
+  // Tile t into buffer t % 3: instruction i of this wave fills chunk c = wave + 4 i (a
+  // wave-uniform region; waves 2 and 3 have no sixth chunk), lane l unit 64 c' + l of its region.
+  // Each load is a wave-uniform base (the tile's first key) plus the lane's fixed byte offset; in
+  // the last tile, rows past the last key read the last key's row instead (finite, never visible).
+  // (The offsets are recomputed at each tile, a few integer operations: kept in registers they
+  // would be spilled, and each reload would wait for every load in flight.)
   const uint32_t lds0 = lds_u32(KV);
   auto issue = [&](int t) {
     const int s0 = klo + DQ_KT * t;
     const uint32_t buf = lds0 + (uint32_t)((t % 3) * KT_BYTES);
+    const int rmax = min(DQ_KT - 1, a.T - 1 - s0);
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // keeps the offsets below inside the loop
 #pragma unroll
     for (int i = 0; i < KT_W; ++i) {
-      const int slot = (wave + 4 * i) * 64 + lane;
-      const void *src;
-      if (slot < K_SLOTS) {
-        const int r = slot / 25, c = min(slot % 25, 23);
-        src = kg + (int64_t)min(s0 + r, a.T - 1) * DQK + 8 * c;
-      } else if (slot < K_SLOTS + V_SLOTS) {
-        const int s2 = slot - K_SLOTS, r = s2 / 17, c = min(s2 % 17, 15);
-        src = vg + (int64_t)min(s0 + r, a.T - 1) * DH + 8 * c;
+      const int c = wave + 4 * i;
+      if (c >= KT_CHUNKS) continue;
+      uint32_t off;
+      if (c < VC0) {
+        const int s = 64 * c + ln;
+        off = (uint32_t)min(s / 25, rmax) * (DQK * 2) + 16u * (uint32_t)min(s % 25, 23);
       } else {
-        src = kg;
+        const int s = 64 * (c - VC0) + ln;
+        off = (uint32_t)min(s / 17, rmax) * (DH * 2) + 16u * (uint32_t)min(s % 17, 15);
       }
-      dma16v(src, __builtin_amdgcn_readfirstlane(buf + (uint32_t)((wave + 4 * i) * 64 * 16)));
+      dma16s(c < VC0 ? (const void *)(kg + (int64_t)s0 * DQK) : (const void *)(vg + (int64_t)s0 * DH), off,
+             __builtin_amdgcn_readfirstlane(buf + (uint32_t)(c * 64 * 16)));
     }
   };
 
   for (int t = 0; t < 2 && t < ntiles; ++t) issue(t);
   for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KT_W) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // at most this wave's loads of tile t + 1 still in flight (6 per tile, 5 for waves 2 and 3)
+    if (t + 1 < ntiles) {
+      if (wave < 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KT_W) : "memory");
+      else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KT_W - 1) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     __syncthreads();  // tile t has landed for every wave; every wave is done with tile t - 1
     if (t + 2 < ntiles) issue(t + 2);
     const int s0 = klo + DQ_KT * t;
     const f16_t *ks = (const f16_t *)(KV + (t % 3) * KT_BYTES);
-    const f16_t *vs = (const f16_t *)(KV + (t % 3) * KT_BYTES + K_SLOTS * 16);
+    const f16_t *vs = (const f16_t *)(KV + (t % 3) * KT_BYTES + VC0 * 64 * 16);
     const bool skip = !active || s0 > wq_hi || s0 + DQ_KT - 1 < wlo_min;
     if (!skip) {
       const bool full = s0 + DQ_KT - 1 <= q0 && s0 >= wlo_max;
