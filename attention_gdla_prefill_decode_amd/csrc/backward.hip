@@ -737,8 +737,18 @@ __global__ void __launch_bounds__(64) rms_bwd_kernel(const float *v, const T *ga
 __global__ void __launch_bounds__(256) absmax_part_kernel(const bf16_t *v, int64_t n, float *part) {
   __shared__ float red[4];
   float m = 0.f;
-  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-    m = fmaxf(m, fabsf((float)v[i]));
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  // 16-byte runs of 8 values when aligned: a bf16's magnitude is its bits without the sign, as the
+  // high half of an fp32 (a NaN stays a NaN, which fmaxf passes over, as in the scalar loop)
+  const int64_t n8 = ((uintptr_t)v & 15) == 0 ? n / 8 : 0;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n8; i += stride) {
+    const uint4 r = ((const uint4 *)v)[i];
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      m = fmaxf(m, fmaxf(__uint_as_float((w[k] << 16) & 0x7fffffffu), __uint_as_float(w[k] & 0x7fff0000u)));
+  }
+  for (int64_t i = n8 * 8 + blockIdx.x * 256ll + threadIdx.x; i < n; i += stride) m = fmaxf(m, fabsf((float)v[i]));
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
@@ -773,7 +783,15 @@ __global__ void __launch_bounds__(256) unscale_grads_kernel(GradList g, const fl
   float *p = g.p[blockIdx.y];
   const int64_t n = g.n[blockIdx.y];
   const float inv = sc[1];
-  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] *= inv;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  // 16-byte runs when aligned, then the rest one by one
+  const int64_t n4 = ((uintptr_t)p & 15) == 0 ? n / 4 : 0;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n4; i += stride) {
+    float4 v = ((float4 *)p)[i];
+    v.x *= inv; v.y *= inv; v.z *= inv; v.w *= inv;
+    ((float4 *)p)[i] = v;
+  }
+  for (int64_t i = n4 * 4 + blockIdx.x * 256ll + threadIdx.x; i < n; i += stride) p[i] *= inv;
 }
 
 __global__ void __launch_bounds__(256) zero_cols_kernel(f16_t *dst, int64_t ldd, int32_t rows, int32_t c0, int32_t c1) {
