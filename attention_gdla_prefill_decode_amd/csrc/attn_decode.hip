@@ -590,13 +590,45 @@ __device__ __forceinline__ int kv_head(int kv, int k, int ns, const LayerDims &d
   return k < ns ? kv + d.n_kv * k : d.n_signal + kv + d.n_kv * (k - ns);
 }
 
-// q~ = [q^C_h W_uk[:, kv(h)]^T ; q^R_h] in bf16.  Each thread keeps one W_uk row slice (d_h values
-// of latent dimension c) in registers and applies it to the block's R query rows.
-__global__ void __launch_bounds__(256) absorb_kernel(const float *qc, const float *qr, const bf16_t *w_uk,
-                                                     bf16_t *qabs, int32_t B, LayerDims d) {
+// Blocks (x >= nrb, kv) of the absorb launch: W_uv^T rows 128 kv .. 128 kv + 127 (the KV head's
+// value columns) as fp16 ([n_kv 128][d_c], K-contiguous for the un-absorbing MFMA), one 64 x 64
+// tile per block: column tile 2 kv + (t & 1), latent tile t >> 1 (t = x - nrb < 16).  Values are
+// exact in the fp16 normal range, rounded to nearest below it, +-inf above.
+__device__ __forceinline__ void transpose_wuv_tile(const bf16_t *w_uv, f16_t *wuvt, int kv, int t, int ldw) {
+  __shared__ bf16_t tt[64][72];  // row stride 144 B
+  const int k0 = (t >> 1) * 64, n0 = kv * 128 + (t & 1) * 64;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = threadIdx.x + 256 * i, r = q >> 3, c = (q & 7) * 8;
+    *(uint4 *)&tt[r][c] = *(const uint4 *)(w_uv + (int64_t)(k0 + r) * ldw + n0 + c);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = threadIdx.x + 256 * i, rn = q >> 3, kc = (q & 7) * 8;
+    f16_t o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (f16_t)(float)tt[kc + e][rn];
+    *(uint4 *)(wuvt + (int64_t)(n0 + rn) * DC + k0 + kc) = *(const uint4 *)o;
+  }
+}
+
+// q~ = [q^C_h W_uk[:, kv(h)]^T ; RoPE(q^R_h)] in bf16, for blocks x < nrb.  Each thread keeps one
+// W_uk row slice (d_h values of latent dimension c) in registers and applies it to the block's R
+// query rows.  q^R arrives unrotated (qrp) and is rotated here to position pos[m / T] + m % T of
+// its row set m (Eq.(2)), in fp32 before the bf16 rounding.  The blocks x >= nrb transpose W_uv
+// for the un-absorbing kernel (run after the split-L kernel in the same stream).
+__global__ void __launch_bounds__(256) absorb_kernel(const float *qc, const float *qrp, const bf16_t *w_uk,
+                                                     bf16_t *qabs, int32_t B, LayerDims d, const int32_t *pos,
+                                                     int32_t T, int32_t nrb, const bf16_t *w_uv, f16_t *wuvt) {
   __shared__ __attribute__((aligned(16))) float qs[R][128];
   __shared__ int64_t rowq[R];
+  __shared__ float2 cs[R][DR / 2];  // (cos, sin) of the block's rows
   const int kv = blockIdx.y, tid = threadIdx.x;
+  if ((int)blockIdx.x >= nrb) {
+    transpose_wuv_tile(w_uv, wuvt, kv, (int)blockIdx.x - nrb, d.n_kv * 128);
+    return;
+  }
   int ns;
   const int hk = kv_heads(kv, d, ns);
   const int r0 = blockIdx.x * R, nr = min(R, B * hk - r0);
@@ -610,9 +642,22 @@ __global__ void __launch_bounds__(256) absorb_kernel(const float *qc, const floa
     const int r = i >> 5, e = (i & 31) * 4;
     *(float4 *)&qs[r][e] = *(const float4 *)(qc + rowq[r] * 128 + e);
   }
-  for (int i = tid; i < nr * DR; i += 256) {
-    const int r = i / DR, e = i % DR;
-    qabs[rowq[r] * ROW + DC + e] = (bf16_t)qr[rowq[r] * DR + e];
+  for (int i = tid; i < nr * (DR / 2); i += 256) {
+    const int r = i / (DR / 2), j = i % (DR / 2);
+    const int m = (int)(rowq[r] / d.n_heads);
+    float c, s;
+    rope_cs(pos[m / T] + m % T, j, DR, d.theta, c, s);
+    cs[r][j] = make_float2(c, s);
+  }
+  __syncthreads();
+  for (int i = tid; i < nr * (DR / 2); i += 256) {
+    const int r = i / (DR / 2), j = i % (DR / 2);
+    const float c = cs[r][j].x, s = cs[r][j].y;
+    const float *q = qrp + rowq[r] * DR;
+    const float u = q[j], v = q[j + DR / 2];
+    const float a = u * c - v * s, b = u * s + v * c;
+    qabs[rowq[r] * ROW + DC + j] = (bf16_t)a;
+    qabs[rowq[r] * ROW + DC + j + DR / 2] = (bf16_t)b;
   }
   for (int i = nr * 32 + tid; i < R * 32; i += 256) {  // rows past the list: zeros
     const int r = i >> 5, e = (i & 31) * 4;
@@ -691,22 +736,50 @@ __global__ void __launch_bounds__(256) unabsorb_kernel(const float *part_o, cons
     if (ok && j == 0) linv[r] = 1.0f / L;
   }
   __syncthreads();
-  for (int i = tid; i < nr * (DC / 4); i += 256) {
-    const int r = i / (DC / 4), c = (i % (DC / 4)) * 4;
-    const int64_t b = rowq[r] / d.n_heads, h = rowq[r] % d.n_heads;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int sp = 0; sp < splits; ++sp) {
-      const float w = wsp[r][sp];
-      if (w == 0.f) continue;  // empty split (its partial is not written) or no weight
-      const float4 v = *(const float4 *)(part_o + ((b * splits + sp) * d.n_heads + h) * DC + c);
-      acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
-    }
-    const float inv = linv[r];
-    *(float4 *)&os[r][c] = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  // Every thread merges PER float4 of the block's rows.  The loads of up to MB splits are issued
+  // together before any is used (the merge is bound by their latency); a split with weight 0
+  // (empty: its partial was never written) is loaded anyway and discarded by the select, so the
+  // sum runs over the same terms in the same order as a loop that skips it.
+  constexpr int PER = R * (DC / 4) / 256, MB = 4;
+  static_assert(R * (DC / 4) % 256 == 0, "the block's rows split evenly over its threads");
+  float4 mrg[PER];
+  int64_t rb[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    mrg[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int r = (tid + 256 * u) / (DC / 4);
+    const int64_t bh = rowq[min(r, nr - 1)];
+    rb[u] = (bh / d.n_heads) * splits * d.n_heads + bh % d.n_heads;  // split 0's partial row
   }
-  for (int i = nr * (DC / 4) + tid; i < R * (DC / 4); i += 256) {
-    const int r = i / (DC / 4), c = (i % (DC / 4)) * 4;
-    *(float4 *)&os[r][c] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int sp0 = 0; sp0 < splits; sp0 += MB) {
+    float4 v[PER][MB];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int c = ((tid + 256 * u) % (DC / 4)) * 4;
+#pragma unroll
+      for (int j = 0; j < MB; ++j) {
+        const int sp = min(sp0 + j, splits - 1);
+        v[u][j] = *(const float4 *)(part_o + (rb[u] + (int64_t)sp * d.n_heads) * DC + c);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int r = (tid + 256 * u) / (DC / 4);
+#pragma unroll
+      for (int j = 0; j < MB; ++j) {
+        const float w = sp0 + j < splits && r < nr ? wsp[r][sp0 + j] : 0.f;
+        if (w != 0.f) {
+          mrg[u].x += w * v[u][j].x; mrg[u].y += w * v[u][j].y;
+          mrg[u].z += w * v[u][j].z; mrg[u].w += w * v[u][j].w;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int r = (tid + 256 * u) / (DC / 4), c = ((tid + 256 * u) % (DC / 4)) * 4;
+    const float inv = r < nr ? linv[r] : 0.f;  // rows past the list: zeros
+    *(float4 *)&os[r][c] = make_float4(mrg[u].x * inv, mrg[u].y * inv, mrg[u].z * inv, mrg[u].w * inv);
   }
   __syncthreads();
   // H[r][e] = sum_c o[r][c] W_uv[c][128 kv + e] on v_mfma_f32_16x16x32_f16 (A[m = r][k = c],
@@ -750,7 +823,7 @@ int32_t fast_decode_splits(int32_t B, int32_t max_len) {
 
 gdla_status run_fast_decode(const LayerDims &d, const gdla_weights *w, int32_t B, int32_t T,
                             const int32_t *pos_dev, const CacheRef &cache, const float *qc,
-                            const float *qr, float *heads, const FastDecodeLayout &L, void *ws, hipStream_t s,
+                            const float *qrp, float *heads, const FastDecodeLayout &L, void *ws, hipStream_t s,
                             StageEvents &se) {
   const int32_t BT = B * T;  // query rows sets: token i of sequence b is row set b T + i
   bf16_t *qabs = (bf16_t *)((char *)ws + L.qabs);
@@ -758,7 +831,15 @@ gdla_status run_fast_decode(const LayerDims &d, const gdla_weights *w, int32_t B
   float *part_ml = (float *)((char *)ws + L.part_ml);
   const int hk_max = (d.n_signal + d.n_kv - 1) / d.n_kv + (d.n_noise + d.n_kv - 1) / d.n_kv;
   const dim3 gk((unsigned)((BT * hk_max + R - 1) / R), (unsigned)d.n_kv);
-  hipLaunchKernelGGL(absorb_kernel, gk, dim3(256), 0, s, qc, qr, (const bf16_t *)w->w_uk, qabs, BT, d);
+  // 16 more blocks per KV head transpose its W_uv columns (128 x d_c in 64 x 64 tiles, 16-byte
+  // accesses); a W_uv that is not 16-byte aligned goes through the general transpose instead
+  f16_t *wuvt = (f16_t *)((char *)ws + L.wuvt);
+  const bool wuv_in_absorb = ((uintptr_t)w->w_uv & 15) == 0;
+  if (!wuv_in_absorb && launch_transpose_weight(w->w_uv, wuvt, DC, d.n_kv * 128, true, s) != hipSuccess)
+    return GDLA_ERR_HIP;
+  const dim3 ga(gk.x + (wuv_in_absorb ? 16 : 0), gk.y);
+  hipLaunchKernelGGL(absorb_kernel, ga, dim3(256), 0, s, qc, qrp, (const bf16_t *)w->w_uk, qabs, BT, d, pos_dev, T,
+                     (int32_t)gk.x, (const bf16_t *)w->w_uv, wuvt);
   if (hipGetLastError() != hipSuccess) return GDLA_ERR_HIP;
   se.end(GDLA_STAGE_PROJ_Q);
   DecodeArgs a{};
@@ -781,8 +862,6 @@ gdla_status run_fast_decode(const LayerDims &d, const gdla_weights *w, int32_t B
   se.end(GDLA_STAGE_ATTN_NOISE);
   se.begin(GDLA_STAGE_ATTN_SIGNAL);
   if (L.splits > MAX_SPLITS) return GDLA_ERR_UNSUPPORTED;
-  f16_t *wuvt = (f16_t *)((char *)ws + L.wuvt);
-  if (launch_transpose_weight(w->w_uv, wuvt, DC, d.n_kv * 128, true, s) != hipSuccess) return GDLA_ERR_HIP;
   hipLaunchKernelGGL(unabsorb_kernel, gk, dim3(256), 0, s, part_o, part_ml, L.splits, (const f16_t *)wuvt, heads,
                      BT, d);
   if (hipGetLastError() != hipSuccess) return GDLA_ERR_HIP;

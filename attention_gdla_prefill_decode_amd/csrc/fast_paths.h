@@ -106,10 +106,11 @@ FastDecodeLayout plan_fast_decode(const LayerDims &d, int32_t B, int32_t max_len
 
 bool fast_decode_supported(const LayerDims &d, gdla_dtype dt);
 // T new tokens per sequence (token i of sequence b at position pos_dev[b] + i, already appended);
-// qc, qr, heads hold B T row sets of n_H heads.
+// qc, qrp (q^R before its rotation, which the path applies itself), heads hold B T row sets of
+// n_H heads.
 gdla_status run_fast_decode(const LayerDims &d, const gdla_weights *w, int32_t B, int32_t T,
                             const int32_t *pos_dev, const CacheRef &cache, const float *qc,
-                            const float *qr, float *heads, const FastDecodeLayout &L, void *ws,
+                            const float *qrp, float *heads, const FastDecodeLayout &L, void *ws,
                             hipStream_t s, StageEvents &se);
 
 // ---- fused backward (bf16 layer, d_head 128, d_rope 64; training sequences from position 0) ----

@@ -892,14 +892,15 @@ gdla_status decode_impl(const gdla_dims *dims, const gdla_weights *w, const void
                   (int64_t)d.n_signal * d.d_h, M, d.n_signal * d.d_h, d.d_cq, true);
   for (int i = 0; i < g.n; ++i) g.p[i].A_lo = cq_lo;
   HIP_TRY(launch_gemm_rows(g, dt, partial, L.skinny_bytes, stream));
-  HIP_TRY(launch_rope_heads(at<float>(ws, L.qrp), at<float>(ws, L.qr), (int64_t)d.n_heads * d.d_r, d.d_r, 0,
-                            M, T, d.n_heads, d.d_r, pos_dev, d.theta, DT::F32, stream));
   if (L.use_fast) {
-    // ends GDLA_STAGE_PROJ_Q after the absorbed query; leaves GDLA_STAGE_ATTN_SIGNAL open
-    st = run_fast_decode(d, w, B, T, pos_dev, cache, at<float>(ws, L.qc), at<float>(ws, L.qr),
+    // rotates q^R itself; ends GDLA_STAGE_PROJ_Q after the absorbed query; leaves
+    // GDLA_STAGE_ATTN_SIGNAL open
+    st = run_fast_decode(d, w, B, T, pos_dev, cache, at<float>(ws, L.qc), at<float>(ws, L.qrp),
                          at<float>(ws, L.heads), L.fast, ws, stream, se);
     if (st != GDLA_OK) return fail(st, "fast decode path failed: %s", hipGetErrorString(hipGetLastError()));
   } else {
+    HIP_TRY(launch_rope_heads(at<float>(ws, L.qrp), at<float>(ws, L.qr), (int64_t)d.n_heads * d.d_r, d.d_r, 0,
+                              M, T, d.n_heads, d.d_r, pos_dev, d.theta, DT::F32, stream));
     se.end(GDLA_STAGE_PROJ_Q);
     se.begin(GDLA_STAGE_ATTN_NOISE);
     HIP_TRY(launch_absorb_generic(at<float>(ws, L.qc), at<float>(ws, L.qr), w->w_uk, at<float>(ws, L.qabs),

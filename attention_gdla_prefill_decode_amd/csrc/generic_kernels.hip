@@ -124,15 +124,6 @@ hipError_t launch_gemm_generic(GemmBatch &batch, DT in_dt, hipStream_t s) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Rotation angles p * theta^(-2j/d_r) are formed and reduced modulo 2*pi in fp64 so that large
-// positions (hundreds of thousands) keep full fp32 accuracy in cos / sin.
-__device__ __forceinline__ void rope_cs(int p, int j, int d_r, float theta, float &c, float &s) {
-  const double freq = pow((double)theta, -2.0 * (double)j / (double)d_r);
-  double a = (double)p * freq;
-  const double two_pi = 6.283185307179586476925286766559;
-  a -= floor(a / two_pi) * two_pi;
-  sincosf((float)a, &s, &c);
-}
 
 template <typename T>
 __global__ void __launch_bounds__(256) prep_kernel(PrepArgs a, LayerDims d) {
