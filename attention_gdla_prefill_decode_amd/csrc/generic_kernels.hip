@@ -173,8 +173,92 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs a, LayerDims d) {
   }
 }
 
+// The same step for bf16 layers of the MFMA paths' sizes (d_cq 1024, d_c 512, d_r 64): one wave per
+// token row, 16-byte loads of the fp32 projections and 8-byte stores, wave reductions only (no
+// block barrier).  Lane l holds elements 4 l + 256 i .. + 3 of each row.
+template <int N>
+__device__ __forceinline__ void rms_row(const float *row, const bf16_t *g, float eps, int lane, float (&v)[N / 64]) {
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < N / 256; ++i) {
+    const float4 x = *(const float4 *)(row + 4 * lane + 256 * i);
+    v[4 * i] = x.x; v[4 * i + 1] = x.y; v[4 * i + 2] = x.z; v[4 * i + 3] = x.w;
+    ss += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+  }
+  const float r = rsqrtf(wave_sum(ss) / N + eps);
+#pragma unroll
+  for (int i = 0; i < N / 256; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[4 * i + e] = v[4 * i + e] * r * (g ? (float)g[4 * lane + 256 * i + e] : 1.f);
+}
+
+__global__ void __launch_bounds__(256) prep_rows_kernel(PrepArgs a, LayerDims d) {
+  constexpr int DCQ = 1024, DCK = 512, DR = 64;
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= a.M) return;
+  const int b = m / a.T, t = m % a.T;
+  const int p = a.pos[b] + t;
+  if (a.cq) {
+    float v[DCQ / 64];
+    rms_row<DCQ>(a.aq + (int64_t)m * DCQ, (const bf16_t *)a.gamma_q, d.eps, lane, v);
+#pragma unroll
+    for (int i = 0; i < DCQ / 256; ++i) {
+      const int64_t o = (int64_t)m * DCQ + 4 * lane + 256 * i;
+      if (a.cq_f16) {
+        f16_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = (f16_t)v[4 * i + e];
+        *(uint2 *)((f16_t *)a.cq + o) = *(const uint2 *)h;
+      } else {
+        bf16_t h[4], l[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          h[e] = (bf16_t)v[4 * i + e];
+          l[e] = (bf16_t)(v[4 * i + e] - (float)h[e]);
+        }
+        *(uint2 *)((bf16_t *)a.cq + o) = *(const uint2 *)h;
+        if (a.cq_lo) *(uint2 *)((bf16_t *)a.cq_lo + o) = *(const uint2 *)l;
+      }
+    }
+  }
+  bf16_t *crow = (bf16_t *)a.cache.base + cache_row(a.cache, b, p) * (DCK + DR);
+  {
+    float v[DCK / 64];
+    rms_row<DCK>(a.ckv + (int64_t)m * DCK, (const bf16_t *)a.gamma_kv, d.eps, lane, v);
+#pragma unroll
+    for (int i = 0; i < DCK / 256; ++i) {
+      bf16_t h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[e] = (bf16_t)v[4 * i + e];
+      *(uint2 *)(crow + 4 * lane + 256 * i) = *(const uint2 *)h;
+    }
+  }
+  if (lane < DR / 2) {
+    float c, s;
+    rope_cs(p, lane, DR, d.theta, c, s);
+    const float u = a.kr[(int64_t)m * DR + lane], v = a.kr[(int64_t)m * DR + lane + DR / 2];
+    crow[DCK + lane] = (bf16_t)(u * c - v * s);
+    crow[DCK + lane + DR / 2] = (bf16_t)(u * s + v * c);
+  }
+  if (a.lam) {
+    for (int i = lane; i < d.n_signal; i += 64) {
+      const int64_t o = (int64_t)m * d.n_signal + i;
+      a.lam[o] = a.lam_override ? a.lam_override[o] : sigmoidf_(a.lam_logit[o]);
+    }
+  }
+}
+
 hipError_t launch_prep(const PrepArgs &a, const LayerDims &d, DT dt, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
+  // every row of the cache holds d_c + d_r = 576 bf16 (1152 B, 8-byte aligned rows)
+  const bool rows = dt == DT::BF16 && d.d_cq == 1024 && d.d_c == 512 && d.d_r == 64 &&
+                    ((uintptr_t)a.aq & 15) == 0 && ((uintptr_t)a.ckv & 15) == 0 && ((uintptr_t)a.cache.base & 7) == 0 &&
+                    (!a.cq || ((uintptr_t)a.cq & 7) == 0) && (!a.cq_lo || ((uintptr_t)a.cq_lo & 7) == 0);
+  if (rows) {
+    hipLaunchKernelGGL(prep_rows_kernel, dim3((unsigned)((a.M + 3) / 4)), dim3(256), 0, s, a, d);
+    return hipGetLastError();
+  }
   if (dt == DT::F32) hipLaunchKernelGGL(prep_kernel<float>, dim3(a.M), dim3(256), 0, s, a, d);
   else hipLaunchKernelGGL(prep_kernel<bf16_t>, dim3(a.M), dim3(256), 0, s, a, d);
   return hipGetLastError();
