@@ -832,12 +832,9 @@ gdla_status run_fast_decode(const LayerDims &d, const gdla_weights *w, int32_t B
   const int hk_max = (d.n_signal + d.n_kv - 1) / d.n_kv + (d.n_noise + d.n_kv - 1) / d.n_kv;
   const dim3 gk((unsigned)((BT * hk_max + R - 1) / R), (unsigned)d.n_kv);
   // 16 more blocks per KV head transpose its W_uv columns (128 x d_c in 64 x 64 tiles, 16-byte
-  // accesses); a W_uv that is not 16-byte aligned goes through the general transpose instead
+  // accesses: the entry points accept only 16-byte aligned weights)
   f16_t *wuvt = (f16_t *)((char *)ws + L.wuvt);
-  const bool wuv_in_absorb = ((uintptr_t)w->w_uv & 15) == 0;
-  if (!wuv_in_absorb && launch_transpose_weight(w->w_uv, wuvt, DC, d.n_kv * 128, true, s) != hipSuccess)
-    return GDLA_ERR_HIP;
-  const dim3 ga(gk.x + (wuv_in_absorb ? 16 : 0), gk.y);
+  const dim3 ga(gk.x + 16, gk.y);
   hipLaunchKernelGGL(absorb_kernel, ga, dim3(256), 0, s, qc, qrp, (const bf16_t *)w->w_uk, qabs, BT, d, pos_dev, T,
                      (int32_t)gk.x, (const bf16_t *)w->w_uv, wuvt);
   if (hipGetLastError() != hipSuccess) return GDLA_ERR_HIP;
