@@ -741,13 +741,22 @@ __global__ void __launch_bounds__(256) absmax_part_kernel(const bf16_t *v, int64
   // 16-byte runs of 8 values when aligned: a bf16's magnitude is its bits without the sign, as the
   // high half of an fp32 (a NaN stays a NaN, which fmaxf passes over, as in the scalar loop)
   const int64_t n8 = ((uintptr_t)v & 15) == 0 ? n / 8 : 0;
-  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n8; i += stride) {
-    const uint4 r = ((const uint4 *)v)[i];
+  auto take = [&](const uint4 r) {
     const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       m = fmaxf(m, fmaxf(__uint_as_float((w[k] << 16) & 0x7fffffffu), __uint_as_float(w[k] & 0x7fff0000u)));
+  };
+  // four runs in flight per thread (the pass is bound by load latency), then the rest
+  int64_t i = blockIdx.x * 256ll + threadIdx.x;
+  for (; i + 3 * stride < n8; i += 4 * stride) {
+    uint4 r[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) r[u] = ((const uint4 *)v)[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) take(r[u]);
   }
+  for (; i < n8; i += stride) take(((const uint4 *)v)[i]);
   for (int64_t i = n8 * 8 + blockIdx.x * 256ll + threadIdx.x; i < n; i += stride) m = fmaxf(m, fabsf((float)v[i]));
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
@@ -786,7 +795,19 @@ __global__ void __launch_bounds__(256) unscale_grads_kernel(GradList g, const fl
   const int64_t stride = (int64_t)gridDim.x * 256;
   // 16-byte runs when aligned, then the rest one by one
   const int64_t n4 = ((uintptr_t)p & 15) == 0 ? n / 4 : 0;
-  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n4; i += stride) {
+  // four runs loaded before any is stored (the pass is bound by load latency), then the rest
+  int64_t i = blockIdx.x * 256ll + threadIdx.x;
+  for (; i + 3 * stride < n4; i += 4 * stride) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = ((float4 *)p)[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      v[u].x *= inv; v[u].y *= inv; v[u].z *= inv; v[u].w *= inv;
+      ((float4 *)p)[i + u * stride] = v[u];
+    }
+  }
+  for (; i < n4; i += stride) {
     float4 v = ((float4 *)p)[i];
     v.x *= inv; v.y *= inv; v.z *= inv; v.w *= inv;
     ((float4 *)p)[i] = v;
