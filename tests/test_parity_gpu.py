@@ -66,6 +66,27 @@ def test_bf16_prefill(seq, p0, window):
         H.check_rows(r["rows"][b], r["exp_rows"][b], "bf16", "bf16 cache rows")
 
 
+# A layer with the full query latent (d_cq 1024): A2 runs on the row-wise kernel (one wave per token
+# row) rather than the general one; its cache rows and outputs against the oracle, in prefill (T =
+# 300, so the query-side latent leaves in fp16 for the transposed-weight GEMM, and T = 40 on the
+# general GEMMs) and in decode (latent with its bf16 remainder for the skinny projections).
+BF_CQ1024 = dict(BF, d_q_latent=1024)
+
+
+@pytest.mark.parametrize("seq,p0", [(300, [0]), (40, [3, 0])])
+def test_bf16_prefill_full_query_latent(seq, p0):
+    r = H.prefill_case(BF_CQ1024, seq, p0, seed=41)
+    _say(H.check(r["out"], r["exp_out"], "bf16", f"bf16 d_cq 1024 T={seq} p0={p0}"))
+    for b in range(len(p0)):
+        H.check_rows(r["rows"][b], r["exp_rows"][b], "bf16", "bf16 d_cq 1024 cache rows")
+
+
+def test_bf16_decode_full_query_latent():
+    r = H.decode_case(BF_CQ1024, [50, 0, 17], seed=43)
+    _say(H.check(r["out"], r["exp_out"], "bf16", "bf16 d_cq 1024 decode"))
+    H.check_rows(r["rows"], r["exp_rows"], "bf16", "bf16 d_cq 1024 decode cache rows")
+
+
 def test_bf16_prefill_odd_signal_heads():
     # 12 signal heads: the lambda projection's 12 columns cannot leave the transposed-weight GEMM
     # as 16-byte segments and go to the general GEMM (>= 256 rows take the transposed path)
